@@ -1,0 +1,358 @@
+"""MonarchAttention forward pass, step by step, in float64 NumPy.
+
+Test infrastructure only (see the package docstring).
+
+What the pages fix
+------------------
+* Attention is replaced by a Monarch matrix M = P L P^T R with L and R block
+  diagonal, so that after a fixed permutation M is a grid of rank-one blocks
+  ([MRT] "Method" part (1); [MA] scime summary "Approach": block rank-one
+  factors).
+* L and R are fitted by alternating maximisation of the softmax variational
+  objective (linear score term plus entropy, entropy maximised) for T steps,
+  never forming the N x N matrix ([MA] scime summary "Proposal"/"Approach";
+  OpenReview first review and the author response on concavity).
+* L and R are constrained to be positive ([MA] OpenReview first review,
+  question on "Alternating Maximization with Constraints", and the response).
+* With L fixed the objective is concave in R (author response), so each
+  half-step is an exact block-wise maximisation.
+* T is small: the objective is stationary after about two steps (author
+  response table of f(M) against T).
+* Cost Theta(N sqrt(N) d) compute, Theta(N d) IO ([MA] abstract).
+* Tiled Monarch: each Monarch block is cut into c1 x c2 sub-tiles that are
+  rank one each ([MRT] "Key claims", Theorem 4.1 / section 4.2, and "Method"
+  part (2)).
+
+Notation (ours)
+---------------
+Grid position of a query: (l, i), l in [b1], i in [b2]; of a key: (k, j).
+Queries already carry the score scale sigma (sigma = 1/sqrt(d) by default).
+
+    M[(l,i),(k,j)] = L[i,l,k] * R[k,i,j]                       (untiled)
+    M[(l,i),(k,j)] = L[i,l,k,s(j)] * R[k,i,t(l),j]             (tiled)
+
+with t(l) = floor(l*c1/b1) the row tile and s(j) = floor(j*c2/b2) the column
+segment.  Rows of R sum to one (per segment when tiled) and rows of L sum to
+one (over (k, s) when tiled); this fixes the scale freedom of a rank-one block
+and loses nothing, since M itself has simplex rows.
+
+The update equations are not printed on the pages.  They follow exactly from
+the objective by maximising it over one factor with the other fixed:
+
+  row entropy splits:  H(M_(l,i)) = H(L[i,l,:]) + sum_k L[i,l,k] H(R[k,i,:])
+
+  R-update (L fixed): for every (k, i), the terms holding R[k,i,:] are
+      beta * ( <R[k,i,:], qt[k,i] . K_k> + H(R[k,i,:]) )
+  with alpha[k,i] = sum_l L[i,l,k] q[l,i], beta[k,i] = sum_l L[i,l,k] and
+  qt = alpha / beta, so R[k,i,:] = softmax_j(qt[k,i] . k[k,j]).
+
+  L-update (R fixed): for every (i, l),
+      L[i,l,:] = softmax_k( q[l,i] . c[k,i] + H_R[k,i] ),
+  c[k,i] = sum_j R[k,i,j] k[k,j] and H_R[k,i] = H(R[k,i,:]).  The entropy
+  enters with a plus sign (a reviewer noted that the paper's printed
+  expansion had two sign errors that turned entropy into negative entropy).
+
+  Output: y[l,i] = sum_k L[i,l,k] u[k,i], u[k,i] = sum_j R[k,i,j] v[k,j].
+
+Readings where the pages are silent (each also listed in the design doc):
+  * initialisation L0 = block identity, so qt[k,i] = q[k,i] for the first
+    R-update; a step is one R-update then one L-update; the first point of
+    the objective trace is f(L0, R1);
+  * tiled initialisation: the tiled block identity gives a zero weight
+    (beta = 0) to every sub-row with t != t(k); there qt is the mean of
+    q[l,i] over the rows l of tile t (the eps -> 0 limit of
+    (1-eps) I + eps * uniform).  The same fallback is used whenever beta is
+    exactly zero.
+
+Parity pins (tests/test_oracle_pins.py): dense product P^T L P R on tiny
+grids, simplex rows, non-decreasing objective bounded by sum logsumexp, dense
+limits b1 = 1 and b2 = 1, exactness on separable scores (all six aligned video
+layouts, and failure on a misaligned one), half-steps equal to a generic
+numerical maximiser of the dense objective, tiled c1 = c2 = 1 equal to
+untiled, tiled c2 = b2 equal to exact attention, and invariance under
+relabelling of keys and blocks.
+"""
+
+import numpy as np
+
+from .layouts import grid_index, to_grid, from_grid
+from .reference_attention import logsumexp, softmax, row_entropy
+
+
+def tile_of_rows(b1, c1):
+    """t(l) = floor(l * c1 / b1) for l in [b1]."""
+    return (np.arange(b1) * c1) // b1
+
+
+def segment_of_cols(b2, c2):
+    """s(j) = floor(j * c2 / b2) for j in [b2]."""
+    return (np.arange(b2) * c2) // b2
+
+
+# ---------------------------------------------------------------------------
+# untiled Monarch
+# ---------------------------------------------------------------------------
+
+def _objective_untiled(q, C, HR, L):
+    """f(L, R) from the factored form: sum over rows (l, i) of
+    sum_k L[i,l,k] (q[l,i].c[k,i] + H_R[k,i]) + H(L[i,l,:])."""
+    w = np.matmul(q.transpose(1, 0, 2), C.transpose(1, 2, 0)) + HR.T[:, None, :]
+    return float(np.sum(L * w) + np.sum(row_entropy(L, axis=-1)))
+
+
+def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False):
+    """One (batch, head) slice of untiled MonarchAttention.
+
+    qg, kg, vg: [b1, b2, d] in grid order (float64).  cols: optional list of
+    columns i to compute (the method is independent across i: R rows [., i, .]
+    and L[i] touch only column i of the queries, and all keys).
+
+    Returns dict:
+      y       [b1, nc, d]   output rows (l, i) for the selected columns
+      L       [nc, b1, b1]  L[i, l, k]
+      R       [b1, nc, b2]  R[k, i, j]
+      lse     [b1, nc]      logsumexp_k of the last L-update's scores
+      f_trace [2*steps]     f(L0,R1), f(L1,R1), f(L1,R2), ..., f(LT,RT)
+      history list of (L, R) after every half-step (if history=True)
+    """
+    b1, b2, d = qg.shape
+    if steps < 1:
+        raise ValueError("steps must be >= 1")
+    cols = np.arange(b2) if cols is None else np.asarray(cols)
+    q = scale * qg[:, cols, :]               # q[l, i], sigma folded in
+    nc = q.shape[1]
+
+    # L0 = block identity: L0[i, l, k] = [l == k], hence qt[k, i] = q[k, i].
+    L = np.broadcast_to(np.eye(b1), (nc, b1, b1)).copy()
+    qt = q.copy()
+    f_trace, hist = [], []
+
+    for step in range(steps):
+        # R-update: R[k,i,:] = softmax_j(qt[k,i] . k[k,j])
+        z = np.matmul(qt, kg.transpose(0, 2, 1))          # z[k, i, j]
+        R = softmax(z, axis=-1)
+        HR = row_entropy(R, axis=-1)                       # H_R[k, i]
+        C = np.matmul(R, kg)                               # c[k, i]
+        f_trace.append(_objective_untiled(q, C, HR, L))
+        if history:
+            hist.append((L.copy(), R.copy()))
+
+        # L-update: L[i,l,:] = softmax_k(q[l,i] . c[k,i] + H_R[k,i])
+        w = np.matmul(q.transpose(1, 0, 2), C.transpose(1, 2, 0)) + HR.T[:, None, :]
+        L = softmax(w, axis=-1)                            # L[i, l, k]
+        lse = logsumexp(w, axis=-1)                        # [i, l]
+        f_trace.append(_objective_untiled(q, C, HR, L))
+        if history:
+            hist.append((L.copy(), R.copy()))
+
+        if step < steps - 1:
+            # next R-update's query: qt = alpha / beta
+            alpha = np.matmul(L.transpose(0, 2, 1), q.transpose(1, 0, 2))  # [i, k, d]
+            beta = np.sum(L, axis=1)                                       # [i, k]
+            safe = np.where(beta > 0, beta, 1.0)
+            qt_i = np.where((beta > 0)[..., None], alpha / safe[..., None],
+                            q.mean(axis=0)[:, None, :])
+            qt = qt_i.transpose(1, 0, 2)                   # [k, i, d]
+
+    U = np.matmul(R, vg)                                   # u[k, i]
+    y = np.matmul(L, U.transpose(1, 0, 2)).transpose(1, 0, 2)   # y[l, i]
+    out = dict(y=y, L=L, R=R, lse=lse.T, f_trace=np.array(f_trace))
+    if history:
+        out["history"] = hist
+    return out
+
+
+# ---------------------------------------------------------------------------
+# tiled Monarch
+# ---------------------------------------------------------------------------
+
+def _objective_tiled(q, C, HR, L, tile):
+    """f(L, R) for the tiled class: sum over rows (l, i) of
+    sum_{k,s} L[i,l,k,s] (q[l,i].c[k,i,t(l),s] + H_R[k,i,t(l),s]) + H(L row)."""
+    total = 0.0
+    for t in np.unique(tile):
+        rows = np.nonzero(tile == t)[0]
+        w = _tiled_scores(q[rows], C[:, :, t], HR[:, :, t])      # [i, rows, k, s]
+        Lt = L[:, rows]
+        nc, nr = Lt.shape[:2]
+        total += np.sum(Lt * w) + np.sum(row_entropy(Lt.reshape(nc, nr, -1), axis=-1))
+    return float(total)
+
+
+def _tiled_scores(q_rows, C_t, HR_t):
+    """w[i, l, k, s] = q[l,i] . c[k,i,t,s] + H_R[k,i,t,s] for rows l of one tile t.
+
+    q_rows [nr, nc, d]; C_t [b1, nc, c2, d]; HR_t [b1, nc, c2]."""
+    b1, nc, c2, d = C_t.shape
+    Ci = C_t.transpose(1, 0, 2, 3).reshape(nc, b1 * c2, d)          # [i, (k,s), d]
+    w = np.matmul(q_rows.transpose(1, 0, 2), Ci.transpose(0, 2, 1))  # [i, l, (k,s)]
+    w = w + HR_t.transpose(1, 0, 2).reshape(nc, 1, b1 * c2)
+    return w.reshape(nc, q_rows.shape[0], b1, c2)
+
+
+def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False):
+    """One slice of tiled MonarchAttention with c1 x c2 sub-tiles per block.
+
+    Requires c1 | b1 and c2 | b2 (tiles and segments are then contiguous and
+    of equal size).  Returns dict:
+      y       [b1, nc, d]
+      L       [nc, b1, b1, c2]   L[i, l, k, s]
+      R       [b1, nc, c1, b2]   R[k, i, t, j]  (each segment of j sums to 1)
+      lse     [b1, nc]
+      f_trace [2*steps]
+    """
+    b1, b2, d = qg.shape
+    if steps < 1:
+        raise ValueError("steps must be >= 1")
+    if b1 % c1 or b2 % c2:
+        raise ValueError("c1 must divide b1 and c2 must divide b2")
+    cols = np.arange(b2) if cols is None else np.asarray(cols)
+    q = scale * qg[:, cols, :]                    # q[l, i]
+    nc = q.shape[1]
+    sw = b2 // c2                                  # keys per segment
+    tile = tile_of_rows(b1, c1)
+    Kseg = kg.reshape(b1, c2, sw, d)               # K[k, s, j'], j = s*sw + j'
+    dv = vg.shape[-1]
+    Vseg = vg.reshape(b1, c2, sw, dv)
+
+    # tile means of the queries, qbar[t, i]
+    qbar = np.stack([q[tile == t].mean(axis=0) for t in range(c1)])   # [c1, nc, d]
+
+    # initial qt[k, i, t, s]: own tile -> q[k, i]; other tiles -> qbar[t, i]
+    qt = np.empty((b1, nc, c1, c2, d))
+    for k in range(b1):
+        for t in range(c1):
+            qt[k, :, t, :, :] = (q[k] if t == tile[k] else qbar[t])[:, None, :]
+
+    # L0: tiled block identity, mass 1/c2 on every segment of the own block
+    L = np.zeros((nc, b1, b1, c2))
+    L[:, np.arange(b1), np.arange(b1), :] = 1.0 / c2
+
+    f_trace, hist = [], []
+    for step in range(steps):
+        # R-update, per (k, i, t, s): R = softmax over j in segment s of
+        # qt[k,i,t,s] . k[k,j]
+        z = np.einsum("kitsd,ksjd->kitsj", qt, Kseg)       # [k, i, t, s, j']
+        Rs = softmax(z, axis=-1)
+        HR = row_entropy(Rs, axis=-1)                      # [k, i, t, s]
+        C = np.einsum("kitsj,ksjd->kitsd", Rs, Kseg)       # [k, i, t, s, d]
+        R = Rs.reshape(b1, nc, c1, b2)
+        f_trace.append(_objective_tiled(q, C, HR, L, tile))
+        if history:
+            hist.append((L.copy(), R.copy()))
+
+        # L-update, per (i, l): L[i,l,:,:] = softmax over (k, s) of
+        # q[l,i] . c[k,i,t(l),s] + H_R[k,i,t(l),s]
+        L = np.empty((nc, b1, b1, c2))
+        lse = np.empty((nc, b1))
+        for t in range(c1):
+            rows = np.nonzero(tile == t)[0]
+            w = _tiled_scores(q[rows], C[:, :, t], HR[:, :, t])   # [i, rows, k, s]
+            wf = w.reshape(nc, rows.size, b1 * c2)
+            L[:, rows] = softmax(wf, axis=-1).reshape(nc, rows.size, b1, c2)
+            lse[:, rows] = logsumexp(wf, axis=-1)
+        f_trace.append(_objective_tiled(q, C, HR, L, tile))
+        if history:
+            hist.append((L.copy(), R.copy()))
+
+        if step < steps - 1:
+            # qt[k,i,t,s] = sum_{l in t} L[i,l,k,s] q[l,i] / sum_{l in t} L[i,l,k,s]
+            qt = np.empty((b1, nc, c1, c2, d))
+            for t in range(c1):
+                rows = np.nonzero(tile == t)[0]
+                Lt = L[:, rows]                                   # [i, rows, k, s]
+                alpha = np.einsum("ilks,lid->kisd", Lt, q[rows])  # [k, i, s, d]
+                beta = np.einsum("ilks->kis", Lt)
+                safe = np.where(beta > 0, beta, 1.0)
+                qt[:, :, t] = np.where((beta > 0)[..., None], alpha / safe[..., None],
+                                       qbar[t][None, :, None, :])
+
+    U = np.einsum("kitsj,ksjd->kitsd", Rs, Vseg)           # u[k, i, t, s]
+    y = np.empty((b1, nc, dv))
+    for t in range(c1):
+        rows = np.nonzero(tile == t)[0]
+        # y[l,i] = sum_{k,s} L[i,l,k,s] u[k,i,t(l),s]
+        y[rows] = np.einsum("ilks,kisd->lid", L[:, rows], U[:, :, t])
+    out = dict(y=y, L=L, R=R, lse=lse.T, f_trace=np.array(f_trace))
+    if history:
+        out["history"] = hist
+    return out
+
+
+# ---------------------------------------------------------------------------
+# dense reconstruction (tiny grids only)
+# ---------------------------------------------------------------------------
+
+def dense_from_factors(L, R, b1, b2, c1=1, c2=1):
+    """Materialise M in grid order ([N, N], rows (l,i) -> l*b2+i, columns
+    (k,j) -> k*b2+j) from the entry formula.  L, R in the untiled shapes
+    [b2,b1,b1] / [b1,b2,b2] or the tiled shapes [b2,b1,b1,c2] / [b1,b2,c1,b2]."""
+    if L.ndim == 3:
+        L = L[..., None]
+    if R.ndim == 3:
+        R = R[:, :, None, :]
+    tile = tile_of_rows(b1, c1)
+    seg = segment_of_cols(b2, c2)
+    N = b1 * b2
+    M = np.empty((N, N))
+    for l in range(b1):
+        for i in range(b2):
+            for k in range(b1):
+                for j in range(b2):
+                    M[l * b2 + i, k * b2 + j] = L[i, l, k, seg[j]] * R[k, i, tile[l], j]
+    return M
+
+
+# ---------------------------------------------------------------------------
+# [B, H, N, d] driver
+# ---------------------------------------------------------------------------
+
+def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
+            fhw=None, cols=None, tiled=None, slices=None):
+    """MonarchAttention on [B, H, N, d] inputs (any float dtype, upcast to
+    float64).  The layout permutation maps token order to the b1 x b2 grid
+    (oracle.layouts); Y is mapped back.
+
+    cols: optional columns i to compute (Y is then NaN outside them).
+    slices: optional list of (b, h) pairs to compute (others left NaN).
+    tiled: force the tiled algorithm (default: tiled iff c1*c2 > 1).
+
+    Returns dict with y [B,H,N,d] (token order), L, R (per slice, grid
+    order, as returned by forward_untiled / forward_tiled, stacked), lse
+    [B,H,N] (token order) and f_trace [B,H,2T].
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, N, d = Q.shape
+    dv = V.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    grid = grid_index(N, b1, b2, layout, fhw)
+    if tiled is None:
+        tiled = c1 * c2 > 1
+    sel = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    colsel = np.arange(b2) if cols is None else np.asarray(cols)
+    nc = colsel.size
+
+    y = np.full((B, H, N, dv), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    if tiled:
+        Ls = np.full((B, H, nc, b1, b1, c2), np.nan)
+        Rs = np.full((B, H, b1, nc, c1, b2), np.nan)
+    else:
+        Ls = np.full((B, H, nc, b1, b1), np.nan)
+        Rs = np.full((B, H, b1, nc, b2), np.nan)
+    ft = np.full((B, H, 2 * steps), np.nan)
+    for (b, h) in sel:
+        qg, kg, vg = (to_grid(X[b, h], grid) for X in (Q, K, V))
+        if tiled:
+            r = forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=colsel)
+        else:
+            r = forward_untiled(qg, kg, vg, steps, scale, cols=colsel)
+        tok = grid[:, colsel]                      # tokens of the computed grid cells
+        y[b, h][tok.reshape(-1)] = r["y"].reshape(-1, dv)
+        lse[b, h][tok.reshape(-1)] = r["lse"].reshape(-1)
+        Ls[b, h] = r["L"]
+        Rs[b, h] = r["R"]
+        ft[b, h] = r["f_trace"]
+    return dict(y=y, L=Ls, R=Rs, lse=lse, f_trace=ft, grid=grid, cols=colsel)

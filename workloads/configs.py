@@ -1,0 +1,83 @@
+"""The five MonarchAttention forward workloads.
+
+Shapes follow the pages' speed workloads: N = 256, 4K and 16K sequences for
+language and vision ([MA] abstract: speed-ups at N = 256, 4K and 16K), and a
+3D video latent with Monarch blocks aligned to its (f, h, w) axes ([MRT] "Key
+claims", section 4.1) plus its tiled c1 x c2 variant ([MRT] Theorem 4.1).
+The video latent 21 x 30 x 52 with 12 heads and d = 128 is this project's
+stand-in for the 480p latents the MonarchRT page times (the page does not give
+the latent shape).
+"""
+
+from dataclasses import dataclass, field, asdict
+from typing import Optional, Tuple
+
+
+@dataclass(frozen=True)
+class WorkloadConfig:
+    index: int
+    name: str
+    batch: int
+    heads: int
+    seq_len: int
+    head_dim: int
+    b1: int
+    b2: int
+    steps: int
+    dtype: str                 # "f32" or "bf16"
+    data: str                  # generator recipe, see generators.py
+    seed: int
+    c1: int = 1
+    c2: int = 1
+    layout: str = "flat"
+    fhw: Optional[Tuple[int, int, int]] = None
+
+    @property
+    def slices(self):
+        return self.batch * self.heads
+
+    def algorithmic_flops(self):
+        """2*N*d*[3*c1*b2 + 2*c2*b1 + (T-1)*2*(c1*b2 + c2*b1)] per slice:
+        stage 1 forms c1*b2 scores per query row and two aggregates (R K, R V);
+        stage 2 forms c2*b1 scores per row and one aggregate (L U); every extra
+        step adds the stage-1 scores and aggregate R K again plus the stage-2
+        scores and the reduction L^T Q."""
+        N, d, b1, b2, c1, c2, T = (self.seq_len, self.head_dim, self.b1, self.b2,
+                                   self.c1, self.c2, self.steps)
+        per = 2 * N * d * (3 * c1 * b2 + 2 * c2 * b1 + (T - 1) * 2 * (c1 * b2 + c2 * b1))
+        return per * self.slices
+
+    def algorithmic_bytes(self):
+        """Q, K, V read once and Y written once."""
+        elt = 4 if self.dtype == "f32" else 2
+        return 4 * self.seq_len * self.head_dim * elt * self.slices
+
+    def describe(self):
+        d = asdict(self)
+        d["slices"] = self.slices
+        return d
+
+
+CONFIGS = {
+    1: WorkloadConfig(1, "N=256 16x16 d=64 T=1 fp32, 1 slice",
+                      batch=1, heads=1, seq_len=256, head_dim=64, b1=16, b2=16,
+                      steps=1, dtype="f32", data="iid", seed=1001),
+    2: WorkloadConfig(2, "N=4096 64x64 d=64 T=3 bf16, batch 8 x 12 heads",
+                      batch=8, heads=12, seq_len=4096, head_dim=64, b1=64, b2=64,
+                      steps=3, dtype="bf16", data="lowrank", seed=1002),
+    3: WorkloadConfig(3, "N=16384 128x128 d=64 T=1 bf16, 12 heads",
+                      batch=1, heads=12, seq_len=16384, head_dim=64, b1=128, b2=128,
+                      steps=1, dtype="bf16", data="normed", seed=1003),
+    4: WorkloadConfig(4, "video f,h,w=21,30,52 (fh,w)=(630,52) d=128 T=1 bf16, 12 heads",
+                      batch=1, heads=12, seq_len=32760, head_dim=128, b1=630, b2=52,
+                      steps=1, dtype="bf16", data="video", seed=1004,
+                      layout="fh_w", fhw=(21, 30, 52)),
+    5: WorkloadConfig(5, "video (630,52) tiled c1=c2=2 d=128 T=1 bf16, 12 heads",
+                      batch=1, heads=12, seq_len=32760, head_dim=128, b1=630, b2=52,
+                      steps=1, dtype="bf16", data="video", seed=1004,
+                      layout="fh_w", fhw=(21, 30, 52), c1=2, c2=2),
+}
+
+
+def get_config(i):
+    return CONFIGS[int(i)]
