@@ -1,0 +1,251 @@
+"""MonarchAttention forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--warm] [--fast-aggregate]
+
+A step is one monarch_attn_forward call (the whole hot path: layout gather,
+stage 1, stage 2, step loop, output scatter) over one batch of seeded
+synthetic input already resident in HBM.  The default workload is
+N=16384 as a 128x128 grid, d=64, 12 heads, T=1, bf16 (the configuration the
+headline metric names); --config picks another of the five workloads.
+
+Timing: W untimed warm-up calls, then exactly K calls bracketed by
+torch.cuda.synchronize().  Each call records HIP events before its first
+kernel and after every kernel on the launch stream (through the library's
+timed entry point), giving the per-call and per-kernel GPU time.  By default
+the K calls rotate over enough copies of Q, K, V, Y to exceed twice the
+256 MB Infinity Cache (cold mode: inputs come from HBM); --warm reuses one.
+
+Prints one JSON line: value = effective TFLOP/s (algorithmic flops of the
+method over the measured time), plus the dominant kernel's roofline and the
+CPU oracle timed on this host as a baseline.
+"""
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MonarchAttention fwd ms/call + effective TFLOP/s (frac. of roofline), N=16K d=64"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+MALL_BYTES = 256 * 1024 * 1024
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "structured_sub_quadratic_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(cfg, name, precise):
+    """Algorithmic HBM bytes of one launch: every operand the kernel must read
+    once and every result it must write once (per slice x slices)."""
+    S, N, d = cfg.slices, cfg.seq_len, cfg.head_dim
+    e = 4 if cfg.dtype == "f32" else 2
+    xc = 4 if (precise or cfg.dtype == "f32") else 2
+    rows = N * cfg.c1 * cfg.c2                       # exchange rows per slice
+    if name == "stage1_last":
+        b = 3 * N * d * e + rows * d * (xc + e) + rows * 8
+    elif name == "stage1":
+        b = 3 * N * d * e + rows * d * xc + rows * 8
+    elif name == "stage2_last":
+        b = N * d * e + rows * d * (xc + e) + rows * 4 + N * d * e + N * 4
+    elif name == "stage2_stats":
+        b = N * d * e + rows * d * xc + rows * 4 + N * 4
+    elif name == "alpha":
+        b = N * d * e + rows * d * xc + rows * 4 + N * 4 + rows * d * 4
+    elif name == "qbar":
+        b = N * d * e + cfg.c1 * cfg.b2 * d * 4
+    else:
+        return None
+    return b * S
+
+
+def cpu_baseline(cfg):
+    """The oracle as it stands, on this host, over the whole workload (or a
+    bounded number of slices), in the metric's unit."""
+    import numpy as np
+    import oracle
+    from workloads import make_inputs
+    cores = len(os.sched_getaffinity(0))
+    per_slice = cfg.algorithmic_flops() / cfg.slices
+    budget_s, spent, done = 20.0, 0.0, 0
+    slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    for sl in slices:
+        Q, K, V = make_inputs(cfg, slices=[sl])
+        t0 = time.perf_counter()
+        oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
+                       layout=cfg.layout, fhw=cfg.fhw, slices=[sl])
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent > budget_s:
+            break
+    tflops = per_slice * done / spent / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(slices)} slices of the same workload, NumPy float64, "
+                      f"{spent:.2f} s ({spent / done * 1e3:.0f} ms/slice; full call "
+                      f"would take {spent / done * len(slices):.1f} s)"}
+
+
+def sampled_parity(cfg, Q, K, V, y):
+    """Y, L, R of one slice at four columns against the oracle (quick check)."""
+    import numpy as np
+    import oracle
+    cols = sorted({0, cfg.b2 // 3, cfg.b2 // 2, cfg.b2 - 1})
+    ref = oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
+                         fhw=cfg.fhw, cols=cols, slices=[(0, 0)])
+    tok = ref["grid"][:, cols].reshape(-1)
+    a, r = y[0, 0][tok].astype(np.float64), ref["y"][0, 0][tok]
+    return float(np.abs(a - r).max() / np.abs(r).max())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--warm", action="store_true", help="reuse one input set (MALL-resident)")
+    ap.add_argument("--fast-aggregate", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy 3 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the slices are "
+              "independent and would shard across GPUs with no communication, but no "
+              "multi-GPU figure is produced here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import structured_sub_quadratic_amd as ma
+    from structured_sub_quadratic_amd import _lib
+    from workloads import get_config, make_inputs
+
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.empty(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    Q, K, V = make_inputs(cfg)
+    set_bytes = 4 * Q.size * (4 if cfg.dtype == "f32" else 2)
+    n_sets = 1 if args.warm else max(2, math.ceil(2.5 * MALL_BYTES / set_bytes))
+    base = [torch.from_numpy(x).to(dev).to(tdt) for x in (Q, K, V)]
+    sets = [(base[0].clone(), base[1].clone(), base[2].clone(), torch.empty_like(base[0]))
+            for _ in range(n_sets)]
+    del base
+
+    flags = ma.MA_FLAG_FAST_AGGREGATE if args.fast_aggregate else 0
+    prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2,
+                           cfg.steps, cfg.c1, cfg.c2, None, cfg.dtype, cfg.layout, cfg.fhw, flags)
+    names = ma.launch_names(prob)
+    nl = len(names)
+    ws_bytes = ma.workspace_size(prob)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nev = nl + 1
+    events = [[ma.Event() for _ in range(nev)] for _ in range(args.steps)]
+    ev_arrays = [(ctypes.c_void_p * nev)(*[e.ptr.value for e in row]) for row in events]
+    cex = _lib.MAExports(None, None, None, None)
+    pprob = ctypes.byref(prob)
+    pcex = ctypes.byref(cex)
+    call_args = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr()) for s in sets]
+
+    def call(i, evs=None, n=0):
+        q, k, v, y = call_args[i % n_sets]
+        if evs is None:
+            st = lib.monarch_attn_forward(pprob, q, k, v, y, pcex, ws.data_ptr(), ws_bytes, stream)
+        else:
+            st = lib.monarch_attn_forward_timed(pprob, q, k, v, y, pcex, ws.data_ptr(), ws_bytes,
+                                                stream, evs, n)
+        if st != 0:
+            raise RuntimeError(f"monarch_attn_forward failed: {st}")
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i, ev_arrays[i], nev)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    per_kernel = {n: [] for n in names}
+    for i in range(args.steps):
+        row = events[i]
+        for j, n in enumerate(names):
+            per_kernel[n].append(row[j].elapsed_ms(row[j + 1]))
+    span_ms = events[0][0].elapsed_ms(events[-1][-1]) / args.steps
+    call_ms = float(np.mean([events[i][0].elapsed_ms(events[i][-1]) for i in range(args.steps)]))
+    kern_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+
+    flops = cfg.algorithmic_flops()
+    ms = span_ms
+    value = flops / (ms * 1e-3) / 1e12
+
+    dom = max(set(names), key=lambda n: kern_ms[n])
+    precise = not args.fast_aggregate
+    kb = kernel_bytes(cfg, dom, precise)
+    achieved = kb / (kern_ms[dom] * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tr = json.load(fh)
+        key = f"config{cfg.index}{'_fast' if args.fast_aggregate else ''}:{dom}"
+        ent = tr.get(key)
+        if ent and ent.get("source_hash") == source_hash():
+            traffic = ent["hbm_bytes_per_launch"]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom, "algorithmic_bytes": kb, "kernel_ms": round(kern_ms[dom], 5)}
+    whole = {"algorithmic_bytes": cfg.algorithmic_bytes(),
+             "hbm_frac_of_call": round(cfg.algorithmic_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "mfma_frac_of_call": round(value / MFMA_PEAK_TFLOPS[cfg.dtype], 4)}
+
+    y = sets[(args.steps - 1) % n_sets][3].float().cpu().numpy()
+    parity = sampled_parity(cfg, Q, K, V, y)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "heads": cfg.heads,
+                   "seq_len": cfg.seq_len, "head_dim": cfg.head_dim, "b1": cfg.b1, "b2": cfg.b2,
+                   "T": cfg.steps, "tiles": [cfg.c1, cfg.c2], "layout": cfg.layout,
+                   "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)",
+                   "aggregate": "fast bf16" if args.fast_aggregate else "split bf16 / fp32"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "whole_call": whole,
+        "kernels_ms": {n: round(v, 5) for n, v in kern_ms.items()},
+        "call_ms_events": round(call_ms, 5),
+        "wall_ms_per_call": round(wall_ms, 5),
+        "parity_sampled_Y_rel_err": parity,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

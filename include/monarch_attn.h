@@ -1,0 +1,170 @@
+/*
+ * monarch_attn.h -- C ABI of the MonarchAttention forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation
+ * -------------
+ * MonarchAttention replaces softmax attention softmax(scale * Q K^T) V by a
+ * Monarch matrix M = P^T L P R (L, R block diagonal; in block form every
+ * block of M is rank one) fitted by alternating maximisation of the softmax
+ * variational objective f(M) = sum over rows of <M_row, S_row> + H(M_row),
+ * S = scale * Q K^T, for `steps` steps, without forming the N x N matrix;
+ * then Y = M V is applied as two batched block contractions, at
+ * Theta(N sqrt(N) d) compute and Theta(N d) IO.
+ *   Sources: "MonarchAttention: Zero-Shot Conversion to Fast, Hardware-Aware
+ *   Structured Attention" (abstract; scime atlas summary "Proposal" and
+ *   "Approach"; OpenReview reviews and author responses on the objective,
+ *   its concavity, the positivity constraints, T and the block sizes).
+ * The tiled variant splits every Monarch block into c1 x c2 independently
+ * rank-one sub-tiles, and the video layouts choose the block grid so that
+ * each of the f, h, w axes of a video latent lies in one factor.
+ *   Source: "MonarchRT: Efficient Attention for Real-Time Video Generation",
+ *   summary page, "Key claims" (section 4.1, Theorem 4.1) and "Method".
+ *
+ * Grid and factors (per (batch, head) slice).  Token n sits at grid position
+ * (l, i), l in [b1] (block), i in [b2] (position in block); for the flat
+ * layout n = l*b2 + i.  With t(l) = floor(l*c1/b1), s(j) = floor(j*c2/b2):
+ *     M[(l,i),(k,j)] = L[i,l,k,s(j)] * R[k,i,t(l),j]
+ * Rows of R sum to one over each segment s, rows of L over (k, s).
+ * Updates (exact block-wise maximisers of f):
+ *     R[k,i,t,j in s] = softmax_j( scale * qt[k,i,t,s] . k[k,j] )
+ *     L[i,l,k,s]      = softmax_(k,s)( scale * q[l,i] . c[k,i,t(l),s] + H_R[k,i,t(l),s] )
+ *     c = sum_j R k,  u = sum_j R v,  H_R = entropy of the R segment,
+ *     qt = sum_(l in t) L q / sum_(l in t) L     (steps 2..T),
+ *     y[l,i] = sum_(k,s) L[i,l,k,s] u[k,i,t(l),s].
+ * Initialisation: L0 = block identity, so qt[k,i,t(k),s] = q[k,i]; sub-rows
+ * with t != t(k) (zero weight) use the mean of q[l,i] over the rows l of
+ * tile t.
+ *
+ * Conventions
+ * -----------
+ * All tensor arguments are DEVICE pointers on the current HIP device.
+ * Q, K, V, Y: [batch, heads, seq_len, head_dim], contiguous, element type
+ * `dtype`; accumulation is always fp32.  The caller owns every buffer; the
+ * library never allocates, frees or synchronises (except the diagnostic
+ * helpers marked so), keeps no pointer after return and holds no mutable
+ * global state.  Work is enqueued asynchronously on `stream` (a hipStream_t;
+ * NULL = the default stream).  Calls on one stream are ordered; calls that
+ * share a workspace must not overlap.
+ *
+ * Errors: every argument check runs on the host before any HIP call and
+ * returns a status with nothing launched.  A launch failure returns
+ * MA_ERR_DEVICE.  No exceptions cross the ABI.  NaN/Inf in the inputs
+ * propagate to the outputs (not checked).
+ */
+#ifndef MONARCH_ATTN_H
+#define MONARCH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MA_OK = 0,
+  MA_ERR_INVALID_ARGUMENT = 1,   /* shapes inconsistent, null or misaligned pointer, aliasing */
+  MA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (head_dim, dtype, segment width) */
+  MA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MA_ERR_DEVICE = 4              /* a HIP call or kernel launch failed */
+} ma_status;
+
+typedef enum { MA_F32 = 0, MA_BF16 = 1 } ma_dtype;
+
+/* Token order -> (b1, b2) grid.  FLAT: n = l*b2 + i.  The video layouts take
+ * a row-major f x h x w latent; the name lists the axes of b1 then of b2, in
+ * major-to-minor order within each factor (MonarchRT summary page, "Key
+ * claims": the six aligned block-size choices). */
+typedef enum {
+  MA_LAYOUT_FLAT = 0,
+  MA_LAYOUT_FH_W = 1,   /* b1 = f*h, b2 = w */
+  MA_LAYOUT_W_FH = 2,   /* b1 = w,   b2 = f*h */
+  MA_LAYOUT_F_HW = 3,   /* b1 = f,   b2 = h*w */
+  MA_LAYOUT_HW_F = 4,   /* b1 = h*w, b2 = f */
+  MA_LAYOUT_FW_H = 5,   /* b1 = f*w, b2 = h */
+  MA_LAYOUT_H_FW = 6    /* b1 = h,   b2 = f*w */
+} ma_layout;
+
+/* Execution-path flags (ma_problem.flags). */
+#define MA_FLAG_FORCE_STAGED 1u   /* never take the fused single-launch T=1 path */
+/* bf16 only: carry the aggregate c = R K (and the next-step queries) in
+ * plain bf16 instead of split hi+lo bf16 / fp32.  Faster (fewer MFMAs, half
+ * the bytes for c) but loses about 1e-2 on L for sharply peaked rows; the
+ * default keeps about 16 significant bits on that path. */
+#define MA_FLAG_FAST_AGGREGATE 2u
+
+typedef struct {
+  int64_t batch, heads, seq_len, head_dim;  /* Q,K,V,Y: [batch, heads, seq_len, head_dim] */
+  int32_t b1, b2;      /* seq_len == b1*b2; b1 = number of blocks (the pages' m),
+                          b2 = block length (the pages' b) */
+  int32_t c1, c2;      /* sub-tiles per block; 1,1 = untiled Monarch; c1 | b1, c2 | b2 */
+  int32_t steps;       /* alternating-maximisation steps T >= 1 */
+  float scale;         /* multiplies Q.K^T; 0 means 1/sqrt(head_dim) */
+  int32_t dtype;       /* ma_dtype of Q, K, V, Y */
+  int32_t layout;      /* ma_layout */
+  int32_t f, h, w;     /* video latent (layout != FLAT): f*h*w == seq_len */
+  uint32_t flags;      /* MA_FLAG_* */
+} ma_problem;
+
+/* Optional exports (device pointers, each may be NULL), always fp32/fp64.
+ * L:   [batch, heads, b2, b1, b1*c2]    L[i][l][k*c2 + s] after the last step
+ * R:   [batch, heads, b1, b2, c1, b2]   R[k][i][t][j]     after the last step
+ * lse: [batch, heads, seq_len]          token order; logsumexp (natural log)
+ *      of the last L-update's scores for each query row
+ * objective: [batch*heads] fp64         f(L_T, R_T) = sum of lse over the slice */
+typedef struct {
+  float* L;
+  float* R;
+  float* lse;
+  double* objective;
+} ma_exports;
+
+/* Current limits: head_dim in {64, 128}; segment width b2/c2 <= 128 for
+ * head_dim 64 and <= 128 for head_dim 128; any b1. */
+
+/* Bytes of device workspace monarch_attn_forward needs for problem *p
+ * (256-byte aligned start required).  Pure host function. */
+ma_status monarch_attn_workspace_size(const ma_problem* p, size_t* bytes);
+
+/* Y = MonarchAttention(Q, K, V).  exports may be NULL.  workspace must be at
+ * least monarch_attn_workspace_size bytes, 256-byte aligned, and not overlap
+ * any other argument.  Y must not overlap Q, K or V.  Q, K, V, Y must be
+ * 16-byte aligned. */
+ma_status monarch_attn_forward(const ma_problem* p, const void* q, const void* k,
+                               const void* v, void* y, const ma_exports* exports,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of kernel launches monarch_attn_forward makes for *p (host only),
+ * or -1 for an invalid problem. */
+int32_t monarch_attn_num_launches(const ma_problem* p);
+
+/* Name of the j-th kernel launch for *p (static string) or NULL. */
+const char* monarch_attn_launch_name(const ma_problem* p, int32_t j);
+
+/* Diagnostic variant of monarch_attn_forward: additionally records
+ * events[0] on `stream` before the first launch and events[j+1] right after
+ * launch j, for j < n_events - 1 (events are hipEvent_t created by the
+ * caller, e.g. with monarch_attn_event_create).  Never synchronises. */
+ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const void* k,
+                                     const void* v, void* y, const ma_exports* exports,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events, int32_t n_events);
+
+/* Diagnostic helpers around hipEvent_t (thin wrappers of the HIP runtime).
+ * monarch_attn_event_elapsed_ms synchronises on event b. */
+ma_status monarch_attn_event_create(void** event);
+ma_status monarch_attn_event_destroy(void* event);
+ma_status monarch_attn_event_elapsed_ms(void* a, void* b, float* ms);
+
+/* Static description of a status code. */
+const char* monarch_attn_status_string(ma_status s);
+
+/* Library version, e.g. "0.1.0". */
+const char* monarch_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MONARCH_ATTN_H */

@@ -1,0 +1,161 @@
+"""MonarchAttention forward pass on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of include/monarch_attn.h.  It only
+marshals arguments: PyTorch supplies device memory and the current stream,
+and every step of the method runs in the HIP kernels of libmonarch_attn.so.
+There is no fallback: without the built library (or on a tensor that is not
+on a HIP device) the calls raise.
+
+    import structured_sub_quadratic_amd as ma
+    y = ma.forward(q, k, v, b1=128, b2=128)               # [B,H,N,d] on cuda
+    y, ex = ma.forward(q, k, v, 630, 52, layout="fh_w", fhw=(21, 30, 52),
+                       c1=2, c2=2, exports=("L", "R", "lse", "objective"))
+"""
+
+import ctypes
+
+from . import _lib
+from ._lib import MonarchAttnError, LAYOUTS, MA_FLAG_FORCE_STAGED, MA_FLAG_FAST_AGGREGATE
+
+__all__ = ["forward", "forward_timed", "make_problem", "workspace_size", "num_launches",
+           "launch_names", "Event", "MonarchAttnError", "LAYOUTS", "library_path",
+           "version"]
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def version():
+    return _lib.load().monarch_attn_version().decode()
+
+
+def _dtype_code(dtype):
+    import torch
+    if dtype == torch.float32:
+        return _lib.MA_F32
+    if dtype == torch.bfloat16:
+        return _lib.MA_BF16
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def make_problem(batch, heads, seq_len, head_dim, b1, b2, steps=1, c1=1, c2=1, scale=None,
+                 dtype="bf16", layout="flat", fhw=None, flags=0):
+    """Build the C problem descriptor.  dtype: "f32"/"bf16" or a torch dtype."""
+    if not isinstance(dtype, int):
+        dtype = {"f32": _lib.MA_F32, "bf16": _lib.MA_BF16}.get(dtype, None) \
+            if isinstance(dtype, str) else _dtype_code(dtype)
+        if dtype is None:
+            raise TypeError("dtype must be 'f32' or 'bf16'")
+    f, h, w = fhw if fhw is not None else (0, 0, 0)
+    return _lib.MAProblem(batch, heads, seq_len, head_dim, b1, b2, c1, c2, steps,
+                          0.0 if scale is None else float(scale), dtype, LAYOUTS[layout],
+                          f, h, w, flags)
+
+
+def workspace_size(problem):
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().monarch_attn_workspace_size(ctypes.byref(problem), ctypes.byref(n)),
+               "monarch_attn_workspace_size")
+    return n.value
+
+
+def num_launches(problem):
+    return _lib.load().monarch_attn_num_launches(ctypes.byref(problem))
+
+
+def launch_names(problem):
+    lib = _lib.load()
+    return [lib.monarch_attn_launch_name(ctypes.byref(problem), j).decode()
+            for j in range(num_launches(problem))]
+
+
+class Event:
+    """A hipEvent_t owned by the library's helper functions (diagnostics)."""
+
+    def __init__(self):
+        self.ptr = ctypes.c_void_p()
+        _lib.check(_lib.load().monarch_attn_event_create(ctypes.byref(self.ptr)),
+                   "monarch_attn_event_create")
+
+    def elapsed_ms(self, later):
+        ms = ctypes.c_float()
+        _lib.check(_lib.load().monarch_attn_event_elapsed_ms(self.ptr, later.ptr, ctypes.byref(ms)),
+                   "monarch_attn_event_elapsed_ms")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self.ptr:
+                _lib.load().monarch_attn_event_destroy(self.ptr)
+        except Exception:
+            pass
+
+
+def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, workspace, out,
+             force_staged, fast_aggregate):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a HIP device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [batch, heads, seq_len, head_dim] tensor")
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    B, H, N, D = q.shape
+    flags = (MA_FLAG_FORCE_STAGED if force_staged else 0) | \
+        (MA_FLAG_FAST_AGGREGATE if fast_aggregate else 0)
+    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags)
+    ws_bytes = workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    ex = {}
+    exports = tuple(exports or ())
+    if "L" in exports:
+        ex["L"] = torch.empty((B, H, b2, b1, b1 * c2), dtype=torch.float32, device=q.device)
+    if "R" in exports:
+        ex["R"] = torch.empty((B, H, b1, b2, c1, b2), dtype=torch.float32, device=q.device)
+    if "lse" in exports:
+        ex["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if "objective" in exports:
+        ex["objective"] = torch.empty((B * H,), dtype=torch.float64, device=q.device)
+    cex = _lib.MAExports(*(ex[n].data_ptr() if n in ex else None
+                           for n in ("L", "R", "lse", "objective")))
+    return prob, workspace, out, ex, cex
+
+
+def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
+            exports=(), workspace=None, out=None, force_staged=False, fast_aggregate=False):
+    """MonarchAttention forward on the current stream.  Returns Y, or (Y, dict
+    of exports) when exports (a subset of "L", "R", "lse", "objective") is
+    non-empty.  Shapes of the exports are documented in monarch_attn.h.
+    fast_aggregate: bf16 only, plain bf16 on the c = R K path (see
+    MA_FLAG_FAST_AGGREGATE)."""
+    import torch
+    prob, workspace, out, ex, cex = _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw,
+                                             exports, workspace, out, force_staged,
+                                             fast_aggregate)
+    st = torch.cuda.current_stream(q.device).cuda_stream
+    status = _lib.load().monarch_attn_forward(
+        ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        ctypes.byref(cex), workspace.data_ptr(), workspace.numel(), st)
+    _lib.check(status, "monarch_attn_forward")
+    return (out, ex) if exports else out
+
+
+def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layout="flat",
+                  fhw=None, workspace=None, out=None, force_staged=False, fast_aggregate=False):
+    """forward() that also records events[0] before the first kernel launch and
+    events[j+1] after launch j (Event objects) on the current stream."""
+    import torch
+    prob, workspace, out, ex, cex = _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw,
+                                             (), workspace, out, force_staged, fast_aggregate)
+    st = torch.cuda.current_stream(q.device).cuda_stream
+    arr = (ctypes.c_void_p * len(events))(*[e.ptr.value for e in events])
+    status = _lib.load().monarch_attn_forward_timed(
+        ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        ctypes.byref(cex), workspace.data_ptr(), workspace.numel(), st, arr, len(events))
+    _lib.check(status, "monarch_attn_forward_timed")
+    return out

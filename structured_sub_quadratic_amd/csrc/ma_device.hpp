@@ -1,0 +1,121 @@
+// Device-side building blocks for the MonarchAttention kernels (gfx950).
+//
+// Everything here is written for CDNA4 wave64: one 16x16 MFMA tile per wave
+// instruction, fp32 accumulation, and the accumulator layout in which lane l
+// holds rows 4*(l/16)+r (r = 0..3) of column l%16.  The kernels compute every
+// score tile transposed (keys on the MFMA M dimension, queries on N), so a
+// lane owns one query and the four lanes l, l^16, l^32, l^48 share it: row
+// reductions over keys are register-local plus two cross-lane steps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ma {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr int WAVES = 4;              // waves per workgroup
+constexpr int THREADS = WAVE * WAVES;
+constexpr int KT = 64;                // keys per streamed tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// MFMA traits: KPL = k-values each lane supplies per instruction (the lane
+// group g = lane/16 supplies the g-th run of KPL consecutive k of a step of
+// 4*KPL).  Only the consistency of this mapping between the A and B operands
+// matters for the result, and both operands are built with it.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KPL = 8;
+  typedef bf16x8 frag;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  typedef float frag;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 16-byte vector of T: 8 bf16 or 4 floats.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
+
+__device__ inline float wave_max_x16x32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ inline float wave_sum_x16x32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Store 4 consecutive values (one accumulator column run) to global memory.
+__device__ inline void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ inline void store4(bf16* p, f32x4 v) {
+  bf16x4 b;
+  b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+
+// ---------------------------------------------------------------------------
+// Token order <-> grid position (l, i): the flat reshape and the six aligned
+// video layouts of an f x h x w latent (row-major tokens).
+// ---------------------------------------------------------------------------
+struct GridMap {
+  int kind;          // ma_layout
+  int b1, b2;
+  int h, w, hw;
+
+  __device__ inline int64_t token(int l, int i) const {
+    switch (kind) {
+      case 2:  // (w, fh): l = w, i = f*h + h
+      case 4:  // (hw, f): l = h*w + w, i = f
+        return (int64_t)i * b1 + l;
+      case 5: {  // (fw, h): l = f*w + w_, i = h_
+        int fi = l / w, wi = l - fi * w;
+        return (int64_t)fi * hw + (int64_t)i * w + wi;
+      }
+      case 6: {  // (h, fw): l = h_, i = f*w + w_
+        int fi = i / w, wi = i - fi * w;
+        return (int64_t)fi * hw + (int64_t)l * w + wi;
+      }
+      default:  // flat, (fh, w), (f, hw): row-major reshape
+        return (int64_t)l * b2 + i;
+    }
+  }
+};
+
+// Map a linear workgroup id so that consecutive logical ids run on the same
+// XCD (the dispatcher deals workgroups to the 8 XCDs round-robin), which lets
+// neighbours that read the same tiles share one L2.  Exact bijection on
+// [0, n) for any n.
+__device__ inline uint32_t xcd_swizzle(uint32_t id, uint32_t n) {
+  constexpr uint32_t X = 8;
+  uint32_t q = n / X, r = n % X;
+  uint32_t xcd = id % X, pos = id / X;
+  // XCDs below r own q+1 workgroups, the others q
+  uint32_t base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  return base + pos;
+}
+
+}  // namespace ma

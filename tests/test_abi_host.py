@@ -1,0 +1,110 @@
+"""CPU tests of the C ABI: the built library loads without a GPU, exports every
+symbol include/monarch_attn.h declares, and rejects bad arguments on the host
+before any HIP call (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import structured_sub_quadratic_amd as ma
+from structured_sub_quadratic_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "monarch_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(monarch_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    names = declared_functions()
+    for must in ("monarch_attn_forward", "monarch_attn_workspace_size",
+                 "monarch_attn_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_problem_struct_layout_matches_header():
+    # int64 x4, int32 x5, float, int32 x5, uint32 -> 32 + 20 + 4 + 20 + 4 = 80
+    assert ctypes.sizeof(_lib.MAProblem) == 80
+    assert ctypes.sizeof(_lib.MAExports) == 32
+
+
+def status(p, n_ws=1 << 30, q=256, k=512, v=768, y=1024 * 1024 * 1024, ws=1 << 40):
+    lib = _lib.load()
+    return lib.monarch_attn_forward(ctypes.byref(p), q, k, v, y, None, ws, n_ws, None)
+
+
+def good(**kw):
+    args = dict(batch=1, heads=2, seq_len=256, head_dim=64, b1=16, b2=16, steps=1)
+    args.update(kw)
+    return ma.make_problem(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b1=16, b2=8), 1),                   # N != b1*b2
+    (dict(c1=3), 1),                          # c1 does not divide b1
+    (dict(c2=5), 1),
+    (dict(steps=0), 1),
+    (dict(head_dim=96), 2),                   # unsupported d
+    (dict(seq_len=512, b1=2, b2=256), 2),     # segment wider than supported
+    (dict(layout="fh_w", fhw=(2, 4, 32)), 0),  # fh=8 != b1: checked below separately
+    (dict(scale=-1.0), 1),
+])
+def test_validation_codes(lib, kw, code):
+    p = good(**kw)
+    if kw.get("layout") == "fh_w":
+        assert status(p) == 1             # (f*h, w) = (8, 32) does not match (16, 16)
+        p = good(layout="fh_w", fhw=(4, 4, 16))
+        assert ma.workspace_size(p) > 0   # (16, 16): valid
+        return
+    assert status(p) == code
+    n = ctypes.c_size_t()
+    assert lib.monarch_attn_workspace_size(ctypes.byref(p), ctypes.byref(n)) == code
+
+
+def test_pointer_checks(lib):
+    p = good()
+    assert status(p, q=0) == 1                       # null
+    assert status(p, q=258) == 1                     # misaligned
+    assert status(p, y=600) == 1                     # y overlaps k
+    assert status(p, n_ws=10) == 3                   # workspace too small
+    assert status(p, ws=(1 << 40) + 8) == 1          # misaligned workspace
+    assert status(p, ws=512) == 1                    # workspace overlaps inputs
+    assert lib.monarch_attn_forward(None, 0, 0, 0, 0, None, 0, 0, None) == 1
+
+
+def test_workspace_size_and_launch_plan(lib):
+    p = ma.make_problem(1, 12, 16384, 64, 128, 128)
+    ws = ma.workspace_size(p)
+    # c, u (bf16) + entropy + two normaliser buffers
+    assert ws >= 12 * 16384 * (2 * 64 * 2 + 3 * 4)
+    assert ma.launch_names(p) == ["stage1_last", "stage2_last"]
+    p = ma.make_problem(8, 12, 4096, 64, 64, 64, steps=3)
+    assert ma.launch_names(p) == ["qbar", "stage1", "stage2_stats", "alpha", "stage1",
+                                  "stage2_stats", "alpha", "stage1_last", "stage2_last"]
+    p = ma.make_problem(1, 12, 32760, 128, 630, 52, c1=2, c2=2, layout="fh_w", fhw=(21, 30, 52))
+    assert ma.launch_names(p) == ["qbar", "stage1_last", "stage2_last"]
+    assert lib.monarch_attn_num_launches(ctypes.byref(good(b2=8))) == -1
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.monarch_attn_status_string(s)
+    assert ma.version()

@@ -1,0 +1,212 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases are compared element by element on Y, L, R, the row
+log-normalisers and the objective; the five benchmark workloads run at their
+full sizes in the launch configuration the benchmark times, and are compared
+on every output of sampled slices and columns (each column i of a slice is an
+independent sub-problem the oracle can compute on its own: R rows [., i, .],
+L[i] and y[., i] depend only on column i of the queries and on all keys)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import CONFIGS, WorkloadConfig, make_inputs
+from parity_utils import TOL, rel_err, oracle_L_as_gpu, oracle_R_as_gpu, run_hip
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import structured_sub_quadratic_amd as ma
+    ma._lib.load()          # raise loudly if the library is missing
+
+
+def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective"),
+               noise=None, tol=None, **kw):
+    all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    slices = all_slices if slices is None else slices
+    Q, K, V = make_inputs(cfg, noise_scale=noise)
+    y, ex = run_hip(cfg, Q, K, V, exports=exports, **kw)
+    ref = oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
+                         layout=cfg.layout, fhw=cfg.fhw, cols=cols, slices=slices)
+    tiled = cfg.c1 * cfg.c2 > 1
+    tol = TOL[cfg.dtype] if tol is None else tol
+    errs = {}
+    tok = ref["grid"][:, ref["cols"]].reshape(-1)
+    errs["Y"] = rel_err(y[:, :, tok], ref["y"][:, :, tok], slices)
+    if "L" in ex:
+        errs["L"] = rel_err(ex["L"][:, :, ref["cols"]], oracle_L_as_gpu(ref["L"], tiled), slices)
+    if "R" in ex:
+        errs["R"] = rel_err(ex["R"][:, :, :, ref["cols"]], oracle_R_as_gpu(ref["R"], tiled), slices)
+    if "lse" in ex:
+        errs["lse"] = rel_err(ex["lse"][:, :, tok], ref["lse"][:, :, tok], slices)
+    if "objective" in ex and cols is None:
+        obj = ex["objective"].reshape(cfg.batch, cfg.heads)
+        ft = ref["f_trace"][:, :, -1]
+        errs["objective"] = max(abs(obj[b, h] - ft[b, h]) / abs(ft[b, h]) for b, h in slices)
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{cfg.name}: {errs} (tol {tol})"
+    return y, ex, ref
+
+
+# ----------------------------------------------------------------- small
+
+def test_config1_full():
+    check_case(CONFIGS[1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("steps", [1, 2])
+def test_ragged_tiles_untiled(dtype, d, steps):
+    """b1 = 70 (stage 2 streams 64 + 6 keys), b2 = 52 (stage 1 ragged)."""
+    cfg = WorkloadConfig(0, f"ragged {dtype} d{d} T{steps}", batch=1, heads=2, seq_len=70 * 52,
+                         head_dim=d, b1=70, b2=52, steps=steps, dtype=dtype, data="iid", seed=11)
+    check_case(cfg)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("tiles", [(2, 2), (2, 1), (1, 4), (5, 2)])
+@pytest.mark.parametrize("steps", [1, 3])
+def test_tiled(dtype, tiles, steps):
+    cfg = WorkloadConfig(0, f"tiled {tiles} {dtype} T{steps}", batch=2, heads=1, seq_len=70 * 52,
+                         head_dim=64, b1=70, b2=52, steps=steps, dtype=dtype, data="normed",
+                         seed=12, c1=tiles[0], c2=tiles[1])
+    check_case(cfg)
+
+
+def test_multi_step_bf16_lowrank():
+    cfg = WorkloadConfig(0, "lowrank T3", batch=2, heads=2, seq_len=96 * 40, head_dim=64,
+                         b1=96, b2=40, steps=3, dtype="bf16", data="lowrank", seed=13)
+    check_case(cfg)
+
+
+@pytest.mark.parametrize("layout", ["fh_w", "w_fh", "f_hw", "hw_f", "fw_h", "h_fw"])
+@pytest.mark.parametrize("steps", [1, 2])
+def test_video_layouts(layout, steps):
+    fhw = (3, 5, 8)
+    sz = dict(f=3, h=5, w=8)
+    a, b = layout.split("_")
+    b1 = int(np.prod([sz[c] for c in a]))
+    b2 = int(np.prod([sz[c] for c in b]))
+    c1 = 3 if b1 % 3 == 0 else 1
+    c2 = 2 if b2 % 2 == 0 else 1
+    for tiles in ((1, 1), (c1, c2)):
+        cfg = WorkloadConfig(0, f"video {layout} T{steps} tiles {tiles}", batch=1, heads=2,
+                             seq_len=120, head_dim=128, b1=b1, b2=b2, steps=steps, dtype="bf16",
+                             data="video", seed=14, layout=layout, fhw=fhw,
+                             c1=tiles[0], c2=tiles[1])
+        check_case(cfg)
+
+
+def test_video_layouts_exact_without_noise_fp32():
+    """Zero-noise per-axis codes: one step reproduces exact softmax attention
+    in every aligned layout, on the GPU as in the oracle."""
+    fhw = (3, 4, 10)
+    sz = dict(f=3, h=4, w=10)
+    base = WorkloadConfig(0, "video exact", batch=1, heads=1, seq_len=120, head_dim=64,
+                          b1=12, b2=10, steps=1, dtype="f32", data="video", seed=15,
+                          layout="fh_w", fhw=fhw)
+    Q, K, V = make_inputs(base, noise_scale=0.0)
+    exact = oracle.exact_attention(Q[0, 0].astype(np.float64), K[0, 0].astype(np.float64),
+                                   V[0, 0].astype(np.float64), 1 / 8)
+    for layout in ("fh_w", "w_fh", "f_hw", "hw_f", "fw_h", "h_fw"):
+        a, b = layout.split("_")
+        b1 = int(np.prod([sz[c] for c in a]))
+        cfg = WorkloadConfig(0, layout, batch=1, heads=1, seq_len=120, head_dim=64, b1=b1,
+                             b2=120 // b1, steps=1, dtype="f32", data="video", seed=15,
+                             layout=layout, fhw=fhw)
+        y, _ = run_hip(cfg, Q, K, V, exports=())
+        err = np.abs(y[0, 0] - exact).max() / np.abs(exact).max()
+        assert err < 1e-4, (layout, err)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_limits(dtype):
+    """b1 = 1 (one block of N keys) and b2 = 1 (N blocks of one key) are
+    exact softmax attention."""
+    for b1, b2 in ((1, 128), (300, 1)):
+        cfg = WorkloadConfig(0, f"dense {b1}x{b2}", batch=1, heads=2, seq_len=b1 * b2,
+                             head_dim=64, b1=b1, b2=b2, steps=2, dtype=dtype, data="iid", seed=16)
+        Q, K, V = make_inputs(cfg)
+        y, _ = run_hip(cfg, Q, K, V, exports=())
+        for h in range(2):
+            ex = oracle.exact_attention(*(X[0, h].astype(np.float64) for X in (Q, K, V)), 1 / 8)
+            err = np.abs(y[0, h] - ex).max() / np.abs(ex).max()
+            assert err < TOL[dtype], (b1, b2, h, err)
+
+
+def test_single_token_and_tiny_grids():
+    for (b1, b2) in ((1, 1), (2, 1), (1, 2), (3, 3)):
+        cfg = WorkloadConfig(0, f"tiny {b1}x{b2}", batch=2, heads=3, seq_len=b1 * b2,
+                             head_dim=64, b1=b1, b2=b2, steps=2, dtype="f32", data="iid", seed=17)
+        check_case(cfg)
+
+
+def test_determinism_and_reuse_of_workspace():
+    import torch
+    import structured_sub_quadratic_amd as ma
+    cfg = WorkloadConfig(0, "det", batch=1, heads=3, seq_len=70 * 52, head_dim=128, b1=70,
+                         b2=52, steps=2, dtype="bf16", data="normed", seed=18, c1=2, c2=2)
+    Q, K, V = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (Q, K, V))
+    prob = ma.make_problem(1, 3, cfg.seq_len, 128, 70, 52, 2, 2, 2, dtype="bf16")
+    ws = torch.empty(ma.workspace_size(prob), dtype=torch.uint8, device=dev)
+    y1 = ma.forward(tq, tk, tv, 70, 52, 2, 2, 2, workspace=ws).clone()
+    ws.fill_(0xFF)          # garbage (NaN patterns) left in the workspace must not matter
+    y2 = ma.forward(tq, tk, tv, 70, 52, 2, 2, 2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+# ------------------------------------------------ benchmark workloads, sampled
+
+def test_config2_sampled():
+    cfg = CONFIGS[2]
+    check_case(cfg, slices=[(0, 0), (3, 7), (7, 11)], exports=("L", "R", "lse"))
+
+
+def test_config3_sampled():
+    cfg = CONFIGS[3]
+    check_case(cfg, slices=[(0, 0), (0, 11)], cols=[0, 1, 63, 64, 127],
+               exports=("L", "R", "lse"))
+
+
+@pytest.mark.parametrize("index", [3, 4, 5])
+def test_fast_aggregate_t1_workloads(index):
+    """The plain-bf16 aggregate path (MA_FLAG_FAST_AGGREGATE) on the T=1
+    workloads it is meant for."""
+    cfg = CONFIGS[index]
+    check_case(cfg, slices=[(0, 0), (0, 5)], cols=[0, 17, cfg.b2 - 1], exports=("L", "R", "lse"),
+               fast_aggregate=True)
+
+
+def test_config4_sampled():
+    cfg = CONFIGS[4]
+    check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 25, 51], exports=("L", "R", "lse"))
+
+
+def test_config5_sampled_and_c1_equality():
+    cfg = CONFIGS[5]
+    check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 26, 51], exports=("L", "R", "lse"))
+    # c1 = c2 = 1 on the same data: equal to the untiled oracle and to the
+    # tiled oracle with c = 1
+    c4 = CONFIGS[4]
+    Q, K, V = make_inputs(c4)
+    y, _ = run_hip(c4, Q, K, V, exports=())
+    cols = [3, 30]
+    for tiled in (False, True):
+        ref = oracle.forward(Q, K, V, 630, 52, 1, 1, 1, layout="fh_w", fhw=(21, 30, 52),
+                             cols=cols, slices=[(0, 2)], tiled=tiled)
+        tok = ref["grid"][:, cols].reshape(-1)
+        err = rel_err(y[:, :, tok], ref["y"][:, :, tok], [(0, 2)])
+        assert err < TOL["bf16"], (tiled, err)
