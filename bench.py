@@ -1,12 +1,14 @@
 """MonarchAttention forward benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--warm] [--fast-aggregate]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload n16k] [--warm]
+                    [--fast-aggregate] [--fused]
 
 A step is one monarch_attn_forward call (the whole hot path: layout gather,
 stage 1, stage 2, step loop, output scatter) over one batch of seeded
 synthetic input already resident in HBM.  The default workload is
 N=16384 as a 128x128 grid, d=64, 12 heads, T=1, bf16 (the configuration the
-headline metric names); --config picks another of the five workloads.
+headline metric names); --workload picks another of the five workloads
+(n256, n4k_t3, n16k, video, video_tiled).
 
 Timing: W untimed warm-up calls, then exactly K calls bracketed by
 torch.cuda.synchronize().  Each call records HIP events before its first
@@ -64,6 +66,10 @@ def kernel_bytes(cfg, name, precise):
         b = N * d * e + rows * d * xc + rows * 4 + N * 4
     elif name == "alpha":
         b = N * d * e + rows * d * xc + rows * 4 + N * 4 + rows * d * 4
+    elif name == "fused_t1":
+        # the whole T = 1 pass in one launch: Q, K, V in and Y out; the exchange
+        # (c, u, entropy, normalisers) is meant to stay in L2 / MALL
+        b = 4 * N * d * e
     elif name == "qbar":
         b = N * d * e + cfg.c1 * cfg.b2 * d * 4
     else:
@@ -114,9 +120,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", default="n16k",
+                    choices=["n256", "n4k_t3", "n16k", "video", "video_tiled"])
     ap.add_argument("--warm", action="store_true", help="reuse one input set (MALL-resident)")
     ap.add_argument("--fast-aggregate", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="T = 1 as one cooperative launch instead of separate stage launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy 3 times (reference for the "
@@ -132,9 +141,9 @@ def main():
     import torch
     import structured_sub_quadratic_amd as ma
     from structured_sub_quadratic_amd import _lib
-    from workloads import get_config, make_inputs
+    from workloads import get_workload, make_inputs
 
-    cfg = get_config(args.config)
+    cfg = get_workload(args.workload)
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         src = torch.empty(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -153,6 +162,8 @@ def main():
     del base
 
     flags = ma.MA_FLAG_FAST_AGGREGATE if args.fast_aggregate else 0
+    if args.fused:
+        flags |= ma.MA_FLAG_FORCE_FUSED
     prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2,
                            cfg.steps, cfg.c1, cfg.c2, None, cfg.dtype, cfg.layout, cfg.fhw, flags)
     names = ma.launch_names(prob)
@@ -210,7 +221,7 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as fh:
             tr = json.load(fh)
-        key = f"config{cfg.index}{'_fast' if args.fast_aggregate else ''}:{dom}"
+        key = f"{cfg.key}{'_fast' if args.fast_aggregate else ''}:{dom}"
         ent = tr.get(key)
         if ent and ent.get("source_hash") == source_hash():
             traffic = ent["hbm_bytes_per_launch"]
@@ -234,7 +245,8 @@ def main():
                    "seq_len": cfg.seq_len, "head_dim": cfg.head_dim, "b1": cfg.b1, "b2": cfg.b2,
                    "T": cfg.steps, "tiles": [cfg.c1, cfg.c2], "layout": cfg.layout,
                    "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)",
-                   "aggregate": "fast bf16" if args.fast_aggregate else "split bf16 / fp32"},
+                   "aggregate": "fast bf16" if args.fast_aggregate else "split bf16 / fp32",
+                   "launches": names},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "whole_call": whole,

@@ -87,7 +87,11 @@ typedef enum {
 } ma_layout;
 
 /* Execution-path flags (ma_problem.flags). */
-#define MA_FLAG_FORCE_STAGED 1u   /* never take the fused single-launch T=1 path */
+/* T = 1 runs either as separate stage launches or as one cooperative launch
+ * (grid-wide barriers between the phases).  The library picks the staged
+ * sequence unless MA_FLAG_FORCE_FUSED is set; FORCE_STAGED wins over it. */
+#define MA_FLAG_FORCE_STAGED 1u
+#define MA_FLAG_FORCE_FUSED 4u
 /* bf16 only: carry the aggregate c = R K (and the next-step queries) in
  * plain bf16 instead of split hi+lo bf16 / fp32.  Faster (fewer MFMAs, half
  * the bytes for c) but loses about 1e-2 on L for sharply peaked rows; the
@@ -120,8 +124,9 @@ typedef struct {
   double* objective;
 } ma_exports;
 
-/* Current limits: head_dim in {64, 128}; segment width b2/c2 <= 128 for
- * head_dim 64 and <= 128 for head_dim 128; any b1. */
+/* Current limits: head_dim in {64, 128}; segment width b2/c2 <= 128, except
+ * <= 64 for fp32 with head_dim 128; any b1.  Other shapes return
+ * MA_ERR_UNSUPPORTED. */
 
 /* Bytes of device workspace monarch_attn_forward needs for problem *p
  * (256-byte aligned start required).  Pure host function. */

@@ -54,7 +54,7 @@ the objective by maximising it over one factor with the other fixed:
 
   Output: y[l,i] = sum_k L[i,l,k] u[k,i], u[k,i] = sum_j R[k,i,j] v[k,j].
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * initialisation L0 = block identity, so qt[k,i] = q[k,i] for the first
     R-update; a step is one R-update then one L-update; the first point of
     the objective trace is f(L0, R1);

@@ -4,7 +4,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmonarch_attn.so")
+# MONARCH_ATTN_LIB may name another build of the same library (tuning sweeps)
+LIB_PATH = os.environ.get("MONARCH_ATTN_LIB") or os.path.join(PKG, "libmonarch_attn.so")
 
 MA_OK = 0
 STATUS_NAMES = {0: "MA_OK", 1: "MA_ERR_INVALID_ARGUMENT", 2: "MA_ERR_UNSUPPORTED",
@@ -13,6 +14,7 @@ MA_F32, MA_BF16 = 0, 1
 LAYOUTS = {"flat": 0, "fh_w": 1, "w_fh": 2, "f_hw": 3, "hw_f": 4, "fw_h": 5, "h_fw": 6}
 MA_FLAG_FORCE_STAGED = 1
 MA_FLAG_FAST_AGGREGATE = 2
+MA_FLAG_FORCE_FUSED = 4
 
 
 class MAProblem(ctypes.Structure):

@@ -1,0 +1,245 @@
+// Launch sequence of one element type and head dimension, included by the
+// per-type translation units (ma_inst_*.hip).
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+
+#include "ma_plan.hpp"
+#include "ma_aux_kernels.hpp"
+#include "ma_stage_kernels.hpp"
+#include "ma_fused.hpp"
+
+namespace ma {
+
+inline unsigned grid1(size_t n) { return (unsigned)n; }
+
+#ifndef MA_NO_PERSISTENT
+#define MA_NO_PERSISTENT 0
+#endif
+
+// Workgroups of a persistent launch: two per compute unit of the current
+// device (the persistent kernels are built for two resident workgroups).
+inline size_t persistent_slots() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  return (size_t)2 * cus;
+}
+
+template <typename T> constexpr bool is_f32() { return std::is_same<T, float>::value; }
+
+// Query sub-tiles of 16 per wave: the choice (1 or 2) that pads the fewest
+// query rows per workgroup group, preferring 2 (more MFMAs per LDS operand).
+inline int pick_nq(int rows) {
+  const int pad1 = (rows + 63) / 64 * 64 - rows, pad2 = (rows + 127) / 128 * 128 - rows;
+  return pad2 <= pad1 ? 2 : 1;
+}
+// Build-time overrides for tuning sweeps (0 = automatic choice).
+#ifndef MA_S1_NQ
+#define MA_S1_NQ 0
+#endif
+#ifndef MA_S2_NQ
+#define MA_S2_NQ 0
+#endif
+template <typename T, int D> int stage1_nq(int slots) {
+  if (D == 128 || is_f32<T>()) return 1;
+  return MA_S1_NQ ? MA_S1_NQ : pick_nq(slots);
+}
+template <typename T, int D> int stage2_nq(int rows) {
+  if (is_f32<T>() && D == 128) return 1;     // two sub-tiles would spill
+  return MA_S2_NQ ? MA_S2_NQ : pick_nq(rows);
+}
+
+// Cooperative launch of a fused kernel: as many workgroups as can be resident
+// at once (the grid-wide barriers need them all), at most one per item.
+template <class K>
+hipError_t launch_cooperative(K kernel, size_t items, void** args, hipStream_t st) {
+  int per_cu = 0, dev = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, THREADS, 0);
+  if (e != hipSuccess) return e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+  const size_t g = std::max<size_t>(1, std::min<size_t>(items, (size_t)per_cu * cus));
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(grid1(g)), dim3(THREADS),
+                                    args, 0, st);
+}
+
+template <typename T, int D, bool PRECISE>
+hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, hipStream_t st) {
+  char* ws = b.ws;
+  void* cx = ws + pl.off_cx;
+  void* ux = ws + pl.off_ux;
+  float* h2 = reinterpret_cast<float*>(ws + pl.off_h2);
+  float* lser = reinterpret_cast<float*>(ws + pl.off_lser);
+  float* lse2 = reinterpret_cast<float*>(ws + pl.off_lse2);
+  float* qtil = pl.need_qtil ? reinterpret_cast<float*>(ws + pl.off_qtil) : nullptr;
+  float* qbar = pl.need_qbar ? reinterpret_cast<float*>(ws + pl.off_qbar) : nullptr;
+  const int S = (int)pl.S, N = (int)pl.N;
+  switch (kind) {
+    case L_FUSED: {
+      QbarParams pq{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt};
+      const int nqs = pl.c1 * pl.b2;
+      const int nq1 = stage1_nq<T, D>(nqs), qg1 = WAVES * nq1 * 16;
+      Stage1Params p1{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
+                      S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg1 - 1) / qg1,
+                      pl.sc2, 1};
+      const int nq2 = stage2_nq<T, D>(pl.rt), qg2 = WAVES * nq2 * 16;
+      Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
+                      S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg2 - 1) / qg2,
+                      pl.sc2};
+      const size_t items = std::max<size_t>(std::max<size_t>((size_t)S * pl.c1 * pl.b2,
+                                                             (size_t)S * pl.b1 * p1.nqg),
+                                            (size_t)S * pl.b2 * pl.c1 * p2.nqg);
+      void* args[] = {&pq, &p1, &p2};
+      const bool ktb64 = pl.b2 <= 64 || (is_f32<T>() && D == 128);
+      const bool qsplit = PRECISE && is_bf16<T>() && pl.c1 > 1;
+      hipError_t e = hipSuccess;
+#define MA_F3(NQ1, KTB, NQ2, QS) e = launch_cooperative(fused_t1_kernel<T, D, NQ1, KTB, NQ2, PRECISE, QS>, items, args, st)
+#define MA_F2(NQ1, KTB, NQ2) do { if (qsplit) MA_F3(NQ1, KTB, NQ2, true); else MA_F3(NQ1, KTB, NQ2, false); } while (0)
+#define MA_F1(NQ1, KTB) do { if (nq2 == 1) MA_F2(NQ1, KTB, 1); else MA_F2(NQ1, KTB, 2); } while (0)
+      if constexpr (D == 128) {
+        if (ktb64) MA_F1(1, 64);
+        else if constexpr (!is_f32<T>()) MA_F1(1, 128);
+      } else {
+        if (nq1 == 1 || is_f32<T>()) {
+          if (ktb64) MA_F1(1, 64); else MA_F1(1, 128);
+        } else if constexpr (!is_f32<T>()) {
+          if (ktb64) MA_F1(2, 64); else MA_F1(2, 128);
+        }
+      }
+#undef MA_F1
+#undef MA_F2
+#undef MA_F3
+      if (e != hipSuccess) return e;
+      break;
+    }
+    case L_QBAR: {
+      QbarParams p{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt};
+      hipLaunchKernelGGL((qbar_kernel<T, D>), dim3(grid1((size_t)S * pl.c1 * pl.b2)), dim3(256), 0, st, p);
+      break;
+    }
+    case L_STAGE1:
+    case L_STAGE1_LAST: {
+      const int nqs = pl.c1 * pl.b2;
+      const int nq = stage1_nq<T, D>(nqs);
+      const int qg = WAVES * nq * 16;
+      Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
+                     S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
+                     pl.sc2, step == 0 ? 1 : 0};
+      const size_t items1 = (size_t)S * pl.b1 * p.nqg;
+      const dim3 grid(grid1(items1));
+      const bool ktb64 = pl.b2 <= 64 || (is_f32<T>() && D == 128);
+      const bool last = kind == L_STAGE1_LAST;
+      // queries from fp32 rows (next-step queries, tile means) need the split
+      const bool qsplit = PRECISE && is_bf16<T>() && (step > 0 || pl.c1 > 1);
+      // persistent pipelined kernel when the whole block fits one LDS tile
+      const bool persistent = pl.b2 <= (ktb64 ? 64 : 128) && !MA_NO_PERSISTENT;
+      const dim3 pgrid(grid1(std::min<size_t>(items1, persistent_slots())));
+#define MA_S1_K(NQ, KTB, U, QS)                                                                   \
+  do {                                                                                            \
+    if (persistent)                                                                               \
+      hipLaunchKernelGGL((stage1_persistent_kernel<T, D, NQ, KTB, U, PRECISE, QS>), pgrid, dim3(THREADS), 0, st, p); \
+    else                                                                                          \
+      hipLaunchKernelGGL((stage1_kernel<T, D, NQ, KTB, U, PRECISE, QS>), grid, dim3(THREADS), 0, st, p); \
+  } while (0)
+#define MA_S1(NQ, KTB, U)                                                                         \
+  do {                                                                                            \
+    if (qsplit) MA_S1_K(NQ, KTB, U, true); else MA_S1_K(NQ, KTB, U, false);                      \
+  } while (0)
+      if constexpr (D == 128) {
+        if (ktb64) {
+          if (last) MA_S1(1, 64, true); else MA_S1(1, 64, false);
+        } else if constexpr (!is_f32<T>()) {
+          if (last) MA_S1(1, 128, true); else MA_S1(1, 128, false);
+        }
+      } else {
+        if (nq == 1 || is_f32<T>()) {
+          if (ktb64) { if (last) MA_S1(1, 64, true); else MA_S1(1, 64, false); }
+          else { if (last) MA_S1(1, 128, true); else MA_S1(1, 128, false); }
+        } else if constexpr (!is_f32<T>()) {
+          if (ktb64) { if (last) MA_S1(2, 64, true); else MA_S1(2, 64, false); }
+          else { if (last) MA_S1(2, 128, true); else MA_S1(2, 128, false); }
+        }
+      }
+#undef MA_S1_K
+#undef MA_S1
+      break;
+    }
+    case L_STAGE2_STATS:
+    case L_STAGE2_LAST: {
+      const int nq = stage2_nq<T, D>(pl.rt);
+      const int qg = WAVES * nq * 16;
+      Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
+                     S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
+                     pl.sc2};
+      const size_t items2 = (size_t)S * pl.b2 * pl.c1 * p.nqg;
+      const dim3 grid(grid1(items2));
+      const bool last = kind == L_STAGE2_LAST;
+      const int nkeys = pl.b1 * pl.c2;
+      const int ktb = nkeys <= 64 ? 64 : 128;
+      const bool persistent = nkeys <= ((is_f32<T>() && D == 128) ? 64 : 128) && !MA_NO_PERSISTENT;
+      const dim3 pgrid(grid1(std::min<size_t>(items2, persistent_slots())));
+#define MA_S2_P(NQ, PV)                                                                           \
+  do {                                                                                            \
+    if (ktb == 64)                                                                                \
+      hipLaunchKernelGGL((stage2_persistent_kernel<T, D, NQ, 64, PV, PRECISE>), pgrid, dim3(THREADS), 0, st, p); \
+    else if constexpr (!(is_f32<T>() && D == 128))                                                \
+      hipLaunchKernelGGL((stage2_persistent_kernel<T, D, NQ, 128, PV, PRECISE>), pgrid, dim3(THREADS), 0, st, p); \
+  } while (0)
+#define MA_S2(NQ, PV)                                                                             \
+  do {                                                                                            \
+    if (persistent) MA_S2_P(NQ, PV);                                                              \
+    else hipLaunchKernelGGL((stage2_kernel<T, D, NQ, PV, PRECISE>), grid, dim3(THREADS), 0, st, p); \
+  } while (0)
+      if (nq == 1) { if (last) MA_S2(1, true); else MA_S2(1, false); }
+      else { if (last) MA_S2(2, true); else MA_S2(2, false); }
+#undef MA_S2_P
+#undef MA_S2
+      break;
+    }
+    case L_ALPHA:
+    case L_EXPORT_L: {
+      const int nkeys = pl.b1 * pl.c2;
+      AlphaParams p{b.q, cx, h2, lse2, qbar, kind == L_ALPHA ? qtil : nullptr,
+                    kind == L_EXPORT_L ? b.L : nullptr, pl.map,
+                    S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, nkeys, (nkeys + KT - 1) / KT, pl.sc2};
+      const size_t wgs = (size_t)S * pl.b2 * pl.c1 * p.nkt;
+      hipLaunchKernelGGL((alpha_kernel<T, D, PRECISE>), dim3(grid1(wgs)), dim3(THREADS), 0, st, p);
+      break;
+    }
+    case L_EXPORT_R: {
+      RExportParams p{b.q, b.k, qtil, qbar, lser, b.R, pl.map, S, N, pl.b1, pl.b2, pl.c1, pl.c2,
+                      pl.sw, pl.rt, (int)pl.D, pl.sc2, step == 0 ? 1 : 0};
+      const size_t total = (size_t)S * pl.b1 * pl.b2 * pl.c1 * pl.b2;
+      hipLaunchKernelGGL(r_export_kernel<T>, dim3(grid1((total + 255) / 256)), dim3(256), 0, st, p);
+      break;
+    }
+    case L_OBJECTIVE: {
+      ObjectiveParams p{lse2, b.obj, N};
+      hipLaunchKernelGGL(objective_kernel, dim3(S), dim3(256), 0, st, p);
+      break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool PRECISE>
+ma_status run_t(const Plan& pl, const Bufs& b, hipStream_t st, void* const* events, int n_events) {
+  ma_status status = MA_OK;
+  if (events && n_events > 0 && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess) return MA_ERR_DEVICE;
+  for_each_launch(pl, b.L != nullptr, b.R != nullptr, b.obj != nullptr,
+                  [&](int j, LaunchKind kind, int step) {
+                    if (status != MA_OK) return;
+                    if (launch_one<T, D, PRECISE>(pl, b, kind, step, st) != hipSuccess) { status = MA_ERR_DEVICE; return; }
+                    if (events && j + 1 < n_events &&
+                        hipEventRecord((hipEvent_t)events[j + 1], st) != hipSuccess)
+                      status = MA_ERR_DEVICE;
+                  });
+  return status;
+}
+
+
+}  // namespace ma

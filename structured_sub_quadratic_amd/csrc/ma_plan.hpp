@@ -1,0 +1,96 @@
+// Host-side plan of a MonarchAttention forward call: the workspace layout and
+// the launch sequence, shared by the C ABI and the per-type launch units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/monarch_attn.h"
+#include "ma_device.hpp"
+
+namespace ma {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Largest segment width (keys per R row): one segment must fit the stage-1
+// LDS tile (128 keys; 64 for fp32 with head_dim 128, whose tiles are twice
+// as large).
+inline int max_segment(const ma_problem* p) {
+  return (p->dtype == MA_F32 && p->head_dim == 128) ? 64 : 128;
+}
+
+struct Plan {
+  int64_t S, N, D;
+  int b1, b2, c1, c2, sw, rt, T;
+  int dtype;
+  float scale, sc2;
+  GridMap map;
+  size_t elt, xc_elt;
+  bool precise;
+  size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, total;
+  bool need_qbar, need_qtil;
+  bool fused;        // single cooperative launch for T = 1
+};
+
+// The launch sequence, shared by the real run, the launch count and the
+// launch names.  `Launcher` is called once per kernel launch in order.
+enum LaunchKind { L_FUSED, L_QBAR, L_STAGE1, L_STAGE1_LAST, L_STAGE2_STATS, L_STAGE2_LAST, L_ALPHA,
+                  L_EXPORT_L, L_EXPORT_R, L_OBJECTIVE };
+
+inline const char* launch_kind_name(LaunchKind k) {
+  switch (k) {
+    case L_FUSED: return "fused_t1";
+    case L_QBAR: return "qbar";
+    case L_STAGE1: return "stage1";
+    case L_STAGE1_LAST: return "stage1_last";
+    case L_STAGE2_STATS: return "stage2_stats";
+    case L_STAGE2_LAST: return "stage2_last";
+    case L_ALPHA: return "alpha";
+    case L_EXPORT_L: return "export_L";
+    case L_EXPORT_R: return "export_R";
+    case L_OBJECTIVE: return "objective";
+  }
+  return "?";
+}
+
+template <class F>
+void for_each_launch(const Plan& pl, bool exp_L, bool exp_R, bool exp_obj, F&& f) {
+  int j = 0;
+  if (pl.fused) {
+    f(j++, L_FUSED, 0);
+  } else {
+    if (pl.need_qbar) f(j++, L_QBAR, 0);
+  }
+  for (int step = 0; step < (pl.fused ? 0 : pl.T); ++step) {
+    const bool last = step == pl.T - 1;
+    f(j++, last ? L_STAGE1_LAST : L_STAGE1, step);
+    f(j++, last ? L_STAGE2_LAST : L_STAGE2_STATS, step);
+    if (!last) f(j++, L_ALPHA, step);
+  }
+  if (exp_L) f(j++, L_EXPORT_L, pl.T - 1);
+  if (exp_R) f(j++, L_EXPORT_R, pl.T - 1);
+  if (exp_obj) f(j++, L_OBJECTIVE, pl.T - 1);
+}
+
+struct Bufs {
+  const void *q, *k, *v;
+  void* y;
+  char* ws;
+  float *L, *R, *lse;
+  double* obj;
+};
+
+// Kernel-launch entry of one element type and head dimension (one
+// translation unit each): runs the whole launch sequence of *pl on st.
+typedef ma_status (*RunFn)(const Plan& pl, const Bufs& b, hipStream_t st, void* const* events,
+                           int n_events);
+ma_status run_bf16_64_precise(const Plan&, const Bufs&, hipStream_t, void* const*, int);
+ma_status run_bf16_64_fast(const Plan&, const Bufs&, hipStream_t, void* const*, int);
+ma_status run_bf16_128_precise(const Plan&, const Bufs&, hipStream_t, void* const*, int);
+ma_status run_bf16_128_fast(const Plan&, const Bufs&, hipStream_t, void* const*, int);
+ma_status run_f32_64(const Plan&, const Bufs&, hipStream_t, void* const*, int);
+ma_status run_f32_128(const Plan&, const Bufs&, hipStream_t, void* const*, int);
+
+}  // namespace ma

@@ -96,11 +96,19 @@ def test_workspace_size_and_launch_plan(lib):
     # c, u (bf16) + entropy + two normaliser buffers
     assert ws >= 12 * 16384 * (2 * 64 * 2 + 3 * 4)
     assert ma.launch_names(p) == ["stage1_last", "stage2_last"]
+    p = ma.make_problem(1, 12, 16384, 64, 128, 128, flags=ma.MA_FLAG_FORCE_FUSED)
+    assert ma.launch_names(p) == ["fused_t1"]
+    p = ma.make_problem(1, 12, 16384, 64, 128, 128,
+                        flags=ma.MA_FLAG_FORCE_FUSED | ma.MA_FLAG_FORCE_STAGED)
+    assert ma.launch_names(p) == ["stage1_last", "stage2_last"]
     p = ma.make_problem(8, 12, 4096, 64, 64, 64, steps=3)
     assert ma.launch_names(p) == ["qbar", "stage1", "stage2_stats", "alpha", "stage1",
                                   "stage2_stats", "alpha", "stage1_last", "stage2_last"]
     p = ma.make_problem(1, 12, 32760, 128, 630, 52, c1=2, c2=2, layout="fh_w", fhw=(21, 30, 52))
     assert ma.launch_names(p) == ["qbar", "stage1_last", "stage2_last"]
+    p = ma.make_problem(1, 12, 32760, 128, 630, 52, c1=2, c2=2, layout="fh_w", fhw=(21, 30, 52),
+                        flags=ma.MA_FLAG_FORCE_FUSED)
+    assert ma.launch_names(p) == ["fused_t1"]
     assert lib.monarch_attn_num_launches(ctypes.byref(good(b2=8))) == -1
 
 

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import CONFIGS, WorkloadConfig, make_inputs
+from workloads import WORKLOADS, WorkloadConfig, make_inputs
 from parity_utils import TOL, rel_err, oracle_L_as_gpu, oracle_R_as_gpu, run_hip
 
 pytestmark = pytest.mark.gpu
@@ -60,7 +60,7 @@ def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective
 # ----------------------------------------------------------------- small
 
 def test_config1_full():
-    check_case(CONFIGS[1])
+    check_case(WORKLOADS["n256"])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -68,7 +68,7 @@ def test_config1_full():
 @pytest.mark.parametrize("steps", [1, 2])
 def test_ragged_tiles_untiled(dtype, d, steps):
     """b1 = 70 (stage 2 streams 64 + 6 keys), b2 = 52 (stage 1 ragged)."""
-    cfg = WorkloadConfig(0, f"ragged {dtype} d{d} T{steps}", batch=1, heads=2, seq_len=70 * 52,
+    cfg = WorkloadConfig("case", f"ragged {dtype} d{d} T{steps}", batch=1, heads=2, seq_len=70 * 52,
                          head_dim=d, b1=70, b2=52, steps=steps, dtype=dtype, data="iid", seed=11)
     check_case(cfg)
 
@@ -77,14 +77,14 @@ def test_ragged_tiles_untiled(dtype, d, steps):
 @pytest.mark.parametrize("tiles", [(2, 2), (2, 1), (1, 4), (5, 2)])
 @pytest.mark.parametrize("steps", [1, 3])
 def test_tiled(dtype, tiles, steps):
-    cfg = WorkloadConfig(0, f"tiled {tiles} {dtype} T{steps}", batch=2, heads=1, seq_len=70 * 52,
+    cfg = WorkloadConfig("case", f"tiled {tiles} {dtype} T{steps}", batch=2, heads=1, seq_len=70 * 52,
                          head_dim=64, b1=70, b2=52, steps=steps, dtype=dtype, data="normed",
                          seed=12, c1=tiles[0], c2=tiles[1])
     check_case(cfg)
 
 
 def test_multi_step_bf16_lowrank():
-    cfg = WorkloadConfig(0, "lowrank T3", batch=2, heads=2, seq_len=96 * 40, head_dim=64,
+    cfg = WorkloadConfig("case", "lowrank T3", batch=2, heads=2, seq_len=96 * 40, head_dim=64,
                          b1=96, b2=40, steps=3, dtype="bf16", data="lowrank", seed=13)
     check_case(cfg)
 
@@ -100,7 +100,7 @@ def test_video_layouts(layout, steps):
     c1 = 3 if b1 % 3 == 0 else 1
     c2 = 2 if b2 % 2 == 0 else 1
     for tiles in ((1, 1), (c1, c2)):
-        cfg = WorkloadConfig(0, f"video {layout} T{steps} tiles {tiles}", batch=1, heads=2,
+        cfg = WorkloadConfig("case", f"video {layout} T{steps} tiles {tiles}", batch=1, heads=2,
                              seq_len=120, head_dim=128, b1=b1, b2=b2, steps=steps, dtype="bf16",
                              data="video", seed=14, layout=layout, fhw=fhw,
                              c1=tiles[0], c2=tiles[1])
@@ -112,7 +112,7 @@ def test_video_layouts_exact_without_noise_fp32():
     in every aligned layout, on the GPU as in the oracle."""
     fhw = (3, 4, 10)
     sz = dict(f=3, h=4, w=10)
-    base = WorkloadConfig(0, "video exact", batch=1, heads=1, seq_len=120, head_dim=64,
+    base = WorkloadConfig("case", "video exact", batch=1, heads=1, seq_len=120, head_dim=64,
                           b1=12, b2=10, steps=1, dtype="f32", data="video", seed=15,
                           layout="fh_w", fhw=fhw)
     Q, K, V = make_inputs(base, noise_scale=0.0)
@@ -121,7 +121,7 @@ def test_video_layouts_exact_without_noise_fp32():
     for layout in ("fh_w", "w_fh", "f_hw", "hw_f", "fw_h", "h_fw"):
         a, b = layout.split("_")
         b1 = int(np.prod([sz[c] for c in a]))
-        cfg = WorkloadConfig(0, layout, batch=1, heads=1, seq_len=120, head_dim=64, b1=b1,
+        cfg = WorkloadConfig("case", layout, batch=1, heads=1, seq_len=120, head_dim=64, b1=b1,
                              b2=120 // b1, steps=1, dtype="f32", data="video", seed=15,
                              layout=layout, fhw=fhw)
         y, _ = run_hip(cfg, Q, K, V, exports=())
@@ -134,7 +134,7 @@ def test_dense_limits(dtype):
     """b1 = 1 (one block of N keys) and b2 = 1 (N blocks of one key) are
     exact softmax attention."""
     for b1, b2 in ((1, 128), (300, 1)):
-        cfg = WorkloadConfig(0, f"dense {b1}x{b2}", batch=1, heads=2, seq_len=b1 * b2,
+        cfg = WorkloadConfig("case", f"dense {b1}x{b2}", batch=1, heads=2, seq_len=b1 * b2,
                              head_dim=64, b1=b1, b2=b2, steps=2, dtype=dtype, data="iid", seed=16)
         Q, K, V = make_inputs(cfg)
         y, _ = run_hip(cfg, Q, K, V, exports=())
@@ -146,7 +146,7 @@ def test_dense_limits(dtype):
 
 def test_single_token_and_tiny_grids():
     for (b1, b2) in ((1, 1), (2, 1), (1, 2), (3, 3)):
-        cfg = WorkloadConfig(0, f"tiny {b1}x{b2}", batch=2, heads=3, seq_len=b1 * b2,
+        cfg = WorkloadConfig("case", f"tiny {b1}x{b2}", batch=2, heads=3, seq_len=b1 * b2,
                              head_dim=64, b1=b1, b2=b2, steps=2, dtype="f32", data="iid", seed=17)
         check_case(cfg)
 
@@ -154,7 +154,7 @@ def test_single_token_and_tiny_grids():
 def test_determinism_and_reuse_of_workspace():
     import torch
     import structured_sub_quadratic_amd as ma
-    cfg = WorkloadConfig(0, "det", batch=1, heads=3, seq_len=70 * 52, head_dim=128, b1=70,
+    cfg = WorkloadConfig("case", "det", batch=1, heads=3, seq_len=70 * 52, head_dim=128, b1=70,
                          b2=52, steps=2, dtype="bf16", data="normed", seed=18, c1=2, c2=2)
     Q, K, V = make_inputs(cfg)
     dev = torch.device("cuda:0")
@@ -168,39 +168,79 @@ def test_determinism_and_reuse_of_workspace():
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("case", [
+    dict(name="c1", dtype="f32", d=64, b1=16, b2=16, c=(1, 1), layout="flat", fhw=None, data="iid"),
+    dict(name="ragged", dtype="bf16", d=128, b1=70, b2=52, c=(1, 1), layout="flat", fhw=None, data="iid"),
+    dict(name="tiled", dtype="bf16", d=64, b1=70, b2=52, c=(2, 2), layout="flat", fhw=None, data="normed"),
+    dict(name="video", dtype="bf16", d=128, b1=8, b2=15, c=(1, 3), layout="w_fh", fhw=(3, 5, 8), data="video"),
+    dict(name="f32d128", dtype="f32", d=128, b1=40, b2=48, c=(2, 1), layout="flat", fhw=None, data="iid"),
+    dict(name="wide", dtype="bf16", d=64, b1=12, b2=200, c=(3, 2), layout="flat", fhw=None, data="normed"),
+])
+def test_t1_fused_and_staged_paths(case):
+    """T = 1 as one cooperative launch and as the staged launch sequence: the
+    same result, and both match the oracle."""
+    cfg = WorkloadConfig("case", f"T1 {case['name']}", batch=2, heads=2, seq_len=case["b1"] * case["b2"],
+                         head_dim=case["d"], b1=case["b1"], b2=case["b2"], steps=1, dtype=case["dtype"],
+                         data=case["data"], seed=19, c1=case["c"][0], c2=case["c"][1],
+                         layout=case["layout"], fhw=case["fhw"])
+    y_f, _, _ = check_case(cfg, force_fused=True)
+    y_s, _, _ = check_case(cfg, force_staged=True)
+    scale = np.abs(y_s).max()
+    assert np.abs(y_f - y_s).max() <= 1e-6 * scale
+
+
+@pytest.mark.parametrize("steps", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wide_blocks(dtype, steps):
+    """b2 = 300 > one key tile: stage 1 streams its segments (c2 = 3, 100
+    keys each) in several tiles."""
+    cfg = WorkloadConfig("case", f"wide {dtype} T{steps}", batch=1, heads=2, seq_len=10 * 300,
+                         head_dim=64, b1=10, b2=300, steps=steps, dtype=dtype, data="normed",
+                         seed=23, c1=2, c2=3)
+    check_case(cfg)
+
+
+def test_launch_plan_fused_vs_staged():
+    import structured_sub_quadratic_amd as ma
+    p = ma.make_problem(1, 12, 16384, 64, 128, 128, flags=ma.MA_FLAG_FORCE_FUSED)
+    assert ma.launch_names(p) == ["fused_t1"]
+    p = ma.make_problem(1, 12, 16384, 64, 128, 128)
+    assert ma.launch_names(p) == ["stage1_last", "stage2_last"]
+
+
 # ------------------------------------------------ benchmark workloads, sampled
 
 def test_config2_sampled():
-    cfg = CONFIGS[2]
+    cfg = WORKLOADS["n4k_t3"]
     check_case(cfg, slices=[(0, 0), (3, 7), (7, 11)], exports=("L", "R", "lse"))
 
 
 def test_config3_sampled():
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS["n16k"]
     check_case(cfg, slices=[(0, 0), (0, 11)], cols=[0, 1, 63, 64, 127],
                exports=("L", "R", "lse"))
 
 
-@pytest.mark.parametrize("index", [3, 4, 5])
-def test_fast_aggregate_t1_workloads(index):
+@pytest.mark.parametrize("key", ["n16k", "video", "video_tiled"])
+def test_fast_aggregate_t1_workloads(key):
     """The plain-bf16 aggregate path (MA_FLAG_FAST_AGGREGATE) on the T=1
     workloads it is meant for."""
-    cfg = CONFIGS[index]
+    cfg = WORKLOADS[key]
     check_case(cfg, slices=[(0, 0), (0, 5)], cols=[0, 17, cfg.b2 - 1], exports=("L", "R", "lse"),
                fast_aggregate=True)
 
 
 def test_config4_sampled():
-    cfg = CONFIGS[4]
+    cfg = WORKLOADS["video"]
     check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 25, 51], exports=("L", "R", "lse"))
 
 
 def test_config5_sampled_and_c1_equality():
-    cfg = CONFIGS[5]
+    cfg = WORKLOADS["video_tiled"]
     check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 26, 51], exports=("L", "R", "lse"))
     # c1 = c2 = 1 on the same data: equal to the untiled oracle and to the
     # tiled oracle with c = 1
-    c4 = CONFIGS[4]
+    c4 = WORKLOADS["video"]
     Q, K, V = make_inputs(c4)
     y, _ = run_hip(c4, Q, K, V, exports=())
     cols = [3, 30]

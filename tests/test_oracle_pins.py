@@ -322,7 +322,7 @@ def test_p5_video_codes_exact_without_noise():
     """The sinusoidal per-axis codes of the video workload, with zero noise,
     give additive per-axis scores, reproduced exactly in every aligned layout."""
     from workloads import WorkloadConfig, make_inputs
-    cfg = WorkloadConfig(0, "tiny video", batch=1, heads=1, seq_len=60, head_dim=12,
+    cfg = WorkloadConfig("case", "tiny video", batch=1, heads=1, seq_len=60, head_dim=12,
                          b1=12, b2=5, steps=1, dtype="f32", data="video", seed=5,
                          layout="fh_w", fhw=(3, 4, 5))
     Q, K, V = (x.astype(np.float64) for x in make_inputs(cfg, noise_scale=0.0))
@@ -486,7 +486,7 @@ def test_p8_convergence_shape_qualitative():
     assert page_gain_1 > 0.9
     from workloads import WorkloadConfig, make_inputs
     for data, d in (("iid", 16), ("normed", 64)):
-        cfg = WorkloadConfig(0, "tiny", batch=1, heads=1, seq_len=256, head_dim=d,
+        cfg = WorkloadConfig("case", "tiny", batch=1, heads=1, seq_len=256, head_dim=d,
                              b1=16, b2=16, steps=5, dtype="f32", data=data, seed=3)
         Q, K, V = make_inputs(cfg)
         r = om.forward(Q, K, V, 16, 16, 5)

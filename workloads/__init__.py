@@ -7,8 +7,8 @@ Q, K and V (and rounds them to the configuration's element type), so both the
 CPU oracle and the HIP path can consume the very same values.
 """
 
-from .configs import CONFIGS, WorkloadConfig, get_config
+from .configs import WORKLOADS, WorkloadConfig, get_workload
 from .generators import make_inputs, round_to_bf16, slice_rngs
 
-__all__ = ["CONFIGS", "WorkloadConfig", "get_config", "make_inputs",
+__all__ = ["WORKLOADS", "WorkloadConfig", "get_workload", "make_inputs",
            "round_to_bf16", "slice_rngs"]

@@ -1,4 +1,4 @@
-"""The five MonarchAttention forward workloads.
+"""The five MonarchAttention forward workloads, by short name.
 
 Shapes follow the pages' speed workloads: N = 256, 4K and 16K sequences for
 language and vision ([MA] abstract: speed-ups at N = 256, 4K and 16K), and a
@@ -15,7 +15,7 @@ from typing import Optional, Tuple
 
 @dataclass(frozen=True)
 class WorkloadConfig:
-    index: int
+    key: str                   # short name of the workload
     name: str
     batch: int
     heads: int
@@ -58,26 +58,26 @@ class WorkloadConfig:
         return d
 
 
-CONFIGS = {
-    1: WorkloadConfig(1, "N=256 16x16 d=64 T=1 fp32, 1 slice",
+WORKLOADS = {
+    "n256": WorkloadConfig("n256", "N=256 16x16 d=64 T=1 fp32, 1 slice",
                       batch=1, heads=1, seq_len=256, head_dim=64, b1=16, b2=16,
                       steps=1, dtype="f32", data="iid", seed=1001),
-    2: WorkloadConfig(2, "N=4096 64x64 d=64 T=3 bf16, batch 8 x 12 heads",
+    "n4k_t3": WorkloadConfig("n4k_t3", "N=4096 64x64 d=64 T=3 bf16, batch 8 x 12 heads",
                       batch=8, heads=12, seq_len=4096, head_dim=64, b1=64, b2=64,
                       steps=3, dtype="bf16", data="lowrank", seed=1002),
-    3: WorkloadConfig(3, "N=16384 128x128 d=64 T=1 bf16, 12 heads",
+    "n16k": WorkloadConfig("n16k", "N=16384 128x128 d=64 T=1 bf16, 12 heads",
                       batch=1, heads=12, seq_len=16384, head_dim=64, b1=128, b2=128,
                       steps=1, dtype="bf16", data="normed", seed=1003),
-    4: WorkloadConfig(4, "video f,h,w=21,30,52 (fh,w)=(630,52) d=128 T=1 bf16, 12 heads",
+    "video": WorkloadConfig("video", "video f,h,w=21,30,52 (fh,w)=(630,52) d=128 T=1 bf16, 12 heads",
                       batch=1, heads=12, seq_len=32760, head_dim=128, b1=630, b2=52,
                       steps=1, dtype="bf16", data="video", seed=1004,
                       layout="fh_w", fhw=(21, 30, 52)),
-    5: WorkloadConfig(5, "video (630,52) tiled c1=c2=2 d=128 T=1 bf16, 12 heads",
+    "video_tiled": WorkloadConfig("video_tiled", "video (630,52) tiled c1=c2=2 d=128 T=1 bf16, 12 heads",
                       batch=1, heads=12, seq_len=32760, head_dim=128, b1=630, b2=52,
                       steps=1, dtype="bf16", data="video", seed=1004,
                       layout="fh_w", fhw=(21, 30, 52), c1=2, c2=2),
 }
 
 
-def get_config(i):
-    return CONFIGS[int(i)]
+def get_workload(key):
+    return WORKLOADS[key]
