@@ -22,14 +22,14 @@ struct AlphaParams {
   GridMap map;
   int S, N, b1, b2, c1, c2, rt, nkeys, nkt;
   float sc2;
+  size_t xlo;           // lo plane of split c (elements after cx)
 };
 
 template <typename T, int D, bool PRECISE>
 __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
   typedef Mfma<T> MM;
   typedef typename MM::frag frag;
-  typedef XcT<T, PRECISE> XC;
-  constexpr bool SPLIT = PRECISE && is_bf16<T>();
+  constexpr bool SPLIT = split_x<T, PRECISE>();
   constexpr int KPL = MM::KPL, KSTEP = 4 * KPL, NKS = D / KSTEP;
   constexpr int QT = 32;
   constexpr int LDQ = D + 16 / (int)sizeof(T);
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
   const bool kvalid = key < p.nkeys;
   const size_t base = (((size_t)sl * p.b2 + i) * p.c1 + t) * (size_t)p.b1 * p.c2;
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
-  const XC* Crow = static_cast<const XC*>(p.cx) + (base + (kvalid ? key : 0)) * D;
+  const T* Crow = static_cast<const T*>(p.cx) + (base + (kvalid ? key : 0)) * D;
 
   frag cf[NKS], cl[NKS];
 #pragma unroll
@@ -60,14 +60,8 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
     if (!kvalid) continue;
     const int off = s_ * KSTEP + g * KPL;
     if constexpr (SPLIT) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(Crow + off);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(Crow + off + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf16 h, lo;
-        split_bf16(a[e], h, lo); cf[s_][e] = h; cl[s_][e] = lo;
-        split_bf16(b[e], h, lo); cf[s_][4 + e] = h; cl[s_][4 + e] = lo;
-      }
+      cf[s_] = *reinterpret_cast<const frag*>(Crow + off);
+      cl[s_] = *reinterpret_cast<const frag*>(Crow + p.xlo + off);
     } else if constexpr (KPL == 8) {
       cf[s_] = *reinterpret_cast<const frag*>(Crow + off);
     } else {

@@ -5,9 +5,10 @@
 // aggregate c = R K enters the next scores multiplied by |q|, so rounding R
 // or c to bf16 moves L by about 1e-2.  With PRECISE, the c path carries
 // about 16 significant bits: R is split into bf16 hi + lo parts for the R K
-// product (two MFMAs), c travels in fp32 and is split again into hi + lo keys
-// for the stage-2 scores, and the next-step queries qt stay in fp32 (split on
-// load).  u = R V and y = L u use plain bf16 operands.
+// product (two MFMAs), c is written as two bf16 planes hi = bf16(c),
+// lo = bf16(c - hi) (the bytes of fp32, but ready to be copied into LDS as
+// MFMA operands), and the next-step queries qt stay in fp32 (split on load).
+// u = R V and y = L u use plain bf16 operands.
 #pragma once
 
 #include <type_traits>
@@ -18,9 +19,8 @@ namespace ma {
 
 template <typename T> constexpr bool is_bf16() { return std::is_same<T, bf16>::value; }
 
-// Element type of the exchanged aggregate c.
-template <typename T, bool PRECISE>
-using XcT = typename std::conditional<(PRECISE || !is_bf16<T>()), float, T>::type;
+// The exchanged aggregate c is stored as two planes (hi, lo) of T.
+template <typename T, bool PRECISE> constexpr bool split_x() { return PRECISE && is_bf16<T>(); }
 
 __device__ inline void split_bf16(float x, bf16& hi, bf16& lo) {
   hi = (bf16)x;

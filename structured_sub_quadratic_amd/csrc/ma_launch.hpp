@@ -9,6 +9,7 @@
 #include "ma_aux_kernels.hpp"
 #include "ma_stage_kernels.hpp"
 #include "ma_fused.hpp"
+#include "ma_async.hpp"
 
 namespace ma {
 
@@ -29,6 +30,23 @@ inline size_t persistent_slots() {
 }
 
 template <typename T> constexpr bool is_f32() { return std::is_same<T, float>::value; }
+
+#ifndef MA_NO_ASYNC
+#define MA_NO_ASYNC 0
+#endif
+
+// Waves per workgroup of the direct-to-LDS kernels: 8 (128 query rows) unless
+// 4 (64 rows) pads fewer rows.
+inline int async_waves(int rows) {
+  const int pad4 = (rows + 63) / 64 * 64 - rows, pad8 = (rows + 127) / 128 * 128 - rows;
+  return pad8 <= pad4 ? 8 : 4;
+}
+
+template <class K, class P>
+void launch_persistent(K kernel, int threads, size_t items, const P& p, hipStream_t st) {
+  const size_t g = resident_slots(kernel, threads, items);
+  hipLaunchKernelGGL(kernel, dim3(grid1(g)), dim3(threads), 0, st, p);
+}
 
 // Query sub-tiles of 16 per wave: the choice (1 or 2) that pads the fewest
 // query rows per workgroup group, preferring 2 (more MFMAs per LDS operand).
@@ -85,11 +103,11 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const int nq1 = stage1_nq<T, D>(nqs), qg1 = WAVES * nq1 * 16;
       Stage1Params p1{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                       S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg1 - 1) / qg1,
-                      pl.sc2, 1};
+                      pl.sc2, 1, pl.xlo};
       const int nq2 = stage2_nq<T, D>(pl.rt), qg2 = WAVES * nq2 * 16;
       Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
                       S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg2 - 1) / qg2,
-                      pl.sc2};
+                      pl.sc2, pl.xlo};
       const size_t items = std::max<size_t>(std::max<size_t>((size_t)S * pl.c1 * pl.b2,
                                                              (size_t)S * pl.b1 * p1.nqg),
                                             (size_t)S * pl.b2 * pl.c1 * p2.nqg);
@@ -124,11 +142,35 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     case L_STAGE1:
     case L_STAGE1_LAST: {
       const int nqs = pl.c1 * pl.b2;
+      if constexpr (!is_f32<T>()) {
+        const int ktb = pl.b2 <= 64 ? 64 : 128;
+        if (pl.b2 <= 128 && !MA_NO_ASYNC) {
+          // head_dim 128 keeps 4 waves: two waves a SIMD would spill the K|V sums
+          const int nw = D == 128 ? 4 : async_waves(nqs), qg = nw * 16;
+          Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
+                         S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
+                         pl.sc2, step == 0 ? 1 : 0, pl.xlo};
+          const size_t items = (size_t)S * pl.b1 * p.nqg;
+          const bool last = kind == L_STAGE1_LAST;
+          const bool qsplit = PRECISE && (step > 0 || pl.c1 > 1);
+#define MA_A1(NW, KTB, U, QS) launch_persistent(stage1_async_kernel<D, NW, 1, KTB, U, PRECISE, QS>, NW * WAVE, items, p, st)
+#define MA_A1Q(NW, KTB, U) do { if (qsplit) MA_A1(NW, KTB, U, true); else MA_A1(NW, KTB, U, false); } while (0)
+#define MA_A1U(NW, KTB) do { if (last) MA_A1Q(NW, KTB, true); else MA_A1Q(NW, KTB, false); } while (0)
+#define MA_A1K(NW) do { if (ktb == 64) MA_A1U(NW, 64); else MA_A1U(NW, 128); } while (0)
+          if constexpr (D == 128) MA_A1K(4);
+          else { if (nw == 8) MA_A1K(8); else MA_A1K(4); }
+#undef MA_A1
+#undef MA_A1Q
+#undef MA_A1U
+#undef MA_A1K
+          break;
+        }
+      }
       const int nq = stage1_nq<T, D>(nqs);
       const int qg = WAVES * nq * 16;
       Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                      S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
-                     pl.sc2, step == 0 ? 1 : 0};
+                     pl.sc2, step == 0 ? 1 : 0, pl.xlo};
       const size_t items1 = (size_t)S * pl.b1 * p.nqg;
       const dim3 grid(grid1(items1));
       const bool ktb64 = pl.b2 <= 64 || (is_f32<T>() && D == 128);
@@ -170,11 +212,26 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     }
     case L_STAGE2_STATS:
     case L_STAGE2_LAST: {
+      if constexpr (!is_f32<T>()) {
+        if (!MA_NO_ASYNC) {
+          const int nw = async_waves(pl.rt), qg = nw * 16;
+          Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
+                         S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
+                         pl.sc2, pl.xlo};
+          const size_t items = (size_t)S * pl.b2 * pl.c1 * p.nqg;
+          const bool last = kind == L_STAGE2_LAST;
+#define MA_A2(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE>, NW * WAVE, items, p, st)
+          if (nw == 8) { if (last) MA_A2(8, true); else MA_A2(8, false); }
+          else { if (last) MA_A2(4, true); else MA_A2(4, false); }
+#undef MA_A2
+          break;
+        }
+      }
       const int nq = stage2_nq<T, D>(pl.rt);
       const int qg = WAVES * nq * 16;
       Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                      S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
-                     pl.sc2};
+                     pl.sc2, pl.xlo};
       const size_t items2 = (size_t)S * pl.b2 * pl.c1 * p.nqg;
       const dim3 grid(grid1(items2));
       const bool last = kind == L_STAGE2_LAST;
@@ -205,7 +262,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const int nkeys = pl.b1 * pl.c2;
       AlphaParams p{b.q, cx, h2, lse2, qbar, kind == L_ALPHA ? qtil : nullptr,
                     kind == L_EXPORT_L ? b.L : nullptr, pl.map,
-                    S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, nkeys, (nkeys + KT - 1) / KT, pl.sc2};
+                    S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, nkeys, (nkeys + KT - 1) / KT, pl.sc2,
+                    pl.xlo};
       const size_t wgs = (size_t)S * pl.b2 * pl.c1 * p.nkt;
       hipLaunchKernelGGL((alpha_kernel<T, D, PRECISE>), dim3(grid1(wgs)), dim3(THREADS), 0, st, p);
       break;

@@ -28,6 +28,7 @@ struct Plan {
   float scale, sc2;
   GridMap map;
   size_t elt, xc_elt;
+  size_t xlo;          // elements from the hi plane of split c to its lo plane (0: not split)
   bool precise;
   size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, total;
   bool need_qbar, need_qtil;

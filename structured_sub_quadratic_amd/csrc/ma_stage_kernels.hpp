@@ -131,10 +131,11 @@ struct FlashCore {
       }
   }
 
-  // Raw scores S^T for the key sub-tiles [mt0, mt1) of the LDS tile.
-  template <int LDK>
-  __device__ inline void scores(const T (*ks)[LDK], const T (*ks_lo)[LDK], int mt0, int mt1) {
-    const int lane = threadIdx.x % WAVE, mrow = lane % 16, g = lane / 16;
+  // Raw scores S^T for the key sub-tiles [mt0, mt1) of a key tile; kv.a(mt,
+  // ks) is this lane's A fragment of key sub-tile mt at head-dim step ks
+  // (kv.alo the low part when KLO).
+  template <class KV>
+  __device__ inline void scores_v(const KV& kv, int mt0, int mt1) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt < mt0 || mt >= mt1) continue;
@@ -142,7 +143,7 @@ struct FlashCore {
       for (int n = 0; n < NQ; ++n) s[n][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks_ = 0; ks_ < NKS; ++ks_) {
-        const frag a = *reinterpret_cast<const frag*>(&ks[mt * 16 + mrow][ks_ * KSTEP + g * KPL]);
+        const frag a = kv.a(mt, ks_);
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
           s[n][mt] = MM::mma(a, qf[n][ks_], s[n][mt]);
@@ -151,12 +152,31 @@ struct FlashCore {
           }
         }
         if constexpr (KLO) {
-          const frag al = *reinterpret_cast<const frag*>(&ks_lo[mt * 16 + mrow][ks_ * KSTEP + g * KPL]);
+          const frag al = kv.alo(mt, ks_);
 #pragma unroll
           for (int n = 0; n < NQ; ++n) s[n][mt] = MM::mma(al, qf[n][ks_], s[n][mt]);
         }
       }
     }
+  }
+
+  // Padded row-major key tiles in LDS (register-staged kernels).
+  template <int LDK> struct PaddedKeys {
+    const T (*ks)[LDK];
+    const T (*ks_lo)[LDK];
+    __device__ inline frag a(int mt, int ks_) const {
+      const int lane = threadIdx.x % WAVE;
+      return *reinterpret_cast<const frag*>(&ks[mt * 16 + lane % 16][ks_ * KSTEP + (lane / 16) * KPL]);
+    }
+    __device__ inline frag alo(int mt, int ks_) const {
+      const int lane = threadIdx.x % WAVE;
+      return *reinterpret_cast<const frag*>(&ks_lo[mt * 16 + lane % 16][ks_ * KSTEP + (lane / 16) * KPL]);
+    }
+  };
+
+  template <int LDK>
+  __device__ inline void scores(const T (*ks)[LDK], const T (*ks_lo)[LDK], int mt0, int mt1) {
+    scores_v(PaddedKeys<LDK>{ks, ks_lo}, mt0, mt1);
   }
 
   // Online-softmax update with the LDS keys [klo, khi) of the tile (scores
@@ -169,8 +189,8 @@ struct FlashCore {
   // probabilities are then at most 2^8 (exact in fp32, same relative
   // precision in bf16) and the final normalisation divides them out.
   // Entropy: e = sum p (z - sref) in raw score units, sref = first maximum.
-  template <int LDV, bool HAS_BIAS, bool MASK>
-  __device__ inline void update(const T (*vt)[LDV], const float* bias, float sc2, int klo, int khi) {
+  template <bool HAS_BIAS, bool MASK>
+  __device__ inline void softmax_step(const float* bias, float sc2, int klo, int khi) {
     constexpr float TAU = 8.f;
     constexpr float MASKED = -1e30f;
     const int lane = threadIdx.x % WAVE, mrow = lane % 16, g = lane / 16;
@@ -220,7 +240,33 @@ struct FlashCore {
       }
     }
     fresh = false;
-    if (!WITH_PV) return;
+  }
+
+  // Value tile transposed in padded LDS rows (register-staged kernels).
+  template <int LDV> struct PaddedVT {
+    const T (*vt)[LDV];
+    // A fragment of V^T for value sub-tile dt and keys {32kk+4g+r, 32kk+16+4g+r}
+    __device__ inline frag at(int dt, int kk) const {
+      const int lane = threadIdx.x % WAVE, mrow = lane % 16, g = lane / 16;
+      const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(&vt[dt * 16 + mrow][32 * kk + 4 * g]);
+      const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(&vt[dt * 16 + mrow][32 * kk + 16 + 4 * g]);
+      return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    __device__ inline float scalar(int dt, int key) const {
+      return to_f32(vt[dt * 16 + (threadIdx.x % WAVE) % 16][key]);
+    }
+  };
+
+  template <int LDV, bool HAS_BIAS, bool MASK>
+  __device__ inline void update(const T (*vt)[LDV], const float* bias, float sc2, int klo, int khi) {
+    softmax_step<HAS_BIAS, MASK>(bias, sc2, klo, khi);
+    if constexpr (WITH_PV) pv<MASK>(PaddedVT<LDV>{vt}, klo, khi);
+  }
+
+  // O^T += V^T P^T over the keys [klo, khi) of the tile (probabilities in s).
+  template <bool MASK, class VV>
+  __device__ inline void pv(const VV& vv, int klo, int khi) {
+    const int lane = threadIdx.x % WAVE, g = lane / 16;
     if constexpr (KPL == 8) {
       // 32 keys per MFMA: lane group g supplies keys {32kk+4g+r, 32kk+16+4g+r}
 #pragma unroll
@@ -241,9 +287,7 @@ struct FlashCore {
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(&vt[dt * 16 + mrow][32 * kk + 4 * g]);
-          const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(&vt[dt * 16 + mrow][32 * kk + 16 + 4 * g]);
-          const frag a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          const frag a = vv.at(dt, kk);
 #pragma unroll
           for (int n = 0; n < NQ; ++n) {
             o[n][dt] = MM::mma(a, b[n], o[n][dt]);
@@ -260,7 +304,7 @@ struct FlashCore {
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const float a = to_f32(vt[dt * 16 + mrow][mt * 16 + 4 * g + r]);
+            const float a = vv.scalar(dt, mt * 16 + 4 * g + r);
 #pragma unroll
             for (int n = 0; n < NQ; ++n) o[n][dt] = MM::mma(a, s[n][mt][r], o[n][dt]);
           }
@@ -303,13 +347,15 @@ struct Stage1Params {
   const void* q; const void* k; const void* v;   // [S, N, D]
   const float* qtil;     // qt buffer [S, b1, c1, c2, b2, D] fp32 (steps after the first)
   const float* qbar;     // tile means [S, c1, b2, D] fp32 (first step, c1 > 1)
-  void* cx; void* ux;    // exchange c (XcT), u (T): [S, b2, c1, b1, c2, D]
+  void* cx; void* ux;    // exchange c, u (T): [S, b2, c1, b1, c2, D]; the lo plane
+                         // of split c starts xlo elements after cx
   float* h2x;            // entropy (bits): [S, b2, c1, b1, c2]
   float* lser;           // stage-1 row normaliser (base 2), same layout
   GridMap map;
   int S, N, b1, b2, c1, c2, sw, rt, nqs, nqg;
   float sc2;
   int first_step;
+  size_t xlo;
 };
 
 template <typename T, int D, int DV, int KTB>
@@ -395,7 +441,7 @@ struct Stage1Keys {
 
 // One segment of a stage-1 item: walk the LDS tile in chunks of KT keys over
 // [klo, khi), then write c, u, H_R and the normaliser of every valid slot.
-template <typename T, typename XC, int D, int NQ, int KTB, bool WITH_U, class Core, class Smem>
+template <typename T, bool SPLITX, int D, int NQ, int KTB, bool WITH_U, class Core, class Smem>
 __device__ inline void stage1_segment(Core& core, const Smem& sm, const Stage1Params& p, int sl,
                                       int k, int qg, int s, int klo, int khi) {
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
@@ -419,9 +465,19 @@ __device__ inline void stage1_segment(Core& core, const Smem& sm, const Stage1Pa
     if (slot >= p.nqs) continue;
     const int t = slot / p.b2, i = slot % p.b2;
     const size_t row = ((((size_t)sl * p.b2 + i) * p.c1 + t) * p.b1 + k) * p.c2 + s;
-    XC* C = static_cast<XC*>(p.cx) + row * D;
+    T* C = static_cast<T*>(p.cx) + row * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) store4(C + dt * 16 + 4 * g, core.o[n][dt]);
+    for (int dt = 0; dt < D / 16; ++dt) {
+      if constexpr (SPLITX) {
+        const f32x4 v = core.o[n][dt];
+        const bf16x4 hi = __builtin_convertvector(v, bf16x4);
+        const bf16x4 lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x4), bf16x4);
+        *reinterpret_cast<bf16x4*>(C + dt * 16 + 4 * g) = hi;
+        *reinterpret_cast<bf16x4*>(C + p.xlo + dt * 16 + 4 * g) = lo;
+      } else {
+        store4(C + dt * 16 + 4 * g, core.o[n][dt]);
+      }
+    }
     if (WITH_U) {
       T* U = static_cast<T*>(p.ux) + row * D;
 #pragma unroll
@@ -436,7 +492,7 @@ __device__ inline void stage1_segment(Core& core, const Smem& sm, const Stage1Pa
 
 template <typename T, int D, int NQ, int KTB, bool WITH_U, bool PRECISE, bool QSPLIT>
 struct Stage1Item {
-  typedef XcT<T, PRECISE> XC;
+  static constexpr bool SPLITX = split_x<T, PRECISE>();
   static constexpr int DV = WITH_U ? 2 * D : D;
   static constexpr int QG = WAVES * NQ * 16;
   static constexpr int NSPLIT = (PRECISE && is_bf16<T>()) ? D / 16 : 0;
@@ -480,7 +536,7 @@ struct Stage1Item {
       }
       if (s > 0 && !p.first_step) core.load_queries([&](int n) { return qrow(n, s); }, mode, split);
       __syncthreads();
-      stage1_segment<T, XC, D, NQ, KTB, WITH_U>(core, sm, p, sl, k, qg, s, klo, khi);
+      stage1_segment<T, SPLITX, D, NQ, KTB, WITH_U>(core, sm, p, sl, k, qg, s, klo, khi);
     }
     __syncthreads();
   }
@@ -507,6 +563,7 @@ struct Stage2Params {
   GridMap map;
   int S, N, b1, b2, c1, c2, rt, nkeys, nqg;
   float sc2;
+  size_t xlo;                        // lo plane of split c (elements after cx)
 };
 
 template <typename T, int D, bool KLO, int KR = KT>
@@ -519,28 +576,29 @@ struct alignas(16) Stage2Smem {
   float bias[KR];
 };
 
-// Register staging of one key tile of stage 2: c rows (XC), u rows (T, four
-// rows per task for the transposed store) and the bias.  Rows past nvalid
-// repeat the last valid row (their scores are masked).
-template <typename T, typename XC, int D, bool WITH_PV, bool KLO, int KR = KT>
+// Register staging of one key tile of stage 2: c rows (hi and, when KLO, lo
+// planes), u rows (four rows per task for the transposed store) and the
+// bias.  Rows past nvalid repeat the last valid row (their scores are
+// masked).
+template <typename T, int D, bool WITH_PV, bool KLO, int KR = KT>
 struct Stage2Prefetch {
-  typedef typename Vec16<XC>::type VX;
   typedef typename Vec16<T>::type VT;
-  static constexpr int VNX = Vec16<XC>::N, VNT = Vec16<T>::N;
-  static constexpr int TC = KR * (D / VNX);              // c chunks per tile
+  static constexpr int VNT = Vec16<T>::N;
+  static constexpr int TC = KR * (D / VNT);              // c chunks per tile
   static constexpr int NC = (TC + THREADS - 1) / THREADS;
   static constexpr int TU = (KR / 4) * (D / VNT);        // u tasks per tile
   static constexpr int NU = WITH_PV ? (TU + THREADS - 1) / THREADS : 0;
-  VX c[NC];
+  VT c[NC], cl[KLO ? NC : 1];
   VT u[NU > 0 ? NU : 1][4];
   float h;
 
-  __device__ inline void load(const XC* C, const T* U, const float* H, int nvalid) {
+  __device__ inline void load(const T* C, size_t xlo, const T* U, const float* H, int nvalid) {
 #pragma unroll
     for (int a = 0; a < NC; ++a) {
       const int task = min((int)threadIdx.x + a * THREADS, TC - 1);
-      const int j = min(task / (D / VNX), nvalid - 1), cc = task % (D / VNX);
-      c[a] = *reinterpret_cast<const VX*>(C + (size_t)j * D + cc * VNX);
+      const int j = min(task / (D / VNT), nvalid - 1), cc = task % (D / VNT);
+      c[a] = *reinterpret_cast<const VT*>(C + (size_t)j * D + cc * VNT);
+      if constexpr (KLO) cl[a] = *reinterpret_cast<const VT*>(C + xlo + (size_t)j * D + cc * VNT);
     }
 #pragma unroll
     for (int a = 0; a < NU; ++a) {
@@ -561,15 +619,9 @@ struct Stage2Prefetch {
     for (int a = 0; a < NC; ++a) {
       const int task = threadIdx.x + a * THREADS;
       if (task >= TC) continue;
-      const int j = task / (D / VNX), cc = task % (D / VNX);
-      if constexpr (KLO) {
-        const bf16x4 hi = __builtin_convertvector(c[a], bf16x4);
-        const bf16x4 lo = __builtin_convertvector(c[a] - __builtin_convertvector(hi, f32x4), bf16x4);
-        *reinterpret_cast<bf16x4*>(&sm.ks[j][cc * 4]) = hi;
-        *reinterpret_cast<bf16x4*>(&sm.ks_lo[j][cc * 4]) = lo;
-      } else {
-        *reinterpret_cast<VX*>(&sm.ks[j][cc * VNX]) = c[a];
-      }
+      const int j = task / (D / VNT), cc = task % (D / VNT);
+      *reinterpret_cast<VT*>(&sm.ks[j][cc * VNT]) = c[a];
+      if constexpr (KLO) *reinterpret_cast<VT*>(&sm.ks_lo[j][cc * VNT]) = cl[a];
     }
 #pragma unroll
     for (int a = 0; a < NU; ++a) {
@@ -615,8 +667,7 @@ __device__ inline void stage2_store(const Core& core, const Stage2Params& p, con
 
 template <typename T, int D, int NQ, bool WITH_PV, bool PRECISE>
 struct Stage2Item {
-  typedef XcT<T, PRECISE> XC;
-  static constexpr bool KLO = PRECISE && is_bf16<T>();
+  static constexpr bool KLO = split_x<T, PRECISE>();
   static constexpr int QG = WAVES * NQ * 16;
   typedef FlashCore<T, D, D, NQ, KT, false, WITH_PV, KLO, 0> Core;
   typedef Stage2Smem<T, D, KLO> Smem;
@@ -631,13 +682,13 @@ struct Stage2Item {
     const int sl = id;
 
     const size_t base = (((size_t)sl * p.b2 + i) * p.c1 + t) * (size_t)p.b1 * p.c2;
-    const XC* C = static_cast<const XC*>(p.cx) + base * D;
+    const T* C = static_cast<const T*>(p.cx) + base * D;
     const T* U = static_cast<const T*>(p.ux) + base * D;
     const float* H = p.h2x + base;
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
 
-    Stage2Prefetch<T, XC, D, WITH_PV, KLO> pf;
-    pf.load(C, U, H, min(KT, p.nkeys));
+    Stage2Prefetch<T, D, WITH_PV, KLO> pf;
+    pf.load(C, p.xlo, U, H, min(KT, p.nkeys));
 
     Core core;
     core.init();
@@ -651,7 +702,7 @@ struct Stage2Item {
       pf.store(sm);
       __syncthreads();
       if (kt0 + KT < p.nkeys)
-        pf.load(C + (size_t)(kt0 + KT) * D, U + (size_t)(kt0 + KT) * D, H + kt0 + KT,
+        pf.load(C + (size_t)(kt0 + KT) * D, p.xlo, U + (size_t)(kt0 + KT) * D, H + kt0 + KT,
                 min(KT, p.nkeys - kt0 - KT));
       core.template scores<Smem::LDK>(sm.ks, sm.ks_lo, 0, Core::MT);
       if (nvalid == KT) core.template update<Smem::LDV, true, false>(sm.vt, sm.bias, p.sc2, 0, nvalid);
@@ -688,7 +739,7 @@ template <typename T, int NQ, int D> constexpr int persistent_waves() {
 
 template <typename T, int D, int NQ, int KTB, bool WITH_U, bool PRECISE, bool QSPLIT>
 __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage1_persistent_kernel(Stage1Params p) {
-  typedef XcT<T, PRECISE> XC;
+  constexpr bool SPLITX = split_x<T, PRECISE>();
   constexpr int DV = WITH_U ? 2 * D : D;
   constexpr int QG = WAVES * NQ * 16;
   constexpr int NSPLIT = (PRECISE && is_bf16<T>()) ? D / 16 : 0;
@@ -731,15 +782,14 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
         core.load_queries([&](int n) {
           return stage1_qsrc<T, D>(p, sl, k, qg * QG + wave * NQ * 16 + n * 16 + lane % 16, s);
         }, mode, split);
-      stage1_segment<T, XC, D, NQ, KTB, WITH_U>(core, sm, p, sl, k, qg, s, s * p.sw, s * p.sw + p.sw);
+      stage1_segment<T, SPLITX, D, NQ, KTB, WITH_U>(core, sm, p, sl, k, qg, s, s * p.sw, s * p.sw + p.sw);
     }
   }
 }
 
 template <typename T, int D, int NQ, int KTB, bool WITH_PV, bool PRECISE>
 __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage2_persistent_kernel(Stage2Params p) {
-  typedef XcT<T, PRECISE> XC;
-  constexpr bool KLO = PRECISE && is_bf16<T>();
+  constexpr bool KLO = split_x<T, PRECISE>();
   constexpr int QG = WAVES * NQ * 16;
   typedef FlashCore<T, D, D, NQ, KT, false, WITH_PV, KLO, 0> Core;
   typedef typename Core::frag frag;
@@ -755,14 +805,14 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
     sl = item / p.b2;
   };
 
-  Stage2Prefetch<T, XC, D, WITH_PV, KLO, KTB> pf;
+  Stage2Prefetch<T, D, WITH_PV, KLO, KTB> pf;
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
   auto fetch = [&](int item) {
     int sl, i, t, qg;
     decode(item, sl, i, t, qg);
     const size_t base = (((size_t)sl * p.b2 + i) * p.c1 + t) * (size_t)p.b1 * p.c2;
-    pf.load(static_cast<const XC*>(p.cx) + base * D, static_cast<const T*>(p.ux) + base * D,
+    pf.load(static_cast<const T*>(p.cx) + base * D, p.xlo, static_cast<const T*>(p.ux) + base * D,
             p.h2x + base, p.nkeys);
     Core::fetch_queries([&](int n) {
       return stage2_qsrc<T, D>(p, sl, i, t, qg * QG + wave * NQ * 16 + n * 16 + lane % 16);

@@ -65,6 +65,7 @@ Plan make_plan(const ma_problem* p) {
   const size_t rows = (size_t)pl.S * pl.N * pl.c1 * pl.c2;   // exchange rows
   size_t off = 0;
   pl.off_cx = off;   off = align_up(off + rows * pl.D * pl.xc_elt);
+  pl.xlo = (pl.precise && p->dtype == MA_BF16) ? rows * pl.D : 0;
   pl.off_ux = off;   off = align_up(off + rows * pl.D * pl.elt);
   pl.off_h2 = off;   off = align_up(off + rows * 4);
   pl.off_lser = off; off = align_up(off + rows * 4);

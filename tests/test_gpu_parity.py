@@ -59,7 +59,7 @@ def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective
 
 # ----------------------------------------------------------------- small
 
-def test_config1_full():
+def test_n256_full():
     check_case(WORKLOADS["n256"])
 
 
@@ -70,6 +70,20 @@ def test_ragged_tiles_untiled(dtype, d, steps):
     """b1 = 70 (stage 2 streams 64 + 6 keys), b2 = 52 (stage 1 ragged)."""
     cfg = WorkloadConfig("case", f"ragged {dtype} d{d} T{steps}", batch=1, heads=2, seq_len=70 * 52,
                          head_dim=d, b1=70, b2=52, steps=steps, dtype=dtype, data="iid", seed=11)
+    check_case(cfg)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tiles,steps", [((1, 1), 1), ((2, 2), 2)])
+def test_blocks_over_64_keys(dtype, d, tiles, steps):
+    """b2 = 100: one 128-key LDS tile in stage 1, walked as a full and a
+    partial 64-key chunk; b1 = 24 keeps stage 2 inside one chunk."""
+    if dtype == "f32" and d == 128 and tiles == (1, 1):
+        pytest.skip("fp32 head_dim 128 supports segments of at most 64 keys")
+    cfg = WorkloadConfig("case", f"b2=100 {dtype} d{d} {tiles} T{steps}", batch=1, heads=2,
+                         seq_len=24 * 100, head_dim=d, b1=24, b2=100, steps=steps, dtype=dtype,
+                         data="normed", seed=29, c1=tiles[0], c2=tiles[1])
     check_case(cfg)
 
 
@@ -210,12 +224,12 @@ def test_launch_plan_fused_vs_staged():
 
 # ------------------------------------------------ benchmark workloads, sampled
 
-def test_config2_sampled():
+def test_n4k_t3_sampled():
     cfg = WORKLOADS["n4k_t3"]
     check_case(cfg, slices=[(0, 0), (3, 7), (7, 11)], exports=("L", "R", "lse"))
 
 
-def test_config3_sampled():
+def test_n16k_sampled():
     cfg = WORKLOADS["n16k"]
     check_case(cfg, slices=[(0, 0), (0, 11)], cols=[0, 1, 63, 64, 127],
                exports=("L", "R", "lse"))
@@ -230,12 +244,12 @@ def test_fast_aggregate_t1_workloads(key):
                fast_aggregate=True)
 
 
-def test_config4_sampled():
+def test_video_sampled():
     cfg = WORKLOADS["video"]
     check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 25, 51], exports=("L", "R", "lse"))
 
 
-def test_config5_sampled_and_c1_equality():
+def test_video_tiled_sampled_and_c1_equality():
     cfg = WORKLOADS["video_tiled"]
     check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 26, 51], exports=("L", "R", "lse"))
     # c1 = c2 = 1 on the same data: equal to the untiled oracle and to the
