@@ -4,7 +4,10 @@
 // Each persistent workgroup keeps two LDS buffers: while it computes on one,
 // the copies of its next unit of work stream into the other, so the loads of
 // a whole tile are in flight behind the arithmetic without holding any
-// registers.  Tiles stay row-major (as they are in HBM); the 16-byte chunks
+// registers.  The two buffers are distinct LDS objects and the work loop is
+// unrolled by two so that every access names its buffer statically: the
+// compiler can then tell that the reads of one buffer do not depend on the
+// copies in flight into the other and does not wait for them.  Tiles stay row-major (as they are in HBM); the 16-byte chunks
 // of a row are XOR-swizzled by (row mod 8) so that the 16 rows an MFMA
 // operand read touches fall in different banks.  The transposed value
 // operand (V^T, K^T and U^T of the weighted sums) is read with the gfx950
@@ -22,7 +25,6 @@
 
 namespace ma {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
@@ -31,8 +33,25 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Copy 16 bytes at g into LDS at wave_base + 16 * lane (wave_base uniform).
+//
+// The copy is issued through inline assembly on purpose: the compiler then
+// does not track it, so it cannot make LDS reads of the other buffer wait
+// for it.  Ordering is explicit instead: every buffer is read only after
+// wait_vmem() and a workgroup barrier, and refilled only after the next
+// barrier.  The instruction writes no register; its address operands are
+// read at issue.  M0 (the LDS base of the copy) is saved and restored
+// around it; the nop covers the M0-write hazard of LDS-bound loads.
 __device__ inline void copy16_to_lds(const void* g, void* wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)wave_base, 16, 0, 0);
+  // low 32 bits of a generic pointer into LDS = the LDS byte address
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)wave_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
 }
 
 __device__ inline bf16x4 lds_read_tr4(const char* p) {
@@ -54,7 +73,7 @@ template <int D> struct SwzTile {
     constexpr int NI = R * CPR / WAVE;    // wave-wide copies per tile
     static_assert((R * CPR) % WAVE == 0, "tile must be whole wave copies");
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-#pragma unroll
+#pragma unroll 1
     for (int i0 = 0; i0 < NI; i0 += NW) {
       const int i = i0 + wave;
       if (NI % NW != 0 && i >= NI) break;
@@ -129,25 +148,33 @@ inline size_t resident_slots(K kernel, int threads, size_t items) {
 // ---------------------------------------------------------------------------
 // Stage 1, whole block in one tile (b2 <= KTB).  Item = (slice, block k,
 // query group of NW*NQ*16 slots); NW waves of NQ sub-tiles of 16 queries.
+// Queries: QS_TILE copies the input query rows of the block with the keys
+// (first step of untiled Monarch, where the queries are rows of Q); QS_REG
+// and QS_SPLIT load fp32 or mixed query rows into registers (split into
+// bf16 hi + lo for QS_SPLIT).
 // ---------------------------------------------------------------------------
-template <int D, int NW, int NQ, int KTB, bool WITH_U>
+enum { QS_TILE = 0, QS_REG = 1, QS_SPLIT = 2 };
+
+template <int D, int NW, int NQ, int KTB, bool WITH_U, int QS>
 struct Stage1AsyncSmem {
   static constexpr int TILE = KTB * SwzTile<D>::RB;            // one K or V tile
-  static constexpr int BUF = (WITH_U ? 2 : 1) * TILE;
-  static constexpr int BYTES = 2 * BUF;
+  static constexpr int QOFF = (WITH_U ? 2 : 1) * TILE;         // query tile (QS_TILE)
+  static constexpr int BUF = QOFF + (QS == QS_TILE ? NW * NQ * 16 * SwzTile<D>::RB : 0);
 };
 
-template <int D, int NW, int NQ, int KTB, bool WITH_U, bool PRECISE, bool QSPLIT>
+template <int D, int NW, int NQ, int KTB, bool WITH_U, bool PRECISE, int QS>
 __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p) {
   typedef bf16 T;
   constexpr bool SPLITX = split_x<T, PRECISE>();
+  constexpr bool QSPLIT = QS == QS_SPLIT;
   constexpr int DV = WITH_U ? 2 * D : D;
   constexpr int QG = NW * NQ * 16;
   constexpr int NSPLIT = PRECISE ? D / 16 : 0;
   typedef FlashCore<T, D, DV, NQ, KT, true, true, false, NSPLIT, QSPLIT> Core;
   typedef typename Core::frag frag;
-  typedef Stage1AsyncSmem<D, NW, NQ, KTB, WITH_U> SM;
-  __shared__ __attribute__((aligned(1024))) char smem[SM::BYTES];
+  typedef Stage1AsyncSmem<D, NW, NQ, KTB, WITH_U, QS> SM;
+  __shared__ __attribute__((aligned(1024))) char buf_a[SM::BUF];
+  __shared__ __attribute__((aligned(1024))) char buf_b[SM::BUF];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b1 * p.nqg;
@@ -157,37 +184,100 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
 
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
-  auto issue = [&](int item, int buf) {
+  auto issue = [&](int item, char* b) {
     const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
     const T* K = static_cast<const T*>(p.k) + (size_t)sl * p.N * D;
-    char* b = smem + buf * SM::BUF;
-    SwzTile<D>::template load<KTB, NW>(b, [&](int r) { return K + (size_t)p.map.token(k, r) * D; }, p.b2);
+    const AxisMap am = p.map.row_axis(k);
+    SwzTile<D>::template load<KTB, NW>(b, [&](int r) { return K + am.at(r) * D; }, p.b2);
     if constexpr (WITH_U) {
       const T* V = static_cast<const T*>(p.v) + (size_t)sl * p.N * D;
-      SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + (size_t)p.map.token(k, r) * D; }, p.b2);
+      SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + am.at(r) * D; }, p.b2);
     }
-    Core::fetch_queries([&](int n) { return stage1_qsrc<T, D>(p, sl, k, slot_of(qg, n), 0); }, mode, qn, qnl);
+    if constexpr (QS == QS_TILE) {
+      // untiled first step: slot i is grid row (k, i)
+      const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
+      SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) { return Q + am.at(min(qg * QG + r, p.nqs - 1)) * D; }, QG);
+    } else {
+      Core::fetch_queries([&](int n) { return stage1_qsrc<T, D>(p, sl, k, slot_of(qg, n), 0); }, mode, qn, qnl);
+    }
   };
 
-  int item = blockIdx.x;
-  if (item >= nitems) return;
-  issue(item, 0);
   Core core;
   core.qsplit = QSPLIT && split;
-  for (int j = 0; item < nitems; ++j, item += gridDim.x) {
-    const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
-    wait_vmem();
-    __syncthreads();              // tile j landed everywhere; buffer j+1 is free
-    core.set_queries(qn, qnl);
-    if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, (j + 1) & 1);
-    const char* kt = smem + (j & 1) * SM::BUF;
-    const char* vt = WITH_U ? kt + SM::TILE : kt;
+
+  // Outputs of one segment (c hi/lo, u, entropy, normaliser of this lane's
+  // slots), held in registers until they are stored.  The last segment of an
+  // item is stored only after the next item's copies have been issued, so
+  // that the wait for those copies does not also wait for these stores.
+  struct Out {
+    bf16x4 c[NQ][D / 16], cl[NQ][SPLITX ? D / 16 : 1], u[NQ][WITH_U ? D / 16 : 1];
+    float h2[NQ], lse[NQ];
+    size_t row[NQ];
+    bool valid[NQ];
+    bool any;
+  };
+  Out out;
+  out.any = false;
+  auto collect = [&](int qg, int k, int sl, int s) {
+    float lse2[NQ], h2[NQ];
+    core.finish(lse2, h2, p.sc2);
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int slot = slot_of(qg, n);
+      const int sv = min(slot, p.nqs - 1);
+      const int t = sv / p.b2, i = sv % p.b2;
+      out.valid[n] = slot < p.nqs;
+      out.row[n] = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, t, i);
+      out.h2[n] = h2[n];
+      out.lse[n] = lse2[n];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const f32x4 v = core.o[n][dt];
+        const bf16x4 h = __builtin_convertvector(v, bf16x4);
+        out.c[n][dt] = h;
+        if constexpr (SPLITX) out.cl[n][dt] = __builtin_convertvector(v - __builtin_convertvector(h, f32x4), bf16x4);
+        if constexpr (WITH_U) out.u[n][dt] = __builtin_convertvector(core.o[n][D / 16 + dt], bf16x4);
+      }
+    }
+    out.any = true;
+  };
+  auto flush = [&]() {
+    if (!out.any) return;
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      if (!out.valid[n]) continue;
+      T* C = static_cast<T*>(p.cx) + out.row[n] * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        *reinterpret_cast<bf16x4*>(C + dt * 16 + 4 * g) = out.c[n][dt];
+        if constexpr (SPLITX) *reinterpret_cast<bf16x4*>(C + p.xlo + dt * 16 + 4 * g) = out.cl[n][dt];
+      }
+      if constexpr (WITH_U) {
+        T* U = static_cast<T*>(p.ux) + out.row[n] * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<bf16x4*>(U + dt * 16 + 4 * g) = out.u[n][dt];
+      }
+      if (g == 0) {
+        p.h2x[out.row[n]] = out.h2[n];
+        p.lser[out.row[n]] = out.lse[n];
+      }
+    }
+    out.any = false;
+  };
+
+  // The segments of one item.  RELOAD: later steps read new queries for
+  // every segment.  The first step keeps its queries, and its loop then
+  // holds no global loads (a load there would make the compiler wait for
+  // the copies in flight into the other buffer as well).
+  auto segments = [&](auto reload, int qg, int k, int sl, const char* kt, const char* vt) {
     for (int s = 0; s < p.c2; ++s) {
-      if (s > 0 && !p.first_step)
-        core.load_queries([&](int n) { return stage1_qsrc<T, D>(p, sl, k, slot_of(qg, n), s); }, mode, split);
+      if constexpr (decltype(reload)::value) {
+        if (s > 0)
+          core.load_queries([&](int n) { return stage1_qsrc<T, D>(p, sl, k, slot_of(qg, n), s); }, mode, split);
+      }
       const int klo = s * p.sw, khi = klo + p.sw;
       core.init();
-#pragma unroll
+#pragma unroll 1
       for (int c0 = 0; c0 < KTB; c0 += KT) {
         if (c0 >= khi || c0 + KT <= klo) continue;
         const int lo = max(klo - c0, 0), hi = min(khi - c0, KT);
@@ -202,37 +292,47 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
           core.template pv<true>(vv, lo, hi);
         }
       }
-      float lse2[NQ], h2[NQ];
-      core.finish(lse2, h2, p.sc2);
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        const int slot = slot_of(qg, n);
-        if (slot >= p.nqs) continue;
-        const int t = slot / p.b2, i = slot % p.b2;
-        const size_t row = ((((size_t)sl * p.b2 + i) * p.c1 + t) * p.b1 + k) * p.c2 + s;
-        T* C = static_cast<T*>(p.cx) + row * D;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const f32x4 v = core.o[n][dt];
-          const bf16x4 h = __builtin_convertvector(v, bf16x4);
-          *reinterpret_cast<bf16x4*>(C + dt * 16 + 4 * g) = h;
-          if constexpr (SPLITX) {
-            const bf16x4 l = __builtin_convertvector(v - __builtin_convertvector(h, f32x4), bf16x4);
-            *reinterpret_cast<bf16x4*>(C + p.xlo + dt * 16 + 4 * g) = l;
-          }
-        }
-        if (WITH_U) {
-          T* U = static_cast<T*>(p.ux) + row * D;
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) store4(U + dt * 16 + 4 * g, core.o[n][D / 16 + dt]);
-        }
-        if (g == 0) {
-          p.h2x[row] = h2[n];
-          p.lser[row] = lse2[n];
-        }
-      }
+      collect(qg, k, sl, s);
+      if (s + 1 < p.c2) flush();    // earlier segments: store now
     }
+  };
+
+  // item from buffer cur; the next item of this workgroup is copied into nxt
+  auto step = [&](int item, const char* cur, char* nxt) {
+    const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
+    wait_vmem();
+    __syncthreads();              // cur landed everywhere; nobody reads nxt any more
+    if constexpr (QS == QS_TILE) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n)
+#pragma unroll
+        for (int ks_ = 0; ks_ < Core::NKS; ++ks_)
+          core.qf[n][ks_] = *reinterpret_cast<const frag*>(
+              cur + SM::QOFF + SwzTile<D>::offset(wave * NQ * 16 + n * 16 + lane % 16, 4 * ks_ + g));
+    } else {
+      core.set_queries(qn, qnl);
+    }
+    if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
+    flush();                      // the previous item's last segment
+    const char* vt = WITH_U ? cur + SM::TILE : cur;
+    if constexpr (QS == QS_TILE) {
+      segments(std::false_type(), qg, k, sl, cur, vt);       // always the first step
+    } else {
+      if (p.first_step || p.c2 == 1) segments(std::false_type(), qg, k, sl, cur, vt);
+      else segments(std::true_type(), qg, k, sl, cur, vt);
+    }
+  };
+
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  issue(item, buf_a);
+  for (;;) {
+    step(item, buf_a, buf_b);
+    if ((item += gridDim.x) >= nitems) break;
+    step(item, buf_b, buf_a);
+    if ((item += gridDim.x) >= nitems) break;
   }
+  flush();
 }
 
 // ---------------------------------------------------------------------------
@@ -248,7 +348,6 @@ struct Stage2AsyncSmem {
   static constexpr int LO = TILE;
   static constexpr int U = (KLO ? 2 : 1) * TILE;
   static constexpr int BUF = U + (WITH_PV ? TILE : 0);
-  static constexpr int BYTES = 2 * BUF;
 };
 
 template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE>
@@ -259,8 +358,9 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
   typedef FlashCore<T, D, D, NQ, KT, false, WITH_PV, KLO, 0> Core;
   typedef typename Core::frag frag;
   typedef Stage2AsyncSmem<D, KLO, WITH_PV> SM;
-  __shared__ __attribute__((aligned(1024))) char smem[SM::BYTES];
-  __shared__ float bias_buf[2][KT];
+  __shared__ __attribute__((aligned(1024))) char buf_a[SM::BUF];
+  __shared__ __attribute__((aligned(1024))) char buf_b[SM::BUF];
+  __shared__ float bias_a[KT], bias_b[KT];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b2 * p.c1 * p.nqg;
@@ -276,21 +376,21 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
   float hn = 0.f;               // bias of the unit in flight (last wave, one key a lane)
-  auto issue = [&](int item, int ch, int buf) {
+  auto issue = [&](int item, int ch, char* b) {
     int sl, i, t, qg;
     decode(item, sl, i, t, qg);
-    const size_t base = (((size_t)sl * p.b2 + i) * p.c1 + t) * (size_t)p.b1 * p.c2 + (size_t)ch * KT;
+    const size_t xs = x_stride(p.b2, p.c1);
+    const size_t base = x_base(p.b1, p.b2, p.c1, p.c2, sl, t, i) + (size_t)ch * KT * xs;
     const int nvalid = min(KT, p.nkeys - ch * KT);
-    char* b = smem + buf * SM::BUF;
     const T* C = static_cast<const T*>(p.cx) + base * D;
-    SwzTile<D>::template load<KT, NW>(b + SM::HI, [&](int r) { return C + (size_t)r * D; }, nvalid);
+    SwzTile<D>::template load<KT, NW>(b + SM::HI, [&](int r) { return C + (size_t)r * xs * D; }, nvalid);
     if constexpr (KLO)
-      SwzTile<D>::template load<KT, NW>(b + SM::LO, [&](int r) { return C + p.xlo + (size_t)r * D; }, nvalid);
+      SwzTile<D>::template load<KT, NW>(b + SM::LO, [&](int r) { return C + p.xlo + (size_t)r * xs * D; }, nvalid);
     if constexpr (WITH_PV) {
       const T* U = static_cast<const T*>(p.ux) + base * D;
-      SwzTile<D>::template load<KT, NW>(b + SM::U, [&](int r) { return U + (size_t)r * D; }, nvalid);
+      SwzTile<D>::template load<KT, NW>(b + SM::U, [&](int r) { return U + (size_t)r * xs * D; }, nvalid);
     }
-    if (wave == NW - 1) hn = p.h2x[base + min(lane, nvalid - 1)];
+    if (wave == NW - 1) hn = p.h2x[base + (size_t)min(lane, nvalid - 1) * xs];
     if (ch == 0)
       Core::fetch_queries([&](int n) { return stage2_qsrc<T, D>(p, sl, i, t, row_of(qg, n)); },
                           Q_INPUT, qn, qnl);
@@ -299,28 +399,61 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
   int item = blockIdx.x;
   if (item >= nitems) return;
   int ch = 0;
-  issue(item, 0, 0);
+  issue(item, 0, buf_a);
   Core core;
-  for (int j = 0;; ++j) {
+
+  // Outputs of an item (y rows and normalisers of this lane's queries),
+  // stored after the next unit's copies are issued.
+  struct Out {
+    bf16x4 y[NQ][WITH_PV ? D / 16 : 1];
+    float lse[NQ];
+    int64_t tok[NQ];
+    int l[NQ];
+    bool valid[NQ];
+    int sl, i;
+    bool any;
+  };
+  Out out;
+  out.any = false;
+  auto flush = [&]() {
+    if (!out.any) return;
+    T* Y = static_cast<T*>(p.y) + (size_t)out.sl * p.N * D;
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      if (!out.valid[n]) continue;
+      if constexpr (WITH_PV) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          *reinterpret_cast<bf16x4*>(Y + (size_t)out.tok[n] * D + dt * 16 + 4 * g) = out.y[n][dt];
+      }
+      if (g == 0) {
+        p.lse2[((size_t)out.sl * p.b2 + out.i) * p.b1 + out.l[n]] = out.lse[n];
+        if (p.lse_out) p.lse_out[(size_t)out.sl * p.N + out.tok[n]] = out.lse[n] * LN2;
+      }
+    }
+    out.any = false;
+  };
+  // unit (item, ch) from buffer cur; the next unit is copied into nxt.
+  // Returns false after the last unit of this workgroup.
+  auto unit = [&](const char* cur, float* bias, char* nxt) -> bool {
     wait_vmem();
-    if (wave == NW - 1) bias_buf[j & 1][lane] = hn;
-    __syncthreads();              // unit j landed everywhere; buffer j+1 is free
+    if (wave == NW - 1) bias[lane] = hn;
+    __syncthreads();              // cur landed everywhere; nobody reads nxt any more
     if (ch == 0) {
       core.init();
       core.set_queries(qn, qnl);
     }
     int nitem = item, nchk = ch + 1;
     if (nchk == nch) { nitem = item + gridDim.x; nchk = 0; }
-    if (nitem < nitems) issue(nitem, nchk, (j + 1) & 1);
+    if (nitem < nitems) issue(nitem, nchk, nxt);
+    flush();
 
-    const char* b = smem + (j & 1) * SM::BUF;
-    const float* bias = bias_buf[j & 1];
     const int nvalid = min(KT, p.nkeys - ch * KT);
-    core.scores_v(SwzKeys<D>(b + SM::HI, b + SM::LO), 0, Core::MT);
+    core.scores_v(SwzKeys<D>(cur + SM::HI, cur + SM::LO), 0, Core::MT);
     if (nvalid == KT) core.template softmax_step<true, false>(bias, p.sc2, 0, nvalid);
     else core.template softmax_step<true, true>(bias, p.sc2, 0, nvalid);
     if constexpr (WITH_PV) {
-      const SwzValuesT<D> vv(b + SM::U, b + SM::U);
+      const SwzValuesT<D> vv(cur + SM::U, cur + SM::U);
       if (nvalid == KT) core.template pv<false>(vv, 0, nvalid);
       else core.template pv<true>(vv, 0, nvalid);
     }
@@ -329,27 +462,31 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
       decode(item, sl, i, t, qg);
       float lse2[NQ], h2[NQ];
       core.finish(lse2, h2, p.sc2);
-      T* Y = static_cast<T*>(p.y) + (size_t)sl * p.N * D;
+      const AxisMap am = p.map.col_axis(i);
+      out.sl = sl;
+      out.i = i;
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
         const int ll = row_of(qg, n);
-        if (ll >= p.rt) continue;
-        const int l = t * p.rt + ll;
-        const int64_t tok = p.map.token(l, i);
-        if (WITH_PV) {
+        out.valid[n] = ll < p.rt;
+        out.l[n] = t * p.rt + min(ll, p.rt - 1);
+        out.tok[n] = am.at(out.l[n]);
+        out.lse[n] = lse2[n];
+        if constexpr (WITH_PV) {
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) store4(Y + (size_t)tok * D + dt * 16 + 4 * g, core.o[n][dt]);
-        }
-        if (g == 0) {
-          p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l] = lse2[n];
-          if (p.lse_out) p.lse_out[(size_t)sl * p.N + tok] = lse2[n] * LN2;
+          for (int dt = 0; dt < D / 16; ++dt) out.y[n][dt] = __builtin_convertvector(core.o[n][dt], bf16x4);
         }
       }
+      out.any = true;
     }
-    if (nitem >= nitems) break;
+    if (nitem >= nitems) return false;
     item = nitem;
     ch = nchk;
+    return true;
+  };
+  while (unit(buf_a, bias_a, buf_b) && unit(buf_b, bias_b, buf_a)) {
   }
+  flush();
 }
 
 }  // namespace ma

@@ -48,9 +48,9 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, mrow = lane % 16, g = lane / 16;
   const int key = kt * KT + wave * 16 + mrow;
   const bool kvalid = key < p.nkeys;
-  const size_t base = (((size_t)sl * p.b2 + i) * p.c1 + t) * (size_t)p.b1 * p.c2;
+  const size_t xrow = x_base(p.b1, p.b2, p.c1, p.c2, sl, t, i) + (size_t)(kvalid ? key : 0) * x_stride(p.b2, p.c1);
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
-  const T* Crow = static_cast<const T*>(p.cx) + (base + (kvalid ? key : 0)) * D;
+  const T* Crow = static_cast<const T*>(p.cx) + xrow * D;
 
   frag cf[NKS], cl[NKS];
 #pragma unroll
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
       cf[s_] = from_f32<T>(to_f32(Crow[off]));
     }
   }
-  const float hk = kvalid ? p.h2x[base + key] : 0.f;
+  const float hk = kvalid ? p.h2x[xrow] : 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void qbar_kernel(QbarParams p) {
 
 struct RExportParams {
   const void* q; const void* k; const float* qtil; const float* qbar;
-  const float* lser;    // [S, b2, c1, b1, c2]
+  const float* lser;    // exchange rows (x_row)
   float* R_out;         // [S, b1, b2, c1, b2]
   GridMap map;
   int S, N, b1, b2, c1, c2, sw, rt, D;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void r_export_kernel(RExportParams p) {
         : p.qbar + (((size_t)sl * p.c1 + t) * p.b2 + i) * p.D;
     for (int d = 0; d < p.D; ++d) dot += qrow[d] * to_f32(krow[d]);
   }
-  const float ln = p.lser[((((size_t)sl * p.b2 + i) * p.c1 + t) * p.b1 + k) * p.c2 + s];
+  const float ln = p.lser[x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, t, i)];
   p.R_out[idx] = __builtin_amdgcn_exp2f(dot * p.sc2 - ln);
 }
 

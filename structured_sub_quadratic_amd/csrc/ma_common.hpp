@@ -22,6 +22,18 @@ template <typename T> constexpr bool is_bf16() { return std::is_same<T, bf16>::v
 // The exchanged aggregate c is stored as two planes (hi, lo) of T.
 template <typename T, bool PRECISE> constexpr bool split_x() { return PRECISE && is_bf16<T>(); }
 
+// Rows of the stage-1 -> stage-2 exchange (c, u, entropy, row normaliser),
+// block-major: row(sl, k, s, t, i) = (((sl*b1 + k)*c2 + s)*c1 + t)*b2 + i.
+// Stage 1 (block k) writes contiguous rows; stage 2 (column i, row tile t)
+// reads its keys kk = k*c2 + s at x_base(sl, t, i) + kk * x_stride.
+__device__ inline size_t x_row(int b1, int b2, int c1, int c2, int sl, int k, int s, int t, int i) {
+  return ((((size_t)sl * b1 + k) * c2 + s) * c1 + t) * b2 + i;
+}
+__device__ inline size_t x_base(int b1, int b2, int c1, int c2, int sl, int t, int i) {
+  return (((size_t)sl * b1 * c2) * c1 + t) * b2 + i;
+}
+__device__ inline size_t x_stride(int b2, int c1) { return (size_t)c1 * b2; }
+
 __device__ inline void split_bf16(float x, bf16& hi, bf16& lo) {
   hi = (bf16)x;
   lo = (bf16)(x - (float)hi);

@@ -58,15 +58,36 @@ template <typename T> struct Vec16;
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
 
+// Reductions over the lanes l, l^16, l^32, l^48 with the gfx950 lane-swap
+// VALU instructions (no LDS round trip).  permlane16_swap(v, v) returns
+// {v of the even 16-lane row of each pair, v of the odd row} in every lane
+// of the pair; permlane32_swap(v, v) does the same for the two 32-lane
+// halves.  Combining the two results gives op(v[l], v[l^16]) and then
+// op(v[l], v[l^32]); operand order differs by lane, which fp max and fp add
+// do not see (both are commutative).
+__device__ inline float xor16_pair(float v, float& w) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  w = __uint_as_float(r[1]);
+  return __uint_as_float(r[0]);
+}
+__device__ inline float xor32_pair(float v, float& w) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  w = __uint_as_float(r[1]);
+  return __uint_as_float(r[0]);
+}
 __device__ inline float wave_max_x16x32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float w;
+  float a = xor16_pair(v, w);
+  v = fmaxf(a, w);
+  a = xor32_pair(v, w);
+  return fmaxf(a, w);
 }
 __device__ inline float wave_sum_x16x32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float w;
+  float a = xor16_pair(v, w);
+  v = a + w;
+  a = xor32_pair(v, w);
+  return a + w;
 }
 
 // Store 4 consecutive values (one accumulator column run) to global memory.
@@ -76,6 +97,18 @@ __device__ inline void store4(bf16* p, f32x4 v) {
   b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
   *reinterpret_cast<bf16x4*>(p) = b;
 }
+
+// Tokens along one grid axis: token(r) = base + (r / m) * s1 + (r % m) * s2,
+// or base + r * s2 when m == 0 (uniform over a workgroup).
+struct AxisMap {
+  int64_t base;
+  int m, s1, s2;
+  __device__ inline int64_t at(int r) const {
+    if (m == 0) return base + (int64_t)r * s2;
+    const int a = r / m;
+    return base + (int64_t)a * s1 + (int64_t)(r - a * m) * s2;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Token order <-> grid position (l, i): the flat reshape and the six aligned
@@ -101,6 +134,27 @@ struct GridMap {
       }
       default:  // flat, (fh, w), (f, hw): row-major reshape
         return (int64_t)l * b2 + i;
+    }
+  }
+
+  // token(l, i) as a function of i (row l of the grid)
+  __device__ inline AxisMap row_axis(int l) const {
+    switch (kind) {
+      case 2:
+      case 4: return AxisMap{l, 0, 0, b1};
+      case 5: { const int fi = l / w; return AxisMap{(int64_t)fi * hw + (l - fi * w), 0, 0, w}; }
+      case 6: return AxisMap{(int64_t)l * w, w, hw, 1};
+      default: return AxisMap{(int64_t)l * b2, 0, 0, 1};
+    }
+  }
+  // token(l, i) as a function of l (column i of the grid)
+  __device__ inline AxisMap col_axis(int i) const {
+    switch (kind) {
+      case 2:
+      case 4: return AxisMap{(int64_t)i * b1, 0, 0, 1};
+      case 5: return AxisMap{(int64_t)i * w, w, hw, 1};
+      case 6: { const int fi = i / w; return AxisMap{(int64_t)fi * hw + (i - fi * w), 0, 0, w}; }
+      default: return AxisMap{i, 0, 0, b2};
     }
   }
 };

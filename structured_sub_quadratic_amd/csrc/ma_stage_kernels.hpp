@@ -347,9 +347,9 @@ struct Stage1Params {
   const void* q; const void* k; const void* v;   // [S, N, D]
   const float* qtil;     // qt buffer [S, b1, c1, c2, b2, D] fp32 (steps after the first)
   const float* qbar;     // tile means [S, c1, b2, D] fp32 (first step, c1 > 1)
-  void* cx; void* ux;    // exchange c, u (T): [S, b2, c1, b1, c2, D]; the lo plane
+  void* cx; void* ux;    // exchange c, u (T): x_row rows of D; the lo plane
                          // of split c starts xlo elements after cx
-  float* h2x;            // entropy (bits): [S, b2, c1, b1, c2]
+  float* h2x;            // entropy (bits), one per exchange row
   float* lser;           // stage-1 row normaliser (base 2), same layout
   GridMap map;
   int S, N, b1, b2, c1, c2, sw, rt, nqs, nqg;
@@ -464,7 +464,7 @@ __device__ inline void stage1_segment(Core& core, const Smem& sm, const Stage1Pa
     const int slot = qg * QG + wave * NQ * 16 + n * 16 + lane % 16;
     if (slot >= p.nqs) continue;
     const int t = slot / p.b2, i = slot % p.b2;
-    const size_t row = ((((size_t)sl * p.b2 + i) * p.c1 + t) * p.b1 + k) * p.c2 + s;
+    const size_t row = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, t, i);
     T* C = static_cast<T*>(p.cx) + row * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(THREADS) void stage1_kernel(Stage1Params p) {
 // ---------------------------------------------------------------------------
 struct Stage2Params {
   const void* q; void* y;            // [S, N, D]
-  const void* cx; const void* ux;    // exchange [S, b2, c1, b1, c2, D]
-  const float* h2x;                  // [S, b2, c1, b1, c2]
+  const void* cx; const void* ux;    // exchange, x_row rows of D
+  const float* h2x;                  // entropy, one per exchange row
   float* lse2;                       // [S, b2, b1] row normaliser (base 2)
   float* lse_out;                    // optional [S, N] natural log, token order
   GridMap map;
@@ -592,13 +592,14 @@ struct Stage2Prefetch {
   VT u[NU > 0 ? NU : 1][4];
   float h;
 
-  __device__ inline void load(const T* C, size_t xlo, const T* U, const float* H, int nvalid) {
+  // C, U, H address the tile's first key row; keys are xs rows apart.
+  __device__ inline void load(const T* C, size_t xlo, const T* U, const float* H, int nvalid, size_t xs) {
 #pragma unroll
     for (int a = 0; a < NC; ++a) {
       const int task = min((int)threadIdx.x + a * THREADS, TC - 1);
       const int j = min(task / (D / VNT), nvalid - 1), cc = task % (D / VNT);
-      c[a] = *reinterpret_cast<const VT*>(C + (size_t)j * D + cc * VNT);
-      if constexpr (KLO) cl[a] = *reinterpret_cast<const VT*>(C + xlo + (size_t)j * D + cc * VNT);
+      c[a] = *reinterpret_cast<const VT*>(C + (size_t)j * xs * D + cc * VNT);
+      if constexpr (KLO) cl[a] = *reinterpret_cast<const VT*>(C + xlo + (size_t)j * xs * D + cc * VNT);
     }
 #pragma unroll
     for (int a = 0; a < NU; ++a) {
@@ -607,10 +608,10 @@ struct Stage2Prefetch {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = min(4 * jq + r, nvalid - 1);
-        u[a][r] = *reinterpret_cast<const VT*>(U + (size_t)j * D + cc * VNT);
+        u[a][r] = *reinterpret_cast<const VT*>(U + (size_t)j * xs * D + cc * VNT);
       }
     }
-    h = H[min((int)threadIdx.x, nvalid - 1)];
+    h = H[(size_t)min((int)threadIdx.x, nvalid - 1) * xs];
   }
 
   template <class Smem>
@@ -681,14 +682,14 @@ struct Stage2Item {
     const int i = id % p.b2; id /= p.b2;
     const int sl = id;
 
-    const size_t base = (((size_t)sl * p.b2 + i) * p.c1 + t) * (size_t)p.b1 * p.c2;
+    const size_t base = x_base(p.b1, p.b2, p.c1, p.c2, sl, t, i), xs = x_stride(p.b2, p.c1);
     const T* C = static_cast<const T*>(p.cx) + base * D;
     const T* U = static_cast<const T*>(p.ux) + base * D;
     const float* H = p.h2x + base;
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
 
     Stage2Prefetch<T, D, WITH_PV, KLO> pf;
-    pf.load(C, p.xlo, U, H, min(KT, p.nkeys));
+    pf.load(C, p.xlo, U, H, min(KT, p.nkeys), xs);
 
     Core core;
     core.init();
@@ -702,8 +703,8 @@ struct Stage2Item {
       pf.store(sm);
       __syncthreads();
       if (kt0 + KT < p.nkeys)
-        pf.load(C + (size_t)(kt0 + KT) * D, p.xlo, U + (size_t)(kt0 + KT) * D, H + kt0 + KT,
-                min(KT, p.nkeys - kt0 - KT));
+        pf.load(C + (size_t)(kt0 + KT) * xs * D, p.xlo, U + (size_t)(kt0 + KT) * xs * D,
+                H + (size_t)(kt0 + KT) * xs, min(KT, p.nkeys - kt0 - KT), xs);
       core.template scores<Smem::LDK>(sm.ks, sm.ks_lo, 0, Core::MT);
       if (nvalid == KT) core.template update<Smem::LDV, true, false>(sm.vt, sm.bias, p.sc2, 0, nvalid);
       else core.template update<Smem::LDV, true, true>(sm.vt, sm.bias, p.sc2, 0, nvalid);
@@ -811,9 +812,9 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
   auto fetch = [&](int item) {
     int sl, i, t, qg;
     decode(item, sl, i, t, qg);
-    const size_t base = (((size_t)sl * p.b2 + i) * p.c1 + t) * (size_t)p.b1 * p.c2;
+    const size_t base = x_base(p.b1, p.b2, p.c1, p.c2, sl, t, i);
     pf.load(static_cast<const T*>(p.cx) + base * D, p.xlo, static_cast<const T*>(p.ux) + base * D,
-            p.h2x + base, p.nkeys);
+            p.h2x + base, p.nkeys, x_stride(p.b2, p.c1));
     Core::fetch_queries([&](int n) {
       return stage2_qsrc<T, D>(p, sl, i, t, qg * QG + wave * NQ * 16 + n * 16 + lane % 16);
     }, Q_INPUT, qn, qnl);
