@@ -129,6 +129,35 @@ template <int D> struct SwzValuesT {
   }
 };
 
+// A wave's 16-row output tile (accumulator layout: lane (q, g) holds
+// elements 16*dt + 4*g .. +3 of row q) written to global memory as whole
+// 16-byte row chunks through a per-wave LDS staging tile of 16 rows: lanes
+// then cover complete rows, so each store instruction writes full lines
+// instead of sixteen partial ones.  Ordering inside a wave needs no barrier.
+template <int D> struct WaveRows {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = WAVE / CPR;     // rows per store instruction
+  static constexpr int BYTES = 16 * SwzTile<D>::RB;
+  __device__ static inline void put(char* stg, const bf16x4 (&v)[D / 16]) {
+    const int lane = threadIdx.x % WAVE, q = lane % 16, g = lane / 16;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<bf16x4*>(stg + SwzTile<D>::offset(q, 2 * dt + g / 2) + 8 * (g % 2)) = v[dt];
+  }
+  // row(r) -> destination of row r (nullptr: skip)
+  template <class RowPtr>
+  __device__ static inline void drain(const char* stg, RowPtr row) {
+    const int lane = threadIdx.x % WAVE, c = lane % CPR;
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += RPI) {
+      const int r = r0 + lane / CPR;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + SwzTile<D>::offset(r, c));
+      bf16* dst = row(r);
+      if (dst) *reinterpret_cast<bf16x8*>(dst + c * 8) = v;
+    }
+  }
+};
+
 // Resident workgroups per CU of a kernel (cached) times the CU count.
 template <class K>
 inline size_t resident_slots(K kernel, int threads, size_t items) {
@@ -160,6 +189,9 @@ struct Stage1AsyncSmem {
   static constexpr int TILE = KTB * SwzTile<D>::RB;            // one K or V tile
   static constexpr int QOFF = (WITH_U ? 2 : 1) * TILE;         // query tile (QS_TILE)
   static constexpr int BUF = QOFF + (QS == QS_TILE ? NW * NQ * 16 * SwzTile<D>::RB : 0);
+  // output staging: the wave's own rows of the consumed query tile, or a
+  // tile of its own when the queries do not come through LDS
+  static constexpr int STAGE = QS == QS_TILE ? 16 : NW * WaveRows<D>::BYTES;
 };
 
 template <int D, int NW, int NQ, int KTB, bool WITH_U, bool PRECISE, int QS>
@@ -173,8 +205,10 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
   typedef FlashCore<T, D, DV, NQ, KT, true, true, false, NSPLIT, QSPLIT> Core;
   typedef typename Core::frag frag;
   typedef Stage1AsyncSmem<D, NW, NQ, KTB, WITH_U, QS> SM;
+  static_assert(NQ == 1, "one 16-query sub-tile per wave");
   __shared__ __attribute__((aligned(1024))) char buf_a[SM::BUF];
   __shared__ __attribute__((aligned(1024))) char buf_b[SM::BUF];
+  __shared__ __attribute__((aligned(1024))) char stage_rows[SM::STAGE];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b1 * p.nqg;
@@ -214,6 +248,8 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
     float h2[NQ], lse[NQ];
     size_t row[NQ];
     bool valid[NQ];
+    size_t xbase;       // exchange row of slot 0 of this item and segment
+    int slot0;          // first slot of this wave
     bool any;
   };
   Out out;
@@ -228,6 +264,8 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
       const int t = sv / p.b2, i = sv % p.b2;
       out.valid[n] = slot < p.nqs;
       out.row[n] = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, t, i);
+      out.xbase = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, 0, 0);
+      out.slot0 = slot_of(qg, 0) - lane % 16;
       out.h2[n] = h2[n];
       out.lse[n] = lse2[n];
 #pragma unroll
@@ -241,26 +279,31 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
     }
     out.any = true;
   };
-  auto flush = [&]() {
+  // stage: the current buffer (its query rows have been read into registers)
+  auto flush = [&](char* cur) {
     if (!out.any) return;
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      if (!out.valid[n]) continue;
-      T* C = static_cast<T*>(p.cx) + out.row[n] * D;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        *reinterpret_cast<bf16x4*>(C + dt * 16 + 4 * g) = out.c[n][dt];
-        if constexpr (SPLITX) *reinterpret_cast<bf16x4*>(C + p.xlo + dt * 16 + 4 * g) = out.cl[n][dt];
-      }
-      if constexpr (WITH_U) {
-        T* U = static_cast<T*>(p.ux) + out.row[n] * D;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<bf16x4*>(U + dt * 16 + 4 * g) = out.u[n][dt];
-      }
-      if (g == 0) {
-        p.h2x[out.row[n]] = out.h2[n];
-        p.lser[out.row[n]] = out.lse[n];
-      }
+    char* stg = QS == QS_TILE ? cur + SM::QOFF + wave * WaveRows<D>::BYTES
+                              : stage_rows + wave * WaveRows<D>::BYTES;
+    // slot slot0 + r of this wave -> exchange row xbase + slot (block-major)
+    auto rows = [&](T* base) {
+      return [&, base](int r) -> T* {
+        const int slot = out.slot0 + r;
+        return slot < p.nqs ? base + (out.xbase + slot) * D : nullptr;
+      };
+    };
+    WaveRows<D>::put(stg, out.c[0]);
+    WaveRows<D>::drain(stg, rows(static_cast<T*>(p.cx)));
+    if constexpr (SPLITX) {
+      WaveRows<D>::put(stg, out.cl[0]);
+      WaveRows<D>::drain(stg, rows(static_cast<T*>(p.cx) + p.xlo));
+    }
+    if constexpr (WITH_U) {
+      WaveRows<D>::put(stg, out.u[0]);
+      WaveRows<D>::drain(stg, rows(static_cast<T*>(p.ux)));
+    }
+    if (g == 0 && out.valid[0]) {
+      p.h2x[out.row[0]] = out.h2[0];
+      p.lser[out.row[0]] = out.lse[0];
     }
     out.any = false;
   };
@@ -269,7 +312,7 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
   // every segment.  The first step keeps its queries, and its loop then
   // holds no global loads (a load there would make the compiler wait for
   // the copies in flight into the other buffer as well).
-  auto segments = [&](auto reload, int qg, int k, int sl, const char* kt, const char* vt) {
+  auto segments = [&](auto reload, int qg, int k, int sl, char* kt, const char* vt) {
     for (int s = 0; s < p.c2; ++s) {
       if constexpr (decltype(reload)::value) {
         if (s > 0)
@@ -293,12 +336,12 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
         }
       }
       collect(qg, k, sl, s);
-      if (s + 1 < p.c2) flush();    // earlier segments: store now
+      if (s + 1 < p.c2) flush(kt);  // earlier segments: store now
     }
   };
 
   // item from buffer cur; the next item of this workgroup is copied into nxt
-  auto step = [&](int item, const char* cur, char* nxt) {
+  auto step = [&](int item, char* cur, char* nxt) {
     const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
     wait_vmem();
     __syncthreads();              // cur landed everywhere; nobody reads nxt any more
@@ -313,7 +356,7 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
       core.set_queries(qn, qnl);
     }
     if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
-    flush();                      // the previous item's last segment
+    flush(cur);                   // the previous item's last segment
     const char* vt = WITH_U ? cur + SM::TILE : cur;
     if constexpr (QS == QS_TILE) {
       segments(std::false_type(), qg, k, sl, cur, vt);       // always the first step
@@ -326,13 +369,16 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
   int item = blockIdx.x;
   if (item >= nitems) return;
   issue(item, buf_a);
+  char* last = buf_a;
   for (;;) {
     step(item, buf_a, buf_b);
     if ((item += gridDim.x) >= nitems) break;
     step(item, buf_b, buf_a);
+    last = buf_b;
     if ((item += gridDim.x) >= nitems) break;
+    last = buf_a;
   }
-  flush();
+  flush(last);
 }
 
 // ---------------------------------------------------------------------------
@@ -358,8 +404,10 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
   typedef FlashCore<T, D, D, NQ, KT, false, WITH_PV, KLO, 0> Core;
   typedef typename Core::frag frag;
   typedef Stage2AsyncSmem<D, KLO, WITH_PV> SM;
+  static_assert(NQ == 1, "one 16-query sub-tile per wave");
   __shared__ __attribute__((aligned(1024))) char buf_a[SM::BUF];
   __shared__ __attribute__((aligned(1024))) char buf_b[SM::BUF];
+  __shared__ __attribute__((aligned(1024))) char stage_rows[WITH_PV ? NW * WaveRows<D>::BYTES : 16];
   __shared__ float bias_a[KT], bias_b[KT];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
@@ -411,21 +459,26 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
     int l[NQ];
     bool valid[NQ];
     int sl, i;
+    int l0, lend;       // grid rows of this wave's first query and of the row tile's end
     bool any;
   };
   Out out;
   out.any = false;
+  char* stg = stage_rows + (WITH_PV ? wave * WaveRows<D>::BYTES : 0);
   auto flush = [&]() {
     if (!out.any) return;
     T* Y = static_cast<T*>(p.y) + (size_t)out.sl * p.N * D;
+    if constexpr (WITH_PV) {
+      const AxisMap am = p.map.col_axis(out.i);
+      WaveRows<D>::put(stg, out.y[0]);
+      WaveRows<D>::drain(stg, [&](int r) -> T* {
+        const int l = out.l0 + r;
+        return l < out.lend ? Y + am.at(l) * D : nullptr;
+      });
+    }
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
       if (!out.valid[n]) continue;
-      if constexpr (WITH_PV) {
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-          *reinterpret_cast<bf16x4*>(Y + (size_t)out.tok[n] * D + dt * 16 + 4 * g) = out.y[n][dt];
-      }
       if (g == 0) {
         p.lse2[((size_t)out.sl * p.b2 + out.i) * p.b1 + out.l[n]] = out.lse[n];
         if (p.lse_out) p.lse_out[(size_t)out.sl * p.N + out.tok[n]] = out.lse[n] * LN2;
@@ -465,6 +518,8 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
       const AxisMap am = p.map.col_axis(i);
       out.sl = sl;
       out.i = i;
+      out.l0 = t * p.rt + row_of(qg, 0) - lane % 16;
+      out.lend = t * p.rt + p.rt;
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
         const int ll = row_of(qg, n);
