@@ -123,7 +123,10 @@ def main():
     ap.add_argument("--workload", default="n16k",
                     choices=["n256", "n4k_t3", "n16k", "video", "video_tiled"])
     ap.add_argument("--warm", action="store_true", help="reuse one input set (MALL-resident)")
-    ap.add_argument("--fast-aggregate", action="store_true")
+    ap.add_argument("--fast-aggregate", action="store_true",
+                    help="plain bf16 c = R K path (the default for T = 1)")
+    ap.add_argument("--precise-aggregate", action="store_true",
+                    help="split bf16 hi+lo c = R K path (the default for T > 1)")
     ap.add_argument("--fused", action="store_true",
                     help="T = 1 as one cooperative launch instead of separate stage launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,7 +164,10 @@ def main():
             for _ in range(n_sets)]
     del base
 
-    flags = ma.MA_FLAG_FAST_AGGREGATE if args.fast_aggregate else 0
+    flags = (ma.MA_FLAG_FAST_AGGREGATE if args.fast_aggregate else 0) | \
+        (ma.MA_FLAG_PRECISE_AGGREGATE if args.precise_aggregate else 0)
+    precise = cfg.dtype == "f32" or args.precise_aggregate or \
+        (not args.fast_aggregate and cfg.steps > 1)
     if args.fused:
         flags |= ma.MA_FLAG_FORCE_FUSED
     prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2,
@@ -213,7 +219,6 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
 
     dom = max(set(names), key=lambda n: kern_ms[n])
-    precise = not args.fast_aggregate
     kb = kernel_bytes(cfg, dom, precise)
     achieved = kb / (kern_ms[dom] * 1e-3) / 1e9
     traffic = None
@@ -221,7 +226,7 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as fh:
             tr = json.load(fh)
-        key = f"{cfg.key}{'_fast' if args.fast_aggregate else ''}:{dom}"
+        key = f"{cfg.key}{'' if precise else '_plain'}:{dom}"
         ent = tr.get(key)
         if ent and ent.get("source_hash") == source_hash():
             traffic = ent["hbm_bytes_per_launch"]
@@ -245,7 +250,8 @@ def main():
                    "seq_len": cfg.seq_len, "head_dim": cfg.head_dim, "b1": cfg.b1, "b2": cfg.b2,
                    "T": cfg.steps, "tiles": [cfg.c1, cfg.c2], "layout": cfg.layout,
                    "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)",
-                   "aggregate": "fast bf16" if args.fast_aggregate else "split bf16 / fp32",
+                   "aggregate": "split bf16 hi+lo" if precise and cfg.dtype != "f32" else
+                                ("fp32" if cfg.dtype == "f32" else "plain bf16"),
                    "launches": names},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -92,11 +92,15 @@ typedef enum {
  * sequence unless MA_FLAG_FORCE_FUSED is set; FORCE_STAGED wins over it. */
 #define MA_FLAG_FORCE_STAGED 1u
 #define MA_FLAG_FORCE_FUSED 4u
-/* bf16 only: carry the aggregate c = R K (and the next-step queries) in
- * plain bf16 instead of split hi+lo bf16 / fp32.  Faster (fewer MFMAs, half
- * the bytes for c) but loses about 1e-2 on L for sharply peaked rows; the
- * default keeps about 16 significant bits on that path. */
+/* Precision of the aggregate c = R K (bf16 only).  Split: R enters R K as
+ * bf16 hi + lo parts, c is exchanged as two bf16 planes hi + lo and the
+ * next-step queries stay fp32 (about 16 significant bits on that path).
+ * Plain: bf16 R and a bf16 c (fewer MFMAs, half the bytes for c).  Errors
+ * on the c path grow with the number of steps (c feeds the next queries), so
+ * the default is plain for T = 1 and split for T > 1; the flags force one or
+ * the other (PRECISE wins over FAST). */
 #define MA_FLAG_FAST_AGGREGATE 2u
+#define MA_FLAG_PRECISE_AGGREGATE 8u
 
 typedef struct {
   int64_t batch, heads, seq_len, head_dim;  /* Q,K,V,Y: [batch, heads, seq_len, head_dim] */

@@ -15,6 +15,7 @@ LAYOUTS = {"flat": 0, "fh_w": 1, "w_fh": 2, "f_hw": 3, "hw_f": 4, "fw_h": 5, "h_
 MA_FLAG_FORCE_STAGED = 1
 MA_FLAG_FAST_AGGREGATE = 2
 MA_FLAG_FORCE_FUSED = 4
+MA_FLAG_PRECISE_AGGREGATE = 8
 
 
 class MAProblem(ctypes.Structure):

@@ -175,149 +175,124 @@ inline size_t resident_slots(K kernel, int threads, size_t items) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1, whole block in one tile (b2 <= KTB).  Item = (slice, block k,
-// query group of NW*NQ*16 slots); NW waves of NQ sub-tiles of 16 queries.
-// Queries: QS_TILE copies the input query rows of the block with the keys
-// (first step of untiled Monarch, where the queries are rows of Q); QS_REG
-// and QS_SPLIT load fp32 or mixed query rows into registers (split into
-// bf16 hi + lo for QS_SPLIT).
+// Stage 1 of the first step of untiled Monarch, whole block in one tile
+// (b2 <= KTB).  The queries of block k are then the rows (k, i) of Q, the
+// same grid rows as its keys, so they are copied into LDS with the keys and
+// values.  Item = (slice, block k, query group of NW*16 slots); NW waves of
+// 16 queries each.  (Later steps and tiled problems read fp32 query rows and
+// use the register-staged kernels.)
 // ---------------------------------------------------------------------------
-enum { QS_TILE = 0, QS_REG = 1, QS_SPLIT = 2 };
-
-template <int D, int NW, int NQ, int KTB, bool WITH_U, int QS>
+template <int D, int NW, int KTB, bool WITH_U>
 struct Stage1AsyncSmem {
   static constexpr int TILE = KTB * SwzTile<D>::RB;            // one K or V tile
-  static constexpr int QOFF = (WITH_U ? 2 : 1) * TILE;         // query tile (QS_TILE)
-  static constexpr int BUF = QOFF + (QS == QS_TILE ? NW * NQ * 16 * SwzTile<D>::RB : 0);
-  // output staging: the wave's own rows of the consumed query tile, or a
-  // tile of its own when the queries do not come through LDS
-  static constexpr int STAGE = QS == QS_TILE ? 16 : NW * WaveRows<D>::BYTES;
+  static constexpr int QOFF = (WITH_U ? 2 : 1) * TILE;         // query tile
+  static constexpr int BUF = QOFF + NW * WaveRows<D>::BYTES;
 };
 
-template <int D, int NW, int NQ, int KTB, bool WITH_U, bool PRECISE, int QS>
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE>
 __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p) {
   typedef bf16 T;
   constexpr bool SPLITX = split_x<T, PRECISE>();
-  constexpr bool QSPLIT = QS == QS_SPLIT;
   constexpr int DV = WITH_U ? 2 * D : D;
-  constexpr int QG = NW * NQ * 16;
+  constexpr int QG = NW * 16;
   constexpr int NSPLIT = PRECISE ? D / 16 : 0;
-  typedef FlashCore<T, D, DV, NQ, KT, true, true, false, NSPLIT, QSPLIT> Core;
+  typedef FlashCore<T, D, DV, 1, KT, true, true, false, NSPLIT> Core;
   typedef typename Core::frag frag;
-  typedef Stage1AsyncSmem<D, NW, NQ, KTB, WITH_U, QS> SM;
-  static_assert(NQ == 1, "one 16-query sub-tile per wave");
+  typedef Stage1AsyncSmem<D, NW, KTB, WITH_U> SM;
   __shared__ __attribute__((aligned(1024))) char buf_a[SM::BUF];
   __shared__ __attribute__((aligned(1024))) char buf_b[SM::BUF];
-  __shared__ __attribute__((aligned(1024))) char stage_rows[SM::STAGE];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b1 * p.nqg;
-  const int mode = stage1_qmode(p);
-  const bool split = PRECISE && mode != Q_INPUT;
-  auto slot_of = [&](int qg, int n) { return qg * QG + wave * NQ * 16 + n * 16 + lane % 16; };
+  const int slot0 = wave * 16;            // this wave's first slot within a query group
 
-  frag qn[NQ][Core::NKS];
-  typename Core::QLo qnl;
   auto issue = [&](int item, char* b) {
     const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
-    const T* K = static_cast<const T*>(p.k) + (size_t)sl * p.N * D;
     const AxisMap am = p.map.row_axis(k);
+    const T* K = static_cast<const T*>(p.k) + (size_t)sl * p.N * D;
     SwzTile<D>::template load<KTB, NW>(b, [&](int r) { return K + am.at(r) * D; }, p.b2);
     if constexpr (WITH_U) {
       const T* V = static_cast<const T*>(p.v) + (size_t)sl * p.N * D;
       SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + am.at(r) * D; }, p.b2);
     }
-    if constexpr (QS == QS_TILE) {
-      // untiled first step: slot i is grid row (k, i)
-      const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
-      SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) { return Q + am.at(min(qg * QG + r, p.nqs - 1)) * D; }, QG);
-    } else {
-      Core::fetch_queries([&](int n) { return stage1_qsrc<T, D>(p, sl, k, slot_of(qg, n), 0); }, mode, qn, qnl);
-    }
+    const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
+    SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) { return Q + am.at(min(qg * QG + r, p.nqs - 1)) * D; }, QG);
   };
 
   Core core;
-  core.qsplit = QSPLIT && split;
 
   // Outputs of one segment (c hi/lo, u, entropy, normaliser of this lane's
-  // slots), held in registers until they are stored.  The last segment of an
+  // slot), held in registers until they are stored.  The last segment of an
   // item is stored only after the next item's copies have been issued, so
   // that the wait for those copies does not also wait for these stores.
   struct Out {
-    bf16x4 c[NQ][D / 16], cl[NQ][SPLITX ? D / 16 : 1], u[NQ][WITH_U ? D / 16 : 1];
-    float h2[NQ], lse[NQ];
-    size_t row[NQ];
-    bool valid[NQ];
-    size_t xbase;       // exchange row of slot 0 of this item and segment
-    int slot0;          // first slot of this wave
+    bf16x4 c[D / 16], cl[SPLITX ? D / 16 : 1], u[WITH_U ? D / 16 : 1];
+    float h2, lse;
+    size_t xbase;       // exchange row of slot 0 of the item's query group
+    int qg0;            // first slot of the query group
     bool any;
   };
   Out out;
   out.any = false;
   auto collect = [&](int qg, int k, int sl, int s) {
-    float lse2[NQ], h2[NQ];
+    float lse2[1], h2[1];
     core.finish(lse2, h2, p.sc2);
+    out.xbase = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, 0, 0);   // untiled: slot = i
+    out.qg0 = qg * QG;
+    out.h2 = h2[0];
+    out.lse = lse2[0];
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      const int slot = slot_of(qg, n);
-      const int sv = min(slot, p.nqs - 1);
-      const int t = sv / p.b2, i = sv % p.b2;
-      out.valid[n] = slot < p.nqs;
-      out.row[n] = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, t, i);
-      out.xbase = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, 0, 0);
-      out.slot0 = slot_of(qg, 0) - lane % 16;
-      out.h2[n] = h2[n];
-      out.lse[n] = lse2[n];
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4 v = core.o[n][dt];
-        const bf16x4 h = __builtin_convertvector(v, bf16x4);
-        out.c[n][dt] = h;
-        if constexpr (SPLITX) out.cl[n][dt] = __builtin_convertvector(v - __builtin_convertvector(h, f32x4), bf16x4);
-        if constexpr (WITH_U) out.u[n][dt] = __builtin_convertvector(core.o[n][D / 16 + dt], bf16x4);
-      }
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const f32x4 v = core.o[0][dt];
+      const bf16x4 h = __builtin_convertvector(v, bf16x4);
+      out.c[dt] = h;
+      if constexpr (SPLITX) out.cl[dt] = __builtin_convertvector(v - __builtin_convertvector(h, f32x4), bf16x4);
+      if constexpr (WITH_U) out.u[dt] = __builtin_convertvector(core.o[0][D / 16 + dt], bf16x4);
     }
     out.any = true;
   };
-  // stage: the current buffer (its query rows have been read into registers)
+  // stage: the wave's rows of the query tile of the current buffer, which
+  // have been read into registers already
   auto flush = [&](char* cur) {
     if (!out.any) return;
-    char* stg = QS == QS_TILE ? cur + SM::QOFF + wave * WaveRows<D>::BYTES
-                              : stage_rows + wave * WaveRows<D>::BYTES;
-    // slot slot0 + r of this wave -> exchange row xbase + slot (block-major)
+    char* stg = cur + SM::QOFF + wave * WaveRows<D>::BYTES;
     auto rows = [&](T* base) {
       return [&, base](int r) -> T* {
-        const int slot = out.slot0 + r;
+        const int slot = out.qg0 + slot0 + r;
         return slot < p.nqs ? base + (out.xbase + slot) * D : nullptr;
       };
     };
-    WaveRows<D>::put(stg, out.c[0]);
+    WaveRows<D>::put(stg, out.c);
     WaveRows<D>::drain(stg, rows(static_cast<T*>(p.cx)));
     if constexpr (SPLITX) {
-      WaveRows<D>::put(stg, out.cl[0]);
+      WaveRows<D>::put(stg, out.cl);
       WaveRows<D>::drain(stg, rows(static_cast<T*>(p.cx) + p.xlo));
     }
     if constexpr (WITH_U) {
-      WaveRows<D>::put(stg, out.u[0]);
+      WaveRows<D>::put(stg, out.u);
       WaveRows<D>::drain(stg, rows(static_cast<T*>(p.ux)));
     }
-    if (g == 0 && out.valid[0]) {
-      p.h2x[out.row[0]] = out.h2[0];
-      p.lser[out.row[0]] = out.lse[0];
+    const int slot = out.qg0 + slot0 + lane % 16;
+    if (g == 0 && slot < p.nqs) {
+      p.h2x[out.xbase + slot] = out.h2;
+      p.lser[out.xbase + slot] = out.lse;
     }
     out.any = false;
   };
 
-  // The segments of one item.  RELOAD: later steps read new queries for
-  // every segment.  The first step keeps its queries, and its loop then
-  // holds no global loads (a load there would make the compiler wait for
-  // the copies in flight into the other buffer as well).
-  auto segments = [&](auto reload, int qg, int k, int sl, char* kt, const char* vt) {
+  // item from buffer cur; the next item of this workgroup is copied into nxt
+  auto step = [&](int item, char* cur, char* nxt) {
+    const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
+    wait_vmem();
+    __syncthreads();              // cur landed everywhere; nobody reads nxt any more
+#pragma unroll
+    for (int ks_ = 0; ks_ < Core::NKS; ++ks_)
+      core.qf[0][ks_] = *reinterpret_cast<const frag*>(
+          cur + SM::QOFF + SwzTile<D>::offset(slot0 + lane % 16, 4 * ks_ + g));
+    if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
+    flush(cur);                   // the previous item's last segment
+    const char* vt = WITH_U ? cur + SM::TILE : cur;
     for (int s = 0; s < p.c2; ++s) {
-      if constexpr (decltype(reload)::value) {
-        if (s > 0)
-          core.load_queries([&](int n) { return stage1_qsrc<T, D>(p, sl, k, slot_of(qg, n), s); }, mode, split);
-      }
       const int klo = s * p.sw, khi = klo + p.sw;
       core.init();
 #pragma unroll 1
@@ -325,8 +300,8 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
         if (c0 >= khi || c0 + KT <= klo) continue;
         const int lo = max(klo - c0, 0), hi = min(khi - c0, KT);
         const int off = c0 * SwzTile<D>::RB;
-        core.scores_v(SwzKeys<D>(kt + off, nullptr), lo / 16, (hi + 15) / 16);
-        const SwzValuesT<D> vv(kt + off, vt + off);
+        core.scores_v(SwzKeys<D>(cur + off, nullptr), lo / 16, (hi + 15) / 16);
+        const SwzValuesT<D> vv(cur + off, vt + off);
         if (lo == 0 && hi == KT) {
           core.template softmax_step<false, false>(nullptr, p.sc2, lo, hi);
           core.template pv<false>(vv, lo, hi);
@@ -336,37 +311,13 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
         }
       }
       collect(qg, k, sl, s);
-      if (s + 1 < p.c2) flush(kt);  // earlier segments: store now
+      if (s + 1 < p.c2) flush(cur);  // earlier segments: store now
     }
   };
 
-  // item from buffer cur; the next item of this workgroup is copied into nxt
-  auto step = [&](int item, char* cur, char* nxt) {
-    const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
-    wait_vmem();
-    __syncthreads();              // cur landed everywhere; nobody reads nxt any more
-    if constexpr (QS == QS_TILE) {
-#pragma unroll
-      for (int n = 0; n < NQ; ++n)
-#pragma unroll
-        for (int ks_ = 0; ks_ < Core::NKS; ++ks_)
-          core.qf[n][ks_] = *reinterpret_cast<const frag*>(
-              cur + SM::QOFF + SwzTile<D>::offset(wave * NQ * 16 + n * 16 + lane % 16, 4 * ks_ + g));
-    } else {
-      core.set_queries(qn, qnl);
-    }
-    if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
-    flush(cur);                   // the previous item's last segment
-    const char* vt = WITH_U ? cur + SM::TILE : cur;
-    if constexpr (QS == QS_TILE) {
-      segments(std::false_type(), qg, k, sl, cur, vt);       // always the first step
-    } else {
-      if (p.first_step || p.c2 == 1) segments(std::false_type(), qg, k, sl, cur, vt);
-      else segments(std::true_type(), qg, k, sl, cur, vt);
-    }
-  };
-
-  int item = blockIdx.x;
+  // Workgroup b takes items pos(b), pos(b) + G, ... where pos groups the
+  // workgroups of one XCD on consecutive items.
+  int item = (int)xcd_swizzle(blockIdx.x, gridDim.x);
   if (item >= nitems) return;
   issue(item, buf_a);
   char* last = buf_a;
@@ -444,7 +395,10 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
                           Q_INPUT, qn, qnl);
   };
 
-  int item = blockIdx.x;
+  // Workgroup b takes items pos(b), pos(b) + G, ... where pos groups the
+  // workgroups of one XCD on consecutive items, so the query groups of one
+  // column (consecutive items) read their shared key tiles through one L2.
+  int item = (int)xcd_swizzle(blockIdx.x, gridDim.x);
   if (item >= nitems) return;
   int ch = 0;
   issue(item, 0, buf_a);

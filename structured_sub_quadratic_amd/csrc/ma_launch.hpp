@@ -144,28 +144,22 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const int nqs = pl.c1 * pl.b2;
       if constexpr (!is_f32<T>()) {
         const int ktb = pl.b2 <= 64 ? 64 : 128;
-        if (pl.b2 <= 128 && !MA_NO_ASYNC) {
-          // Query rows from Q (untiled first step) are copied with the keys;
-          // the other query sources hold more registers, so they and head_dim
-          // 128 keep 4 waves (two waves a SIMD would spill).
-          const int qs = (step == 0 && pl.c1 == 1) ? QS_TILE : (PRECISE ? QS_SPLIT : QS_REG);
-          const int nw = (D == 64 && qs == QS_TILE) ? async_waves(nqs) : 4, qg = nw * 16;
+        // the copied-tile kernel serves the untiled first step (queries are
+        // rows of Q); fp32 query sources stay on the register-staged kernels
+        if (pl.b2 <= 128 && step == 0 && pl.c1 == 1 && !MA_NO_ASYNC) {
+          // head_dim 128 keeps 4 waves (two waves a SIMD would spill the
+          // K|V sums)
+          const int nw = D == 64 ? async_waves(nqs) : 4, qg = nw * 16;
           Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
                          pl.sc2, step == 0 ? 1 : 0, pl.xlo};
           const size_t items = (size_t)S * pl.b1 * p.nqg;
           const bool last = kind == L_STAGE1_LAST;
-#define MA_A1(NW, KTB, U, QS) launch_persistent(stage1_async_kernel<D, NW, 1, KTB, U, PRECISE, QS>, NW * WAVE, items, p, st)
-#define MA_A1U(NW, KTB, QS) do { if (last) MA_A1(NW, KTB, true, QS); else MA_A1(NW, KTB, false, QS); } while (0)
-#define MA_A1K(NW, QS) do { if (ktb == 64) MA_A1U(NW, 64, QS); else MA_A1U(NW, 128, QS); } while (0)
-          if (qs == QS_TILE) {
-            if constexpr (D == 64) { if (nw == 8) MA_A1K(8, QS_TILE); else MA_A1K(4, QS_TILE); }
-            else MA_A1K(4, QS_TILE);
-          } else if constexpr (PRECISE) {
-            MA_A1K(4, QS_SPLIT);
-          } else {
-            MA_A1K(4, QS_REG);
-          }
+#define MA_A1(NW, KTB, U) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE>, NW * WAVE, items, p, st)
+#define MA_A1U(NW, KTB) do { if (last) MA_A1(NW, KTB, true); else MA_A1(NW, KTB, false); } while (0)
+#define MA_A1K(NW) do { if (ktb == 64) MA_A1U(NW, 64); else MA_A1U(NW, 128); } while (0)
+          if constexpr (D == 64) { if (nw == 8) MA_A1K(8); else MA_A1K(4); }
+          else MA_A1K(4);
 #undef MA_A1
 #undef MA_A1U
 #undef MA_A1K

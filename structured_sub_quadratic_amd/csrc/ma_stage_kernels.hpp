@@ -189,14 +189,35 @@ struct FlashCore {
   // probabilities are then at most 2^8 (exact in fp32, same relative
   // precision in bf16) and the final normalisation divides them out.
   // Entropy: e = sum p (z - sref) in raw score units, sref = first maximum.
+  // Maxima and sums over the lane's 4*MT keys are pairwise trees, so the
+  // dependent chains are short.
+  template <int K> __device__ static inline float tree_max(const float (&v)[K]) {
+    if constexpr (K == 1) return v[0];
+    else {
+      float h[K / 2];
+#pragma unroll
+      for (int j = 0; j < K / 2; ++j) h[j] = fmaxf(v[2 * j], v[2 * j + 1]);
+      return tree_max(h);
+    }
+  }
+  template <int K> __device__ static inline float tree_sum(const float (&v)[K]) {
+    if constexpr (K == 1) return v[0];
+    else {
+      float h[K / 2];
+#pragma unroll
+      for (int j = 0; j < K / 2; ++j) h[j] = v[2 * j] + v[2 * j + 1];
+      return tree_sum(h);
+    }
+  }
+
   template <bool HAS_BIAS, bool MASK>
   __device__ inline void softmax_step(const float* bias, float sc2, int klo, int khi) {
     constexpr float TAU = 8.f;
     constexpr float MASKED = -1e30f;
-    const int lane = threadIdx.x % WAVE, mrow = lane % 16, g = lane / 16;
+    const int lane = threadIdx.x % WAVE, g = lane / 16;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-      float tmax = MASKED;
+      float zs[4 * MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -208,10 +229,10 @@ struct FlashCore {
             if (key < klo || key >= khi) z = MASKED;
           }
           s[n][mt][r] = z;
-          tmax = fmaxf(tmax, z);
+          zs[4 * mt + r] = z;
         }
       }
-      tmax = wave_max_x16x32(tmax);
+      float tmax = wave_max_x16x32(tree_max(zs));
       const float tm = HAS_BIAS ? tmax : tmax * sc2;          // base-2 units
       const bool raise = tm > m[n] + TAU;                       // true on the first tile
       const float mnew = raise ? tm : m[n];
@@ -226,6 +247,7 @@ struct FlashCore {
       }
       if (ENTROPY && fresh) sref[n] = tmax;
       m[n] = mnew;
+      float ps[4 * MT], es[4 * MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -233,11 +255,13 @@ struct FlashCore {
           const float z = s[n][mt][r];
           const float p = HAS_BIAS ? __builtin_amdgcn_exp2f(z - mnew)
                                    : __builtin_amdgcn_exp2f(fmaf(z, sc2, -mnew));
-          l[n] += p;
-          if (ENTROPY) e[n] = fmaf(p, z - sref[n], e[n]);
+          ps[4 * mt + r] = p;
+          if (ENTROPY) es[4 * mt + r] = p * (z - sref[n]);
           s[n][mt][r] = p;
         }
       }
+      l[n] += tree_sum(ps);
+      if (ENTROPY) e[n] += tree_sum(es);
     }
     fresh = false;
   }

@@ -57,7 +57,8 @@ Plan make_plan(const ma_problem* p) {
   pl.map.b1 = p->b1; pl.map.b2 = p->b2;
   pl.map.h = p->h; pl.map.w = p->w; pl.map.hw = p->h * p->w;
   pl.elt = p->dtype == MA_F32 ? 4 : 2;
-  pl.precise = p->dtype == MA_F32 || !(p->flags & MA_FLAG_FAST_AGGREGATE);
+  pl.precise = p->dtype == MA_F32 || (p->flags & MA_FLAG_PRECISE_AGGREGATE) ||
+               (!(p->flags & MA_FLAG_FAST_AGGREGATE) && p->steps > 1);
   pl.xc_elt = pl.precise ? 4 : 2;
   pl.need_qtil = p->steps > 1;
   pl.need_qbar = p->steps > 1 || p->c1 > 1;

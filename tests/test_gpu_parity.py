@@ -236,12 +236,12 @@ def test_n16k_sampled():
 
 
 @pytest.mark.parametrize("key", ["n16k", "video", "video_tiled"])
-def test_fast_aggregate_t1_workloads(key):
-    """The plain-bf16 aggregate path (MA_FLAG_FAST_AGGREGATE) on the T=1
-    workloads it is meant for."""
+def test_precise_aggregate_t1_workloads(key):
+    """The split aggregate path (MA_FLAG_PRECISE_AGGREGATE) on the T = 1
+    workloads, whose default is the plain bf16 path."""
     cfg = WORKLOADS[key]
     check_case(cfg, slices=[(0, 0), (0, 5)], cols=[0, 17, cfg.b2 - 1], exports=("L", "R", "lse"),
-               fast_aggregate=True)
+               precise_aggregate=True)
 
 
 def test_video_sampled():
