@@ -21,6 +21,8 @@
 // two-stage structure and the tiled variant follow MonarchRT ("Method").
 #pragma once
 
+#include <hip/hip_cooperative_groups.h>
+
 #include "ma_stage_kernels.hpp"
 
 namespace ma {
@@ -190,7 +192,10 @@ struct Stage1AsyncSmem {
 };
 
 template <int D, int NW, int KTB, bool WITH_U, bool PRECISE>
-__global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p) {
+struct Stage1Async {
+  static constexpr int LDS_BYTES = 2 * Stage1AsyncSmem<D, NW, KTB, WITH_U>::BUF;
+
+  __device__ static void run(const Stage1Params& p, char* lds) {
   typedef bf16 T;
   constexpr bool SPLITX = split_x<T, PRECISE>();
   constexpr int DV = WITH_U ? 2 * D : D;
@@ -199,8 +204,8 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
   typedef FlashCore<T, D, DV, 1, KT, true, true, false, NSPLIT> Core;
   typedef typename Core::frag frag;
   typedef Stage1AsyncSmem<D, NW, KTB, WITH_U> SM;
-  __shared__ __attribute__((aligned(1024))) char buf_a[SM::BUF];
-  __shared__ __attribute__((aligned(1024))) char buf_b[SM::BUF];
+  char* const buf_a = lds;
+  char* const buf_b = lds + SM::BUF;
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b1 * p.nqg;
@@ -330,6 +335,14 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
     last = buf_a;
   }
   flush(last);
+  }
+};
+
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE>
+__global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p) {
+  typedef Stage1Async<D, NW, KTB, WITH_U, PRECISE> S;
+  __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
+  S::run(p, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,7 +361,12 @@ struct Stage2AsyncSmem {
 };
 
 template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE>
-__global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p) {
+struct Stage2Async {
+  typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV> SM0;
+  static constexpr int STG = WITH_PV ? NW * WaveRows<D>::BYTES : 0;
+  static constexpr int LDS_BYTES = 2 * SM0::BUF + STG + 2 * KT * 4;
+
+  __device__ static void run(const Stage2Params& p, char* lds) {
   typedef bf16 T;
   constexpr bool KLO = split_x<T, PRECISE>();
   constexpr int QG = NW * NQ * 16;
@@ -356,10 +374,11 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
   typedef typename Core::frag frag;
   typedef Stage2AsyncSmem<D, KLO, WITH_PV> SM;
   static_assert(NQ == 1, "one 16-query sub-tile per wave");
-  __shared__ __attribute__((aligned(1024))) char buf_a[SM::BUF];
-  __shared__ __attribute__((aligned(1024))) char buf_b[SM::BUF];
-  __shared__ __attribute__((aligned(1024))) char stage_rows[WITH_PV ? NW * WaveRows<D>::BYTES : 16];
-  __shared__ float bias_a[KT], bias_b[KT];
+  char* const buf_a = lds;
+  char* const buf_b = lds + SM::BUF;
+  char* const stage_rows = lds + 2 * SM::BUF;
+  float* const bias_a = reinterpret_cast<float*>(lds + 2 * SM::BUF + STG);
+  float* const bias_b = bias_a + KT;
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b2 * p.c1 * p.nqg;
@@ -496,6 +515,33 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
   while (unit(buf_a, bias_a, buf_b) && unit(buf_b, bias_b, buf_a)) {
   }
   flush();
+  }
+};
+
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE>
+__global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p) {
+  typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE> S;
+  __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
+  S::run(p, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Fused single launch for T = 1 (untiled): stage 1 over every block, a
+// grid-wide barrier, stage 2 over every column, in one cooperative launch of
+// resident persistent workgroups.  Removes the launch gap between the stages;
+// the exchange written by phase 1 is read by phase 2 while it is still warm
+// in the Infinity Cache.  Both phases use NW waves per workgroup.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int KTB, bool PRECISE>
+__global__ __launch_bounds__(NW * WAVE) void fused_async_kernel(Stage1Params p1, Stage2Params p2) {
+  typedef Stage1Async<D, NW, KTB, true, PRECISE> S1;
+  typedef Stage2Async<D, NW, 1, true, PRECISE> S2;
+  constexpr int BYTES = S1::LDS_BYTES > S2::LDS_BYTES ? S1::LDS_BYTES : S2::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[BYTES];
+  S1::run(p1, lds);
+  __syncthreads();
+  cooperative_groups::this_grid().sync();
+  S2::run(p2, lds);
 }
 
 }  // namespace ma

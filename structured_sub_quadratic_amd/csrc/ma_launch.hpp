@@ -73,15 +73,15 @@ template <typename T, int D> int stage2_nq(int rows) {
 // Cooperative launch of a fused kernel: as many workgroups as can be resident
 // at once (the grid-wide barriers need them all), at most one per item.
 template <class K>
-hipError_t launch_cooperative(K kernel, size_t items, void** args, hipStream_t st) {
+hipError_t launch_cooperative(K kernel, size_t items, void** args, hipStream_t st, int threads = THREADS) {
   int per_cu = 0, dev = 0, cus = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, THREADS, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
   if (e != hipSuccess) return e;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
   const size_t g = std::max<size_t>(1, std::min<size_t>(items, (size_t)per_cu * cus));
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(grid1(g)), dim3(THREADS),
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(grid1(g)), dim3(threads),
                                     args, 0, st);
 }
 
@@ -98,6 +98,33 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
   const int S = (int)pl.S, N = (int)pl.N;
   switch (kind) {
     case L_FUSED: {
+      if constexpr (!is_f32<T>()) {
+        if (pl.c1 == 1 && pl.b2 <= 128 && !MA_NO_ASYNC) {
+          // copied-tile stages in one cooperative launch; both phases use
+          // the stage-1 wave count
+          const int nqs = pl.b2, ktb = pl.b2 <= 64 ? 64 : 128;
+          const int nw = D == 64 ? async_waves(nqs) : 4, qg = nw * 16;
+          Stage1Params p1{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
+                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
+                          pl.sc2, 1, pl.xlo};
+          Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
+                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
+                          pl.sc2, pl.xlo};
+          const size_t items = std::max<size_t>((size_t)S * pl.b1 * p1.nqg, (size_t)S * pl.b2 * p2.nqg);
+          void* args[] = {&p1, &p2};
+          hipError_t e = hipSuccess;
+#define MA_FA(NW, KTB) e = launch_cooperative(fused_async_kernel<D, NW, KTB, PRECISE>, items, args, st, NW * WAVE)
+          if constexpr (D == 64) {
+            if (nw == 8) { if (ktb == 64) MA_FA(8, 64); else MA_FA(8, 128); }
+            else { if (ktb == 64) MA_FA(4, 64); else MA_FA(4, 128); }
+          } else {
+            if (ktb == 64) MA_FA(4, 64); else MA_FA(4, 128);
+          }
+#undef MA_FA
+          if (e != hipSuccess) return e;
+          break;
+        }
+      }
       QbarParams pq{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt};
       const int nqs = pl.c1 * pl.b2;
       const int nq1 = stage1_nq<T, D>(nqs), qg1 = WAVES * nq1 * 16;
