@@ -34,6 +34,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 // (direct-to-LDS copies included): vmcnt(0), other counters untouched.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+
 // Copy 16 bytes at g into LDS at wave_base + 16 * lane (wave_base uniform).
 //
 // The copy is issued through inline assembly on purpose: the compiler then
@@ -351,38 +352,37 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
 // flat sequence of (item, chunk) units of its items, copying unit u+1 into
 // the other buffer while unit u computes.
 // ---------------------------------------------------------------------------
-template <int D, bool KLO, bool WITH_PV>
+template <int D, bool KLO, bool WITH_PV, int KC>
 struct Stage2AsyncSmem {
-  static constexpr int TILE = KT * SwzTile<D>::RB;
+  static constexpr int TILE = KC * SwzTile<D>::RB;
   static constexpr int HI = 0;
   static constexpr int LO = TILE;
   static constexpr int U = (KLO ? 2 : 1) * TILE;
   static constexpr int BUF = U + (WITH_PV ? TILE : 0);
 };
 
-template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE>
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT>
 struct Stage2Async {
-  typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV> SM0;
+  typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV, KC> SM0;
   static constexpr int STG = WITH_PV ? NW * WaveRows<D>::BYTES : 0;
-  static constexpr int LDS_BYTES = 2 * SM0::BUF + STG + 2 * KT * 4;
+  static constexpr int LDS_BYTES = 2 * SM0::BUF + STG + 2 * KC * 4;
 
   __device__ static void run(const Stage2Params& p, char* lds) {
   typedef bf16 T;
   constexpr bool KLO = split_x<T, PRECISE>();
   constexpr int QG = NW * NQ * 16;
-  typedef FlashCore<T, D, D, NQ, KT, false, WITH_PV, KLO, 0> Core;
+  typedef FlashCore<T, D, D, NQ, KC, false, WITH_PV, KLO, 0> Core;
   typedef typename Core::frag frag;
-  typedef Stage2AsyncSmem<D, KLO, WITH_PV> SM;
-  static_assert(NQ == 1, "one 16-query sub-tile per wave");
+  typedef Stage2AsyncSmem<D, KLO, WITH_PV, KC> SM;
   char* const buf_a = lds;
   char* const buf_b = lds + SM::BUF;
   char* const stage_rows = lds + 2 * SM::BUF;
   float* const bias_a = reinterpret_cast<float*>(lds + 2 * SM::BUF + STG);
-  float* const bias_b = bias_a + KT;
+  float* const bias_b = bias_a + KC;
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b2 * p.c1 * p.nqg;
-  const int nch = (p.nkeys + KT - 1) / KT;
+  const int nch = (p.nkeys + KC - 1) / KC;
   auto decode = [&](int item, int& sl, int& i, int& t, int& qg) {
     qg = item % p.nqg; item /= p.nqg;
     t = item % p.c1; item /= p.c1;
@@ -393,22 +393,25 @@ struct Stage2Async {
 
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
-  float hn = 0.f;               // bias of the unit in flight (last wave, one key a lane)
+  float hn[KC / WAVE];          // bias of the unit in flight (last wave, KC/64 keys a lane)
   auto issue = [&](int item, int ch, char* b) {
     int sl, i, t, qg;
     decode(item, sl, i, t, qg);
     const size_t xs = x_stride(p.b2, p.c1);
-    const size_t base = x_base(p.b1, p.b2, p.c1, p.c2, sl, t, i) + (size_t)ch * KT * xs;
-    const int nvalid = min(KT, p.nkeys - ch * KT);
+    const size_t base = x_base(p.b1, p.b2, p.c1, p.c2, sl, t, i) + (size_t)ch * KC * xs;
+    const int nvalid = min(KC, p.nkeys - ch * KC);
     const T* C = static_cast<const T*>(p.cx) + base * D;
-    SwzTile<D>::template load<KT, NW>(b + SM::HI, [&](int r) { return C + (size_t)r * xs * D; }, nvalid);
+    SwzTile<D>::template load<KC, NW>(b + SM::HI, [&](int r) { return C + (size_t)r * xs * D; }, nvalid);
     if constexpr (KLO)
-      SwzTile<D>::template load<KT, NW>(b + SM::LO, [&](int r) { return C + p.xlo + (size_t)r * xs * D; }, nvalid);
+      SwzTile<D>::template load<KC, NW>(b + SM::LO, [&](int r) { return C + p.xlo + (size_t)r * xs * D; }, nvalid);
     if constexpr (WITH_PV) {
       const T* U = static_cast<const T*>(p.ux) + base * D;
-      SwzTile<D>::template load<KT, NW>(b + SM::U, [&](int r) { return U + (size_t)r * xs * D; }, nvalid);
+      SwzTile<D>::template load<KC, NW>(b + SM::U, [&](int r) { return U + (size_t)r * xs * D; }, nvalid);
     }
-    if (wave == NW - 1) hn = p.h2x[base + (size_t)min(lane, nvalid - 1) * xs];
+    if (wave == NW - 1) {
+#pragma unroll
+      for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[base + (size_t)min(lane + WAVE * j, nvalid - 1) * xs];
+    }
     if (ch == 0)
       Core::fetch_queries([&](int n) { return stage2_qsrc<T, D>(p, sl, i, t, row_of(qg, n)); },
                           Q_INPUT, qn, qnl);
@@ -443,11 +446,14 @@ struct Stage2Async {
     T* Y = static_cast<T*>(p.y) + (size_t)out.sl * p.N * D;
     if constexpr (WITH_PV) {
       const AxisMap am = p.map.col_axis(out.i);
-      WaveRows<D>::put(stg, out.y[0]);
-      WaveRows<D>::drain(stg, [&](int r) -> T* {
-        const int l = out.l0 + r;
-        return l < out.lend ? Y + am.at(l) * D : nullptr;
-      });
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        WaveRows<D>::put(stg, out.y[n]);
+        WaveRows<D>::drain(stg, [&](int r) -> T* {
+          const int l = out.l0 + n * 16 + r;
+          return l < out.lend ? Y + am.at(l) * D : nullptr;
+        });
+      }
     }
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
@@ -463,7 +469,10 @@ struct Stage2Async {
   // Returns false after the last unit of this workgroup.
   auto unit = [&](const char* cur, float* bias, char* nxt) -> bool {
     wait_vmem();
-    if (wave == NW - 1) bias[lane] = hn;
+    if (wave == NW - 1) {
+#pragma unroll
+      for (int j = 0; j < KC / WAVE; ++j) bias[lane + WAVE * j] = hn[j];
+    }
     __syncthreads();              // cur landed everywhere; nobody reads nxt any more
     if (ch == 0) {
       core.init();
@@ -474,13 +483,13 @@ struct Stage2Async {
     if (nitem < nitems) issue(nitem, nchk, nxt);
     flush();
 
-    const int nvalid = min(KT, p.nkeys - ch * KT);
+    const int nvalid = min(KC, p.nkeys - ch * KC);
     core.scores_v(SwzKeys<D>(cur + SM::HI, cur + SM::LO), 0, Core::MT);
-    if (nvalid == KT) core.template softmax_step<true, false>(bias, p.sc2, 0, nvalid);
+    if (nvalid == KC) core.template softmax_step<true, false>(bias, p.sc2, 0, nvalid);
     else core.template softmax_step<true, true>(bias, p.sc2, 0, nvalid);
     if constexpr (WITH_PV) {
       const SwzValuesT<D> vv(cur + SM::U, cur + SM::U);
-      if (nvalid == KT) core.template pv<false>(vv, 0, nvalid);
+      if (nvalid == KC) core.template pv<false>(vv, 0, nvalid);
       else core.template pv<true>(vv, 0, nvalid);
     }
     if (ch == nch - 1) {
@@ -518,9 +527,9 @@ struct Stage2Async {
   }
 };
 
-template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE>
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT>
 __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p) {
-  typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE> S;
+  typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE, KC> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
 }

@@ -35,6 +35,7 @@ template <typename T> constexpr bool is_f32() { return std::is_same<T, float>::v
 #define MA_NO_ASYNC 0
 #endif
 
+
 // Waves per workgroup of the direct-to-LDS kernels: 8 (128 query rows) unless
 // 4 (64 rows) pads fewer rows.
 inline int async_waves(int rows) {
