@@ -178,12 +178,13 @@ inline size_t resident_slots(K kernel, int threads, size_t items) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1 of the first step of untiled Monarch, whole block in one tile
-// (b2 <= KTB).  The queries of block k are then the rows (k, i) of Q, the
-// same grid rows as its keys, so they are copied into LDS with the keys and
-// values.  Item = (slice, block k, query group of NW*16 slots); NW waves of
-// 16 queries each.  (Later steps and tiled problems read fp32 query rows and
-// use the register-staged kernels.)
+// Stage 1 of the first step, whole block in one tile (b2 <= KTB).  The
+// queries of block k are then bf16 rows: the rows (k, i) of Q (the same grid
+// rows as its keys) and, when tiled, the tile means of the other row tiles
+// kept in bf16 for the plain c path; they are copied into LDS with the keys
+// and values.  Item = (slice, block k, query group of NW*16 slots
+// t*b2 + i); NW waves of 16 queries each.  (Later steps and the split c path
+// read fp32 query rows and use the register-staged kernels.)
 // ---------------------------------------------------------------------------
 template <int D, int NW, int KTB, bool WITH_U>
 struct Stage1AsyncSmem {
@@ -221,8 +222,16 @@ struct Stage1Async {
       const T* V = static_cast<const T*>(p.v) + (size_t)sl * p.N * D;
       SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + am.at(r) * D; }, p.b2);
     }
+    // slot = t*b2 + i: row (k, i) of Q in the own row tile t = k / rt, the
+    // tile mean of (t, i) elsewhere (tiled first step)
     const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
-    SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) { return Q + am.at(min(qg * QG + r, p.nqs - 1)) * D; }, QG);
+    const T* QB = p.qbar_lp ? static_cast<const T*>(p.qbar_lp) + (size_t)sl * p.c1 * p.b2 * D : Q;
+    const int town = k / p.rt;
+    SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) {
+      const int slot = min(qg * QG + r, p.nqs - 1);
+      const int t = slot / p.b2, i = slot - t * p.b2;
+      return t == town ? Q + am.at(i) * D : QB + ((size_t)t * p.b2 + i) * D;
+    }, QG);
   };
 
   Core core;
@@ -243,7 +252,7 @@ struct Stage1Async {
   auto collect = [&](int qg, int k, int sl, int s) {
     float lse2[1], h2[1];
     core.finish(lse2, h2, p.sc2);
-    out.xbase = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, 0, 0);   // untiled: slot = i
+    out.xbase = x_row(p.b1, p.b2, p.c1, p.c2, sl, k, s, 0, 0);   // slot t*b2 + i -> xbase + slot
     out.qg0 = qg * QG;
     out.h2 = h2[0];
     out.lse = lse2[0];

@@ -177,6 +177,7 @@ struct QbarParams {
   const void* q; float* qbar;   // qbar [S, c1, b2, D] fp32
   GridMap map;
   int S, N, b2, c1, rt;
+  void* qbar_lp;                // optional copy in the input type, same layout
 };
 
 template <typename T, int D>
@@ -207,7 +208,9 @@ struct QbarItem {
     if (threadIdx.x < D) {
       float s = 0.f;
       for (int r = 0; r < RL; ++r) s += part[r][threadIdx.x];
-      p.qbar[(((size_t)sl * p.c1 + t) * p.b2 + i) * D + threadIdx.x] = s / (float)p.rt;
+      const size_t at = (((size_t)sl * p.c1 + t) * p.b2 + i) * D + threadIdx.x;
+      p.qbar[at] = s / (float)p.rt;
+      if (p.qbar_lp) static_cast<T*>(p.qbar_lp)[at] = from_f32<T>(s / (float)p.rt);
     }
     __syncthreads();
   }

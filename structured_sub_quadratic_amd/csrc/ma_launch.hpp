@@ -43,6 +43,14 @@ inline int async_waves(int rows) {
   return pad8 <= pad4 ? 8 : 4;
 }
 
+// Stage 2: at head_dim 128 the 4-wave kernel holds one wave a SIMD (it
+// needs more than 256 registers), so 8 waves win whenever there are more
+// than 64 query rows, even with up to a quarter of them padding.
+template <int D> inline int stage2_waves(int rows) {
+  if (rows <= 64) return 4;
+  return D == 128 ? 8 : async_waves(rows);
+}
+
 template <class K, class P>
 void launch_persistent(K kernel, int threads, size_t items, const P& p, hipStream_t st) {
   const size_t g = resident_slots(kernel, threads, items);
@@ -96,6 +104,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
   float* lse2 = reinterpret_cast<float*>(ws + pl.off_lse2);
   float* qtil = pl.need_qtil ? reinterpret_cast<float*>(ws + pl.off_qtil) : nullptr;
   float* qbar = pl.need_qbar ? reinterpret_cast<float*>(ws + pl.off_qbar) : nullptr;
+  void* qbar_lp = (pl.need_qbar && pl.c1 > 1 && !pl.precise) ? ws + pl.off_qbar_lp : nullptr;
   const int S = (int)pl.S, N = (int)pl.N;
   switch (kind) {
     case L_FUSED: {
@@ -163,7 +172,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       break;
     }
     case L_QBAR: {
-      QbarParams p{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt};
+      QbarParams p{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt, qbar_lp};
       hipLaunchKernelGGL((qbar_kernel<T, D>), dim3(grid1((size_t)S * pl.c1 * pl.b2)), dim3(256), 0, st, p);
       break;
     }
@@ -172,15 +181,16 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const int nqs = pl.c1 * pl.b2;
       if constexpr (!is_f32<T>()) {
         const int ktb = pl.b2 <= 64 ? 64 : 128;
-        // the copied-tile kernel serves the untiled first step (queries are
-        // rows of Q); fp32 query sources stay on the register-staged kernels
-        if (pl.b2 <= 128 && step == 0 && pl.c1 == 1 && !MA_NO_ASYNC) {
+        // the copied-tile kernel serves the first step when its queries are
+        // bf16 rows: rows of Q, and with tiles the bf16 tile means of the
+        // plain c path; fp32 query sources stay on the register-staged kernels
+        if (pl.b2 <= 128 && step == 0 && (pl.c1 == 1 || qbar_lp) && !MA_NO_ASYNC) {
           // head_dim 128 keeps 4 waves (two waves a SIMD would spill the
           // K|V sums)
           const int nw = D == 64 ? async_waves(nqs) : 4, qg = nw * 16;
           Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
-                         pl.sc2, step == 0 ? 1 : 0, pl.xlo};
+                         pl.sc2, step == 0 ? 1 : 0, pl.xlo, qbar_lp};
           const size_t items = (size_t)S * pl.b1 * p.nqg;
           const bool last = kind == L_STAGE1_LAST;
 #define MA_A1(NW, KTB, U) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE>, NW * WAVE, items, p, st)
@@ -242,7 +252,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     case L_STAGE2_LAST: {
       if constexpr (!is_f32<T>()) {
         if (!MA_NO_ASYNC) {
-          const int nw = async_waves(pl.rt), qg = nw * 16;
+          const int nw = stage2_waves<D>(pl.rt), qg = nw * 16;
           Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
                          pl.sc2, pl.xlo};

@@ -30,7 +30,7 @@ struct Plan {
   size_t elt, xc_elt;
   size_t xlo;          // elements from the hi plane of split c to its lo plane (0: not split)
   bool precise;
-  size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, total;
+  size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, off_qbar_lp, total;
   bool need_qbar, need_qtil;
   bool fused;        // single cooperative launch for T = 1
 };

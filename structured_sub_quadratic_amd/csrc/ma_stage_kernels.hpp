@@ -380,6 +380,7 @@ struct Stage1Params {
   float sc2;
   int first_step;
   size_t xlo;
+  const void* qbar_lp;   // tile means in the input type (first tiled step, plain c path)
 };
 
 template <typename T, int D, int DV, int KTB>

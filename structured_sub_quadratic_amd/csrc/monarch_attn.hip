@@ -73,6 +73,9 @@ Plan make_plan(const ma_problem* p) {
   pl.off_lse2 = off; off = align_up(off + (size_t)pl.S * pl.N * 4);
   pl.off_qtil = off; if (pl.need_qtil) off = align_up(off + rows * pl.D * 4);
   pl.off_qbar = off; if (pl.need_qbar) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * 4);
+  // tile means in bf16 for the copied-tile first step of the plain c path
+  pl.off_qbar_lp = off;
+  if (pl.need_qbar && pl.c1 > 1 && !pl.precise) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * pl.elt);
   pl.total = off;
   return pl;
 }
