@@ -103,7 +103,8 @@ typedef enum {
 #define MA_FLAG_PRECISE_AGGREGATE 8u
 
 typedef struct {
-  int64_t batch, heads, seq_len, head_dim;  /* Q,K,V,Y: [batch, heads, seq_len, head_dim] */
+  int64_t batch, heads, seq_len, head_dim;  /* Q, Y: [batch, heads, seq_len, head_dim];
+                                               K, V: [batch, kv_heads, seq_len, head_dim] */
   int32_t b1, b2;      /* seq_len == b1*b2; b1 = number of blocks (the pages' m),
                           b2 = block length (the pages' b) */
   int32_t c1, c2;      /* sub-tiles per block; 1,1 = untiled Monarch; c1 | b1, c2 | b2 */
@@ -113,6 +114,12 @@ typedef struct {
   int32_t layout;      /* ma_layout */
   int32_t f, h, w;     /* video latent (layout != FLAT): f*h*w == seq_len */
   uint32_t flags;      /* MA_FLAG_* */
+  int32_t kv_heads;    /* heads of K and V; 0 means heads.  Grouped-query
+                          attention: heads % kv_heads == 0 and query head h
+                          uses K/V head h / (heads / kv_heads) (MonarchAttention
+                          OpenReview author response on GQA/MLA: the method
+                          applies per query head, stage 1 reading the shared
+                          K/V of its group) */
 } ma_problem;
 
 /* Optional exports (device pointers, each may be NULL), always fp32/fp64.

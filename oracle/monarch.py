@@ -309,9 +309,12 @@ def dense_from_factors(L, R, b1, b2, c1=1, c2=1):
 
 def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
             fhw=None, cols=None, tiled=None, slices=None):
-    """MonarchAttention on [B, H, N, d] inputs (any float dtype, upcast to
-    float64).  The layout permutation maps token order to the b1 x b2 grid
-    (oracle.layouts); Y is mapped back.
+    """MonarchAttention on [B, H, N, d] queries and [B, Hkv, N, d] keys and
+    values (any float dtype, upcast to float64).  Hkv < H is grouped-query
+    attention: query head h uses key/value head h // (H // Hkv), and the
+    method runs per query head unchanged (MonarchAttention, OpenReview author
+    response on GQA/MLA: a direct transfer).  The layout permutation maps
+    token order to the b1 x b2 grid (oracle.layouts); Y is mapped back.
 
     cols: optional columns i to compute (Y is then NaN outside them).
     slices: optional list of (b, h) pairs to compute (others left NaN).
@@ -326,6 +329,10 @@ def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
     V = np.asarray(V, dtype=np.float64)
     B, H, N, d = Q.shape
     dv = V.shape[-1]
+    Hkv = K.shape[1]
+    if K.shape[:3] != (B, Hkv, N) or V.shape[:3] != (B, Hkv, N) or H % Hkv:
+        raise ValueError("K, V must be [B, Hkv, N, .] with Hkv dividing H")
+    group = H // Hkv
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     grid = grid_index(N, b1, b2, layout, fhw)
     if tiled is None:
@@ -344,7 +351,8 @@ def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
         Rs = np.full((B, H, b1, nc, b2), np.nan)
     ft = np.full((B, H, 2 * steps), np.nan)
     for (b, h) in sel:
-        qg, kg, vg = (to_grid(X[b, h], grid) for X in (Q, K, V))
+        qg = to_grid(Q[b, h], grid)
+        kg, vg = (to_grid(X[b, h // group], grid) for X in (K, V))
         if tiled:
             r = forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=colsel)
         else:

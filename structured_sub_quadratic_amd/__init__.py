@@ -41,8 +41,10 @@ def _dtype_code(dtype):
 
 
 def make_problem(batch, heads, seq_len, head_dim, b1, b2, steps=1, c1=1, c2=1, scale=None,
-                 dtype="bf16", layout="flat", fhw=None, flags=0):
-    """Build the C problem descriptor.  dtype: "f32"/"bf16" or a torch dtype."""
+                 dtype="bf16", layout="flat", fhw=None, flags=0, kv_heads=0):
+    """Build the C problem descriptor.  dtype: "f32"/"bf16" or a torch dtype.
+    kv_heads: heads of K and V (0: heads); grouped-query attention when
+    smaller."""
     if not isinstance(dtype, int):
         dtype = {"f32": _lib.MA_F32, "bf16": _lib.MA_BF16}.get(dtype, None) \
             if isinstance(dtype, str) else _dtype_code(dtype)
@@ -51,7 +53,7 @@ def make_problem(batch, heads, seq_len, head_dim, b1, b2, steps=1, c1=1, c2=1, s
     f, h, w = fhw if fhw is not None else (0, 0, 0)
     return _lib.MAProblem(batch, heads, seq_len, head_dim, b1, b2, c1, c2, steps,
                           0.0 if scale is None else float(scale), dtype, LAYOUTS[layout],
-                          f, h, w, flags)
+                          f, h, w, flags, kv_heads)
 
 
 def workspace_size(problem):
@@ -101,14 +103,18 @@ def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, worksp
             raise ValueError(f"{name} must be a HIP device tensor")
         if t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [batch, heads, seq_len, head_dim] tensor")
-    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k, v must share shape and dtype")
+    if k.shape != v.shape or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("k and v must share shape, and q, k, v their dtype")
     B, H, N, D = q.shape
+    Hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, N, D) or Hkv < 1 or H % Hkv:
+        raise ValueError("k, v must be [batch, kv_heads, seq_len, head_dim] with kv_heads | heads")
     flags = (MA_FLAG_FORCE_STAGED if force_staged else 0) | \
         (MA_FLAG_FAST_AGGREGATE if fast_aggregate else 0) | \
         (MA_FLAG_FORCE_FUSED if force_fused else 0) | \
         (MA_FLAG_PRECISE_AGGREGATE if precise_aggregate else 0)
-    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags)
+    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags,
+                        kv_heads=Hkv)
     ws_bytes = workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)

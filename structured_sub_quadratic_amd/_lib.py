@@ -30,6 +30,7 @@ class MAProblem(ctypes.Structure):
         ("layout", ctypes.c_int32),
         ("f", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("kv_heads", ctypes.c_int32),
     ]
 
 

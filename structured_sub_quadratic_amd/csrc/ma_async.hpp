@@ -216,10 +216,11 @@ struct Stage1Async {
   auto issue = [&](int item, char* b) {
     const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
     const AxisMap am = p.map.row_axis(k);
-    const T* K = static_cast<const T*>(p.k) + (size_t)sl * p.N * D;
+    const int kvs = kv_slice(sl, p.heads, p.group);
+    const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
     SwzTile<D>::template load<KTB, NW>(b, [&](int r) { return K + am.at(r) * D; }, p.b2);
     if constexpr (WITH_U) {
-      const T* V = static_cast<const T*>(p.v) + (size_t)sl * p.N * D;
+      const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
       SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + am.at(r) * D; }, p.b2);
     }
     // slot = t*b2 + i: row (k, i) of Q in the own row tile t = k / rt, the

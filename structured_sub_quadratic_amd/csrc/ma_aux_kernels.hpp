@@ -230,6 +230,7 @@ struct RExportParams {
   int S, N, b1, b2, c1, c2, sw, rt, D;
   float sc2;
   int first_step;
+  int heads, group;     // K slice of query slice sl: kv_slice(sl, heads, group)
 };
 
 template <typename T>
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256) void r_export_kernel(RExportParams p) {
   const int sl = r / p.b1;
   const int s = j / p.sw;
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * p.D;
-  const T* K = static_cast<const T*>(p.k) + (size_t)sl * p.N * p.D;
+  const T* K = static_cast<const T*>(p.k) + (size_t)kv_slice(sl, p.heads, p.group) * p.N * p.D;
   const T* krow = K + (size_t)p.map.token(k, j) * p.D;
   float dot = 0.f;
   if (p.first_step && t == k / p.rt) {

@@ -34,6 +34,12 @@ __device__ inline size_t x_base(int b1, int b2, int c1, int c2, int sl, int t, i
 }
 __device__ inline size_t x_stride(int b2, int c1) { return (size_t)c1 * b2; }
 
+// K/V slice of query slice sl (= batch * heads + head) when groups of `group`
+// consecutive query heads share one K/V head.
+__device__ inline int kv_slice(int sl, int heads, int group) {
+  return group == 1 ? sl : (sl / heads) * (heads / group) + (sl % heads) / group;
+}
+
 __device__ inline void split_bf16(float x, bf16& hi, bf16& lo) {
   hi = (bf16)x;
   lo = (bf16)(x - (float)hi);

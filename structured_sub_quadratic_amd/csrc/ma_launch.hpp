@@ -117,6 +117,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           Stage1Params p1{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                           S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
                           pl.sc2, 1, pl.xlo};
+          p1.heads = pl.heads;
+          p1.group = pl.group;
           Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
                           S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
                           pl.sc2, pl.xlo};
@@ -141,6 +143,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       Stage1Params p1{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                       S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg1 - 1) / qg1,
                       pl.sc2, 1, pl.xlo};
+      p1.heads = pl.heads;
+      p1.group = pl.group;
       const int nq2 = stage2_nq<T, D>(pl.rt), qg2 = WAVES * nq2 * 16;
       Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
                       S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg2 - 1) / qg2,
@@ -191,6 +195,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
                          pl.sc2, step == 0 ? 1 : 0, pl.xlo, qbar_lp};
+          p.heads = pl.heads;
+          p.group = pl.group;
           const size_t items = (size_t)S * pl.b1 * p.nqg;
           const bool last = kind == L_STAGE1_LAST;
 #define MA_A1(NW, KTB, U) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE>, NW * WAVE, items, p, st)
@@ -209,6 +215,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                      S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
                      pl.sc2, step == 0 ? 1 : 0, pl.xlo};
+      p.heads = pl.heads;
+      p.group = pl.group;
       const size_t items1 = (size_t)S * pl.b1 * p.nqg;
       const dim3 grid(grid1(items1));
       const bool ktb64 = pl.b2 <= 64 || (is_f32<T>() && D == 128);
@@ -309,6 +317,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     case L_EXPORT_R: {
       RExportParams p{b.q, b.k, qtil, qbar, lser, b.R, pl.map, S, N, pl.b1, pl.b2, pl.c1, pl.c2,
                       pl.sw, pl.rt, (int)pl.D, pl.sc2, step == 0 ? 1 : 0};
+      p.heads = pl.heads;
+      p.group = pl.group;
       const size_t total = (size_t)S * pl.b1 * pl.b2 * pl.c1 * pl.b2;
       hipLaunchKernelGGL(r_export_kernel<T>, dim3(grid1((total + 255) / 256)), dim3(256), 0, st, p);
       break;

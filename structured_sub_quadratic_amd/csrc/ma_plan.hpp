@@ -23,6 +23,7 @@ inline int max_segment(const ma_problem* p) {
 
 struct Plan {
   int64_t S, N, D;
+  int heads, group;    // query heads; query heads per K/V head
   int b1, b2, c1, c2, sw, rt, T;
   int dtype;
   float scale, sc2;

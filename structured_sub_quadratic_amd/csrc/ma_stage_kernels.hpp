@@ -381,6 +381,7 @@ struct Stage1Params {
   int first_step;
   size_t xlo;
   const void* qbar_lp;   // tile means in the input type (first tiled step, plain c path)
+  int heads, group;      // K/V slice of query slice sl: kv_slice(sl, heads, group)
 };
 
 template <typename T, int D, int DV, int KTB>
@@ -532,8 +533,9 @@ struct Stage1Item {
     const int qg = id % p.nqg; id /= p.nqg;
     const int k = id % p.b1; id /= p.b1;
     const int sl = id;
-    const T* K = static_cast<const T*>(p.k) + (size_t)sl * p.N * D;
-    const T* Vv = static_cast<const T*>(p.v) + (size_t)sl * p.N * D;
+    const int kvs = kv_slice(sl, p.heads, p.group);
+    const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
+    const T* Vv = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
     const bool whole = p.b2 <= KTB;
     const int mode = stage1_qmode(p);
@@ -784,8 +786,9 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
   typename Core::QLo qnl;
   auto fetch = [&](int item) {
     const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
-    keys.load(p, static_cast<const T*>(p.k) + (size_t)sl * p.N * D,
-              static_cast<const T*>(p.v) + (size_t)sl * p.N * D, k, 0, p.b2);
+    const int kvs = kv_slice(sl, p.heads, p.group);
+    keys.load(p, static_cast<const T*>(p.k) + (size_t)kvs * p.N * D,
+              static_cast<const T*>(p.v) + (size_t)kvs * p.N * D, k, 0, p.b2);
     Core::fetch_queries([&](int n) {
       return stage1_qsrc<T, D>(p, sl, k, qg * QG + wave * NQ * 16 + n * 16 + lane % 16, 0);
     }, mode, qn, qnl);

@@ -34,6 +34,8 @@ ma_status validate_problem(const ma_problem* p) {
     }
     if (e1 != p->b1 || e2 != p->b2) return MA_ERR_INVALID_ARGUMENT;
   }
+  const int64_t kvh = p->kv_heads ? p->kv_heads : p->heads;
+  if (kvh < 1 || kvh > p->heads || p->heads % kvh != 0) return MA_ERR_INVALID_ARGUMENT;
   if (p->head_dim != 64 && p->head_dim != 128) return MA_ERR_UNSUPPORTED;
   if (p->b2 / p->c2 > max_segment(p)) return MA_ERR_UNSUPPORTED;
   const int64_t slices = p->batch * p->heads;
@@ -44,6 +46,8 @@ ma_status validate_problem(const ma_problem* p) {
 Plan make_plan(const ma_problem* p) {
   Plan pl;
   pl.S = p->batch * p->heads;
+  pl.heads = (int)p->heads;
+  pl.group = (int)(p->heads / (p->kv_heads ? p->kv_heads : p->heads));
   pl.N = p->seq_len;
   pl.D = p->head_dim;
   pl.b1 = p->b1; pl.b2 = p->b2; pl.c1 = p->c1; pl.c2 = p->c2;
@@ -96,13 +100,14 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(y, 16))
     return MA_ERR_INVALID_ARGUMENT;
   const size_t tbytes = (size_t)pl.S * pl.N * pl.D * pl.elt;
-  if (overlaps(y, tbytes, q, tbytes) || overlaps(y, tbytes, k, tbytes) || overlaps(y, tbytes, v, tbytes))
+  const size_t kvbytes = tbytes / pl.group;
+  if (overlaps(y, tbytes, q, tbytes) || overlaps(y, tbytes, k, kvbytes) || overlaps(y, tbytes, v, kvbytes))
     return MA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < pl.total) return MA_ERR_WORKSPACE_TOO_SMALL;
   if (pl.total > 0) {
     if (!workspace || misaligned(workspace, ALIGN)) return MA_ERR_INVALID_ARGUMENT;
-    if (overlaps(workspace, pl.total, q, tbytes) || overlaps(workspace, pl.total, k, tbytes) ||
-        overlaps(workspace, pl.total, v, tbytes) || overlaps(workspace, pl.total, y, tbytes))
+    if (overlaps(workspace, pl.total, q, tbytes) || overlaps(workspace, pl.total, k, kvbytes) ||
+        overlaps(workspace, pl.total, v, kvbytes) || overlaps(workspace, pl.total, y, tbytes))
       return MA_ERR_INVALID_ARGUMENT;
   }
   Bufs b{q, k, v, y, static_cast<char*>(workspace), nullptr, nullptr, nullptr, nullptr};

@@ -29,10 +29,12 @@ def _gpu():
 
 
 def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective"),
-               noise=None, tol=None, **kw):
+               noise=None, tol=None, kv_heads=None, **kw):
     all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     slices = all_slices if slices is None else slices
     Q, K, V = make_inputs(cfg, noise_scale=noise)
+    if kv_heads is not None:        # grouped-query attention: keep the first kv_heads
+        K, V = (np.ascontiguousarray(X[:, :kv_heads]) for X in (K, V))
     y, ex = run_hip(cfg, Q, K, V, exports=exports, **kw)
     ref = oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
                          layout=cfg.layout, fhw=cfg.fhw, cols=cols, slices=slices)
@@ -220,6 +222,36 @@ def test_launch_plan_fused_vs_staged():
     assert ma.launch_names(p) == ["fused_t1"]
     p = ma.make_problem(1, 12, 16384, 64, 128, 128)
     assert ma.launch_names(p) == ["stage1_last", "stage2_last"]
+
+
+# ------------------------------------------------ grouped-query attention
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="f32", d=64, c=(1, 1), steps=1, kvh=1),
+    dict(dtype="f32", d=128, c=(2, 1), steps=2, kvh=2),
+    dict(dtype="bf16", d=64, c=(1, 1), steps=1, kvh=2),
+    dict(dtype="bf16", d=128, c=(1, 1), steps=2, kvh=1),
+    dict(dtype="bf16", d=64, c=(2, 2), steps=1, kvh=2),
+    dict(dtype="bf16", d=128, c=(2, 2), steps=2, kvh=4),
+])
+def test_grouped_query_attention(case):
+    """K, V with fewer heads than Q: query head h reads K/V head
+    h // (heads / kv_heads), on the staged path and, for T = 1, the fused one."""
+    cfg = WorkloadConfig("case", f"gqa {case}", batch=2, heads=4, seq_len=70 * 52,
+                         head_dim=case["d"], b1=70, b2=52, steps=case["steps"], dtype=case["dtype"],
+                         data="normed", seed=31, c1=case["c"][0], c2=case["c"][1])
+    y, _, _ = check_case(cfg, kv_heads=case["kvh"])
+    if case["steps"] == 1:
+        y_f, _, _ = check_case(cfg, kv_heads=case["kvh"], force_fused=True)
+        assert np.abs(y_f - y).max() <= 1e-6 * np.abs(y).max()
+
+
+def test_grouped_query_attention_n16k_sampled():
+    """The n16k shape with 12 query heads over 4 K/V heads, in the default
+    launch configuration."""
+    cfg = WORKLOADS["n16k"]
+    check_case(cfg, slices=[(0, 0), (0, 5), (0, 11)], cols=[0, 64, 127],
+               exports=("L", "R", "lse"), kv_heads=4)
 
 
 # ------------------------------------------------ benchmark workloads, sampled

@@ -628,3 +628,32 @@ def test_driver_layout_roundtrip():
         ref = om.forward_untiled(Q[0, h][g], K[0, h][g], V[0, h][g], 2, 1 / math.sqrt(5))
         np.testing.assert_allclose(r["y"][0, h][g], ref["y"], atol=1e-14)
         np.testing.assert_allclose(r["lse"][0, h][g], ref["lse"], atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention (MonarchAttention, OpenReview author response on
+# GQA/MLA: the method applies per query head; stage 1 reads the shared K/V of
+# the head's group).  Pinned against the plain multi-head oracle on K/V
+# repeated per group, and shown sensitive to the head-to-group map.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tiles,steps", [((1, 1), 2), ((2, 2), 1)])
+def test_gqa_equals_repeated_kv(tiles, steps):
+    rng = np.random.default_rng(5)
+    B, H, Hkv, b1, b2, d = 1, 6, 2, 6, 4, 8
+    N = b1 * b2
+    Q = rng.standard_normal((B, H, N, d))
+    K = rng.standard_normal((B, Hkv, N, d))
+    V = rng.standard_normal((B, Hkv, N, d))
+    r = oracle.forward(Q, K, V, b1, b2, steps, *tiles)
+    group = H // Hkv
+    rep = oracle.forward(Q, np.repeat(K, group, axis=1), np.repeat(V, group, axis=1), b1, b2,
+                         steps, *tiles)
+    assert np.allclose(r["y"], rep["y"], rtol=0, atol=1e-12)
+    # consecutive query heads share a K/V head: cycling the K/V heads instead
+    # gives a different result
+    cyc = oracle.forward(Q, np.tile(K, (1, group, 1, 1)), np.tile(V, (1, group, 1, 1)), b1, b2,
+                         steps, *tiles)
+    assert not np.allclose(r["y"], cyc["y"], rtol=0, atol=1e-6)
+    with pytest.raises(ValueError):
+        oracle.forward(Q, K[:, :1].repeat(4, axis=1), V[:, :1].repeat(4, axis=1), b1, b2, steps)
