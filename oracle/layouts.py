@@ -34,18 +34,30 @@ LAYOUTS = {
 }
 
 
-def grid_index(seq_len, b1, b2, layout="flat", fhw=None):
+def grid_index(seq_len, b1, b2, layout="flat", fhw=None, pad="post"):
     """Return an int array G of shape [b1, b2]: G[l, i] is the token at grid
-    position (l, i).
+    position (l, i), or -1 for a padding position.
 
-    layout "flat": G[l, i] = l*b2 + i.  Otherwise fhw = (f, h, w) with
-    f*h*w == seq_len, and the token grid arange(N).reshape(f, h, w) is
-    transposed so that the b1 axes come first, then reshaped to [b1, b2].
+    layout "flat": G[l, i] = l*b2 + i.  A flat sequence with b1*b2 > seq_len
+    is padded to the grid ([MA] OpenReview author response on block sizes: b
+    is chosen, m = ceil(N/b), and padding goes before the sequence -- "pre",
+    as for ViT's leading class token -- or after it -- "post"): with P =
+    b1*b2 - seq_len padding positions, G[l, i] = l*b2 + i - P for "pre" and
+    l*b2 + i for "post", and positions outside [0, seq_len) are padding.
+    Otherwise fhw = (f, h, w) with f*h*w == seq_len, and the token grid
+    arange(N).reshape(f, h, w) is transposed so that the b1 axes come first,
+    then reshaped to [b1, b2].
     """
+    if layout == "flat":
+        if b1 * b2 < seq_len:
+            raise ValueError("b1*b2 must be at least seq_len")
+        if pad not in ("pre", "post"):
+            raise ValueError("pad must be 'pre' or 'post'")
+        g = np.arange(b1 * b2) - (b1 * b2 - seq_len if pad == "pre" else 0)
+        g[(g < 0) | (g >= seq_len)] = -1
+        return g.reshape(b1, b2)
     if b1 * b2 != seq_len:
         raise ValueError("b1*b2 must equal seq_len")
-    if layout == "flat":
-        return np.arange(seq_len).reshape(b1, b2)
     if layout not in LAYOUTS:
         raise ValueError(f"unknown layout {layout!r}")
     f, h, w = fhw
@@ -62,12 +74,18 @@ def grid_index(seq_len, b1, b2, layout="flat", fhw=None):
 
 
 def to_grid(x, grid):
-    """[N, ...] in token order -> [b1, b2, ...] in grid order."""
-    return x[grid]
+    """[N, ...] in token order -> [b1, b2, ...] in grid order (zeros at
+    padding positions)."""
+    out = x[np.maximum(grid, 0)]
+    out[grid < 0] = 0
+    return out
 
 
 def from_grid(xg, grid):
-    """[b1, b2, ...] in grid order -> [N, ...] in token order."""
-    out = np.empty((grid.size,) + xg.shape[2:], dtype=xg.dtype)
-    out[grid.reshape(-1)] = xg.reshape((grid.size,) + xg.shape[2:])
+    """[b1, b2, ...] in grid order -> [N, ...] in token order (padding
+    positions dropped)."""
+    real = grid.reshape(-1) >= 0
+    n = int(real.sum())
+    out = np.empty((n,) + xg.shape[2:], dtype=xg.dtype)
+    out[grid.reshape(-1)[real]] = xg.reshape((grid.size,) + xg.shape[2:])[real]
     return out

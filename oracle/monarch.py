@@ -63,6 +63,16 @@ Readings where the pages are silent:
     q[l,i] over the rows l of tile t (the eps -> 0 limit of
     (1-eps) I + eps * uniform).  The same fallback is used whenever beta is
     exactly zero.
+  * padding ([MA] author response on block sizes: m = ceil(N/b), pre- or
+    post-padding): the objective is the one of the real N x N attention, so
+    it sums over real query rows only and M puts no mass on padding keys.
+    Hence R rows are softmaxes over the real keys of a segment, padding
+    rows carry no L row (exported as zeros), and alpha, beta and the tile
+    means run over real rows.  L0 is the block identity on real rows, so a
+    padding position (k, i) has beta = 0 at the first R-update and takes the
+    fallback: the mean of q over the real rows of its tile and column (zero
+    if there are none; its R row then weighs nothing).  Every segment must
+    hold a real key.
 
 Parity pins (tests/test_oracle_pins.py): dense product P^T L P R on tiny
 grids, simplex rows, non-decreasing objective bounded by sum logsumexp, dense
@@ -100,12 +110,31 @@ def _objective_untiled(q, C, HR, L):
     return float(np.sum(L * w) + np.sum(row_entropy(L, axis=-1)))
 
 
-def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False):
+def _real_mean(q, rows):
+    """Mean of q[l, i] over the real rows l (rows[l, i] True) of each column
+    i; zero for a column without real rows.  q [nr, nc, d], rows [nr, nc]."""
+    n = rows.sum(axis=0)
+    tot = np.sum(np.where(rows[..., None], q, 0.0), axis=0)
+    return tot / np.maximum(n, 1)[:, None]
+
+
+def _check_real(real, b1, b2, c2=1):
+    real = np.ones((b1, b2), bool) if real is None else np.asarray(real, bool)
+    if real.shape != (b1, b2):
+        raise ValueError("real must be [b1, b2]")
+    if not real.reshape(b1, c2, b2 // c2).any(axis=-1).all():
+        raise ValueError("every key segment needs a real key")
+    return real
+
+
+def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False, real=None):
     """One (batch, head) slice of untiled MonarchAttention.
 
     qg, kg, vg: [b1, b2, d] in grid order (float64).  cols: optional list of
     columns i to compute (the method is independent across i: R rows [., i, .]
-    and L[i] touch only column i of the queries, and all keys).
+    and L[i] touch only column i of the queries, and all keys).  real:
+    optional [b1, b2] bool, False at padding positions (their rows of qg, kg,
+    vg are ignored).
 
     Returns dict:
       y       [b1, nc, d]   output rows (l, i) for the selected columns
@@ -119,17 +148,22 @@ def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False):
     if steps < 1:
         raise ValueError("steps must be >= 1")
     cols = np.arange(b2) if cols is None else np.asarray(cols)
-    q = scale * qg[:, cols, :]               # q[l, i], sigma folded in
+    real = _check_real(real, b1, b2)
+    rq = real[:, cols]                       # real query rows (l, i)
+    q = scale * np.where(rq[..., None], qg[:, cols, :], 0.0)   # q[l, i], sigma folded in
     nc = q.shape[1]
+    qmean = _real_mean(q, rq)                # [i, d], the zero-weight fallback
 
-    # L0 = block identity: L0[i, l, k] = [l == k], hence qt[k, i] = q[k, i].
-    L = np.broadcast_to(np.eye(b1), (nc, b1, b1)).copy()
-    qt = q.copy()
+    # L0 = block identity on real rows: L0[i, l, k] = [l == k], hence
+    # qt[k, i] = q[k, i]; a padding row (k, i) has beta = 0 -> fallback.
+    L = np.broadcast_to(np.eye(b1), (nc, b1, b1)) * rq.T[:, :, None]
+    qt = np.where(rq[..., None], q, qmean[None])
     f_trace, hist = [], []
 
     for step in range(steps):
-        # R-update: R[k,i,:] = softmax_j(qt[k,i] . k[k,j])
+        # R-update: R[k,i,:] = softmax over the real keys j of qt[k,i] . k[k,j]
         z = np.matmul(qt, kg.transpose(0, 2, 1))          # z[k, i, j]
+        z = np.where(real[:, None, :], z, -np.inf)
         R = softmax(z, axis=-1)
         HR = row_entropy(R, axis=-1)                       # H_R[k, i]
         C = np.matmul(R, kg)                               # c[k, i]
@@ -139,7 +173,7 @@ def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False):
 
         # L-update: L[i,l,:] = softmax_k(q[l,i] . c[k,i] + H_R[k,i])
         w = np.matmul(q.transpose(1, 0, 2), C.transpose(1, 2, 0)) + HR.T[:, None, :]
-        L = softmax(w, axis=-1)                            # L[i, l, k]
+        L = softmax(w, axis=-1) * rq.T[:, :, None]         # L[i, l, k]; padding rows 0
         lse = logsumexp(w, axis=-1)                        # [i, l]
         f_trace.append(_objective_untiled(q, C, HR, L))
         if history:
@@ -151,7 +185,7 @@ def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False):
             beta = np.sum(L, axis=1)                                       # [i, k]
             safe = np.where(beta > 0, beta, 1.0)
             qt_i = np.where((beta > 0)[..., None], alpha / safe[..., None],
-                            q.mean(axis=0)[:, None, :])
+                            qmean[:, None, :])
             qt = qt_i.transpose(1, 0, 2)                   # [k, i, d]
 
     U = np.matmul(R, vg)                                   # u[k, i]
@@ -190,11 +224,11 @@ def _tiled_scores(q_rows, C_t, HR_t):
     return w.reshape(nc, q_rows.shape[0], b1, c2)
 
 
-def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False):
+def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False, real=None):
     """One slice of tiled MonarchAttention with c1 x c2 sub-tiles per block.
 
     Requires c1 | b1 and c2 | b2 (tiles and segments are then contiguous and
-    of equal size).  Returns dict:
+    of equal size).  real: as for forward_untiled.  Returns dict:
       y       [b1, nc, d]
       L       [nc, b1, b1, c2]   L[i, l, k, s]
       R       [b1, nc, c1, b2]   R[k, i, t, j]  (each segment of j sums to 1)
@@ -207,32 +241,39 @@ def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False):
     if b1 % c1 or b2 % c2:
         raise ValueError("c1 must divide b1 and c2 must divide b2")
     cols = np.arange(b2) if cols is None else np.asarray(cols)
-    q = scale * qg[:, cols, :]                    # q[l, i]
+    real = _check_real(real, b1, b2, c2)
+    rq = real[:, cols]                             # real query rows (l, i)
+    q = scale * np.where(rq[..., None], qg[:, cols, :], 0.0)   # q[l, i]
     nc = q.shape[1]
     sw = b2 // c2                                  # keys per segment
     tile = tile_of_rows(b1, c1)
     Kseg = kg.reshape(b1, c2, sw, d)               # K[k, s, j'], j = s*sw + j'
+    kreal = real.reshape(b1, c2, sw)               # real keys
     dv = vg.shape[-1]
     Vseg = vg.reshape(b1, c2, sw, dv)
 
-    # tile means of the queries, qbar[t, i]
-    qbar = np.stack([q[tile == t].mean(axis=0) for t in range(c1)])   # [c1, nc, d]
+    # tile means of the queries over real rows, qbar[t, i]
+    qbar = np.stack([_real_mean(q[tile == t], rq[tile == t]) for t in range(c1)])   # [c1, nc, d]
 
-    # initial qt[k, i, t, s]: own tile -> q[k, i]; other tiles -> qbar[t, i]
+    # initial qt[k, i, t, s]: own tile -> q[k, i]; other tiles (and padding
+    # rows) have beta = 0 -> qbar[t, i]
     qt = np.empty((b1, nc, c1, c2, d))
     for k in range(b1):
         for t in range(c1):
-            qt[k, :, t, :, :] = (q[k] if t == tile[k] else qbar[t])[:, None, :]
+            own = np.where(rq[k][:, None], q[k], qbar[t]) if t == tile[k] else qbar[t]
+            qt[k, :, t, :, :] = own[:, None, :]
 
-    # L0: tiled block identity, mass 1/c2 on every segment of the own block
+    # L0: tiled block identity on real rows, mass 1/c2 on every segment of
+    # the own block
     L = np.zeros((nc, b1, b1, c2))
-    L[:, np.arange(b1), np.arange(b1), :] = 1.0 / c2
+    L[:, np.arange(b1), np.arange(b1), :] = rq.T[:, :, None] / c2
 
     f_trace, hist = [], []
     for step in range(steps):
         # R-update, per (k, i, t, s): R = softmax over j in segment s of
         # qt[k,i,t,s] . k[k,j]
         z = np.einsum("kitsd,ksjd->kitsj", qt, Kseg)       # [k, i, t, s, j']
+        z = np.where(kreal[:, None, None], z, -np.inf)     # padding keys take no weight
         Rs = softmax(z, axis=-1)
         HR = row_entropy(Rs, axis=-1)                      # [k, i, t, s]
         C = np.einsum("kitsj,ksjd->kitsd", Rs, Kseg)       # [k, i, t, s, d]
@@ -249,7 +290,7 @@ def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False):
             rows = np.nonzero(tile == t)[0]
             w = _tiled_scores(q[rows], C[:, :, t], HR[:, :, t])   # [i, rows, k, s]
             wf = w.reshape(nc, rows.size, b1 * c2)
-            L[:, rows] = softmax(wf, axis=-1).reshape(nc, rows.size, b1, c2)
+            L[:, rows] = (softmax(wf, axis=-1) * rq[rows].T[:, :, None]).reshape(nc, rows.size, b1, c2)
             lse[:, rows] = logsumexp(wf, axis=-1)
         f_trace.append(_objective_tiled(q, C, HR, L, tile))
         if history:
@@ -308,13 +349,15 @@ def dense_from_factors(L, R, b1, b2, c1=1, c2=1):
 # ---------------------------------------------------------------------------
 
 def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
-            fhw=None, cols=None, tiled=None, slices=None):
+            fhw=None, cols=None, tiled=None, slices=None, pad="post"):
     """MonarchAttention on [B, H, N, d] queries and [B, Hkv, N, d] keys and
     values (any float dtype, upcast to float64).  Hkv < H is grouped-query
     attention: query head h uses key/value head h // (H // Hkv), and the
     method runs per query head unchanged (MonarchAttention, OpenReview author
     response on GQA/MLA: a direct transfer).  The layout permutation maps
-    token order to the b1 x b2 grid (oracle.layouts); Y is mapped back.
+    token order to the b1 x b2 grid (oracle.layouts); Y is mapped back.  A
+    flat sequence with N < b1*b2 is padded ("pre" or "post", see
+    oracle.layouts.grid_index); L rows of padding positions are zero.
 
     cols: optional columns i to compute (Y is then NaN outside them).
     slices: optional list of (b, h) pairs to compute (others left NaN).
@@ -334,7 +377,8 @@ def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
         raise ValueError("K, V must be [B, Hkv, N, .] with Hkv dividing H")
     group = H // Hkv
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
-    grid = grid_index(N, b1, b2, layout, fhw)
+    grid = grid_index(N, b1, b2, layout, fhw, pad)
+    real = grid >= 0
     if tiled is None:
         tiled = c1 * c2 > 1
     sel = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
@@ -354,12 +398,13 @@ def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
         qg = to_grid(Q[b, h], grid)
         kg, vg = (to_grid(X[b, h // group], grid) for X in (K, V))
         if tiled:
-            r = forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=colsel)
+            r = forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=colsel, real=real)
         else:
-            r = forward_untiled(qg, kg, vg, steps, scale, cols=colsel)
-        tok = grid[:, colsel]                      # tokens of the computed grid cells
-        y[b, h][tok.reshape(-1)] = r["y"].reshape(-1, dv)
-        lse[b, h][tok.reshape(-1)] = r["lse"].reshape(-1)
+            r = forward_untiled(qg, kg, vg, steps, scale, cols=colsel, real=real)
+        tok = grid[:, colsel].reshape(-1)          # tokens of the computed grid cells
+        ok = tok >= 0
+        y[b, h][tok[ok]] = r["y"].reshape(-1, dv)[ok]
+        lse[b, h][tok[ok]] = r["lse"].reshape(-1)[ok]
         Ls[b, h] = r["L"]
         Rs[b, h] = r["R"]
         ft[b, h] = r["f_trace"]

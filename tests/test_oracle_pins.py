@@ -657,3 +657,217 @@ def test_gqa_equals_repeated_kv(tiles, steps):
     assert not np.allclose(r["y"], cyc["y"], rtol=0, atol=1e-6)
     with pytest.raises(ValueError):
         oracle.forward(Q, K[:, :1].repeat(4, axis=1), V[:, :1].repeat(4, axis=1), b1, b2, steps)
+
+
+# ---------------------------------------------------------------------------
+# Padding (MonarchAttention, OpenReview author response on block sizes: b is
+# chosen, m = ceil(N/b), padding before or after the sequence).  The method
+# approximates the real N x N attention: the objective sums over real query
+# rows and M puts no mass on padding keys.
+# ---------------------------------------------------------------------------
+
+def padded_grid(N, b1, b2, pad):
+    g = oracle.grid_index(N, b1, b2, "flat", None, pad)
+    return g, g >= 0
+
+
+def test_pad_grid_by_hand():
+    g = oracle.grid_index(5, 2, 3, "flat", None, "pre")
+    assert g.tolist() == [[-1, 0, 1], [2, 3, 4]]
+    g = oracle.grid_index(5, 2, 3, "flat", None, "post")
+    assert g.tolist() == [[0, 1, 2], [3, 4, -1]]
+    x = np.arange(5.0)[:, None] + 1
+    for pad in ("pre", "post"):
+        g = oracle.grid_index(5, 2, 3, "flat", None, pad)
+        xg = oracle.to_grid(x, g)
+        assert xg[g < 0].sum() == 0
+        np.testing.assert_array_equal(oracle.from_grid(xg, g), x)
+    with pytest.raises(ValueError):
+        oracle.grid_index(7, 2, 3)
+    with pytest.raises(ValueError):       # a segment without a real key
+        oracle.forward(*(np.ones((1, 1, 3, 2)),) * 3, 2, 4, 1, c2=2, pad="pre")
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("c2,steps", [(1, 1), (1, 3), (3, 2)])
+def test_pad_single_block_is_exact_attention(pad, c2, steps):
+    """b1 = 1: one block holding all real tokens; the method gives exact
+    attention over the real keys (padding keys carry no weight)."""
+    rng = np.random.default_rng(3)
+    N, b2, d = 7, 9, 4
+    Q, K, V = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    r = oracle.forward(Q, K, V, 1, b2, steps, 1, c2, pad=pad)
+    ref = oracle.exact_attention(Q[0, 0], K[0, 0], V[0, 0], 1 / np.sqrt(d))
+    np.testing.assert_allclose(r["y"][0, 0], ref, atol=1e-12)
+
+
+def _dense_real(L, R, real, b1, b2, c1=1, c2=1):
+    M = om.dense_from_factors(L, R, b1, b2, c1, c2)
+    idx = np.nonzero(real.reshape(-1))[0]
+    return M, M[np.ix_(idx, idx)], idx
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("tiles", [None, (2, 2)])
+def test_pad_separable_scores_exact(pad, tiles):
+    """Separable scores on the real entries are reproduced exactly in one
+    step: R rows are softmaxes over the real keys only."""
+    b1, b2 = 4, 6
+    N = b1 * b2 - 2
+    g, real = padded_grid(N, b1, b2, pad)
+    rng = np.random.default_rng(9)
+    x = 2.0 * rng.standard_normal((b2, b1, b1))
+    y = 2.0 * rng.standard_normal((b1, b2, b2))
+    qg, kg = separable_qk(x, y)
+    vg = rng.standard_normal((b1, b2, 3))
+    S = dense_scores(qg, kg, 1.0)
+    if tiles is None:
+        r = om.forward_untiled(qg, kg, vg, 1, 1.0, real=real)
+        M, Mr, idx = _dense_real(r["L"], r["R"], real, b1, b2)
+    else:
+        r = om.forward_tiled(qg, kg, vg, 1, 1.0, *tiles, real=real)
+        M, Mr, idx = _dense_real(r["L"], r["R"], real, b1, b2, *tiles)
+    A = oracle.softmax(S[np.ix_(idx, idx)], axis=-1)
+    np.testing.assert_allclose(Mr, A, atol=1e-12, rtol=0)
+    # no mass on padding keys, no rows for padding queries
+    assert np.abs(M[:, ~real.reshape(-1)]).max() == 0
+    assert np.abs(M[~real.reshape(-1)]).max() == 0
+    # unmasked keys would be visible: the same data with every position real differs
+    full = om.forward_untiled(qg, kg, vg, 1, 1.0) if tiles is None else \
+        om.forward_tiled(qg, kg, vg, 1, 1.0, *tiles)
+    Mf = om.dense_from_factors(full["L"], full["R"], b1, b2, *(tiles or (1, 1)))
+    assert np.abs(Mf[np.ix_(idx, idx)] - A).max() > 1e-3
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("tiled", [False, True])
+def test_pad_objective_monotone_and_dense(pad, tiled):
+    b1, b2, d, T = 4, 6, 5, 4
+    N = b1 * b2 - (1 if tiled else 4)
+    g, real = padded_grid(N, b1, b2, pad)
+    rng = np.random.default_rng(17)
+    qg, kg, vg = rand_qkv(rng, b1, b2, d, 1.5)
+    scale = 0.7
+    c1, c2 = (2, 3) if tiled else (1, 1)
+    if tiled:
+        r = om.forward_tiled(qg, kg, vg, T, scale, c1, c2, history=True, real=real)
+    else:
+        r = om.forward_untiled(qg, kg, vg, T, scale, history=True, real=real)
+    idx = np.nonzero(real.reshape(-1))[0]
+    S = dense_scores(qg, kg, scale)[np.ix_(idx, idx)]
+    ft = r["f_trace"]
+    assert np.all(np.diff(ft) >= -1e-10 * np.abs(ft[:-1]).max())
+    assert ft.max() <= oracle.logsumexp(S, axis=-1).sum() + 1e-10
+    for (L, R), f in zip(r["history"], ft):
+        M, Mr, _ = _dense_real(L, R, real, b1, b2, c1, c2)
+        np.testing.assert_allclose(Mr.sum(axis=-1), 1.0, atol=1e-13)
+        assert np.abs(M[:, ~real.reshape(-1)]).max() == 0
+        assert abs(oracle.dense_objective(Mr, S) - f) <= 1e-10 * abs(f) + 1e-12
+
+
+def _dense_f_real(Lt, Rt, S, b1, b2, c1, c2, idx):
+    tile = torch.as_tensor(om.tile_of_rows(b1, c1))
+    seg = torch.as_tensor(om.segment_of_cols(b2, c2))
+    M = Lt[:, :, :, seg].permute(1, 0, 2, 3) * Rt[:, :, tile, :].permute(2, 1, 0, 3)
+    M = M.reshape(b1 * b2, b1 * b2)[idx][:, idx]
+    return (M * S).sum() - torch.special.xlogy(M, M).sum()
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("b1,b2,c1,c2", [(3, 3, 1, 1), (2, 4, 1, 2), (4, 2, 2, 1)])
+def test_pad_half_steps_are_argmax(pad, b1, b2, c1, c2):
+    """Step 2's half-steps maximise the objective of the real attention: a
+    generic maximiser over R (real keys) with L1 fixed, then over the L rows
+    of real queries with R2 fixed."""
+    N = b1 * b2 - 1
+    g, real = padded_grid(N, b1, b2, pad)
+    rng = np.random.default_rng(b1 * 13 + b2 + c1 + c2)
+    qg, kg, vg = rand_qkv(rng, b1, b2, 3)
+    scale = 0.9
+    if c1 * c2 > 1:
+        r = om.forward_tiled(qg, kg, vg, 2, scale, c1, c2, history=True, real=real)
+    else:
+        r = om.forward_untiled(qg, kg, vg, 2, scale, history=True, real=real)
+    idx = torch.as_tensor(np.nonzero(real.reshape(-1))[0])
+    S = torch.from_numpy(dense_scores(qg, kg, scale))[idx][:, idx]
+    hist = r["history"]
+
+    def as4(L, R):
+        L = L if L.ndim == 4 else L[..., None]
+        R = R if R.ndim == 4 else R[:, :, None, :]
+        return torch.from_numpy(L), torch.from_numpy(R)
+    sw = b2 // c2
+    kmask = torch.from_numpy(real.reshape(b1, 1, 1, c2, sw))
+    L1, _ = as4(*hist[1])
+    _, R2 = as4(*hist[2])
+
+    def R_of(theta):
+        th = theta.reshape(b1, b2, c1, c2, sw).masked_fill(~kmask, float("-inf"))
+        return torch.softmax(th, dim=-1).reshape(b1, b2, c1, b2)
+    th = _maximise(lambda t: _dense_f_real(L1, R_of(t), S, b1, b2, c1, c2, idx),
+                   (b1, b2, c1, b2), 0)
+    np.testing.assert_allclose(R_of(th).numpy(), R2.numpy(), atol=2e-6)
+
+    L2, _ = as4(*hist[3])
+
+    def L_of(theta):
+        return torch.softmax(theta.reshape(b2, b1, b1 * c2), dim=-1).reshape(b2, b1, b1, c2)
+    th = _maximise(lambda t: _dense_f_real(L_of(t), R2, S, b1, b2, c1, c2, idx),
+                   (b2, b1, b1 * c2), 1)
+    rows = torch.from_numpy(real.T)                    # [i, l]
+    np.testing.assert_allclose(L_of(th).numpy()[rows.numpy()], L2.numpy()[rows.numpy()], atol=2e-6)
+    assert np.abs(L2.numpy()[~rows.numpy()]).max() == 0
+
+
+@pytest.mark.parametrize("case", [
+    dict(b1=3, b2=3, c1=1, c2=1, pad="pre", P=2),
+    dict(b1=3, b2=4, c1=1, c2=2, pad="post", P=1),
+    dict(b1=4, b2=3, c1=2, c2=1, pad=None, P=0),      # tiled zero-weight sub-rows
+    dict(b1=4, b2=4, c1=2, c2=2, pad="pre", P=1),
+])
+def test_zero_weight_fallback_is_eps_limit(case):
+    """The first R-update where L0 gives a sub-row zero weight (padding rows;
+    tiles other than the own one): the oracle's tile-mean query equals the
+    limit eps -> 0 of the exact maximiser under L0_eps = (1 - eps) L0 +
+    eps * uniform over the real rows, found by a generic maximiser (no
+    closed form).  For those sub-rows the maximiser is the same at every
+    eps > 0, so eps = 1e-2 (a well-conditioned problem) pins them tightly;
+    the other sub-rows move by O(eps)."""
+    b1, b2, c1, c2 = case["b1"], case["b2"], case["c1"], case["c2"]
+    N = b1 * b2 - case["P"]
+    g, real = padded_grid(N, b1, b2, case["pad"] or "post")
+    rng = np.random.default_rng(41 + b1 + b2)
+    qg, kg, vg = rand_qkv(rng, b1, b2, 3)
+    scale = 0.8
+    if c1 * c2 > 1:
+        r = om.forward_tiled(qg, kg, vg, 1, scale, c1, c2, history=True, real=real)
+    else:
+        r = om.forward_untiled(qg, kg, vg, 1, scale, history=True, real=real)
+    L0, R1 = r["history"][0]
+    L0 = torch.from_numpy(L0 if L0.ndim == 4 else L0[..., None])
+    R1 = R1 if R1.ndim == 4 else R1[:, :, None, :]
+    eps = 1e-2
+    rows = torch.from_numpy(real.T)[:, :, None, None].double()      # [i, l, 1, 1]
+    Leps = (1 - eps) * L0 + eps * rows / (b1 * c2)
+    idx = torch.as_tensor(np.nonzero(real.reshape(-1))[0])
+    S = torch.from_numpy(dense_scores(qg, kg, scale))[idx][:, idx]
+    sw = b2 // c2
+    kmask = torch.from_numpy(real.reshape(b1, 1, 1, c2, sw))
+
+    def R_of(theta):
+        th = theta.reshape(b1, b2, c1, c2, sw).masked_fill(~kmask, float("-inf"))
+        return torch.softmax(th, dim=-1).reshape(b1, b2, c1, b2)
+    th = _maximise(lambda t: _dense_f_real(Leps, R_of(t), S, b1, b2, c1, c2, idx),
+                   (b1, b2, c1, b2), 2)
+    Rn = R_of(th).numpy()
+    # sub-rows with zero weight in L0: q~ is the same real-row tile mean for
+    # every eps; the others move by O(eps)
+    tile = om.tile_of_rows(b1, c1)
+    zero = np.zeros((b1, b2, c1), bool)
+    for k in range(b1):
+        for t in range(c1):
+            zero[k, :, t] = (t != tile[k]) | ~real[k]
+    assert zero.any()
+    np.testing.assert_allclose(Rn[zero], R1[zero], atol=2e-5)
+    np.testing.assert_allclose(Rn[~zero], R1[~zero], atol=5e-2)
+    assert np.abs(Rn[~zero] - R1[~zero]).max() > 1e-5    # eps really moved them
