@@ -101,12 +101,24 @@ typedef enum {
  * the other (PRECISE wins over FAST). */
 #define MA_FLAG_FAST_AGGREGATE 2u
 #define MA_FLAG_PRECISE_AGGREGATE 8u
+/* Padding of a flat sequence with seq_len < b1*b2 (MonarchAttention,
+ * OpenReview author response on block sizes: b is chosen, m = ceil(N/b), and
+ * the sequence is padded before -- as for ViT's leading class token -- or
+ * after its tokens).  Default: after; this flag: before.  The P = b1*b2 -
+ * seq_len padding positions are not tokens: the method fits the attention
+ * among the real tokens only (R rows are softmaxes over real keys, padding
+ * rows carry no L row and no output, the column sums for the next queries
+ * and the tile means run over real rows; a padding position takes the tile
+ * mean as its first-step query).  Requires P < b2 / c2, so that every key
+ * segment holds a real key. */
+#define MA_FLAG_PAD_FRONT 16u
 
 typedef struct {
   int64_t batch, heads, seq_len, head_dim;  /* Q, Y: [batch, heads, seq_len, head_dim];
                                                K, V: [batch, kv_heads, seq_len, head_dim] */
-  int32_t b1, b2;      /* seq_len == b1*b2; b1 = number of blocks (the pages' m),
-                          b2 = block length (the pages' b) */
+  int32_t b1, b2;      /* seq_len == b1*b2, or for FLAT b1*b2 - b2/c2 < seq_len <=
+                          b1*b2 (padded, see MA_FLAG_PAD_FRONT); b1 = number of
+                          blocks (the pages' m), b2 = block length (the pages' b) */
   int32_t c1, c2;      /* sub-tiles per block; 1,1 = untiled Monarch; c1 | b1, c2 | b2 */
   int32_t steps;       /* alternating-maximisation steps T >= 1 */
   float scale;         /* multiplies Q.K^T; 0 means 1/sqrt(head_dim) */
@@ -124,6 +136,7 @@ typedef struct {
 
 /* Optional exports (device pointers, each may be NULL), always fp32/fp64.
  * L:   [batch, heads, b2, b1, b1*c2]    L[i][l][k*c2 + s] after the last step
+ *                                       (grid positions; zero rows at padding)
  * R:   [batch, heads, b1, b2, c1, b2]   R[k][i][t][j]     after the last step
  * lse: [batch, heads, seq_len]          token order; logsumexp (natural log)
  *      of the last L-update's scores for each query row

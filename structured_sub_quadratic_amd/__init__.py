@@ -16,7 +16,7 @@ import ctypes
 
 from . import _lib
 from ._lib import (MonarchAttnError, LAYOUTS, MA_FLAG_FORCE_STAGED, MA_FLAG_FAST_AGGREGATE,
-                   MA_FLAG_FORCE_FUSED, MA_FLAG_PRECISE_AGGREGATE)
+                   MA_FLAG_FORCE_FUSED, MA_FLAG_PRECISE_AGGREGATE, MA_FLAG_PAD_FRONT)
 
 __all__ = ["forward", "forward_timed", "make_problem", "workspace_size", "num_launches",
            "launch_names", "Event", "MonarchAttnError", "LAYOUTS", "library_path",
@@ -96,7 +96,8 @@ class Event:
 
 
 def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, workspace, out,
-             force_staged, fast_aggregate, force_fused=False, precise_aggregate=False):
+             force_staged, fast_aggregate, force_fused=False, precise_aggregate=False,
+             pad="post"):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -113,6 +114,10 @@ def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, worksp
         (MA_FLAG_FAST_AGGREGATE if fast_aggregate else 0) | \
         (MA_FLAG_FORCE_FUSED if force_fused else 0) | \
         (MA_FLAG_PRECISE_AGGREGATE if precise_aggregate else 0)
+    if pad not in ("pre", "post"):
+        raise ValueError("pad must be 'pre' or 'post'")
+    if pad == "pre":
+        flags |= MA_FLAG_PAD_FRONT
     prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags,
                         kv_heads=Hkv)
     ws_bytes = workspace_size(prob)
@@ -137,10 +142,12 @@ def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, worksp
 
 def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
             exports=(), workspace=None, out=None, force_staged=False, fast_aggregate=False,
-            force_fused=False, precise_aggregate=False):
+            force_fused=False, precise_aggregate=False, pad="post"):
     """MonarchAttention forward on the current stream.  Returns Y, or (Y, dict
     of exports) when exports (a subset of "L", "R", "lse", "objective") is
     non-empty.  Shapes of the exports are documented in monarch_attn.h.
+    A flat sequence with seq_len < b1*b2 is padded to the grid, after its
+    tokens (pad="post") or before them (pad="pre"; see MA_FLAG_PAD_FRONT).
     fast_aggregate / precise_aggregate: bf16 only, force the plain or the
     split precision of the c = R K path (default: plain for T = 1, split for
     T > 1; see MA_FLAG_FAST_AGGREGATE).  force_fused / force_staged: T = 1 as
@@ -148,7 +155,7 @@ def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw
     import torch
     prob, workspace, out, ex, cex = _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw,
                                              exports, workspace, out, force_staged,
-                                             fast_aggregate, force_fused, precise_aggregate)
+                                             fast_aggregate, force_fused, precise_aggregate, pad)
     st = torch.cuda.current_stream(q.device).cuda_stream
     status = _lib.load().monarch_attn_forward(
         ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -159,13 +166,13 @@ def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw
 
 def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layout="flat",
                   fhw=None, workspace=None, out=None, force_staged=False, fast_aggregate=False,
-                  force_fused=False, precise_aggregate=False):
+                  force_fused=False, precise_aggregate=False, pad="post"):
     """forward() that also records events[0] before the first kernel launch and
     events[j+1] after launch j (Event objects) on the current stream."""
     import torch
     prob, workspace, out, ex, cex = _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw,
                                              (), workspace, out, force_staged, fast_aggregate,
-                                             force_fused, precise_aggregate)
+                                             force_fused, precise_aggregate, pad)
     st = torch.cuda.current_stream(q.device).cuda_stream
     arr = (ctypes.c_void_p * len(events))(*[e.ptr.value for e in events])
     status = _lib.load().monarch_attn_forward_timed(

@@ -16,6 +16,7 @@ MA_FLAG_FORCE_STAGED = 1
 MA_FLAG_FAST_AGGREGATE = 2
 MA_FLAG_FORCE_FUSED = 4
 MA_FLAG_PRECISE_AGGREGATE = 8
+MA_FLAG_PAD_FRONT = 16
 
 
 class MAProblem(ctypes.Structure):

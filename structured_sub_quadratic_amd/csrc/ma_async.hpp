@@ -193,7 +193,10 @@ struct Stage1AsyncSmem {
   static constexpr int BUF = QOFF + NW * WaveRows<D>::BYTES;
 };
 
-template <int D, int NW, int KTB, bool WITH_U, bool PRECISE>
+// PAD: a padded flat sequence (padding positions clamped on load, padding
+// keys masked, padding query positions read the tile means); the unpadded
+// build keeps the plain row addressing.
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false>
 struct Stage1Async {
   static constexpr int LDS_BYTES = 2 * Stage1AsyncSmem<D, NW, KTB, WITH_U>::BUF;
 
@@ -215,23 +218,26 @@ struct Stage1Async {
 
   auto issue = [&](int item, char* b) {
     const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
-    const AxisMap am = p.map.row_axis(k);
+    const AxisMap am = p.map.template row_axis<PAD>(k);
+    auto tok = [&](int r) -> int64_t { if constexpr (PAD) return am.at(r); else return am.raw(r); };
     const int kvs = kv_slice(sl, p.heads, p.group);
     const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
-    SwzTile<D>::template load<KTB, NW>(b, [&](int r) { return K + am.at(r) * D; }, p.b2);
+    SwzTile<D>::template load<KTB, NW>(b, [&](int r) { return K + tok(r) * D; }, p.b2);
     if constexpr (WITH_U) {
       const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
-      SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + am.at(r) * D; }, p.b2);
+      SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + tok(r) * D; }, p.b2);
     }
     // slot = t*b2 + i: row (k, i) of Q in the own row tile t = k / rt, the
-    // tile mean of (t, i) elsewhere (tiled first step)
+    // tile mean of (t, i) elsewhere (tiled first step) and at padding
+    // positions (k, i)
     const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
     const T* QB = p.qbar_lp ? static_cast<const T*>(p.qbar_lp) + (size_t)sl * p.c1 * p.b2 * D : Q;
     const int town = k / p.rt;
     SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) {
       const int slot = min(qg * QG + r, p.nqs - 1);
       const int t = slot / p.b2, i = slot - t * p.b2;
-      return t == town ? Q + am.at(i) * D : QB + ((size_t)t * p.b2 + i) * D;
+      if constexpr (PAD) return t == town && am.valid(i) ? Q + am.at(i) * D : QB + ((size_t)t * p.b2 + i) * D;
+      else return t == town ? Q + am.raw(i) * D : QB + ((size_t)t * p.b2 + i) * D;
     }, QG);
   };
 
@@ -309,7 +315,11 @@ struct Stage1Async {
     flush(cur);                   // the previous item's last segment
     const char* vt = WITH_U ? cur + SM::TILE : cur;
     for (int s = 0; s < p.c2; ++s) {
-      const int klo = s * p.sw, khi = klo + p.sw;
+      int klo = s * p.sw, khi = klo + p.sw;
+      if constexpr (PAD) {     // real keys of block k
+        klo = max(klo, p.map.key_lo(k));
+        khi = min(khi, p.map.key_hi(k));
+      }
       core.init();
 #pragma unroll 1
       for (int c0 = 0; c0 < KTB; c0 += KT) {
@@ -349,9 +359,9 @@ struct Stage1Async {
   }
 };
 
-template <int D, int NW, int KTB, bool WITH_U, bool PRECISE>
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false>
 __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p) {
-  typedef Stage1Async<D, NW, KTB, WITH_U, PRECISE> S;
+  typedef Stage1Async<D, NW, KTB, WITH_U, PRECISE, PAD> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
 }
@@ -371,7 +381,8 @@ struct Stage2AsyncSmem {
   static constexpr int BUF = U + (WITH_PV ? TILE : 0);
 };
 
-template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT>
+// PAD: a padded flat sequence (no output at padding positions).
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false>
 struct Stage2Async {
   typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV, KC> SM0;
   static constexpr int STG = WITH_PV ? NW * WaveRows<D>::BYTES : 0;
@@ -423,7 +434,7 @@ struct Stage2Async {
       for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[base + (size_t)min(lane + WAVE * j, nvalid - 1) * xs];
     }
     if (ch == 0)
-      Core::fetch_queries([&](int n) { return stage2_qsrc<T, D>(p, sl, i, t, row_of(qg, n)); },
+      Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, sl, i, t, row_of(qg, n)); },
                           Q_INPUT, qn, qnl);
   };
 
@@ -455,13 +466,14 @@ struct Stage2Async {
     if (!out.any) return;
     T* Y = static_cast<T*>(p.y) + (size_t)out.sl * p.N * D;
     if constexpr (WITH_PV) {
-      const AxisMap am = p.map.col_axis(out.i);
+      const AxisMap am = p.map.template col_axis<PAD>(out.i);
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
         WaveRows<D>::put(stg, out.y[n]);
         WaveRows<D>::drain(stg, [&](int r) -> T* {
           const int l = out.l0 + n * 16 + r;
-          return l < out.lend ? Y + am.at(l) * D : nullptr;
+          if constexpr (PAD) return l < out.lend && am.valid(l) ? Y + am.at(l) * D : nullptr;
+          else return l < out.lend ? Y + am.raw(l) * D : nullptr;
         });
       }
     }
@@ -470,7 +482,7 @@ struct Stage2Async {
       if (!out.valid[n]) continue;
       if (g == 0) {
         p.lse2[((size_t)out.sl * p.b2 + out.i) * p.b1 + out.l[n]] = out.lse[n];
-        if (p.lse_out) p.lse_out[(size_t)out.sl * p.N + out.tok[n]] = out.lse[n] * LN2;
+        if (p.lse_out && (!PAD || out.tok[n] >= 0)) p.lse_out[(size_t)out.sl * p.N + out.tok[n]] = out.lse[n] * LN2;
       }
     }
     out.any = false;
@@ -507,7 +519,7 @@ struct Stage2Async {
       decode(item, sl, i, t, qg);
       float lse2[NQ], h2[NQ];
       core.finish(lse2, h2, p.sc2);
-      const AxisMap am = p.map.col_axis(i);
+      const AxisMap am = p.map.template col_axis<PAD>(i);
       out.sl = sl;
       out.i = i;
       out.l0 = t * p.rt + row_of(qg, 0) - lane % 16;
@@ -517,7 +529,8 @@ struct Stage2Async {
         const int ll = row_of(qg, n);
         out.valid[n] = ll < p.rt;
         out.l[n] = t * p.rt + min(ll, p.rt - 1);
-        out.tok[n] = am.at(out.l[n]);
+        if constexpr (PAD) out.tok[n] = am.valid(out.l[n]) ? am.at(out.l[n]) : -1;   // -1: padding row
+        else out.tok[n] = am.raw(out.l[n]);
         out.lse[n] = lse2[n];
         if constexpr (WITH_PV) {
 #pragma unroll
@@ -537,9 +550,9 @@ struct Stage2Async {
   }
 };
 
-template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT>
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false>
 __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p) {
-  typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE, KC> S;
+  typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE, KC, PAD> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
 }

@@ -11,6 +11,7 @@ namespace ma {
 // Column reduction for the next step's queries, and the L export:
 //   L[i,l,(k,s)] = 2^(w2 - lse2[l]),  w2 = sc2 * q[l,i].c[k,i,t,s] + h2[k,i,t,s]
 //   qt[k,i,t,s]  = sum_{l in t} L q[l,i] / sum_{l in t} L
+// (sums over real rows: padding rows have no L row and export zeros).
 // One workgroup per (slice, column i, tile t, 64 keys); each wave owns 16
 // keys and streams the query rows of tile t in chunks of 32.
 // ---------------------------------------------------------------------------
@@ -90,8 +91,9 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
         for (int e = 0; e < VN; ++e) qtr[c * VN + e][j] = v[e];
       }
     }
+    // an infinite normaliser gives L = 0: rows past the tile and padding rows
     if (threadIdx.x < QT)
-      lq[threadIdx.x] = threadIdx.x < nq
+      lq[threadIdx.x] = threadIdx.x < nq && p.map.valid(t * p.rt + q0 + threadIdx.x, i)
           ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + t * p.rt + q0 + threadIdx.x] : INFINITY;
     __syncthreads();
 
@@ -169,9 +171,9 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile means of the queries, qbar[t, i] = mean over rows l of tile t of
-// q[l, i] (fp32): one workgroup per (slice, t, i); 16 row lanes x D/VN
-// column chunks, reduced through LDS.
+// Tile means of the queries, qbar[t, i] = mean over the real rows l of tile t
+// of q[l, i] (fp32; zero if the tile has none): one workgroup per (slice, t,
+// i); 16 row lanes x D/VN column chunks, reduced through LDS.
 // ---------------------------------------------------------------------------
 struct QbarParams {
   const void* q; float* qbar;   // qbar [S, c1, b2, D] fp32
@@ -197,11 +199,21 @@ struct QbarItem {
     float acc[VN];
 #pragma unroll
     for (int e = 0; e < VN; ++e) acc[e] = 0.f;
+    const bool padded = p.map.padded();
+    int nreal = p.rt;
+    if (padded) {
+      nreal = 0;
+      for (int ll = 0; ll < p.rt; ++ll) nreal += p.map.valid(t * p.rt + ll, i) ? 1 : 0;
+    }
+    const AxisMap am = p.map.col_axis(i);
     for (int ll = rl; ll < p.rt; ll += RL) {
-      const V v = *reinterpret_cast<const V*>(Q + (size_t)p.map.token(t * p.rt + ll, i) * D + c * VN);
+      const int l = t * p.rt + ll;
+      if (padded && !am.valid(l)) continue;
+      const V v = *reinterpret_cast<const V*>(Q + (size_t)am.at(l) * D + c * VN);
 #pragma unroll
       for (int e = 0; e < VN; ++e) acc[e] += to_f32(v[e]);
     }
+    const float inv = nreal > 0 ? 1.f / (float)nreal : 0.f;
 #pragma unroll
     for (int e = 0; e < VN; ++e) part[rl][c * VN + e] = acc[e];
     __syncthreads();
@@ -209,8 +221,8 @@ struct QbarItem {
       float s = 0.f;
       for (int r = 0; r < RL; ++r) s += part[r][threadIdx.x];
       const size_t at = (((size_t)sl * p.c1 + t) * p.b2 + i) * D + threadIdx.x;
-      p.qbar[at] = s / (float)p.rt;
-      if (p.qbar_lp) static_cast<T*>(p.qbar_lp)[at] = from_f32<T>(s / (float)p.rt);
+      p.qbar[at] = s * inv;
+      if (p.qbar_lp) static_cast<T*>(p.qbar_lp)[at] = from_f32<T>(s * inv);
     }
     __syncthreads();
   }
@@ -247,9 +259,13 @@ __global__ __launch_bounds__(256) void r_export_kernel(RExportParams p) {
   const int s = j / p.sw;
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * p.D;
   const T* K = static_cast<const T*>(p.k) + (size_t)kv_slice(sl, p.heads, p.group) * p.N * p.D;
+  if (j < p.map.key_lo(k) || j >= p.map.key_hi(k)) {   // padding key: no weight
+    p.R_out[idx] = 0.f;
+    return;
+  }
   const T* krow = K + (size_t)p.map.token(k, j) * p.D;
   float dot = 0.f;
-  if (p.first_step && t == k / p.rt) {
+  if (p.first_step && t == k / p.rt && p.map.valid(k, i)) {
     const T* qrow = Q + (size_t)p.map.token(k, i) * p.D;
     for (int d = 0; d < p.D; ++d) dot += to_f32(qrow[d]) * to_f32(krow[d]);
   } else {
@@ -265,14 +281,16 @@ __global__ __launch_bounds__(256) void r_export_kernel(RExportParams p) {
 struct ObjectiveParams {
   const float* lse2;    // [S, b2, b1]
   double* out;          // [S]
-  int N;
+  GridMap map;          // real rows only
 };
 
 static __global__ __launch_bounds__(256) void objective_kernel(ObjectiveParams p) {
   __shared__ double part[256];
-  const float* src = p.lse2 + (size_t)blockIdx.x * p.N;
+  const int b1 = p.map.b1, G = p.map.b1 * p.map.b2;
+  const float* src = p.lse2 + (size_t)blockIdx.x * G;
   double acc = 0.0;
-  for (int n = threadIdx.x; n < p.N; n += 256) acc += (double)src[n];
+  for (int n = threadIdx.x; n < G; n += 256)
+    if (p.map.valid(n % b1, n / b1)) acc += (double)src[n];
   part[threadIdx.x] = acc;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {

@@ -99,14 +99,26 @@ __device__ inline void store4(bf16* p, f32x4 v) {
 }
 
 // Tokens along one grid axis: token(r) = base + (r / m) * s1 + (r % m) * s2,
-// or base + r * s2 when m == 0 (uniform over a workgroup).
+// or base + r * s2 when m == 0 (uniform over a workgroup).  In a padded flat
+// sequence the grid positions whose token falls outside [0, hi] are padding:
+// at() clamps them to a real token, so every load through it stays in
+// bounds, and valid() tells them apart (stores must check it).
 struct AxisMap {
   int64_t base;
   int m, s1, s2;
-  __device__ inline int64_t at(int r) const {
+  int64_t hi;           // last real token
+  __device__ inline int64_t raw(int r) const {
     if (m == 0) return base + (int64_t)r * s2;
     const int a = r / m;
     return base + (int64_t)a * s1 + (int64_t)(r - a * m) * s2;
+  }
+  // tokens fit 32 bits (the grid is limited to 2^26 positions)
+  __device__ inline int64_t at(int r) const {
+    return min(max((int)raw(r), 0), (int)hi);      // one v_med3_i32
+  }
+  __device__ inline bool valid(int r) const {
+    const int t = (int)raw(r);
+    return t >= 0 && t <= (int)hi;
   }
 };
 
@@ -118,8 +130,36 @@ struct GridMap {
   int kind;          // ma_layout
   int b1, b2;
   int h, w, hw;
+  int pre;           // padding positions before the first token (flat only)
+  int n;             // real tokens; n < b1*b2 for a padded flat sequence
 
+  // Padding (flat layout only): the grid holds b1*b2 >= n positions; with
+  // `pre` leading padding positions, position l*b2 + i holds token
+  // l*b2 + i - pre, and positions outside [0, n) are padding (MonarchAttention,
+  // OpenReview author response on block sizes: m = ceil(N/b), pre- or
+  // post-padding).
+  __device__ inline bool padded() const { return n != b1 * b2; }
+
+  // Token at grid position (l, i), clamped to a real token at padding
+  // positions (loads only; see valid()).
   __device__ inline int64_t token(int l, int i) const {
+    return min(max((int)raw_token(l, i), 0), n - 1);
+  }
+  __device__ inline bool valid(int l, int i) const {
+    const int t = (int)raw_token(l, i);
+    return t >= 0 && t < n;
+  }
+  // Real keys of block k: positions j in [key_lo(k), key_hi(k)).
+  __device__ inline int key_lo(int k) const {
+    return kind == 0 ? min(max(pre - k * b2, 0), b2) : 0;
+  }
+  __device__ inline int key_hi(int k) const {
+    return kind == 0 ? min(max(n + pre - k * b2, 0), b2) : b2;
+  }
+
+  // PAD = false: an unpadded grid (no leading padding to subtract)
+  template <bool PAD = true>
+  __device__ inline int64_t raw_token(int l, int i) const {
     switch (kind) {
       case 2:  // (w, fh): l = w, i = f*h + h
       case 4:  // (hw, f): l = h*w + w, i = f
@@ -133,28 +173,32 @@ struct GridMap {
         return (int64_t)fi * hw + (int64_t)l * w + wi;
       }
       default:  // flat, (fh, w), (f, hw): row-major reshape
-        return (int64_t)l * b2 + i;
+        return (int64_t)l * b2 + i - (PAD ? pre : 0);
     }
   }
 
   // token(l, i) as a function of i (row l of the grid)
+  template <bool PAD = true>
   __device__ inline AxisMap row_axis(int l) const {
+    const int64_t hi = n - 1;
     switch (kind) {
       case 2:
-      case 4: return AxisMap{l, 0, 0, b1};
-      case 5: { const int fi = l / w; return AxisMap{(int64_t)fi * hw + (l - fi * w), 0, 0, w}; }
-      case 6: return AxisMap{(int64_t)l * w, w, hw, 1};
-      default: return AxisMap{(int64_t)l * b2, 0, 0, 1};
+      case 4: return AxisMap{l, 0, 0, b1, hi};
+      case 5: { const int fi = l / w; return AxisMap{(int64_t)fi * hw + (l - fi * w), 0, 0, w, hi}; }
+      case 6: return AxisMap{(int64_t)l * w, w, hw, 1, hi};
+      default: return AxisMap{(int64_t)l * b2 - (PAD ? pre : 0), 0, 0, 1, hi};
     }
   }
   // token(l, i) as a function of l (column i of the grid)
+  template <bool PAD = true>
   __device__ inline AxisMap col_axis(int i) const {
+    const int64_t hi = n - 1;
     switch (kind) {
       case 2:
-      case 4: return AxisMap{(int64_t)i * b1, 0, 0, 1};
-      case 5: return AxisMap{(int64_t)i * w, w, hw, 1};
-      case 6: { const int fi = i / w; return AxisMap{(int64_t)fi * hw + (i - fi * w), 0, 0, w}; }
-      default: return AxisMap{i, 0, 0, b2};
+      case 4: return AxisMap{(int64_t)i * b1, 0, 0, 1, hi};
+      case 5: return AxisMap{(int64_t)i * w, w, hw, 1, hi};
+      case 6: { const int fi = i / w; return AxisMap{(int64_t)fi * hw + (i - fi * w), 0, 0, w, hi}; }
+      default: return AxisMap{(int64_t)i - (PAD ? pre : 0), 0, 0, b2, hi};
     }
   }
 };

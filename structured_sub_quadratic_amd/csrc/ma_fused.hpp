@@ -18,17 +18,17 @@ namespace ma {
 
 template <size_t A, size_t B> constexpr size_t cmax() { return A > B ? A : B; }
 
-template <typename T, int D, int NQ1, int KTB, int NQ2, bool PRECISE, bool QSPLIT>
+template <typename T, int D, int NQ1, int KTB, int NQ2, bool PRECISE, bool QSPLIT, bool PAD = false>
 __global__ __launch_bounds__(THREADS) void fused_t1_kernel(QbarParams pq, Stage1Params p1, Stage2Params p2) {
-  typedef Stage1Item<T, D, NQ1, KTB, true, PRECISE, QSPLIT> S1;
-  typedef Stage2Item<T, D, NQ2, true, PRECISE> S2;
+  typedef Stage1Item<T, D, NQ1, KTB, true, PRECISE, QSPLIT, PAD> S1;
+  typedef Stage2Item<T, D, NQ2, true, PRECISE, PAD> S2;
   typedef QbarItem<T, D> QB;
   constexpr size_t SZ = cmax<cmax<sizeof(typename S1::Smem), sizeof(typename S2::Smem)>(),
                              sizeof(typename QB::Smem)>();
   __shared__ __attribute__((aligned(16))) char buf[SZ];
   cooperative_groups::grid_group grid = cooperative_groups::this_grid();
 
-  if (p1.c1 > 1) {
+  if (p1.c1 > 1 || PAD) {
     const int n0 = QB::items(pq);
     for (int it = blockIdx.x; it < n0; it += gridDim.x)
       QB::run(pq, *reinterpret_cast<typename QB::Smem*>(buf), it);

@@ -104,12 +104,12 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
   float* lse2 = reinterpret_cast<float*>(ws + pl.off_lse2);
   float* qtil = pl.need_qtil ? reinterpret_cast<float*>(ws + pl.off_qtil) : nullptr;
   float* qbar = pl.need_qbar ? reinterpret_cast<float*>(ws + pl.off_qbar) : nullptr;
-  void* qbar_lp = (pl.need_qbar && pl.c1 > 1 && !pl.precise) ? ws + pl.off_qbar_lp : nullptr;
+  void* qbar_lp = pl.need_qbar_lp ? ws + pl.off_qbar_lp : nullptr;
   const int S = (int)pl.S, N = (int)pl.N;
   switch (kind) {
     case L_FUSED: {
       if constexpr (!is_f32<T>()) {
-        if (pl.c1 == 1 && pl.b2 <= 128 && !MA_NO_ASYNC) {
+        if (pl.c1 == 1 && !pl.padded && pl.b2 <= 128 && !MA_NO_ASYNC) {
           // copied-tile stages in one cooperative launch; both phases use
           // the stage-1 wave count
           const int nqs = pl.b2, ktb = pl.b2 <= 64 ? 64 : 128;
@@ -154,8 +154,20 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
                                             (size_t)S * pl.b2 * pl.c1 * p2.nqg);
       void* args[] = {&pq, &p1, &p2};
       const bool ktb64 = pl.b2 <= 64 || (is_f32<T>() && D == 128);
-      const bool qsplit = PRECISE && is_bf16<T>() && pl.c1 > 1;
+      const bool qsplit = PRECISE && is_bf16<T>() && (pl.c1 > 1 || pl.padded);
       hipError_t e = hipSuccess;
+      if (pl.padded) {     // one build: one query sub-tile a wave in both phases
+        constexpr int KP = (is_f32<T>() && D == 128) ? 64 : 128;
+        p1.nqg = (nqs + WAVES * 16 - 1) / (WAVES * 16);
+        p2.nqg = (pl.rt + WAVES * 16 - 1) / (WAVES * 16);
+        const size_t itp = std::max<size_t>(std::max<size_t>((size_t)S * pl.c1 * pl.b2,
+                                                             (size_t)S * pl.b1 * p1.nqg),
+                                            (size_t)S * pl.b2 * pl.c1 * p2.nqg);
+        if (qsplit) e = launch_cooperative(fused_t1_kernel<T, D, 1, KP, 1, PRECISE, true, true>, itp, args, st);
+        else e = launch_cooperative(fused_t1_kernel<T, D, 1, KP, 1, PRECISE, false, true>, itp, args, st);
+        if (e != hipSuccess) return e;
+        break;
+      }
 #define MA_F3(NQ1, KTB, NQ2, QS) e = launch_cooperative(fused_t1_kernel<T, D, NQ1, KTB, NQ2, PRECISE, QS>, items, args, st)
 #define MA_F2(NQ1, KTB, NQ2) do { if (qsplit) MA_F3(NQ1, KTB, NQ2, true); else MA_F3(NQ1, KTB, NQ2, false); } while (0)
 #define MA_F1(NQ1, KTB) do { if (nq2 == 1) MA_F2(NQ1, KTB, 1); else MA_F2(NQ1, KTB, 2); } while (0)
@@ -186,12 +198,14 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       if constexpr (!is_f32<T>()) {
         const int ktb = pl.b2 <= 64 ? 64 : 128;
         // the copied-tile kernel serves the first step when its queries are
-        // bf16 rows: rows of Q, and with tiles the bf16 tile means of the
-        // plain c path; fp32 query sources stay on the register-staged kernels
-        if (pl.b2 <= 128 && step == 0 && (pl.c1 == 1 || qbar_lp) && !MA_NO_ASYNC) {
+        // bf16 rows: rows of Q, and with tiles or padding the bf16 tile means
+        // of the plain c path; fp32 query sources stay on the register-staged
+        // kernels
+        if (pl.b2 <= 128 && step == 0 && ((pl.c1 == 1 && !pl.padded) || qbar_lp) && !MA_NO_ASYNC) {
           // head_dim 128 keeps 4 waves (two waves a SIMD would spill the
           // K|V sums)
-          const int nw = D == 64 ? async_waves(nqs) : 4, qg = nw * 16;
+          // a padded sequence uses one build: 4 waves, 128-key tiles
+          const int nw = D == 64 && !pl.padded ? async_waves(nqs) : 4, qg = nw * 16;
           Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
                          pl.sc2, step == 0 ? 1 : 0, pl.xlo, qbar_lp};
@@ -202,7 +216,10 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_A1(NW, KTB, U) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE>, NW * WAVE, items, p, st)
 #define MA_A1U(NW, KTB) do { if (last) MA_A1(NW, KTB, true); else MA_A1(NW, KTB, false); } while (0)
 #define MA_A1K(NW) do { if (ktb == 64) MA_A1U(NW, 64); else MA_A1U(NW, 128); } while (0)
-          if constexpr (D == 64) { if (nw == 8) MA_A1K(8); else MA_A1K(4); }
+          if (pl.padded) {
+            if (last) launch_persistent(stage1_async_kernel<D, 4, 128, true, PRECISE, true>, 4 * WAVE, items, p, st);
+            else launch_persistent(stage1_async_kernel<D, 4, 128, false, PRECISE, true>, 4 * WAVE, items, p, st);
+          } else if constexpr (D == 64) { if (nw == 8) MA_A1K(8); else MA_A1K(4); }
           else MA_A1K(4);
 #undef MA_A1
 #undef MA_A1U
@@ -222,7 +239,18 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const bool ktb64 = pl.b2 <= 64 || (is_f32<T>() && D == 128);
       const bool last = kind == L_STAGE1_LAST;
       // queries from fp32 rows (next-step queries, tile means) need the split
-      const bool qsplit = PRECISE && is_bf16<T>() && (step > 0 || pl.c1 > 1);
+      const bool qsplit = PRECISE && is_bf16<T>() && (step > 0 || pl.c1 > 1 || pl.padded);
+      if (pl.padded) {     // one build: one query sub-tile a wave, 128-key tiles
+        constexpr int KP = (is_f32<T>() && D == 128) ? 64 : 128;
+        const int qgp = WAVES * 16;
+        p.nqg = (nqs + qgp - 1) / qgp;
+        const dim3 gp(grid1((size_t)S * pl.b1 * p.nqg));
+#define MA_S1P(U, QS) hipLaunchKernelGGL((stage1_kernel<T, D, 1, KP, U, PRECISE, QS, true>), gp, dim3(THREADS), 0, st, p)
+        if (last) { if (qsplit) MA_S1P(true, true); else MA_S1P(true, false); }
+        else { if (qsplit) MA_S1P(false, true); else MA_S1P(false, false); }
+#undef MA_S1P
+        break;
+      }
       // persistent pipelined kernel when the whole block fits one LDS tile
       const bool persistent = pl.b2 <= (ktb64 ? 64 : 128) && !MA_NO_PERSISTENT;
       const dim3 pgrid(grid1(std::min<size_t>(items1, persistent_slots())));
@@ -260,14 +288,17 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     case L_STAGE2_LAST: {
       if constexpr (!is_f32<T>()) {
         if (!MA_NO_ASYNC) {
-          const int nw = stage2_waves<D>(pl.rt), qg = nw * 16;
+          const int nw = pl.padded ? 4 : stage2_waves<D>(pl.rt), qg = nw * 16;
           Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
                          pl.sc2, pl.xlo};
           const size_t items = (size_t)S * pl.b2 * pl.c1 * p.nqg;
           const bool last = kind == L_STAGE2_LAST;
 #define MA_A2(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE>, NW * WAVE, items, p, st)
-          if (nw == 8) { if (last) MA_A2(8, true); else MA_A2(8, false); }
+          if (pl.padded) {   // one build: 4 waves
+            if (last) launch_persistent(stage2_async_kernel<D, 4, 1, true, PRECISE, KT, true>, 4 * WAVE, items, p, st);
+            else launch_persistent(stage2_async_kernel<D, 4, 1, false, PRECISE, KT, true>, 4 * WAVE, items, p, st);
+          } else if (nw == 8) { if (last) MA_A2(8, true); else MA_A2(8, false); }
           else { if (last) MA_A2(4, true); else MA_A2(4, false); }
 #undef MA_A2
           break;
@@ -278,9 +309,16 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                      S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
                      pl.sc2, pl.xlo};
+      const bool last = kind == L_STAGE2_LAST;
+      if (pl.padded) {     // one build: one query sub-tile a wave
+        p.nqg = (pl.rt + WAVES * 16 - 1) / (WAVES * 16);
+        const dim3 gp(grid1((size_t)S * pl.b2 * pl.c1 * p.nqg));
+        if (last) hipLaunchKernelGGL((stage2_kernel<T, D, 1, true, PRECISE, true>), gp, dim3(THREADS), 0, st, p);
+        else hipLaunchKernelGGL((stage2_kernel<T, D, 1, false, PRECISE, true>), gp, dim3(THREADS), 0, st, p);
+        break;
+      }
       const size_t items2 = (size_t)S * pl.b2 * pl.c1 * p.nqg;
       const dim3 grid(grid1(items2));
-      const bool last = kind == L_STAGE2_LAST;
       const int nkeys = pl.b1 * pl.c2;
       const int ktb = nkeys <= 64 ? 64 : 128;
       const bool persistent = nkeys <= ((is_f32<T>() && D == 128) ? 64 : 128) && !MA_NO_PERSISTENT;
@@ -324,7 +362,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       break;
     }
     case L_OBJECTIVE: {
-      ObjectiveParams p{lse2, b.obj, N};
+      ObjectiveParams p{lse2, b.obj, pl.map};
       hipLaunchKernelGGL(objective_kernel, dim3(S), dim3(256), 0, st, p);
       break;
     }

@@ -23,6 +23,8 @@ inline int max_segment(const ma_problem* p) {
 
 struct Plan {
   int64_t S, N, D;
+  int64_t G;           // grid positions b1*b2 (N, or more for a padded flat sequence)
+  bool padded;
   int heads, group;    // query heads; query heads per K/V head
   int b1, b2, c1, c2, sw, rt, T;
   int dtype;
@@ -33,6 +35,7 @@ struct Plan {
   bool precise;
   size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, off_qbar_lp, total;
   bool need_qbar, need_qtil;
+  bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1
 };
 

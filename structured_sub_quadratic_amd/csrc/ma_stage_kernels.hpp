@@ -392,36 +392,39 @@ struct alignas(16) Stage1Smem {
   T vt[DV][LDV];        // [K | V] transposed
 };
 
-// Query source of one stage-1 slot (every pointer valid; padding slots read
-// slot 0).  mode: Q_INPUT at the first step of untiled Monarch, Q_MIXED at the
-// first tiled step (own row tile from Q, other tiles from the tile means),
-// Q_F32 at later steps.
-template <typename T, int D>
+// Query source of one stage-1 slot (every pointer valid; slots past the last
+// read the last).  mode: Q_INPUT at the first step of untiled Monarch, Q_MIXED
+// at the first tiled or padded step (own row tile from Q, other tiles and
+// padding positions from the tile means), Q_F32 at later steps.  PAD: a
+// padded flat sequence (padding positions clamped on load).
+template <typename T, int D, bool PAD = false>
 __device__ inline QSrc<T> stage1_qsrc(const Stage1Params& p, int sl, int k, int slot, int s) {
   slot = min(slot, p.nqs - 1);
   const int t = slot / p.b2, i = slot % p.b2;
   QSrc<T> r;
-  r.t = static_cast<const T*>(p.q) + ((size_t)sl * p.N + p.map.token(k, i)) * D;
+  const int64_t tok = PAD ? p.map.token(k, i) : p.map.template raw_token<false>(k, i);
+  r.t = static_cast<const T*>(p.q) + ((size_t)sl * p.N + tok) * D;
   if (!p.first_step) {
     r.f = p.qtil + (((((size_t)sl * p.b1 + k) * p.c1 + t) * p.c2 + s) * p.b2 + i) * D;
     r.use_f = true;
-  } else if (p.c1 > 1) {
+  } else if (p.c1 > 1 || PAD) {
     r.f = p.qbar + (((size_t)sl * p.c1 + t) * p.b2 + i) * D;
-    r.use_f = t != k / p.rt;
+    r.use_f = t != k / p.rt || (PAD && !p.map.valid(k, i));
   } else {
     r.f = nullptr;
     r.use_f = false;
   }
   return r;
 }
+template <bool PAD = false>
 __device__ inline int stage1_qmode(const Stage1Params& p) {
-  return !p.first_step ? Q_F32 : (p.c1 > 1 ? Q_MIXED : Q_INPUT);
+  return !p.first_step ? Q_F32 : (p.c1 > 1 || PAD ? Q_MIXED : Q_INPUT);
 }
 
 // Keys (and values) j0 .. j0+nk of block k held by this thread: NT tasks of
 // four rows x one 16-byte chunk.  Rows past nk repeat row j0 (their scores are
 // masked); tasks past the tile are not stored.
-template <typename T, int D, int KTB, bool WITH_U>
+template <typename T, int D, int KTB, bool WITH_U, bool PAD = false>
 struct Stage1Keys {
   typedef typename Vec16<T>::type V;
   static constexpr int VN = Vec16<T>::N, CH = D / VN;
@@ -438,7 +441,8 @@ struct Stage1Keys {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = min(4 * jq + r, nk - 1);
-        off[a][r] = (size_t)p.map.token(k, j0 + j) * D + c * VN;
+        const int64_t tok = PAD ? p.map.token(k, j0 + j) : p.map.template raw_token<false>(k, j0 + j);
+        off[a][r] = (size_t)tok * D + c * VN;
       }
     }
 #pragma unroll
@@ -516,7 +520,7 @@ __device__ inline void stage1_segment(Core& core, const Smem& sm, const Stage1Pa
   }
 }
 
-template <typename T, int D, int NQ, int KTB, bool WITH_U, bool PRECISE, bool QSPLIT>
+template <typename T, int D, int NQ, int KTB, bool WITH_U, bool PRECISE, bool QSPLIT, bool PAD = false>
 struct Stage1Item {
   static constexpr bool SPLITX = split_x<T, PRECISE>();
   static constexpr int DV = WITH_U ? 2 * D : D;
@@ -538,13 +542,13 @@ struct Stage1Item {
     const T* Vv = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
     const bool whole = p.b2 <= KTB;
-    const int mode = stage1_qmode(p);
+    const int mode = stage1_qmode<PAD>(p);
     const bool split = PRECISE && mode != Q_INPUT;
     auto qrow = [&](int n, int s) {
-      return stage1_qsrc<T, D>(p, sl, k, qg * QG + wave * NQ * 16 + n * 16 + lane % 16, s);
+      return stage1_qsrc<T, D, PAD>(p, sl, k, qg * QG + wave * NQ * 16 + n * 16 + lane % 16, s);
     };
 
-    Stage1Keys<T, D, KTB, WITH_U> keys;
+    Stage1Keys<T, D, KTB, WITH_U, PAD> keys;
     Core core;
     core.load_queries([&](int n) { return qrow(n, 0); }, mode, split);
     if (whole) {
@@ -552,10 +556,15 @@ struct Stage1Item {
       keys.store(sm);
     }
     for (int s = 0; s < p.c2; ++s) {
+      // key range of segment s within the LDS tile
       int klo = 0, khi = p.sw;
+      if constexpr (PAD) {     // real keys of block k
+        klo = max(p.map.key_lo(k) - s * p.sw, 0);
+        khi = min(p.map.key_hi(k) - s * p.sw, p.sw);
+      }
       if (whole) {
-        klo = s * p.sw;
-        khi = klo + p.sw;
+        klo += s * p.sw;
+        khi += s * p.sw;
       } else {
         __syncthreads();
         keys.load(p, K, Vv, k, s * p.sw, p.sw);
@@ -569,9 +578,9 @@ struct Stage1Item {
   }
 };
 
-template <typename T, int D, int NQ, int KTB, bool WITH_U, bool PRECISE, bool QSPLIT>
+template <typename T, int D, int NQ, int KTB, bool WITH_U, bool PRECISE, bool QSPLIT, bool PAD = false>
 __global__ __launch_bounds__(THREADS) void stage1_kernel(Stage1Params p) {
-  typedef Stage1Item<T, D, NQ, KTB, WITH_U, PRECISE, QSPLIT> Item;
+  typedef Stage1Item<T, D, NQ, KTB, WITH_U, PRECISE, QSPLIT, PAD> Item;
   __shared__ typename Item::Smem sm;
   Item::run(p, sm, xcd_swizzle(blockIdx.x, gridDim.x));
 }
@@ -662,15 +671,17 @@ struct Stage2Prefetch {
   }
 };
 
-template <typename T, int D>
+// CLAMP: padding positions read a real row (their results are not stored)
+template <typename T, int D, bool CLAMP>
 __device__ inline QSrc<T> stage2_qsrc(const Stage2Params& p, int sl, int i, int t, int ll) {
   ll = min(ll, p.rt - 1);
-  return QSrc<T>{static_cast<const T*>(p.q) + ((size_t)sl * p.N + p.map.token(t * p.rt + ll, i)) * D,
-                 nullptr, false};
+  const int64_t tok = CLAMP ? p.map.token(t * p.rt + ll, i) : p.map.template raw_token<false>(t * p.rt + ll, i);
+  return QSrc<T>{static_cast<const T*>(p.q) + ((size_t)sl * p.N + tok) * D, nullptr, false};
 }
 
-// Output of a stage-2 item: y rows (last step) and the row normalisers.
-template <typename T, int D, int NQ, bool WITH_PV, class Core>
+// Output of a stage-2 item: y rows (last step) and the row normalisers (PAD:
+// no output at padding positions).
+template <typename T, int D, int NQ, bool WITH_PV, bool PAD, class Core>
 __device__ inline void stage2_store(const Core& core, const Stage2Params& p, const float (&lse2)[NQ],
                                     int sl, int i, int t, int qg) {
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
@@ -681,19 +692,20 @@ __device__ inline void stage2_store(const Core& core, const Stage2Params& p, con
     const int ll = qg * QG + wave * NQ * 16 + n * 16 + lane % 16;
     if (ll >= p.rt) continue;
     const int l = t * p.rt + ll;
-    const int64_t tok = p.map.token(l, i);
-    if (WITH_PV) {
+    const int64_t tok = PAD ? p.map.token(l, i) : p.map.template raw_token<false>(l, i);
+    const bool real = !PAD || p.map.valid(l, i);
+    if (WITH_PV && real) {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) store4(Y + (size_t)tok * D + dt * 16 + 4 * g, core.o[n][dt]);
     }
     if (g == 0) {
       p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l] = lse2[n];
-      if (p.lse_out) p.lse_out[(size_t)sl * p.N + tok] = lse2[n] * LN2;
+      if (p.lse_out && real) p.lse_out[(size_t)sl * p.N + tok] = lse2[n] * LN2;
     }
   }
 }
 
-template <typename T, int D, int NQ, bool WITH_PV, bool PRECISE>
+template <typename T, int D, int NQ, bool WITH_PV, bool PRECISE, bool PAD = false>
 struct Stage2Item {
   static constexpr bool KLO = split_x<T, PRECISE>();
   static constexpr int QG = WAVES * NQ * 16;
@@ -721,7 +733,7 @@ struct Stage2Item {
     Core core;
     core.init();
     core.load_queries([&](int n) {
-      return stage2_qsrc<T, D>(p, sl, i, t, qg * QG + wave * NQ * 16 + n * 16 + lane % 16);
+      return stage2_qsrc<T, D, PAD>(p, sl, i, t, qg * QG + wave * NQ * 16 + n * 16 + lane % 16);
     }, Q_INPUT, false);
 
     for (int kt0 = 0; kt0 < p.nkeys; kt0 += KT) {
@@ -739,14 +751,14 @@ struct Stage2Item {
 
     float lse2[NQ], h2[NQ];
     core.finish(lse2, h2, p.sc2);
-    stage2_store<T, D, NQ, WITH_PV>(core, p, lse2, sl, i, t, qg);
+    stage2_store<T, D, NQ, WITH_PV, PAD>(core, p, lse2, sl, i, t, qg);
     __syncthreads();
   }
 };
 
-template <typename T, int D, int NQ, bool WITH_PV, bool PRECISE>
+template <typename T, int D, int NQ, bool WITH_PV, bool PRECISE, bool PAD = false>
 __global__ __launch_bounds__(THREADS) void stage2_kernel(Stage2Params p) {
-  typedef Stage2Item<T, D, NQ, WITH_PV, PRECISE> Item;
+  typedef Stage2Item<T, D, NQ, WITH_PV, PRECISE, PAD> Item;
   __shared__ typename Item::Smem sm;
   Item::run(p, sm, xcd_swizzle(blockIdx.x, gridDim.x));
 }
@@ -781,7 +793,7 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
   const int mode = stage1_qmode(p);
   const bool split = PRECISE && mode != Q_INPUT;
 
-  Stage1Keys<T, D, KTB, WITH_U> keys;
+  Stage1Keys<T, D, KTB, WITH_U> keys;     // unpadded sequences only
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
   auto fetch = [&](int item) {
@@ -844,7 +856,7 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
     pf.load(static_cast<const T*>(p.cx) + base * D, p.xlo, static_cast<const T*>(p.ux) + base * D,
             p.h2x + base, p.nkeys, x_stride(p.b2, p.c1));
     Core::fetch_queries([&](int n) {
-      return stage2_qsrc<T, D>(p, sl, i, t, qg * QG + wave * NQ * 16 + n * 16 + lane % 16);
+      return stage2_qsrc<T, D, false>(p, sl, i, t, qg * QG + wave * NQ * 16 + n * 16 + lane % 16);
     }, Q_INPUT, qn, qnl);
   };
 
@@ -874,7 +886,7 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
     }
     float lse2[NQ], h2[NQ];
     core.finish(lse2, h2, p.sc2);
-    stage2_store<T, D, NQ, WITH_PV>(core, p, lse2, sl, i, t, qg);
+    stage2_store<T, D, NQ, WITH_PV, false>(core, p, lse2, sl, i, t, qg);
   }
 }
 

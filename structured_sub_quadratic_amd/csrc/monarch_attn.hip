@@ -14,8 +14,16 @@ using namespace ma;
 ma_status validate_problem(const ma_problem* p) {
   if (!p) return MA_ERR_INVALID_ARGUMENT;
   if (p->batch < 1 || p->heads < 1 || p->seq_len < 1 || p->head_dim < 1) return MA_ERR_INVALID_ARGUMENT;
-  if (p->b1 < 1 || p->b2 < 1 || (int64_t)p->b1 * p->b2 != p->seq_len) return MA_ERR_INVALID_ARGUMENT;
+  if (p->b1 < 1 || p->b2 < 1) return MA_ERR_INVALID_ARGUMENT;
   if (p->c1 < 1 || p->c2 < 1 || p->b1 % p->c1 != 0 || p->b2 % p->c2 != 0) return MA_ERR_INVALID_ARGUMENT;
+  const int64_t grid = (int64_t)p->b1 * p->b2;
+  if (p->layout == MA_LAYOUT_FLAT) {
+    // a flat sequence may be padded to the grid, as long as every key
+    // segment keeps a real key
+    if (grid < p->seq_len || grid - p->seq_len >= p->b2 / p->c2) return MA_ERR_INVALID_ARGUMENT;
+  } else if (grid != p->seq_len) {
+    return MA_ERR_INVALID_ARGUMENT;
+  }
   if (p->steps < 1) return MA_ERR_INVALID_ARGUMENT;
   if (!(std::isfinite(p->scale)) || p->scale < 0.f) return MA_ERR_INVALID_ARGUMENT;
   if (p->dtype != MA_F32 && p->dtype != MA_BF16) return MA_ERR_INVALID_ARGUMENT;
@@ -39,7 +47,7 @@ ma_status validate_problem(const ma_problem* p) {
   if (p->head_dim != 64 && p->head_dim != 128) return MA_ERR_UNSUPPORTED;
   if (p->b2 / p->c2 > max_segment(p)) return MA_ERR_UNSUPPORTED;
   const int64_t slices = p->batch * p->heads;
-  if (slices > (int64_t)1 << 24 || p->seq_len > (int64_t)1 << 26) return MA_ERR_UNSUPPORTED;
+  if (slices > (int64_t)1 << 24 || grid > (int64_t)1 << 26) return MA_ERR_UNSUPPORTED;
   return MA_OK;
 }
 
@@ -49,6 +57,8 @@ Plan make_plan(const ma_problem* p) {
   pl.heads = (int)p->heads;
   pl.group = (int)(p->heads / (p->kv_heads ? p->kv_heads : p->heads));
   pl.N = p->seq_len;
+  pl.G = (int64_t)p->b1 * p->b2;
+  pl.padded = pl.G != pl.N;
   pl.D = p->head_dim;
   pl.b1 = p->b1; pl.b2 = p->b2; pl.c1 = p->c1; pl.c2 = p->c2;
   pl.sw = p->b2 / p->c2;
@@ -60,26 +70,31 @@ Plan make_plan(const ma_problem* p) {
   pl.map.kind = p->layout;
   pl.map.b1 = p->b1; pl.map.b2 = p->b2;
   pl.map.h = p->h; pl.map.w = p->w; pl.map.hw = p->h * p->w;
+  pl.map.pre = (p->flags & MA_FLAG_PAD_FRONT) ? (int)(pl.G - pl.N) : 0;
+  pl.map.n = (int)pl.N;
   pl.elt = p->dtype == MA_F32 ? 4 : 2;
   pl.precise = p->dtype == MA_F32 || (p->flags & MA_FLAG_PRECISE_AGGREGATE) ||
                (!(p->flags & MA_FLAG_FAST_AGGREGATE) && p->steps > 1);
   pl.xc_elt = pl.precise ? 4 : 2;
   pl.need_qtil = p->steps > 1;
-  pl.need_qbar = p->steps > 1 || p->c1 > 1;
+  // tile means: the zero-weight fallback (tiles other than the own one,
+  // padding rows, zero column weight at later steps)
+  pl.need_qbar = p->steps > 1 || p->c1 > 1 || pl.padded;
+  pl.need_qbar_lp = pl.need_qbar && (p->c1 > 1 || pl.padded) && !pl.precise;
   pl.fused = p->steps == 1 && (p->flags & MA_FLAG_FORCE_FUSED) && !(p->flags & MA_FLAG_FORCE_STAGED);
-  const size_t rows = (size_t)pl.S * pl.N * pl.c1 * pl.c2;   // exchange rows
+  const size_t rows = (size_t)pl.S * pl.G * pl.c1 * pl.c2;   // exchange rows
   size_t off = 0;
   pl.off_cx = off;   off = align_up(off + rows * pl.D * pl.xc_elt);
   pl.xlo = (pl.precise && p->dtype == MA_BF16) ? rows * pl.D : 0;
   pl.off_ux = off;   off = align_up(off + rows * pl.D * pl.elt);
   pl.off_h2 = off;   off = align_up(off + rows * 4);
   pl.off_lser = off; off = align_up(off + rows * 4);
-  pl.off_lse2 = off; off = align_up(off + (size_t)pl.S * pl.N * 4);
+  pl.off_lse2 = off; off = align_up(off + (size_t)pl.S * pl.G * 4);
   pl.off_qtil = off; if (pl.need_qtil) off = align_up(off + rows * pl.D * 4);
   pl.off_qbar = off; if (pl.need_qbar) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * 4);
   // tile means in bf16 for the copied-tile first step of the plain c path
   pl.off_qbar_lp = off;
-  if (pl.need_qbar && pl.c1 > 1 && !pl.precise) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * pl.elt);
+  if (pl.need_qbar_lp) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * pl.elt);
   pl.total = off;
   return pl;
 }

@@ -43,7 +43,8 @@ def run_hip(cfg_like, Q, K, V, exports=("L", "R", "lse", "objective"), **kw):
     dev = torch.device("cuda:0")
     tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt) for x in (Q, K, V))
     res = ma.forward(tq, tk, tv, cfg_like.b1, cfg_like.b2, cfg_like.steps, cfg_like.c1,
-                     cfg_like.c2, layout=cfg_like.layout, fhw=cfg_like.fhw, exports=exports, **kw)
+                     cfg_like.c2, layout=cfg_like.layout, fhw=cfg_like.fhw, exports=exports,
+                     pad=getattr(cfg_like, "pad", "post"), **kw)
     torch.cuda.synchronize()
     if exports:
         y, ex = res

@@ -70,6 +70,11 @@ def good(**kw):
     (dict(kv_heads=3), 1),                    # does not divide heads = 2
     (dict(kv_heads=4), 1),                    # more K/V heads than query heads
     (dict(kv_heads=1), 0),                    # grouped-query attention, valid
+    (dict(seq_len=250), 0),                   # flat sequence padded to the 16 x 16 grid
+    (dict(seq_len=241), 0),                   # 15 padding positions < b2
+    (dict(seq_len=240), 1),                   # a whole block of padding
+    (dict(seq_len=247, c2=2), 1),             # 9 padding positions fill a segment of 8
+    (dict(seq_len=249, c2=2), 0),
 ])
 def test_validation_codes(lib, kw, code):
     p = good(**kw)
@@ -117,6 +122,13 @@ def test_workspace_size_and_launch_plan(lib):
                         flags=ma.MA_FLAG_FORCE_FUSED)
     assert ma.launch_names(p) == ["fused_t1"]
     assert lib.monarch_attn_num_launches(ctypes.byref(good(b2=8))) == -1
+    # a padded flat sequence (ViT: 197 tokens as 15 blocks of 14) needs the
+    # tile means for its padding positions; the workspace covers the grid
+    p = ma.make_problem(1, 12, 197, 64, 15, 14)
+    assert ma.launch_names(p) == ["qbar", "stage1_last", "stage2_last"]
+    full = ma.make_problem(1, 12, 210, 64, 15, 14)
+    assert ma.launch_names(full) == ["stage1_last", "stage2_last"]
+    assert ma.workspace_size(p) >= ma.workspace_size(full)
 
 
 def test_status_strings(lib):

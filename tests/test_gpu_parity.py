@@ -37,11 +37,12 @@ def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective
         K, V = (np.ascontiguousarray(X[:, :kv_heads]) for X in (K, V))
     y, ex = run_hip(cfg, Q, K, V, exports=exports, **kw)
     ref = oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                         layout=cfg.layout, fhw=cfg.fhw, cols=cols, slices=slices)
+                         layout=cfg.layout, fhw=cfg.fhw, cols=cols, slices=slices, pad=cfg.pad)
     tiled = cfg.c1 * cfg.c2 > 1
     tol = TOL[cfg.dtype] if tol is None else tol
     errs = {}
     tok = ref["grid"][:, ref["cols"]].reshape(-1)
+    tok = tok[tok >= 0]                 # padding positions have no token
     errs["Y"] = rel_err(y[:, :, tok], ref["y"][:, :, tok], slices)
     if "L" in ex:
         errs["L"] = rel_err(ex["L"][:, :, ref["cols"]], oracle_L_as_gpu(ref["L"], tiled), slices)
@@ -252,6 +253,52 @@ def test_grouped_query_attention_n16k_sampled():
     cfg = WORKLOADS["n16k"]
     check_case(cfg, slices=[(0, 0), (0, 5), (0, 11)], cols=[0, 64, 127],
                exports=("L", "R", "lse"), kv_heads=4)
+
+
+# ------------------------------------------------ padded flat sequences
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("dtype,steps", [("f32", 1), ("f32", 2), ("bf16", 1), ("bf16", 2)])
+def test_padded_vit_shape(pad, dtype, steps):
+    """197 tokens (a ViT class token plus 14 x 14 patches) as 15 blocks of
+    14: 13 padding positions, before or after the tokens."""
+    cfg = WorkloadConfig("case", f"vit pad={pad} {dtype} T{steps}", batch=2, heads=3, seq_len=197,
+                         head_dim=64, b1=15, b2=14, steps=steps, dtype=dtype, data="iid", seed=37,
+                         pad=pad)
+    check_case(cfg)
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", d=128, c=(1, 1), steps=1),
+    dict(dtype="bf16", d=64, c=(2, 2), steps=1),
+    dict(dtype="bf16", d=64, c=(2, 2), steps=3),
+    dict(dtype="f32", d=64, c=(5, 2), steps=2),
+    dict(dtype="bf16", d=128, c=(1, 1), steps=2),
+])
+def test_padded_tiles(pad, case):
+    """b1 x b2 = 70 x 52 with 20 padding positions (fewer than a segment of
+    26 keys), tiled and untiled, one and several steps."""
+    cfg = WorkloadConfig("case", f"pad={pad} {case}", batch=1, heads=2, seq_len=70 * 52 - 20,
+                         head_dim=case["d"], b1=70, b2=52, steps=case["steps"], dtype=case["dtype"],
+                         data="normed", seed=43, c1=case["c"][0], c2=case["c"][1], pad=pad)
+    y, _, _ = check_case(cfg)
+    if case["steps"] == 1:
+        y_f, _, _ = check_case(cfg, force_fused=True)
+        assert np.abs(y_f - y).max() <= 1e-6 * np.abs(y).max()
+    if case["dtype"] == "bf16" and case["steps"] == 1:
+        check_case(cfg, precise_aggregate=True)
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+def test_padded_long_sequence_sampled(pad):
+    """16384 - 100 tokens on the 128 x 128 grid, 12 query heads over 4 K/V
+    heads, in the default launch configuration."""
+    cfg = WorkloadConfig("case", f"n16k-100 pad={pad}", batch=1, heads=12, seq_len=16384 - 100,
+                         head_dim=64, b1=128, b2=128, steps=1, dtype="bf16", data="normed",
+                         seed=47, pad=pad)
+    check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 50, 99, 100, 127], exports=("L", "R", "lse"),
+               kv_heads=4)
 
 
 # ------------------------------------------------ benchmark workloads, sampled

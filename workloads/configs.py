@@ -31,6 +31,7 @@ class WorkloadConfig:
     c2: int = 1
     layout: str = "flat"
     fhw: Optional[Tuple[int, int, int]] = None
+    pad: str = "post"          # padding side when seq_len < b1*b2 (flat only)
 
     @property
     def slices(self):
