@@ -55,11 +55,12 @@ def kernel_bytes(cfg, name, precise):
     S, N, d = cfg.slices, cfg.seq_len, cfg.head_dim
     e = 4 if cfg.dtype == "f32" else 2
     xc = 4 if (precise or cfg.dtype == "f32") else 2
-    rows = N * cfg.c1 * cfg.c2                       # exchange rows per slice
+    rows = cfg.b1 * cfg.b2 * cfg.c1 * cfg.c2         # exchange rows per slice (grid positions)
+    qkv = (1 + 2 / cfg.kv_group) * N * d * e         # Q, and K, V once per K/V head
     if name == "stage1_last":
-        b = 3 * N * d * e + rows * d * (xc + e) + rows * 8
+        b = qkv + rows * d * (xc + e) + rows * 8
     elif name == "stage1":
-        b = 3 * N * d * e + rows * d * xc + rows * 8
+        b = qkv + rows * d * xc + rows * 8
     elif name == "stage2_last":
         b = N * d * e + rows * d * (xc + e) + rows * 4 + N * d * e + N * 4
     elif name == "stage2_stats":
@@ -69,7 +70,7 @@ def kernel_bytes(cfg, name, precise):
     elif name == "fused_t1":
         # the whole T = 1 pass in one launch: Q, K, V in and Y out; the exchange
         # (c, u, entropy, normalisers) is meant to stay in L2 / MALL
-        b = 4 * N * d * e
+        b = qkv + N * d * e
     elif name == "qbar":
         b = N * d * e + cfg.c1 * cfg.b2 * d * 4
     else:
@@ -91,7 +92,7 @@ def cpu_baseline(cfg):
         Q, K, V = make_inputs(cfg, slices=[sl])
         t0 = time.perf_counter()
         oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                       layout=cfg.layout, fhw=cfg.fhw, slices=[sl])
+                       layout=cfg.layout, fhw=cfg.fhw, slices=[sl], pad=cfg.pad)
         spent += time.perf_counter() - t0
         done += 1
         if spent > budget_s:
@@ -109,8 +110,9 @@ def sampled_parity(cfg, Q, K, V, y):
     import oracle
     cols = sorted({0, cfg.b2 // 3, cfg.b2 // 2, cfg.b2 - 1})
     ref = oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
-                         fhw=cfg.fhw, cols=cols, slices=[(0, 0)])
+                         fhw=cfg.fhw, cols=cols, slices=[(0, 0)], pad=cfg.pad)
     tok = ref["grid"][:, cols].reshape(-1)
+    tok = tok[tok >= 0]
     a, r = y[0, 0][tok].astype(np.float64), ref["y"][0, 0][tok]
     return float(np.abs(a - r).max() / np.abs(r).max())
 
@@ -121,7 +123,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="n16k",
-                    choices=["n256", "n4k_t3", "n16k", "video", "video_tiled"])
+                    choices=["n256", "n4k_t3", "n16k", "video", "video_tiled", "n16k_pad",
+                             "n16k_gqa"])
     ap.add_argument("--warm", action="store_true", help="reuse one input set (MALL-resident)")
     ap.add_argument("--fast-aggregate", action="store_true",
                     help="plain bf16 c = R K path (the default for T = 1)")
@@ -157,7 +160,7 @@ def main():
         del src, dst
     tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     Q, K, V = make_inputs(cfg)
-    set_bytes = 4 * Q.size * (4 if cfg.dtype == "f32" else 2)
+    set_bytes = (2 * Q.size + K.size + V.size) * (4 if cfg.dtype == "f32" else 2)
     n_sets = 1 if args.warm else max(2, math.ceil(2.5 * MALL_BYTES / set_bytes))
     base = [torch.from_numpy(x).to(dev).to(tdt) for x in (Q, K, V)]
     sets = [(base[0].clone(), base[1].clone(), base[2].clone(), torch.empty_like(base[0]))
@@ -170,8 +173,11 @@ def main():
         (not args.fast_aggregate and cfg.steps > 1)
     if args.fused:
         flags |= ma.MA_FLAG_FORCE_FUSED
+    if cfg.pad == "pre":
+        flags |= ma.MA_FLAG_PAD_FRONT
     prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2,
-                           cfg.steps, cfg.c1, cfg.c2, None, cfg.dtype, cfg.layout, cfg.fhw, flags)
+                           cfg.steps, cfg.c1, cfg.c2, None, cfg.dtype, cfg.layout, cfg.fhw, flags,
+                           kv_heads=cfg.kv_heads)
     names = ma.launch_names(prob)
     nl = len(names)
     ws_bytes = ma.workspace_size(prob)
@@ -249,6 +255,9 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "heads": cfg.heads,
                    "seq_len": cfg.seq_len, "head_dim": cfg.head_dim, "b1": cfg.b1, "b2": cfg.b2,
                    "T": cfg.steps, "tiles": [cfg.c1, cfg.c2], "layout": cfg.layout,
+                   "kv_heads": cfg.kv_heads or cfg.heads,
+                   "padding": (f"{cfg.b1 * cfg.b2 - cfg.seq_len} positions, {cfg.pad}"
+                               if cfg.b1 * cfg.b2 > cfg.seq_len else None),
                    "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)",
                    "aggregate": "split bf16 hi+lo" if precise and cfg.dtype != "f32" else
                                 ("fp32" if cfg.dtype == "f32" else "plain bf16"),

@@ -200,11 +200,7 @@ struct QbarItem {
 #pragma unroll
     for (int e = 0; e < VN; ++e) acc[e] = 0.f;
     const bool padded = p.map.padded();
-    int nreal = p.rt;
-    if (padded) {
-      nreal = 0;
-      for (int ll = 0; ll < p.rt; ++ll) nreal += p.map.valid(t * p.rt + ll, i) ? 1 : 0;
-    }
+    const int nreal = padded ? p.map.real_rows(i, t * p.rt, t * p.rt + p.rt) : p.rt;
     const AxisMap am = p.map.col_axis(i);
     for (int ll = rl; ll < p.rt; ll += RL) {
       const int l = t * p.rt + ll;

@@ -149,6 +149,15 @@ struct GridMap {
     const int t = (int)raw_token(l, i);
     return t >= 0 && t < n;
   }
+  // Number of real rows l in [l0, l1) of column i.
+  __device__ inline int real_rows(int i, int l0, int l1) const {
+    if (kind != 0) return l1 - l0;
+    // token l*b2 + i - pre in [0, n)  <=>  l in [lo, hi)
+    const int a = pre - i, c = n + pre - i;                // l*b2 >= a, l*b2 < c
+    const int lo = a <= 0 ? 0 : (a + b2 - 1) / b2;
+    const int hi = c <= 0 ? 0 : (c + b2 - 1) / b2;
+    return max(0, min(hi, l1) - max(lo, l0));
+  }
   // Real keys of block k: positions j in [key_lo(k), key_hi(k)).
   __device__ inline int key_lo(int k) const {
     return kind == 0 ? min(max(pre - k * b2, 0), b2) : 0;

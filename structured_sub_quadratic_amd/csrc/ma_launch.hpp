@@ -204,8 +204,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
         if (pl.b2 <= 128 && step == 0 && ((pl.c1 == 1 && !pl.padded) || qbar_lp) && !MA_NO_ASYNC) {
           // head_dim 128 keeps 4 waves (two waves a SIMD would spill the
           // K|V sums)
-          // a padded sequence uses one build: 4 waves, 128-key tiles
-          const int nw = D == 64 && !pl.padded ? async_waves(nqs) : 4, qg = nw * 16;
+          const int nw = D == 64 ? async_waves(nqs) : 4, qg = nw * 16;
           Stage1Params p{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.sw, pl.rt, nqs, (nqs + qg - 1) / qg,
                          pl.sc2, step == 0 ? 1 : 0, pl.xlo, qbar_lp};
@@ -216,14 +215,18 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_A1(NW, KTB, U) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE>, NW * WAVE, items, p, st)
 #define MA_A1U(NW, KTB) do { if (last) MA_A1(NW, KTB, true); else MA_A1(NW, KTB, false); } while (0)
 #define MA_A1K(NW) do { if (ktb == 64) MA_A1U(NW, 64); else MA_A1U(NW, 128); } while (0)
-          if (pl.padded) {
-            if (last) launch_persistent(stage1_async_kernel<D, 4, 128, true, PRECISE, true>, 4 * WAVE, items, p, st);
-            else launch_persistent(stage1_async_kernel<D, 4, 128, false, PRECISE, true>, 4 * WAVE, items, p, st);
+#define MA_A1P(NW) do { if (last) MA_A1X(NW, true); else MA_A1X(NW, false); } while (0)
+#define MA_A1X(NW, U) launch_persistent(stage1_async_kernel<D, NW, 128, U, PRECISE, true>, NW * WAVE, items, p, st)
+          if (pl.padded) {     // padded sequences: 128-key tiles only
+            if (nw == 8) { if constexpr (D == 64) MA_A1P(8); }
+            else MA_A1P(4);
           } else if constexpr (D == 64) { if (nw == 8) MA_A1K(8); else MA_A1K(4); }
           else MA_A1K(4);
 #undef MA_A1
 #undef MA_A1U
 #undef MA_A1K
+#undef MA_A1P
+#undef MA_A1X
           break;
         }
       }
@@ -288,19 +291,21 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     case L_STAGE2_LAST: {
       if constexpr (!is_f32<T>()) {
         if (!MA_NO_ASYNC) {
-          const int nw = pl.padded ? 4 : stage2_waves<D>(pl.rt), qg = nw * 16;
+          const int nw = stage2_waves<D>(pl.rt), qg = nw * 16;
           Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
                          pl.sc2, pl.xlo};
           const size_t items = (size_t)S * pl.b2 * pl.c1 * p.nqg;
           const bool last = kind == L_STAGE2_LAST;
 #define MA_A2(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE>, NW * WAVE, items, p, st)
-          if (pl.padded) {   // one build: 4 waves
-            if (last) launch_persistent(stage2_async_kernel<D, 4, 1, true, PRECISE, KT, true>, 4 * WAVE, items, p, st);
-            else launch_persistent(stage2_async_kernel<D, 4, 1, false, PRECISE, KT, true>, 4 * WAVE, items, p, st);
+#define MA_A2P(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE, KT, true>, NW * WAVE, items, p, st)
+          if (pl.padded) {
+            if (nw == 8) { if (last) MA_A2P(8, true); else MA_A2P(8, false); }
+            else { if (last) MA_A2P(4, true); else MA_A2P(4, false); }
           } else if (nw == 8) { if (last) MA_A2(8, true); else MA_A2(8, false); }
           else { if (last) MA_A2(4, true); else MA_A2(4, false); }
 #undef MA_A2
+#undef MA_A2P
           break;
         }
       }

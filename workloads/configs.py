@@ -32,6 +32,12 @@ class WorkloadConfig:
     layout: str = "flat"
     fhw: Optional[Tuple[int, int, int]] = None
     pad: str = "post"          # padding side when seq_len < b1*b2 (flat only)
+    kv_heads: int = 0          # heads of K and V (0: heads); fewer = grouped-query attention
+
+    @property
+    def kv_group(self):
+        """Query heads per K/V head."""
+        return self.heads // (self.kv_heads or self.heads)
 
     @property
     def slices(self):
@@ -49,9 +55,9 @@ class WorkloadConfig:
         return per * self.slices
 
     def algorithmic_bytes(self):
-        """Q, K, V read once and Y written once."""
+        """Q, K, V read once and Y written once (K and V once per K/V head)."""
         elt = 4 if self.dtype == "f32" else 2
-        return 4 * self.seq_len * self.head_dim * elt * self.slices
+        return (2 + 2 / self.kv_group) * self.seq_len * self.head_dim * elt * self.slices
 
     def describe(self):
         d = asdict(self)
@@ -73,6 +79,14 @@ WORKLOADS = {
                       batch=1, heads=12, seq_len=32760, head_dim=128, b1=630, b2=52,
                       steps=1, dtype="bf16", data="video", seed=1004,
                       layout="fh_w", fhw=(21, 30, 52)),
+    # the headline shape with the two generalisations: 100 tokens short of the
+    # grid (padding in front), and 12 query heads sharing 4 K/V heads
+    "n16k_pad": WorkloadConfig("n16k_pad", "N=16284 padded to 128x128 (pre) d=64 T=1 bf16, 12 heads",
+                      batch=1, heads=12, seq_len=16384 - 100, head_dim=64, b1=128, b2=128,
+                      steps=1, dtype="bf16", data="normed", seed=1003, pad="pre"),
+    "n16k_gqa": WorkloadConfig("n16k_gqa", "N=16384 128x128 d=64 T=1 bf16, 12 query heads over 4 K/V heads",
+                      batch=1, heads=12, seq_len=16384, head_dim=64, b1=128, b2=128,
+                      steps=1, dtype="bf16", data="normed", seed=1003, kv_heads=4),
     "video_tiled": WorkloadConfig("video_tiled", "video (630,52) tiled c1=c2=2 d=128 T=1 bf16, 12 heads",
                       batch=1, heads=12, seq_len=32760, head_dim=128, b1=630, b2=52,
                       steps=1, dtype="bf16", data="video", seed=1004,

@@ -101,7 +101,8 @@ def _draw_slice(rng, cfg, noise_scale=None):
 def make_inputs(cfg, slices=None, noise_scale=None):
     """Q, K, V as float32 arrays [B, H, N, d] (values representable in the
     configuration's dtype).  slices: optional list of (b, h) to generate;
-    other slices are left zero (their streams are not drawn)."""
+    other slices are left zero (their streams are not drawn).  With
+    cfg.kv_heads < heads, K and V keep their first kv_heads heads."""
     B, H, N, d = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim
     rngs = slice_rngs(cfg.seed, B, H)
     Q = np.zeros((B, H, N, d), np.float32)
@@ -113,4 +114,7 @@ def make_inputs(cfg, slices=None, noise_scale=None):
         for X, x in ((Q, q), (K, k), (V, v)):
             x = x.astype(np.float32)
             X[b, h] = round_to_bf16(x) if cfg.dtype == "bf16" else x
+    kvh = getattr(cfg, "kv_heads", 0) or H
+    if kvh < H:
+        K, V = np.ascontiguousarray(K[:, :kvh]), np.ascontiguousarray(V[:, :kvh])
     return Q, K, V
