@@ -6,8 +6,9 @@ the CPU-baseline leg of the benchmark use it.  It shares no code with the HIP
 path (no kernels, headers, helpers or constant tables); the two meet only in
 the seeded input generators, which hold none of the method's arithmetic.
 
-Everything here is plain NumPy in float64, written for a reader checking it
-against the pages by eye, not for speed.
+Everything here is plain NumPy in float64 (the gradients in oracle.backward:
+plain float64 PyTorch on the CPU, differentiated by torch.autograd), written
+for a reader checking it against the pages by eye, not for speed.
 
 Sources (cited by page title and section):
   [MA]    "MonarchAttention: Zero-Shot Conversion to Fast, Hardware-Aware
@@ -22,6 +23,7 @@ Parity status of each public function is stated in its docstring; functions
 whose results no pin fixes say "parity unpinned".
 """
 
+from . import backward
 from .layouts import LAYOUTS, grid_index, to_grid, from_grid
 from .monarch import (
     forward_untiled,
@@ -43,5 +45,5 @@ __all__ = [
     "LAYOUTS", "grid_index", "to_grid", "from_grid",
     "forward_untiled", "forward_tiled", "forward", "dense_from_factors",
     "tile_of_rows", "segment_of_cols",
-    "exact_attention", "dense_objective", "row_entropy", "logsumexp", "softmax",
+    "exact_attention", "dense_objective", "row_entropy", "logsumexp", "softmax", "backward",
 ]

@@ -871,3 +871,83 @@ def test_zero_weight_fallback_is_eps_limit(case):
     np.testing.assert_allclose(Rn[zero], R1[zero], atol=2e-5)
     np.testing.assert_allclose(Rn[~zero], R1[~zero], atol=5e-2)
     assert np.abs(Rn[~zero] - R1[~zero]).max() > 1e-5    # eps really moved them
+
+
+# ---------------------------------------------------------------------------
+# Gradients (oracle.backward): reverse-mode differentiation of a float64
+# torch transcription of the forward steps.  Pinned to the NumPy forward it
+# transcribes, to central finite differences of that forward, and to exact
+# attention's gradients when the grid has one block.
+# ---------------------------------------------------------------------------
+
+from oracle import backward as obw
+
+GRAD_CASES = [
+    dict(b1=4, b2=6, c1=1, c2=1, T=1, N=24, pad="post", H=2, Hkv=2),
+    dict(b1=4, b2=6, c1=1, c2=1, T=3, N=24, pad="post", H=2, Hkv=2),
+    dict(b1=4, b2=6, c1=2, c2=3, T=2, N=24, pad="post", H=2, Hkv=2),
+    dict(b1=4, b2=6, c1=1, c2=1, T=2, N=21, pad="pre", H=2, Hkv=2),
+    dict(b1=3, b2=5, c1=1, c2=1, T=1, N=15, pad="post", H=4, Hkv=2),
+]
+
+
+@pytest.mark.parametrize("case", GRAD_CASES)
+def test_backward_transcription_matches_forward(case):
+    rng = np.random.default_rng(7)
+    b1, b2, N = case["b1"], case["b2"], case["N"]
+    Q = rng.standard_normal((1, case["H"], N, 5))
+    K, V = (rng.standard_normal((1, case["Hkv"], N, 5)) for _ in range(2))
+    r = oracle.forward(Q, K, V, b1, b2, case["T"], case["c1"], case["c2"], pad=case["pad"])
+    g, real = padded_grid(N, b1, b2, case["pad"])
+    gi, rm = torch.as_tensor(np.maximum(g, 0)), torch.as_tensor(real)
+    grp = case["H"] // case["Hkv"]
+    for h in range(case["H"]):
+        tg = lambda x: torch.where(rm[..., None], torch.as_tensor(x)[gi], torch.zeros((), dtype=torch.float64))
+        y = obw.forward_slice(tg(Q[0, h]), tg(K[0, h // grp]), tg(V[0, h // grp]), case["T"],
+                              1 / np.sqrt(5), case["c1"], case["c2"], rm).detach().numpy()
+        np.testing.assert_allclose(y[real], r["y"][0, h][g[real]], atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("case", GRAD_CASES)
+def test_backward_matches_finite_differences(case):
+    """<dQ, E> = (f(Q + eps E) - f(Q - eps E)) / (2 eps) for f = <dY, Y>, with
+    Y from the NumPy oracle, along random directions E (and the same for K,
+    V)."""
+    rng = np.random.default_rng(11)
+    b1, b2, N, T = case["b1"], case["b2"], case["N"], case["T"]
+    Q = rng.standard_normal((1, case["H"], N, 5))
+    K, V = (rng.standard_normal((1, case["Hkv"], N, 5)) for _ in range(2))
+    dY = rng.standard_normal(Q.shape)
+    kw = dict(c1=case["c1"], c2=case["c2"], pad=case["pad"])
+    dQ, dK, dV = obw.backward(Q, K, V, dY, b1, b2, T, **kw)
+
+    def f(q, k, v):
+        return float(np.sum(dY * oracle.forward(q, k, v, b1, b2, T, **kw)["y"]))
+    eps = 1e-5
+    for which, grad in ((0, dQ), (1, dK), (2, dV)):
+        for s in range(3):
+            E = np.random.default_rng(100 * which + s).standard_normal(grad.shape)
+            args_p = [Q, K, V]
+            args_m = [Q, K, V]
+            args_p[which] = args_p[which] + eps * E
+            args_m[which] = args_m[which] - eps * E
+            fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+            an = float(np.sum(grad * E))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, s, fd, an)
+
+
+@pytest.mark.parametrize("pad,N", [("post", 9), ("pre", 7)])
+def test_backward_single_block_is_exact_attention_grad(pad, N):
+    """b1 = 1: the method is exact attention over the real keys, so its
+    gradients are those of softmax(scale Q K^T) V (torch's scaled dot-product
+    attention, differentiated by torch)."""
+    rng = np.random.default_rng(5)
+    d, b2 = 4, 9
+    Q, K, V, dY = (rng.standard_normal((1, 2, N, d)) for _ in range(4))
+    for T in (1, 2):
+        dQ, dK, dV = obw.backward(Q, K, V, dY, 1, b2, T, pad=pad)
+        q, k, v = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+        y = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+        (y * torch.as_tensor(dY)).sum().backward()
+        for a, b in ((dQ, q.grad), (dK, k.grad), (dV, v.grad)):
+            np.testing.assert_allclose(a, b.numpy(), atol=1e-12, rtol=0)
