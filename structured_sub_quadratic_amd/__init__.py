@@ -18,9 +18,9 @@ from . import _lib
 from ._lib import (MonarchAttnError, LAYOUTS, MA_FLAG_FORCE_STAGED, MA_FLAG_FAST_AGGREGATE,
                    MA_FLAG_FORCE_FUSED, MA_FLAG_PRECISE_AGGREGATE, MA_FLAG_PAD_FRONT)
 
-__all__ = ["forward", "forward_timed", "make_problem", "workspace_size", "num_launches",
-           "launch_names", "Event", "MonarchAttnError", "LAYOUTS", "library_path",
-           "version"]
+__all__ = ["forward", "forward_timed", "backward", "make_problem", "workspace_size",
+           "backward_workspace_size", "num_launches", "launch_names", "Event",
+           "MonarchAttnError", "LAYOUTS", "library_path", "version"]
 
 
 def library_path():
@@ -60,6 +60,14 @@ def workspace_size(problem):
     n = ctypes.c_size_t(0)
     _lib.check(_lib.load().monarch_attn_workspace_size(ctypes.byref(problem), ctypes.byref(n)),
                "monarch_attn_workspace_size")
+    return n.value
+
+
+def backward_workspace_size(problem):
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().monarch_attn_backward_workspace_size(ctypes.byref(problem),
+                                                                ctypes.byref(n)),
+               "monarch_attn_backward_workspace_size")
     return n.value
 
 
@@ -180,3 +188,31 @@ def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layo
         ctypes.byref(cex), workspace.data_ptr(), workspace.numel(), st, arr, len(events))
     _lib.check(status, "monarch_attn_forward_timed")
     return out
+
+
+def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
+             workspace=None, out=None):
+    """Gradients (dq, dk, dv) of <dy, forward(q, k, v, ...)> on the current
+    stream.  Covers what monarch_attn_backward documents (T = 1, untiled, one
+    K/V head per query head, no padding, blocks of at most 128 keys).
+    out: optional (dq, dk, dv) tensors to write."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("dy", dy)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a HIP device tensor")
+        if t.dim() != 4 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+    B, H, N, D = q.shape
+    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, 0,
+                        kv_heads=H)
+    ws_bytes = backward_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k),
+                                              torch.empty_like(v))
+    st = torch.cuda.current_stream(q.device).cuda_stream
+    status = _lib.load().monarch_attn_backward(
+        ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), st)
+    _lib.check(status, "monarch_attn_backward")
+    return dq, dk, dv

@@ -34,6 +34,7 @@ struct Plan {
   size_t xlo;          // elements from the hi plane of split c to its lo plane (0: not split)
   bool precise;
   size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, off_qbar_lp, total;
+  size_t off_dq2, off_dcx, off_dux, off_dhx;   // backward only
   bool need_qbar, need_qtil;
   bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1
@@ -87,6 +88,18 @@ struct Bufs {
   double* obj;
 };
 
+struct BwdBufs {
+  const void *q, *k, *v, *dy;
+  void *dq, *dk, *dv;
+  char* ws;
+};
+
+// Largest block (keys of either stage) of the backward: the keys of a block
+// or column sit in LDS whole.
+inline int bwd_max_block(const ma_problem* p) {
+  return (p->dtype == MA_F32 && p->head_dim == 128) ? 64 : 128;
+}
+
 // Kernel-launch entry of one element type and head dimension (one
 // translation unit each): runs the whole launch sequence of *pl on st.
 typedef ma_status (*RunFn)(const Plan& pl, const Bufs& b, hipStream_t st, void* const* events,
@@ -97,5 +110,9 @@ ma_status run_bf16_128_precise(const Plan&, const Bufs&, hipStream_t, void* cons
 ma_status run_bf16_128_fast(const Plan&, const Bufs&, hipStream_t, void* const*, int);
 ma_status run_f32_64(const Plan&, const Bufs&, hipStream_t, void* const*, int);
 ma_status run_f32_128(const Plan&, const Bufs&, hipStream_t, void* const*, int);
+ma_status run_bwd_bf16_64(const Plan&, const BwdBufs&, hipStream_t);
+ma_status run_bwd_bf16_128(const Plan&, const BwdBufs&, hipStream_t);
+ma_status run_bwd_f32_64(const Plan&, const BwdBufs&, hipStream_t);
+ma_status run_bwd_f32_128(const Plan&, const BwdBufs&, hipStream_t);
 
 }  // namespace ma

@@ -51,7 +51,9 @@ ma_status validate_problem(const ma_problem* p) {
   return MA_OK;
 }
 
-Plan make_plan(const ma_problem* p) {
+// backward: the forward state it recomputes uses the plain c path for bf16
+// (its own gradient), and the workspace adds the gradient buffers
+Plan make_plan(const ma_problem* p, bool backward = false) {
   Plan pl;
   pl.S = p->batch * p->heads;
   pl.heads = (int)p->heads;
@@ -75,13 +77,15 @@ Plan make_plan(const ma_problem* p) {
   pl.elt = p->dtype == MA_F32 ? 4 : 2;
   pl.precise = p->dtype == MA_F32 || (p->flags & MA_FLAG_PRECISE_AGGREGATE) ||
                (!(p->flags & MA_FLAG_FAST_AGGREGATE) && p->steps > 1);
+  if (backward) pl.precise = p->dtype == MA_F32;
   pl.xc_elt = pl.precise ? 4 : 2;
   pl.need_qtil = p->steps > 1;
   // tile means: the zero-weight fallback (tiles other than the own one,
   // padding rows, zero column weight at later steps)
   pl.need_qbar = p->steps > 1 || p->c1 > 1 || pl.padded;
   pl.need_qbar_lp = pl.need_qbar && (p->c1 > 1 || pl.padded) && !pl.precise;
-  pl.fused = p->steps == 1 && (p->flags & MA_FLAG_FORCE_FUSED) && !(p->flags & MA_FLAG_FORCE_STAGED);
+  pl.fused = !backward && p->steps == 1 && (p->flags & MA_FLAG_FORCE_FUSED) &&
+             !(p->flags & MA_FLAG_FORCE_STAGED);
   const size_t rows = (size_t)pl.S * pl.G * pl.c1 * pl.c2;   // exchange rows
   size_t off = 0;
   pl.off_cx = off;   off = align_up(off + rows * pl.D * pl.xc_elt);
@@ -95,6 +99,13 @@ Plan make_plan(const ma_problem* p) {
   // tile means in bf16 for the copied-tile first step of the plain c path
   pl.off_qbar_lp = off;
   if (pl.need_qbar_lp) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * pl.elt);
+  pl.off_dq2 = pl.off_dcx = pl.off_dux = pl.off_dhx = off;
+  if (backward) {
+    pl.off_dq2 = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
+    pl.off_dcx = off; off = align_up(off + rows * pl.D * 4);
+    pl.off_dux = off; off = align_up(off + rows * pl.D * 4);
+    pl.off_dhx = off; off = align_up(off + rows * 4);
+  }
   pl.total = off;
   return pl;
 }
@@ -145,9 +156,68 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   return run_f32_128(pl, b, st, events, n_events);
 }
 
+// The backward covers T = 1, untiled, one K/V head per query head, no
+// padding, and blocks whose keys fit LDS whole.
+ma_status validate_backward(const ma_problem* p) {
+  const ma_status s = validate_problem(p);
+  if (s != MA_OK) return s;
+  if (p->steps != 1 || p->c1 != 1 || p->c2 != 1) return MA_ERR_UNSUPPORTED;
+  if (p->kv_heads != 0 && p->kv_heads != p->heads) return MA_ERR_UNSUPPORTED;
+  if ((int64_t)p->b1 * p->b2 != p->seq_len) return MA_ERR_UNSUPPORTED;
+  if (p->b1 > bwd_max_block(p) || p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
+  return MA_OK;
+}
+
+ma_status backward_impl(const ma_problem* p, const void* q, const void* k, const void* v,
+                        const void* dy, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  ma_status s = validate_backward(p);
+  if (s != MA_OK) return s;
+  const Plan pl = make_plan(p, true);
+  const void* in[] = {q, k, v, dy};
+  void* out[] = {dq, dk, dv};
+  auto misaligned = [](const void* x, uintptr_t a) { return ((uintptr_t)x % a) != 0; };
+  for (const void* x : in)
+    if (!x || misaligned(x, 16)) return MA_ERR_INVALID_ARGUMENT;
+  for (void* x : out)
+    if (!x || misaligned(x, 16)) return MA_ERR_INVALID_ARGUMENT;
+  const size_t tbytes = (size_t)pl.S * pl.N * pl.D * pl.elt;
+  for (int a = 0; a < 3; ++a) {
+    for (const void* x : in)
+      if (overlaps(out[a], tbytes, x, tbytes)) return MA_ERR_INVALID_ARGUMENT;
+    for (int c = a + 1; c < 3; ++c)
+      if (overlaps(out[a], tbytes, out[c], tbytes)) return MA_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < pl.total) return MA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || misaligned(workspace, ALIGN)) return MA_ERR_INVALID_ARGUMENT;
+  for (const void* x : in)
+    if (overlaps(workspace, pl.total, x, tbytes)) return MA_ERR_INVALID_ARGUMENT;
+  for (void* o : out)
+    if (overlaps(workspace, pl.total, o, tbytes)) return MA_ERR_INVALID_ARGUMENT;
+  BwdBufs b{q, k, v, dy, dq, dk, dv, static_cast<char*>(workspace)};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pl.dtype == MA_BF16)
+    return pl.D == 64 ? run_bwd_bf16_64(pl, b, st) : run_bwd_bf16_128(pl, b, st);
+  return pl.D == 64 ? run_bwd_f32_64(pl, b, st) : run_bwd_f32_128(pl, b, st);
+}
+
 }  // namespace
 
 extern "C" {
+
+ma_status monarch_attn_backward_workspace_size(const ma_problem* p, size_t* bytes) {
+  if (!bytes) return MA_ERR_INVALID_ARGUMENT;
+  const ma_status s = validate_backward(p);
+  if (s != MA_OK) return s;
+  *bytes = make_plan(p, true).total;
+  return MA_OK;
+}
+
+ma_status monarch_attn_backward(const ma_problem* p, const void* q, const void* k, const void* v,
+                                const void* dy, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return backward_impl(p, q, k, v, dy, dq, dk, dv, workspace, workspace_bytes, stream);
+}
 
 ma_status monarch_attn_workspace_size(const ma_problem* p, size_t* bytes) {
   if (!bytes) return MA_ERR_INVALID_ARGUMENT;

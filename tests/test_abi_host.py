@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_expected_api():
     names = declared_functions()
     for must in ("monarch_attn_forward", "monarch_attn_workspace_size",
+                 "monarch_attn_backward", "monarch_attn_backward_workspace_size",
                  "monarch_attn_status_string"):
         assert must in names
 
@@ -135,3 +136,29 @@ def test_status_strings(lib):
     for s in range(5):
         assert lib.monarch_attn_status_string(s)
     assert ma.version()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(steps=2), 2),                       # T > 1 not covered by the backward
+    (dict(c1=2), 2),                          # tiled
+    (dict(kv_heads=1), 2),                    # grouped K/V
+    (dict(seq_len=250), 2),                   # padded
+    (dict(seq_len=256 * 200, b1=200, b2=256), 2),   # blocks wider than 128 keys
+    (dict(seq_len=96 * 96, b1=96, b2=96, head_dim=128, dtype="f32"), 2),   # fp32 d128: 64 max
+    (dict(seq_len=64 * 64, b1=64, b2=64, head_dim=128, dtype="f32"), 0),
+    (dict(steps=0), 1),
+])
+def test_backward_validation(lib, kw, code):
+    p = good(**kw)
+    n = ctypes.c_size_t()
+    assert lib.monarch_attn_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == code
+    if code == 0:
+        assert n.value >= ma.workspace_size(p)
+        # null pointers and a short workspace are rejected before any HIP call
+        assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == 1
+        q, k, v, dy, dq, dk, dv = (256 * 1024 * 1024 * (j + 1) for j in range(7))
+        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, dy, dq, dk, dv, 1 << 40, 10,
+                                         None) == 3
+        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, dy, dq, dq, dv, 1 << 40,
+                                         n.value, None) == 1      # dK overlaps dQ

@@ -1,0 +1,111 @@
+"""Parity of the HIP backward pass (through the C ABI) with the gradient
+oracle (oracle.backward: float64 autograd of the forward's steps).
+
+Every case compares dQ, dK and dV of whole slices with the per-slice relative
+error max|X - X_ref| / max|X_ref| (1e-4 for fp32 inputs, 2e-2 for bf16), on
+seeded synthetic inputs and a seeded upstream gradient dY."""
+
+import numpy as np
+import pytest
+
+from oracle import backward as obw
+from workloads import WORKLOADS, WorkloadConfig, make_inputs
+from workloads.generators import round_to_bf16
+from parity_utils import TOL, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import structured_sub_quadratic_amd as ma
+    ma._lib.load()          # raise loudly if the library is missing
+
+
+def run_backward(cfg, Q, K, V, dY):
+    import torch
+    import structured_sub_quadratic_amd as ma
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdy = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt) for x in (Q, K, V, dY))
+    dq, dk, dv = ma.backward(tq, tk, tv, tdy, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
+                             layout=cfg.layout, fhw=cfg.fhw)
+    torch.cuda.synchronize()
+    return tuple(x.float().cpu().numpy() for x in (dq, dk, dv))
+
+
+def upstream(cfg, seed=77):
+    dY = np.random.default_rng(seed).standard_normal(
+        (cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim)).astype(np.float32)
+    return round_to_bf16(dY) if cfg.dtype == "bf16" else dY
+
+
+def check_backward(cfg, slices=None, tol=None):
+    Q, K, V = make_inputs(cfg)
+    dY = upstream(cfg)
+    got = run_backward(cfg, Q, K, V, dY)
+    all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    slices = all_slices if slices is None else slices
+    ref = obw.backward(Q, K, V, dY, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
+                       layout=cfg.layout, fhw=cfg.fhw, slices=slices)
+    tol = TOL[cfg.dtype] if tol is None else tol
+    errs = {n: rel_err(g, r, slices) for n, g, r in zip(("dQ", "dK", "dV"), got, ref)}
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{cfg.name}: {errs} (tol {tol})"
+    return got
+
+
+def case(name, dtype, d, b1, b2, batch=1, heads=2, data="normed", layout="flat", fhw=None, seed=61):
+    return WorkloadConfig("case", name, batch=batch, heads=heads, seq_len=b1 * b2, head_dim=d,
+                          b1=b1, b2=b2, steps=1, dtype=dtype, data=data, seed=seed,
+                          layout=layout, fhw=fhw)
+
+
+def test_n256_backward():
+    check_backward(WORKLOADS["n256"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_blocks(dtype, d):
+    """b1 = 52, b2 = 40 (neither a multiple of 32) for fp32 head_dim 128's
+    64-key limit; 70 x 52 otherwise."""
+    b1, b2 = (52, 40) if (dtype == "f32" and d == 128) else (70, 52)
+    check_backward(case(f"bwd ragged {dtype} d{d}", dtype, d, b1, b2, data="iid"))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_blocks(dtype):
+    """128 x 128 keys per block and per column (64 x 64 for fp32 head_dim 128)."""
+    check_backward(case(f"bwd 128x96 {dtype}", dtype, 64, 128, 96, heads=2))
+    b = 64 if dtype == "f32" else 128
+    check_backward(case(f"bwd {b}x{b} {dtype} d128", dtype, 128, b, b, heads=1, seed=62))
+
+
+def test_video_layout():
+    cfg = case("bwd video w_fh", "bf16", 128, 8, 15, data="video", layout="w_fh", fhw=(3, 5, 8))
+    check_backward(cfg)
+
+
+def test_linear_in_upstream_and_zero():
+    """dQ, dK, dV are linear in dY: zero for dY = 0, doubled for 2 dY."""
+    import torch
+    cfg = case("bwd linear", "f32", 64, 16, 16)
+    Q, K, V = make_inputs(cfg)
+    dY = upstream(cfg)
+    g1 = run_backward(cfg, Q, K, V, dY)
+    g2 = run_backward(cfg, Q, K, V, 2 * dY)
+    g0 = run_backward(cfg, Q, K, V, 0 * dY)
+    for a, b, z in zip(g1, g2, g0):
+        assert np.abs(z).max() == 0
+        np.testing.assert_allclose(b, 2 * a, rtol=1e-5, atol=1e-6 * np.abs(a).max())
+
+
+def test_n16k_backward_sampled():
+    """The 16k-token headline shape (12 heads); the oracle differentiates two
+    slices, compared whole."""
+    check_backward(WORKLOADS["n16k"], slices=[(0, 0), (0, 11)])
