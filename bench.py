@@ -117,6 +117,65 @@ def sampled_parity(cfg, Q, K, V, y):
     return float(np.abs(a - r).max() / np.abs(r).max())
 
 
+def backward_flops(cfg):
+    """Products of the backward as computed (per slice, T = 1 untiled): stage 2
+    forms P, dP, dQ, dc, du over b1 x b1 per column (5), stage 1 forms R, dR
+    (two products), dQ, dK (two products), dV over b2 x b2 per block (7); the
+    forward state it rebuilds (c, u and the stage-2 normalisers) adds 3 + 1."""
+    N, d, b1, b2 = cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2
+    return 2 * N * d * (5 * b1 + 7 * b2 + 3 * b2 + b1) * cfg.slices
+
+
+def bench_backward(args, cfg, dev):
+    """One JSON line: the backward call's time and effective TFLOP/s."""
+    import numpy as np
+    import torch
+    import structured_sub_quadratic_amd as ma
+    from workloads import make_inputs
+    from workloads.generators import round_to_bf16
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    Q, K, V = make_inputs(cfg)
+    dY = np.random.default_rng(77).standard_normal(Q.shape).astype(np.float32)
+    if cfg.dtype == "bf16":
+        dY = round_to_bf16(dY)
+    set_bytes = 7 * Q.size * (4 if cfg.dtype == "f32" else 2)
+    n_sets = 1 if args.warm else max(2, math.ceil(2.5 * MALL_BYTES / set_bytes))
+    base = [torch.from_numpy(x).to(dev).to(tdt) for x in (Q, K, V, dY)]
+    sets = [tuple(x.clone() for x in base) + tuple(torch.empty_like(base[0]) for _ in range(3))
+            for _ in range(n_sets)]
+    del base
+    prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2,
+                           cfg.steps, cfg.c1, cfg.c2, None, cfg.dtype, cfg.layout, cfg.fhw, 0)
+    ws = torch.empty(max(ma.backward_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        q, k, v, dy, dq, dk, dv = sets[i % n_sets]
+        ma.backward(q, k, v, dy, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
+                    fhw=cfg.fhw, workspace=ws, out=(dq, dk, dv))
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        call(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = backward_flops(cfg)
+    out = {
+        "metric": "MonarchAttention bwd ms/call + effective TFLOP/s", "value":
+            round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "pass": "backward (dQ, dK, dV), forward state rebuilt",
+                   "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)"},
+        "flops_counted": flops,
+        "mfma_frac_of_call": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.dtype], 4),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +191,9 @@ def main():
                     help="split bf16 hi+lo c = R K path (the default for T > 1)")
     ap.add_argument("--fused", action="store_true",
                     help="T = 1 as one cooperative launch instead of separate stage launches")
+    ap.add_argument("--backward", action="store_true",
+                    help="time monarch_attn_backward (dQ, dK, dV for a seeded dY) instead of "
+                         "the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy 3 times (reference for the "
@@ -151,6 +213,9 @@ def main():
 
     cfg = get_workload(args.workload)
     dev = torch.device("cuda:0")
+    if args.backward:
+        bench_backward(args, cfg, dev)
+        return
     if args.calibrate_copy:
         src = torch.empty(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
