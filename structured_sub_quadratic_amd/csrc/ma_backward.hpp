@@ -22,7 +22,10 @@
 // inputs stay exact bf16 operands, and the fp32 matrices computed in the
 // kernel (P, dW, R, dz, du, dc) enter as bf16 hi + lo pairs (16 significant
 // bits).  Query rows stream in chunks of RB; the per-key sums (dc, du, dK,
-// dV) stay in registers across the chunks, so no atomics are needed.
+// dV) stay in registers across the chunks, so no global atomics are needed.
+// Each wave computes strips of output tiles that share one A fragment per
+// k-step, and the chunk's q, dY and the gradients of c, u are also stored
+// transposed so that most operands are contiguous 16-byte LDS reads.
 #pragma once
 
 #include <type_traits>
@@ -49,18 +52,29 @@ struct BwdParams {
 template <typename T, int D> struct BwdShape {
   static constexpr bool F32 = std::is_same<T, float>::value;
   static constexpr int NB = (F32 && D == 128) ? 64 : 128;   // keys held in LDS
-  static constexpr int RB = (D == 64 && !F32) ? 64 : 32;    // query rows per chunk
-  static constexpr int LDI = D + 16 / (int)sizeof(T);       // input-type row stride
-  static constexpr int LDF = D + 4;                         // fp32 row stride over d
+  static constexpr int RB = 32;                             // query rows per chunk
+  static constexpr int LDI = D + 16 / (int)sizeof(T);       // row stride over d (input type)
+  static constexpr int LDN = NB + 16 / (int)sizeof(T);      // row stride over keys (input type)
+  static constexpr int LDR = RB + 16 / (int)sizeof(T);      // row stride over chunk rows
   static constexpr int LDP = NB + 4;                        // fp32 row stride over keys
   static constexpr int KQ = F32 ? 16 : 32;                  // key count granularity
-  static constexpr int KPL = Mfma<T>::KPL;
+  // transposed copies of the keys (K^T, c^T) for the dQ product when LDS allows
+  static constexpr bool KT_COPY = D == 64 && !F32;
+  // waves per workgroup: 8 at head_dim 128 halve the per-wave accumulators
+  static constexpr int NW = D == 64 ? 8 : 4;
+  static constexpr int NG = NW == 8 ? 2 : 4;                // key tiles per score strip
+  static constexpr int DQ = NW == 8 ? 1 : (D / 16 < 4 ? D / 16 : 4);   // d tiles per dQ strip
+  static constexpr int NTH = NW * WAVE;
+  static constexpr int SK = (NB / 16 + NW - 1) / NW;        // key-tile strips per wave
 };
 
 // Operand access for one MFMA step: ROW reads X[idx][k] (k contiguous), COL
-// reads X[k][idx].  Input-type matrices are exact operands; fp32 matrices are
-// split into hi + lo for bf16.
+// reads X[k][idx].  Operand kinds: IN, an exact matrix of the element type;
+// F32, an fp32 matrix split into hi + lo on the fly (bf16 only); PL, two
+// planes hi, lo of the element type (lo `plane` elements after hi; for fp32
+// only hi is read).
 enum { ROW = 0, COL = 1 };
+enum { IN = 0, F32 = 1, PL = 2 };
 
 template <int KIND>
 __device__ inline bf16x8 frag_in(const bf16* X, int ld, int idx, int k) {
@@ -90,59 +104,101 @@ __device__ inline void frag_f32(const float* X, int ld, int idx, int k, bf16x8& 
   }
 }
 
-// acc += A B over k in [0, K) for the 16 x 16 tile (m0, n0): A(m, k) from
-// matrix A (input type when FA is false, fp32 otherwise) in layout KA, B(k, n)
-// likewise.  K is a multiple of 4 * KPL.
-template <typename T, int KA, bool FA, int KB, bool FB>
-__device__ inline f32x4 tile_mma(const void* A, int lda, const void* B, int ldb, int m0, int n0,
-                                 int K, f32x4 acc) {
+// One lane's operand fragment of kind OK in layout L (bf16): hi, and lo when
+// the kind carries one.
+template <int OK, int L>
+__device__ inline void frag(const void* X, int ld, size_t plane, int idx, int k, bf16x8& hi, bf16x8& lo) {
+  if constexpr (OK == F32) {
+    frag_f32<L>(static_cast<const float*>(X), ld, idx, k, hi, lo);
+  } else {
+    hi = frag_in<L>(static_cast<const bf16*>(X), ld, idx, k);
+    if constexpr (OK == PL) lo = frag_in<L>(static_cast<const bf16*>(X) + plane, ld, idx, k);
+  }
+}
+
+// acc[t] += A B for the NT tiles (m0, n0 + 16 t): the A fragment of each
+// k-step is built once and shared by the NT tiles.  A(m, k) has kind AK in
+// layout AL, B(k, n) kind BK in layout BL; K is a multiple of 4 * KPL.  For
+// bf16, a split operand adds the products of its low part (lo x lo is below
+// the result's precision and skipped).
+template <typename T, int NT, int AK, int AL, int BK, int BL>
+__device__ inline void strip_mma(f32x4 (&acc)[NT], const void* A, int lda, size_t aplane, const void* B,
+                                 int ldb, size_t bplane, int m0, int n0, int K) {
   const int lane = threadIdx.x % WAVE, r = lane % 16, g = lane / 16;
   if constexpr (std::is_same<T, float>::value) {
     const float* a = static_cast<const float*>(A);
     const float* b = static_cast<const float*>(B);
     for (int k0 = 0; k0 < K; k0 += 4) {
       const int k = k0 + g;
-      const float av = KA == ROW ? a[(size_t)(m0 + r) * lda + k] : a[(size_t)k * lda + m0 + r];
-      const float bv = KB == ROW ? b[(size_t)(n0 + r) * ldb + k] : b[(size_t)k * ldb + n0 + r];
-      acc = Mfma<float>::mma(av, bv, acc);
+      const float av = AL == ROW ? a[(size_t)(m0 + r) * lda + k] : a[(size_t)k * lda + m0 + r];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int n = n0 + 16 * t + r;
+        const float bv = BL == ROW ? b[(size_t)n * ldb + k] : b[(size_t)k * ldb + n];
+        acc[t] = Mfma<float>::mma(av, bv, acc[t]);
+      }
     }
   } else {
     for (int k0 = 0; k0 < K; k0 += 32) {
       const int k = k0 + 8 * g;
-      bf16x8 ah, al, bh, bl;
-      if constexpr (FA) frag_f32<KA>(static_cast<const float*>(A), lda, m0 + r, k, ah, al);
-      else ah = frag_in<KA>(static_cast<const bf16*>(A), lda, m0 + r, k);
-      if constexpr (FB) frag_f32<KB>(static_cast<const float*>(B), ldb, n0 + r, k, bh, bl);
-      else bh = frag_in<KB>(static_cast<const bf16*>(B), ldb, n0 + r, k);
-      acc = Mfma<bf16>::mma(ah, bh, acc);
-      if constexpr (FA) acc = Mfma<bf16>::mma(al, bh, acc);
-      if constexpr (FB) acc = Mfma<bf16>::mma(ah, bl, acc);
+      bf16x8 ah, al;
+      frag<AK, AL>(A, lda, aplane, m0 + r, k, ah, al);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bf16x8 bh, bl;
+        frag<BK, BL>(B, ldb, bplane, n0 + 16 * t + r, k, bh, bl);
+        acc[t] = Mfma<bf16>::mma(ah, bh, acc[t]);
+        if constexpr (AK != IN) acc[t] = Mfma<bf16>::mma(al, bh, acc[t]);
+        if constexpr (BK != IN) acc[t] = Mfma<bf16>::mma(ah, bl, acc[t]);
+      }
     }
   }
-  return acc;
+}
+
+// Sum over the 16 lanes that share lane / 16 (one output row group of a tile).
+__device__ inline float sum16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 // Rows of an input-type matrix into LDS: dst[j][0..D) = src(j) for j < n,
-// zero for n <= j < NR.
-template <typename T, int D, int LD, class Src>
-__device__ inline void bwd_load_rows(T* dst, int NR, int n, Src src) {
+// zero for n <= j < NR; with TR, also the transpose dt[c][j] (stride LDT).
+template <typename T, int D, int LD, int NTH, bool TR = false, int LDT = 0, class Src>
+__device__ inline void bwd_load_rows(T* dst, T* dt, int NR, int n, Src src) {
   typedef typename Vec16<T>::type V;
   constexpr int VN = Vec16<T>::N, CH = D / VN;
-  for (int task = threadIdx.x; task < NR * CH; task += THREADS) {
+  for (int task = threadIdx.x; task < NR * CH; task += NTH) {
     const int j = task / CH, c = task % CH;
     V v = {};
     if (j < n) v = *reinterpret_cast<const V*>(src(j) + c * VN);
     *reinterpret_cast<V*>(dst + (size_t)j * LD + c * VN) = v;
+    if constexpr (TR) {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) dt[(size_t)(c * VN + e) * LDT + j] = v[e];
+    }
   }
 }
-template <int D, int LD, class Src>
-__device__ inline void bwd_load_rows_f32(float* dst, int NR, int n, Src src) {
+// fp32 rows (gradients of c, u) into transposed planes of the element type:
+// hi[d][j] (and lo for bf16), zero for n <= j < NR.
+template <typename T, int D, int LDT, int NTH, class Src>
+__device__ inline void bwd_load_rows_tplanes(T* hi, size_t plane, int NR, int n, Src src) {
   constexpr int CH = D / 4;
-  for (int task = threadIdx.x; task < NR * CH; task += THREADS) {
+  for (int task = threadIdx.x; task < NR * CH; task += NTH) {
     const int j = task / CH, c = task % CH;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (j < n) v = *reinterpret_cast<const f32x4*>(src(j) + c * 4);
-    *reinterpret_cast<f32x4*>(dst + (size_t)j * LD + c * 4) = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      T* at = hi + (size_t)(c * 4 + e) * LDT + j;
+      if constexpr (std::is_same<T, float>::value) {
+        *at = v[e];
+      } else {
+        const bf16 h = (bf16)v[e];
+        at[0] = h;
+        at[plane] = (bf16)(v[e] - (float)h);
+      }
+    }
   }
 }
 
@@ -150,14 +206,21 @@ __device__ inline void bwd_load_rows_f32(float* dst, int NR, int n, Src src) {
 // Stage 2 backward: one workgroup per (slice, column i).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(THREADS) void stage2_bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdParams p) {
   typedef BwdShape<T, D> SH;
-  constexpr int NB = SH::NB, RB = SH::RB, LDI = SH::LDI, LDP = SH::LDP;
-  constexpr int MJ = (NB / 16) * (D / 16) / WAVES;          // dc, du tiles per wave
+  constexpr int NW = SH::NW, NTH = SH::NTH;
+  constexpr int NB = SH::NB, RB = SH::RB, LDI = SH::LDI, LDN = SH::LDN, LDR = SH::LDR, LDP = SH::LDP;
+  constexpr int DT = D / 16, NG = SH::NG;                    // d tiles; key tiles per score strip
+  constexpr int DS = DT < 4 ? DT : 4;                        // d tiles per dc, du strip
+  constexpr int DQ = SH::DQ;                                 // d tiles per dQ strip
+  constexpr int SK = SH::SK;                                 // key-tile strips of dc, du per wave
   __shared__ __attribute__((aligned(16))) T cs[NB * LDI];
   __shared__ __attribute__((aligned(16))) T us[NB * LDI];
+  __shared__ __attribute__((aligned(16))) T ct[SH::KT_COPY ? D * LDN : 1];   // c^T
   __shared__ __attribute__((aligned(16))) T qs[RB * LDI];
   __shared__ __attribute__((aligned(16))) T dys[RB * LDI];
+  __shared__ __attribute__((aligned(16))) T qt[D * LDR];    // q^T of the chunk
+  __shared__ __attribute__((aligned(16))) T dyt[D * LDR];   // dY^T of the chunk
   __shared__ __attribute__((aligned(16))) float ps[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dws[RB * LDP];
   __shared__ float h2k[NB], dhk[NB], lsel[RB], dl[RB];
@@ -173,110 +236,163 @@ __global__ __launch_bounds__(THREADS) void stage2_bwd_kernel(BwdParams p) {
   const T* dY = static_cast<const T*>(p.dy) + (size_t)sl * p.N * D;
   const AxisMap col = p.map.col_axis(i);
 
-  bwd_load_rows<T, D, LDI>(cs, NB, nb, [&](int k) { return C + (xb + k * xs) * D; });
-  bwd_load_rows<T, D, LDI>(us, NB, nb, [&](int k) { return U + (xb + k * xs) * D; });
-  for (int k = threadIdx.x; k < NB; k += THREADS) {
+  bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(cs, ct, NB, nb, [&](int k) { return C + (xb + k * xs) * D; });
+  bwd_load_rows<T, D, LDI, NTH>(us, nullptr, NB, nb, [&](int k) { return U + (xb + k * xs) * D; });
+  for (int k = threadIdx.x; k < NB; k += NTH) {
     h2k[k] = k < nb ? p.h2x[xb + k * xs] : 0.f;
     dhk[k] = 0.f;
   }
-  f32x4 adc[MJ], adu[MJ];
+  f32x4 adc[SK][DT], adu[SK][DT];
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) adc[j] = adu[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < SK; ++s)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) adc[s][t] = adu[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int l0 = 0; l0 < p.b1; l0 += RB) {
     const int nr = min(RB, p.b1 - l0);
     __syncthreads();
-    bwd_load_rows<T, D, LDI>(qs, RB, nr, [&](int r) { return Q + col.at(l0 + r) * D; });
-    bwd_load_rows<T, D, LDI>(dys, RB, nr, [&](int r) { return dY + col.at(l0 + r) * D; });
-    for (int r = threadIdx.x; r < RB; r += THREADS)
+    bwd_load_rows<T, D, LDI, NTH, true, LDR>(qs, qt, RB, nr, [&](int r) { return Q + col.at(l0 + r) * D; });
+    bwd_load_rows<T, D, LDI, NTH, true, LDR>(dys, dyt, RB, nr, [&](int r) { return dY + col.at(l0 + r) * D; });
+    for (int r = threadIdx.x; r < RB; r += NTH) {
       lsel[r] = r < nr ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + r] : 0.f;
+      dl[r] = 0.f;
+    }
     __syncthreads();
-    // P = exp2(sc2 q.c + h2 - lse2) and dP = dY u^T, RB x nbp
-    for (int t = wave; t < (RB / 16) * (nbp / 16); t += WAVES) {
-      const int m0 = (t / (nbp / 16)) * 16, n0 = (t % (nbp / 16)) * 16;
-      f32x4 s = tile_mma<T, ROW, false, ROW, false>(qs, LDI, cs, LDI, m0, n0, D, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 dp = tile_mma<T, ROW, false, ROW, false>(dys, LDI, us, LDI, m0, n0, D, f32x4{0.f, 0.f, 0.f, 0.f});
-      const int key = n0 + lane % 16;
+    // P = exp2(sc2 q.c + h2 - lse2), dP = dY u^T and D = rowsum(P dP), in
+    // strips of one row tile x NG key tiles
+    const int ng = (nbp / 16 + NG - 1) / NG;
+    for (int st = wave; st < (RB / 16) * ng; st += NW) {
+      const int m0 = (st / ng) * 16, n0 = (st % ng) * 16 * NG;
+      const int nt = min(NG, nbp / 16 - n0 / 16);
+      f32x4 s[NG], dp[NG];
+#pragma unroll
+      for (int t = 0; t < NG; ++t) s[t] = dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (nt == NG) {
+        strip_mma<T, NG, IN, ROW, IN, ROW>(s, qs, LDI, 0, cs, LDI, 0, m0, n0, D);
+        strip_mma<T, NG, IN, ROW, IN, ROW>(dp, dys, LDI, 0, us, LDI, 0, m0, n0, D);
+      } else {
+        for (int t = 0; t < nt; ++t) {
+          f32x4 a1[1] = {s[t]}, a2[1] = {dp[t]};
+          strip_mma<T, 1, IN, ROW, IN, ROW>(a1, qs, LDI, 0, cs, LDI, 0, m0, n0 + 16 * t, D);
+          strip_mma<T, 1, IN, ROW, IN, ROW>(a2, dys, LDI, 0, us, LDI, 0, m0, n0 + 16 * t, D);
+          s[t] = a1[0];
+          dp[t] = a2[0];
+        }
+      }
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        if (t >= nt) continue;
+        const int key = n0 + 16 * t + lane % 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + 4 * g + e;
+          const bool ok = row < nr && key < nb;
+          const float pv = ok ? __builtin_amdgcn_exp2f(s[t][e] * p.sc2 + h2k[key] - lsel[row]) : 0.f;
+          const float dv = ok ? dp[t][e] : 0.f;
+          ps[row * LDP + key] = pv;
+          dws[row * LDP + key] = dv;
+          part[e] += pv * dv;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + 4 * g + e;
-        const bool ok = row < nr && key < nb;
-        ps[row * LDP + key] = ok ? __builtin_amdgcn_exp2f(s[e] * p.sc2 + h2k[key] - lsel[row]) : 0.f;
-        dws[row * LDP + key] = ok ? dp[e] : 0.f;
+        const float v = sum16(part[e]);
+        if (lane % 16 == 0) atomicAdd(&dl[m0 + 4 * g + e], v);
       }
     }
     __syncthreads();
-    // D_l = sum_k P dP
-    for (int r = threadIdx.x; r < RB; r += THREADS) {
-      float acc = 0.f;
-      for (int k = 0; k < nbp; ++k) acc += ps[r * LDP + k] * dws[r * LDP + k];
-      dl[r] = acc;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < RB * nbp; idx += THREADS) {
+    // dW = P (dP - D)
+    for (int idx = threadIdx.x; idx < RB * nbp; idx += NTH) {
       const int r = idx / nbp, k = idx % nbp;
       dws[r * LDP + k] = ps[r * LDP + k] * (dws[r * LDP + k] - dl[r]);
     }
     __syncthreads();
-    // dQ (stage-2 part) = sc dW c, RB x D
-    for (int t = wave; t < (RB / 16) * (D / 16); t += WAVES) {
-      const int m0 = (t / (D / 16)) * 16, n0 = (t % (D / 16)) * 16;
-      const f32x4 a = tile_mma<T, ROW, true, COL, false>(dws, LDP, cs, LDI, m0, n0, nbp,
-                                                          f32x4{0.f, 0.f, 0.f, 0.f});
-      const int d = n0 + lane % 16;
+    // dQ (stage-2 part) = sc dW c: strips of one row tile x DQ d tiles
+    for (int st = wave; st < (RB / 16) * (DT / DQ); st += NW) {
+      const int m0 = (st / (DT / DQ)) * 16, h = st % (DT / DQ);
+      {
+      f32x4 a[DQ];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + 4 * g + e;
-        if (row < nr) p.dq2[((size_t)sl * p.N + col.at(l0 + row)) * D + d] = a[e] * p.sc;
+      for (int t = 0; t < DQ; ++t) a[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, IN, ROW>(a, dws, LDP, 0, ct, LDN, 0, m0, 16 * DQ * h, nbp);
+      else strip_mma<T, DQ, F32, ROW, IN, COL>(a, dws, LDP, 0, cs, LDI, 0, m0, 16 * DQ * h, nbp);
+#pragma unroll
+      for (int t = 0; t < DQ; ++t) {
+        const int d = 16 * (DQ * h + t) + lane % 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + 4 * g + e;
+          if (row < nr) p.dq2[((size_t)sl * p.N + col.at(l0 + row)) * D + d] = a[t][e] * p.sc;
+        }
+      }
       }
     }
-    // dc += dW^T q, du += P^T dY (NB x D, over the chunk's rows)
+    // dc += dW^T q, du += P^T dY: strips of one key tile over all d tiles;
+    // the strip's wave also adds the key tile's column sums of dW to dH
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) {
-      const int t = wave + WAVES * j;
-      const int m0 = (t / (D / 16)) * 16, n0 = (t % (D / 16)) * 16;
+    for (int s = 0; s < SK; ++s) {
+      const int m0 = (wave + NW * s) * 16;
       if (m0 >= nbp) continue;
-      adc[j] = tile_mma<T, COL, true, COL, false>(dws, LDP, qs, LDI, m0, n0, RB, adc[j]);
-      adu[j] = tile_mma<T, COL, true, COL, false>(ps, LDP, dys, LDI, m0, n0, RB, adu[j]);
-    }
-    for (int k = threadIdx.x; k < nbp; k += THREADS) {
-      float acc = 0.f;
-      for (int r = 0; r < RB; ++r) acc += dws[r * LDP + k];
-      dhk[k] += acc;
+      {
+        float cs8 = 0.f;                      // rows 8g .. 8g + 7 of key m0 + lane % 16
+#pragma unroll
+        for (int e = 0; e < RB / 4; ++e) cs8 += dws[(g * (RB / 4) + e) * LDP + m0 + lane % 16];
+        cs8 += __shfl_xor(cs8, 16);
+        cs8 += __shfl_xor(cs8, 32);
+        if (g == 0) dhk[m0 + lane % 16] += cs8;
+      }
+#pragma unroll
+      for (int h = 0; h < DT / DS; ++h) {
+        f32x4 (&c)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adc[s][DS * h]);
+        f32x4 (&u)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adu[s][DS * h]);
+        strip_mma<T, DS, F32, COL, IN, ROW>(c, dws, LDP, 0, qt, LDR, 0, m0, 16 * DS * h, RB);
+        strip_mma<T, DS, F32, COL, IN, ROW>(u, ps, LDP, 0, dyt, LDR, 0, m0, 16 * DS * h, RB);
+      }
     }
   }
   // per-key results
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) {
-    const int t = wave + WAVES * j;
-    const int m0 = (t / (D / 16)) * 16, n0 = (t % (D / 16)) * 16;
-    const int d = n0 + lane % 16;
+  for (int s = 0; s < SK; ++s) {
+    const int m0 = (wave + NW * s) * 16;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = m0 + 4 * g + e;
-      if (key >= nb) continue;
-      const size_t row = xb + key * xs;
-      p.dcx[row * D + d] = adc[j][e] * p.sc;
-      p.dux[row * D + d] = adu[j][e];
+    for (int t = 0; t < DT; ++t) {
+      const int d = 16 * t + lane % 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = m0 + 4 * g + e;
+        if (key >= nb) continue;
+        const size_t row = xb + key * xs;
+        p.dcx[row * D + d] = adc[s][t][e] * p.sc;
+        p.dux[row * D + d] = adu[s][t][e];
+      }
     }
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < nb; k += THREADS) p.dhx[xb + k * xs] = dhk[k];
+  for (int k = threadIdx.x; k < nb; k += NTH) p.dhx[xb + k * xs] = dhk[k];
 }
 
 // ---------------------------------------------------------------------------
 // Stage 1 backward: one workgroup per (slice, block k).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(THREADS) void stage1_bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdParams p) {
   typedef BwdShape<T, D> SH;
-  constexpr int NB = SH::NB, RB = SH::RB, LDI = SH::LDI, LDF = SH::LDF, LDP = SH::LDP;
-  constexpr int MJ = (NB / 16) * (D / 16) / WAVES;          // dK, dV tiles per wave
+  constexpr int NW = SH::NW, NTH = SH::NTH;
+  constexpr int NB = SH::NB, RB = SH::RB, LDI = SH::LDI, LDN = SH::LDN, LDR = SH::LDR, LDP = SH::LDP;
+  constexpr int DT = D / 16, NG = SH::NG;
+  constexpr int DS = DT < 4 ? DT : 4;                        // d tiles per dK, dV strip
+  constexpr int DQ = SH::DQ;                                 // d tiles per dQ strip
+  constexpr int SK = SH::SK;                                 // key-tile strips of dK, dV per wave
+  constexpr bool SPLIT = !std::is_same<T, float>::value;
+  constexpr size_t TPL = (size_t)D * LDR;                    // plane offset of the transposed grads
   __shared__ __attribute__((aligned(16))) T ks[NB * LDI];
   __shared__ __attribute__((aligned(16))) T vs[NB * LDI];
+  __shared__ __attribute__((aligned(16))) T kt[SH::KT_COPY ? D * LDN : 1];   // K^T
   __shared__ __attribute__((aligned(16))) T qs[RB * LDI];
-  __shared__ __attribute__((aligned(16))) float dus[RB * LDF];
-  __shared__ __attribute__((aligned(16))) float dcs[RB * LDF];
+  __shared__ __attribute__((aligned(16))) T qt[D * LDR];                   // q^T of the chunk
+  __shared__ __attribute__((aligned(16))) T dut[(SPLIT ? 2 : 1) * D * LDR]; // du^T (hi, lo)
+  __shared__ __attribute__((aligned(16))) T dct[(SPLIT ? 2 : 1) * D * LDR]; // dc^T (hi, lo)
   __shared__ __attribute__((aligned(16))) float rs[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dzs[RB * LDP];
   __shared__ float lser[RB], dhr[RB], gr[RB], hr[RB];
@@ -290,100 +406,140 @@ __global__ __launch_bounds__(THREADS) void stage1_bwd_kernel(BwdParams p) {
   const T* V = static_cast<const T*>(p.v) + (size_t)sl * p.N * D;
   const AxisMap row = p.map.row_axis(k);
 
-  bwd_load_rows<T, D, LDI>(ks, NB, nb, [&](int j) { return K + row.at(j) * D; });
-  bwd_load_rows<T, D, LDI>(vs, NB, nb, [&](int j) { return V + row.at(j) * D; });
-  f32x4 adk[MJ], adv[MJ];
+  bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(ks, kt, NB, nb, [&](int j) { return K + row.at(j) * D; });
+  bwd_load_rows<T, D, LDI, NTH>(vs, nullptr, NB, nb, [&](int j) { return V + row.at(j) * D; });
+  f32x4 adk[SK][DT], adv[SK][DT];
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) adk[j] = adv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < SK; ++s)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) adk[s][t] = adv[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int i0 = 0; i0 < p.b2; i0 += RB) {
     const int nr = min(RB, p.b2 - i0);
     __syncthreads();
-    bwd_load_rows<T, D, LDI>(qs, RB, nr, [&](int r) { return Q + row.at(i0 + r) * D; });
-    bwd_load_rows_f32<D, LDF>(dus, RB, nr, [&](int r) { return p.dux + (xb + i0 + r) * D; });
-    bwd_load_rows_f32<D, LDF>(dcs, RB, nr, [&](int r) { return p.dcx + (xb + i0 + r) * D; });
-    for (int r = threadIdx.x; r < RB; r += THREADS) {
+    bwd_load_rows<T, D, LDI, NTH, true, LDR>(qs, qt, RB, nr, [&](int r) { return Q + row.at(i0 + r) * D; });
+    bwd_load_rows_tplanes<T, D, LDR, NTH>(dut, TPL, RB, nr, [&](int r) { return p.dux + (xb + i0 + r) * D; });
+    bwd_load_rows_tplanes<T, D, LDR, NTH>(dct, TPL, RB, nr, [&](int r) { return p.dcx + (xb + i0 + r) * D; });
+    for (int r = threadIdx.x; r < RB; r += NTH) {
       lser[r] = r < nr ? p.lser[xb + i0 + r] : 0.f;
       dhr[r] = r < nr ? p.dhx[xb + i0 + r] : 0.f;
+      gr[r] = 0.f;
+      hr[r] = 0.f;
     }
     __syncthreads();
-    // R = exp2(sc2 q.k - lse2) and dR = du V^T + dc K^T, RB x nbp
-    for (int t = wave; t < (RB / 16) * (nbp / 16); t += WAVES) {
-      const int m0 = (t / (nbp / 16)) * 16, n0 = (t % (nbp / 16)) * 16;
-      const f32x4 z = tile_mma<T, ROW, false, ROW, false>(qs, LDI, ks, LDI, m0, n0, D,
-                                                          f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 dr = tile_mma<T, ROW, true, ROW, false>(dus, LDF, vs, LDI, m0, n0, D, f32x4{0.f, 0.f, 0.f, 0.f});
-      dr = tile_mma<T, ROW, true, ROW, false>(dcs, LDF, ks, LDI, m0, n0, D, dr);
-      const int key = n0 + lane % 16;
+    // R = exp2(sc2 q.k - lse2), dR = du V^T + dc K^T, G = rowsum(R dR) and
+    // H = -rowsum(R log R), in strips of one row tile x NG key tiles
+    const int ng = (nbp / 16 + NG - 1) / NG;
+    for (int st = wave; st < (RB / 16) * ng; st += NW) {
+      const int m0 = (st / ng) * 16, n0 = (st % ng) * 16 * NG;
+      const int nt = min(NG, nbp / 16 - n0 / 16);
+      f32x4 z[NG], dr[NG];
+#pragma unroll
+      for (int t = 0; t < NG; ++t) z[t] = dr[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (nt == NG) {
+        strip_mma<T, NG, IN, ROW, IN, ROW>(z, qs, LDI, 0, ks, LDI, 0, m0, n0, D);
+        strip_mma<T, NG, PL, COL, IN, ROW>(dr, dut, LDR, TPL, vs, LDI, 0, m0, n0, D);
+        strip_mma<T, NG, PL, COL, IN, ROW>(dr, dct, LDR, TPL, ks, LDI, 0, m0, n0, D);
+      } else {
+        for (int t = 0; t < nt; ++t) {
+          f32x4 a1[1] = {z[t]}, a2[1] = {dr[t]};
+          strip_mma<T, 1, IN, ROW, IN, ROW>(a1, qs, LDI, 0, ks, LDI, 0, m0, n0 + 16 * t, D);
+          strip_mma<T, 1, PL, COL, IN, ROW>(a2, dut, LDR, TPL, vs, LDI, 0, m0, n0 + 16 * t, D);
+          strip_mma<T, 1, PL, COL, IN, ROW>(a2, dct, LDR, TPL, ks, LDI, 0, m0, n0 + 16 * t, D);
+          z[t] = a1[0];
+          dr[t] = a2[0];
+        }
+      }
+      float pg[4] = {0.f, 0.f, 0.f, 0.f}, ph[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        if (t >= nt) continue;
+        const int key = n0 + 16 * t + lane % 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = m0 + 4 * g + e;
+          const bool ok = r < nr && key < nb;
+          const float lg2 = z[t][e] * p.sc2 - lser[r];        // log2 R
+          const float rv = ok ? __builtin_amdgcn_exp2f(lg2) : 0.f;
+          const float dv = ok ? dr[t][e] : 0.f;
+          rs[r * LDP + key] = rv;
+          dzs[r * LDP + key] = dv;
+          pg[e] += rv * dv;
+          ph[e] -= rv > 0.f ? rv * lg2 * LN2 : 0.f;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = m0 + 4 * g + e;
-        const bool ok = r < nr && key < nb;
-        rs[r * LDP + key] = ok ? __builtin_amdgcn_exp2f(z[e] * p.sc2 - lser[r]) : 0.f;
-        dzs[r * LDP + key] = ok ? dr[e] : 0.f;
+        const float vg = sum16(pg[e]), vh = sum16(ph[e]);
+        if (lane % 16 == 0) {
+          atomicAdd(&gr[m0 + 4 * g + e], vg);
+          atomicAdd(&hr[m0 + 4 * g + e], vh);
+        }
       }
-    }
-    __syncthreads();
-    // G_i = sum_j R dR and H_i = -sum_j R log R
-    for (int r = threadIdx.x; r < RB; r += THREADS) {
-      float ga = 0.f, ha = 0.f;
-      for (int j = 0; j < nbp; ++j) {
-        const float rv = rs[r * LDP + j];
-        ga += rv * dzs[r * LDP + j];
-        ha -= rv > 0.f ? rv * __logf(rv) : 0.f;
-      }
-      gr[r] = ga;
-      hr[r] = ha;
     }
     __syncthreads();
     // sc * dz = sc * (R (dR - G) - dH R (log R + H))
-    for (int idx = threadIdx.x; idx < RB * nbp; idx += THREADS) {
+    for (int idx = threadIdx.x; idx < RB * nbp; idx += NTH) {
       const int r = idx / nbp, j = idx % nbp;
       const float rv = rs[r * LDP + j];
       const float lg = rv > 0.f ? __logf(rv) : 0.f;
       dzs[r * LDP + j] = p.sc * rv * ((dzs[r * LDP + j] - gr[r]) - dhr[r] * (lg + hr[r]));
     }
     __syncthreads();
-    // dQ = dQ (stage 2) + sc dz K, RB x D
+    // dQ = dQ (stage 2) + sc dz K: strips of one row tile x DQ d tiles
     T* dQ = static_cast<T*>(p.dq) + (size_t)sl * p.N * D;
-    for (int t = wave; t < (RB / 16) * (D / 16); t += WAVES) {
-      const int m0 = (t / (D / 16)) * 16, n0 = (t % (D / 16)) * 16;
-      const f32x4 a = tile_mma<T, ROW, true, COL, false>(dzs, LDP, ks, LDI, m0, n0, nbp,
-                                                          f32x4{0.f, 0.f, 0.f, 0.f});
-      const int d = n0 + lane % 16;
+    for (int st = wave; st < (RB / 16) * (DT / DQ); st += NW) {
+      const int m0 = (st / (DT / DQ)) * 16, h = st % (DT / DQ);
+      {
+      f32x4 a[DQ];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = m0 + 4 * g + e;
-        if (r >= nr) continue;
-        const int64_t tok = row.at(i0 + r);
-        dQ[tok * D + d] = from_f32<T>(a[e] + p.dq2[((size_t)sl * p.N + tok) * D + d]);
+      for (int t = 0; t < DQ; ++t) a[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, IN, ROW>(a, dzs, LDP, 0, kt, LDN, 0, m0, 16 * DQ * h, nbp);
+      else strip_mma<T, DQ, F32, ROW, IN, COL>(a, dzs, LDP, 0, ks, LDI, 0, m0, 16 * DQ * h, nbp);
+#pragma unroll
+      for (int t = 0; t < DQ; ++t) {
+        const int d = 16 * (DQ * h + t) + lane % 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = m0 + 4 * g + e;
+          if (r >= nr) continue;
+          const int64_t tok = row.at(i0 + r);
+          dQ[tok * D + d] = from_f32<T>(a[t][e] + p.dq2[((size_t)sl * p.N + tok) * D + d]);
+        }
+      }
       }
     }
-    // dK += sc dz^T q + R^T dc, dV += R^T du (NB x D, over the chunk's rows)
+    // dK += sc dz^T q + R^T dc, dV += R^T du: strips of one key tile over all d tiles
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) {
-      const int t = wave + WAVES * j;
-      const int m0 = (t / (D / 16)) * 16, n0 = (t % (D / 16)) * 16;
+    for (int s = 0; s < SK; ++s) {
+      const int m0 = (wave + NW * s) * 16;
       if (m0 >= nbp) continue;
-      adk[j] = tile_mma<T, COL, true, COL, false>(dzs, LDP, qs, LDI, m0, n0, RB, adk[j]);
-      adk[j] = tile_mma<T, COL, true, COL, true>(rs, LDP, dcs, LDF, m0, n0, RB, adk[j]);
-      adv[j] = tile_mma<T, COL, true, COL, true>(rs, LDP, dus, LDF, m0, n0, RB, adv[j]);
+#pragma unroll
+      for (int h = 0; h < DT / DS; ++h) {
+        f32x4 (&a)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adk[s][DS * h]);
+        f32x4 (&v)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adv[s][DS * h]);
+        strip_mma<T, DS, F32, COL, IN, ROW>(a, dzs, LDP, 0, qt, LDR, 0, m0, 16 * DS * h, RB);
+        strip_mma<T, DS, F32, COL, PL, ROW>(a, rs, LDP, 0, dct, LDR, TPL, m0, 16 * DS * h, RB);
+        strip_mma<T, DS, F32, COL, PL, ROW>(v, rs, LDP, 0, dut, LDR, TPL, m0, 16 * DS * h, RB);
+      }
     }
   }
   T* dK = static_cast<T*>(p.dk) + (size_t)sl * p.N * D;
   T* dV = static_cast<T*>(p.dv) + (size_t)sl * p.N * D;
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) {
-    const int t = wave + WAVES * j;
-    const int m0 = (t / (D / 16)) * 16, n0 = (t % (D / 16)) * 16;
-    const int d = n0 + lane % 16;
+  for (int s = 0; s < SK; ++s) {
+    const int m0 = (wave + NW * s) * 16;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = m0 + 4 * g + e;
-      if (key >= nb) continue;
-      const int64_t tok = row.at(key);
-      dK[tok * D + d] = from_f32<T>(adk[j][e]);
-      dV[tok * D + d] = from_f32<T>(adv[j][e]);
+    for (int t = 0; t < DT; ++t) {
+      const int d = 16 * t + lane % 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = m0 + 4 * g + e;
+        if (key >= nb) continue;
+        const int64_t tok = row.at(key);
+        dK[tok * D + d] = from_f32<T>(adk[s][t][e]);
+        dV[tok * D + d] = from_f32<T>(adv[s][t][e]);
+      }
     }
   }
 }
@@ -406,8 +562,9 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
               reinterpret_cast<float*>(ws + pl.off_dcx), reinterpret_cast<float*>(ws + pl.off_dux),
               reinterpret_cast<float*>(ws + pl.off_dhx),
               pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2};
-  hipLaunchKernelGGL((stage2_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(THREADS), 0, st, p);
-  hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(THREADS), 0, st, p);
+  constexpr int NTH = BwdShape<T, D>::NTH;
+  hipLaunchKernelGGL((stage2_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(NTH), 0, st, p);
+  hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
   return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
 }
 
