@@ -181,14 +181,15 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
                                      void* const* events, int32_t n_events);
 
 /* Backward pass: dQ, dK, dV of <dY, Y> for Y = MonarchAttention(Q, K, V)
- * (all [batch, heads, seq_len, head_dim] in the problem's dtype; dY likewise).
+ * (Q, dY, dQ: [batch, heads, seq_len, head_dim] in the problem's dtype).
  * The pages train through the method (MonarchRT "Method" part (3): one-step
  * fine-tuning) without stating a backward; this is the exact gradient of
  * the forward's steps, computed by recomputing the forward's block softmaxes
  * from its normalisers (the forward state is rebuilt inside the call).
- * Covers steps = 1, c1 = c2 = 1, kv_heads = heads (or 0), seq_len =
- * b1*b2, and b1, b2 <= 128 (<= 64 for fp32 with head_dim 128); other
- * problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
+ * dK, dV have K's shape [batch, kv_heads, seq_len, head_dim]; with grouped
+ * K/V they sum over the query heads of each group.  Covers steps = 1,
+ * c1 = c2 = 1, seq_len = b1*b2, and b1, b2 <= 128 (<= 64 for fp32 with
+ * head_dim 128); other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
  * the plain c path (the T = 1 default), so these are its gradients.
  * workspace: at least monarch_attn_backward_workspace_size bytes, 256-byte
  * aligned, overlapping no other argument; dQ, dK, dV must not overlap each

@@ -193,18 +193,22 @@ def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layo
 def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
              workspace=None, out=None):
     """Gradients (dq, dk, dv) of <dy, forward(q, k, v, ...)> on the current
-    stream.  Covers what monarch_attn_backward documents (T = 1, untiled, one
-    K/V head per query head, no padding, blocks of at most 128 keys).
+    stream.  Covers what monarch_attn_backward documents (T = 1, untiled, no
+    padding, blocks of at most 128 keys; k, v may have fewer heads).
     out: optional (dq, dk, dv) tensors to write."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("dy", dy)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a HIP device tensor")
-        if t.dim() != 4 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor typed like q")
     B, H, N, D = q.shape
+    Hkv = k.shape[1]
+    if dy.shape != q.shape or k.shape != v.shape or (k.shape[0], k.shape[2], k.shape[3]) != (B, N, D) \
+            or H % Hkv:
+        raise ValueError("dy must be shaped like q, and k, v [batch, kv_heads, seq_len, head_dim]")
     prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, 0,
-                        kv_heads=H)
+                        kv_heads=Hkv)
     ws_bytes = backward_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)

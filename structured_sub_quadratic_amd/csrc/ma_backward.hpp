@@ -44,9 +44,11 @@ struct BwdParams {
   float* dq2;                       // [S, N, D] stage-2 part of dQ, token order
   float* dcx; float* dux;           // [rows, D] gradients of c and u
   float* dhx;                       // [rows] gradient of H_R (nats)
+  float* dkp; float* dvp;           // [S, N, D] per-query-head dK, dV (grouped K/V), or null
   GridMap map;
   int S, N, b1, b2;
   float sc, sc2;                    // scale, scale * log2(e)
+  int heads, group;                 // K/V slice of query slice sl: kv_slice(sl, heads, group)
 };
 
 template <typename T, int D> struct BwdShape {
@@ -402,8 +404,9 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   const int nb = p.b2, nbp = (nb + SH::KQ - 1) / SH::KQ * SH::KQ;
   const size_t xb = ((size_t)sl * p.b1 + k) * p.b2;          // exchange row of (k, i = 0)
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
-  const T* K = static_cast<const T*>(p.k) + (size_t)sl * p.N * D;
-  const T* V = static_cast<const T*>(p.v) + (size_t)sl * p.N * D;
+  const int kvs = kv_slice(sl, p.heads, p.group);
+  const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
+  const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
   const AxisMap row = p.map.row_axis(k);
 
   bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(ks, kt, NB, nb, [&](int j) { return K + row.at(j) * D; });
@@ -537,11 +540,37 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
         const int key = m0 + 4 * g + e;
         if (key >= nb) continue;
         const int64_t tok = row.at(key);
-        dK[tok * D + d] = from_f32<T>(adk[s][t][e]);
-        dV[tok * D + d] = from_f32<T>(adv[s][t][e]);
+        if (p.dkp) {     // grouped K/V: this query head's share, summed by kv_reduce_kernel
+          p.dkp[((size_t)sl * p.N + tok) * D + d] = adk[s][t][e];
+          p.dvp[((size_t)sl * p.N + tok) * D + d] = adv[s][t][e];
+        } else {
+          dK[tok * D + d] = from_f32<T>(adk[s][t][e]);
+          dV[tok * D + d] = from_f32<T>(adv[s][t][e]);
+        }
       }
     }
   }
+}
+
+// Grouped K/V: dK, dV of K/V slice kv = the sums of the per-query-head
+// shares of its `group` query heads (consecutive heads of one batch).
+template <typename T>
+__global__ __launch_bounds__(256) void kv_reduce_kernel(const float* dkp, const float* dvp, T* dk, T* dv,
+                                                        int heads, int group, size_t per_slice,
+                                                        size_t total) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const size_t kv = idx / per_slice, off = idx % per_slice;
+  const int hkv = heads / group;
+  const size_t b = kv / hkv, h0 = (kv % hkv) * group;
+  float sk = 0.f, sv = 0.f;
+  for (int j = 0; j < group; ++j) {
+    const size_t src = (b * heads + h0 + j) * per_slice + off;
+    sk += dkp[src];
+    sv += dvp[src];
+  }
+  dk[idx] = from_f32<T>(sk);
+  dv[idx] = from_f32<T>(sv);
 }
 
 // The whole backward call on stream st: the forward's stage 1 (last-step
@@ -561,10 +590,17 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
               reinterpret_cast<float*>(ws + pl.off_dq2),
               reinterpret_cast<float*>(ws + pl.off_dcx), reinterpret_cast<float*>(ws + pl.off_dux),
               reinterpret_cast<float*>(ws + pl.off_dhx),
-              pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2};
+              pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
+              pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
+              pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2, pl.heads, pl.group};
   constexpr int NTH = BwdShape<T, D>::NTH;
   hipLaunchKernelGGL((stage2_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(NTH), 0, st, p);
   hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
+  if (pl.group > 1) {
+    const size_t per = (size_t)pl.N * D, total = (size_t)pl.S / pl.group * per;
+    hipLaunchKernelGGL((kv_reduce_kernel<T>), dim3(grid1((total + 255) / 256)), dim3(256), 0, st, p.dkp,
+                       p.dvp, static_cast<T*>(b.dk), static_cast<T*>(b.dv), pl.heads, pl.group, per, total);
+  }
   return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
 }
 

@@ -99,12 +99,16 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
   // tile means in bf16 for the copied-tile first step of the plain c path
   pl.off_qbar_lp = off;
   if (pl.need_qbar_lp) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * pl.elt);
-  pl.off_dq2 = pl.off_dcx = pl.off_dux = pl.off_dhx = off;
+  pl.off_dq2 = pl.off_dcx = pl.off_dux = pl.off_dhx = pl.off_dkp = pl.off_dvp = off;
   if (backward) {
     pl.off_dq2 = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
     pl.off_dcx = off; off = align_up(off + rows * pl.D * 4);
     pl.off_dux = off; off = align_up(off + rows * pl.D * 4);
     pl.off_dhx = off; off = align_up(off + rows * 4);
+    if (pl.group > 1) {   // per-query-head shares of dK, dV
+      pl.off_dkp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
+      pl.off_dvp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
+    }
   }
   pl.total = off;
   return pl;
@@ -156,13 +160,12 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   return run_f32_128(pl, b, st, events, n_events);
 }
 
-// The backward covers T = 1, untiled, one K/V head per query head, no
-// padding, and blocks whose keys fit LDS whole.
+// The backward covers T = 1, untiled, no padding, and blocks whose keys fit
+// LDS whole (grouped K/V included).
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
   if (p->steps != 1 || p->c1 != 1 || p->c2 != 1) return MA_ERR_UNSUPPORTED;
-  if (p->kv_heads != 0 && p->kv_heads != p->heads) return MA_ERR_UNSUPPORTED;
   if ((int64_t)p->b1 * p->b2 != p->seq_len) return MA_ERR_UNSUPPORTED;
   if (p->b1 > bwd_max_block(p) || p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
   return MA_OK;
@@ -181,19 +184,21 @@ ma_status backward_impl(const ma_problem* p, const void* q, const void* k, const
     if (!x || misaligned(x, 16)) return MA_ERR_INVALID_ARGUMENT;
   for (void* x : out)
     if (!x || misaligned(x, 16)) return MA_ERR_INVALID_ARGUMENT;
-  const size_t tbytes = (size_t)pl.S * pl.N * pl.D * pl.elt;
+  const size_t tbytes = (size_t)pl.S * pl.N * pl.D * pl.elt;     // q, dy, dq
+  const size_t kvbytes = tbytes / pl.group;                       // k, v, dk, dv
+  const size_t isz[] = {tbytes, kvbytes, kvbytes, tbytes}, osz[] = {tbytes, kvbytes, kvbytes};
   for (int a = 0; a < 3; ++a) {
-    for (const void* x : in)
-      if (overlaps(out[a], tbytes, x, tbytes)) return MA_ERR_INVALID_ARGUMENT;
+    for (int c = 0; c < 4; ++c)
+      if (overlaps(out[a], osz[a], in[c], isz[c])) return MA_ERR_INVALID_ARGUMENT;
     for (int c = a + 1; c < 3; ++c)
-      if (overlaps(out[a], tbytes, out[c], tbytes)) return MA_ERR_INVALID_ARGUMENT;
+      if (overlaps(out[a], osz[a], out[c], osz[c])) return MA_ERR_INVALID_ARGUMENT;
   }
   if (workspace_bytes < pl.total) return MA_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || misaligned(workspace, ALIGN)) return MA_ERR_INVALID_ARGUMENT;
-  for (const void* x : in)
-    if (overlaps(workspace, pl.total, x, tbytes)) return MA_ERR_INVALID_ARGUMENT;
-  for (void* o : out)
-    if (overlaps(workspace, pl.total, o, tbytes)) return MA_ERR_INVALID_ARGUMENT;
+  for (int c = 0; c < 4; ++c)
+    if (overlaps(workspace, pl.total, in[c], isz[c])) return MA_ERR_INVALID_ARGUMENT;
+  for (int a = 0; a < 3; ++a)
+    if (overlaps(workspace, pl.total, out[a], osz[a])) return MA_ERR_INVALID_ARGUMENT;
   BwdBufs b{q, k, v, dy, dq, dk, dv, static_cast<char*>(workspace)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (pl.dtype == MA_BF16)

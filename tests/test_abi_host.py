@@ -142,7 +142,7 @@ def test_status_strings(lib):
     (dict(), 0),
     (dict(steps=2), 2),                       # T > 1 not covered by the backward
     (dict(c1=2), 2),                          # tiled
-    (dict(kv_heads=1), 2),                    # grouped K/V
+    (dict(kv_heads=1), 0),                    # grouped K/V
     (dict(seq_len=250), 2),                   # padded
     (dict(seq_len=256 * 200, b1=200, b2=256), 2),   # blocks wider than 128 keys
     (dict(seq_len=96 * 96, b1=96, b2=96, head_dim=128, dtype="f32"), 2),   # fp32 d128: 64 max

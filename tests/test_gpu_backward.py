@@ -43,8 +43,10 @@ def upstream(cfg, seed=77):
     return round_to_bf16(dY) if cfg.dtype == "bf16" else dY
 
 
-def check_backward(cfg, slices=None, tol=None):
+def check_backward(cfg, slices=None, tol=None, kv_heads=None):
     Q, K, V = make_inputs(cfg)
+    if kv_heads is not None:        # grouped-query attention: keep the first kv_heads
+        K, V = (np.ascontiguousarray(X[:, :kv_heads]) for X in (K, V))
     dY = upstream(cfg)
     got = run_backward(cfg, Q, K, V, dY)
     all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
@@ -52,7 +54,10 @@ def check_backward(cfg, slices=None, tol=None):
     ref = obw.backward(Q, K, V, dY, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
                        layout=cfg.layout, fhw=cfg.fhw, slices=slices)
     tol = TOL[cfg.dtype] if tol is None else tol
-    errs = {n: rel_err(g, r, slices) for n, g, r in zip(("dQ", "dK", "dV"), got, ref)}
+    group = cfg.heads // K.shape[1]
+    kv_slices = sorted({(b, h // group) for (b, h) in slices})
+    errs = {n: rel_err(g, r, slices if n == "dQ" else kv_slices)
+            for n, g, r in zip(("dQ", "dK", "dV"), got, ref)}
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{cfg.name}: {errs} (tol {tol})"
@@ -93,7 +98,6 @@ def test_video_layout():
 
 def test_linear_in_upstream_and_zero():
     """dQ, dK, dV are linear in dY: zero for dY = 0, doubled for 2 dY."""
-    import torch
     cfg = case("bwd linear", "f32", 64, 16, 16)
     Q, K, V = make_inputs(cfg)
     dY = upstream(cfg)
@@ -103,6 +107,13 @@ def test_linear_in_upstream_and_zero():
     for a, b, z in zip(g1, g2, g0):
         assert np.abs(z).max() == 0
         np.testing.assert_allclose(b, 2 * a, rtol=1e-5, atol=1e-6 * np.abs(a).max())
+
+
+@pytest.mark.parametrize("dtype,kvh", [("f32", 1), ("bf16", 2)])
+def test_grouped_query_attention(dtype, kvh):
+    """Four query heads over kv_heads K/V heads: dK, dV sum the group's shares."""
+    cfg = case(f"bwd gqa {dtype} kv{kvh}", dtype, 64, 40, 52, batch=2, heads=4)
+    check_backward(cfg, kv_heads=kvh)
 
 
 def test_n16k_backward_sampled():
