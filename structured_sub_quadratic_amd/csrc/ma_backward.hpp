@@ -68,6 +68,79 @@ template <typename T, int D> struct BwdShape {
   static constexpr int DQ = NW == 8 ? 1 : (D / 16 < 4 ? D / 16 : 4);   // d tiles per dQ strip
   static constexpr int NTH = NW * WAVE;
   static constexpr int SK = (NB / 16 + NW - 1) / NW;        // key-tile strips per wave
+  // the next row chunk's global inputs are held in registers while the
+  // current chunk computes (head_dim 64: a few registers a thread), and the
+  // stage-2 part of dQ is staged in LDS with them
+  static constexpr bool PREFETCH = D == 64;
+};
+
+// Register staging of up to RB rows of a matrix: the loads of the next row
+// chunk are issued before the current chunk computes and land in LDS at the
+// start of the next one.  Input-type rows (store: row major, optionally also
+// transposed) or fp32 rows (store: transposed hi/lo planes, or fp32 rows).
+template <typename T, int D, int RB, int NTH>
+struct RowsIn {
+  typedef typename Vec16<T>::type V;
+  static constexpr int VN = Vec16<T>::N, CH = D / VN, NT = (RB * CH + NTH - 1) / NTH;
+  V v[NT];
+  template <class Src> __device__ inline void load(int n, Src src) {
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
+      v[a] = V{};
+      if (task < RB * CH && j < n) v[a] = *reinterpret_cast<const V*>(src(j) + c * VN);
+    }
+  }
+  template <int LD, bool TR, int LDT> __device__ inline void store(T* dst, T* dt) const {
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
+      if (task >= RB * CH) continue;
+      *reinterpret_cast<V*>(dst + (size_t)j * LD + c * VN) = v[a];
+      if constexpr (TR) {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) dt[(size_t)(c * VN + e) * LDT + j] = v[a][e];
+      }
+    }
+  }
+};
+template <typename T, int D, int RB, int NTH>
+struct RowsF32 {
+  static constexpr int CH = D / 4, NT = (RB * CH + NTH - 1) / NTH;
+  f32x4 v[NT];
+  template <class Src> __device__ inline void load(int n, Src src) {
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
+      v[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (task < RB * CH && j < n) v[a] = *reinterpret_cast<const f32x4*>(src(j) + c * 4);
+    }
+  }
+  template <int LDT> __device__ inline void store_tplanes(T* hi, size_t plane) const {
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
+      if (task >= RB * CH) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        T* at = hi + (size_t)(c * 4 + e) * LDT + j;
+        if constexpr (std::is_same<T, float>::value) {
+          *at = v[a][e];
+        } else {
+          const bf16 h = (bf16)v[a][e];
+          at[0] = h;
+          at[plane] = (bf16)(v[a][e] - (float)h);
+        }
+      }
+    }
+  }
+  template <int LD> __device__ inline void store_rows(float* dst) const {
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
+      if (task < RB * CH) *reinterpret_cast<f32x4*>(dst + (size_t)j * LD + c * 4) = v[a];
+    }
+  }
 };
 
 // Operand access for one MFMA step: ROW reads X[idx][k] (k contiguous), COL
@@ -181,29 +254,6 @@ __device__ inline void bwd_load_rows(T* dst, T* dt, int NR, int n, Src src) {
     }
   }
 }
-// fp32 rows (gradients of c, u) into transposed planes of the element type:
-// hi[d][j] (and lo for bf16), zero for n <= j < NR.
-template <typename T, int D, int LDT, int NTH, class Src>
-__device__ inline void bwd_load_rows_tplanes(T* hi, size_t plane, int NR, int n, Src src) {
-  constexpr int CH = D / 4;
-  for (int task = threadIdx.x; task < NR * CH; task += NTH) {
-    const int j = task / CH, c = task % CH;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (j < n) v = *reinterpret_cast<const f32x4*>(src(j) + c * 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      T* at = hi + (size_t)(c * 4 + e) * LDT + j;
-      if constexpr (std::is_same<T, float>::value) {
-        *at = v[e];
-      } else {
-        const bf16 h = (bf16)v[e];
-        at[0] = h;
-        at[plane] = (bf16)(v[e] - (float)h);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Stage 2 backward: one workgroup per (slice, column i).
 // ---------------------------------------------------------------------------
@@ -250,14 +300,28 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
 #pragma unroll
     for (int t = 0; t < DT; ++t) adc[s][t] = adu[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  RowsIn<T, D, RB, NTH> pq, pdy;
+  float pls = 0.f;
+  auto fetch = [&](int l0) {
+    const int n = min(RB, p.b1 - l0);
+    pq.load(n, [&](int r) { return Q + col.at(l0 + r) * D; });
+    pdy.load(n, [&](int r) { return dY + col.at(l0 + r) * D; });
+    if (threadIdx.x < RB)
+      pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + threadIdx.x] : 0.f;
+  };
+  if constexpr (SH::PREFETCH) fetch(0);
   for (int l0 = 0; l0 < p.b1; l0 += RB) {
     const int nr = min(RB, p.b1 - l0);
     __syncthreads();
-    bwd_load_rows<T, D, LDI, NTH, true, LDR>(qs, qt, RB, nr, [&](int r) { return Q + col.at(l0 + r) * D; });
-    bwd_load_rows<T, D, LDI, NTH, true, LDR>(dys, dyt, RB, nr, [&](int r) { return dY + col.at(l0 + r) * D; });
-    for (int r = threadIdx.x; r < RB; r += NTH) {
-      lsel[r] = r < nr ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + r] : 0.f;
-      dl[r] = 0.f;
+    if constexpr (!SH::PREFETCH) fetch(l0);
+    pq.template store<LDI, true, LDR>(qs, qt);
+    pdy.template store<LDI, true, LDR>(dys, dyt);
+    if (threadIdx.x < RB) {
+      lsel[threadIdx.x] = pls;
+      dl[threadIdx.x] = 0.f;
+    }
+    if constexpr (SH::PREFETCH) {
+      if (l0 + RB < p.b1) fetch(l0 + RB);     // in flight while this chunk computes
     }
     __syncthreads();
     // P = exp2(sc2 q.c + h2 - lse2), dP = dY u^T and D = rowsum(P dP), in
@@ -398,6 +462,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   __shared__ __attribute__((aligned(16))) float rs[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dzs[RB * LDP];
   __shared__ float lser[RB], dhr[RB], gr[RB], hr[RB];
+  __shared__ __attribute__((aligned(16))) float dq2s[SH::PREFETCH ? RB * (D + 4) : 1];   // dQ (stage 2)
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int k = blockIdx.x % p.b1, sl = blockIdx.x / p.b1;
@@ -417,17 +482,38 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
 #pragma unroll
     for (int t = 0; t < DT; ++t) adk[s][t] = adv[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  RowsIn<T, D, RB, NTH> pq;
+  RowsF32<T, D, RB, NTH> pdu, pdc, pdq;
+  float pls = 0.f, pdh = 0.f;
+  auto fetch = [&](int i0) {
+    const int n = min(RB, p.b2 - i0);
+    pq.load(n, [&](int r) { return Q + row.at(i0 + r) * D; });
+    pdu.load(n, [&](int r) { return p.dux + (xb + i0 + r) * D; });
+    pdc.load(n, [&](int r) { return p.dcx + (xb + i0 + r) * D; });
+    if constexpr (SH::PREFETCH)
+      pdq.load(n, [&](int r) { return p.dq2 + ((size_t)sl * p.N + row.at(i0 + r)) * D; });
+    if (threadIdx.x < RB) {
+      pls = (int)threadIdx.x < n ? p.lser[xb + i0 + threadIdx.x] : 0.f;
+      pdh = (int)threadIdx.x < n ? p.dhx[xb + i0 + threadIdx.x] : 0.f;
+    }
+  };
+  if constexpr (SH::PREFETCH) fetch(0);
   for (int i0 = 0; i0 < p.b2; i0 += RB) {
     const int nr = min(RB, p.b2 - i0);
     __syncthreads();
-    bwd_load_rows<T, D, LDI, NTH, true, LDR>(qs, qt, RB, nr, [&](int r) { return Q + row.at(i0 + r) * D; });
-    bwd_load_rows_tplanes<T, D, LDR, NTH>(dut, TPL, RB, nr, [&](int r) { return p.dux + (xb + i0 + r) * D; });
-    bwd_load_rows_tplanes<T, D, LDR, NTH>(dct, TPL, RB, nr, [&](int r) { return p.dcx + (xb + i0 + r) * D; });
-    for (int r = threadIdx.x; r < RB; r += NTH) {
-      lser[r] = r < nr ? p.lser[xb + i0 + r] : 0.f;
-      dhr[r] = r < nr ? p.dhx[xb + i0 + r] : 0.f;
-      gr[r] = 0.f;
-      hr[r] = 0.f;
+    if constexpr (!SH::PREFETCH) fetch(i0);
+    pq.template store<LDI, true, LDR>(qs, qt);
+    pdu.template store_tplanes<LDR>(dut, TPL);
+    pdc.template store_tplanes<LDR>(dct, TPL);
+    if constexpr (SH::PREFETCH) pdq.template store_rows<D + 4>(dq2s);
+    if (threadIdx.x < RB) {
+      lser[threadIdx.x] = pls;
+      dhr[threadIdx.x] = pdh;
+      gr[threadIdx.x] = 0.f;
+      hr[threadIdx.x] = 0.f;
+    }
+    if constexpr (SH::PREFETCH) {
+      if (i0 + RB < p.b2) fetch(i0 + RB);     // in flight while this chunk computes
     }
     __syncthreads();
     // R = exp2(sc2 q.k - lse2), dR = du V^T + dc K^T, G = rowsum(R dR) and
@@ -507,7 +593,8 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
           const int r = m0 + 4 * g + e;
           if (r >= nr) continue;
           const int64_t tok = row.at(i0 + r);
-          dQ[tok * D + d] = from_f32<T>(a[t][e] + p.dq2[((size_t)sl * p.N + tok) * D + d]);
+          const float q2 = SH::PREFETCH ? dq2s[r * (D + 4) + d] : p.dq2[((size_t)sl * p.N + tok) * D + d];
+          dQ[tok * D + d] = from_f32<T>(a[t][e] + q2);
         }
       }
       }
