@@ -72,6 +72,9 @@ template <typename T, int D> struct BwdShape {
   // current chunk computes (head_dim 64: a few registers a thread), and the
   // stage-2 part of dQ is staged in LDS with them
   static constexpr bool PREFETCH = D == 64;
+  // rows of a stage-2 column (its key count b1) whose D = rowsum(P dP) fit
+  // LDS when the keys are walked in several chunks of NB
+  static constexpr int MAXC = (F32 && D == 128) ? 1024 : 2048;
 };
 
 // Register staging of up to RB rows of a matrix: the loads of the next row
@@ -276,10 +279,11 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
   __shared__ __attribute__((aligned(16))) float ps[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dws[RB * LDP];
   __shared__ float h2k[NB], dhk[NB], lsel[RB], dl[RB];
+  __shared__ float dall[SH::MAXC];     // D of every row, when the keys take several chunks
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int i = blockIdx.x % p.b2, sl = blockIdx.x / p.b2;
-  const int nb = p.b1, nbp = (nb + SH::KQ - 1) / SH::KQ * SH::KQ;
+  const int nkc = (p.b1 + NB - 1) / NB;                      // key chunks of NB keys
   const size_t xs = (size_t)p.b2;                            // exchange stride between keys
   const size_t xb = (size_t)sl * p.b1 * p.b2 + i;            // exchange row of key 0
   const T* C = static_cast<const T*>(p.cx);
@@ -287,19 +291,18 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
   const T* dY = static_cast<const T*>(p.dy) + (size_t)sl * p.N * D;
   const AxisMap col = p.map.col_axis(i);
-
-  bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(cs, ct, NB, nb, [&](int k) { return C + (xb + k * xs) * D; });
-  bwd_load_rows<T, D, LDI, NTH>(us, nullptr, NB, nb, [&](int k) { return U + (xb + k * xs) * D; });
-  for (int k = threadIdx.x; k < NB; k += NTH) {
-    h2k[k] = k < nb ? p.h2x[xb + k * xs] : 0.f;
-    dhk[k] = 0.f;
-  }
-  f32x4 adc[SK][DT], adu[SK][DT];
-#pragma unroll
-  for (int s = 0; s < SK; ++s)
-#pragma unroll
-    for (int t = 0; t < DT; ++t) adc[s][t] = adu[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  int k0 = 0, nb = 0, nbp = 0;                               // current key chunk
+  auto load_keys = [&](int kc) {
+    k0 = kc * NB;
+    nb = min(NB, p.b1 - k0);
+    nbp = (nb + SH::KQ - 1) / SH::KQ * SH::KQ;
+    bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(cs, ct, NB, nb, [&](int k) { return C + (xb + (k0 + k) * xs) * D; });
+    bwd_load_rows<T, D, LDI, NTH>(us, nullptr, NB, nb, [&](int k) { return U + (xb + (k0 + k) * xs) * D; });
+    for (int k = threadIdx.x; k < NB; k += NTH) {
+      h2k[k] = k < nb ? p.h2x[xb + (k0 + k) * xs] : 0.f;
+      dhk[k] = 0.f;
+    }
+  };
   RowsIn<T, D, RB, NTH> pq, pdy;
   float pls = 0.f;
   auto fetch = [&](int l0) {
@@ -309,23 +312,10 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
     if (threadIdx.x < RB)
       pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + threadIdx.x] : 0.f;
   };
-  if constexpr (SH::PREFETCH) fetch(0);
-  for (int l0 = 0; l0 < p.b1; l0 += RB) {
-    const int nr = min(RB, p.b1 - l0);
-    __syncthreads();
-    if constexpr (!SH::PREFETCH) fetch(l0);
-    pq.template store<LDI, true, LDR>(qs, qt);
-    pdy.template store<LDI, true, LDR>(dys, dyt);
-    if (threadIdx.x < RB) {
-      lsel[threadIdx.x] = pls;
-      dl[threadIdx.x] = 0.f;
-    }
-    if constexpr (SH::PREFETCH) {
-      if (l0 + RB < p.b1) fetch(l0 + RB);     // in flight while this chunk computes
-    }
-    __syncthreads();
-    // P = exp2(sc2 q.c + h2 - lse2), dP = dY u^T and D = rowsum(P dP), in
-    // strips of one row tile x NG key tiles
+  // P = exp2(sc2 q.c + h2 - lse2) and dP = dY u^T of a row chunk against the
+  // current key chunk, in strips of one row tile x NG key tiles; STORE keeps
+  // them in LDS, and the row sums of P dP go to dsum[row] (if not null)
+  auto scores = [&](int nr, bool store, float* dsum) {
     const int ng = (nbp / 16 + NG - 1) / NG;
     for (int st = wave; st < (RB / 16) * ng; st += NW) {
       const int m0 = (st / ng) * 16, n0 = (st % ng) * 16 * NG;
@@ -356,17 +346,66 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
           const bool ok = row < nr && key < nb;
           const float pv = ok ? __builtin_amdgcn_exp2f(s[t][e] * p.sc2 + h2k[key] - lsel[row]) : 0.f;
           const float dv = ok ? dp[t][e] : 0.f;
-          ps[row * LDP + key] = pv;
-          dws[row * LDP + key] = dv;
+          if (store) {
+            ps[row * LDP + key] = pv;
+            dws[row * LDP + key] = dv;
+          }
           part[e] += pv * dv;
         }
       }
+      if (dsum) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = sum16(part[e]);
-        if (lane % 16 == 0) atomicAdd(&dl[m0 + 4 * g + e], v);
+        for (int e = 0; e < 4; ++e) {
+          const float v = sum16(part[e]);
+          if (lane % 16 == 0) atomicAdd(&dsum[m0 + 4 * g + e], v);
+        }
       }
     }
+  };
+
+  if (nkc > 1) {
+    // first sweep: D = rowsum(P dP) of every row over all key chunks
+    for (int r = threadIdx.x; r < p.b1; r += NTH) dall[r] = 0.f;
+    for (int kc = 0; kc < nkc; ++kc) {
+      __syncthreads();
+      load_keys(kc);
+      for (int l0 = 0; l0 < p.b1; l0 += RB) {
+        const int nr = min(RB, p.b1 - l0);
+        __syncthreads();
+        fetch(l0);
+        pq.template store<LDI, false, LDR>(qs, nullptr);
+        pdy.template store<LDI, false, LDR>(dys, nullptr);
+        if (threadIdx.x < RB) lsel[threadIdx.x] = pls;
+        __syncthreads();
+        scores(nr, false, dall + l0);
+      }
+    }
+  }
+
+  for (int kc = 0; kc < nkc; ++kc) {
+  __syncthreads();
+  load_keys(kc);
+  f32x4 adc[SK][DT], adu[SK][DT];
+#pragma unroll
+  for (int s = 0; s < SK; ++s)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) adc[s][t] = adu[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (SH::PREFETCH) fetch(0);
+  for (int l0 = 0; l0 < p.b1; l0 += RB) {
+    const int nr = min(RB, p.b1 - l0);
+    __syncthreads();
+    if constexpr (!SH::PREFETCH) fetch(l0);
+    pq.template store<LDI, true, LDR>(qs, qt);
+    pdy.template store<LDI, true, LDR>(dys, dyt);
+    if (threadIdx.x < RB) {
+      lsel[threadIdx.x] = pls;
+      dl[threadIdx.x] = nkc > 1 && (int)threadIdx.x < nr ? dall[l0 + threadIdx.x] : 0.f;
+    }
+    if constexpr (SH::PREFETCH) {
+      if (l0 + RB < p.b1) fetch(l0 + RB);     // in flight while this chunk computes
+    }
+    __syncthreads();
+    scores(nr, true, nkc > 1 ? nullptr : dl);
     __syncthreads();
     // dW = P (dP - D)
     for (int idx = threadIdx.x; idx < RB * nbp; idx += NTH) {
@@ -389,7 +428,10 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
-          if (row < nr) p.dq2[((size_t)sl * p.N + col.at(l0 + row)) * D + d] = a[t][e] * p.sc;
+          if (row >= nr) continue;
+          float* at = p.dq2 + ((size_t)sl * p.N + col.at(l0 + row)) * D + d;
+          if (nkc > 1) atomicAdd(at, a[t][e] * p.sc);     // zeroed before the kernel
+          else *at = a[t][e] * p.sc;
         }
       }
       }
@@ -417,7 +459,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
       }
     }
   }
-  // per-key results
+  // per-key results of the key chunk
 #pragma unroll
   for (int s = 0; s < SK; ++s) {
     const int m0 = (wave + NW * s) * 16;
@@ -428,14 +470,21 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
       for (int e = 0; e < 4; ++e) {
         const int key = m0 + 4 * g + e;
         if (key >= nb) continue;
-        const size_t row = xb + key * xs;
+        const size_t row = xb + (k0 + key) * xs;
         p.dcx[row * D + d] = adc[s][t][e] * p.sc;
         p.dux[row * D + d] = adu[s][t][e];
       }
     }
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < nb; k += NTH) p.dhx[xb + k * xs] = dhk[k];
+  for (int k = threadIdx.x; k < nb; k += NTH) p.dhx[xb + (k0 + k) * xs] = dhk[k];
+  }
+}
+
+// Zero n floats (the dQ accumulator of a multi-chunk stage-2 backward).
+static __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, size_t n) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx < n) p[idx] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -681,6 +730,10 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
               pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
               pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2, pl.heads, pl.group};
   constexpr int NTH = BwdShape<T, D>::NTH;
+  if (pl.b1 > BwdShape<T, D>::NB) {       // dQ accumulates over key chunks
+    const size_t n = (size_t)pl.S * pl.N * D;
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2, n);
+  }
   hipLaunchKernelGGL((stage2_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(NTH), 0, st, p);
   hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
   if (pl.group > 1) {

@@ -94,10 +94,14 @@ struct BwdBufs {
   char* ws;
 };
 
-// Largest block (keys of either stage) of the backward: the keys of a block
-// or column sit in LDS whole.
+// Largest blocks of the backward: the keys of a stage-1 block sit in LDS
+// whole (b2 <= bwd_max_block); a stage-2 column walks its b1 keys in chunks
+// and keeps one fp32 value per row in LDS (b1 <= bwd_max_column).
 inline int bwd_max_block(const ma_problem* p) {
   return (p->dtype == MA_F32 && p->head_dim == 128) ? 64 : 128;
+}
+inline int bwd_max_column(const ma_problem* p) {
+  return (p->dtype == MA_F32 && p->head_dim == 128) ? 1024 : 2048;
 }
 
 // Kernel-launch entry of one element type and head dimension (one

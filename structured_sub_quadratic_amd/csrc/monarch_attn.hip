@@ -160,14 +160,15 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   return run_f32_128(pl, b, st, events, n_events);
 }
 
-// The backward covers T = 1, untiled, no padding, and blocks whose keys fit
-// LDS whole (grouped K/V included).
+// The backward covers T = 1, untiled, no padding, stage-1 blocks whose keys
+// fit LDS whole and stage-2 columns of at most bwd_max_column keys (grouped
+// K/V included).
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
   if (p->steps != 1 || p->c1 != 1 || p->c2 != 1) return MA_ERR_UNSUPPORTED;
   if ((int64_t)p->b1 * p->b2 != p->seq_len) return MA_ERR_UNSUPPORTED;
-  if (p->b1 > bwd_max_block(p) || p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
+  if (p->b1 > bwd_max_column(p) || p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
   return MA_OK;
 }
 

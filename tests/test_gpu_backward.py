@@ -91,6 +91,16 @@ def test_full_blocks(dtype):
     check_backward(case(f"bwd {b}x{b} {dtype} d128", dtype, 128, b, b, heads=1, seed=62))
 
 
+@pytest.mark.parametrize("dtype,d,b1", [("bf16", 64, 300), ("f32", 64, 200), ("bf16", 128, 150),
+                                         ("f32", 128, 130)])
+def test_columns_over_one_key_chunk(dtype, d, b1):
+    """Stage-2 columns of more than 128 (fp32 head_dim 128: 64) keys: the
+    keys are walked in chunks, D = rowsum(P dP) takes a first sweep, and dQ
+    accumulates over the chunks."""
+    b2 = 40 if (dtype == "f32" and d == 128) else 52
+    check_backward(case(f"bwd b1={b1} {dtype} d{d}", dtype, d, b1, b2, heads=1, data="normed"))
+
+
 def test_video_layout():
     cfg = case("bwd video w_fh", "bf16", 128, 8, 15, data="video", layout="w_fh", fhw=(3, 5, 8))
     check_backward(cfg)
@@ -120,3 +130,8 @@ def test_n16k_backward_sampled():
     """The 16k-token headline shape (12 heads); the oracle differentiates two
     slices, compared whole."""
     check_backward(WORKLOADS["n16k"], slices=[(0, 0), (0, 11)])
+
+
+def test_video_backward_sampled():
+    """The video latent (630, 52), d = 128, 12 heads: two slices compared whole."""
+    check_backward(WORKLOADS["video"], slices=[(0, 0), (0, 7)])
