@@ -188,9 +188,8 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * from its normalisers (the forward state is rebuilt inside the call).
  * dK, dV have K's shape [batch, kv_heads, seq_len, head_dim]; with grouped
  * K/V they sum over the query heads of each group.  Covers steps = 1,
- * c1 = c2 = 1, seq_len = b1*b2, b2 <= 128 and b1 <= 2048 (b2 <= 64 and
- * b1 <= 1024 for fp32 with head_dim 128); other problems return
- * MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
+ * c1 = c2 = 1, seq_len = b1*b2 and b2 <= 128 (<= 64 for fp32 with
+ * head_dim 128); other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
  * the plain c path (the T = 1 default), so these are its gradients.
  * workspace: at least monarch_attn_backward_workspace_size bytes, 256-byte
  * aligned, overlapping no other argument; dQ, dK, dV must not overlap each

@@ -45,6 +45,7 @@ struct BwdParams {
   float* dcx; float* dux;           // [rows, D] gradients of c and u
   float* dhx;                       // [rows] gradient of H_R (nats)
   float* dkp; float* dvp;           // [S, N, D] per-query-head dK, dV (grouped K/V), or null
+  float* dlx;                       // [S, b2, b1] D = rowsum(P dP) (columns of several key chunks)
   GridMap map;
   int S, N, b1, b2;
   float sc, sc2;                    // scale, scale * log2(e)
@@ -72,9 +73,11 @@ template <typename T, int D> struct BwdShape {
   // current chunk computes (head_dim 64: a few registers a thread), and the
   // stage-2 part of dQ is staged in LDS with them
   static constexpr bool PREFETCH = D == 64;
-  // rows of a stage-2 column (its key count b1) whose D = rowsum(P dP) fit
-  // LDS when the keys are walked in several chunks of NB
-  static constexpr int MAXC = (F32 && D == 128) ? 1024 : 2048;
+  // stage 2 (fewer live registers than stage 1) runs 8 waves at every
+  // head_dim, with the prefetch
+  static constexpr int NW2 = 8, NTH2 = NW2 * WAVE, NG2 = 2, DQ2 = 1;
+  static constexpr int SK2 = (NB / 16 + NW2 - 1) / NW2;
+  static constexpr int RG = (F32 && D == 128) ? 2 : 4;     // row chunks of a D-only workgroup
 };
 
 // Register staging of up to RB rows of a matrix: the loads of the next row
@@ -258,17 +261,24 @@ __device__ inline void bwd_load_rows(T* dst, T* dt, int NR, int n, Src src) {
   }
 }
 // ---------------------------------------------------------------------------
-// Stage 2 backward: one workgroup per (slice, column i).
+// Stage 2 backward.  MODE S2_COLUMN: one workgroup per (slice, column i)
+// whose b1 keys fit one chunk, D computed on the way.  Columns of more keys
+// take two launches: S2_ROWSUM, one workgroup per (slice, column, chunk of
+// RB rows), computes D = rowsum(P dP) over all key chunks into dlx; then
+// S2_KEYS, one workgroup per (slice, column, chunk of NB keys), the
+// gradients of that key chunk, adding its part of dQ with fp32 atomics.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdParams p) {
+enum { S2_COLUMN = 0, S2_ROWSUM = 1, S2_KEYS = 2 };
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdParams p) {
   typedef BwdShape<T, D> SH;
-  constexpr int NW = SH::NW, NTH = SH::NTH;
+  constexpr int NW = SH::NW2, NTH = SH::NTH2, RG = SH::RG;
   constexpr int NB = SH::NB, RB = SH::RB, LDI = SH::LDI, LDN = SH::LDN, LDR = SH::LDR, LDP = SH::LDP;
-  constexpr int DT = D / 16, NG = SH::NG;                    // d tiles; key tiles per score strip
+  constexpr int DT = D / 16, NG = SH::NG2;                   // d tiles; key tiles per score strip
   constexpr int DS = DT < 4 ? DT : 4;                        // d tiles per dc, du strip
-  constexpr int DQ = SH::DQ;                                 // d tiles per dQ strip
-  constexpr int SK = SH::SK;                                 // key-tile strips of dc, du per wave
+  constexpr int DQ = SH::DQ2;                                // d tiles per dQ strip
+  constexpr int SK = SH::SK2;                                // key-tile strips of dc, du per wave
   __shared__ __attribute__((aligned(16))) T cs[NB * LDI];
   __shared__ __attribute__((aligned(16))) T us[NB * LDI];
   __shared__ __attribute__((aligned(16))) T ct[SH::KT_COPY ? D * LDN : 1];   // c^T
@@ -279,11 +289,17 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
   __shared__ __attribute__((aligned(16))) float ps[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dws[RB * LDP];
   __shared__ float h2k[NB], dhk[NB], lsel[RB], dl[RB];
-  __shared__ float dall[SH::MAXC];     // D of every row, when the keys take several chunks
+  constexpr bool RS = MODE == S2_ROWSUM;   // D-only workgroup: RG row chunks stay in LDS
+  __shared__ __attribute__((aligned(16))) T qsb[RS ? RG * RB * LDI : 1];
+  __shared__ __attribute__((aligned(16))) T dysb[RS ? RG * RB * LDI : 1];
+  __shared__ float lsb[RS ? RG * RB : 1], dlb[RS ? RG * RB : 1];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
-  const int i = blockIdx.x % p.b2, sl = blockIdx.x / p.b2;
   const int nkc = (p.b1 + NB - 1) / NB;                      // key chunks of NB keys
+  const int nsub = MODE == S2_COLUMN ? 1 : (MODE == S2_ROWSUM ? (p.b1 + RG * RB - 1) / (RG * RB) : nkc);
+  const int sub = blockIdx.x % nsub;                         // row chunk (ROWSUM) or key chunk (KEYS)
+  const int i = (blockIdx.x / nsub) % p.b2, sl = blockIdx.x / nsub / p.b2;
+  float* const dlx = p.dlx + ((size_t)sl * p.b2 + i) * p.b1;   // D of the column's rows
   const size_t xs = (size_t)p.b2;                            // exchange stride between keys
   const size_t xb = (size_t)sl * p.b1 * p.b2 + i;            // exchange row of key 0
   const T* C = static_cast<const T*>(p.cx);
@@ -304,18 +320,20 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
     }
   };
   RowsIn<T, D, RB, NTH> pq, pdy;
-  float pls = 0.f;
+  float pls = 0.f, pdl = 0.f;
   auto fetch = [&](int l0) {
     const int n = min(RB, p.b1 - l0);
     pq.load(n, [&](int r) { return Q + col.at(l0 + r) * D; });
     pdy.load(n, [&](int r) { return dY + col.at(l0 + r) * D; });
-    if (threadIdx.x < RB)
+    if (threadIdx.x < RB) {
       pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + threadIdx.x] : 0.f;
+      if (MODE == S2_KEYS) pdl = (int)threadIdx.x < n ? dlx[l0 + threadIdx.x] : 0.f;
+    }
   };
   // P = exp2(sc2 q.c + h2 - lse2) and dP = dY u^T of a row chunk against the
   // current key chunk, in strips of one row tile x NG key tiles; STORE keeps
   // them in LDS, and the row sums of P dP go to dsum[row] (if not null)
-  auto scores = [&](int nr, bool store, float* dsum) {
+  auto scores = [&](int nr, bool store, float* dsum, const T* qs, const T* dys, const float* lsel) {
     const int ng = (nbp / 16 + NG - 1) / NG;
     for (int st = wave; st < (RB / 16) * ng; st += NW) {
       const int m0 = (st / ng) * 16, n0 = (st % ng) * 16 * NG;
@@ -363,49 +381,56 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
     }
   };
 
-  if (nkc > 1) {
-    // first sweep: D = rowsum(P dP) of every row over all key chunks
-    for (int r = threadIdx.x; r < p.b1; r += NTH) dall[r] = 0.f;
+  if constexpr (MODE == S2_ROWSUM) {
+    // D = rowsum(P dP) of RG row chunks over all key chunks
+    const int g0 = sub * RG * RB;
+    for (int c = 0; c < RG; ++c) {
+      const int l0 = g0 + c * RB;
+      fetch(l0);
+      pq.template store<LDI, false, LDR>(qsb + c * RB * LDI, nullptr);
+      pdy.template store<LDI, false, LDR>(dysb + c * RB * LDI, nullptr);
+      if (threadIdx.x < RB) {
+        lsb[c * RB + threadIdx.x] = pls;
+        dlb[c * RB + threadIdx.x] = 0.f;
+      }
+    }
     for (int kc = 0; kc < nkc; ++kc) {
       __syncthreads();
       load_keys(kc);
-      for (int l0 = 0; l0 < p.b1; l0 += RB) {
-        const int nr = min(RB, p.b1 - l0);
-        __syncthreads();
-        fetch(l0);
-        pq.template store<LDI, false, LDR>(qs, nullptr);
-        pdy.template store<LDI, false, LDR>(dys, nullptr);
-        if (threadIdx.x < RB) lsel[threadIdx.x] = pls;
-        __syncthreads();
-        scores(nr, false, dall + l0);
+      __syncthreads();
+      for (int c = 0; c < RG; ++c) {
+        const int l0 = g0 + c * RB;
+        if (l0 >= p.b1) break;
+        scores(min(RB, p.b1 - l0), false, dlb + c * RB, qsb + c * RB * LDI, dysb + c * RB * LDI, lsb + c * RB);
       }
     }
+    __syncthreads();
+    for (int r = threadIdx.x; r < RG * RB; r += NTH)
+      if (g0 + r < p.b1) dlx[g0 + r] = dlb[r];
+    return;
   }
 
-  for (int kc = 0; kc < nkc; ++kc) {
-  __syncthreads();
+  {
+  const int kc = MODE == S2_KEYS ? sub : 0;
   load_keys(kc);
   f32x4 adc[SK][DT], adu[SK][DT];
 #pragma unroll
   for (int s = 0; s < SK; ++s)
 #pragma unroll
     for (int t = 0; t < DT; ++t) adc[s][t] = adu[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (SH::PREFETCH) fetch(0);
+  fetch(0);
   for (int l0 = 0; l0 < p.b1; l0 += RB) {
     const int nr = min(RB, p.b1 - l0);
     __syncthreads();
-    if constexpr (!SH::PREFETCH) fetch(l0);
     pq.template store<LDI, true, LDR>(qs, qt);
     pdy.template store<LDI, true, LDR>(dys, dyt);
     if (threadIdx.x < RB) {
       lsel[threadIdx.x] = pls;
-      dl[threadIdx.x] = nkc > 1 && (int)threadIdx.x < nr ? dall[l0 + threadIdx.x] : 0.f;
+      dl[threadIdx.x] = MODE == S2_KEYS ? pdl : 0.f;
     }
-    if constexpr (SH::PREFETCH) {
-      if (l0 + RB < p.b1) fetch(l0 + RB);     // in flight while this chunk computes
-    }
+    if (l0 + RB < p.b1) fetch(l0 + RB);       // in flight while this chunk computes
     __syncthreads();
-    scores(nr, true, nkc > 1 ? nullptr : dl);
+    scores(nr, true, MODE == S2_KEYS ? nullptr : dl, qs, dys, lsel);
     __syncthreads();
     // dW = P (dP - D)
     for (int idx = threadIdx.x; idx < RB * nbp; idx += NTH) {
@@ -430,7 +455,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage2_bwd_kernel(BwdPa
           const int row = m0 + 4 * g + e;
           if (row >= nr) continue;
           float* at = p.dq2 + ((size_t)sl * p.N + col.at(l0 + row)) * D + d;
-          if (nkc > 1) atomicAdd(at, a[t][e] * p.sc);     // zeroed before the kernel
+          if (MODE == S2_KEYS) atomicAdd(at, a[t][e] * p.sc);     // zeroed before the kernel
           else *at = a[t][e] * p.sc;
         }
       }
@@ -728,13 +753,22 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
               reinterpret_cast<float*>(ws + pl.off_dhx),
               pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
               pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
+              reinterpret_cast<float*>(ws + pl.off_dlx),
               pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2, pl.heads, pl.group};
-  constexpr int NTH = BwdShape<T, D>::NTH;
-  if (pl.b1 > BwdShape<T, D>::NB) {       // dQ accumulates over key chunks
+  constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
+  constexpr int NB = BwdShape<T, D>::NB, RB = BwdShape<T, D>::RB, RG = BwdShape<T, D>::RG;
+  if (pl.b1 <= NB) {
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_COLUMN>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(NTH2), 0,
+                       st, p);
+  } else {                                 // D first, then one workgroup per key chunk
     const size_t n = (size_t)pl.S * pl.N * D;
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2, n);
+    const size_t cols = (size_t)pl.S * pl.b2;
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM>),
+                       dim3(grid1(cols * ((pl.b1 + RG * RB - 1) / (RG * RB)))), dim3(NTH2), 0, st, p);
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS>), dim3(grid1(cols * ((pl.b1 + NB - 1) / NB))),
+                       dim3(NTH2), 0, st, p);
   }
-  hipLaunchKernelGGL((stage2_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(NTH), 0, st, p);
   hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
   if (pl.group > 1) {
     const size_t per = (size_t)pl.N * D, total = (size_t)pl.S / pl.group * per;

@@ -34,7 +34,7 @@ struct Plan {
   size_t xlo;          // elements from the hi plane of split c to its lo plane (0: not split)
   bool precise;
   size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, off_qbar_lp, total;
-  size_t off_dq2, off_dcx, off_dux, off_dhx, off_dkp, off_dvp;   // backward only
+  size_t off_dq2, off_dcx, off_dux, off_dhx, off_dkp, off_dvp, off_dlx;   // backward only
   bool need_qbar, need_qtil;
   bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1
@@ -95,13 +95,10 @@ struct BwdBufs {
 };
 
 // Largest blocks of the backward: the keys of a stage-1 block sit in LDS
-// whole (b2 <= bwd_max_block); a stage-2 column walks its b1 keys in chunks
-// and keeps one fp32 value per row in LDS (b1 <= bwd_max_column).
+// whole (b2 <= bwd_max_block); a stage-2 column of more keys walks them in
+// chunks of that size.
 inline int bwd_max_block(const ma_problem* p) {
   return (p->dtype == MA_F32 && p->head_dim == 128) ? 64 : 128;
-}
-inline int bwd_max_column(const ma_problem* p) {
-  return (p->dtype == MA_F32 && p->head_dim == 128) ? 1024 : 2048;
 }
 
 // Kernel-launch entry of one element type and head dimension (one

@@ -146,7 +146,7 @@ def test_status_strings(lib):
     (dict(seq_len=250), 2),                   # padded
     (dict(seq_len=256 * 200, b1=200, b2=256), 2),   # blocks wider than 128 keys
     (dict(seq_len=630 * 52, b1=630, b2=52), 0),     # columns of 630 keys (walked in chunks)
-    (dict(seq_len=4096 * 8, b1=4096, b2=8), 2),     # columns over 2048 keys
+    (dict(seq_len=4096 * 8, b1=4096, b2=8), 0),     # columns of 4096 keys
     (dict(seq_len=96 * 96, b1=96, b2=96, head_dim=128, dtype="f32"), 2),   # fp32 d128: 64 max
     (dict(seq_len=64 * 64, b1=64, b2=64, head_dim=128, dtype="f32"), 0),
     (dict(steps=0), 1),
