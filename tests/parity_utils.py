@@ -18,7 +18,9 @@ def rel_err(x, ref, slices):
     for (b, h) in slices:
         a, r = np.asarray(x[b, h], np.float64), np.asarray(ref[b, h], np.float64)
         m = np.nanmax(np.abs(r))
-        worst = max(worst, float(np.nanmax(np.abs(a - r)) / m))
+        d = float(np.nanmax(np.abs(a - r)))
+        # an all-zero reference (e.g. dQ of a single token) is compared absolutely
+        worst = max(worst, d / m if m > 0 else d)
     return worst
 
 

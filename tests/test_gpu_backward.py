@@ -135,3 +135,11 @@ def test_n16k_backward_sampled():
 def test_video_backward_sampled():
     """The video latent (630, 52), d = 128, 12 heads: two slices compared whole."""
     check_backward(WORKLOADS["video"], slices=[(0, 0), (0, 7)])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("b1,b2", [(1, 40), (40, 1), (1, 1), (3, 5)])
+def test_degenerate_grids(dtype, b1, b2):
+    """One block (exact attention), one key per block, a single token, and a
+    grid smaller than one MFMA tile."""
+    check_backward(case(f"bwd {b1}x{b2} {dtype}", dtype, 64, b1, b2, heads=2, data="iid"))
