@@ -149,7 +149,8 @@ typedef struct {
 } ma_exports;
 
 /* Current limits: head_dim in {64, 128}; segment width b2/c2 <= 128, except
- * <= 64 for fp32 with head_dim 128; any b1.  Other shapes return
+ * <= 64 for fp32 with head_dim 128; any b1; batch*heads <= 2^24, b1*b2 <=
+ * 2^26 and batch*heads*b1*b2*c1*c2 < 2^31.  Other shapes return
  * MA_ERR_UNSUPPORTED. */
 
 /* Bytes of device workspace monarch_attn_forward needs for problem *p

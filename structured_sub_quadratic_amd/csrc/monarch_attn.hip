@@ -48,6 +48,8 @@ ma_status validate_problem(const ma_problem* p) {
   if (p->b2 / p->c2 > max_segment(p)) return MA_ERR_UNSUPPORTED;
   const int64_t slices = p->batch * p->heads;
   if (slices > (int64_t)1 << 24 || grid > (int64_t)1 << 26) return MA_ERR_UNSUPPORTED;
+  // work items and exchange rows are counted in 32 bits
+  if (slices * grid * p->c1 * p->c2 > INT32_MAX) return MA_ERR_UNSUPPORTED;
   return MA_OK;
 }
 

@@ -76,6 +76,8 @@ def good(**kw):
     (dict(seq_len=240), 1),                   # a whole block of padding
     (dict(seq_len=247, c2=2), 1),             # 9 padding positions fill a segment of 8
     (dict(seq_len=249, c2=2), 0),
+    (dict(batch=1 << 14, heads=16, seq_len=1 << 14, b1=128, b2=128), 2),   # 2^32 exchange rows
+    (dict(batch=1 << 12, heads=16, seq_len=1 << 14, b1=128, b2=128), 0),   # 2^30
 ])
 def test_validation_codes(lib, kw, code):
     p = good(**kw)
