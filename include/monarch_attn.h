@@ -188,9 +188,11 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * the forward's steps, computed by recomputing the forward's block softmaxes
  * from its normalisers (the forward state is rebuilt inside the call).
  * dK, dV have K's shape [batch, kv_heads, seq_len, head_dim]; with grouped
- * K/V they sum over the query heads of each group.  Covers steps = 1,
- * c1 = c2 = 1, seq_len = b1*b2 and b2 <= 128 (<= 64 for fp32 with
- * head_dim 128); other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
+ * K/V they sum over the query heads of each group.  A padded sequence
+ * (MA_FLAG_PAD_FRONT or post-padding) routes the query gradient of a padding
+ * position through the tile mean it used.  Covers steps = 1, c1 = c2 = 1
+ * and b2 <= 128 (<= 64 for fp32 with head_dim 128); other problems return
+ * MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
  * the plain c path (the T = 1 default), so these are its gradients.
  * workspace: at least monarch_attn_backward_workspace_size bytes, 256-byte
  * aligned, overlapping no other argument; dQ, dK, dV must not overlap each

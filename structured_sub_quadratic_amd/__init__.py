@@ -191,10 +191,11 @@ def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layo
 
 
 def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
-             workspace=None, out=None):
+             workspace=None, out=None, pad="post"):
     """Gradients (dq, dk, dv) of <dy, forward(q, k, v, ...)> on the current
-    stream.  Covers what monarch_attn_backward documents (T = 1, untiled, no
-    padding, blocks of at most 128 keys; k, v may have fewer heads).
+    stream.  Covers what monarch_attn_backward documents (T = 1, untiled,
+    blocks of at most 128 keys; k, v may have fewer heads; pad as in
+    forward).
     out: optional (dq, dk, dv) tensors to write."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("dy", dy)):
@@ -207,8 +208,10 @@ def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat"
     if dy.shape != q.shape or k.shape != v.shape or (k.shape[0], k.shape[2], k.shape[3]) != (B, N, D) \
             or H % Hkv:
         raise ValueError("dy must be shaped like q, and k, v [batch, kv_heads, seq_len, head_dim]")
-    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, 0,
-                        kv_heads=Hkv)
+    if pad not in ("pre", "post"):
+        raise ValueError("pad must be 'pre' or 'post'")
+    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw,
+                        MA_FLAG_PAD_FRONT if pad == "pre" else 0, kv_heads=Hkv)
     ws_bytes = backward_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)

@@ -46,6 +46,9 @@ struct BwdParams {
   float* dhx;                       // [rows] gradient of H_R (nats)
   float* dkp; float* dvp;           // [S, N, D] per-query-head dK, dV (grouped K/V), or null
   float* dlx;                       // [S, b2, b1] D = rowsum(P dP) (columns of several key chunks)
+  const void* qbt;                  // padded: tile means [S, b2, D] in the input type (first-step
+                                    // queries of padding positions), else null
+  float* dqbar;                     // padded: [S, b2, D] gradient of those tile means
   GridMap map;
   int S, N, b1, b2;
   float sc, sc2;                    // scale, scale * log2(e)
@@ -94,7 +97,10 @@ struct RowsIn {
     for (int a = 0; a < NT; ++a) {
       const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
       v[a] = V{};
-      if (task < RB * CH && j < n) v[a] = *reinterpret_cast<const V*>(src(j) + c * VN);
+      if (task < RB * CH && j < n) {
+        const T* row = src(j);             // null: a padding row, zeros
+        if (row) v[a] = *reinterpret_cast<const V*>(row + c * VN);
+      }
     }
   }
   template <int LD, bool TR, int LDT> __device__ inline void store(T* dst, T* dt) const {
@@ -307,6 +313,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
   const T* dY = static_cast<const T*>(p.dy) + (size_t)sl * p.N * D;
   const AxisMap col = p.map.col_axis(i);
+  const bool padded = p.map.padded();
   int k0 = 0, nb = 0, nbp = 0;                               // current key chunk
   auto load_keys = [&](int kc) {
     k0 = kc * NB;
@@ -324,7 +331,9 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   auto fetch = [&](int l0) {
     const int n = min(RB, p.b1 - l0);
     pq.load(n, [&](int r) { return Q + col.at(l0 + r) * D; });
-    pdy.load(n, [&](int r) { return dY + col.at(l0 + r) * D; });
+    pdy.load(n, [&](int r) -> const T* {     // no upstream gradient at padding rows
+      return !padded || col.valid(l0 + r) ? dY + col.at(l0 + r) * D : nullptr;
+    });
     if (threadIdx.x < RB) {
       pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + threadIdx.x] : 0.f;
       if (MODE == S2_KEYS) pdl = (int)threadIdx.x < n ? dlx[l0 + threadIdx.x] : 0.f;
@@ -453,7 +462,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
-          if (row >= nr) continue;
+          if (row >= nr || (padded && !col.valid(l0 + row))) continue;
           float* at = p.dq2 + ((size_t)sl * p.N + col.at(l0 + row)) * D + d;
           if (MODE == S2_KEYS) atomicAdd(at, a[t][e] * p.sc);     // zeroed before the kernel
           else *at = a[t][e] * p.sc;
@@ -559,9 +568,15 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   RowsIn<T, D, RB, NTH> pq;
   RowsF32<T, D, RB, NTH> pdu, pdc, pdq;
   float pls = 0.f, pdh = 0.f;
+  // a padding position (k, i) took the tile mean of column i as its query
+  const bool padded = p.map.padded();
+  const T* QB = static_cast<const T*>(p.qbt) + (size_t)sl * p.b2 * D;
+  const int jlo = p.map.key_lo(k), jhi = p.map.key_hi(k);   // real keys of block k
   auto fetch = [&](int i0) {
     const int n = min(RB, p.b2 - i0);
-    pq.load(n, [&](int r) { return Q + row.at(i0 + r) * D; });
+    pq.load(n, [&](int r) {
+      return !padded || row.valid(i0 + r) ? Q + row.at(i0 + r) * D : QB + (size_t)(i0 + r) * D;
+    });
     pdu.load(n, [&](int r) { return p.dux + (xb + i0 + r) * D; });
     pdc.load(n, [&](int r) { return p.dcx + (xb + i0 + r) * D; });
     if constexpr (SH::PREFETCH)
@@ -621,7 +636,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = m0 + 4 * g + e;
-          const bool ok = r < nr && key < nb;
+          const bool ok = r < nr && key < nb && (!padded || (key >= jlo && key < jhi));
           const float lg2 = z[t][e] * p.sc2 - lser[r];        // log2 R
           const float rv = ok ? __builtin_amdgcn_exp2f(lg2) : 0.f;
           const float dv = ok ? dr[t][e] : 0.f;
@@ -666,6 +681,10 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
         for (int e = 0; e < 4; ++e) {
           const int r = m0 + 4 * g + e;
           if (r >= nr) continue;
+          if (padded && !row.valid(i0 + r)) {     // gradient of the tile mean it used
+            p.dqbar[((size_t)sl * p.b2 + i0 + r) * D + d] = a[t][e];
+            continue;
+          }
           const int64_t tok = row.at(i0 + r);
           const float q2 = SH::PREFETCH ? dq2s[r * (D + 4) + d] : p.dq2[((size_t)sl * p.N + tok) * D + d];
           dQ[tok * D + d] = from_f32<T>(a[t][e] + q2);
@@ -699,7 +718,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = m0 + 4 * g + e;
-        if (key >= nb) continue;
+        if (key >= nb || (padded && (key < jlo || key >= jhi))) continue;
         const int64_t tok = row.at(key);
         if (p.dkp) {     // grouped K/V: this query head's share, summed by kv_reduce_kernel
           p.dkp[((size_t)sl * p.N + tok) * D + d] = adk[s][t][e];
@@ -710,6 +729,24 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
         }
       }
     }
+  }
+}
+
+// Padded sequences: a padding position (k, i) used the mean of the real rows
+// of column i as its first-step query, so its query gradient dqbar(i) goes
+// to each of those rows divided by their number.  One workgroup per (slice,
+// column), one thread per d.
+template <typename T>
+__global__ __launch_bounds__(128) void qbar_grad_kernel(const float* dqbar, T* dq, GridMap map, int N, int D) {
+  const int i = blockIdx.x % map.b2, sl = blockIdx.x / map.b2, d = threadIdx.x;
+  const int nreal = map.real_rows(i, 0, map.b1);
+  if (nreal == map.b1 || nreal == 0 || d >= D) return;       // no padding row in this column
+  const float gv = dqbar[((size_t)sl * map.b2 + i) * D + d] / (float)nreal;
+  T* Y = dq + (size_t)sl * N * D;
+  for (int l = 0; l < map.b1; ++l) {
+    if (!map.valid(l, i)) continue;
+    T* at = Y + map.token(l, i) * D + d;
+    *at = from_f32<T>(to_f32(*at) + gv);
   }
 }
 
@@ -740,6 +777,7 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(const float* dkp, const 
 template <typename T, int D, bool PRECISE>
 ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   Bufs fb{b.q, b.k, b.v, nullptr, b.ws, nullptr, nullptr, nullptr, nullptr};
+  if (pl.need_qbar && launch_one<T, D, PRECISE>(pl, fb, L_QBAR, 0, st) != hipSuccess) return MA_ERR_DEVICE;
   if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE1_LAST, 0, st) != hipSuccess) return MA_ERR_DEVICE;
   if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE2_STATS, 0, st) != hipSuccess) return MA_ERR_DEVICE;
   char* ws = b.ws;
@@ -754,6 +792,9 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
               pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
               pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
               reinterpret_cast<float*>(ws + pl.off_dlx),
+              pl.padded ? (pl.precise ? (const void*)(ws + pl.off_qbar) : (const void*)(ws + pl.off_qbar_lp))
+                        : nullptr,
+              pl.padded ? reinterpret_cast<float*>(ws + pl.off_dqbar) : nullptr,
               pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2, pl.heads, pl.group};
   constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
   constexpr int NB = BwdShape<T, D>::NB, RB = BwdShape<T, D>::RB, RG = BwdShape<T, D>::RG;
@@ -770,6 +811,9 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
                        dim3(NTH2), 0, st, p);
   }
   hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
+  if (pl.padded)
+    hipLaunchKernelGGL((qbar_grad_kernel<T>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(128), 0, st, p.dqbar,
+                       static_cast<T*>(b.dq), pl.map, (int)pl.N, D);
   if (pl.group > 1) {
     const size_t per = (size_t)pl.N * D, total = (size_t)pl.S / pl.group * per;
     hipLaunchKernelGGL((kv_reduce_kernel<T>), dim3(grid1((total + 255) / 256)), dim3(256), 0, st, p.dkp,

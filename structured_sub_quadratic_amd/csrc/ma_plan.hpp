@@ -34,7 +34,7 @@ struct Plan {
   size_t xlo;          // elements from the hi plane of split c to its lo plane (0: not split)
   bool precise;
   size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, off_qbar_lp, total;
-  size_t off_dq2, off_dcx, off_dux, off_dhx, off_dkp, off_dvp, off_dlx;   // backward only
+  size_t off_dq2, off_dcx, off_dux, off_dhx, off_dkp, off_dvp, off_dlx, off_dqbar;   // backward only
   bool need_qbar, need_qtil;
   bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1

@@ -102,12 +102,14 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
   pl.off_qbar_lp = off;
   if (pl.need_qbar_lp) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * pl.elt);
   pl.off_dq2 = pl.off_dcx = pl.off_dux = pl.off_dhx = pl.off_dkp = pl.off_dvp = pl.off_dlx = off;
+  pl.off_dqbar = off;
   if (backward) {
     pl.off_dq2 = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
     pl.off_dcx = off; off = align_up(off + rows * pl.D * 4);
     pl.off_dux = off; off = align_up(off + rows * pl.D * 4);
     pl.off_dhx = off; off = align_up(off + rows * 4);
     pl.off_dlx = off; off = align_up(off + (size_t)pl.S * pl.G * 4);   // D of stage-2 rows
+    if (pl.padded) { pl.off_dqbar = off; off = align_up(off + (size_t)pl.S * pl.b2 * pl.D * 4); }
     if (pl.group > 1) {   // per-query-head shares of dK, dV
       pl.off_dkp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
       pl.off_dvp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
@@ -163,13 +165,12 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   return run_f32_128(pl, b, st, events, n_events);
 }
 
-// The backward covers T = 1, untiled, no padding, and stage-1 blocks whose
-// keys fit LDS whole (grouped K/V included; any b1).
+// The backward covers T = 1, untiled, and stage-1 blocks whose keys fit LDS
+// whole (grouped K/V and padding included; any b1).
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
   if (p->steps != 1 || p->c1 != 1 || p->c2 != 1) return MA_ERR_UNSUPPORTED;
-  if ((int64_t)p->b1 * p->b2 != p->seq_len) return MA_ERR_UNSUPPORTED;
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
   return MA_OK;
 }

@@ -145,7 +145,7 @@ def test_status_strings(lib):
     (dict(steps=2), 2),                       # T > 1 not covered by the backward
     (dict(c1=2), 2),                          # tiled
     (dict(kv_heads=1), 0),                    # grouped K/V
-    (dict(seq_len=250), 2),                   # padded
+    (dict(seq_len=250), 0),                   # padded
     (dict(seq_len=256 * 200, b1=200, b2=256), 2),   # blocks wider than 128 keys
     (dict(seq_len=630 * 52, b1=630, b2=52), 0),     # columns of 630 keys (walked in chunks)
     (dict(seq_len=4096 * 8, b1=4096, b2=8), 0),     # columns of 4096 keys

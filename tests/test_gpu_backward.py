@@ -32,7 +32,7 @@ def run_backward(cfg, Q, K, V, dY):
     dev = torch.device("cuda:0")
     tq, tk, tv, tdy = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt) for x in (Q, K, V, dY))
     dq, dk, dv = ma.backward(tq, tk, tv, tdy, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                             layout=cfg.layout, fhw=cfg.fhw)
+                             layout=cfg.layout, fhw=cfg.fhw, pad=cfg.pad)
     torch.cuda.synchronize()
     return tuple(x.float().cpu().numpy() for x in (dq, dk, dv))
 
@@ -52,7 +52,7 @@ def check_backward(cfg, slices=None, tol=None, kv_heads=None):
     all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     slices = all_slices if slices is None else slices
     ref = obw.backward(Q, K, V, dY, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                       layout=cfg.layout, fhw=cfg.fhw, slices=slices)
+                       layout=cfg.layout, fhw=cfg.fhw, slices=slices, pad=cfg.pad)
     tol = TOL[cfg.dtype] if tol is None else tol
     group = cfg.heads // K.shape[1]
     kv_slices = sorted({(b, h // group) for (b, h) in slices})
@@ -143,3 +143,24 @@ def test_degenerate_grids(dtype, b1, b2):
     """One block (exact attention), one key per block, a single token, and a
     grid smaller than one MFMA tile."""
     check_backward(case(f"bwd {b1}x{b2} {dtype}", dtype, 64, b1, b2, heads=2, data="iid"))
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_padded_vit_shape(pad, dtype):
+    """197 tokens as 15 blocks of 14 (13 padding positions): padding keys get
+    no gradient, and the query gradient of a padding position goes through
+    the tile mean of its column."""
+    cfg = WorkloadConfig("case", f"bwd vit pad={pad} {dtype}", batch=2, heads=3, seq_len=197,
+                         head_dim=64, b1=15, b2=14, steps=1, dtype=dtype, data="iid", seed=53,
+                         pad=pad)
+    check_backward(cfg)
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+def test_padded_long_columns(pad):
+    """Padding with columns of more than one key chunk (b1 = 200), head_dim 128."""
+    cfg = WorkloadConfig("case", f"bwd b1=200 pad={pad}", batch=1, heads=2, seq_len=200 * 40 - 30,
+                         head_dim=128, b1=200, b2=40, steps=1, dtype="bf16", data="normed", seed=59,
+                         pad=pad)
+    check_backward(cfg)
