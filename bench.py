@@ -118,12 +118,17 @@ def sampled_parity(cfg, Q, K, V, y):
 
 
 def backward_flops(cfg):
-    """Products of the backward as computed (per slice, T = 1 untiled): stage 2
-    forms P, dP, dQ, dc, du over b1 x b1 per column (5), stage 1 forms R, dR
-    (two products), dQ, dK (two products), dV over b2 x b2 per block (7); the
-    forward state it rebuilds (c, u and the stage-2 normalisers) adds 3 + 1."""
-    N, d, b1, b2 = cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2
-    return 2 * N * d * (5 * b1 + 7 * b2 + 3 * b2 + b1) * cfg.slices
+    """Products of the backward as computed (per slice, untiled).  Last step:
+    stage 2 forms P, dP, dQ, dc, du over b1 x b1 per column (5), stage 1
+    forms R, dR (two products), dQ, dK (two products), dV over b2 x b2 per
+    block (7).  Each earlier step of T > 1: stage 2 forms P, dP, dQ, the
+    direct P dalpha term and dc (5 over b1), stage 1 R, dR, dq~ and dK (two
+    products; 5 over b2).  The rebuilt forward: per step c (2 over b2) and
+    the stage-2 normalisers (1 over b1), u once (1 over b2), and the next
+    queries of every step but the last (2 over b1)."""
+    N, d, b1, b2, T = cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2, cfg.steps
+    per = (5 * b1 + 7 * b2) + (T - 1) * (5 * b1 + 5 * b2) + T * (2 * b2 + b1) + b2 + (T - 1) * 2 * b1
+    return 2 * N * d * per * cfg.slices
 
 
 def bench_backward(args, cfg, dev):

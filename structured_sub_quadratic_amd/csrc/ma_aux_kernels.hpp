@@ -24,6 +24,7 @@ struct AlphaParams {
   int S, N, b1, b2, c1, c2, rt, nkeys, nkt;
   float sc2;
   size_t xlo;           // lo plane of split c (elements after cx)
+  float* beta_out;      // [rows] column sums of L (exchange rows), or null
 };
 
 template <typename T, int D, bool PRECISE>
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
   }
   if (!p.qt_out || !kvalid) return;
   beta = wave_sum_x16x32(beta);
+  if (p.beta_out && g == 0) p.beta_out[xrow] = beta;
   const int k = key / p.c2, s = key % p.c2;
   float* out = p.qt_out + (((((size_t)sl * p.b1 + k) * p.c1 + t) * p.c2 + s) * p.b2 + i) * D;
   if (beta > 0.f) {

@@ -49,6 +49,11 @@ struct BwdParams {
   const void* qbt;                  // padded: tile means [S, b2, D] in the input type (first-step
                                     // queries of padding positions), else null
   float* dqbar;                     // padded: [S, b2, D] gradient of those tile means
+  // several steps: the step's queries q~ ([rows, D] fp32, exchange rows), the
+  // gradient of the next step's queries (in: dq~, rewritten as dalpha =
+  // dq~ / beta) and dbeta = -dq~ . q~ / beta, and the lo plane of split c
+  const float* qtil; float* dqt; const float* dbt;
+  size_t xlo;
   GridMap map;
   int S, N, b1, b2;
   float sc, sc2;                    // scale, scale * log2(e)
@@ -136,6 +141,25 @@ struct RowsF32 {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         T* at = hi + (size_t)(c * 4 + e) * LDT + j;
+        if constexpr (std::is_same<T, float>::value) {
+          *at = v[a][e];
+        } else {
+          const bf16 h = (bf16)v[a][e];
+          at[0] = h;
+          at[plane] = (bf16)(v[a][e] - (float)h);
+        }
+      }
+    }
+  }
+  // rows as planes of the element type: hi[j][.] (and lo for bf16)
+  template <int LD> __device__ inline void store_planes(T* hi, size_t plane) const {
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
+      if (task >= RB * CH) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        T* at = hi + (size_t)j * LD + c * 4 + e;
         if constexpr (std::is_same<T, float>::value) {
           *at = v[a][e];
         } else {
@@ -273,10 +297,15 @@ __device__ inline void bwd_load_rows(T* dst, T* dt, int NR, int n, Src src) {
 // RB rows), computes D = rowsum(P dP) over all key chunks into dlx; then
 // S2_KEYS, one workgroup per (slice, column, chunk of NB keys), the
 // gradients of that key chunk, adding its part of dQ with fp32 atomics.
+// S2_ALPHA, a step before the last one of T > 1 (columns of one key chunk):
+// that step's L fed the next queries q~ = alpha / beta (alpha = L^T q, beta =
+// column sums of L), so dP = q dalpha^T + dbeta, dQ gains the direct term
+// P dalpha on top of the softmax part, and there is no u.  SPLITC: c is
+// read as its two bf16 planes (the split path of bf16 with T > 1).
 // ---------------------------------------------------------------------------
-enum { S2_COLUMN = 0, S2_ROWSUM = 1, S2_KEYS = 2 };
+enum { S2_COLUMN = 0, S2_ROWSUM = 1, S2_KEYS = 2, S2_ALPHA = 3 };
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool SPLITC = false>
 __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdParams p) {
   typedef BwdShape<T, D> SH;
   constexpr int NW = SH::NW2, NTH = SH::NTH2, RG = SH::RG;
@@ -285,13 +314,19 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   constexpr int DS = DT < 4 ? DT : 4;                        // d tiles per dc, du strip
   constexpr int DQ = SH::DQ2;                                // d tiles per dQ strip
   constexpr int SK = SH::SK2;                                // key-tile strips of dc, du per wave
-  __shared__ __attribute__((aligned(16))) T cs[NB * LDI];
-  __shared__ __attribute__((aligned(16))) T us[NB * LDI];
-  __shared__ __attribute__((aligned(16))) T ct[SH::KT_COPY ? D * LDN : 1];   // c^T
+  constexpr bool AL = MODE == S2_ALPHA;
+  constexpr int CK = SPLITC ? PL : IN;                       // operand kind of c
+  constexpr size_t CPL = (size_t)NB * LDI, CTPL = (size_t)D * LDN;   // lo planes of c, c^T
+  constexpr int LDA = D + 4;                                 // fp32 row stride of dalpha
+  __shared__ __attribute__((aligned(16))) T cs[(SPLITC ? 2 : 1) * NB * LDI];
+  __shared__ __attribute__((aligned(16))) T us[AL ? 1 : NB * LDI];
+  __shared__ __attribute__((aligned(16))) T ct[SH::KT_COPY ? (SPLITC ? 2 : 1) * D * LDN : 1];   // c^T
   __shared__ __attribute__((aligned(16))) T qs[RB * LDI];
-  __shared__ __attribute__((aligned(16))) T dys[RB * LDI];
+  __shared__ __attribute__((aligned(16))) T dys[AL ? 1 : RB * LDI];
   __shared__ __attribute__((aligned(16))) T qt[D * LDR];    // q^T of the chunk
-  __shared__ __attribute__((aligned(16))) T dyt[D * LDR];   // dY^T of the chunk
+  __shared__ __attribute__((aligned(16))) T dyt[AL ? 1 : D * LDR];   // dY^T of the chunk
+  __shared__ __attribute__((aligned(16))) float das[AL ? NB * LDA : 1];   // dalpha of the keys
+  __shared__ float dbk[AL ? NB : 1];                                      // dbeta of the keys
   __shared__ __attribute__((aligned(16))) float ps[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dws[RB * LDP];
   __shared__ float h2k[NB], dhk[NB], lsel[RB], dl[RB];
@@ -320,10 +355,23 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
     nb = min(NB, p.b1 - k0);
     nbp = (nb + SH::KQ - 1) / SH::KQ * SH::KQ;
     bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(cs, ct, NB, nb, [&](int k) { return C + (xb + (k0 + k) * xs) * D; });
-    bwd_load_rows<T, D, LDI, NTH>(us, nullptr, NB, nb, [&](int k) { return U + (xb + (k0 + k) * xs) * D; });
+    if constexpr (SPLITC)
+      bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(cs + CPL, SH::KT_COPY ? ct + CTPL : nullptr, NB, nb,
+                                                      [&](int k) { return C + p.xlo + (xb + (k0 + k) * xs) * D; });
+    if constexpr (AL) {
+      for (int task = threadIdx.x; task < NB * (D / 4); task += NTH) {
+        const int k = task / (D / 4), c = task % (D / 4);
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (k < nb) v = *reinterpret_cast<const f32x4*>(p.dqt + (xb + (k0 + k) * xs) * D + c * 4);
+        *reinterpret_cast<f32x4*>(das + k * LDA + c * 4) = v;
+      }
+    } else {
+      bwd_load_rows<T, D, LDI, NTH>(us, nullptr, NB, nb, [&](int k) { return U + (xb + (k0 + k) * xs) * D; });
+    }
     for (int k = threadIdx.x; k < NB; k += NTH) {
       h2k[k] = k < nb ? p.h2x[xb + (k0 + k) * xs] : 0.f;
       dhk[k] = 0.f;
+      if constexpr (AL) dbk[k] = k < nb ? p.dbt[xb + (k0 + k) * xs] : 0.f;
     }
   };
   RowsIn<T, D, RB, NTH> pq, pdy;
@@ -331,17 +379,19 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   auto fetch = [&](int l0) {
     const int n = min(RB, p.b1 - l0);
     pq.load(n, [&](int r) { return Q + col.at(l0 + r) * D; });
-    pdy.load(n, [&](int r) -> const T* {     // no upstream gradient at padding rows
-      return !padded || col.valid(l0 + r) ? dY + col.at(l0 + r) * D : nullptr;
-    });
+    if constexpr (!AL)
+      pdy.load(n, [&](int r) -> const T* {     // no upstream gradient at padding rows
+        return !padded || col.valid(l0 + r) ? dY + col.at(l0 + r) * D : nullptr;
+      });
     if (threadIdx.x < RB) {
       pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + threadIdx.x] : 0.f;
       if (MODE == S2_KEYS) pdl = (int)threadIdx.x < n ? dlx[l0 + threadIdx.x] : 0.f;
     }
   };
-  // P = exp2(sc2 q.c + h2 - lse2) and dP = dY u^T of a row chunk against the
-  // current key chunk, in strips of one row tile x NG key tiles; STORE keeps
-  // them in LDS, and the row sums of P dP go to dsum[row] (if not null)
+  // P = exp2(sc2 q.c + h2 - lse2) and dP = dY u^T (S2_ALPHA: q dalpha^T +
+  // dbeta) of a row chunk against the current key chunk, in strips of one row
+  // tile x NG key tiles; STORE keeps them in LDS, and the row sums of P dP go
+  // to dsum[row] (if not null)
   auto scores = [&](int nr, bool store, float* dsum, const T* qs, const T* dys, const float* lsel) {
     const int ng = (nbp / 16 + NG - 1) / NG;
     for (int st = wave; st < (RB / 16) * ng; st += NW) {
@@ -351,13 +401,15 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
 #pragma unroll
       for (int t = 0; t < NG; ++t) s[t] = dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (nt == NG) {
-        strip_mma<T, NG, IN, ROW, IN, ROW>(s, qs, LDI, 0, cs, LDI, 0, m0, n0, D);
-        strip_mma<T, NG, IN, ROW, IN, ROW>(dp, dys, LDI, 0, us, LDI, 0, m0, n0, D);
+        strip_mma<T, NG, IN, ROW, CK, ROW>(s, qs, LDI, 0, cs, LDI, CPL, m0, n0, D);
+        if constexpr (AL) strip_mma<T, NG, IN, ROW, F32, ROW>(dp, qs, LDI, 0, das, LDA, 0, m0, n0, D);
+        else strip_mma<T, NG, IN, ROW, IN, ROW>(dp, dys, LDI, 0, us, LDI, 0, m0, n0, D);
       } else {
         for (int t = 0; t < nt; ++t) {
           f32x4 a1[1] = {s[t]}, a2[1] = {dp[t]};
-          strip_mma<T, 1, IN, ROW, IN, ROW>(a1, qs, LDI, 0, cs, LDI, 0, m0, n0 + 16 * t, D);
-          strip_mma<T, 1, IN, ROW, IN, ROW>(a2, dys, LDI, 0, us, LDI, 0, m0, n0 + 16 * t, D);
+          strip_mma<T, 1, IN, ROW, CK, ROW>(a1, qs, LDI, 0, cs, LDI, CPL, m0, n0 + 16 * t, D);
+          if constexpr (AL) strip_mma<T, 1, IN, ROW, F32, ROW>(a2, qs, LDI, 0, das, LDA, 0, m0, n0 + 16 * t, D);
+          else strip_mma<T, 1, IN, ROW, IN, ROW>(a2, dys, LDI, 0, us, LDI, 0, m0, n0 + 16 * t, D);
           s[t] = a1[0];
           dp[t] = a2[0];
         }
@@ -372,7 +424,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
           const int row = m0 + 4 * g + e;
           const bool ok = row < nr && key < nb;
           const float pv = ok ? __builtin_amdgcn_exp2f(s[t][e] * p.sc2 + h2k[key] - lsel[row]) : 0.f;
-          const float dv = ok ? dp[t][e] : 0.f;
+          const float dv = ok ? dp[t][e] + (AL ? dbk[key] : 0.f) : 0.f;
           if (store) {
             ps[row * LDP + key] = pv;
             dws[row * LDP + key] = dv;
@@ -432,7 +484,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
     const int nr = min(RB, p.b1 - l0);
     __syncthreads();
     pq.template store<LDI, true, LDR>(qs, qt);
-    pdy.template store<LDI, true, LDR>(dys, dyt);
+    if constexpr (!AL) pdy.template store<LDI, true, LDR>(dys, dyt);
     if (threadIdx.x < RB) {
       lsel[threadIdx.x] = pls;
       dl[threadIdx.x] = MODE == S2_KEYS ? pdl : 0.f;
@@ -451,11 +503,13 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
     for (int st = wave; st < (RB / 16) * (DT / DQ); st += NW) {
       const int m0 = (st / (DT / DQ)) * 16, h = st % (DT / DQ);
       {
-      f32x4 a[DQ];
+      f32x4 a[DQ], a2[DQ];
 #pragma unroll
-      for (int t = 0; t < DQ; ++t) a[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, IN, ROW>(a, dws, LDP, 0, ct, LDN, 0, m0, 16 * DQ * h, nbp);
-      else strip_mma<T, DQ, F32, ROW, IN, COL>(a, dws, LDP, 0, cs, LDI, 0, m0, 16 * DQ * h, nbp);
+      for (int t = 0; t < DQ; ++t) a[t] = a2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, CK, ROW>(a, dws, LDP, 0, ct, LDN, CTPL, m0, 16 * DQ * h, nbp);
+      else strip_mma<T, DQ, F32, ROW, CK, COL>(a, dws, LDP, 0, cs, LDI, CPL, m0, 16 * DQ * h, nbp);
+      // the direct term of the next queries: P dalpha
+      if constexpr (AL) strip_mma<T, DQ, F32, ROW, F32, COL>(a2, ps, LDP, 0, das, LDA, 0, m0, 16 * DQ * h, nbp);
 #pragma unroll
       for (int t = 0; t < DQ; ++t) {
         const int d = 16 * (DQ * h + t) + lane % 16;
@@ -465,6 +519,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
           if (row >= nr || (padded && !col.valid(l0 + row))) continue;
           float* at = p.dq2 + ((size_t)sl * p.N + col.at(l0 + row)) * D + d;
           if (MODE == S2_KEYS) atomicAdd(at, a[t][e] * p.sc);     // zeroed before the kernel
+          else if (AL) *at += a[t][e] * p.sc + a2[t][e];          // later steps' parts are in
           else *at = a[t][e] * p.sc;
         }
       }
@@ -489,7 +544,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
         f32x4 (&c)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adc[s][DS * h]);
         f32x4 (&u)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adu[s][DS * h]);
         strip_mma<T, DS, F32, COL, IN, ROW>(c, dws, LDP, 0, qt, LDR, 0, m0, 16 * DS * h, RB);
-        strip_mma<T, DS, F32, COL, IN, ROW>(u, ps, LDP, 0, dyt, LDR, 0, m0, 16 * DS * h, RB);
+        if constexpr (!AL) strip_mma<T, DS, F32, COL, IN, ROW>(u, ps, LDP, 0, dyt, LDR, 0, m0, 16 * DS * h, RB);
       }
     }
   }
@@ -506,7 +561,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
         if (key >= nb) continue;
         const size_t row = xb + (k0 + key) * xs;
         p.dcx[row * D + d] = adc[s][t][e] * p.sc;
-        p.dux[row * D + d] = adu[s][t][e];
+        if constexpr (!AL) p.dux[row * D + d] = adu[s][t][e];
       }
     }
   }
@@ -522,9 +577,15 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, size_t n
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1 backward: one workgroup per (slice, block k).
+// Stage 1 backward: one workgroup per (slice, block k).  SM (step mode):
+// S1_ONLY, the single step of T = 1 (queries q, dQ = stage-2 part + own);
+// with several steps, S1_LAST (queries q~ in fp32, u and V path, dq~ out,
+// dK and dV stored in fp32), S1_MID (q~, no V path, dq~ out, dK added) and
+// S1_FIRST (queries q, no V path, dQ part added, dK added).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3 };
+
+template <typename T, int D, int SM = S1_ONLY>
 __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdParams p) {
   typedef BwdShape<T, D> SH;
   constexpr int NW = SH::NW, NTH = SH::NTH;
@@ -534,18 +595,22 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   constexpr int DQ = SH::DQ;                                 // d tiles per dQ strip
   constexpr int SK = SH::SK;                                 // key-tile strips of dK, dV per wave
   constexpr bool SPLIT = !std::is_same<T, float>::value;
+  constexpr bool QF = SM == S1_LAST || SM == S1_MID;         // queries q~ (fp32 planes)
+  constexpr bool WV = SM == S1_ONLY || SM == S1_LAST;        // u = R V path
+  constexpr bool QP = QF && SPLIT;                           // queries carry a lo plane
   constexpr size_t TPL = (size_t)D * LDR;                    // plane offset of the transposed grads
+  constexpr size_t QPL = (size_t)RB * LDI;                   // plane offset of the query rows
   __shared__ __attribute__((aligned(16))) T ks[NB * LDI];
-  __shared__ __attribute__((aligned(16))) T vs[NB * LDI];
+  __shared__ __attribute__((aligned(16))) T vs[WV ? NB * LDI : 1];
   __shared__ __attribute__((aligned(16))) T kt[SH::KT_COPY ? D * LDN : 1];   // K^T
-  __shared__ __attribute__((aligned(16))) T qs[RB * LDI];
-  __shared__ __attribute__((aligned(16))) T qt[D * LDR];                   // q^T of the chunk
-  __shared__ __attribute__((aligned(16))) T dut[(SPLIT ? 2 : 1) * D * LDR]; // du^T (hi, lo)
+  __shared__ __attribute__((aligned(16))) T qs[(QP ? 2 : 1) * RB * LDI];
+  __shared__ __attribute__((aligned(16))) T qt[(QP ? 2 : 1) * D * LDR];    // q^T of the chunk
+  __shared__ __attribute__((aligned(16))) T dut[WV ? (SPLIT ? 2 : 1) * D * LDR : 1]; // du^T (hi, lo)
   __shared__ __attribute__((aligned(16))) T dct[(SPLIT ? 2 : 1) * D * LDR]; // dc^T (hi, lo)
   __shared__ __attribute__((aligned(16))) float rs[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dzs[RB * LDP];
   __shared__ float lser[RB], dhr[RB], gr[RB], hr[RB];
-  __shared__ __attribute__((aligned(16))) float dq2s[SH::PREFETCH ? RB * (D + 4) : 1];   // dQ (stage 2)
+  __shared__ __attribute__((aligned(16))) float dq2s[SH::PREFETCH && SM == S1_ONLY ? RB * (D + 4) : 1];   // dQ (stage 2)
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int k = blockIdx.x % p.b1, sl = blockIdx.x / p.b1;
@@ -558,7 +623,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   const AxisMap row = p.map.row_axis(k);
 
   bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(ks, kt, NB, nb, [&](int j) { return K + row.at(j) * D; });
-  bwd_load_rows<T, D, LDI, NTH>(vs, nullptr, NB, nb, [&](int j) { return V + row.at(j) * D; });
+  if constexpr (WV) bwd_load_rows<T, D, LDI, NTH>(vs, nullptr, NB, nb, [&](int j) { return V + row.at(j) * D; });
   f32x4 adk[SK][DT], adv[SK][DT];
 #pragma unroll
   for (int s = 0; s < SK; ++s)
@@ -566,7 +631,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
     for (int t = 0; t < DT; ++t) adk[s][t] = adv[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   RowsIn<T, D, RB, NTH> pq;
-  RowsF32<T, D, RB, NTH> pdu, pdc, pdq;
+  RowsF32<T, D, RB, NTH> pdu, pdc, pdq, pqf;
   float pls = 0.f, pdh = 0.f;
   // a padding position (k, i) took the tile mean of column i as its query
   const bool padded = p.map.padded();
@@ -574,12 +639,16 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   const int jlo = p.map.key_lo(k), jhi = p.map.key_hi(k);   // real keys of block k
   auto fetch = [&](int i0) {
     const int n = min(RB, p.b2 - i0);
-    pq.load(n, [&](int r) {
-      return !padded || row.valid(i0 + r) ? Q + row.at(i0 + r) * D : QB + (size_t)(i0 + r) * D;
-    });
-    pdu.load(n, [&](int r) { return p.dux + (xb + i0 + r) * D; });
+    if constexpr (QF) {
+      pqf.load(n, [&](int r) { return p.qtil + (xb + i0 + r) * D; });
+    } else {
+      pq.load(n, [&](int r) {
+        return !padded || row.valid(i0 + r) ? Q + row.at(i0 + r) * D : QB + (size_t)(i0 + r) * D;
+      });
+    }
+    if constexpr (WV) pdu.load(n, [&](int r) { return p.dux + (xb + i0 + r) * D; });
     pdc.load(n, [&](int r) { return p.dcx + (xb + i0 + r) * D; });
-    if constexpr (SH::PREFETCH)
+    if constexpr (SH::PREFETCH && SM == S1_ONLY)
       pdq.load(n, [&](int r) { return p.dq2 + ((size_t)sl * p.N + row.at(i0 + r)) * D; });
     if (threadIdx.x < RB) {
       pls = (int)threadIdx.x < n ? p.lser[xb + i0 + threadIdx.x] : 0.f;
@@ -591,10 +660,15 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
     const int nr = min(RB, p.b2 - i0);
     __syncthreads();
     if constexpr (!SH::PREFETCH) fetch(i0);
-    pq.template store<LDI, true, LDR>(qs, qt);
-    pdu.template store_tplanes<LDR>(dut, TPL);
+    if constexpr (QF) {
+      pqf.template store_planes<LDI>(qs, QPL);
+      pqf.template store_tplanes<LDR>(qt, TPL);
+    } else {
+      pq.template store<LDI, true, LDR>(qs, qt);
+    }
+    if constexpr (WV) pdu.template store_tplanes<LDR>(dut, TPL);
     pdc.template store_tplanes<LDR>(dct, TPL);
-    if constexpr (SH::PREFETCH) pdq.template store_rows<D + 4>(dq2s);
+    if constexpr (SH::PREFETCH && SM == S1_ONLY) pdq.template store_rows<D + 4>(dq2s);
     if (threadIdx.x < RB) {
       lser[threadIdx.x] = pls;
       dhr[threadIdx.x] = pdh;
@@ -615,14 +689,14 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
 #pragma unroll
       for (int t = 0; t < NG; ++t) z[t] = dr[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (nt == NG) {
-        strip_mma<T, NG, IN, ROW, IN, ROW>(z, qs, LDI, 0, ks, LDI, 0, m0, n0, D);
-        strip_mma<T, NG, PL, COL, IN, ROW>(dr, dut, LDR, TPL, vs, LDI, 0, m0, n0, D);
+        strip_mma<T, NG, QP ? PL : IN, ROW, IN, ROW>(z, qs, LDI, QPL, ks, LDI, 0, m0, n0, D);
+        if constexpr (WV) strip_mma<T, NG, PL, COL, IN, ROW>(dr, dut, LDR, TPL, vs, LDI, 0, m0, n0, D);
         strip_mma<T, NG, PL, COL, IN, ROW>(dr, dct, LDR, TPL, ks, LDI, 0, m0, n0, D);
       } else {
         for (int t = 0; t < nt; ++t) {
           f32x4 a1[1] = {z[t]}, a2[1] = {dr[t]};
-          strip_mma<T, 1, IN, ROW, IN, ROW>(a1, qs, LDI, 0, ks, LDI, 0, m0, n0 + 16 * t, D);
-          strip_mma<T, 1, PL, COL, IN, ROW>(a2, dut, LDR, TPL, vs, LDI, 0, m0, n0 + 16 * t, D);
+          strip_mma<T, 1, QP ? PL : IN, ROW, IN, ROW>(a1, qs, LDI, QPL, ks, LDI, 0, m0, n0 + 16 * t, D);
+          if constexpr (WV) strip_mma<T, 1, PL, COL, IN, ROW>(a2, dut, LDR, TPL, vs, LDI, 0, m0, n0 + 16 * t, D);
           strip_mma<T, 1, PL, COL, IN, ROW>(a2, dct, LDR, TPL, ks, LDI, 0, m0, n0 + 16 * t, D);
           z[t] = a1[0];
           dr[t] = a2[0];
@@ -681,11 +755,19 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
         for (int e = 0; e < 4; ++e) {
           const int r = m0 + 4 * g + e;
           if (r >= nr) continue;
+          if constexpr (QF) {                       // gradient of this step's query q~
+            p.dqt[(xb + i0 + r) * D + d] = a[t][e];
+            continue;
+          }
           if (padded && !row.valid(i0 + r)) {     // gradient of the tile mean it used
             p.dqbar[((size_t)sl * p.b2 + i0 + r) * D + d] = a[t][e];
             continue;
           }
           const int64_t tok = row.at(i0 + r);
+          if constexpr (SM == S1_FIRST) {           // several steps: dQ accumulates in fp32
+            p.dq2[((size_t)sl * p.N + tok) * D + d] += a[t][e];
+            continue;
+          }
           const float q2 = SH::PREFETCH ? dq2s[r * (D + 4) + d] : p.dq2[((size_t)sl * p.N + tok) * D + d];
           dQ[tok * D + d] = from_f32<T>(a[t][e] + q2);
         }
@@ -701,9 +783,9 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
       for (int h = 0; h < DT / DS; ++h) {
         f32x4 (&a)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adk[s][DS * h]);
         f32x4 (&v)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adv[s][DS * h]);
-        strip_mma<T, DS, F32, COL, IN, ROW>(a, dzs, LDP, 0, qt, LDR, 0, m0, 16 * DS * h, RB);
+        strip_mma<T, DS, F32, COL, QP ? PL : IN, ROW>(a, dzs, LDP, 0, qt, LDR, TPL, m0, 16 * DS * h, RB);
         strip_mma<T, DS, F32, COL, PL, ROW>(a, rs, LDP, 0, dct, LDR, TPL, m0, 16 * DS * h, RB);
-        strip_mma<T, DS, F32, COL, PL, ROW>(v, rs, LDP, 0, dut, LDR, TPL, m0, 16 * DS * h, RB);
+        if constexpr (WV) strip_mma<T, DS, F32, COL, PL, ROW>(v, rs, LDP, 0, dut, LDR, TPL, m0, 16 * DS * h, RB);
       }
     }
   }
@@ -720,6 +802,16 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
         const int key = m0 + 4 * g + e;
         if (key >= nb || (padded && (key < jlo || key >= jhi))) continue;
         const int64_t tok = row.at(key);
+        if constexpr (SM != S1_ONLY) {            // several steps: fp32 sums over the steps
+          const size_t at = ((size_t)sl * p.N + tok) * D + d;
+          if constexpr (SM == S1_LAST) {
+            p.dkp[at] = adk[s][t][e];
+            p.dvp[at] = adv[s][t][e];
+          } else {
+            p.dkp[at] += adk[s][t][e];
+          }
+          continue;
+        }
         if (p.dkp) {     // grouped K/V: this query head's share, summed by kv_reduce_kernel
           p.dkp[((size_t)sl * p.N + tok) * D + d] = adk[s][t][e];
           p.dvp[((size_t)sl * p.N + tok) * D + d] = adv[s][t][e];
@@ -771,17 +863,48 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(const float* dkp, const 
   dv[idx] = from_f32<T>(sv);
 }
 
-// The whole backward call on stream st: the forward's stage 1 (last-step
-// kind: c, u, entropy, normaliser) and stage 2 statistics (row normalisers,
-// no output) refill the workspace, then the two backward kernels run.
-template <typename T, int D, bool PRECISE>
-ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
-  Bufs fb{b.q, b.k, b.v, nullptr, b.ws, nullptr, nullptr, nullptr, nullptr};
-  if (pl.need_qbar && launch_one<T, D, PRECISE>(pl, fb, L_QBAR, 0, st) != hipSuccess) return MA_ERR_DEVICE;
-  if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE1_LAST, 0, st) != hipSuccess) return MA_ERR_DEVICE;
-  if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE2_STATS, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+// T > 1: the gradient of the next step's queries q~ = alpha / beta, per
+// exchange row (16 lanes a row): dalpha = dq~ / beta, written over dq~, and
+// dbeta = -dq~ . q~ / beta.  A row whose L weights all underflowed (beta =
+// 0) took the tile mean in the forward; no gradient is passed back there.
+template <int D>
+__global__ __launch_bounds__(256) void alpha_grad_kernel(float* dqt, const float* beta, const float* qnext,
+                                                          float* dbt, size_t rows) {
+  constexpr int PER = D / 16;                   // floats a lane
+  const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / 16;
+  const int l = threadIdx.x % 16;
+  if (row >= rows) return;                      // whole groups of 16 lanes leave together
+  float* gq = dqt + row * D + l * PER;
+  const float* qn = qnext + row * D + l * PER;
+  f32x4 v[PER / 4];
+  float dot = 0.f;
+#pragma unroll
+  for (int c = 0; c < PER / 4; ++c) {
+    v[c] = *reinterpret_cast<const f32x4*>(gq + 4 * c);
+    const f32x4 q = *reinterpret_cast<const f32x4*>(qn + 4 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot += v[c][e] * q[e];
+  }
+  dot = sum16(dot);
+  const float b = beta[row];
+  const float inv = b > 0.f ? 1.f / b : 0.f;
+#pragma unroll
+  for (int c = 0; c < PER / 4; ++c) *reinterpret_cast<f32x4*>(gq + 4 * c) = v[c] * inv;
+  if (l == 0) dbt[row] = -dot * inv;
+}
+
+// fp32 accumulator -> output type.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_convert_kernel(const float* src, T* dst, size_t n) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx < n) dst[idx] = from_f32<T>(src[idx]);
+}
+
+template <typename T, int D>
+BwdParams bwd_params(const Plan& pl, const BwdBufs& b) {
   char* ws = b.ws;
-  BwdParams p{b.q, b.k, b.v, b.dy, b.dq, b.dk, b.dv,
+  const bool kvp = pl.group > 1 || pl.T > 1;     // fp32 dK, dV shares
+  return BwdParams{b.q, b.k, b.v, b.dy, b.dq, b.dk, b.dv,
               ws + pl.off_cx, ws + pl.off_ux,
               reinterpret_cast<const float*>(ws + pl.off_lser),
               reinterpret_cast<const float*>(ws + pl.off_h2),
@@ -789,13 +912,97 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
               reinterpret_cast<float*>(ws + pl.off_dq2),
               reinterpret_cast<float*>(ws + pl.off_dcx), reinterpret_cast<float*>(ws + pl.off_dux),
               reinterpret_cast<float*>(ws + pl.off_dhx),
-              pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
-              pl.group > 1 ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
+              kvp ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
+              kvp ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
               reinterpret_cast<float*>(ws + pl.off_dlx),
               pl.padded ? (pl.precise ? (const void*)(ws + pl.off_qbar) : (const void*)(ws + pl.off_qbar_lp))
                         : nullptr,
               pl.padded ? reinterpret_cast<float*>(ws + pl.off_dqbar) : nullptr,
+              pl.T > 1 ? reinterpret_cast<const float*>(ws + pl.off_qtil) : nullptr,
+              pl.T > 1 ? reinterpret_cast<float*>(ws + pl.off_dqt) : nullptr,
+              pl.T > 1 ? reinterpret_cast<const float*>(ws + pl.off_dbt) : nullptr,
+              pl.xlo,
               pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2, pl.heads, pl.group};
+}
+
+// dK, dV from their fp32 shares (grouped K/V: summed over the group).
+template <typename T, int D>
+void bwd_kv_out(const Plan& pl, const BwdParams& p, const BwdBufs& b, hipStream_t st) {
+  const size_t per = (size_t)pl.N * D, total = (size_t)pl.S / pl.group * per;
+  hipLaunchKernelGGL((kv_reduce_kernel<T>), dim3(grid1((total + 255) / 256)), dim3(256), 0, st, p.dkp,
+                     p.dvp, static_cast<T*>(b.dk), static_cast<T*>(b.dv), pl.heads, pl.group, per, total);
+}
+
+// T > 1 (untiled, unpadded, stage-2 columns of one key chunk).  The forward
+// is recomputed step by step into per-step state (c, entropy, both
+// normalisers, the step's queries q~ and the column sums beta of L); then
+// the steps are differentiated in reverse.  The last step as for T = 1 but
+// with q~ as its stage-1 queries (giving dq~); every earlier step t takes
+// dq~ of step t + 1 through q~ = alpha / beta into its stage 2 (dQ direct
+// and softmax parts, dc, dH) and its stage 1 (dq~ of step t, or at t = 0
+// the rest of dQ; dK).  dQ, dK and dV accumulate in fp32 over the steps.
+template <typename T, int D, bool PRECISE>
+ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
+  Bufs fb{b.q, b.k, b.v, nullptr, b.ws, nullptr, nullptr, nullptr, nullptr};
+  if (pl.need_qbar && launch_one<T, D, PRECISE>(pl, fb, L_QBAR, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+  for (int t = 0; t < pl.T; ++t) {
+    const Plan sp = step_plan(pl, t);
+    const bool last = t == pl.T - 1;
+    if (launch_one<T, D, PRECISE>(sp, fb, last ? L_STAGE1_LAST : L_STAGE1, t, st) != hipSuccess)
+      return MA_ERR_DEVICE;
+    if (launch_one<T, D, PRECISE>(sp, fb, L_STAGE2_STATS, t, st) != hipSuccess) return MA_ERR_DEVICE;
+    if (!last) {       // next queries into step t + 1's region, beta into step t's
+      Plan ap = sp;
+      ap.off_qtil = step_plan(pl, t + 1).off_qtil;
+      ap.beta_out = true;
+      if (launch_one<T, D, PRECISE>(ap, fb, L_ALPHA, t, st) != hipSuccess) return MA_ERR_DEVICE;
+    }
+  }
+  constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
+  constexpr bool SPLITC = !std::is_same<T, float>::value && PRECISE;
+  const dim3 g2(grid1((size_t)pl.S * pl.b2)), g1(grid1((size_t)pl.S * pl.b1));
+  const size_t rows = (size_t)pl.S * pl.G;
+  BwdParams p = bwd_params<T, D>(pl, b);
+  hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_COLUMN, SPLITC>), g2, dim3(NTH2), 0, st, p);
+  hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_LAST>), g1, dim3(NTH), 0, st, p);
+  for (int t = pl.T - 2; t >= 0; --t) {
+    const Plan sp = step_plan(pl, t);
+    char* ws = b.ws;
+    p.cx = ws + sp.off_cx;
+    p.lser = reinterpret_cast<const float*>(ws + sp.off_lser);
+    p.h2x = reinterpret_cast<const float*>(ws + sp.off_h2);
+    p.lse2 = reinterpret_cast<const float*>(ws + sp.off_lse2);
+    p.qtil = reinterpret_cast<const float*>(ws + sp.off_qtil);
+    hipLaunchKernelGGL((alpha_grad_kernel<D>), dim3(grid1((rows * 16 + 255) / 256)), dim3(256), 0, st, p.dqt,
+                       reinterpret_cast<const float*>(ws + sp.off_beta),
+                       reinterpret_cast<const float*>(ws + step_plan(pl, t + 1).off_qtil),
+                       reinterpret_cast<float*>(ws + pl.off_dbt), rows);
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ALPHA, SPLITC>), g2, dim3(NTH2), 0, st, p);
+    if (t > 0) hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_MID>), g1, dim3(NTH), 0, st, p);
+    else hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_FIRST>), g1, dim3(NTH), 0, st, p);
+  }
+  const size_t n = (size_t)pl.S * pl.N * D;
+  hipLaunchKernelGGL((bwd_convert_kernel<T>), dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2,
+                     static_cast<T*>(b.dq), n);
+  bwd_kv_out<T, D>(pl, p, b, st);
+  return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
+}
+
+// The whole backward call on stream st: the forward's stage 1 (last-step
+// kind: c, u, entropy, normaliser) and stage 2 statistics (row normalisers,
+// no output) refill the workspace, then the two backward kernels run.
+template <typename T, int D, bool PRECISE>
+ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
+  if constexpr (std::is_same<T, float>::value) {
+    if (pl.T > 1) return run_bwd_steps_t<T, D, PRECISE>(pl, b, st);
+  } else if (pl.T > 1) {
+    return MA_ERR_UNSUPPORTED;      // bf16 T > 1 runs the split-c entry
+  }
+  Bufs fb{b.q, b.k, b.v, nullptr, b.ws, nullptr, nullptr, nullptr, nullptr};
+  if (pl.need_qbar && launch_one<T, D, PRECISE>(pl, fb, L_QBAR, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+  if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE1_LAST, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+  if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE2_STATS, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+  const BwdParams p = bwd_params<T, D>(pl, b);
   constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
   constexpr int NB = BwdShape<T, D>::NB, RB = BwdShape<T, D>::RB, RG = BwdShape<T, D>::RG;
   if (pl.b1 <= NB) {
@@ -814,11 +1021,7 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   if (pl.padded)
     hipLaunchKernelGGL((qbar_grad_kernel<T>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(128), 0, st, p.dqbar,
                        static_cast<T*>(b.dq), pl.map, (int)pl.N, D);
-  if (pl.group > 1) {
-    const size_t per = (size_t)pl.N * D, total = (size_t)pl.S / pl.group * per;
-    hipLaunchKernelGGL((kv_reduce_kernel<T>), dim3(grid1((total + 255) / 256)), dim3(256), 0, st, p.dkp,
-                       p.dvp, static_cast<T*>(b.dk), static_cast<T*>(b.dv), pl.heads, pl.group, per, total);
-  }
+  if (pl.group > 1) bwd_kv_out<T, D>(pl, p, b, st);
   return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
 }
 

@@ -353,6 +353,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
                     kind == L_EXPORT_L ? b.L : nullptr, pl.map,
                     S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, nkeys, (nkeys + KT - 1) / KT, pl.sc2,
                     pl.xlo};
+      p.beta_out = kind == L_ALPHA && pl.beta_out ? reinterpret_cast<float*>(ws + pl.off_beta) : nullptr;
       const size_t wgs = (size_t)S * pl.b2 * pl.c1 * p.nkt;
       hipLaunchKernelGGL((alpha_kernel<T, D, PRECISE>), dim3(grid1(wgs)), dim3(THREADS), 0, st, p);
       break;

@@ -35,10 +35,30 @@ struct Plan {
   bool precise;
   size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, off_qbar_lp, total;
   size_t off_dq2, off_dcx, off_dux, off_dhx, off_dkp, off_dvp, off_dlx, off_dqbar;   // backward only
+  // backward of T > 1: per-step forward state, T regions of step_bytes from
+  // off_steps (offsets so_* inside one), the column sums beta of L, and the
+  // gradients of the next queries (dq~ / dalpha rows and dbeta)
+  size_t off_steps, step_bytes, so_cx, so_h2, so_lser, so_lse2, so_qtil, so_beta;
+  size_t off_beta, off_dqt, off_dbt;
+  bool beta_out;       // the alpha launch also stores beta at off_beta
   bool need_qbar, need_qtil;
   bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1
 };
+
+// The plan of step t of a T > 1 backward: the forward kernels read and write
+// that step's state region.
+inline Plan step_plan(const Plan& pl, int t) {
+  Plan s = pl;
+  const size_t base = pl.off_steps + (size_t)t * pl.step_bytes;
+  s.off_cx = base + pl.so_cx;
+  s.off_h2 = base + pl.so_h2;
+  s.off_lser = base + pl.so_lser;
+  s.off_lse2 = base + pl.so_lse2;
+  s.off_qtil = base + pl.so_qtil;
+  s.off_beta = base + pl.so_beta;
+  return s;
+}
 
 // The launch sequence, shared by the real run, the launch count and the
 // launch names.  `Launcher` is called once per kernel launch in order.
@@ -115,5 +135,6 @@ ma_status run_bwd_bf16_64(const Plan&, const BwdBufs&, hipStream_t);
 ma_status run_bwd_bf16_128(const Plan&, const BwdBufs&, hipStream_t);
 ma_status run_bwd_f32_64(const Plan&, const BwdBufs&, hipStream_t);
 ma_status run_bwd_f32_128(const Plan&, const BwdBufs&, hipStream_t);
+ma_status run_bwd_steps_bf16_64(const Plan&, const BwdBufs&, hipStream_t);   // T > 1, split c
 
 }  // namespace ma

@@ -53,8 +53,9 @@ ma_status validate_problem(const ma_problem* p) {
   return MA_OK;
 }
 
-// backward: the forward state it recomputes uses the plain c path for bf16
-// (its own gradient), and the workspace adds the gradient buffers
+// backward: the forward state it recomputes takes the forward's default c
+// path (bf16: plain for T = 1, split for T > 1), T > 1 keeps that state per
+// step, and the workspace adds the gradient buffers
 Plan make_plan(const ma_problem* p, bool backward = false) {
   Plan pl;
   pl.S = p->batch * p->heads;
@@ -79,7 +80,8 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
   pl.elt = p->dtype == MA_F32 ? 4 : 2;
   pl.precise = p->dtype == MA_F32 || (p->flags & MA_FLAG_PRECISE_AGGREGATE) ||
                (!(p->flags & MA_FLAG_FAST_AGGREGATE) && p->steps > 1);
-  if (backward) pl.precise = p->dtype == MA_F32;
+  if (backward) pl.precise = p->dtype == MA_F32 || p->steps > 1;
+  const bool steps_state = backward && p->steps > 1;   // per-step regions instead of one
   pl.xc_elt = pl.precise ? 4 : 2;
   pl.need_qtil = p->steps > 1;
   // tile means: the zero-weight fallback (tiles other than the own one,
@@ -90,13 +92,31 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
              !(p->flags & MA_FLAG_FORCE_STAGED);
   const size_t rows = (size_t)pl.S * pl.G * pl.c1 * pl.c2;   // exchange rows
   size_t off = 0;
-  pl.off_cx = off;   off = align_up(off + rows * pl.D * pl.xc_elt);
   pl.xlo = (pl.precise && p->dtype == MA_BF16) ? rows * pl.D : 0;
+  pl.beta_out = false;
+  pl.off_steps = pl.step_bytes = pl.so_cx = pl.so_h2 = pl.so_lser = pl.so_lse2 = pl.so_qtil = 0;
+  pl.so_beta = pl.off_beta = pl.off_dqt = pl.off_dbt = 0;
+  if (steps_state) {
+    size_t so = 0;
+    pl.so_cx = so;   so = align_up(so + rows * pl.D * pl.xc_elt);
+    pl.so_h2 = so;   so = align_up(so + rows * 4);
+    pl.so_lser = so; so = align_up(so + rows * 4);
+    pl.so_lse2 = so; so = align_up(so + (size_t)pl.S * pl.G * 4);
+    pl.so_qtil = so; so = align_up(so + rows * pl.D * 4);
+    pl.so_beta = so; so = align_up(so + rows * 4);
+    pl.step_bytes = so;
+    pl.off_steps = off; off += (size_t)pl.T * so;
+    const Plan last = step_plan(pl, pl.T - 1);   // the state the gradient kernels read first
+    pl.off_cx = last.off_cx; pl.off_h2 = last.off_h2; pl.off_lser = last.off_lser;
+    pl.off_lse2 = last.off_lse2; pl.off_qtil = last.off_qtil; pl.off_beta = last.off_beta;
+  } else {
+    pl.off_cx = off;   off = align_up(off + rows * pl.D * pl.xc_elt);
+    pl.off_h2 = off;   off = align_up(off + rows * 4);
+    pl.off_lser = off; off = align_up(off + rows * 4);
+    pl.off_lse2 = off; off = align_up(off + (size_t)pl.S * pl.G * 4);
+    pl.off_qtil = off; if (pl.need_qtil) off = align_up(off + rows * pl.D * 4);
+  }
   pl.off_ux = off;   off = align_up(off + rows * pl.D * pl.elt);
-  pl.off_h2 = off;   off = align_up(off + rows * 4);
-  pl.off_lser = off; off = align_up(off + rows * 4);
-  pl.off_lse2 = off; off = align_up(off + (size_t)pl.S * pl.G * 4);
-  pl.off_qtil = off; if (pl.need_qtil) off = align_up(off + rows * pl.D * 4);
   pl.off_qbar = off; if (pl.need_qbar) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * 4);
   // tile means in bf16 for the copied-tile first step of the plain c path
   pl.off_qbar_lp = off;
@@ -110,9 +130,13 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
     pl.off_dhx = off; off = align_up(off + rows * 4);
     pl.off_dlx = off; off = align_up(off + (size_t)pl.S * pl.G * 4);   // D of stage-2 rows
     if (pl.padded) { pl.off_dqbar = off; off = align_up(off + (size_t)pl.S * pl.b2 * pl.D * 4); }
-    if (pl.group > 1) {   // per-query-head shares of dK, dV
+    if (pl.group > 1 || steps_state) {   // per-query-head (and per-step summed) dK, dV in fp32
       pl.off_dkp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
       pl.off_dvp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
+    }
+    if (steps_state) {
+      pl.off_dqt = off; off = align_up(off + rows * pl.D * 4);
+      pl.off_dbt = off; off = align_up(off + rows * 4);
     }
   }
   pl.total = off;
@@ -165,13 +189,18 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   return run_f32_128(pl, b, st, events, n_events);
 }
 
-// The backward covers T = 1, untiled, and stage-1 blocks whose keys fit LDS
-// whole (grouped K/V and padding included; any b1).
+// The backward covers the untiled method with stage-1 blocks whose keys fit
+// LDS whole: T = 1 with grouped K/V, padding and any b1; T > 1 unpadded with
+// stage-2 columns of one key chunk (b1 <= b2 limit), bf16 at head_dim 64.
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
-  if (p->steps != 1 || p->c1 != 1 || p->c2 != 1) return MA_ERR_UNSUPPORTED;
+  if (p->c1 != 1 || p->c2 != 1) return MA_ERR_UNSUPPORTED;
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
+  if (p->steps > 1) {
+    if ((int64_t)p->b1 * p->b2 != p->seq_len || p->b1 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
+    if (p->dtype == MA_BF16 && p->head_dim != 64) return MA_ERR_UNSUPPORTED;
+  }
   return MA_OK;
 }
 
@@ -206,7 +235,8 @@ ma_status backward_impl(const ma_problem* p, const void* q, const void* k, const
   BwdBufs b{q, k, v, dy, dq, dk, dv, static_cast<char*>(workspace)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (pl.dtype == MA_BF16)
-    return pl.D == 64 ? run_bwd_bf16_64(pl, b, st) : run_bwd_bf16_128(pl, b, st);
+    return pl.T > 1 ? run_bwd_steps_bf16_64(pl, b, st)
+                    : pl.D == 64 ? run_bwd_bf16_64(pl, b, st) : run_bwd_bf16_128(pl, b, st);
   return pl.D == 64 ? run_bwd_f32_64(pl, b, st) : run_bwd_f32_128(pl, b, st);
 }
 

@@ -142,7 +142,12 @@ def test_status_strings(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(), 0),
-    (dict(steps=2), 2),                       # T > 1 not covered by the backward
+    (dict(steps=2), 0),                       # T > 1: unrolled steps
+    (dict(steps=3, dtype="f32", head_dim=128, seq_len=64 * 64, b1=64, b2=64), 0),
+    (dict(steps=2, seq_len=250), 2),          # T > 1 padded
+    (dict(steps=2, seq_len=200 * 8, b1=200, b2=8), 2),   # T > 1: columns over one key chunk
+    (dict(steps=2, head_dim=128), 2),         # T > 1 bf16 at head_dim 128 (split c over LDS)
+    (dict(steps=2, kv_heads=1), 0),           # T > 1 grouped K/V
     (dict(c1=2), 2),                          # tiled
     (dict(kv_heads=1), 0),                    # grouped K/V
     (dict(seq_len=250), 0),                   # padded

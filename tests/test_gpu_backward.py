@@ -64,9 +64,10 @@ def check_backward(cfg, slices=None, tol=None, kv_heads=None):
     return got
 
 
-def case(name, dtype, d, b1, b2, batch=1, heads=2, data="normed", layout="flat", fhw=None, seed=61):
+def case(name, dtype, d, b1, b2, batch=1, heads=2, data="normed", layout="flat", fhw=None, seed=61,
+         steps=1):
     return WorkloadConfig("case", name, batch=batch, heads=heads, seq_len=b1 * b2, head_dim=d,
-                          b1=b1, b2=b2, steps=1, dtype=dtype, data=data, seed=seed,
+                          b1=b1, b2=b2, steps=steps, dtype=dtype, data=data, seed=seed,
                           layout=layout, fhw=fhw)
 
 
@@ -164,3 +165,45 @@ def test_padded_long_columns(pad):
                          head_dim=128, b1=200, b2=40, steps=1, dtype="bf16", data="normed", seed=59,
                          pad=pad)
     check_backward(cfg)
+
+
+# ---------------------------------------------------------------------------
+# T > 1: the gradient through the unrolled steps (each step's L feeds the next
+# step's queries q~ = sum_l L q / sum_l L).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d,steps", [("f32", 64, 2), ("f32", 64, 3), ("f32", 128, 2),
+                                           ("bf16", 64, 2), ("bf16", 64, 3)])
+def test_unrolled_steps_ragged(dtype, d, steps):
+    """Ragged blocks (neither b1 nor b2 a multiple of 32)."""
+    b1, b2 = (52, 40) if (dtype == "f32" and d == 128) else (70, 52)
+    check_backward(case(f"bwd T={steps} {dtype} d{d}", dtype, d, b1, b2, data="iid", steps=steps))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unrolled_steps_full_blocks(dtype):
+    """128 x 128 (fp32 head_dim 128: 64 x 64), T = 2."""
+    check_backward(case(f"bwd T=2 128x128 {dtype}", dtype, 64, 128, 128, heads=2, steps=2))
+    if dtype == "f32":
+        check_backward(case("bwd T=2 64x64 f32 d128", dtype, 128, 64, 64, heads=1, steps=2, seed=63))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("b1,b2", [(1, 40), (40, 1), (3, 5)])
+def test_unrolled_steps_degenerate(dtype, b1, b2):
+    """One block (every step is exact attention), one key per block, a grid
+    smaller than one MFMA tile; T = 2."""
+    check_backward(case(f"bwd T=2 {b1}x{b2} {dtype}", dtype, 64, b1, b2, heads=2, data="iid", steps=2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unrolled_steps_grouped_kv(dtype):
+    """Four query heads over two K/V heads, T = 2."""
+    cfg = case(f"bwd T=2 gqa {dtype}", dtype, 64, 40, 52, batch=2, heads=4, steps=2)
+    check_backward(cfg, kv_heads=2)
+
+
+def test_n4k_t3_backward_sampled():
+    """The T = 3 workload (batch 8 x 12 heads, 64 x 64 blocks, low-rank data):
+    two slices compared whole."""
+    check_backward(WORKLOADS["n4k_t3"], slices=[(0, 0), (7, 11)])
