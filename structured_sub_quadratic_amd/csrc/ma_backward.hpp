@@ -317,7 +317,9 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   constexpr bool AL = MODE == S2_ALPHA;
   constexpr int CK = SPLITC ? PL : IN;                       // operand kind of c
   constexpr size_t CPL = (size_t)NB * LDI, CTPL = (size_t)D * LDN;   // lo planes of c, c^T
-  constexpr int LDA = D + 4;                                 // fp32 row stride of dalpha
+  constexpr bool SPLIT = !std::is_same<T, float>::value;
+  constexpr int DAK = SPLIT ? PL : IN;                       // dalpha: hi, lo planes for bf16
+  constexpr size_t DPL = (size_t)NB * LDI;
   __shared__ __attribute__((aligned(16))) T cs[(SPLITC ? 2 : 1) * NB * LDI];
   __shared__ __attribute__((aligned(16))) T us[AL ? 1 : NB * LDI];
   __shared__ __attribute__((aligned(16))) T ct[SH::KT_COPY ? (SPLITC ? 2 : 1) * D * LDN : 1];   // c^T
@@ -325,7 +327,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   __shared__ __attribute__((aligned(16))) T dys[AL ? 1 : RB * LDI];
   __shared__ __attribute__((aligned(16))) T qt[D * LDR];    // q^T of the chunk
   __shared__ __attribute__((aligned(16))) T dyt[AL ? 1 : D * LDR];   // dY^T of the chunk
-  __shared__ __attribute__((aligned(16))) float das[AL ? NB * LDA : 1];   // dalpha of the keys
+  __shared__ __attribute__((aligned(16))) T das[AL ? (SPLIT ? 2 : 1) * NB * LDI : 1];   // dalpha of the keys
   __shared__ float dbk[AL ? NB : 1];                                      // dbeta of the keys
   __shared__ __attribute__((aligned(16))) float ps[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dws[RB * LDP];
@@ -363,7 +365,17 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
         const int k = task / (D / 4), c = task % (D / 4);
         f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
         if (k < nb) v = *reinterpret_cast<const f32x4*>(p.dqt + (xb + (k0 + k) * xs) * D + c * 4);
-        *reinterpret_cast<f32x4*>(das + k * LDA + c * 4) = v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          T* at = das + k * LDI + c * 4 + e;
+          if constexpr (SPLIT) {
+            const bf16 h = (bf16)v[e];
+            at[0] = h;
+            at[DPL] = (bf16)(v[e] - (float)h);
+          } else {
+            *at = v[e];
+          }
+        }
       }
     } else {
       bwd_load_rows<T, D, LDI, NTH>(us, nullptr, NB, nb, [&](int k) { return U + (xb + (k0 + k) * xs) * D; });
@@ -402,13 +414,13 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
       for (int t = 0; t < NG; ++t) s[t] = dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (nt == NG) {
         strip_mma<T, NG, IN, ROW, CK, ROW>(s, qs, LDI, 0, cs, LDI, CPL, m0, n0, D);
-        if constexpr (AL) strip_mma<T, NG, IN, ROW, F32, ROW>(dp, qs, LDI, 0, das, LDA, 0, m0, n0, D);
+        if constexpr (AL) strip_mma<T, NG, IN, ROW, DAK, ROW>(dp, qs, LDI, 0, das, LDI, DPL, m0, n0, D);
         else strip_mma<T, NG, IN, ROW, IN, ROW>(dp, dys, LDI, 0, us, LDI, 0, m0, n0, D);
       } else {
         for (int t = 0; t < nt; ++t) {
           f32x4 a1[1] = {s[t]}, a2[1] = {dp[t]};
           strip_mma<T, 1, IN, ROW, CK, ROW>(a1, qs, LDI, 0, cs, LDI, CPL, m0, n0 + 16 * t, D);
-          if constexpr (AL) strip_mma<T, 1, IN, ROW, F32, ROW>(a2, qs, LDI, 0, das, LDA, 0, m0, n0 + 16 * t, D);
+          if constexpr (AL) strip_mma<T, 1, IN, ROW, DAK, ROW>(a2, qs, LDI, 0, das, LDI, DPL, m0, n0 + 16 * t, D);
           else strip_mma<T, 1, IN, ROW, IN, ROW>(a2, dys, LDI, 0, us, LDI, 0, m0, n0 + 16 * t, D);
           s[t] = a1[0];
           dp[t] = a2[0];
@@ -509,7 +521,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
       if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, CK, ROW>(a, dws, LDP, 0, ct, LDN, CTPL, m0, 16 * DQ * h, nbp);
       else strip_mma<T, DQ, F32, ROW, CK, COL>(a, dws, LDP, 0, cs, LDI, CPL, m0, 16 * DQ * h, nbp);
       // the direct term of the next queries: P dalpha
-      if constexpr (AL) strip_mma<T, DQ, F32, ROW, F32, COL>(a2, ps, LDP, 0, das, LDA, 0, m0, 16 * DQ * h, nbp);
+      if constexpr (AL) strip_mma<T, DQ, F32, ROW, DAK, COL>(a2, ps, LDP, 0, das, LDI, DPL, m0, 16 * DQ * h, nbp);
 #pragma unroll
       for (int t = 0; t < DQ; ++t) {
         const int d = 16 * (DQ * h + t) + lane % 16;
@@ -580,8 +592,9 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, size_t n
 // Stage 1 backward: one workgroup per (slice, block k).  SM (step mode):
 // S1_ONLY, the single step of T = 1 (queries q, dQ = stage-2 part + own);
 // with several steps, S1_LAST (queries q~ in fp32, u and V path, dq~ out,
-// dK and dV stored in fp32), S1_MID (q~, no V path, dq~ out, dK added) and
-// S1_FIRST (queries q, no V path, dQ part added, dK added).
+// dK into its fp32 sum, dV out), S1_MID (q~, no V path, dq~ out, dK added)
+// and S1_FIRST (queries q, no V path, dQ = the other parts + own, dK
+// finished).  With grouped K/V every step keeps dK, dV as fp32 shares.
 // ---------------------------------------------------------------------------
 enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3 };
 
@@ -598,6 +611,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   constexpr bool QF = SM == S1_LAST || SM == S1_MID;         // queries q~ (fp32 planes)
   constexpr bool WV = SM == S1_ONLY || SM == S1_LAST;        // u = R V path
   constexpr bool QP = QF && SPLIT;                           // queries carry a lo plane
+  constexpr bool DQO = SM == S1_ONLY || SM == S1_FIRST;      // dQ finished here
   constexpr size_t TPL = (size_t)D * LDR;                    // plane offset of the transposed grads
   constexpr size_t QPL = (size_t)RB * LDI;                   // plane offset of the query rows
   __shared__ __attribute__((aligned(16))) T ks[NB * LDI];
@@ -610,7 +624,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   __shared__ __attribute__((aligned(16))) float rs[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dzs[RB * LDP];
   __shared__ float lser[RB], dhr[RB], gr[RB], hr[RB];
-  __shared__ __attribute__((aligned(16))) float dq2s[SH::PREFETCH && SM == S1_ONLY ? RB * (D + 4) : 1];   // dQ (stage 2)
+  __shared__ __attribute__((aligned(16))) float dq2s[SH::PREFETCH && DQO ? RB * (D + 4) : 1];   // dQ (stage 2)
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int k = blockIdx.x % p.b1, sl = blockIdx.x / p.b1;
@@ -648,7 +662,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
     }
     if constexpr (WV) pdu.load(n, [&](int r) { return p.dux + (xb + i0 + r) * D; });
     pdc.load(n, [&](int r) { return p.dcx + (xb + i0 + r) * D; });
-    if constexpr (SH::PREFETCH && SM == S1_ONLY)
+    if constexpr (SH::PREFETCH && DQO)
       pdq.load(n, [&](int r) { return p.dq2 + ((size_t)sl * p.N + row.at(i0 + r)) * D; });
     if (threadIdx.x < RB) {
       pls = (int)threadIdx.x < n ? p.lser[xb + i0 + threadIdx.x] : 0.f;
@@ -668,7 +682,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
     }
     if constexpr (WV) pdu.template store_tplanes<LDR>(dut, TPL);
     pdc.template store_tplanes<LDR>(dct, TPL);
-    if constexpr (SH::PREFETCH && SM == S1_ONLY) pdq.template store_rows<D + 4>(dq2s);
+    if constexpr (SH::PREFETCH && DQO) pdq.template store_rows<D + 4>(dq2s);
     if (threadIdx.x < RB) {
       lser[threadIdx.x] = pls;
       dhr[threadIdx.x] = pdh;
@@ -764,10 +778,6 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
             continue;
           }
           const int64_t tok = row.at(i0 + r);
-          if constexpr (SM == S1_FIRST) {           // several steps: dQ accumulates in fp32
-            p.dq2[((size_t)sl * p.N + tok) * D + d] += a[t][e];
-            continue;
-          }
           const float q2 = SH::PREFETCH ? dq2s[r * (D + 4) + d] : p.dq2[((size_t)sl * p.N + tok) * D + d];
           dQ[tok * D + d] = from_f32<T>(a[t][e] + q2);
         }
@@ -791,6 +801,21 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   }
   T* dK = static_cast<T*>(p.dk) + (size_t)sl * p.N * D;
   T* dV = static_cast<T*>(p.dv) + (size_t)sl * p.N * D;
+  // several steps: the fp32 sum of dK over the later steps, all loads issued
+  // before the first store
+  constexpr bool ADD = SM == S1_MID || SM == S1_FIRST;
+  float old[ADD ? SK : 1][ADD ? DT : 1][4];
+  if constexpr (ADD) {
+#pragma unroll
+    for (int s = 0; s < SK; ++s)
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = (wave + NW * s) * 16 + 4 * g + e;
+          old[s][t][e] = key < nb ? p.dkp[((size_t)sl * p.N + row.at(key)) * D + 16 * t + lane % 16] : 0.f;
+        }
+  }
 #pragma unroll
   for (int s = 0; s < SK; ++s) {
     const int m0 = (wave + NW * s) * 16;
@@ -802,13 +827,16 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
         const int key = m0 + 4 * g + e;
         if (key >= nb || (padded && (key < jlo || key >= jhi))) continue;
         const int64_t tok = row.at(key);
-        if constexpr (SM != S1_ONLY) {            // several steps: fp32 sums over the steps
+        if constexpr (SM != S1_ONLY) {
           const size_t at = ((size_t)sl * p.N + tok) * D + d;
           if constexpr (SM == S1_LAST) {
             p.dkp[at] = adk[s][t][e];
-            p.dvp[at] = adv[s][t][e];
+            if (p.group > 1) p.dvp[at] = adv[s][t][e];
+            else dV[tok * D + d] = from_f32<T>(adv[s][t][e]);
+          } else if (SM == S1_FIRST && p.group == 1) {
+            dK[tok * D + d] = from_f32<T>(old[s][t][e] + adk[s][t][e]);
           } else {
-            p.dkp[at] += adk[s][t][e];
+            p.dkp[at] = old[s][t][e] + adk[s][t][e];
           }
           continue;
         }
@@ -893,13 +921,6 @@ __global__ __launch_bounds__(256) void alpha_grad_kernel(float* dqt, const float
   if (l == 0) dbt[row] = -dot * inv;
 }
 
-// fp32 accumulator -> output type.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_convert_kernel(const float* src, T* dst, size_t n) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx < n) dst[idx] = from_f32<T>(src[idx]);
-}
-
 template <typename T, int D>
 BwdParams bwd_params(const Plan& pl, const BwdBufs& b) {
   char* ws = b.ws;
@@ -940,7 +961,8 @@ void bwd_kv_out(const Plan& pl, const BwdParams& p, const BwdBufs& b, hipStream_
 // with q~ as its stage-1 queries (giving dq~); every earlier step t takes
 // dq~ of step t + 1 through q~ = alpha / beta into its stage 2 (dQ direct
 // and softmax parts, dc, dH) and its stage 1 (dq~ of step t, or at t = 0
-// the rest of dQ; dK).  dQ, dK and dV accumulate in fp32 over the steps.
+// the rest of dQ; dK).  dQ and dK accumulate in fp32 over the steps; the
+// step-0 stage 1, which runs last, writes them out.
 template <typename T, int D, bool PRECISE>
 ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   Bufs fb{b.q, b.k, b.v, nullptr, b.ws, nullptr, nullptr, nullptr, nullptr};
@@ -981,10 +1003,7 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
     if (t > 0) hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_MID>), g1, dim3(NTH), 0, st, p);
     else hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_FIRST>), g1, dim3(NTH), 0, st, p);
   }
-  const size_t n = (size_t)pl.S * pl.N * D;
-  hipLaunchKernelGGL((bwd_convert_kernel<T>), dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2,
-                     static_cast<T*>(b.dq), n);
-  bwd_kv_out<T, D>(pl, p, b, st);
+  if (pl.group > 1) bwd_kv_out<T, D>(pl, p, b, st);
   return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
 }
 
