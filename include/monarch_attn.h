@@ -190,11 +190,13 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * dK, dV have K's shape [batch, kv_heads, seq_len, head_dim]; with grouped
  * K/V they sum over the query heads of each group.  A padded sequence
  * (MA_FLAG_PAD_FRONT or post-padding) routes the query gradient of a padding
- * position through the tile mean it used.  Covers c1 = c2 = 1 and b2 <= 128
- * (<= 64 for fp32 with head_dim 128); with steps > 1 (the gradient through
- * every unrolled step, each step's L feeding the next step's queries) also
- * b1 within that limit, no padding, and for bf16 head_dim 64; other
- * problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
+ * position through the tile mean it used.  Covers b2 <= 128 (<= 64 for
+ * fp32 with head_dim 128) with: steps = 1, with padding or with row tiles
+ * and key segments c1, c2 (whose other-tile queries route their gradient
+ * through the tile means), not both; steps > 1 (the gradient through every
+ * unrolled step, each step's L feeding the next step's queries) with
+ * c1 = c2 = 1, b1 within the same limit, no padding, and for bf16 head_dim
+ * 64.  Other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
  * the c path the forward defaults to (plain for steps = 1, split for
  * steps > 1), so these are its gradients.  A column whose next-step weights
  * all underflow to zero (the forward then takes the tile mean as the next

@@ -55,7 +55,7 @@ struct BwdParams {
   const float* qtil; float* dqt; const float* dbt;
   size_t xlo;
   GridMap map;
-  int S, N, b1, b2;
+  int S, N, b1, b2, c1, c2;         // c1 row tiles, c2 key segments
   float sc, sc2;                    // scale, scale * log2(e)
   int heads, group;                 // K/V slice of query slice sl: kv_slice(sl, heads, group)
 };
@@ -338,13 +338,17 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   __shared__ float lsb[RS ? RG * RB : 1], dlb[RS ? RG * RB : 1];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
-  const int nkc = (p.b1 + NB - 1) / NB;                      // key chunks of NB keys
-  const int nsub = MODE == S2_COLUMN ? 1 : (MODE == S2_ROWSUM ? (p.b1 + RG * RB - 1) / (RG * RB) : nkc);
+  // the column's queries: rows r0 .. r0 + rt of row tile t; its keys: the
+  // b1 * c2 exchange rows (k, s) of (t, i)
+  const int rt = p.b1 / p.c1, nkeys = p.b1 * p.c2;
+  const int nkc = (nkeys + NB - 1) / NB;                     // key chunks of NB keys
+  const int nsub = MODE == S2_COLUMN ? 1 : (MODE == S2_ROWSUM ? (rt + RG * RB - 1) / (RG * RB) : nkc);
   const int sub = blockIdx.x % nsub;                         // row chunk (ROWSUM) or key chunk (KEYS)
-  const int i = (blockIdx.x / nsub) % p.b2, sl = blockIdx.x / nsub / p.b2;
-  float* const dlx = p.dlx + ((size_t)sl * p.b2 + i) * p.b1;   // D of the column's rows
-  const size_t xs = (size_t)p.b2;                            // exchange stride between keys
-  const size_t xb = (size_t)sl * p.b1 * p.b2 + i;            // exchange row of key 0
+  const int cid = blockIdx.x / nsub;
+  const int i = cid % p.b2, t = (cid / p.b2) % p.c1, sl = cid / p.b2 / p.c1, r0 = t * rt;
+  float* const dlx = p.dlx + ((size_t)sl * p.b2 + i) * p.b1 + r0;   // D of the column's rows
+  const size_t xs = (size_t)p.c1 * p.b2;                     // exchange stride between keys
+  const size_t xb = ((size_t)sl * p.b1 * p.c2 * p.c1 + t) * p.b2 + i;   // exchange row of key 0
   const T* C = static_cast<const T*>(p.cx);
   const T* U = static_cast<const T*>(p.ux);
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
@@ -354,7 +358,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   int k0 = 0, nb = 0, nbp = 0;                               // current key chunk
   auto load_keys = [&](int kc) {
     k0 = kc * NB;
-    nb = min(NB, p.b1 - k0);
+    nb = min(NB, nkeys - k0);
     nbp = (nb + SH::KQ - 1) / SH::KQ * SH::KQ;
     bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(cs, ct, NB, nb, [&](int k) { return C + (xb + (k0 + k) * xs) * D; });
     if constexpr (SPLITC)
@@ -389,14 +393,14 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
   RowsIn<T, D, RB, NTH> pq, pdy;
   float pls = 0.f, pdl = 0.f;
   auto fetch = [&](int l0) {
-    const int n = min(RB, p.b1 - l0);
-    pq.load(n, [&](int r) { return Q + col.at(l0 + r) * D; });
+    const int n = min(RB, rt - l0);
+    pq.load(n, [&](int r) { return Q + col.at(r0 + l0 + r) * D; });
     if constexpr (!AL)
       pdy.load(n, [&](int r) -> const T* {     // no upstream gradient at padding rows
-        return !padded || col.valid(l0 + r) ? dY + col.at(l0 + r) * D : nullptr;
+        return !padded || col.valid(r0 + l0 + r) ? dY + col.at(r0 + l0 + r) * D : nullptr;
       });
     if (threadIdx.x < RB) {
-      pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + l0 + threadIdx.x] : 0.f;
+      pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + r0 + l0 + threadIdx.x] : 0.f;
       if (MODE == S2_KEYS) pdl = (int)threadIdx.x < n ? dlx[l0 + threadIdx.x] : 0.f;
     }
   };
@@ -473,13 +477,13 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
       __syncthreads();
       for (int c = 0; c < RG; ++c) {
         const int l0 = g0 + c * RB;
-        if (l0 >= p.b1) break;
-        scores(min(RB, p.b1 - l0), false, dlb + c * RB, qsb + c * RB * LDI, dysb + c * RB * LDI, lsb + c * RB);
+        if (l0 >= rt) break;
+        scores(min(RB, rt - l0), false, dlb + c * RB, qsb + c * RB * LDI, dysb + c * RB * LDI, lsb + c * RB);
       }
     }
     __syncthreads();
     for (int r = threadIdx.x; r < RG * RB; r += NTH)
-      if (g0 + r < p.b1) dlx[g0 + r] = dlb[r];
+      if (g0 + r < rt) dlx[g0 + r] = dlb[r];
     return;
   }
 
@@ -492,8 +496,8 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
 #pragma unroll
     for (int t = 0; t < DT; ++t) adc[s][t] = adu[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   fetch(0);
-  for (int l0 = 0; l0 < p.b1; l0 += RB) {
-    const int nr = min(RB, p.b1 - l0);
+  for (int l0 = 0; l0 < rt; l0 += RB) {
+    const int nr = min(RB, rt - l0);
     __syncthreads();
     pq.template store<LDI, true, LDR>(qs, qt);
     if constexpr (!AL) pdy.template store<LDI, true, LDR>(dys, dyt);
@@ -501,7 +505,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
       lsel[threadIdx.x] = pls;
       dl[threadIdx.x] = MODE == S2_KEYS ? pdl : 0.f;
     }
-    if (l0 + RB < p.b1) fetch(l0 + RB);       // in flight while this chunk computes
+    if (l0 + RB < rt) fetch(l0 + RB);       // in flight while this chunk computes
     __syncthreads();
     scores(nr, true, MODE == S2_KEYS ? nullptr : dl, qs, dys, lsel);
     __syncthreads();
@@ -528,8 +532,8 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdP
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
-          if (row >= nr || (padded && !col.valid(l0 + row))) continue;
-          float* at = p.dq2 + ((size_t)sl * p.N + col.at(l0 + row)) * D + d;
+          if (row >= nr || (padded && !col.valid(r0 + l0 + row))) continue;
+          float* at = p.dq2 + ((size_t)sl * p.N + col.at(r0 + l0 + row)) * D + d;
           if (MODE == S2_KEYS) atomicAdd(at, a[t][e] * p.sc);     // zeroed before the kernel
           else if (AL) *at += a[t][e] * p.sc + a2[t][e];          // later steps' parts are in
           else *at = a[t][e] * p.sc;
@@ -595,8 +599,12 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, size_t n
 // dK into its fp32 sum, dV out), S1_MID (q~, no V path, dq~ out, dK added)
 // and S1_FIRST (queries q, no V path, dQ = the other parts + own, dK
 // finished).  With grouped K/V every step keeps dK, dV as fp32 shares.
+// S1_TILED (T = 1 with row tiles and key segments): one workgroup per
+// (slice, block k, segment s) with the segment's keys and the c1 * b2
+// queries (t, i) -- q(k, i) for k's own row tile, the tile mean of (t, i)
+// otherwise; each query's gradient goes to its exchange row (dq~).
 // ---------------------------------------------------------------------------
-enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3 };
+enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3, S1_TILED = 4 };
 
 template <typename T, int D, int SM = S1_ONLY>
 __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdParams p) {
@@ -609,7 +617,8 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   constexpr int SK = SH::SK;                                 // key-tile strips of dK, dV per wave
   constexpr bool SPLIT = !std::is_same<T, float>::value;
   constexpr bool QF = SM == S1_LAST || SM == S1_MID;         // queries q~ (fp32 planes)
-  constexpr bool WV = SM == S1_ONLY || SM == S1_LAST;        // u = R V path
+  constexpr bool TL = SM == S1_TILED;
+  constexpr bool WV = SM == S1_ONLY || SM == S1_LAST || TL;  // u = R V path
   constexpr bool QP = QF && SPLIT;                           // queries carry a lo plane
   constexpr bool DQO = SM == S1_ONLY || SM == S1_FIRST;      // dQ finished here
   constexpr size_t TPL = (size_t)D * LDR;                    // plane offset of the transposed grads
@@ -627,17 +636,23 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   __shared__ __attribute__((aligned(16))) float dq2s[SH::PREFETCH && DQO ? RB * (D + 4) : 1];   // dQ (stage 2)
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
-  const int k = blockIdx.x % p.b1, sl = blockIdx.x / p.b1;
-  const int nb = p.b2, nbp = (nb + SH::KQ - 1) / SH::KQ * SH::KQ;
-  const size_t xb = ((size_t)sl * p.b1 + k) * p.b2;          // exchange row of (k, i = 0)
+  const int nseg = TL ? p.c2 : 1, sg = blockIdx.x % nseg;
+  const int k = (blockIdx.x / nseg) % p.b1, sl = blockIdx.x / nseg / p.b1;
+  const int nb = p.b2 / nseg, nbp = (nb + SH::KQ - 1) / SH::KQ * SH::KQ;
+  const int j0 = sg * nb;                                    // first key of the segment
+  const int nq = TL ? p.c1 * p.b2 : p.b2;                    // query rows (t, i)
+  const int own = k / (p.b1 / p.c1);                         // row tile of block k
+  // exchange row of query row 0 (rows (t, i) of one (k, s) are contiguous)
+  const size_t xb = ((size_t)sl * p.b1 + k) * (TL ? (size_t)p.c2 * p.c1 * p.b2 : (size_t)p.b2) +
+                    (TL ? (size_t)sg * p.c1 * p.b2 : 0);
   const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
   const int kvs = kv_slice(sl, p.heads, p.group);
   const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
   const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
   const AxisMap row = p.map.row_axis(k);
 
-  bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(ks, kt, NB, nb, [&](int j) { return K + row.at(j) * D; });
-  if constexpr (WV) bwd_load_rows<T, D, LDI, NTH>(vs, nullptr, NB, nb, [&](int j) { return V + row.at(j) * D; });
+  bwd_load_rows<T, D, LDI, NTH, SH::KT_COPY, LDN>(ks, kt, NB, nb, [&](int j) { return K + row.at(j0 + j) * D; });
+  if constexpr (WV) bwd_load_rows<T, D, LDI, NTH>(vs, nullptr, NB, nb, [&](int j) { return V + row.at(j0 + j) * D; });
   f32x4 adk[SK][DT], adv[SK][DT];
 #pragma unroll
   for (int s = 0; s < SK; ++s)
@@ -649,12 +664,17 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
   float pls = 0.f, pdh = 0.f;
   // a padding position (k, i) took the tile mean of column i as its query
   const bool padded = p.map.padded();
-  const T* QB = static_cast<const T*>(p.qbt) + (size_t)sl * p.b2 * D;
+  const T* QB = static_cast<const T*>(p.qbt) + (size_t)sl * (TL ? p.c1 : 1) * p.b2 * D;
   const int jlo = p.map.key_lo(k), jhi = p.map.key_hi(k);   // real keys of block k
   auto fetch = [&](int i0) {
-    const int n = min(RB, p.b2 - i0);
+    const int n = min(RB, nq - i0);
     if constexpr (QF) {
       pqf.load(n, [&](int r) { return p.qtil + (xb + i0 + r) * D; });
+    } else if constexpr (TL) {
+      pq.load(n, [&](int r) {
+        const int q = i0 + r, t = q / p.b2, i = q % p.b2;
+        return t == own ? Q + row.at(i) * D : QB + (size_t)q * D;
+      });
     } else {
       pq.load(n, [&](int r) {
         return !padded || row.valid(i0 + r) ? Q + row.at(i0 + r) * D : QB + (size_t)(i0 + r) * D;
@@ -670,8 +690,8 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
     }
   };
   if constexpr (SH::PREFETCH) fetch(0);
-  for (int i0 = 0; i0 < p.b2; i0 += RB) {
-    const int nr = min(RB, p.b2 - i0);
+  for (int i0 = 0; i0 < nq; i0 += RB) {
+    const int nr = min(RB, nq - i0);
     __syncthreads();
     if constexpr (!SH::PREFETCH) fetch(i0);
     if constexpr (QF) {
@@ -690,7 +710,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
       hr[threadIdx.x] = 0.f;
     }
     if constexpr (SH::PREFETCH) {
-      if (i0 + RB < p.b2) fetch(i0 + RB);     // in flight while this chunk computes
+      if (i0 + RB < nq) fetch(i0 + RB);     // in flight while this chunk computes
     }
     __syncthreads();
     // R = exp2(sc2 q.k - lse2), dR = du V^T + dc K^T, G = rowsum(R dR) and
@@ -769,7 +789,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
         for (int e = 0; e < 4; ++e) {
           const int r = m0 + 4 * g + e;
           if (r >= nr) continue;
-          if constexpr (QF) {                       // gradient of this step's query q~
+          if constexpr (QF || TL) {                 // gradient of this query row (q~, or own / tile mean)
             p.dqt[(xb + i0 + r) * D + d] = a[t][e];
             continue;
           }
@@ -813,7 +833,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = (wave + NW * s) * 16 + 4 * g + e;
-          old[s][t][e] = key < nb ? p.dkp[((size_t)sl * p.N + row.at(key)) * D + 16 * t + lane % 16] : 0.f;
+          old[s][t][e] = key < nb ? p.dkp[((size_t)sl * p.N + row.at(j0 + key)) * D + 16 * t + lane % 16] : 0.f;
         }
   }
 #pragma unroll
@@ -826,8 +846,8 @@ __global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdPa
       for (int e = 0; e < 4; ++e) {
         const int key = m0 + 4 * g + e;
         if (key >= nb || (padded && (key < jlo || key >= jhi))) continue;
-        const int64_t tok = row.at(key);
-        if constexpr (SM != S1_ONLY) {
+        const int64_t tok = row.at(j0 + key);
+        if constexpr (SM == S1_LAST || SM == S1_MID || SM == S1_FIRST) {   // several steps
           const size_t at = ((size_t)sl * p.N + tok) * D + d;
           if constexpr (SM == S1_LAST) {
             p.dkp[at] = adk[s][t][e];
@@ -867,6 +887,34 @@ __global__ __launch_bounds__(128) void qbar_grad_kernel(const float* dqbar, T* d
     if (!map.valid(l, i)) continue;
     T* at = Y + map.token(l, i) * D + d;
     *at = from_f32<T>(to_f32(*at) + gv);
+  }
+}
+
+// Row tiles / key segments (T = 1): the query gradient of exchange row
+// (k, s, t, i) belongs to q(k, i) when t is k's own row tile and to the tile
+// mean qbar(t, i) otherwise; qbar(t, i) is the mean of the rt rows of tile t,
+// so each of them gets 1/rt of its gradient.  One workgroup per (slice, t,
+// i), one thread per d: dQ(l, i) = stage-2 part + own rows + dqbar / rt.
+template <typename T>
+__global__ __launch_bounds__(128) void tiled_dq_kernel(const float* dqx, const float* dq2, T* dq, GridMap map,
+                                                       int N, int D, int b1, int b2, int c1, int c2) {
+  const int i = blockIdx.x % b2, t = (blockIdx.x / b2) % c1, sl = blockIdx.x / b2 / c1, d = threadIdx.x;
+  if (d >= D) return;
+  const int rt = b1 / c1;
+  // exchange row (k, s, t, i) = (((sl b1 + k) c2 + s) c1 + t) b2 + i
+  auto at = [&](int k, int s) { return dqx[(((((size_t)sl * b1 + k) * c2 + s) * c1 + t) * b2 + i) * D + d]; };
+  float bar = 0.f;
+  for (int k = 0; k < b1; ++k) {
+    if (k / rt == t) continue;
+    for (int s = 0; s < c2; ++s) bar += at(k, s);
+  }
+  bar /= (float)rt;
+  for (int r = 0; r < rt; ++r) {
+    const int l = t * rt + r;
+    float own = 0.f;
+    for (int s = 0; s < c2; ++s) own += at(l, s);
+    const size_t o = ((size_t)sl * N + map.token(l, i)) * D + d;
+    dq[o] = from_f32<T>(dq2[o] + own + bar);
   }
 }
 
@@ -936,14 +984,16 @@ BwdParams bwd_params(const Plan& pl, const BwdBufs& b) {
               kvp ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
               kvp ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
               reinterpret_cast<float*>(ws + pl.off_dlx),
-              pl.padded ? (pl.precise ? (const void*)(ws + pl.off_qbar) : (const void*)(ws + pl.off_qbar_lp))
-                        : nullptr,
+              pl.padded || pl.c1 > 1
+                  ? (pl.precise ? (const void*)(ws + pl.off_qbar) : (const void*)(ws + pl.off_qbar_lp))
+                  : nullptr,
               pl.padded ? reinterpret_cast<float*>(ws + pl.off_dqbar) : nullptr,
               pl.T > 1 ? reinterpret_cast<const float*>(ws + pl.off_qtil) : nullptr,
-              pl.T > 1 ? reinterpret_cast<float*>(ws + pl.off_dqt) : nullptr,
+              pl.T > 1 || pl.c1 > 1 || pl.c2 > 1 ? reinterpret_cast<float*>(ws + pl.off_dqt) : nullptr,
               pl.T > 1 ? reinterpret_cast<const float*>(ws + pl.off_dbt) : nullptr,
               pl.xlo,
-              pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.scale, pl.sc2, pl.heads, pl.group};
+              pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.c1, pl.c2, pl.scale, pl.sc2, pl.heads,
+              pl.group};
 }
 
 // dK, dV from their fp32 shares (grouped K/V: summed over the group).
@@ -1024,19 +1074,27 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   const BwdParams p = bwd_params<T, D>(pl, b);
   constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
   constexpr int NB = BwdShape<T, D>::NB, RB = BwdShape<T, D>::RB, RG = BwdShape<T, D>::RG;
-  if (pl.b1 <= NB) {
-    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_COLUMN>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(NTH2), 0,
-                       st, p);
+  // stage-2 columns: (slice, row tile t, column i), rt queries over b1 * c2 keys
+  const size_t cols = (size_t)pl.S * pl.c1 * pl.b2;
+  const int nkeys = pl.b1 * pl.c2;
+  if (nkeys <= NB) {
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_COLUMN>), dim3(grid1(cols)), dim3(NTH2), 0, st, p);
   } else {                                 // D first, then one workgroup per key chunk
     const size_t n = (size_t)pl.S * pl.N * D;
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2, n);
-    const size_t cols = (size_t)pl.S * pl.b2;
     hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM>),
-                       dim3(grid1(cols * ((pl.b1 + RG * RB - 1) / (RG * RB)))), dim3(NTH2), 0, st, p);
-    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS>), dim3(grid1(cols * ((pl.b1 + NB - 1) / NB))),
+                       dim3(grid1(cols * ((pl.rt + RG * RB - 1) / (RG * RB)))), dim3(NTH2), 0, st, p);
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS>), dim3(grid1(cols * ((nkeys + NB - 1) / NB))),
                        dim3(NTH2), 0, st, p);
   }
-  hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
+  if (pl.c1 > 1 || pl.c2 > 1) {            // per (block, segment), then the query gradients
+    hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_TILED>), dim3(grid1((size_t)pl.S * pl.b1 * pl.c2)),
+                       dim3(NTH), 0, st, p);
+    hipLaunchKernelGGL((tiled_dq_kernel<T>), dim3(grid1(cols)), dim3(128), 0, st, p.dqt, p.dq2,
+                       static_cast<T*>(b.dq), pl.map, (int)pl.N, D, pl.b1, pl.b2, pl.c1, pl.c2);
+  } else {
+    hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
+  }
   if (pl.padded)
     hipLaunchKernelGGL((qbar_grad_kernel<T>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(128), 0, st, p.dqbar,
                        static_cast<T*>(b.dq), pl.map, (int)pl.N, D);

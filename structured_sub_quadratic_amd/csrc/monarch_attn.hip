@@ -82,6 +82,7 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
                (!(p->flags & MA_FLAG_FAST_AGGREGATE) && p->steps > 1);
   if (backward) pl.precise = p->dtype == MA_F32 || p->steps > 1;
   const bool steps_state = backward && p->steps > 1;   // per-step regions instead of one
+  const bool tiled_bwd = backward && (p->c1 > 1 || p->c2 > 1);   // query gradients per exchange row
   pl.xc_elt = pl.precise ? 4 : 2;
   pl.need_qtil = p->steps > 1;
   // tile means: the zero-weight fallback (tiles other than the own one,
@@ -134,10 +135,8 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
       pl.off_dkp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
       pl.off_dvp = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
     }
-    if (steps_state) {
-      pl.off_dqt = off; off = align_up(off + rows * pl.D * 4);
-      pl.off_dbt = off; off = align_up(off + rows * 4);
-    }
+    if (steps_state || tiled_bwd) { pl.off_dqt = off; off = align_up(off + rows * pl.D * 4); }
+    if (steps_state) { pl.off_dbt = off; off = align_up(off + rows * 4); }
   }
   pl.total = off;
   return pl;
@@ -189,13 +188,15 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   return run_f32_128(pl, b, st, events, n_events);
 }
 
-// The backward covers the untiled method with stage-1 blocks whose keys fit
-// LDS whole: T = 1 with grouped K/V, padding and any b1; T > 1 unpadded with
-// stage-2 columns of one key chunk (b1 <= b2 limit), bf16 at head_dim 64.
+// The backward covers stage-1 blocks whose keys fit LDS whole: T = 1 with
+// grouped K/V, any b1, and padding or row tiles / key segments (not both);
+// T > 1 untiled and unpadded with stage-2 columns of one key chunk (b1
+// within the same limit), bf16 at head_dim 64.
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
-  if (p->c1 != 1 || p->c2 != 1) return MA_ERR_UNSUPPORTED;
+  const bool tiled = p->c1 != 1 || p->c2 != 1;
+  if (tiled && (p->steps > 1 || (int64_t)p->b1 * p->b2 != p->seq_len)) return MA_ERR_UNSUPPORTED;
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
   if (p->steps > 1) {
     if ((int64_t)p->b1 * p->b2 != p->seq_len || p->b1 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;

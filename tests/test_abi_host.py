@@ -148,7 +148,10 @@ def test_status_strings(lib):
     (dict(steps=2, seq_len=200 * 8, b1=200, b2=8), 2),   # T > 1: columns over one key chunk
     (dict(steps=2, head_dim=128), 2),         # T > 1 bf16 at head_dim 128 (split c over LDS)
     (dict(steps=2, kv_heads=1), 0),           # T > 1 grouped K/V
-    (dict(c1=2), 2),                          # tiled
+    (dict(c1=2), 0),                          # row tiles
+    (dict(c1=2, c2=4), 0),                    # row tiles and key segments
+    (dict(c1=2, steps=2), 2),                 # tiled T > 1
+    (dict(c2=2, seq_len=250), 2),             # tiled and padded
     (dict(kv_heads=1), 0),                    # grouped K/V
     (dict(seq_len=250), 0),                   # padded
     (dict(seq_len=256 * 200, b1=200, b2=256), 2),   # blocks wider than 128 keys

@@ -65,10 +65,10 @@ def check_backward(cfg, slices=None, tol=None, kv_heads=None):
 
 
 def case(name, dtype, d, b1, b2, batch=1, heads=2, data="normed", layout="flat", fhw=None, seed=61,
-         steps=1):
+         steps=1, c1=1, c2=1):
     return WorkloadConfig("case", name, batch=batch, heads=heads, seq_len=b1 * b2, head_dim=d,
                           b1=b1, b2=b2, steps=steps, dtype=dtype, data=data, seed=seed,
-                          layout=layout, fhw=fhw)
+                          layout=layout, fhw=fhw, c1=c1, c2=c2)
 
 
 def test_n256_backward():
@@ -207,3 +207,38 @@ def test_n4k_t3_backward_sampled():
     """The T = 3 workload (batch 8 x 12 heads, 64 x 64 blocks, low-rank data):
     two slices compared whole."""
     check_backward(WORKLOADS["n4k_t3"], slices=[(0, 0), (7, 11)])
+
+
+# ---------------------------------------------------------------------------
+# Row tiles and key segments (T = 1): each block's R rows run per (row tile,
+# key segment), with the tile mean as the query of the other tiles.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("c1,c2", [(2, 2), (2, 1), (1, 2), (4, 4)])
+def test_tiled_small(dtype, c1, c2):
+    check_backward(case(f"bwd tiled {c1}x{c2} {dtype}", dtype, 64, 16, 16, data="iid", c1=c1, c2=c2))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("f32", 128), ("bf16", 128)])
+def test_tiled_ragged(dtype, d):
+    """Three row tiles of 16 rows, two segments of 26 keys (neither a
+    multiple of 32)."""
+    check_backward(case(f"bwd tiled ragged {dtype} d{d}", dtype, d, 48, 52, data="normed", c1=3, c2=2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiled_columns_over_one_key_chunk(dtype):
+    """b1 * c2 = 200 stage-2 keys per (row tile, column): the key-chunk path."""
+    check_backward(case(f"bwd tiled b1=100 {dtype}", dtype, 64, 100, 24, heads=1, c1=2, c2=2))
+
+
+def test_tiled_grouped_kv():
+    cfg = case("bwd tiled gqa", "bf16", 64, 32, 24, batch=2, heads=4, c1=2, c2=3)
+    check_backward(cfg, kv_heads=1)
+
+
+def test_video_tiled_backward_sampled():
+    """The tiled video latent (630 x 52, c1 = c2 = 2, d = 128, 12 heads): two
+    slices compared whole."""
+    check_backward(WORKLOADS["video_tiled"], slices=[(0, 0), (0, 5)])
