@@ -125,8 +125,11 @@ def backward_flops(cfg):
     direct P dalpha term and dc (5 over b1), stage 1 R, dR, dq~ and dK (two
     products; 5 over b2).  The rebuilt forward: per step c (2 over b2) and
     the stage-2 normalisers (1 over b1), u once (1 over b2), and the next
-    queries of every step but the last (2 over b1)."""
-    N, d, b1, b2, T = cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2, cfg.steps
+    queries of every step but the last (2 over b1).  With row tiles and key
+    segments a stage-2 query meets b1 * c2 keys and a key c1 * b2 stage-1
+    queries, which take the places of b1 and b2."""
+    N, d, T = cfg.seq_len, cfg.head_dim, cfg.steps
+    b1, b2 = cfg.b1 * cfg.c2, cfg.c1 * cfg.b2
     per = (5 * b1 + 7 * b2) + (T - 1) * (5 * b1 + 5 * b2) + T * (2 * b2 + b1) + b2 + (T - 1) * 2 * b1
     return 2 * N * d * per * cfg.slices
 

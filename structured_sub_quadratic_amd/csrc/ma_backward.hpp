@@ -894,22 +894,30 @@ __global__ __launch_bounds__(128) void qbar_grad_kernel(const float* dqbar, T* d
 // (k, s, t, i) belongs to q(k, i) when t is k's own row tile and to the tile
 // mean qbar(t, i) otherwise; qbar(t, i) is the mean of the rt rows of tile t,
 // so each of them gets 1/rt of its gradient.  One workgroup per (slice, t,
-// i), one thread per d: dQ(l, i) = stage-2 part + own rows + dqbar / rt.
-template <typename T>
-__global__ __launch_bounds__(128) void tiled_dq_kernel(const float* dqx, const float* dq2, T* dq, GridMap map,
-                                                       int N, int D, int b1, int b2, int c1, int c2) {
-  const int i = blockIdx.x % b2, t = (blockIdx.x / b2) % c1, sl = blockIdx.x / b2 / c1, d = threadIdx.x;
-  if (d >= D) return;
+// i): 512 / D groups of D threads split the blocks k (the sum for qbar, then
+// the rows of tile t): dQ(l, i) = stage-2 part + own rows + dqbar / rt.
+template <typename T, int D>
+__global__ __launch_bounds__(512) void tiled_dq_kernel(const float* dqx, const float* dq2, T* dq, GridMap map,
+                                                       int N, int b1, int b2, int c1, int c2) {
+  constexpr int NG = 512 / D;
+  __shared__ float part[NG][D];
+  const int i = blockIdx.x % b2, t = (blockIdx.x / b2) % c1, sl = blockIdx.x / b2 / c1;
+  const int d = threadIdx.x % D, grp = threadIdx.x / D;
   const int rt = b1 / c1;
   // exchange row (k, s, t, i) = (((sl b1 + k) c2 + s) c1 + t) b2 + i
   auto at = [&](int k, int s) { return dqx[(((((size_t)sl * b1 + k) * c2 + s) * c1 + t) * b2 + i) * D + d]; };
   float bar = 0.f;
-  for (int k = 0; k < b1; ++k) {
+  for (int k = grp; k < b1; k += NG) {
     if (k / rt == t) continue;
     for (int s = 0; s < c2; ++s) bar += at(k, s);
   }
+  part[grp][d] = bar;
+  __syncthreads();
+  bar = 0.f;
+#pragma unroll
+  for (int g2 = 0; g2 < NG; ++g2) bar += part[g2][d];
   bar /= (float)rt;
-  for (int r = 0; r < rt; ++r) {
+  for (int r = grp; r < rt; r += NG) {
     const int l = t * rt + r;
     float own = 0.f;
     for (int s = 0; s < c2; ++s) own += at(l, s);
@@ -1090,8 +1098,8 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   if (pl.c1 > 1 || pl.c2 > 1) {            // per (block, segment), then the query gradients
     hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_TILED>), dim3(grid1((size_t)pl.S * pl.b1 * pl.c2)),
                        dim3(NTH), 0, st, p);
-    hipLaunchKernelGGL((tiled_dq_kernel<T>), dim3(grid1(cols)), dim3(128), 0, st, p.dqt, p.dq2,
-                       static_cast<T*>(b.dq), pl.map, (int)pl.N, D, pl.b1, pl.b2, pl.c1, pl.c2);
+    hipLaunchKernelGGL((tiled_dq_kernel<T, D>), dim3(grid1(cols)), dim3(512), 0, st, p.dqt, p.dq2,
+                       static_cast<T*>(b.dq), pl.map, (int)pl.N, pl.b1, pl.b2, pl.c1, pl.c2);
   } else {
     hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
   }
