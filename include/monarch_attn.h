@@ -195,8 +195,8 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * and key segments c1, c2 (whose other-tile queries route their gradient
  * through the tile means), not both; steps > 1 (the gradient through every
  * unrolled step, each step's L feeding the next step's queries) with
- * c1 = c2 = 1, b1 within the same limit, no padding, and for bf16 head_dim
- * 64.  Other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
+ * c1 = c2 = 1, b1 within the same limit, no padding, and for bf16 at
+ * head_dim 128 b1, b2 <= 64.  Other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
  * the c path the forward defaults to (plain for steps = 1, split for
  * steps > 1), so these are its gradients.  A column whose next-step weights
  * all underflow to zero (the forward then takes the tile mean as the next

@@ -60,17 +60,21 @@ struct BwdParams {
   int heads, group;                 // K/V slice of query slice sl: kv_slice(sl, heads, group)
 };
 
-template <typename T, int D> struct BwdShape {
+// NBK: keys held in LDS (0: the largest that fits, 128; 64 for fp32 with
+// head_dim 128).  A 64-key build serves blocks and columns of at most 64
+// keys with about half the LDS, so two workgroups share a CU.
+template <typename T, int D, int NBK = 0> struct BwdShape {
   static constexpr bool F32 = std::is_same<T, float>::value;
-  static constexpr int NB = (F32 && D == 128) ? 64 : 128;   // keys held in LDS
+  static constexpr int NB = NBK ? NBK : ((F32 && D == 128) ? 64 : 128);   // keys held in LDS
   static constexpr int RB = 32;                             // query rows per chunk
   static constexpr int LDI = D + 16 / (int)sizeof(T);       // row stride over d (input type)
   static constexpr int LDN = NB + 16 / (int)sizeof(T);      // row stride over keys (input type)
   static constexpr int LDR = RB + 16 / (int)sizeof(T);      // row stride over chunk rows
   static constexpr int LDP = NB + 4;                        // fp32 row stride over keys
   static constexpr int KQ = F32 ? 16 : 32;                  // key count granularity
-  // transposed copies of the keys (K^T, c^T) for the dQ product when LDS allows
-  static constexpr bool KT_COPY = D == 64 && !F32;
+  // transposed copies of the keys (K^T, c^T) for the dQ product when LDS
+  // allows (not in 64-key builds, which are there to halve the LDS)
+  static constexpr bool KT_COPY = D == 64 && !F32 && NB == 128;
   // waves per workgroup: 8 at head_dim 128 halve the per-wave accumulators
   static constexpr int NW = D == 64 ? 8 : 4;
   static constexpr int NG = NW == 8 ? 2 : 4;                // key tiles per score strip
@@ -305,9 +309,9 @@ __device__ inline void bwd_load_rows(T* dst, T* dt, int NR, int n, Src src) {
 // ---------------------------------------------------------------------------
 enum { S2_COLUMN = 0, S2_ROWSUM = 1, S2_KEYS = 2, S2_ALPHA = 3 };
 
-template <typename T, int D, int MODE, bool SPLITC = false>
-__global__ __launch_bounds__((BwdShape<T, D>::NTH2)) void stage2_bwd_kernel(BwdParams p) {
-  typedef BwdShape<T, D> SH;
+template <typename T, int D, int MODE, bool SPLITC = false, int NBK = 0>
+__global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel(BwdParams p) {
+  typedef BwdShape<T, D, NBK> SH;
   constexpr int NW = SH::NW2, NTH = SH::NTH2, RG = SH::RG;
   constexpr int NB = SH::NB, RB = SH::RB, LDI = SH::LDI, LDN = SH::LDN, LDR = SH::LDR, LDP = SH::LDP;
   constexpr int DT = D / 16, NG = SH::NG2;                   // d tiles; key tiles per score strip
@@ -606,9 +610,9 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, size_t n
 // ---------------------------------------------------------------------------
 enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3, S1_TILED = 4 };
 
-template <typename T, int D, int SM = S1_ONLY>
-__global__ __launch_bounds__((BwdShape<T, D>::NTH)) void stage1_bwd_kernel(BwdParams p) {
-  typedef BwdShape<T, D> SH;
+template <typename T, int D, int SM = S1_ONLY, int NBK = 0>
+__global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(BwdParams p) {
+  typedef BwdShape<T, D, NBK> SH;
   constexpr int NW = SH::NW, NTH = SH::NTH;
   constexpr int NB = SH::NB, RB = SH::RB, LDI = SH::LDI, LDN = SH::LDN, LDR = SH::LDR, LDP = SH::LDP;
   constexpr int DT = D / 16, NG = SH::NG;
@@ -1012,6 +1016,29 @@ void bwd_kv_out(const Plan& pl, const BwdParams& p, const BwdBufs& b, hipStream_
                      p.dvp, static_cast<T*>(b.dk), static_cast<T*>(b.dv), pl.heads, pl.group, per, total);
 }
 
+// Launch of a stage-2 backward build: the 64-key build (two workgroups a CU
+// where the registers allow) when the default holds more and `small` says
+// the keys fit 64; ONLY64 launches nothing else (bf16 head_dim 128 with
+// split c, whose 128-key tiles exceed LDS).
+#define MA_BWD2(MODE, SC, small, grid)                                                               \
+  do {                                                                                             \
+    if constexpr (BwdShape<T, D>::NB > 64) {                                                       \
+      if (ONLY64 || (small)) {                                                                     \
+        hipLaunchKernelGGL((stage2_bwd_kernel<T, D, MODE, SC, 64>), grid, dim3(NTH2), 0, st, p);   \
+        break;                                                                                     \
+      }                                                                                            \
+    }                                                                                              \
+    if constexpr (!ONLY64) hipLaunchKernelGGL((stage2_bwd_kernel<T, D, MODE, SC>), grid, dim3(NTH2), 0, st, p); \
+  } while (0)
+// Stage 1: the 64-key build only where the default does not fit (ONLY64);
+// its registers allow one workgroup a CU either way, and the default keeps
+// the transposed key copy.
+#define MA_BWD1(SM, grid)                                                                            \
+  do {                                                                                             \
+    if constexpr (ONLY64) hipLaunchKernelGGL((stage1_bwd_kernel<T, D, SM, 64>), grid, dim3(NTH), 0, st, p); \
+    else hipLaunchKernelGGL((stage1_bwd_kernel<T, D, SM>), grid, dim3(NTH), 0, st, p);             \
+  } while (0)
+
 // T > 1 (untiled, unpadded, stage-2 columns of one key chunk).  The forward
 // is recomputed step by step into per-step state (c, entropy, both
 // normalisers, the step's queries q~ and the column sums beta of L); then
@@ -1040,11 +1067,13 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   }
   constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
   constexpr bool SPLITC = !std::is_same<T, float>::value && PRECISE;
+  constexpr bool ONLY64 = SPLITC && D == 128;              // blocks and columns of <= 64 keys
   const dim3 g2(grid1((size_t)pl.S * pl.b2)), g1(grid1((size_t)pl.S * pl.b1));
   const size_t rows = (size_t)pl.S * pl.G;
   BwdParams p = bwd_params<T, D>(pl, b);
-  hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_COLUMN, SPLITC>), g2, dim3(NTH2), 0, st, p);
-  hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_LAST>), g1, dim3(NTH), 0, st, p);
+  const bool k2 = pl.b1 <= 64;                            // 64-key stage-2 build
+  MA_BWD2(S2_COLUMN, SPLITC, k2, g2);
+  MA_BWD1(S1_LAST, g1);
   for (int t = pl.T - 2; t >= 0; --t) {
     const Plan sp = step_plan(pl, t);
     char* ws = b.ws;
@@ -1057,9 +1086,9 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
                        reinterpret_cast<const float*>(ws + sp.off_beta),
                        reinterpret_cast<const float*>(ws + step_plan(pl, t + 1).off_qtil),
                        reinterpret_cast<float*>(ws + pl.off_dbt), rows);
-    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ALPHA, SPLITC>), g2, dim3(NTH2), 0, st, p);
-    if (t > 0) hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_MID>), g1, dim3(NTH), 0, st, p);
-    else hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_FIRST>), g1, dim3(NTH), 0, st, p);
+    MA_BWD2(S2_ALPHA, SPLITC, k2, g2);
+    if (t > 0) MA_BWD1(S1_MID, g1);
+    else MA_BWD1(S1_FIRST, g1);
   }
   if (pl.group > 1) bwd_kv_out<T, D>(pl, p, b, st);
   return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
@@ -1082,11 +1111,12 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   const BwdParams p = bwd_params<T, D>(pl, b);
   constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
   constexpr int NB = BwdShape<T, D>::NB, RB = BwdShape<T, D>::RB, RG = BwdShape<T, D>::RG;
+  constexpr bool ONLY64 = false;
   // stage-2 columns: (slice, row tile t, column i), rt queries over b1 * c2 keys
   const size_t cols = (size_t)pl.S * pl.c1 * pl.b2;
   const int nkeys = pl.b1 * pl.c2;
   if (nkeys <= NB) {
-    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_COLUMN>), dim3(grid1(cols)), dim3(NTH2), 0, st, p);
+    MA_BWD2(S2_COLUMN, false, nkeys <= 64, dim3(grid1(cols)));
   } else {                                 // D first, then one workgroup per key chunk
     const size_t n = (size_t)pl.S * pl.N * D;
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2, n);
@@ -1096,12 +1126,11 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
                        dim3(NTH2), 0, st, p);
   }
   if (pl.c1 > 1 || pl.c2 > 1) {            // per (block, segment), then the query gradients
-    hipLaunchKernelGGL((stage1_bwd_kernel<T, D, S1_TILED>), dim3(grid1((size_t)pl.S * pl.b1 * pl.c2)),
-                       dim3(NTH), 0, st, p);
+    MA_BWD1(S1_TILED, dim3(grid1((size_t)pl.S * pl.b1 * pl.c2)));
     hipLaunchKernelGGL((tiled_dq_kernel<T, D>), dim3(grid1(cols)), dim3(512), 0, st, p.dqt, p.dq2,
                        static_cast<T*>(b.dq), pl.map, (int)pl.N, pl.b1, pl.b2, pl.c1, pl.c2);
   } else {
-    hipLaunchKernelGGL((stage1_bwd_kernel<T, D>), dim3(grid1((size_t)pl.S * pl.b1)), dim3(NTH), 0, st, p);
+    MA_BWD1(S1_ONLY, dim3(grid1((size_t)pl.S * pl.b1)));
   }
   if (pl.padded)
     hipLaunchKernelGGL((qbar_grad_kernel<T>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(128), 0, st, p.dqbar,
@@ -1109,5 +1138,8 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   if (pl.group > 1) bwd_kv_out<T, D>(pl, p, b, st);
   return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
 }
+
+#undef MA_BWD1
+#undef MA_BWD2
 
 }  // namespace ma

@@ -136,5 +136,6 @@ ma_status run_bwd_bf16_128(const Plan&, const BwdBufs&, hipStream_t);
 ma_status run_bwd_f32_64(const Plan&, const BwdBufs&, hipStream_t);
 ma_status run_bwd_f32_128(const Plan&, const BwdBufs&, hipStream_t);
 ma_status run_bwd_steps_bf16_64(const Plan&, const BwdBufs&, hipStream_t);   // T > 1, split c
+ma_status run_bwd_steps_bf16_128(const Plan&, const BwdBufs&, hipStream_t);
 
 }  // namespace ma

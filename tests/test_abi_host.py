@@ -146,7 +146,8 @@ def test_status_strings(lib):
     (dict(steps=3, dtype="f32", head_dim=128, seq_len=64 * 64, b1=64, b2=64), 0),
     (dict(steps=2, seq_len=250), 2),          # T > 1 padded
     (dict(steps=2, seq_len=200 * 8, b1=200, b2=8), 2),   # T > 1: columns over one key chunk
-    (dict(steps=2, head_dim=128), 2),         # T > 1 bf16 at head_dim 128 (split c over LDS)
+    (dict(steps=2, head_dim=128), 0),         # T > 1 bf16 at head_dim 128: 64-key blocks
+    (dict(steps=2, head_dim=128, seq_len=96 * 16, b1=96, b2=16), 2),   # ... columns over 64 keys
     (dict(steps=2, kv_heads=1), 0),           # T > 1 grouped K/V
     (dict(c1=2), 0),                          # row tiles
     (dict(c1=2, c2=4), 0),                    # row tiles and key segments

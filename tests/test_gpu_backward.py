@@ -173,19 +173,21 @@ def test_padded_long_columns(pad):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype,d,steps", [("f32", 64, 2), ("f32", 64, 3), ("f32", 128, 2),
-                                           ("bf16", 64, 2), ("bf16", 64, 3)])
+                                           ("bf16", 64, 2), ("bf16", 64, 3), ("bf16", 128, 2),
+                                           ("bf16", 128, 3)])
 def test_unrolled_steps_ragged(dtype, d, steps):
-    """Ragged blocks (neither b1 nor b2 a multiple of 32)."""
-    b1, b2 = (52, 40) if (dtype == "f32" and d == 128) else (70, 52)
+    """Ragged blocks (neither b1 nor b2 a multiple of 32); head_dim 128 within
+    its 64-key limit."""
+    b1, b2 = (52, 40) if d == 128 else (70, 52)
     check_backward(case(f"bwd T={steps} {dtype} d{d}", dtype, d, b1, b2, data="iid", steps=steps))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_unrolled_steps_full_blocks(dtype):
-    """128 x 128 (fp32 head_dim 128: 64 x 64), T = 2."""
+    """128 x 128 at head_dim 64, 64 x 64 (the 64-key builds) at both."""
     check_backward(case(f"bwd T=2 128x128 {dtype}", dtype, 64, 128, 128, heads=2, steps=2))
-    if dtype == "f32":
-        check_backward(case("bwd T=2 64x64 f32 d128", dtype, 128, 64, 64, heads=1, steps=2, seed=63))
+    check_backward(case(f"bwd T=2 64x64 {dtype} d128", dtype, 128, 64, 64, heads=1, steps=2, seed=63))
+    check_backward(case(f"bwd T=2 64x64 {dtype} d64", dtype, 64, 64, 64, heads=2, steps=2, seed=64))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
