@@ -195,7 +195,7 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * and key segments c1, c2 (whose other-tile queries route their gradient
  * through the tile means), not both; steps > 1 (the gradient through every
  * unrolled step, each step's L feeding the next step's queries) with
- * c1 = c2 = 1, b1 within the same limit, no padding, and for bf16 at
+ * c1 = c2 = 1 (padding allowed), b1 within the same limit, and for bf16 at
  * head_dim 128 b1, b2 <= 64.  Other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
  * the c path the forward defaults to (plain for steps = 1, split for
  * steps > 1), so these are its gradients.  A column whose next-step weights

@@ -195,7 +195,7 @@ def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat"
     """Gradients (dq, dk, dv) of <dy, forward(q, k, v, ...)> on the current
     stream.  Covers what monarch_attn_backward documents (blocks of at most
     128 keys; k, v may have fewer heads; T = 1 with pad as in forward or with
-    tiles c1, c2; T > 1 untiled and unpadded with b1 within the same limit,
+    tiles c1, c2; T > 1 untiled (pad allowed) with b1 within the same limit,
     bf16 at head_dim 128 with b1, b2 <= 64).
     out: optional (dq, dk, dv) tensors to write."""
     import torch

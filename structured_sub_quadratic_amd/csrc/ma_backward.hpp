@@ -137,6 +137,24 @@ struct RowsF32 {
       if (task < RB * CH && j < n) v[a] = *reinterpret_cast<const f32x4*>(src(j) + c * 4);
     }
   }
+  // rows of the input type (st(j) not null) or fp32 rows (sf(j))
+  template <class SrcT, class SrcF> __device__ inline void load_mixed(int n, SrcT st, SrcF sf) {
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
+      v[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (task >= RB * CH || j >= n) continue;
+      const T* t = st(j);
+      if (!t) {
+        v[a] = *reinterpret_cast<const f32x4*>(sf(j) + c * 4);
+      } else if constexpr (std::is_same<T, float>::value) {
+        v[a] = *reinterpret_cast<const f32x4*>(t + c * 4);
+      } else {
+        const bf16x4 h = *reinterpret_cast<const bf16x4*>(t + c * 4);
+        v[a] = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      }
+    }
+  }
   template <int LDT> __device__ inline void store_tplanes(T* hi, size_t plane) const {
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
@@ -411,8 +429,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   // P = exp2(sc2 q.c + h2 - lse2) and dP = dY u^T (S2_ALPHA: q dalpha^T +
   // dbeta) of a row chunk against the current key chunk, in strips of one row
   // tile x NG key tiles; STORE keeps them in LDS, and the row sums of P dP go
-  // to dsum[row] (if not null)
-  auto scores = [&](int nr, bool store, float* dsum, const T* qs, const T* dys, const float* lsel) {
+  // to dsum[row] (if not null); l0s is the chunk's first row in the tile
+  auto scores = [&](int l0s, int nr, bool store, float* dsum, const T* qs, const T* dys, const float* lsel) {
     const int ng = (nbp / 16 + NG - 1) / NG;
     for (int st = wave; st < (RB / 16) * ng; st += NW) {
       const int m0 = (st / ng) * 16, n0 = (st % ng) * 16 * NG;
@@ -442,7 +460,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
-          const bool ok = row < nr && key < nb;
+          // padding rows carry no L row (no upstream gradient, no next-query weight)
+          const bool ok = row < nr && key < nb && (!padded || col.valid(r0 + l0s + row));
           const float pv = ok ? __builtin_amdgcn_exp2f(s[t][e] * p.sc2 + h2k[key] - lsel[row]) : 0.f;
           const float dv = ok ? dp[t][e] + (AL ? dbk[key] : 0.f) : 0.f;
           if (store) {
@@ -482,7 +501,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
       for (int c = 0; c < RG; ++c) {
         const int l0 = g0 + c * RB;
         if (l0 >= rt) break;
-        scores(min(RB, rt - l0), false, dlb + c * RB, qsb + c * RB * LDI, dysb + c * RB * LDI, lsb + c * RB);
+        scores(l0, min(RB, rt - l0), false, dlb + c * RB, qsb + c * RB * LDI, dysb + c * RB * LDI, lsb + c * RB);
       }
     }
     __syncthreads();
@@ -511,7 +530,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
     }
     if (l0 + RB < rt) fetch(l0 + RB);       // in flight while this chunk computes
     __syncthreads();
-    scores(nr, true, MODE == S2_KEYS ? nullptr : dl, qs, dys, lsel);
+    scores(l0, nr, true, MODE == S2_KEYS ? nullptr : dl, qs, dys, lsel);
     __syncthreads();
     // dW = P (dP - D)
     for (int idx = threadIdx.x; idx < RB * nbp; idx += NTH) {
@@ -607,8 +626,11 @@ static __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, size_t n
 // (slice, block k, segment s) with the segment's keys and the c1 * b2
 // queries (t, i) -- q(k, i) for k's own row tile, the tile mean of (t, i)
 // otherwise; each query's gradient goes to its exchange row (dq~).
+// S1_FIRSTP: S1_FIRST of a padded sequence, whose padding positions took the
+// fp32 tile means as queries (held as fp32 planes like q~; their gradient
+// goes to dqbar).
 // ---------------------------------------------------------------------------
-enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3, S1_TILED = 4 };
+enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3, S1_TILED = 4, S1_FIRSTP = 5 };
 
 template <typename T, int D, int SM = S1_ONLY, int NBK = 0>
 __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(BwdParams p) {
@@ -620,11 +642,14 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
   constexpr int DQ = SH::DQ;                                 // d tiles per dQ strip
   constexpr int SK = SH::SK;                                 // key-tile strips of dK, dV per wave
   constexpr bool SPLIT = !std::is_same<T, float>::value;
-  constexpr bool QF = SM == S1_LAST || SM == S1_MID;         // queries q~ (fp32 planes)
+  constexpr bool FP = SM == S1_FIRSTP;
+  constexpr bool FIRST = SM == S1_FIRST || FP;               // step 0 of several
+  constexpr bool QF = SM == S1_LAST || SM == S1_MID || FP;   // queries as fp32 planes
   constexpr bool TL = SM == S1_TILED;
+  constexpr bool XQ = SM == S1_LAST || SM == S1_MID || TL;   // query gradients to exchange rows
   constexpr bool WV = SM == S1_ONLY || SM == S1_LAST || TL;  // u = R V path
   constexpr bool QP = QF && SPLIT;                           // queries carry a lo plane
-  constexpr bool DQO = SM == S1_ONLY || SM == S1_FIRST;      // dQ finished here
+  constexpr bool DQO = SM == S1_ONLY || FIRST;               // dQ finished here
   constexpr size_t TPL = (size_t)D * LDR;                    // plane offset of the transposed grads
   constexpr size_t QPL = (size_t)RB * LDI;                   // plane offset of the query rows
   __shared__ __attribute__((aligned(16))) T ks[NB * LDI];
@@ -672,7 +697,10 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
   const int jlo = p.map.key_lo(k), jhi = p.map.key_hi(k);   // real keys of block k
   auto fetch = [&](int i0) {
     const int n = min(RB, nq - i0);
-    if constexpr (QF) {
+    if constexpr (FP) {
+      pqf.load_mixed(n, [&](int r) -> const T* { return row.valid(i0 + r) ? Q + row.at(i0 + r) * D : nullptr; },
+                     [&](int r) { return static_cast<const float*>(p.qbt) + ((size_t)sl * p.b2 + i0 + r) * D; });
+    } else if constexpr (QF) {
       pqf.load(n, [&](int r) { return p.qtil + (xb + i0 + r) * D; });
     } else if constexpr (TL) {
       pq.load(n, [&](int r) {
@@ -793,7 +821,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = m0 + 4 * g + e;
           if (r >= nr) continue;
-          if constexpr (QF || TL) {                 // gradient of this query row (q~, or own / tile mean)
+          if constexpr (XQ) {                       // gradient of this query row (q~, or own / tile mean)
             p.dqt[(xb + i0 + r) * D + d] = a[t][e];
             continue;
           }
@@ -827,7 +855,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
   T* dV = static_cast<T*>(p.dv) + (size_t)sl * p.N * D;
   // several steps: the fp32 sum of dK over the later steps, all loads issued
   // before the first store
-  constexpr bool ADD = SM == S1_MID || SM == S1_FIRST;
+  constexpr bool ADD = SM == S1_MID || FIRST;
   float old[ADD ? SK : 1][ADD ? DT : 1][4];
   if constexpr (ADD) {
 #pragma unroll
@@ -851,13 +879,13 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
         const int key = m0 + 4 * g + e;
         if (key >= nb || (padded && (key < jlo || key >= jhi))) continue;
         const int64_t tok = row.at(j0 + key);
-        if constexpr (SM == S1_LAST || SM == S1_MID || SM == S1_FIRST) {   // several steps
+        if constexpr (SM == S1_LAST || SM == S1_MID || FIRST) {   // several steps
           const size_t at = ((size_t)sl * p.N + tok) * D + d;
           if constexpr (SM == S1_LAST) {
             p.dkp[at] = adk[s][t][e];
             if (p.group > 1) p.dvp[at] = adv[s][t][e];
             else dV[tok * D + d] = from_f32<T>(adv[s][t][e]);
-          } else if (SM == S1_FIRST && p.group == 1) {
+          } else if (FIRST && p.group == 1) {
             dK[tok * D + d] = from_f32<T>(old[s][t][e] + adk[s][t][e]);
           } else {
             p.dkp[at] = old[s][t][e] + adk[s][t][e];
@@ -1039,7 +1067,7 @@ void bwd_kv_out(const Plan& pl, const BwdParams& p, const BwdBufs& b, hipStream_
     else hipLaunchKernelGGL((stage1_bwd_kernel<T, D, SM>), grid, dim3(NTH), 0, st, p);             \
   } while (0)
 
-// T > 1 (untiled, unpadded, stage-2 columns of one key chunk).  The forward
+// T > 1 (untiled, stage-2 columns of one key chunk).  The forward
 // is recomputed step by step into per-step state (c, entropy, both
 // normalisers, the step's queries q~ and the column sums beta of L); then
 // the steps are differentiated in reverse.  The last step as for T = 1 but
@@ -1088,8 +1116,12 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
                        reinterpret_cast<float*>(ws + pl.off_dbt), rows);
     MA_BWD2(S2_ALPHA, SPLITC, k2, g2);
     if (t > 0) MA_BWD1(S1_MID, g1);
+    else if (pl.padded) MA_BWD1(S1_FIRSTP, g1);
     else MA_BWD1(S1_FIRST, g1);
   }
+  if (pl.padded)
+    hipLaunchKernelGGL((qbar_grad_kernel<T>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(128), 0, st, p.dqbar,
+                       static_cast<T*>(b.dq), pl.map, (int)pl.N, D);
   if (pl.group > 1) bwd_kv_out<T, D>(pl, p, b, st);
   return hipGetLastError() == hipSuccess ? MA_OK : MA_ERR_DEVICE;
 }

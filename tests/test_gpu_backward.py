@@ -244,3 +244,32 @@ def test_video_tiled_backward_sampled():
     """The tiled video latent (630 x 52, c1 = c2 = 2, d = 128, 12 heads): two
     slices compared whole."""
     check_backward(WORKLOADS["video_tiled"], slices=[(0, 0), (0, 5)])
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unrolled_steps_padded_vit(pad, dtype):
+    """197 tokens as 15 blocks of 14 at T = 2 (the ViT case): padding rows
+    hold no L row at either step, padding keys no R mass, and a padding
+    position's first query is the tile mean of its column."""
+    cfg = WorkloadConfig("case", f"bwd T=2 vit pad={pad} {dtype}", batch=2, heads=3, seq_len=197,
+                         head_dim=64, b1=15, b2=14, steps=2, dtype=dtype, data="iid", seed=57,
+                         pad=pad)
+    check_backward(cfg)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 128), ("bf16", 64)])
+def test_unrolled_steps_padded(dtype, d):
+    """Ragged padded grids at T = 3: 52 x 40 less 20 positions in front."""
+    cfg = WorkloadConfig("case", f"bwd T=3 pad {dtype} d{d}", batch=1, heads=2, seq_len=52 * 40 - 20,
+                         head_dim=d, b1=52, b2=40, steps=3, dtype=dtype, data="normed", seed=58,
+                         pad="pre")
+    check_backward(cfg)
+
+
+def test_n16k_pad_t2_backward_sampled():
+    """The padded headline shape (16284 tokens, 100 padding positions in
+    front) at T = 2: two slices compared whole."""
+    cfg = WorkloadConfig("case", "bwd T=2 n16k pad", batch=1, heads=12, seq_len=16284, head_dim=64,
+                         b1=128, b2=128, steps=2, dtype="bf16", data="normed", seed=1006, pad="pre")
+    check_backward(cfg, slices=[(0, 0), (0, 11)])
