@@ -173,22 +173,25 @@ struct RowsF32 {
       }
     }
   }
-  // rows as planes of the element type: hi[j][.] (and lo for bf16)
+  // rows as planes of the element type: hi[j][.] (and lo for bf16); rows of
+  // LD elements, 8-byte aligned
   template <int LD> __device__ inline void store_planes(T* hi, size_t plane) const {
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
       const int task = threadIdx.x + a * NTH, j = task / CH, c = task % CH;
       if (task >= RB * CH) continue;
+      T* at = hi + (size_t)j * LD + c * 4;
+      if constexpr (std::is_same<T, float>::value) {
+        *reinterpret_cast<f32x4*>(at) = v[a];
+      } else {
+        bf16x4 h, l;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        T* at = hi + (size_t)j * LD + c * 4 + e;
-        if constexpr (std::is_same<T, float>::value) {
-          *at = v[a][e];
-        } else {
-          const bf16 h = (bf16)v[a][e];
-          at[0] = h;
-          at[plane] = (bf16)(v[a][e] - (float)h);
+        for (int e = 0; e < 4; ++e) {
+          h[e] = (bf16)v[a][e];
+          l[e] = (bf16)(v[a][e] - (float)h[e]);
         }
+        *reinterpret_cast<bf16x4*>(at) = h;
+        *reinterpret_cast<bf16x4*>(at + plane) = l;
       }
     }
   }
@@ -659,6 +662,12 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
   __shared__ __attribute__((aligned(16))) T qt[(QP ? 2 : 1) * D * LDR];    // q^T of the chunk
   __shared__ __attribute__((aligned(16))) T dut[WV ? (SPLIT ? 2 : 1) * D * LDR : 1]; // du^T (hi, lo)
   __shared__ __attribute__((aligned(16))) T dct[(SPLIT ? 2 : 1) * D * LDR]; // dc^T (hi, lo)
+  // bf16 at head_dim 64: du and dc also row major (hi, lo), so that dR reads
+  // its A operand as 16-byte rows instead of gathering the transposed copy
+  constexpr bool RC = SPLIT && D == 64;
+  constexpr size_t RPL = (size_t)RB * LDI;
+  __shared__ __attribute__((aligned(16))) T dur[RC && WV ? 2 * RB * LDI : 1];
+  __shared__ __attribute__((aligned(16))) T dcr[RC ? 2 * RB * LDI : 1];
   __shared__ __attribute__((aligned(16))) float rs[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dzs[RB * LDP];
   __shared__ float lser[RB], dhr[RB], gr[RB], hr[RB];
@@ -734,6 +743,10 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
     }
     if constexpr (WV) pdu.template store_tplanes<LDR>(dut, TPL);
     pdc.template store_tplanes<LDR>(dct, TPL);
+    if constexpr (RC) {
+      if constexpr (WV) pdu.template store_planes<LDI>(dur, RPL);
+      pdc.template store_planes<LDI>(dcr, RPL);
+    }
     if constexpr (SH::PREFETCH && DQO) pdq.template store_rows<D + 4>(dq2s);
     if (threadIdx.x < RB) {
       lser[threadIdx.x] = pls;
@@ -756,14 +769,24 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
       for (int t = 0; t < NG; ++t) z[t] = dr[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (nt == NG) {
         strip_mma<T, NG, QP ? PL : IN, ROW, IN, ROW>(z, qs, LDI, QPL, ks, LDI, 0, m0, n0, D);
-        if constexpr (WV) strip_mma<T, NG, PL, COL, IN, ROW>(dr, dut, LDR, TPL, vs, LDI, 0, m0, n0, D);
-        strip_mma<T, NG, PL, COL, IN, ROW>(dr, dct, LDR, TPL, ks, LDI, 0, m0, n0, D);
+        if constexpr (RC) {
+          if constexpr (WV) strip_mma<T, NG, PL, ROW, IN, ROW>(dr, dur, LDI, RPL, vs, LDI, 0, m0, n0, D);
+          strip_mma<T, NG, PL, ROW, IN, ROW>(dr, dcr, LDI, RPL, ks, LDI, 0, m0, n0, D);
+        } else {
+          if constexpr (WV) strip_mma<T, NG, PL, COL, IN, ROW>(dr, dut, LDR, TPL, vs, LDI, 0, m0, n0, D);
+          strip_mma<T, NG, PL, COL, IN, ROW>(dr, dct, LDR, TPL, ks, LDI, 0, m0, n0, D);
+        }
       } else {
         for (int t = 0; t < nt; ++t) {
           f32x4 a1[1] = {z[t]}, a2[1] = {dr[t]};
           strip_mma<T, 1, QP ? PL : IN, ROW, IN, ROW>(a1, qs, LDI, QPL, ks, LDI, 0, m0, n0 + 16 * t, D);
-          if constexpr (WV) strip_mma<T, 1, PL, COL, IN, ROW>(a2, dut, LDR, TPL, vs, LDI, 0, m0, n0 + 16 * t, D);
-          strip_mma<T, 1, PL, COL, IN, ROW>(a2, dct, LDR, TPL, ks, LDI, 0, m0, n0 + 16 * t, D);
+          if constexpr (RC) {
+            if constexpr (WV) strip_mma<T, 1, PL, ROW, IN, ROW>(a2, dur, LDI, RPL, vs, LDI, 0, m0, n0 + 16 * t, D);
+            strip_mma<T, 1, PL, ROW, IN, ROW>(a2, dcr, LDI, RPL, ks, LDI, 0, m0, n0 + 16 * t, D);
+          } else {
+            if constexpr (WV) strip_mma<T, 1, PL, COL, IN, ROW>(a2, dut, LDR, TPL, vs, LDI, 0, m0, n0 + 16 * t, D);
+            strip_mma<T, 1, PL, COL, IN, ROW>(a2, dct, LDR, TPL, ks, LDI, 0, m0, n0 + 16 * t, D);
+          }
           z[t] = a1[0];
           dr[t] = a2[0];
         }
