@@ -117,7 +117,7 @@ def sampled_parity(cfg, Q, K, V, y):
     return float(np.abs(a - r).max() / np.abs(r).max())
 
 
-def backward_flops(cfg):
+def backward_flops(cfg, rebuilt=True):
     """Products of the backward as computed (per slice, untiled).  Last step:
     stage 2 forms P, dP, dQ, dc, du over b1 x b1 per column (5), stage 1
     forms R, dR (two products), dQ, dK (two products), dV over b2 x b2 per
@@ -127,10 +127,13 @@ def backward_flops(cfg):
     the stage-2 normalisers (1 over b1), u once (1 over b2), and the next
     queries of every step but the last (2 over b1).  With row tiles and key
     segments a stage-2 query meets b1 * c2 keys and a key c1 * b2 stage-1
-    queries, which take the places of b1 and b2."""
+    queries, which take the places of b1 and b2.  rebuilt=False: the forward
+    state was kept, so the rebuilt forward's products are not counted."""
     N, d, T = cfg.seq_len, cfg.head_dim, cfg.steps
     b1, b2 = cfg.b1 * cfg.c2, cfg.c1 * cfg.b2
-    per = (5 * b1 + 7 * b2) + (T - 1) * (5 * b1 + 5 * b2) + T * (2 * b2 + b1) + b2 + (T - 1) * 2 * b1
+    per = (5 * b1 + 7 * b2) + (T - 1) * (5 * b1 + 5 * b2)
+    if rebuilt:
+        per += T * (2 * b2 + b1) + b2 + (T - 1) * 2 * b1
     return 2 * N * d * per * cfg.slices
 
 
@@ -154,12 +157,19 @@ def bench_backward(args, cfg, dev):
     del base
     prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2,
                            cfg.steps, cfg.c1, cfg.c2, None, cfg.dtype, cfg.layout, cfg.fhw, 0)
-    ws = torch.empty(max(ma.backward_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
+    nws = n_sets if args.reuse_state else 1
+    wss = [torch.empty(max(ma.backward_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
+           for _ in range(nws)]
+    if args.reuse_state:      # each set's forward state stays in its own workspace
+        for (q, k, v, *_), w in zip(sets, wss):
+            ma.forward(q, k, v, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
+                       fhw=cfg.fhw, workspace=w)
 
     def call(i):
         q, k, v, dy, dq, dk, dv = sets[i % n_sets]
         ma.backward(q, k, v, dy, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
-                    fhw=cfg.fhw, workspace=ws, out=(dq, dk, dv))
+                    fhw=cfg.fhw, workspace=wss[i % nws], out=(dq, dk, dv),
+                    reuse_forward_state=args.reuse_state)
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
@@ -170,13 +180,15 @@ def bench_backward(args, cfg, dev):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    flops = backward_flops(cfg)
+    flops = backward_flops(cfg, rebuilt=not args.reuse_state)
     out = {
         "metric": "MonarchAttention bwd ms/call + effective TFLOP/s", "value":
             round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "pass": "backward (dQ, dK, dV), forward state rebuilt",
+        "config": {"workload": cfg.name,
+                   "pass": "backward (dQ, dK, dV), forward state " +
+                           ("kept from the forward call" if args.reuse_state else "rebuilt"),
                    "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)"},
         "flops_counted": flops,
         "mfma_frac_of_call": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.dtype], 4),
@@ -199,6 +211,9 @@ def main():
                     help="split bf16 hi+lo c = R K path (the default for T > 1)")
     ap.add_argument("--fused", action="store_true",
                     help="T = 1 as one cooperative launch instead of separate stage launches")
+    ap.add_argument("--reuse-state", action="store_true",
+                    help="with --backward (T = 1): each input set's forward call leaves its state in "
+                         "the workspace and the timed backward calls reuse it")
     ap.add_argument("--backward", action="store_true",
                     help="time monarch_attn_backward (dQ, dK, dV for a seeded dY) instead of "
                          "the forward")

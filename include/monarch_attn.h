@@ -112,6 +112,15 @@ typedef enum {
  * mean as its first-step query).  Requires P < b2 / c2, so that every key
  * segment holds a real key. */
 #define MA_FLAG_PAD_FRONT 16u
+/* Backward only, steps = 1: the workspace already holds the forward state of
+ * these inputs (c, u, entropies and both normalisers), left there by a
+ * monarch_attn_forward call of the same problem and inputs that was given
+ * this workspace (at least monarch_attn_backward_workspace_size bytes); the
+ * backward then skips rebuilding it, as a training step that keeps its
+ * forward's state would.  The flag does not change the forward.  Returns
+ * MA_ERR_UNSUPPORTED where the forward's state layout is not the backward's
+ * (steps > 1, or a bf16 aggregate path other than the plain one). */
+#define MA_FLAG_REUSE_FORWARD_STATE 32u
 
 typedef struct {
   int64_t batch, heads, seq_len, head_dim;  /* Q, Y: [batch, heads, seq_len, head_dim];
@@ -196,7 +205,9 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * through the tile means), not both; steps > 1 (the gradient through every
  * unrolled step, each step's L feeding the next step's queries) with
  * c1 = c2 = 1 (padding allowed), b1 within the same limit, and for bf16 at
- * head_dim 128 b1, b2 <= 64.  Other problems return MA_ERR_UNSUPPORTED.  For bf16 the recomputed forward takes
+ * head_dim 128 b1, b2 <= 64.  Other problems return MA_ERR_UNSUPPORTED.
+ * With MA_FLAG_REUSE_FORWARD_STATE the forward state is read from the
+ * workspace instead of rebuilt.  For bf16 the recomputed forward takes
  * the c path the forward defaults to (plain for steps = 1, split for
  * steps > 1), so these are its gradients.  A column whose next-step weights
  * all underflow to zero (the forward then takes the tile mean as the next

@@ -16,7 +16,8 @@ import ctypes
 
 from . import _lib
 from ._lib import (MonarchAttnError, LAYOUTS, MA_FLAG_FORCE_STAGED, MA_FLAG_FAST_AGGREGATE,
-                   MA_FLAG_FORCE_FUSED, MA_FLAG_PRECISE_AGGREGATE, MA_FLAG_PAD_FRONT)
+                   MA_FLAG_FORCE_FUSED, MA_FLAG_PRECISE_AGGREGATE, MA_FLAG_PAD_FRONT,
+                   MA_FLAG_REUSE_FORWARD_STATE)
 
 __all__ = ["forward", "forward_timed", "backward", "make_problem", "workspace_size",
            "backward_workspace_size", "num_launches", "launch_names", "Event",
@@ -191,13 +192,16 @@ def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layo
 
 
 def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
-             workspace=None, out=None, pad="post"):
+             workspace=None, out=None, pad="post", reuse_forward_state=False):
     """Gradients (dq, dk, dv) of <dy, forward(q, k, v, ...)> on the current
     stream.  Covers what monarch_attn_backward documents (blocks of at most
     128 keys; k, v may have fewer heads; T = 1 with pad as in forward or with
     tiles c1, c2; T > 1 untiled (pad allowed) with b1 within the same limit,
     bf16 at head_dim 128 with b1, b2 <= 64).
-    out: optional (dq, dk, dv) tensors to write."""
+    out: optional (dq, dk, dv) tensors to write.
+    reuse_forward_state (T = 1): `workspace` holds the state a forward call
+    of the same inputs left there (that call was given this workspace, of at
+    least backward_workspace_size bytes); the backward does not rebuild it."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("dy", dy)):
         if not t.is_cuda:
@@ -211,9 +215,13 @@ def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat"
         raise ValueError("dy must be shaped like q, and k, v [batch, kv_heads, seq_len, head_dim]")
     if pad not in ("pre", "post"):
         raise ValueError("pad must be 'pre' or 'post'")
-    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw,
-                        MA_FLAG_PAD_FRONT if pad == "pre" else 0, kv_heads=Hkv)
+    flags = (MA_FLAG_PAD_FRONT if pad == "pre" else 0) | \
+        (MA_FLAG_REUSE_FORWARD_STATE if reuse_forward_state else 0)
+    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags,
+                        kv_heads=Hkv)
     ws_bytes = backward_workspace_size(prob)
+    if reuse_forward_state and workspace is None:
+        raise ValueError("reuse_forward_state needs the workspace the forward call used")
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k),

@@ -17,6 +17,7 @@ MA_FLAG_FAST_AGGREGATE = 2
 MA_FLAG_FORCE_FUSED = 4
 MA_FLAG_PRECISE_AGGREGATE = 8
 MA_FLAG_PAD_FRONT = 16
+MA_FLAG_REUSE_FORWARD_STATE = 32
 
 
 class MAProblem(ctypes.Structure):

@@ -1151,7 +1151,8 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
 
 // The whole backward call on stream st: the forward's stage 1 (last-step
 // kind: c, u, entropy, normaliser) and stage 2 statistics (row normalisers,
-// no output) refill the workspace, then the two backward kernels run.
+// no output) refill the workspace (unless a forward call left them there),
+// then the two backward kernels run.
 template <typename T, int D, bool PRECISE>
 ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   if constexpr (std::is_same<T, float>::value) {
@@ -1160,9 +1161,11 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
     return MA_ERR_UNSUPPORTED;      // bf16 T > 1 runs the split-c entry
   }
   Bufs fb{b.q, b.k, b.v, nullptr, b.ws, nullptr, nullptr, nullptr, nullptr};
-  if (pl.need_qbar && launch_one<T, D, PRECISE>(pl, fb, L_QBAR, 0, st) != hipSuccess) return MA_ERR_DEVICE;
-  if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE1_LAST, 0, st) != hipSuccess) return MA_ERR_DEVICE;
-  if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE2_STATS, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+  if (!pl.reuse_state) {
+    if (pl.need_qbar && launch_one<T, D, PRECISE>(pl, fb, L_QBAR, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+    if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE1_LAST, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+    if (launch_one<T, D, PRECISE>(pl, fb, L_STAGE2_STATS, 0, st) != hipSuccess) return MA_ERR_DEVICE;
+  }
   const BwdParams p = bwd_params<T, D>(pl, b);
   constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
   constexpr int NB = BwdShape<T, D>::NB, RB = BwdShape<T, D>::RB, RG = BwdShape<T, D>::RG;

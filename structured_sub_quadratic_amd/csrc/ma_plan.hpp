@@ -41,6 +41,7 @@ struct Plan {
   size_t off_steps, step_bytes, so_cx, so_h2, so_lser, so_lse2, so_qtil, so_beta;
   size_t off_beta, off_dqt, off_dbt;
   bool beta_out;       // the alpha launch also stores beta at off_beta
+  bool reuse_state;    // backward: the forward state is in the workspace already
   bool need_qbar, need_qtil;
   bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1

@@ -95,6 +95,7 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
   size_t off = 0;
   pl.xlo = (pl.precise && p->dtype == MA_BF16) ? rows * pl.D : 0;
   pl.beta_out = false;
+  pl.reuse_state = backward && (p->flags & MA_FLAG_REUSE_FORWARD_STATE);
   pl.off_steps = pl.step_bytes = pl.so_cx = pl.so_h2 = pl.so_lser = pl.so_lse2 = pl.so_qtil = 0;
   pl.so_beta = pl.off_beta = pl.off_dqt = pl.off_dbt = 0;
   if (steps_state) {
@@ -212,6 +213,14 @@ ma_status backward_impl(const ma_problem* p, const void* q, const void* k, const
   ma_status s = validate_backward(p);
   if (s != MA_OK) return s;
   const Plan pl = make_plan(p, true);
+  if (pl.reuse_state) {     // the forward's state regions must be the backward's
+    const Plan f = make_plan(p);
+    if (pl.T != 1 || f.precise != pl.precise || f.off_cx != pl.off_cx || f.off_ux != pl.off_ux ||
+        f.off_h2 != pl.off_h2 || f.off_lser != pl.off_lser || f.off_lse2 != pl.off_lse2 ||
+        f.need_qbar != pl.need_qbar || f.off_qbar != pl.off_qbar ||
+        f.need_qbar_lp != pl.need_qbar_lp || f.off_qbar_lp != pl.off_qbar_lp || f.xlo != pl.xlo)
+      return MA_ERR_UNSUPPORTED;
+  }
   const void* in[] = {q, k, v, dy};
   void* out[] = {dq, dk, dv};
   auto misaligned = [](const void* x, uintptr_t a) { return ((uintptr_t)x % a) != 0; };

@@ -175,3 +175,19 @@ def test_backward_validation(lib, kw, code):
                                          None) == 3
         assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, dy, dq, dq, dv, 1 << 40,
                                          n.value, None) == 1      # dK overlaps dQ
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 1),                                   # layouts agree: the pointer checks run (null -> 1)
+    (dict(dtype="f32"), 1),
+    (dict(c1=2, c2=2), 1),
+    (dict(seq_len=250), 1),
+    (dict(steps=2), 2),                            # per-step state: nothing to reuse
+    (dict(flags=8), 2),                            # bf16 split aggregate: not the backward's c path
+])
+def test_backward_reuse_forward_state_layouts(lib, kw, code):
+    """MA_FLAG_REUSE_FORWARD_STATE is accepted only where the forward's state
+    regions are the backward's; the check runs before any HIP call."""
+    flags = kw.pop("flags", 0) | ma.MA_FLAG_REUSE_FORWARD_STATE
+    p = good(flags=flags, **kw)
+    assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == code

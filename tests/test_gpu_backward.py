@@ -273,3 +273,36 @@ def test_n16k_pad_t2_backward_sampled():
     cfg = WorkloadConfig("case", "bwd T=2 n16k pad", batch=1, heads=12, seq_len=16284, head_dim=64,
                          b1=128, b2=128, steps=2, dtype="bf16", data="normed", seed=1006, pad="pre")
     check_backward(cfg, slices=[(0, 0), (0, 11)])
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("bf16", dict(dtype="bf16", d=64, b1=70, b2=52)),
+    ("f32 d128", dict(dtype="f32", d=128, b1=52, b2=40)),
+    ("tiled", dict(dtype="bf16", d=64, b1=48, b2=52, c1=3, c2=2)),
+])
+def test_reuse_forward_state(name, kw):
+    """A forward call given the backward's workspace leaves its state there;
+    the backward with reuse_forward_state skips rebuilding it and gives the
+    gradients of the rebuilding call (fp32 to 1e-6; bf16 outputs may differ
+    by one bf16 step (2^-8 of the largest), since the forward's output launch and the rebuild's
+    statistics launch reach the same normalisers by different code)."""
+    import torch
+    import structured_sub_quadratic_amd as ma
+    cfg = case(f"bwd reuse {name}", kw["dtype"], kw["d"], kw["b1"], kw["b2"], data="normed",
+               c1=kw.get("c1", 1), c2=kw.get("c2", 1))
+    Q, K, V = make_inputs(cfg)
+    dY = upstream(cfg)
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdy = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt) for x in (Q, K, V, dY))
+    prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2, 1,
+                           cfg.c1, cfg.c2, None, cfg.dtype)
+    ws = torch.empty(ma.backward_workspace_size(prob), dtype=torch.uint8, device=dev)
+    args = (cfg.b1, cfg.b2, 1, cfg.c1, cfg.c2)
+    ref = ma.backward(tq, tk, tv, tdy, *args)
+    ma.forward(tq, tk, tv, *args, workspace=ws)
+    got = ma.backward(tq, tk, tv, tdy, *args, workspace=ws, reuse_forward_state=True)
+    torch.cuda.synchronize()
+    for g, r in zip(got, ref):
+        g, r = g.float().cpu().numpy(), r.float().cpu().numpy()
+        assert np.abs(g - r).max() <= (1e-6 if cfg.dtype == "f32" else 2.0 ** -7) * np.abs(r).max(), name
