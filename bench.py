@@ -160,16 +160,17 @@ def bench_backward(args, cfg, dev):
     nws = n_sets if args.reuse_state else 1
     wss = [torch.empty(max(ma.backward_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
            for _ in range(nws)]
-    if args.reuse_state:      # each set's forward state stays in its own workspace
-        for (q, k, v, *_), w in zip(sets, wss):
-            ma.forward(q, k, v, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
-                       fhw=cfg.fhw, workspace=w)
+    ys = [None] * n_sets
+    if args.reuse_state:      # each set's forward state stays in its own workspace, with its Y
+        for j, ((q, k, v, *_), w) in enumerate(zip(sets, wss)):
+            ys[j] = ma.forward(q, k, v, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
+                               fhw=cfg.fhw, workspace=w)
 
     def call(i):
         q, k, v, dy, dq, dk, dv = sets[i % n_sets]
         ma.backward(q, k, v, dy, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
                     fhw=cfg.fhw, workspace=wss[i % nws], out=(dq, dk, dv),
-                    reuse_forward_state=args.reuse_state)
+                    reuse_forward_state=args.reuse_state, y=ys[i % n_sets])
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
@@ -188,7 +189,8 @@ def bench_backward(args, cfg, dev):
         "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name,
                    "pass": "backward (dQ, dK, dV), forward state " +
-                           ("kept from the forward call" if args.reuse_state else "rebuilt"),
+                           ("and output Y kept from the forward call" if args.reuse_state
+                            else "rebuilt"),
                    "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)"},
         "flops_counted": flops,
         "mfma_frac_of_call": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.dtype], 4),
@@ -213,7 +215,7 @@ def main():
                     help="T = 1 as one cooperative launch instead of separate stage launches")
     ap.add_argument("--reuse-state", action="store_true",
                     help="with --backward (T = 1): each input set's forward call leaves its state in "
-                         "the workspace and the timed backward calls reuse it")
+                         "the workspace and its output Y, and the timed backward calls reuse both")
     ap.add_argument("--backward", action="store_true",
                     help="time monarch_attn_backward (dQ, dK, dV for a seeded dY) instead of "
                          "the forward")

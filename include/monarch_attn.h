@@ -212,14 +212,20 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * steps > 1), so these are its gradients.  A column whose next-step weights
  * all underflow to zero (the forward then takes the tile mean as the next
  * query) passes no gradient back through that query.
+ * y: null, or the forward's output Y for these inputs (shaped like Q).  The
+ * softmax gradient of every stage-2 row needs D = sum over keys of P dP,
+ * which equals dY . y; a column of more than one key chunk then takes D from
+ * y instead of a separate pass over all its keys (as FlashAttention-2 does).
+ * With y the result is that of the given output; for bf16 it may differ from
+ * the call without y by the rounding of y.
  * workspace: at least monarch_attn_backward_workspace_size bytes, 256-byte
  * aligned, overlapping no other argument; dQ, dK, dV must not overlap each
- * other or the inputs; every tensor 16-byte aligned.  The outputs are
- * written, not accumulated. */
+ * other or the inputs (y included); every tensor 16-byte aligned.  The
+ * outputs are written, not accumulated. */
 ma_status monarch_attn_backward_workspace_size(const ma_problem* p, size_t* bytes);
 ma_status monarch_attn_backward(const ma_problem* p, const void* q, const void* k,
-                                const void* v, const void* dy, void* dq, void* dk, void* dv,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                const void* v, const void* y, const void* dy, void* dq, void* dk,
+                                void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Diagnostic helpers around hipEvent_t (thin wrappers of the HIP runtime).
  * monarch_attn_event_elapsed_ms synchronises on event b. */

@@ -192,7 +192,7 @@ def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layo
 
 
 def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
-             workspace=None, out=None, pad="post", reuse_forward_state=False):
+             workspace=None, out=None, pad="post", reuse_forward_state=False, y=None):
     """Gradients (dq, dk, dv) of <dy, forward(q, k, v, ...)> on the current
     stream.  Covers what monarch_attn_backward documents (blocks of at most
     128 keys; k, v may have fewer heads; T = 1 with pad as in forward or with
@@ -201,7 +201,10 @@ def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat"
     out: optional (dq, dk, dv) tensors to write.
     reuse_forward_state (T = 1): `workspace` holds the state a forward call
     of the same inputs left there (that call was given this workspace, of at
-    least backward_workspace_size bytes); the backward does not rebuild it."""
+    least backward_workspace_size bytes); the backward does not rebuild it.
+    y: optional forward output for these inputs; long stage-2 columns then
+    take their softmax-gradient row sums from dy . y instead of a pass over
+    their keys."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("dy", dy)):
         if not t.is_cuda:
@@ -215,6 +218,9 @@ def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat"
         raise ValueError("dy must be shaped like q, and k, v [batch, kv_heads, seq_len, head_dim]")
     if pad not in ("pre", "post"):
         raise ValueError("pad must be 'pre' or 'post'")
+    if y is not None and (not y.is_cuda or y.shape != q.shape or y.dtype != q.dtype
+                          or not y.is_contiguous()):
+        raise ValueError("y must be a contiguous device tensor shaped and typed like q")
     flags = (MA_FLAG_PAD_FRONT if pad == "pre" else 0) | \
         (MA_FLAG_REUSE_FORWARD_STATE if reuse_forward_state else 0)
     prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags,
@@ -228,7 +234,8 @@ def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat"
                                               torch.empty_like(v))
     st = torch.cuda.current_stream(q.device).cuda_stream
     status = _lib.load().monarch_attn_backward(
-        ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(),
+        ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        y.data_ptr() if y is not None else None, dy.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), st)
     _lib.check(status, "monarch_attn_backward")
     return dq, dk, dv

@@ -74,7 +74,7 @@ def load():
     lib.monarch_attn_forward_timed.restype = ctypes.c_int
     lib.monarch_attn_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.monarch_attn_backward_workspace_size.restype = ctypes.c_int
-    lib.monarch_attn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.monarch_attn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.monarch_attn_backward.restype = ctypes.c_int
     lib.monarch_attn_num_launches.argtypes = [P]
     lib.monarch_attn_num_launches.restype = ctypes.c_int32

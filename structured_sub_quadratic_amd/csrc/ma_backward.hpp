@@ -945,6 +945,28 @@ __global__ __launch_bounds__(128) void qbar_grad_kernel(const float* dqbar, T* d
   }
 }
 
+// D = rowsum(P dP) of every stage-2 row from the forward's output: P dP
+// summed over the keys is dY . y (y = P u).  One 16-lane group per (slice,
+// column, row) of dlx; padding rows get 0.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dy_dot_y_kernel(const T* dy, const T* y, float* dlx, GridMap map,
+                                                       int N, size_t rows) {
+  constexpr int PER = D / 16;
+  const size_t r = ((size_t)blockIdx.x * 256 + threadIdx.x) / 16;
+  const int lane = threadIdx.x % 16;
+  if (r >= rows) return;                      // whole groups of 16 lanes leave together
+  const int l = r % map.b1, i = (r / map.b1) % map.b2;
+  const size_t sl = r / map.b1 / map.b2;
+  float acc = 0.f;
+  if (map.valid(l, i)) {
+    const size_t o = ((size_t)sl * N + map.token(l, i)) * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc += to_f32(dy[o + e]) * to_f32(y[o + e]);
+  }
+  acc = sum16(acc);
+  if (lane == 0) dlx[r] = acc;
+}
+
 // Row tiles / key segments (T = 1): the query gradient of exchange row
 // (k, s, t, i) belongs to q(k, i) when t is k's own row tile and to the tile
 // mean qbar(t, i) otherwise; qbar(t, i) is the mean of the rt rows of tile t,
@@ -1178,8 +1200,15 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   } else {                                 // D first, then one workgroup per key chunk
     const size_t n = (size_t)pl.S * pl.N * D;
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2, n);
-    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM>),
-                       dim3(grid1(cols * ((pl.rt + RG * RB - 1) / (RG * RB)))), dim3(NTH2), 0, st, p);
+    if (b.y) {                             // D = dY . y
+      const size_t rows = (size_t)pl.S * pl.G;
+      hipLaunchKernelGGL((dy_dot_y_kernel<T, D>), dim3(grid1((rows * 16 + 255) / 256)), dim3(256), 0, st,
+                         static_cast<const T*>(b.dy), static_cast<const T*>(b.y), p.dlx, pl.map, (int)pl.N,
+                         rows);
+    } else {
+      hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM>),
+                         dim3(grid1(cols * ((pl.rt + RG * RB - 1) / (RG * RB)))), dim3(NTH2), 0, st, p);
+    }
     hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS>), dim3(grid1(cols * ((nkeys + NB - 1) / NB))),
                        dim3(NTH2), 0, st, p);
   }

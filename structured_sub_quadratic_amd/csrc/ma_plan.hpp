@@ -113,6 +113,7 @@ struct BwdBufs {
   const void *q, *k, *v, *dy;
   void *dq, *dk, *dv;
   char* ws;
+  const void* y;       // the forward's output, or null
 };
 
 // Largest blocks of the backward: the keys of a stage-1 block sit in LDS

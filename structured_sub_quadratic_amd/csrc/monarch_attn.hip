@@ -208,7 +208,7 @@ ma_status validate_backward(const ma_problem* p) {
 }
 
 ma_status backward_impl(const ma_problem* p, const void* q, const void* k, const void* v,
-                        const void* dy, void* dq, void* dk, void* dv, void* workspace,
+                        const void* y, const void* dy, void* dq, void* dk, void* dv, void* workspace,
                         size_t workspace_bytes, void* stream) {
   ma_status s = validate_backward(p);
   if (s != MA_OK) return s;
@@ -228,12 +228,14 @@ ma_status backward_impl(const ma_problem* p, const void* q, const void* k, const
     if (!x || misaligned(x, 16)) return MA_ERR_INVALID_ARGUMENT;
   for (void* x : out)
     if (!x || misaligned(x, 16)) return MA_ERR_INVALID_ARGUMENT;
+  if (y && misaligned(y, 16)) return MA_ERR_INVALID_ARGUMENT;
   const size_t tbytes = (size_t)pl.S * pl.N * pl.D * pl.elt;     // q, dy, dq
   const size_t kvbytes = tbytes / pl.group;                       // k, v, dk, dv
   const size_t isz[] = {tbytes, kvbytes, kvbytes, tbytes}, osz[] = {tbytes, kvbytes, kvbytes};
   for (int a = 0; a < 3; ++a) {
     for (int c = 0; c < 4; ++c)
       if (overlaps(out[a], osz[a], in[c], isz[c])) return MA_ERR_INVALID_ARGUMENT;
+    if (y && overlaps(out[a], osz[a], y, tbytes)) return MA_ERR_INVALID_ARGUMENT;
     for (int c = a + 1; c < 3; ++c)
       if (overlaps(out[a], osz[a], out[c], osz[c])) return MA_ERR_INVALID_ARGUMENT;
   }
@@ -243,7 +245,8 @@ ma_status backward_impl(const ma_problem* p, const void* q, const void* k, const
     if (overlaps(workspace, pl.total, in[c], isz[c])) return MA_ERR_INVALID_ARGUMENT;
   for (int a = 0; a < 3; ++a)
     if (overlaps(workspace, pl.total, out[a], osz[a])) return MA_ERR_INVALID_ARGUMENT;
-  BwdBufs b{q, k, v, dy, dq, dk, dv, static_cast<char*>(workspace)};
+  if (y && overlaps(workspace, pl.total, y, tbytes)) return MA_ERR_INVALID_ARGUMENT;
+  BwdBufs b{q, k, v, dy, dq, dk, dv, static_cast<char*>(workspace), y};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (pl.dtype == MA_BF16)
     return pl.T > 1 ? (pl.D == 64 ? run_bwd_steps_bf16_64(pl, b, st) : run_bwd_steps_bf16_128(pl, b, st))
@@ -264,9 +267,9 @@ ma_status monarch_attn_backward_workspace_size(const ma_problem* p, size_t* byte
 }
 
 ma_status monarch_attn_backward(const ma_problem* p, const void* q, const void* k, const void* v,
-                                const void* dy, void* dq, void* dk, void* dv, void* workspace,
-                                size_t workspace_bytes, void* stream) {
-  return backward_impl(p, q, k, v, dy, dq, dk, dv, workspace, workspace_bytes, stream);
+                                const void* y, const void* dy, void* dq, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(p, q, k, v, y, dy, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 ma_status monarch_attn_workspace_size(const ma_problem* p, size_t* bytes) {

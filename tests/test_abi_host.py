@@ -169,12 +169,18 @@ def test_backward_validation(lib, kw, code):
     if code == 0:
         assert n.value >= ma.workspace_size(p)
         # null pointers and a short workspace are rejected before any HIP call
-        assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == 1
-        q, k, v, dy, dq, dk, dv = (256 * 1024 * 1024 * (j + 1) for j in range(7))
-        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, dy, dq, dk, dv, 1 << 40, 10,
+        assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == 1
+        q, k, v, dy, dq, dk, dv, y = (256 * 1024 * 1024 * (j + 1) for j in range(8))
+        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, None, dy, dq, dk, dv, 1 << 40, 10,
                                          None) == 3
-        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, dy, dq, dq, dv, 1 << 40,
+        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, y, dy, dq, dk, dv, 1 << 40, 10,
+                                         None) == 3
+        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, None, dy, dq, dq, dv, 1 << 40,
                                          n.value, None) == 1      # dK overlaps dQ
+        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, dq, dy, dq, dk, dv, 1 << 40,
+                                         n.value, None) == 1      # y overlaps dQ
+        assert lib.monarch_attn_backward(ctypes.byref(p), q, k, v, y + 4, dy, dq, dk, dv, 1 << 40,
+                                         n.value, None) == 1      # y misaligned
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -190,4 +196,4 @@ def test_backward_reuse_forward_state_layouts(lib, kw, code):
     regions are the backward's; the check runs before any HIP call."""
     flags = kw.pop("flags", 0) | ma.MA_FLAG_REUSE_FORWARD_STATE
     p = good(flags=flags, **kw)
-    assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == code
+    assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == code

@@ -25,14 +25,18 @@ def _gpu():
     ma._lib.load()          # raise loudly if the library is missing
 
 
-def run_backward(cfg, Q, K, V, dY):
+def run_backward(cfg, Q, K, V, dY, with_y=False):
     import torch
     import structured_sub_quadratic_amd as ma
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     dev = torch.device("cuda:0")
     tq, tk, tv, tdy = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt) for x in (Q, K, V, dY))
+    y = None
+    if with_y:        # the forward's output: row sums of the softmax gradient from dY . y
+        y = ma.forward(tq, tk, tv, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
+                       fhw=cfg.fhw, pad=cfg.pad)
     dq, dk, dv = ma.backward(tq, tk, tv, tdy, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                             layout=cfg.layout, fhw=cfg.fhw, pad=cfg.pad)
+                             layout=cfg.layout, fhw=cfg.fhw, pad=cfg.pad, y=y)
     torch.cuda.synchronize()
     return tuple(x.float().cpu().numpy() for x in (dq, dk, dv))
 
@@ -43,12 +47,12 @@ def upstream(cfg, seed=77):
     return round_to_bf16(dY) if cfg.dtype == "bf16" else dY
 
 
-def check_backward(cfg, slices=None, tol=None, kv_heads=None):
+def check_backward(cfg, slices=None, tol=None, kv_heads=None, with_y=False):
     Q, K, V = make_inputs(cfg)
     if kv_heads is not None:        # grouped-query attention: keep the first kv_heads
         K, V = (np.ascontiguousarray(X[:, :kv_heads]) for X in (K, V))
     dY = upstream(cfg)
-    got = run_backward(cfg, Q, K, V, dY)
+    got = run_backward(cfg, Q, K, V, dY, with_y)
     all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     slices = all_slices if slices is None else slices
     ref = obw.backward(Q, K, V, dY, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
@@ -306,3 +310,24 @@ def test_reuse_forward_state(name, kw):
     for g, r in zip(got, ref):
         g, r = g.float().cpu().numpy(), r.float().cpu().numpy()
         assert np.abs(g - r).max() <= (1e-6 if cfg.dtype == "f32" else 2.0 ** -7) * np.abs(r).max(), name
+
+
+@pytest.mark.parametrize("dtype,d,b1", [("bf16", 64, 300), ("f32", 128, 130), ("bf16", 128, 150)])
+def test_long_columns_with_output(dtype, d, b1):
+    """Columns over one key chunk given the forward's output: the row sums
+    D come from dY . y instead of the D pass."""
+    b2 = 40 if (dtype == "f32" and d == 128) else 52
+    check_backward(case(f"bwd y b1={b1} {dtype} d{d}", dtype, d, b1, b2, heads=1), with_y=True)
+
+
+@pytest.mark.parametrize("variant", ["pad", "tiled", "video"])
+def test_long_columns_with_output_variants(variant):
+    if variant == "pad":
+        cfg = WorkloadConfig("case", "bwd y b1=200 pad=pre", batch=1, heads=2, seq_len=200 * 40 - 30,
+                             head_dim=128, b1=200, b2=40, steps=1, dtype="bf16", data="normed",
+                             seed=59, pad="pre")
+        check_backward(cfg, with_y=True)
+    elif variant == "tiled":
+        check_backward(case("bwd y tiled b1=100", "bf16", 64, 100, 24, heads=1, c1=2, c2=2), with_y=True)
+    else:
+        check_backward(WORKLOADS["video"], slices=[(0, 0), (0, 7)], with_y=True)
