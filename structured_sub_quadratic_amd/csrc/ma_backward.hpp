@@ -92,6 +92,17 @@ template <typename T, int D, int NBK = 0> struct BwdShape {
   static constexpr int RG = (F32 && D == 128) ? 2 : 4;     // row chunks of a D-only workgroup
 };
 
+// Transposed bf16 tiles X^T[d][j] hold element (d, j) at column j ^ tsw(d):
+// the 16-byte column chunks of row d are permuted by the row's 16-row group,
+// so that the 16 lanes that write one column j with consecutive d (the
+// transposing stores) fall in distinct LDS banks.  Readers of a whole chunk
+// apply the same permutation to its start.
+__device__ inline int tsw(int d) { return ((d >> 4) & 3) << 3; }
+template <typename T> __device__ inline int tcol(int d, int j) {
+  if constexpr (std::is_same<T, float>::value) return j;
+  else return j ^ tsw(d);
+}
+
 // Register staging of up to RB rows of a matrix: the loads of the next row
 // chunk are issued before the current chunk computes and land in LDS at the
 // start of the next one.  Input-type rows (store: row major, optionally also
@@ -120,7 +131,7 @@ struct RowsIn {
       *reinterpret_cast<V*>(dst + (size_t)j * LD + c * VN) = v[a];
       if constexpr (TR) {
 #pragma unroll
-        for (int e = 0; e < VN; ++e) dt[(size_t)(c * VN + e) * LDT + j] = v[a][e];
+        for (int e = 0; e < VN; ++e) dt[(size_t)(c * VN + e) * LDT + tcol<T>(c * VN + e, j)] = v[a][e];
       }
     }
   }
@@ -162,7 +173,7 @@ struct RowsF32 {
       if (task >= RB * CH) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        T* at = hi + (size_t)(c * 4 + e) * LDT + j;
+        T* at = hi + (size_t)(c * 4 + e) * LDT + tcol<T>(c * 4 + e, j);
         if constexpr (std::is_same<T, float>::value) {
           *at = v[a][e];
         } else {
@@ -208,16 +219,18 @@ struct RowsF32 {
 // reads X[k][idx].  Operand kinds: IN, an exact matrix of the element type;
 // F32, an fp32 matrix split into hi + lo on the fly (bf16 only); PL, two
 // planes hi, lo of the element type (lo `plane` elements after hi; for fp32
-// only hi is read).
+// only hi is read); INS, PLS: IN, PL of a transposed tile stored with the
+// tcol permutation (bf16; for fp32 the same as IN, PL).
 enum { ROW = 0, COL = 1 };
-enum { IN = 0, F32 = 1, PL = 2 };
+enum { IN = 0, F32 = 1, PL = 2, INS = 3, PLS = 4 };
+constexpr bool has_lo(int kind) { return kind == F32 || kind == PL || kind == PLS; }
 
-template <int KIND>
+template <int KIND, bool SW = false>
 __device__ inline bf16x8 frag_in(const bf16* X, int ld, int idx, int k) {
-  if constexpr (KIND == ROW) return *reinterpret_cast<const bf16x8*>(X + (size_t)idx * ld + k);
+  if constexpr (KIND == ROW) return *reinterpret_cast<const bf16x8*>(X + (size_t)idx * ld + (SW ? k ^ tsw(idx) : k));
   bf16x8 f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = X[(size_t)(k + e) * ld + idx];
+  for (int e = 0; e < 8; ++e) f[e] = X[(size_t)(k + e) * ld + (SW ? idx ^ tsw(k + e) : idx)];
   return f;
 }
 template <int KIND>
@@ -247,8 +260,9 @@ __device__ inline void frag(const void* X, int ld, size_t plane, int idx, int k,
   if constexpr (OK == F32) {
     frag_f32<L>(static_cast<const float*>(X), ld, idx, k, hi, lo);
   } else {
-    hi = frag_in<L>(static_cast<const bf16*>(X), ld, idx, k);
-    if constexpr (OK == PL) lo = frag_in<L>(static_cast<const bf16*>(X) + plane, ld, idx, k);
+    constexpr bool SW = OK == INS || OK == PLS;
+    hi = frag_in<L, SW>(static_cast<const bf16*>(X), ld, idx, k);
+    if constexpr (OK == PL || OK == PLS) lo = frag_in<L, SW>(static_cast<const bf16*>(X) + plane, ld, idx, k);
   }
 }
 
@@ -284,8 +298,8 @@ __device__ inline void strip_mma(f32x4 (&acc)[NT], const void* A, int lda, size_
         bf16x8 bh, bl;
         frag<BK, BL>(B, ldb, bplane, n0 + 16 * t + r, k, bh, bl);
         acc[t] = Mfma<bf16>::mma(ah, bh, acc[t]);
-        if constexpr (AK != IN) acc[t] = Mfma<bf16>::mma(al, bh, acc[t]);
-        if constexpr (BK != IN) acc[t] = Mfma<bf16>::mma(ah, bl, acc[t]);
+        if constexpr (has_lo(AK)) acc[t] = Mfma<bf16>::mma(al, bh, acc[t]);
+        if constexpr (has_lo(BK)) acc[t] = Mfma<bf16>::mma(ah, bl, acc[t]);
       }
     }
   }
@@ -311,7 +325,7 @@ __device__ inline void bwd_load_rows(T* dst, T* dt, int NR, int n, Src src) {
     *reinterpret_cast<V*>(dst + (size_t)j * LD + c * VN) = v;
     if constexpr (TR) {
 #pragma unroll
-      for (int e = 0; e < VN; ++e) dt[(size_t)(c * VN + e) * LDT + j] = v[e];
+      for (int e = 0; e < VN; ++e) dt[(size_t)(c * VN + e) * LDT + tcol<T>(c * VN + e, j)] = v[e];
     }
   }
 }
@@ -341,6 +355,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   constexpr int SK = SH::SK2;                                // key-tile strips of dc, du per wave
   constexpr bool AL = MODE == S2_ALPHA;
   constexpr int CK = SPLITC ? PL : IN;                       // operand kind of c
+  constexpr int CKT = SPLITC ? PLS : INS;                    // and of its transposed copy
   constexpr size_t CPL = (size_t)NB * LDI, CTPL = (size_t)D * LDN;   // lo planes of c, c^T
   constexpr bool SPLIT = !std::is_same<T, float>::value;
   constexpr int DAK = SPLIT ? PL : IN;                       // dalpha: hi, lo planes for bf16
@@ -548,7 +563,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
       f32x4 a[DQ], a2[DQ];
 #pragma unroll
       for (int t = 0; t < DQ; ++t) a[t] = a2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, CK, ROW>(a, dws, LDP, 0, ct, LDN, CTPL, m0, 16 * DQ * h, nbp);
+      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, CKT, ROW>(a, dws, LDP, 0, ct, LDN, CTPL, m0, 16 * DQ * h, nbp);
       else strip_mma<T, DQ, F32, ROW, CK, COL>(a, dws, LDP, 0, cs, LDI, CPL, m0, 16 * DQ * h, nbp);
       // the direct term of the next queries: P dalpha
       if constexpr (AL) strip_mma<T, DQ, F32, ROW, DAK, COL>(a2, ps, LDP, 0, das, LDI, DPL, m0, 16 * DQ * h, nbp);
@@ -585,8 +600,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
       for (int h = 0; h < DT / DS; ++h) {
         f32x4 (&c)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adc[s][DS * h]);
         f32x4 (&u)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adu[s][DS * h]);
-        strip_mma<T, DS, F32, COL, IN, ROW>(c, dws, LDP, 0, qt, LDR, 0, m0, 16 * DS * h, RB);
-        if constexpr (!AL) strip_mma<T, DS, F32, COL, IN, ROW>(u, ps, LDP, 0, dyt, LDR, 0, m0, 16 * DS * h, RB);
+        strip_mma<T, DS, F32, COL, INS, ROW>(c, dws, LDP, 0, qt, LDR, 0, m0, 16 * DS * h, RB);
+        if constexpr (!AL) strip_mma<T, DS, F32, COL, INS, ROW>(u, ps, LDP, 0, dyt, LDR, 0, m0, 16 * DS * h, RB);
       }
     }
   }
@@ -773,8 +788,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
           if constexpr (WV) strip_mma<T, NG, PL, ROW, IN, ROW>(dr, dur, LDI, RPL, vs, LDI, 0, m0, n0, D);
           strip_mma<T, NG, PL, ROW, IN, ROW>(dr, dcr, LDI, RPL, ks, LDI, 0, m0, n0, D);
         } else {
-          if constexpr (WV) strip_mma<T, NG, PL, COL, IN, ROW>(dr, dut, LDR, TPL, vs, LDI, 0, m0, n0, D);
-          strip_mma<T, NG, PL, COL, IN, ROW>(dr, dct, LDR, TPL, ks, LDI, 0, m0, n0, D);
+          if constexpr (WV) strip_mma<T, NG, PLS, COL, IN, ROW>(dr, dut, LDR, TPL, vs, LDI, 0, m0, n0, D);
+          strip_mma<T, NG, PLS, COL, IN, ROW>(dr, dct, LDR, TPL, ks, LDI, 0, m0, n0, D);
         }
       } else {
         for (int t = 0; t < nt; ++t) {
@@ -784,8 +799,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
             if constexpr (WV) strip_mma<T, 1, PL, ROW, IN, ROW>(a2, dur, LDI, RPL, vs, LDI, 0, m0, n0 + 16 * t, D);
             strip_mma<T, 1, PL, ROW, IN, ROW>(a2, dcr, LDI, RPL, ks, LDI, 0, m0, n0 + 16 * t, D);
           } else {
-            if constexpr (WV) strip_mma<T, 1, PL, COL, IN, ROW>(a2, dut, LDR, TPL, vs, LDI, 0, m0, n0 + 16 * t, D);
-            strip_mma<T, 1, PL, COL, IN, ROW>(a2, dct, LDR, TPL, ks, LDI, 0, m0, n0 + 16 * t, D);
+            if constexpr (WV) strip_mma<T, 1, PLS, COL, IN, ROW>(a2, dut, LDR, TPL, vs, LDI, 0, m0, n0 + 16 * t, D);
+            strip_mma<T, 1, PLS, COL, IN, ROW>(a2, dct, LDR, TPL, ks, LDI, 0, m0, n0 + 16 * t, D);
           }
           z[t] = a1[0];
           dr[t] = a2[0];
@@ -835,7 +850,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
       f32x4 a[DQ];
 #pragma unroll
       for (int t = 0; t < DQ; ++t) a[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, IN, ROW>(a, dzs, LDP, 0, kt, LDN, 0, m0, 16 * DQ * h, nbp);
+      if constexpr (SH::KT_COPY) strip_mma<T, DQ, F32, ROW, INS, ROW>(a, dzs, LDP, 0, kt, LDN, 0, m0, 16 * DQ * h, nbp);
       else strip_mma<T, DQ, F32, ROW, IN, COL>(a, dzs, LDP, 0, ks, LDI, 0, m0, 16 * DQ * h, nbp);
 #pragma unroll
       for (int t = 0; t < DQ; ++t) {
@@ -868,9 +883,9 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
       for (int h = 0; h < DT / DS; ++h) {
         f32x4 (&a)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adk[s][DS * h]);
         f32x4 (&v)[DS] = *reinterpret_cast<f32x4(*)[DS]>(&adv[s][DS * h]);
-        strip_mma<T, DS, F32, COL, QP ? PL : IN, ROW>(a, dzs, LDP, 0, qt, LDR, TPL, m0, 16 * DS * h, RB);
-        strip_mma<T, DS, F32, COL, PL, ROW>(a, rs, LDP, 0, dct, LDR, TPL, m0, 16 * DS * h, RB);
-        if constexpr (WV) strip_mma<T, DS, F32, COL, PL, ROW>(v, rs, LDP, 0, dut, LDR, TPL, m0, 16 * DS * h, RB);
+        strip_mma<T, DS, F32, COL, QP ? PLS : INS, ROW>(a, dzs, LDP, 0, qt, LDR, TPL, m0, 16 * DS * h, RB);
+        strip_mma<T, DS, F32, COL, PLS, ROW>(a, rs, LDP, 0, dct, LDR, TPL, m0, 16 * DS * h, RB);
+        if constexpr (WV) strip_mma<T, DS, F32, COL, PLS, ROW>(v, rs, LDP, 0, dut, LDR, TPL, m0, 16 * DS * h, RB);
       }
     }
   }
