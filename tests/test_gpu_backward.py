@@ -331,3 +331,29 @@ def test_long_columns_with_output_variants(variant):
         check_backward(case("bwd y tiled b1=100", "bf16", 64, 100, 24, heads=1, c1=2, c2=2), with_y=True)
     else:
         check_backward(WORKLOADS["video"], slices=[(0, 0), (0, 7)], with_y=True)
+
+
+VIDEO_LAYOUTS = {"fh_w": (15, 8), "w_fh": (8, 15), "f_hw": (3, 40), "hw_f": (40, 3),
+                 "fw_h": (24, 5), "h_fw": (5, 24)}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", sorted(VIDEO_LAYOUTS))
+def test_video_layouts(layout, dtype):
+    """Every aligned video layout of a 3 x 5 x 8 latent (rows and columns of
+    the grid gather strided tokens)."""
+    b1, b2 = VIDEO_LAYOUTS[layout]
+    check_backward(case(f"bwd {layout} {dtype}", dtype, 64, b1, b2, data="video", layout=layout,
+                        fhw=(3, 5, 8)))
+
+
+@pytest.mark.parametrize("variant", ["steps", "tiled"])
+def test_video_layout_variants(variant):
+    """A video layout at T = 2, and with row tiles and key segments."""
+    if variant == "steps":
+        cfg = case("bwd fh_w T=2", "bf16", 64, 15, 8, data="video", layout="fh_w", fhw=(3, 5, 8),
+                   steps=2)
+    else:
+        cfg = case("bwd fh_w tiled", "bf16", 128, 15, 8, data="video", layout="fh_w", fhw=(3, 5, 8),
+                   c1=3, c2=2)
+    check_backward(cfg)
