@@ -314,6 +314,23 @@ struct Stage1Async {
     if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
     flush(cur);                   // the previous item's last segment
     const char* vt = WITH_U ? cur + SM::TILE : cur;
+    if constexpr (KTB == 2 * KT && !PAD) {
+      if (p.c2 == 1 && p.b2 == KTB) {
+        // two full key tiles: both score products are issued before the
+        // first softmax, so the second tile's MFMAs overlap the first
+        // tile's exp and sums (the online-softmax updates keep their order)
+        constexpr int OFF1 = KT * SwzTile<D>::RB;
+        core.init();
+        core.template scores_v<0>(SwzKeys<D>(cur, nullptr), 0, KT / 16);
+        core.template scores_v<1>(SwzKeys<D>(cur + OFF1, nullptr), 0, KT / 16);
+        core.template softmax_step<false, false, 0>(nullptr, p.sc2, 0, KT);
+        core.template pv<false, 0>(SwzValuesT<D>(cur, vt), 0, KT);
+        core.template softmax_step<false, false, 1>(nullptr, p.sc2, 0, KT);
+        core.template pv<false, 1>(SwzValuesT<D>(cur + OFF1, vt + OFF1), 0, KT);
+        collect(qg, k, sl, 0);
+        return;
+      }
+    }
     for (int s = 0; s < p.c2; ++s) {
       int klo = s * p.sw, khi = klo + p.sw;
       if constexpr (PAD) {     // real keys of block k

@@ -51,6 +51,11 @@ struct FlashCore {
   bool qsplit = false;
   f32x4 o[NQ][DT];        // O^T accumulators: lane holds O[q][16dt + 4g + r]
   f32x4 s[NQ][MT];        // score / probability tile
+  f32x4 s2[NQ][MT];       // a second one (two tiles in flight; unused registers otherwise)
+  template <int B> __device__ inline f32x4 (&buf())[NQ][MT] {
+    if constexpr (B == 0) return s;
+    else return s2;
+  }
   float m[NQ], l[NQ], e[NQ], sref[NQ];
   bool fresh;             // no key seen since init()
 
@@ -134,8 +139,9 @@ struct FlashCore {
   // Raw scores S^T for the key sub-tiles [mt0, mt1) of a key tile; kv.a(mt,
   // ks) is this lane's A fragment of key sub-tile mt at head-dim step ks
   // (kv.alo the low part when KLO).
-  template <class KV>
+  template <int B = 0, class KV>
   __device__ inline void scores_v(const KV& kv, int mt0, int mt1) {
+    f32x4 (&s)[NQ][MT] = buf<B>();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt < mt0 || mt >= mt1) continue;
@@ -210,8 +216,9 @@ struct FlashCore {
     }
   }
 
-  template <bool HAS_BIAS, bool MASK>
+  template <bool HAS_BIAS, bool MASK, int B = 0>
   __device__ inline void softmax_step(const float* bias, float sc2, int klo, int khi) {
+    f32x4 (&s)[NQ][MT] = buf<B>();
     constexpr float TAU = 8.f;
     constexpr float MASKED = -1e30f;
     const int lane = threadIdx.x % WAVE, g = lane / 16;
@@ -288,8 +295,9 @@ struct FlashCore {
   }
 
   // O^T += V^T P^T over the keys [klo, khi) of the tile (probabilities in s).
-  template <bool MASK, class VV>
+  template <bool MASK, int B = 0, class VV>
   __device__ inline void pv(const VV& vv, int klo, int khi) {
+    f32x4 (&s)[NQ][MT] = buf<B>();
     const int lane = threadIdx.x % WAVE, g = lane / 16;
     if constexpr (KPL == 8) {
       // 32 keys per MFMA: lane group g supplies keys {32kk+4g+r, 32kk+16+4g+r}
