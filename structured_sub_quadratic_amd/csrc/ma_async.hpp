@@ -314,8 +314,9 @@ struct Stage1Async {
     if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
     flush(cur);                   // the previous item's last segment
     const char* vt = WITH_U ? cur + SM::TILE : cur;
-    if constexpr (KTB == 2 * KT && !PAD) {
-      if (p.c2 == 1 && p.b2 == KTB) {
+    if constexpr (KTB == 2 * KT) {
+      // (padded: blocks whose keys are all real)
+      if (p.c2 == 1 && p.b2 == KTB && (!PAD || (p.map.key_lo(k) == 0 && p.map.key_hi(k) == KTB))) {
         // two full key tiles: both score products are issued before the
         // first softmax, so the second tile's MFMAs overlap the first
         // tile's exp and sums (the online-softmax updates keep their order)
