@@ -196,7 +196,10 @@ struct Stage1AsyncSmem {
 // PAD: a padded flat sequence (padding positions clamped on load, padding
 // keys masked, padding query positions read the tile means); the unpadded
 // build keeps the plain row addressing.
-template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false>
+// QF: a step after the first of an untiled, unpadded run; the queries are
+// the fp32 next-step queries q~ (split into hi + lo when `split`), read from
+// global memory into registers, and no query tile is copied.
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false, bool QF = false>
 struct Stage1Async {
   static constexpr int LDS_BYTES = 2 * Stage1AsyncSmem<D, NW, KTB, WITH_U>::BUF;
 
@@ -206,7 +209,7 @@ struct Stage1Async {
   constexpr int DV = WITH_U ? 2 * D : D;
   constexpr int QG = NW * 16;
   constexpr int NSPLIT = PRECISE ? D / 16 : 0;
-  typedef FlashCore<T, D, DV, 1, KT, true, true, false, NSPLIT> Core;
+  typedef FlashCore<T, D, DV, 1, KT, true, true, false, NSPLIT, QF> Core;
   typedef typename Core::frag frag;
   typedef Stage1AsyncSmem<D, NW, KTB, WITH_U> SM;
   char* const buf_a = lds;
@@ -227,6 +230,7 @@ struct Stage1Async {
       const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
       SwzTile<D>::template load<KTB, NW>(b + SM::TILE, [&](int r) { return V + tok(r) * D; }, p.b2);
     }
+    if constexpr (QF) return;     // queries come from q~ in global memory
     // slot = t*b2 + i: row (k, i) of Q in the own row tile t = k / rt, the
     // tile mean of (t, i) elsewhere (tiled first step) and at padding
     // positions (k, i)
@@ -307,10 +311,21 @@ struct Stage1Async {
     const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
     wait_vmem();
     __syncthreads();              // cur landed everywhere; nobody reads nxt any more
+    if constexpr (QF) {
+      core.load_queries([&](int) {
+        const int slot = min(qg * QG + slot0 + lane % 16, p.nqs - 1);
+        QSrc<T> r;
+        r.t = nullptr;
+        r.f = p.qtil + (((size_t)sl * p.b1 + k) * p.b2 + slot) * D;
+        r.use_f = true;
+        return r;
+      }, Q_F32, PRECISE);
+    } else {
 #pragma unroll
-    for (int ks_ = 0; ks_ < Core::NKS; ++ks_)
-      core.qf[0][ks_] = *reinterpret_cast<const frag*>(
-          cur + SM::QOFF + SwzTile<D>::offset(slot0 + lane % 16, 4 * ks_ + g));
+      for (int ks_ = 0; ks_ < Core::NKS; ++ks_)
+        core.qf[0][ks_] = *reinterpret_cast<const frag*>(
+            cur + SM::QOFF + SwzTile<D>::offset(slot0 + lane % 16, 4 * ks_ + g));
+    }
     if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
     flush(cur);                   // the previous item's last segment
     const char* vt = WITH_U ? cur + SM::TILE : cur;
@@ -377,9 +392,9 @@ struct Stage1Async {
   }
 };
 
-template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false>
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false, bool QF = false>
 __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p) {
-  typedef Stage1Async<D, NW, KTB, WITH_U, PRECISE, PAD> S;
+  typedef Stage1Async<D, NW, KTB, WITH_U, PRECISE, PAD, QF> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
 }

@@ -198,10 +198,12 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       if constexpr (!is_f32<T>()) {
         const int ktb = pl.b2 <= 64 ? 64 : 128;
         // the copied-tile kernel serves the first step when its queries are
-        // bf16 rows: rows of Q, and with tiles or padding the bf16 tile means
-        // of the plain c path; fp32 query sources stay on the register-staged
-        // kernels
-        if (pl.b2 <= 128 && step == 0 && ((pl.c1 == 1 && !pl.padded) || qbar_lp) && !MA_NO_ASYNC) {
+        // bf16 rows (rows of Q, and with tiles or padding the bf16 tile means
+        // of the plain c path), and the later steps of untiled, unpadded runs,
+        // whose fp32 queries q~ it reads into registers (QF builds); other
+        // fp32 query sources stay on the register-staged kernels
+        const bool qf = step > 0 && pl.c1 == 1 && pl.c2 == 1 && !pl.padded;
+        if (pl.b2 <= 128 && ((step == 0 && ((pl.c1 == 1 && !pl.padded) || qbar_lp)) || qf) && !MA_NO_ASYNC) {
           // head_dim 128 keeps 4 waves (two waves a SIMD would spill the
           // K|V sums)
           const int nw = D == 64 ? async_waves(nqs) : 4, qg = nw * 16;
@@ -212,7 +214,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           p.group = pl.group;
           const size_t items = (size_t)S * pl.b1 * p.nqg;
           const bool last = kind == L_STAGE1_LAST;
-#define MA_A1(NW, KTB, U) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE>, NW * WAVE, items, p, st)
+#define MA_A1Q(NW, KTB, U, Q) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE, false, Q>, NW * WAVE, items, p, st)
+#define MA_A1(NW, KTB, U) do { if (qf) MA_A1Q(NW, KTB, U, true); else MA_A1Q(NW, KTB, U, false); } while (0)
 #define MA_A1U(NW, KTB) do { if (last) MA_A1(NW, KTB, true); else MA_A1(NW, KTB, false); } while (0)
 #define MA_A1K(NW) do { if (ktb == 64) MA_A1U(NW, 64); else MA_A1U(NW, 128); } while (0)
 #define MA_A1P(NW) do { if (last) MA_A1X(NW, true); else MA_A1X(NW, false); } while (0)
@@ -223,6 +226,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           } else if constexpr (D == 64) { if (nw == 8) MA_A1K(8); else MA_A1K(4); }
           else MA_A1K(4);
 #undef MA_A1
+#undef MA_A1Q
 #undef MA_A1U
 #undef MA_A1K
 #undef MA_A1P
