@@ -1,10 +1,12 @@
-// Backward pass of MonarchAttention (T = 1, untiled) for gfx950.
+// Backward pass of MonarchAttention for gfx950.
 //
 // The forward of one slice is two block-local attentions (MonarchAttention,
 // OpenReview author response on GQA/MLA: every intermediate step is a
-// FlashAttention-like call), so its gradient is two block-local attention
-// backward passes in reverse order, each recomputing its softmax from the
-// normalisers the forward stored:
+// FlashAttention-like call), so the gradient of one step is two block-local
+// attention backward passes in reverse order, each recomputing its softmax
+// from the normalisers the forward stored (T = 1, untiled, below; row tiles
+// and key segments, and the steps before the last of T > 1, are variants
+// described at their kernels):
 //
 //   stage 2, one workgroup per column i (queries q_l = Q(l, i), keys c_k,
 //   values u_k, bias H_k):
