@@ -195,7 +195,8 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * The pages train through the method (MonarchRT "Method" part (3): one-step
  * fine-tuning) without stating a backward; this is the exact gradient of
  * the forward's steps, computed by recomputing the forward's block softmaxes
- * from its normalisers (the forward state is rebuilt inside the call).
+ * from its normalisers (the forward state is rebuilt inside the call unless
+ * MA_FLAG_REUSE_FORWARD_STATE says the workspace holds it).
  * dK, dV have K's shape [batch, kv_heads, seq_len, head_dim]; with grouped
  * K/V they sum over the query heads of each group.  A padded sequence
  * (MA_FLAG_PAD_FRONT or post-padding) routes the query gradient of a padding
@@ -214,8 +215,10 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * query) passes no gradient back through that query.
  * y: null, or the forward's output Y for these inputs (shaped like Q).  The
  * softmax gradient of every stage-2 row needs D = sum over keys of P dP,
- * which equals dY . y; a column of more than one key chunk then takes D from
- * y instead of a separate pass over all its keys (as FlashAttention-2 does).
+ * which equals dY . y; a column of more than one key chunk (more than 128
+ * keys; 64 for fp32 with head_dim 128; steps = 1 only) then takes D from y
+ * instead of a separate pass over all its keys (as FlashAttention-2 does);
+ * elsewhere y is not read.
  * With y the result is that of the given output; for bf16 it may differ from
  * the call without y by the rounding of y.
  * workspace: at least monarch_attn_backward_workspace_size bytes, 256-byte
