@@ -77,8 +77,10 @@ template <typename T, int D, int NBK = 0> struct BwdShape {
   // transposed copies of the keys (K^T, c^T) for the dQ product when LDS
   // allows (not in 64-key builds, which are there to halve the LDS)
   static constexpr bool KT_COPY = D == 64 && !F32 && NB == 128;
-  // waves per workgroup: 8 at head_dim 128 halve the per-wave accumulators
-  static constexpr int NW = D == 64 ? 8 : 4;
+  // waves per workgroup: 8 (at head_dim 128 this halves the per-wave dK, dV
+  // accumulators against 4 waves, so nothing spills and two waves share a
+  // SIMD)
+  static constexpr int NW = 8;
   static constexpr int NG = NW == 8 ? 2 : 4;                // key tiles per score strip
   static constexpr int DQ = NW == 8 ? 1 : (D / 16 < 4 ? D / 16 : 4);   // d tiles per dQ strip
   static constexpr int NTH = NW * WAVE;
