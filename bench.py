@@ -18,8 +18,11 @@ the K calls rotate over enough copies of Q, K, V, Y to exceed twice the
 256 MB Infinity Cache (cold mode: inputs come from HBM); --warm reuses one.
 
 Prints one JSON line: value = effective TFLOP/s (algorithmic flops of the
-method over the measured time), plus the dominant kernel's roofline and the
-CPU oracle timed on this host as a baseline.
+method over the measured time), plus the dominant kernel's roofline (its share
+of the method's bytes Q, K, V in and Y out over its measured time; the design's
+bytes with the stage exchange and the counted HBM traffic as separate fields),
+the CPU oracle timed on this host as a baseline, and the error of Y against
+exact softmax attention.
 """
 
 import argparse
@@ -49,9 +52,26 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def kernel_bytes(cfg, name, precise):
-    """Algorithmic HBM bytes of one launch: every operand the kernel must read
-    once and every result it must write once (per slice x slices)."""
+def method_bytes(cfg, name):
+    """HBM bytes the method itself makes a launch move, whatever the design:
+    its share of Q, K, V read and Y written (the whole call's algorithmic bytes
+    split over the launches that touch them).  Stage 1 reads Q (its first-step
+    queries) and the keys (and on the last step the values) of every block;
+    stage 2 reads Q and, on the last step, writes Y.  The exchange between the
+    stages is the design's, not the method's, and is not counted here."""
+    S, N, d = cfg.slices, cfg.seq_len, cfg.head_dim
+    e = 4 if cfg.dtype == "f32" else 2
+    t = N * d * e                 # one [N, d] tensor of one slice
+    kv = t / cfg.kv_group         # K or V, read once per K/V head
+    per = {"stage1_last": t + 2 * kv, "stage1": t + kv, "stage2_last": 2 * t,
+           "stage2_stats": t, "alpha": t, "qbar": t, "fused_t1": 2 * t + 2 * kv}.get(name)
+    return None if per is None else per * S
+
+
+def design_bytes(cfg, name, precise):
+    """HBM bytes of one launch as designed: every operand the kernel reads
+    once and every result it writes once, including the stage-1 -> stage-2
+    exchange (c, u, entropies, normalisers) and the next-step queries."""
     S, N, d = cfg.slices, cfg.seq_len, cfg.head_dim
     e = 4 if cfg.dtype == "f32" else 2
     xc = 4 if (precise or cfg.dtype == "f32") else 2
@@ -68,14 +88,66 @@ def kernel_bytes(cfg, name, precise):
     elif name == "alpha":
         b = N * d * e + rows * d * xc + rows * 4 + N * 4 + rows * d * 4
     elif name == "fused_t1":
-        # the whole T = 1 pass in one launch: Q, K, V in and Y out; the exchange
-        # (c, u, entropy, normalisers) is meant to stay in L2 / MALL
-        b = qkv + N * d * e
+        # the whole T = 1 pass in one launch: Q, K, V in and Y out, plus the
+        # exchange written and read back
+        b = qkv + N * d * e + 2 * rows * d * (xc + e) + rows * 12
     elif name == "qbar":
         b = N * d * e + cfg.c1 * cfg.b2 * d * 4
     else:
         return None
     return b * S
+
+
+def host_description():
+    """CPU model (from /proc/cpuinfo) and the BLAS library NumPy links."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy as np
+        info = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{info.get('name', '?')} {info.get('version', '')}".strip()
+    except Exception:
+        pass
+    return model, blas
+
+
+def exact_attention_error(cfg, Q, K, V, y, rows_per_head=None, seed=4242):
+    """P9, reported only: the relative Frobenius error ||Y - Y_exact|| /
+    ||Y_exact|| of the method's output against exact softmax attention
+    softmax(Q K^T / sqrt(d)) V, computed in float64 on the host in row
+    chunks.  Every row when rows_per_head is None, else that many seeded
+    query rows per head (the same rows for every head)."""
+    import numpy as np
+    B, H, N, d = Q.shape
+    group = H // K.shape[1]
+    scale = 1.0 / math.sqrt(d)
+    rows = np.arange(N) if rows_per_head is None else \
+        np.sort(np.random.default_rng(seed).choice(N, size=min(rows_per_head, N), replace=False))
+    num = den = 0.0
+    for b in range(B):
+        for h in range(H):
+            k = K[b, h // group].astype(np.float64)
+            v = V[b, h // group].astype(np.float64)
+            for c0 in range(0, rows.size, 2048):
+                r = rows[c0:c0 + 2048]
+                s_ = scale * (Q[b, h, r].astype(np.float64) @ k.T)
+                s_ -= s_.max(axis=1, keepdims=True)
+                p = np.exp(s_)
+                ex = (p @ v) / p.sum(axis=1, keepdims=True)
+                num += float(np.sum((y[b, h, r].astype(np.float64) - ex) ** 2))
+                den += float(np.sum(ex ** 2))
+    return {"value": math.sqrt(num / den), "rows": "all" if rows_per_head is None else
+            f"{rows.size} seeded query rows per head (seed {seed})",
+            "measure": "||Y - Y_exact||_F / ||Y_exact||_F, Y_exact = softmax(QK^T/sqrt(d))V in "
+                       "float64 on the host"}
 
 
 def cpu_baseline(cfg):
@@ -98,10 +170,12 @@ def cpu_baseline(cfg):
         if spent > budget_s:
             break
     tflops = per_slice * done / spent / 1e12
+    model, blas = host_description()
     return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} of {len(slices)} slices of the same workload, NumPy float64, "
                       f"{spent:.2f} s ({spent / done * 1e3:.0f} ms/slice; full call "
-                      f"would take {spent / done * len(slices):.1f} s)"}
+                      f"would take {spent / done * len(slices):.1f} s)",
+            "cpu_model": model, "blas": blas}
 
 
 def sampled_parity(cfg, Q, K, V, y):
@@ -220,6 +294,8 @@ def main():
                     help="time monarch_attn_backward (dQ, dK, dV for a seeded dY) instead of "
                          "the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-p9", action="store_true",
+                    help="skip the error of Y against exact softmax attention (host float64)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy 3 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -315,7 +391,8 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
 
     dom = max(set(names), key=lambda n: kern_ms[n])
-    kb = kernel_bytes(cfg, dom, precise)
+    kb = method_bytes(cfg, dom)
+    db = design_bytes(cfg, dom, precise)
     achieved = kb / (kern_ms[dom] * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
@@ -328,7 +405,11 @@ def main():
             traffic = ent["hbm_bytes_per_launch"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom, "algorithmic_bytes": kb, "kernel_ms": round(kern_ms[dom], 5)}
+                "kernel": dom, "algorithmic_bytes": kb, "kernel_ms": round(kern_ms[dom], 5),
+                "design_bytes": db,
+                "design_frac": round(db / (kern_ms[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic_over_algorithmic": round(traffic / kb, 3) if traffic else None,
+                "traffic_over_design": round(traffic / db, 3) if traffic else None}
     whole = {"algorithmic_bytes": cfg.algorithmic_bytes(),
              "hbm_frac_of_call": round(cfg.algorithmic_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "mfma_frac_of_call": round(value / MFMA_PEAK_TFLOPS[cfg.dtype], 4)}
@@ -336,6 +417,12 @@ def main():
     y = sets[(args.steps - 1) % n_sets][3].float().cpu().numpy()
     parity = sampled_parity(cfg, Q, K, V, y)
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+    p9 = None
+    if not args.no_p9:
+        # every row where the exact product fits a few seconds of host time,
+        # 4096 seeded rows per head for the video latents
+        p9 = exact_attention_error(cfg, Q, K, V, y,
+                                   rows_per_head=4096 if cfg.seq_len > 16384 else None)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -359,6 +446,7 @@ def main():
         "call_ms_events": round(call_ms, 5),
         "wall_ms_per_call": round(wall_ms, 5),
         "parity_sampled_Y_rel_err": parity,
+        "error_vs_exact_attention": p9,
         "source_hash": source_hash(),
     }
     print(json.dumps(out))

@@ -4,8 +4,7 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# MONARCH_ATTN_LIB may name another build of the same library (tuning sweeps)
-LIB_PATH = os.environ.get("MONARCH_ATTN_LIB") or os.path.join(PKG, "libmonarch_attn.so")
+LIB_PATH = os.path.join(PKG, "libmonarch_attn.so")
 
 MA_OK = 0
 STATUS_NAMES = {0: "MA_OK", 1: "MA_ERR_INVALID_ARGUMENT", 2: "MA_ERR_UNSUPPORTED",

@@ -23,6 +23,10 @@
 
 #include <hip/hip_cooperative_groups.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "ma_stage_kernels.hpp"
 
 namespace ma {
@@ -161,19 +165,30 @@ template <int D> struct WaveRows {
   }
 };
 
-// Resident workgroups per CU of a kernel (cached) times the CU count.
+// Resident workgroups per CU of a kernel on a device, cached per (kernel
+// address, device): every instantiation of a kernel template has its own
+// register and LDS footprint.
+inline int cached_occupancy(const void* kernel, int dev, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, dev);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int v = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, 0) != hipSuccess || v < 1) v = 1;
+  cache.emplace(key, v);
+  return v;
+}
+
+// Resident workgroups per CU of a kernel times the CU count, at most items.
 template <class K>
 inline size_t resident_slots(K kernel, int threads, size_t items) {
-  static int per_cu = -1;
-  if (per_cu < 0) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, 0) != hipSuccess || v < 1) v = 1;
-    per_cu = v;
-  }
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
+  const int per_cu = cached_occupancy(reinterpret_cast<const void*>(kernel), dev, threads);
   return std::max<size_t>(1, std::min<size_t>(items, (size_t)per_cu * cus));
 }
 

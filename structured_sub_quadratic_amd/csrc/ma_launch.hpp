@@ -15,10 +15,6 @@ namespace ma {
 
 inline unsigned grid1(size_t n) { return (unsigned)n; }
 
-#ifndef MA_NO_PERSISTENT
-#define MA_NO_PERSISTENT 0
-#endif
-
 // Workgroups of a persistent launch: two per compute unit of the current
 // device (the persistent kernels are built for two resident workgroups).
 inline size_t persistent_slots() {
@@ -30,10 +26,6 @@ inline size_t persistent_slots() {
 }
 
 template <typename T> constexpr bool is_f32() { return std::is_same<T, float>::value; }
-
-#ifndef MA_NO_ASYNC
-#define MA_NO_ASYNC 0
-#endif
 
 
 // Waves per workgroup of the direct-to-LDS kernels: 8 (128 query rows) unless
@@ -63,20 +55,13 @@ inline int pick_nq(int rows) {
   const int pad1 = (rows + 63) / 64 * 64 - rows, pad2 = (rows + 127) / 128 * 128 - rows;
   return pad2 <= pad1 ? 2 : 1;
 }
-// Build-time overrides for tuning sweeps (0 = automatic choice).
-#ifndef MA_S1_NQ
-#define MA_S1_NQ 0
-#endif
-#ifndef MA_S2_NQ
-#define MA_S2_NQ 0
-#endif
 template <typename T, int D> int stage1_nq(int slots) {
   if (D == 128 || is_f32<T>()) return 1;
-  return MA_S1_NQ ? MA_S1_NQ : pick_nq(slots);
+  return pick_nq(slots);
 }
 template <typename T, int D> int stage2_nq(int rows) {
   if (is_f32<T>() && D == 128) return 1;     // two sub-tiles would spill
-  return MA_S2_NQ ? MA_S2_NQ : pick_nq(rows);
+  return pick_nq(rows);
 }
 
 // Cooperative launch of a fused kernel: as many workgroups as can be resident
@@ -109,7 +94,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
   switch (kind) {
     case L_FUSED: {
       if constexpr (!is_f32<T>()) {
-        if (pl.c1 == 1 && !pl.padded && pl.b2 <= 128 && !MA_NO_ASYNC) {
+        if (pl.c1 == 1 && !pl.padded && pl.b2 <= 128) {
           // copied-tile stages in one cooperative launch; both phases use
           // the stage-1 wave count
           const int nqs = pl.b2, ktb = pl.b2 <= 64 ? 64 : 128;
@@ -125,10 +110,12 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           const size_t items = std::max<size_t>((size_t)S * pl.b1 * p1.nqg, (size_t)S * pl.b2 * p2.nqg);
           void* args[] = {&p1, &p2};
           hipError_t e = hipSuccess;
+          // with one row tile the query slots are the b2 positions of a
+          // block, so head_dim 64 takes 4 waves exactly when the block fits
+          // one 64-key tile, 8 waves otherwise
 #define MA_FA(NW, KTB) e = launch_cooperative(fused_async_kernel<D, NW, KTB, PRECISE>, items, args, st, NW * WAVE)
           if constexpr (D == 64) {
-            if (nw == 8) { if (ktb == 64) MA_FA(8, 64); else MA_FA(8, 128); }
-            else { if (ktb == 64) MA_FA(4, 64); else MA_FA(4, 128); }
+            if (ktb == 64) MA_FA(4, 64); else MA_FA(8, 128);
           } else {
             if (ktb == 64) MA_FA(4, 64); else MA_FA(4, 128);
           }
@@ -137,7 +124,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           break;
         }
       }
-      QbarParams pq{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt};
+      // the bf16 tile means too (a backward that reuses this state reads them)
+      QbarParams pq{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt, qbar_lp};
       const int nqs = pl.c1 * pl.b2;
       const int nq1 = stage1_nq<T, D>(nqs), qg1 = WAVES * nq1 * 16;
       Stage1Params p1{b.q, b.k, b.v, qtil, qbar, cx, ux, h2, lser, pl.map,
@@ -203,7 +191,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
         // whose fp32 queries q~ it reads into registers (QF builds); other
         // fp32 query sources stay on the register-staged kernels
         const bool qf = step > 0 && pl.c1 == 1 && pl.c2 == 1 && !pl.padded;
-        if (pl.b2 <= 128 && ((step == 0 && ((pl.c1 == 1 && !pl.padded) || qbar_lp)) || qf) && !MA_NO_ASYNC) {
+        if (pl.b2 <= 128 && ((step == 0 && ((pl.c1 == 1 && !pl.padded) || qbar_lp)) || qf)) {
           // head_dim 128 keeps 4 waves (two waves a SIMD would spill the
           // K|V sums)
           const int nw = D == 64 ? async_waves(nqs) : 4, qg = nw * 16;
@@ -259,7 +247,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
         break;
       }
       // persistent pipelined kernel when the whole block fits one LDS tile
-      const bool persistent = pl.b2 <= (ktb64 ? 64 : 128) && !MA_NO_PERSISTENT;
+      const bool persistent = pl.b2 <= (ktb64 ? 64 : 128);
       const dim3 pgrid(grid1(std::min<size_t>(items1, persistent_slots())));
 #define MA_S1_K(NQ, KTB, U, QS)                                                                   \
   do {                                                                                            \
@@ -294,7 +282,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     case L_STAGE2_STATS:
     case L_STAGE2_LAST: {
       if constexpr (!is_f32<T>()) {
-        if (!MA_NO_ASYNC) {
+        {
           const int nw = stage2_waves<D>(pl.rt), qg = nw * 16;
           Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
@@ -330,7 +318,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const dim3 grid(grid1(items2));
       const int nkeys = pl.b1 * pl.c2;
       const int ktb = nkeys <= 64 ? 64 : 128;
-      const bool persistent = nkeys <= ((is_f32<T>() && D == 128) ? 64 : 128) && !MA_NO_PERSISTENT;
+      const bool persistent = nkeys <= ((is_f32<T>() && D == 128) ? 64 : 128);
       const dim3 pgrid(grid1(std::min<size_t>(items2, persistent_slots())));
 #define MA_S2_P(NQ, PV)                                                                           \
   do {                                                                                            \

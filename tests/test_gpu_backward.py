@@ -283,6 +283,12 @@ def test_n16k_pad_t2_backward_sampled():
     ("bf16", dict(dtype="bf16", d=64, b1=70, b2=52)),
     ("f32 d128", dict(dtype="f32", d=128, b1=52, b2=40)),
     ("tiled", dict(dtype="bf16", d=64, b1=48, b2=52, c1=3, c2=2)),
+    # the forward as one cooperative launch leaves the same state, the bf16
+    # tile means of tiled and padded problems included
+    ("fused bf16", dict(dtype="bf16", d=128, b1=40, b2=100, fused=True)),
+    ("fused tiled", dict(dtype="bf16", d=64, b1=48, b2=52, c1=3, c2=2, fused=True)),
+    ("fused padded", dict(dtype="bf16", d=64, b1=70, b2=52, pad=20, fused=True)),
+    ("fused padded front", dict(dtype="bf16", d=128, b1=30, b2=40, pad=7, front=True, fused=True)),
 ])
 def test_reuse_forward_state(name, kw):
     """A forward call given the backward's workspace leaves its state there;
@@ -292,23 +298,30 @@ def test_reuse_forward_state(name, kw):
     statistics launch reach the same normalisers by different code)."""
     import torch
     import structured_sub_quadratic_amd as ma
-    cfg = case(f"bwd reuse {name}", kw["dtype"], kw["d"], kw["b1"], kw["b2"], data="normed",
-               c1=kw.get("c1", 1), c2=kw.get("c2", 1))
+    padn = kw.get("pad", 0)
+    pad = "pre" if kw.get("front") else "post"
+    cfg = WorkloadConfig("case", f"bwd reuse {name}", batch=1, heads=2,
+                         seq_len=kw["b1"] * kw["b2"] - padn, head_dim=kw["d"], b1=kw["b1"],
+                         b2=kw["b2"], steps=1, dtype=kw["dtype"], data="normed", seed=61,
+                         c1=kw.get("c1", 1), c2=kw.get("c2", 1), pad=pad)
     Q, K, V = make_inputs(cfg)
     dY = upstream(cfg)
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     dev = torch.device("cuda:0")
     tq, tk, tv, tdy = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt) for x in (Q, K, V, dY))
     prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2, 1,
-                           cfg.c1, cfg.c2, None, cfg.dtype)
+                           cfg.c1, cfg.c2, None, cfg.dtype,
+                           flags=ma.MA_FLAG_PAD_FRONT if pad == "pre" else 0)
     ws = torch.empty(ma.backward_workspace_size(prob), dtype=torch.uint8, device=dev)
+    ws.fill_(0xFF)          # what the forward leaves must be all the backward reads
     args = (cfg.b1, cfg.b2, 1, cfg.c1, cfg.c2)
-    ref = ma.backward(tq, tk, tv, tdy, *args)
-    ma.forward(tq, tk, tv, *args, workspace=ws)
-    got = ma.backward(tq, tk, tv, tdy, *args, workspace=ws, reuse_forward_state=True)
+    ref = ma.backward(tq, tk, tv, tdy, *args, pad=pad)
+    ma.forward(tq, tk, tv, *args, workspace=ws, pad=pad, force_fused=kw.get("fused", False))
+    got = ma.backward(tq, tk, tv, tdy, *args, workspace=ws, reuse_forward_state=True, pad=pad)
     torch.cuda.synchronize()
     for g, r in zip(got, ref):
         g, r = g.float().cpu().numpy(), r.float().cpu().numpy()
+        assert np.isfinite(g).all(), name
         assert np.abs(g - r).max() <= (1e-6 if cfg.dtype == "f32" else 2.0 ** -7) * np.abs(r).max(), name
 
 

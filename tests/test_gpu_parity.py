@@ -30,34 +30,47 @@ def _gpu():
 
 def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective"),
                noise=None, tol=None, kv_heads=None, **kw):
+    """Run the HIP path once on the whole problem, then compare every
+    requested slice with the oracle run on that slice alone (so that the
+    oracle's memory stays that of one slice at the full sizes)."""
     all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     slices = all_slices if slices is None else slices
     Q, K, V = make_inputs(cfg, noise_scale=noise)
     if kv_heads is not None:        # grouped-query attention: keep the first kv_heads
         K, V = (np.ascontiguousarray(X[:, :kv_heads]) for X in (K, V))
+    group = cfg.heads // K.shape[1]
     y, ex = run_hip(cfg, Q, K, V, exports=exports, **kw)
-    ref = oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                         layout=cfg.layout, fhw=cfg.fhw, cols=cols, slices=slices, pad=cfg.pad)
     tiled = cfg.c1 * cfg.c2 > 1
     tol = TOL[cfg.dtype] if tol is None else tol
     errs = {}
-    tok = ref["grid"][:, ref["cols"]].reshape(-1)
-    tok = tok[tok >= 0]                 # padding positions have no token
-    errs["Y"] = rel_err(y[:, :, tok], ref["y"][:, :, tok], slices)
-    if "L" in ex:
-        errs["L"] = rel_err(ex["L"][:, :, ref["cols"]], oracle_L_as_gpu(ref["L"], tiled), slices)
-    if "R" in ex:
-        errs["R"] = rel_err(ex["R"][:, :, :, ref["cols"]], oracle_R_as_gpu(ref["R"], tiled), slices)
-    if "lse" in ex:
-        errs["lse"] = rel_err(ex["lse"][:, :, tok], ref["lse"][:, :, tok], slices)
-    if "objective" in ex and cols is None:
-        obj = ex["objective"].reshape(cfg.batch, cfg.heads)
-        ft = ref["f_trace"][:, :, -1]
-        errs["objective"] = max(abs(obj[b, h] - ft[b, h]) / abs(ft[b, h]) for b, h in slices)
-    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+    for (b, h) in slices:
+        hk = h // group
+        ref = oracle.forward(Q[b:b + 1, h:h + 1], K[b:b + 1, hk:hk + 1], V[b:b + 1, hk:hk + 1],
+                             cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
+                             fhw=cfg.fhw, cols=cols, pad=cfg.pad)
+        one = [(0, 0)]
+        tok = ref["grid"][:, ref["cols"]].reshape(-1)
+        tok = tok[tok >= 0]                 # padding positions have no token
+        e = {"Y": rel_err(y[b:b + 1, h:h + 1, tok], ref["y"][:, :, tok], one)}
+        if "L" in ex:
+            e["L"] = rel_err(ex["L"][b:b + 1, h:h + 1, ref["cols"]],
+                             oracle_L_as_gpu(ref["L"], tiled), one)
+        if "R" in ex:
+            e["R"] = rel_err(ex["R"][b:b + 1, h:h + 1, :, ref["cols"]],
+                             oracle_R_as_gpu(ref["R"], tiled), one)
+        if "lse" in ex:
+            e["lse"] = rel_err(ex["lse"][b:b + 1, h:h + 1, tok], ref["lse"][:, :, tok], one)
+        if "objective" in ex and cols is None:
+            obj = ex["objective"].reshape(cfg.batch, cfg.heads)[b, h]
+            ft = ref["f_trace"][0, 0, -1]
+            e["objective"] = abs(obj - ft) / abs(ft)
+        for k_, v_ in e.items():
+            errs[k_] = max(errs.get(k_, 0.0), v_)
+    print(cfg.name, f"{len(slices)} slices x {cfg.b2 if cols is None else len(cols)} columns",
+          {k: f"{v:.2e}" for k, v in errs.items()})
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{cfg.name}: {errs} (tol {tol})"
-    return y, ex, ref
+    return y, ex, None
 
 
 # ----------------------------------------------------------------- small
@@ -192,6 +205,12 @@ def test_determinism_and_reuse_of_workspace():
     dict(name="video", dtype="bf16", d=128, b1=8, b2=15, c=(1, 3), layout="w_fh", fhw=(3, 5, 8), data="video"),
     dict(name="f32d128", dtype="f32", d=128, b1=40, b2=48, c=(2, 1), layout="flat", fhw=None, data="iid"),
     dict(name="wide", dtype="bf16", d=64, b1=12, b2=200, c=(3, 2), layout="flat", fhw=None, data="normed"),
+    # blocks of 65..128 keys reach the copied-tile fused builds with 128-key
+    # tiles: 8 waves at head_dim 64, 4 waves at head_dim 128 (ragged and full)
+    dict(name="blk100 d64", dtype="bf16", d=64, b1=24, b2=100, c=(1, 1), layout="flat", fhw=None, data="normed"),
+    dict(name="blk100 d128", dtype="bf16", d=128, b1=24, b2=100, c=(1, 1), layout="flat", fhw=None, data="normed"),
+    dict(name="blk128 d128", dtype="bf16", d=128, b1=40, b2=128, c=(1, 1), layout="flat", fhw=None, data="iid"),
+    dict(name="blk64 d64", dtype="bf16", d=64, b1=72, b2=64, c=(1, 1), layout="flat", fhw=None, data="iid"),
 ])
 def test_t1_fused_and_staged_paths(case):
     """T = 1 as one cooperative launch and as the staged launch sequence: the
@@ -249,10 +268,10 @@ def test_grouped_query_attention(case):
 
 def test_grouped_query_attention_n16k_sampled():
     """The n16k shape with 12 query heads over 4 K/V heads, in the default
-    launch configuration."""
+    launch configuration: three slices, every column."""
     cfg = WORKLOADS["n16k"]
-    check_case(cfg, slices=[(0, 0), (0, 5), (0, 11)], cols=[0, 64, 127],
-               exports=("L", "R", "lse"), kv_heads=4)
+    check_case(cfg, slices=[(0, 0), (0, 5), (0, 11)], exports=("L", "R", "lse", "objective"),
+               kv_heads=4)
 
 
 # ------------------------------------------------ padded flat sequences
@@ -293,44 +312,58 @@ def test_padded_tiles(pad, case):
 @pytest.mark.parametrize("pad", ["pre", "post"])
 def test_padded_long_sequence_sampled(pad):
     """16384 - 100 tokens on the 128 x 128 grid, 12 query heads over 4 K/V
-    heads, in the default launch configuration."""
+    heads, in the default launch configuration: two slices, every column."""
     cfg = WorkloadConfig("case", f"n16k-100 pad={pad}", batch=1, heads=12, seq_len=16384 - 100,
                          head_dim=64, b1=128, b2=128, steps=1, dtype="bf16", data="normed",
                          seed=47, pad=pad)
-    check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 50, 99, 100, 127], exports=("L", "R", "lse"),
-               kv_heads=4)
+    check_case(cfg, slices=[(0, 0), (0, 7)], exports=("L", "R", "lse", "objective"), kv_heads=4)
 
 
-# ------------------------------------------------ benchmark workloads, sampled
+# ------------------------------------------------ benchmark workloads at full size
+
+N4K_T3_SLICES = [(0, 0), (0, 11), (1, 5), (2, 3), (3, 7), (3, 10), (4, 1), (5, 6), (5, 9),
+                 (6, 2), (7, 4), (7, 11)]
+
 
 def test_n4k_t3_sampled():
-    cfg = WORKLOADS["n4k_t3"]
-    check_case(cfg, slices=[(0, 0), (3, 7), (7, 11)], exports=("L", "R", "lse"))
+    """The T = 3 workload: 12 of its 96 slices (spread over batch and head),
+    every column, every export."""
+    check_case(WORKLOADS["n4k_t3"], slices=N4K_T3_SLICES)
 
 
-def test_n16k_sampled():
+def test_n16k_full():
+    """The headline workload in the launch configuration the benchmark times:
+    every slice, every column, every export."""
+    check_case(WORKLOADS["n16k"])
+
+
+def test_n16k_fused_full():
+    """The headline workload as one cooperative launch (the 8-wave, 128-key
+    copied-tile fused build): every slice, every column, every export, and the
+    same output as the staged launches."""
     cfg = WORKLOADS["n16k"]
-    check_case(cfg, slices=[(0, 0), (0, 11)], cols=[0, 1, 63, 64, 127],
-               exports=("L", "R", "lse"))
+    y_f, _, _ = check_case(cfg, force_fused=True)
+    y_s, _, _ = check_case(cfg, exports=(), force_staged=True)
+    assert np.abs(y_f - y_s).max() <= 1e-6 * np.abs(y_s).max()
 
 
 @pytest.mark.parametrize("key", ["n16k", "video", "video_tiled"])
 def test_precise_aggregate_t1_workloads(key):
     """The split aggregate path (MA_FLAG_PRECISE_AGGREGATE) on the T = 1
-    workloads, whose default is the plain bf16 path."""
+    workloads, whose default is the plain bf16 path: two slices, every
+    column."""
     cfg = WORKLOADS[key]
-    check_case(cfg, slices=[(0, 0), (0, 5)], cols=[0, 17, cfg.b2 - 1], exports=("L", "R", "lse"),
-               precise_aggregate=True)
+    check_case(cfg, slices=[(0, 0), (0, 5)], exports=("L", "R", "lse"), precise_aggregate=True)
 
 
 def test_video_sampled():
-    cfg = WORKLOADS["video"]
-    check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 25, 51], exports=("L", "R", "lse"))
+    """The video latent: two slices, all 52 columns, every export."""
+    check_case(WORKLOADS["video"], slices=[(0, 0), (0, 7)])
 
 
 def test_video_tiled_sampled_and_c1_equality():
     cfg = WORKLOADS["video_tiled"]
-    check_case(cfg, slices=[(0, 0), (0, 7)], cols=[0, 26, 51], exports=("L", "R", "lse"))
+    check_case(cfg, slices=[(0, 0), (0, 7)])
     # c1 = c2 = 1 on the same data: equal to the untiled oracle and to the
     # tiled oracle with c = 1
     c4 = WORKLOADS["video"]
@@ -338,8 +371,39 @@ def test_video_tiled_sampled_and_c1_equality():
     y, _ = run_hip(c4, Q, K, V, exports=())
     cols = [3, 30]
     for tiled in (False, True):
-        ref = oracle.forward(Q, K, V, 630, 52, 1, 1, 1, layout="fh_w", fhw=(21, 30, 52),
-                             cols=cols, slices=[(0, 2)], tiled=tiled)
+        ref = oracle.forward(Q[:, 2:3], K[:, 2:3], V[:, 2:3], 630, 52, 1, 1, 1, layout="fh_w",
+                             fhw=(21, 30, 52), cols=cols, tiled=tiled)
         tok = ref["grid"][:, cols].reshape(-1)
-        err = rel_err(y[:, :, tok], ref["y"][:, :, tok], [(0, 2)])
+        err = rel_err(y[:, 2:3, tok], ref["y"][:, :, tok], [(0, 0)])
         assert err < TOL["bf16"], (tiled, err)
+
+
+# ------------------------------------------------ error against exact attention
+
+@pytest.mark.parametrize("key", ["n256", "n4k_t3", "n16k", "video", "video_tiled"])
+def test_error_vs_exact_attention_reported(key):
+    """The error of Y against exact softmax attention softmax(QK^T/sqrt(d))V,
+    ||Y - Y_exact||_F / ||Y_exact||_F, in the launch configuration the
+    benchmark times: every row of the language shapes, 4096 seeded query rows
+    per head of the video latents.  The method approximates attention and
+    the pages give no bound, so the value is reported (printed), and only
+    checked to be finite and well below the scale of Y."""
+    cfg = WORKLOADS[key]
+    Q, K, V = make_inputs(cfg)
+    y, _ = run_hip(cfg, Q, K, V, exports=())
+    rows = np.arange(cfg.seq_len) if cfg.seq_len <= 16384 else \
+        np.sort(np.random.default_rng(4242).choice(cfg.seq_len, 4096, replace=False))
+    num = den = 0.0
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            k, v = (X[b, h].astype(np.float64) for X in (K, V))
+            for c0 in range(0, rows.size, 2048):
+                r = rows[c0:c0 + 2048]
+                ex = oracle.exact_attention(Q[b, h, r].astype(np.float64), k, v,
+                                            1 / math.sqrt(cfg.head_dim))
+                num += float(np.sum((y[b, h, r] - ex) ** 2))
+                den += float(np.sum(ex ** 2))
+    err = math.sqrt(num / den)
+    print(f"{cfg.name}: ||Y - Y_exact|| / ||Y_exact|| = {err:.4f} over "
+          f"{'all' if rows.size == cfg.seq_len else rows.size} rows per head")
+    assert np.isfinite(err) and err < 1.0
