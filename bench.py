@@ -68,6 +68,19 @@ def method_bytes(cfg, name):
     return None if per is None else per * S
 
 
+def method_flops(cfg, causal=0):
+    """Algorithmic flops of the call.  With a block-causal mask a stage-2 row
+    l meets only the allowed key blocks, min(b1, (l // g + 1) * g) of them,
+    so b1 in the stage-2 terms becomes their mean over the rows."""
+    if not causal:
+        return cfg.algorithmic_flops()
+    N, d, b1, b2, c1, c2, T = (cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2, cfg.c1, cfg.c2,
+                               cfg.steps)
+    kb = sum(min(b1, (l // causal + 1) * causal) for l in range(b1)) / b1
+    per = 2 * N * d * (3 * c1 * b2 + 2 * c2 * kb + (T - 1) * 2 * (c1 * b2 + c2 * kb))
+    return per * cfg.slices
+
+
 def design_bytes(cfg, name, precise):
     """HBM bytes of one launch as designed: every operand the kernel reads
     once and every result it writes once, including the stage-1 -> stage-2
@@ -119,14 +132,23 @@ def host_description():
     return model, blas
 
 
-def exact_attention_error(cfg, Q, K, V, y, rows_per_head=None, seed=4242):
+def exact_attention_error(cfg, Q, K, V, y, rows_per_head=None, seed=4242, causal=0):
     """P9, reported only: the relative Frobenius error ||Y - Y_exact|| /
     ||Y_exact|| of the method's output against exact softmax attention
     softmax(Q K^T / sqrt(d)) V, computed in float64 on the host in row
     chunks.  Every row when rows_per_head is None, else that many seeded
-    query rows per head (the same rows for every head)."""
+    query rows per head (the same rows for every head).  With a block-causal
+    mask (layouts whose blocks are runs of b2 consecutive tokens) the exact
+    product is masked the same way: token n attends to n' iff
+    unit(n') <= unit(n), unit = grid block // g."""
     import numpy as np
     B, H, N, d = Q.shape
+    unit = None
+    if causal:
+        if cfg.layout not in ("flat", "fh_w", "f_hw"):
+            return None
+        pre = cfg.b1 * cfg.b2 - N if cfg.pad == "pre" else 0
+        unit = ((np.arange(N) + pre) // cfg.b2) // causal
     group = H // K.shape[1]
     scale = 1.0 / math.sqrt(d)
     rows = np.arange(N) if rows_per_head is None else \
@@ -139,6 +161,8 @@ def exact_attention_error(cfg, Q, K, V, y, rows_per_head=None, seed=4242):
             for c0 in range(0, rows.size, 2048):
                 r = rows[c0:c0 + 2048]
                 s_ = scale * (Q[b, h, r].astype(np.float64) @ k.T)
+                if unit is not None:
+                    s_ = np.where(unit[None, :] <= unit[r][:, None], s_, -np.inf)
                 s_ -= s_.max(axis=1, keepdims=True)
                 p = np.exp(s_)
                 ex = (p @ v) / p.sum(axis=1, keepdims=True)
@@ -150,21 +174,21 @@ def exact_attention_error(cfg, Q, K, V, y, rows_per_head=None, seed=4242):
                        "float64 on the host"}
 
 
-def cpu_baseline(cfg):
+def cpu_baseline(cfg, causal=0):
     """The oracle as it stands, on this host, over the whole workload (or a
     bounded number of slices), in the metric's unit."""
     import numpy as np
     import oracle
     from workloads import make_inputs
     cores = len(os.sched_getaffinity(0))
-    per_slice = cfg.algorithmic_flops() / cfg.slices
+    per_slice = method_flops(cfg, causal) / cfg.slices
     budget_s, spent, done = 20.0, 0.0, 0
     slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     for sl in slices:
         Q, K, V = make_inputs(cfg, slices=[sl])
         t0 = time.perf_counter()
         oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                       layout=cfg.layout, fhw=cfg.fhw, slices=[sl], pad=cfg.pad)
+                       layout=cfg.layout, fhw=cfg.fhw, slices=[sl], pad=cfg.pad, causal=causal)
         spent += time.perf_counter() - t0
         done += 1
         if spent > budget_s:
@@ -178,13 +202,14 @@ def cpu_baseline(cfg):
             "cpu_model": model, "blas": blas}
 
 
-def sampled_parity(cfg, Q, K, V, y):
+def sampled_parity(cfg, Q, K, V, y, causal=0):
     """Y, L, R of one slice at four columns against the oracle (quick check)."""
     import numpy as np
     import oracle
     cols = sorted({0, cfg.b2 // 3, cfg.b2 // 2, cfg.b2 - 1})
-    ref = oracle.forward(Q, K, V, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
-                         fhw=cfg.fhw, cols=cols, slices=[(0, 0)], pad=cfg.pad)
+    ref = oracle.forward(Q[:1, :1], K[:1, :1], V[:1, :1], cfg.b1, cfg.b2, cfg.steps, cfg.c1,
+                         cfg.c2, layout=cfg.layout, fhw=cfg.fhw, cols=cols, pad=cfg.pad,
+                         causal=causal)
     tok = ref["grid"][:, cols].reshape(-1)
     tok = tok[tok >= 0]
     a, r = y[0, 0][tok].astype(np.float64), ref["y"][0, 0][tok]
@@ -293,6 +318,8 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time monarch_attn_backward (dQ, dK, dV for a seeded dY) instead of "
                          "the forward")
+    ap.add_argument("--causal", type=int, default=0,
+                    help="block-causal use: g grid blocks per causal unit (0: bidirectional)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-p9", action="store_true",
                     help="skip the error of Y against exact softmax attention (host float64)")
@@ -343,7 +370,7 @@ def main():
         flags |= ma.MA_FLAG_PAD_FRONT
     prob = ma.make_problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.b1, cfg.b2,
                            cfg.steps, cfg.c1, cfg.c2, None, cfg.dtype, cfg.layout, cfg.fhw, flags,
-                           kv_heads=cfg.kv_heads)
+                           kv_heads=cfg.kv_heads, causal=args.causal)
     names = ma.launch_names(prob)
     nl = len(names)
     ws_bytes = ma.workspace_size(prob)
@@ -386,7 +413,7 @@ def main():
     call_ms = float(np.mean([events[i][0].elapsed_ms(events[i][-1]) for i in range(args.steps)]))
     kern_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
 
-    flops = cfg.algorithmic_flops()
+    flops = method_flops(cfg, args.causal)
     ms = span_ms
     value = flops / (ms * 1e-3) / 1e12
 
@@ -415,14 +442,15 @@ def main():
              "mfma_frac_of_call": round(value / MFMA_PEAK_TFLOPS[cfg.dtype], 4)}
 
     y = sets[(args.steps - 1) % n_sets][3].float().cpu().numpy()
-    parity = sampled_parity(cfg, Q, K, V, y)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+    parity = sampled_parity(cfg, Q, K, V, y, args.causal)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.causal)
     p9 = None
     if not args.no_p9:
         # every row where the exact product fits a few seconds of host time,
         # 4096 seeded rows per head for the video latents
         p9 = exact_attention_error(cfg, Q, K, V, y,
-                                   rows_per_head=4096 if cfg.seq_len > 16384 else None)
+                                   rows_per_head=4096 if cfg.seq_len > 16384 else None,
+                                   causal=args.causal)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -438,7 +466,8 @@ def main():
                    "inputs": "warm (one set)" if args.warm else f"cold ({n_sets} rotating sets)",
                    "aggregate": "split bf16 hi+lo" if precise and cfg.dtype != "f32" else
                                 ("fp32" if cfg.dtype == "f32" else "plain bf16"),
-                   "launches": names},
+                   "launches": names,
+                   "block_causal_units": args.causal or None},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "whole_call": whole,

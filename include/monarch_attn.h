@@ -141,11 +141,30 @@ typedef struct {
                           OpenReview author response on GQA/MLA: the method
                           applies per query head, stage 1 reading the shared
                           K/V of its group) */
+  int32_t causal;      /* 0: bidirectional.  g >= 1: block-causal use, query
+                          block l (grid row) attends to key block k iff
+                          floor(k/g) <= floor(l/g), i.e. causally across
+                          units of g consecutive grid blocks and fully inside
+                          one.  On a flat sequence g = 1 is the usual
+                          block-causal mask with blocks of b2 tokens; on the
+                          (fh, w) video layout g = h (times frames per chunk)
+                          is frame-causal.  The pages note that token-level
+                          causal masking does not fit the method
+                          (MonarchAttention, scime summary "Limitations") and
+                          target autoregressive video models (MonarchRT,
+                          summary page); a mask over whole blocks keeps every
+                          block rank one: M and L are zero on masked blocks,
+                          the objective runs over the allowed entries, the
+                          L-update is a softmax over the allowed keys and the
+                          R-update keeps its form.  g >= b1 masks nothing.
+                          Forward only (the backward returns
+                          MA_ERR_UNSUPPORTED for a mask that masks). */
 } ma_problem;
 
 /* Optional exports (device pointers, each may be NULL), always fp32/fp64.
  * L:   [batch, heads, b2, b1, b1*c2]    L[i][l][k*c2 + s] after the last step
- *                                       (grid positions; zero rows at padding)
+ *                                       (grid positions; zero rows at padding,
+ *                                       zero at blocks a causal mask removes)
  * R:   [batch, heads, b1, b2, c1, b2]   R[k][i][t][j]     after the last step
  * lse: [batch, heads, seq_len]          token order; logsumexp (natural log)
  *      of the last L-update's scores for each query row

@@ -32,6 +32,7 @@ from .monarch import (
     dense_from_factors,
     tile_of_rows,
     segment_of_cols,
+    causal_allowed,
 )
 from .reference_attention import (
     exact_attention,
@@ -44,6 +45,6 @@ from .reference_attention import (
 __all__ = [
     "LAYOUTS", "grid_index", "to_grid", "from_grid",
     "forward_untiled", "forward_tiled", "forward", "dense_from_factors",
-    "tile_of_rows", "segment_of_cols",
+    "tile_of_rows", "segment_of_cols", "causal_allowed",
     "exact_attention", "dense_objective", "row_entropy", "logsumexp", "softmax", "backward",
 ]

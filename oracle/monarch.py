@@ -73,6 +73,19 @@ Readings where the pages are silent:
     fallback: the mean of q over the real rows of its tile and column (zero
     if there are none; its R row then weighs nothing).  Every segment must
     hold a real key.
+  * block-causal use ([MA] scime summary "Limitations": causal masking does
+    not fit the method; MonarchRT, summary page: few-step autoregressive
+    video DiTs, which attend causally across chunks of frames and
+    bidirectionally inside a chunk).  Token-level causality cuts through the
+    rank-one blocks, but a mask over whole blocks does not: with causal = g,
+    query block l may attend to key block k iff floor(k/g) <= floor(l/g)
+    (units of g consecutive blocks; g = 1 on a flat sequence is the usual
+    block-causal mask with blocks of b2 tokens, g = h on the (fh, w) video
+    layout is frame-causal).  M is zero on masked entries, i.e. L[i,l,k] = 0
+    there, and the objective runs over the allowed entries only.  Then the
+    R-update keeps its form (L is simply zero on masked (l, k), and the
+    diagonal k = l is always allowed, so L0 = block identity is admissible),
+    and the L-update is the softmax over the allowed k only.
 
 Parity pins (tests/test_oracle_pins.py): dense product P^T L P R on tiny
 grids, simplex rows, non-decreasing objective bounded by sum logsumexp, dense
@@ -127,14 +140,24 @@ def _check_real(real, b1, b2, c2=1):
     return real
 
 
-def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False, real=None):
+def causal_allowed(b1, causal):
+    """allowed[l, k]: query block l may attend to key block k, i.e.
+    floor(k / causal) <= floor(l / causal); everything when causal == 0."""
+    if not causal:
+        return np.ones((b1, b1), bool)
+    unit = np.arange(b1) // causal
+    return unit[None, :] <= unit[:, None]
+
+
+def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False, real=None, causal=0):
     """One (batch, head) slice of untiled MonarchAttention.
 
     qg, kg, vg: [b1, b2, d] in grid order (float64).  cols: optional list of
     columns i to compute (the method is independent across i: R rows [., i, .]
     and L[i] touch only column i of the queries, and all keys).  real:
     optional [b1, b2] bool, False at padding positions (their rows of qg, kg,
-    vg are ignored).
+    vg are ignored).  causal: 0 (bidirectional) or the number g of blocks per
+    causal unit (see causal_allowed).
 
     Returns dict:
       y       [b1, nc, d]   output rows (l, i) for the selected columns
@@ -149,6 +172,7 @@ def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False, real=Non
         raise ValueError("steps must be >= 1")
     cols = np.arange(b2) if cols is None else np.asarray(cols)
     real = _check_real(real, b1, b2)
+    allow = causal_allowed(b1, causal)       # allow[l, k]
     rq = real[:, cols]                       # real query rows (l, i)
     q = scale * np.where(rq[..., None], qg[:, cols, :], 0.0)   # q[l, i], sigma folded in
     nc = q.shape[1]
@@ -171,10 +195,12 @@ def forward_untiled(qg, kg, vg, steps, scale, cols=None, history=False, real=Non
         if history:
             hist.append((L.copy(), R.copy()))
 
-        # L-update: L[i,l,:] = softmax_k(q[l,i] . c[k,i] + H_R[k,i])
+        # L-update: L[i,l,:] = softmax over the allowed k of
+        # q[l,i] . c[k,i] + H_R[k,i]
         w = np.matmul(q.transpose(1, 0, 2), C.transpose(1, 2, 0)) + HR.T[:, None, :]
-        L = softmax(w, axis=-1) * rq.T[:, :, None]         # L[i, l, k]; padding rows 0
-        lse = logsumexp(w, axis=-1)                        # [i, l]
+        wm = np.where(allow[None], w, -np.inf)
+        L = softmax(wm, axis=-1) * rq.T[:, :, None]        # L[i, l, k]; padding rows 0
+        lse = logsumexp(wm, axis=-1)                       # [i, l]
         f_trace.append(_objective_untiled(q, C, HR, L))
         if history:
             hist.append((L.copy(), R.copy()))
@@ -224,11 +250,14 @@ def _tiled_scores(q_rows, C_t, HR_t):
     return w.reshape(nc, q_rows.shape[0], b1, c2)
 
 
-def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False, real=None):
+def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False, real=None,
+                  causal=0):
     """One slice of tiled MonarchAttention with c1 x c2 sub-tiles per block.
 
     Requires c1 | b1 and c2 | b2 (tiles and segments are then contiguous and
-    of equal size).  real: as for forward_untiled.  Returns dict:
+    of equal size).  real, causal: as for forward_untiled (the mask is over
+    blocks l, k, so every segment s of an allowed block is allowed).  Returns
+    dict:
       y       [b1, nc, d]
       L       [nc, b1, b1, c2]   L[i, l, k, s]
       R       [b1, nc, c1, b2]   R[k, i, t, j]  (each segment of j sums to 1)
@@ -242,6 +271,7 @@ def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False, re
         raise ValueError("c1 must divide b1 and c2 must divide b2")
     cols = np.arange(b2) if cols is None else np.asarray(cols)
     real = _check_real(real, b1, b2, c2)
+    allow = causal_allowed(b1, causal)             # allow[l, k]
     rq = real[:, cols]                             # real query rows (l, i)
     q = scale * np.where(rq[..., None], qg[:, cols, :], 0.0)   # q[l, i]
     nc = q.shape[1]
@@ -289,6 +319,7 @@ def forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=None, history=False, re
         for t in range(c1):
             rows = np.nonzero(tile == t)[0]
             w = _tiled_scores(q[rows], C[:, :, t], HR[:, :, t])   # [i, rows, k, s]
+            w = np.where(allow[rows][None, :, :, None], w, -np.inf)
             wf = w.reshape(nc, rows.size, b1 * c2)
             L[:, rows] = (softmax(wf, axis=-1) * rq[rows].T[:, :, None]).reshape(nc, rows.size, b1, c2)
             lse[:, rows] = logsumexp(wf, axis=-1)
@@ -349,7 +380,7 @@ def dense_from_factors(L, R, b1, b2, c1=1, c2=1):
 # ---------------------------------------------------------------------------
 
 def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
-            fhw=None, cols=None, tiled=None, slices=None, pad="post"):
+            fhw=None, cols=None, tiled=None, slices=None, pad="post", causal=0):
     """MonarchAttention on [B, H, N, d] queries and [B, Hkv, N, d] keys and
     values (any float dtype, upcast to float64).  Hkv < H is grouped-query
     attention: query head h uses key/value head h // (H // Hkv), and the
@@ -362,6 +393,8 @@ def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
     cols: optional columns i to compute (Y is then NaN outside them).
     slices: optional list of (b, h) pairs to compute (others left NaN).
     tiled: force the tiled algorithm (default: tiled iff c1*c2 > 1).
+    causal: 0 (bidirectional) or g, the grid blocks per causal unit: query
+    block l attends to key block k iff floor(k/g) <= floor(l/g).
 
     Returns dict with y [B,H,N,d] (token order), L, R (per slice, grid
     order, as returned by forward_untiled / forward_tiled, stacked), lse
@@ -398,9 +431,10 @@ def forward(Q, K, V, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat",
         qg = to_grid(Q[b, h], grid)
         kg, vg = (to_grid(X[b, h // group], grid) for X in (K, V))
         if tiled:
-            r = forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=colsel, real=real)
+            r = forward_tiled(qg, kg, vg, steps, scale, c1, c2, cols=colsel, real=real,
+                              causal=causal)
         else:
-            r = forward_untiled(qg, kg, vg, steps, scale, cols=colsel, real=real)
+            r = forward_untiled(qg, kg, vg, steps, scale, cols=colsel, real=real, causal=causal)
         tok = grid[:, colsel].reshape(-1)          # tokens of the computed grid cells
         ok = tok >= 0
         y[b, h][tok[ok]] = r["y"].reshape(-1, dv)[ok]

@@ -19,7 +19,8 @@ from ._lib import (MonarchAttnError, LAYOUTS, MA_FLAG_FORCE_STAGED, MA_FLAG_FAST
                    MA_FLAG_FORCE_FUSED, MA_FLAG_PRECISE_AGGREGATE, MA_FLAG_PAD_FRONT,
                    MA_FLAG_REUSE_FORWARD_STATE)
 
-__all__ = ["forward", "forward_timed", "backward", "make_problem", "workspace_size",
+__all__ = ["forward", "forward_timed", "backward", "make_problem",
+           "workspace_size",
            "backward_workspace_size", "num_launches", "launch_names", "Event",
            "MonarchAttnError", "LAYOUTS", "library_path", "version"]
 
@@ -42,10 +43,11 @@ def _dtype_code(dtype):
 
 
 def make_problem(batch, heads, seq_len, head_dim, b1, b2, steps=1, c1=1, c2=1, scale=None,
-                 dtype="bf16", layout="flat", fhw=None, flags=0, kv_heads=0):
+                 dtype="bf16", layout="flat", fhw=None, flags=0, kv_heads=0, causal=0):
     """Build the C problem descriptor.  dtype: "f32"/"bf16" or a torch dtype.
     kv_heads: heads of K and V (0: heads); grouped-query attention when
-    smaller."""
+    smaller.  causal: 0, or g grid blocks per causal unit (block-causal use,
+    see ma_problem.causal)."""
     if not isinstance(dtype, int):
         dtype = {"f32": _lib.MA_F32, "bf16": _lib.MA_BF16}.get(dtype, None) \
             if isinstance(dtype, str) else _dtype_code(dtype)
@@ -54,7 +56,7 @@ def make_problem(batch, heads, seq_len, head_dim, b1, b2, steps=1, c1=1, c2=1, s
     f, h, w = fhw if fhw is not None else (0, 0, 0)
     return _lib.MAProblem(batch, heads, seq_len, head_dim, b1, b2, c1, c2, steps,
                           0.0 if scale is None else float(scale), dtype, LAYOUTS[layout],
-                          f, h, w, flags, kv_heads)
+                          f, h, w, flags, kv_heads, causal)
 
 
 def workspace_size(problem):
@@ -106,7 +108,7 @@ class Event:
 
 def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, workspace, out,
              force_staged, fast_aggregate, force_fused=False, precise_aggregate=False,
-             pad="post"):
+             pad="post", causal=0):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -128,7 +130,7 @@ def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, worksp
     if pad == "pre":
         flags |= MA_FLAG_PAD_FRONT
     prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags,
-                        kv_heads=Hkv)
+                        kv_heads=Hkv, causal=causal)
     ws_bytes = workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
@@ -151,7 +153,7 @@ def _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw, exports, worksp
 
 def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
             exports=(), workspace=None, out=None, force_staged=False, fast_aggregate=False,
-            force_fused=False, precise_aggregate=False, pad="post"):
+            force_fused=False, precise_aggregate=False, pad="post", causal=0):
     """MonarchAttention forward on the current stream.  Returns Y, or (Y, dict
     of exports) when exports (a subset of "L", "R", "lse", "objective") is
     non-empty.  Shapes of the exports are documented in monarch_attn.h.
@@ -160,11 +162,14 @@ def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw
     fast_aggregate / precise_aggregate: bf16 only, force the plain or the
     split precision of the c = R K path (default: plain for T = 1, split for
     T > 1; see MA_FLAG_FAST_AGGREGATE).  force_fused / force_staged: T = 1 as
-    one cooperative launch / as separate stage launches."""
+    one cooperative launch / as separate stage launches.  causal: 0
+    (bidirectional) or g >= 1, block-causal use: query block l attends to
+    key block k iff floor(k/g) <= floor(l/g) (ma_problem.causal)."""
     import torch
     prob, workspace, out, ex, cex = _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw,
                                              exports, workspace, out, force_staged,
-                                             fast_aggregate, force_fused, precise_aggregate, pad)
+                                             fast_aggregate, force_fused, precise_aggregate, pad,
+                                             causal)
     st = torch.cuda.current_stream(q.device).cuda_stream
     status = _lib.load().monarch_attn_forward(
         ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -175,13 +180,13 @@ def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw
 
 def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layout="flat",
                   fhw=None, workspace=None, out=None, force_staged=False, fast_aggregate=False,
-                  force_fused=False, precise_aggregate=False, pad="post"):
+                  force_fused=False, precise_aggregate=False, pad="post", causal=0):
     """forward() that also records events[0] before the first kernel launch and
     events[j+1] after launch j (Event objects) on the current stream."""
     import torch
     prob, workspace, out, ex, cex = _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw,
                                              (), workspace, out, force_staged, fast_aggregate,
-                                             force_fused, precise_aggregate, pad)
+                                             force_fused, precise_aggregate, pad, causal)
     st = torch.cuda.current_stream(q.device).cuda_stream
     arr = (ctypes.c_void_p * len(events))(*[e.ptr.value for e in events])
     status = _lib.load().monarch_attn_forward_timed(

@@ -32,6 +32,7 @@ class MAProblem(ctypes.Structure):
         ("f", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
         ("kv_heads", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
     ]
 
 

@@ -451,7 +451,6 @@ struct Stage2Async {
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b2 * p.c1 * p.nqg;
-  const int nch = (p.nkeys + KC - 1) / KC;
   auto decode = [&](int item, int& sl, int& i, int& t, int& qg) {
     qg = item % p.nqg; item /= p.nqg;
     t = item % p.c1; item /= p.c1;
@@ -459,6 +458,13 @@ struct Stage2Async {
     sl = item / p.b2;
   };
   auto row_of = [&](int qg, int n) { return qg * QG + wave * NQ * 16 + n * 16 + lane % 16; };
+  // key chunks of an item: all of them, or (block-causal) those below the
+  // key bound of the item's last row
+  auto nch_of = [&](int item) {
+    int sl, i, t, qg;
+    decode(item, sl, i, t, qg);
+    return (stage2_keys(p, t, qg * QG + QG) + KC - 1) / KC;
+  };
 
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
@@ -491,7 +497,7 @@ struct Stage2Async {
   // column (consecutive items) read their shared key tiles through one L2.
   int item = (int)xcd_swizzle(blockIdx.x, gridDim.x);
   if (item >= nitems) return;
-  int ch = 0;
+  int ch = 0, nch = nch_of(item);
   issue(item, 0, buf_a);
   Core core;
 
@@ -554,13 +560,26 @@ struct Stage2Async {
     flush();
 
     const int nvalid = min(KC, p.nkeys - ch * KC);
-    core.scores_v(SwzKeys<D>(cur + SM::HI, cur + SM::LO), 0, Core::MT);
-    if (nvalid == KC) core.template softmax_step<true, false>(bias, p.sc2, 0, nvalid);
-    else core.template softmax_step<true, true>(bias, p.sc2, 0, nvalid);
-    if constexpr (WITH_PV) {
-      const SwzValuesT<D> vv(cur + SM::U, cur + SM::U);
-      if (nvalid == KC) core.template pv<false>(vv, 0, nvalid);
-      else core.template pv<true>(vv, 0, nvalid);
+    // block-causal use: a wave whose rows all end before this chunk skips
+    // it; a chunk that crosses the bound of one of its rows is masked per row
+    int how = CH_WHOLE;
+    if (p.causal) {
+      int sl, i, t, qg;
+      decode(item, sl, i, t, qg);
+      how = causal_chunk<NQ>(core, p, t, row_of(qg, 0) - lane % 16,
+                             [&](int n) { return row_of(qg, n); }, ch * KC, nvalid);
+    }
+    const bool rowmask = how == CH_ROWMASK;
+    if (how != CH_SKIP) {
+      core.scores_v(SwzKeys<D>(cur + SM::HI, cur + SM::LO), 0, Core::MT);
+      if (rowmask) core.template softmax_step<true, true, 0, true>(bias, p.sc2, 0, nvalid);
+      else if (nvalid == KC) core.template softmax_step<true, false>(bias, p.sc2, 0, nvalid);
+      else core.template softmax_step<true, true>(bias, p.sc2, 0, nvalid);
+      if constexpr (WITH_PV) {
+        const SwzValuesT<D> vv(cur + SM::U, cur + SM::U);
+        if (nvalid == KC && !rowmask) core.template pv<false>(vv, 0, nvalid);
+        else core.template pv<true>(vv, 0, nvalid);
+      }
     }
     if (ch == nch - 1) {
       int sl, i, t, qg;
@@ -588,6 +607,7 @@ struct Stage2Async {
       out.any = true;
     }
     if (nitem >= nitems) return false;
+    if (nitem != item) nch = nch_of(nitem);
     item = nitem;
     ch = nchk;
     return true;

@@ -25,6 +25,7 @@ struct AlphaParams {
   float sc2;
   size_t xlo;           // lo plane of split c (elements after cx)
   float* beta_out;      // [rows] column sums of L (exchange rows), or null
+  int causal;           // 0, or grid blocks per causal unit (L is zero past causal_key_end)
 };
 
 template <typename T, int D, bool PRECISE>
@@ -113,6 +114,7 @@ __global__ __launch_bounds__(THREADS) void alpha_kernel(AlphaParams p) {
         const int qq = n * 16 + 4 * g + r;
         float lv = __builtin_amdgcn_exp2f(sacc[r] * p.sc2 + hk - lq[qq]);
         if (!kvalid || qq >= nq) lv = 0.f;
+        if (p.causal && key >= causal_key_end(t * p.rt + q0 + qq, p.causal, p.b1, p.c2)) lv = 0.f;
         if (p.L_out && kvalid && qq < nq)
           p.L_out[(((size_t)sl * p.b2 + i) * p.b1 + t * p.rt + q0 + qq) * p.nkeys + key] = lv;
         if (KPL == 8 && !SPLIT) lv = (float)(bf16)lv;   // the value the MFMA consumes

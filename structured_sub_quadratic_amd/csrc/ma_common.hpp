@@ -34,6 +34,17 @@ __device__ inline size_t x_base(int b1, int b2, int c1, int c2, int sl, int t, i
 }
 __device__ inline size_t x_stride(int b2, int c1) { return (size_t)c1 * b2; }
 
+// Block-causal use: query row l (grid row) attends to key block k iff
+// floor(k / causal) <= floor(l / causal), i.e. to the stage-2 keys
+// kk = k*c2 + s below causal_key_end(l); causal = 0 allows every key.
+// (MonarchAttention scime summary "Limitations": causal masking does not fit
+// the method at token level; MonarchRT summary: autoregressive video, causal
+// across chunks of frames.  A mask over whole blocks keeps every block rank
+// one.)
+__device__ inline int causal_key_end(int l, int causal, int b1, int c2) {
+  return (causal ? min(b1, (l / causal + 1) * causal) : b1) * c2;
+}
+
 // K/V slice of query slice sl (= batch * heads + head) when groups of `group`
 // consecutive query heads share one K/V head.
 __device__ inline int kv_slice(int sl, int heads, int group) {

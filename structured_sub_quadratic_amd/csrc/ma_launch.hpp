@@ -106,7 +106,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           p1.group = pl.group;
           Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
                           S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
-                          pl.sc2, pl.xlo};
+                          pl.sc2, pl.xlo, pl.causal};
           const size_t items = std::max<size_t>((size_t)S * pl.b1 * p1.nqg, (size_t)S * pl.b2 * p2.nqg);
           void* args[] = {&p1, &p2};
           hipError_t e = hipSuccess;
@@ -136,7 +136,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const int nq2 = stage2_nq<T, D>(pl.rt), qg2 = WAVES * nq2 * 16;
       Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
                       S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg2 - 1) / qg2,
-                      pl.sc2, pl.xlo};
+                      pl.sc2, pl.xlo, pl.causal};
       const size_t items = std::max<size_t>(std::max<size_t>((size_t)S * pl.c1 * pl.b2,
                                                              (size_t)S * pl.b1 * p1.nqg),
                                             (size_t)S * pl.b2 * pl.c1 * p2.nqg);
@@ -286,7 +286,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           const int nw = stage2_waves<D>(pl.rt), qg = nw * 16;
           Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
-                         pl.sc2, pl.xlo};
+                         pl.sc2, pl.xlo, pl.causal};
           const size_t items = (size_t)S * pl.b2 * pl.c1 * p.nqg;
           const bool last = kind == L_STAGE2_LAST;
 #define MA_A2(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE>, NW * WAVE, items, p, st)
@@ -305,7 +305,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       const int qg = WAVES * nq * 16;
       Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                      S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
-                     pl.sc2, pl.xlo};
+                     pl.sc2, pl.xlo, pl.causal};
       const bool last = kind == L_STAGE2_LAST;
       if (pl.padded) {     // one build: one query sub-tile a wave
         p.nqg = (pl.rt + WAVES * 16 - 1) / (WAVES * 16);
@@ -346,6 +346,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
                     S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, nkeys, (nkeys + KT - 1) / KT, pl.sc2,
                     pl.xlo};
       p.beta_out = kind == L_ALPHA && pl.beta_out ? reinterpret_cast<float*>(ws + pl.off_beta) : nullptr;
+      p.causal = pl.causal;
       const size_t wgs = (size_t)S * pl.b2 * pl.c1 * p.nkt;
       hipLaunchKernelGGL((alpha_kernel<T, D, PRECISE>), dim3(grid1(wgs)), dim3(THREADS), 0, st, p);
       break;

@@ -45,6 +45,7 @@ struct Plan {
   bool need_qbar, need_qtil;
   bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1
+  int causal;        // 0, or grid blocks per causal unit when that masks anything (< b1)
 };
 
 // The plan of step t of a T > 1 backward: the forward kernels read and write

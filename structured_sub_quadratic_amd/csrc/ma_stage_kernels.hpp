@@ -57,6 +57,7 @@ struct FlashCore {
     else return s2;
   }
   float m[NQ], l[NQ], e[NQ], sref[NQ];
+  int qlim[NQ];           // QLIM steps: keys at or past qlim[n] (tile-local) are masked for query n
   bool fresh;             // no key seen since init()
 
   __device__ inline void init() {
@@ -216,7 +217,10 @@ struct FlashCore {
     }
   }
 
-  template <bool HAS_BIAS, bool MASK, int B = 0>
+  // QLIM (with MASK): each query n also masks the keys at or past qlim[n]
+  // (block-causal use: the keys a query row may attend to end at a bound of
+  // its own); the first tile of every row must keep at least one key.
+  template <bool HAS_BIAS, bool MASK, int B = 0, bool QLIM = false>
   __device__ inline void softmax_step(const float* bias, float sc2, int klo, int khi) {
     f32x4 (&s)[NQ][MT] = buf<B>();
     constexpr float TAU = 8.f;
@@ -233,7 +237,7 @@ struct FlashCore {
           if constexpr (HAS_BIAS) z = fmaf(z, sc2, bias[mt * 16 + 4 * g + r]);
           if constexpr (MASK) {
             const int key = mt * 16 + 4 * g + r;
-            if (key < klo || key >= khi) z = MASKED;
+            if (key < klo || key >= khi || (QLIM && key >= qlim[n])) z = MASKED;
           }
           s[n][mt][r] = z;
           zs[4 * mt + r] = z;
@@ -608,7 +612,36 @@ struct Stage2Params {
   int S, N, b1, b2, c1, c2, rt, nkeys, nqg;
   float sc2;
   size_t xlo;                        // lo plane of split c (elements after cx)
+  int causal;                        // 0, or grid blocks per causal unit (causal_key_end)
 };
+
+// Block-causal use: how one wave treats the stage-2 key chunk [base, base +
+// nvalid) of row tile t.  Its query rows (within the tile) start at r0 and
+// row(n) is the row of this lane in sub-tile n.  Returns CH_SKIP when every
+// row of the wave ends before the chunk (nothing to compute), CH_ROWMASK
+// (core.qlim set to each row's bound relative to base) when the chunk
+// crosses the bound of one of them, CH_WHOLE otherwise.
+enum { CH_WHOLE = 0, CH_ROWMASK = 1, CH_SKIP = 2 };
+template <int NQ, class Core, class RowFn>
+__device__ inline int causal_chunk(Core& core, const Stage2Params& p, int t, int r0, RowFn row, int base,
+                                   int nvalid) {
+  if (!p.causal) return CH_WHOLE;
+  if (r0 >= p.rt) return CH_SKIP;      // no real row in this wave (results unused)
+  const int lo = causal_key_end(t * p.rt + r0, p.causal, p.b1, p.c2);
+  const int hi = causal_key_end(t * p.rt + min(r0 + NQ * 16, p.rt) - 1, p.causal, p.b1, p.c2);
+  if (base >= hi) return CH_SKIP;
+  if (base + nvalid <= lo) return CH_WHOLE;
+#pragma unroll
+  for (int n = 0; n < NQ; ++n)
+    core.qlim[n] = causal_key_end(t * p.rt + min(row(n), p.rt - 1), p.causal, p.b1, p.c2) - base;
+  return CH_ROWMASK;
+}
+
+// Keys the rows [r0, r1) of row tile t read: all, or (block-causal) those
+// below the bound of the last of them.
+__device__ inline int stage2_keys(const Stage2Params& p, int t, int r1) {
+  return p.causal ? causal_key_end(t * p.rt + min(r1, p.rt) - 1, p.causal, p.b1, p.c2) : p.nkeys;
+}
 
 template <typename T, int D, bool KLO, int KR = KT>
 struct alignas(16) Stage2Smem {
@@ -740,21 +773,29 @@ struct Stage2Item {
 
     Core core;
     core.init();
-    core.load_queries([&](int n) {
-      return stage2_qsrc<T, D, PAD>(p, sl, i, t, qg * QG + wave * NQ * 16 + n * 16 + lane % 16);
-    }, Q_INPUT, false);
+    auto row = [&](int n) { return qg * QG + wave * NQ * 16 + n * 16 + lane % 16; };
+    core.load_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, sl, i, t, row(n)); }, Q_INPUT, false);
 
-    for (int kt0 = 0; kt0 < p.nkeys; kt0 += KT) {
+    const int kmax = stage2_keys(p, t, qg * QG + QG);
+    for (int kt0 = 0; kt0 < kmax; kt0 += KT) {
       const int nvalid = min(KT, p.nkeys - kt0);
       __syncthreads();
       pf.store(sm);
       __syncthreads();
-      if (kt0 + KT < p.nkeys)
+      if (kt0 + KT < kmax)
         pf.load(C + (size_t)(kt0 + KT) * xs * D, p.xlo, U + (size_t)(kt0 + KT) * xs * D,
                 H + (size_t)(kt0 + KT) * xs, min(KT, p.nkeys - kt0 - KT), xs);
+      const int how = causal_chunk<NQ>(core, p, t, row(0) - lane % 16, row, kt0, nvalid);
+      if (how == CH_SKIP) continue;
       core.template scores<Smem::LDK>(sm.ks, sm.ks_lo, 0, Core::MT);
-      if (nvalid == KT) core.template update<Smem::LDV, true, false>(sm.vt, sm.bias, p.sc2, 0, nvalid);
-      else core.template update<Smem::LDV, true, true>(sm.vt, sm.bias, p.sc2, 0, nvalid);
+      if (how == CH_ROWMASK) {
+        core.template softmax_step<true, true, 0, true>(sm.bias, p.sc2, 0, nvalid);
+        if constexpr (WITH_PV) core.template pv<true>(typename Core::template PaddedVT<Smem::LDV>{sm.vt}, 0, nvalid);
+      } else if (nvalid == KT) {
+        core.template update<Smem::LDV, true, false>(sm.vt, sm.bias, p.sc2, 0, nvalid);
+      } else {
+        core.template update<Smem::LDV, true, true>(sm.vt, sm.bias, p.sc2, 0, nvalid);
+      }
     }
 
     float lse2[NQ], h2[NQ];
@@ -881,16 +922,25 @@ __global__ __launch_bounds__(THREADS, (persistent_waves<T, NQ, D>())) void stage
     __syncthreads();
     if (item + (int)gridDim.x < nitems) fetch(item + gridDim.x);
     core.init();
+    auto row = [&](int n) { return qg * QG + wave * NQ * 16 + n * 16 + lane % 16; };
 #pragma unroll
     for (int c0 = 0; c0 < KTB; c0 += KT) {
       if (c0 >= p.nkeys) continue;
+      const int nv = min(KT, p.nkeys - c0);
+      const int how = causal_chunk<NQ>(core, p, t, row(0) - lane % 16, row, c0, nv);
+      if (how == CH_SKIP) continue;
       const T (*vtc)[Smem::LDV] = reinterpret_cast<const T (*)[Smem::LDV]>(&sm.vt[0][c0]);
       core.template scores<Smem::LDK>(reinterpret_cast<const T (*)[Smem::LDK]>(&sm.ks[c0][0]),
                                       reinterpret_cast<const T (*)[Smem::LDK]>(&sm.ks_lo[KLO ? c0 : 0][0]),
                                       0, Core::MT);
-      const int nv = min(KT, p.nkeys - c0);
-      if (nv == KT) core.template update<Smem::LDV, true, false>(vtc, sm.bias + c0, p.sc2, 0, nv);
-      else core.template update<Smem::LDV, true, true>(vtc, sm.bias + c0, p.sc2, 0, nv);
+      if (how == CH_ROWMASK) {
+        core.template softmax_step<true, true, 0, true>(sm.bias + c0, p.sc2, 0, nv);
+        if constexpr (WITH_PV) core.template pv<true>(typename Core::template PaddedVT<Smem::LDV>{vtc}, 0, nv);
+      } else if (nv == KT) {
+        core.template update<Smem::LDV, true, false>(vtc, sm.bias + c0, p.sc2, 0, nv);
+      } else {
+        core.template update<Smem::LDV, true, true>(vtc, sm.bias + c0, p.sc2, 0, nv);
+      }
     }
     float lse2[NQ], h2[NQ];
     core.finish(lse2, h2, p.sc2);

@@ -24,7 +24,7 @@ ma_status validate_problem(const ma_problem* p) {
   } else if (grid != p->seq_len) {
     return MA_ERR_INVALID_ARGUMENT;
   }
-  if (p->steps < 1) return MA_ERR_INVALID_ARGUMENT;
+  if (p->steps < 1 || p->causal < 0) return MA_ERR_INVALID_ARGUMENT;
   if (!(std::isfinite(p->scale)) || p->scale < 0.f) return MA_ERR_INVALID_ARGUMENT;
   if (p->dtype != MA_F32 && p->dtype != MA_BF16) return MA_ERR_INVALID_ARGUMENT;
   if (p->layout < MA_LAYOUT_FLAT || p->layout > MA_LAYOUT_H_FW) return MA_ERR_INVALID_ARGUMENT;
@@ -91,6 +91,8 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
   pl.need_qbar_lp = pl.need_qbar && (p->c1 > 1 || pl.padded) && !pl.precise;
   pl.fused = !backward && p->steps == 1 && (p->flags & MA_FLAG_FORCE_FUSED) &&
              !(p->flags & MA_FLAG_FORCE_STAGED);
+  // a causal unit of at least b1 blocks masks nothing
+  pl.causal = p->causal < p->b1 ? p->causal : 0;
   const size_t rows = (size_t)pl.S * pl.G * pl.c1 * pl.c2;   // exchange rows
   size_t off = 0;
   pl.xlo = (pl.precise && p->dtype == MA_BF16) ? rows * pl.D : 0;
@@ -162,6 +164,12 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   const size_t kvbytes = tbytes / pl.group;
   if (overlaps(y, tbytes, q, tbytes) || overlaps(y, tbytes, k, kvbytes) || overlaps(y, tbytes, v, kvbytes))
     return MA_ERR_INVALID_ARGUMENT;
+  if (ex) {
+    if ((ex->L && misaligned(ex->L, 4)) || (ex->R && misaligned(ex->R, 4)) ||
+        (ex->lse && misaligned(ex->lse, 4)) || (ex->objective && misaligned(ex->objective, 8)))
+      return MA_ERR_INVALID_ARGUMENT;
+  }
+  if (n_events < 0) return MA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < pl.total) return MA_ERR_WORKSPACE_TOO_SMALL;
   if (pl.total > 0) {
     if (!workspace || misaligned(workspace, ALIGN)) return MA_ERR_INVALID_ARGUMENT;
@@ -170,13 +178,7 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
       return MA_ERR_INVALID_ARGUMENT;
   }
   Bufs b{q, k, v, y, static_cast<char*>(workspace), nullptr, nullptr, nullptr, nullptr};
-  if (ex) {
-    b.L = ex->L; b.R = ex->R; b.lse = ex->lse; b.obj = ex->objective;
-    if ((b.L && misaligned(b.L, 4)) || (b.R && misaligned(b.R, 4)) || (b.lse && misaligned(b.lse, 4)) ||
-        (b.obj && misaligned(b.obj, 8)))
-      return MA_ERR_INVALID_ARGUMENT;
-  }
-  if (n_events < 0) return MA_ERR_INVALID_ARGUMENT;
+  if (ex) { b.L = ex->L; b.R = ex->R; b.lse = ex->lse; b.obj = ex->objective; }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (pl.dtype == MA_BF16) {
     if (pl.D == 64)
@@ -197,6 +199,7 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
+  if (p->causal > 0 && p->causal < p->b1) return MA_ERR_UNSUPPORTED;   // forward only
   const bool tiled = p->c1 != 1 || p->c2 != 1;
   if (tiled && (p->steps > 1 || (int64_t)p->b1 * p->b2 != p->seq_len)) return MA_ERR_UNSUPPORTED;
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;

@@ -42,9 +42,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_problem_struct_layout_matches_header():
-    # int64 x4, int32 x5, float, int32 x5, uint32, int32 -> 32 + 20 + 4 + 20 + 4 + 4
-    # = 84, padded to the 8-byte alignment of the int64 fields
+    # int64 x4, int32 x5, float, int32 x5, uint32, int32 x2 -> 32 + 20 + 4 + 20 + 4 + 8
+    # = 88 (a multiple of the 8-byte alignment of the int64 fields)
     assert ctypes.sizeof(_lib.MAProblem) == 88
+    assert _lib.MAProblem.causal.offset == 84
     assert ctypes.sizeof(_lib.MAExports) == 32
 
 
@@ -71,6 +72,9 @@ def good(**kw):
     (dict(kv_heads=3), 1),                    # does not divide heads = 2
     (dict(kv_heads=4), 1),                    # more K/V heads than query heads
     (dict(kv_heads=1), 0),                    # grouped-query attention, valid
+    (dict(causal=1), 0),                      # block-causal use
+    (dict(causal=3, c1=2, c2=2, steps=2), 0),
+    (dict(causal=-2), 1),
     (dict(seq_len=250), 0),                   # flat sequence padded to the 16 x 16 grid
     (dict(seq_len=241), 0),                   # 15 padding positions < b2
     (dict(seq_len=240), 1),                   # a whole block of padding
@@ -161,6 +165,9 @@ def test_status_strings(lib):
     (dict(seq_len=96 * 96, b1=96, b2=96, head_dim=128, dtype="f32"), 2),   # fp32 d128: 64 max
     (dict(seq_len=64 * 64, b1=64, b2=64, head_dim=128, dtype="f32"), 0),
     (dict(steps=0), 1),
+    (dict(causal=1), 2),                      # block-causal: forward only
+    (dict(causal=16), 0),                     # a unit of all 16 blocks masks nothing
+    (dict(causal=-1), 1),
 ])
 def test_backward_validation(lib, kw, code):
     p = good(**kw)
@@ -197,3 +204,4 @@ def test_backward_reuse_forward_state_layouts(lib, kw, code):
     flags = kw.pop("flags", 0) | ma.MA_FLAG_REUSE_FORWARD_STATE
     p = good(flags=flags, **kw)
     assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == code
+

@@ -39,6 +39,7 @@ def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective
     if kv_heads is not None:        # grouped-query attention: keep the first kv_heads
         K, V = (np.ascontiguousarray(X[:, :kv_heads]) for X in (K, V))
     group = cfg.heads // K.shape[1]
+    causal = kw.get("causal", 0)
     y, ex = run_hip(cfg, Q, K, V, exports=exports, **kw)
     tiled = cfg.c1 * cfg.c2 > 1
     tol = TOL[cfg.dtype] if tol is None else tol
@@ -47,7 +48,7 @@ def check_case(cfg, slices=None, cols=None, exports=("L", "R", "lse", "objective
         hk = h // group
         ref = oracle.forward(Q[b:b + 1, h:h + 1], K[b:b + 1, hk:hk + 1], V[b:b + 1, hk:hk + 1],
                              cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
-                             fhw=cfg.fhw, cols=cols, pad=cfg.pad)
+                             fhw=cfg.fhw, cols=cols, pad=cfg.pad, causal=causal)
         one = [(0, 0)]
         tok = ref["grid"][:, ref["cols"]].reshape(-1)
         tok = tok[tok >= 0]                 # padding positions have no token
@@ -407,3 +408,80 @@ def test_error_vs_exact_attention_reported(key):
     print(f"{cfg.name}: ||Y - Y_exact|| / ||Y_exact|| = {err:.4f} over "
           f"{'all' if rows.size == cfg.seq_len else rows.size} rows per head")
     assert np.isfinite(err) and err < 1.0
+
+
+# ------------------------------------------------ block-causal use
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="f32", d=64, b1=16, b2=16, g=1, c=(1, 1), steps=1),
+    dict(dtype="f32", d=128, b1=40, b2=48, g=3, c=(2, 1), steps=2),
+    dict(dtype="bf16", d=64, b1=70, b2=52, g=1, c=(1, 1), steps=1),
+    dict(dtype="bf16", d=64, b1=130, b2=40, g=1, c=(1, 1), steps=1),      # stage-2 columns of 3 chunks
+    dict(dtype="bf16", d=128, b1=70, b2=52, g=5, c=(1, 1), steps=2),
+    dict(dtype="bf16", d=64, b1=70, b2=52, g=2, c=(2, 2), steps=1),
+    dict(dtype="bf16", d=64, b1=70, b2=52, g=1, c=(5, 2), steps=3),
+    dict(dtype="bf16", d=128, b1=24, b2=100, g=4, c=(1, 1), steps=1),
+    dict(dtype="bf16", d=64, b1=96, b2=40, g=7, c=(1, 1), steps=3),
+])
+def test_block_causal(case):
+    """Block-causal use: query block l attends to key block k iff
+    floor(k/g) <= floor(l/g); every output against the oracle, staged and,
+    for T = 1, fused."""
+    cfg = WorkloadConfig("case", f"causal {case}", batch=2, heads=2, seq_len=case["b1"] * case["b2"],
+                         head_dim=case["d"], b1=case["b1"], b2=case["b2"], steps=case["steps"],
+                         dtype=case["dtype"], data="normed", seed=71, c1=case["c"][0], c2=case["c"][1])
+    y, _, _ = check_case(cfg, causal=case["g"])
+    if case["steps"] == 1:
+        y_f, _, _ = check_case(cfg, causal=case["g"], force_fused=True)
+        assert np.abs(y_f - y).max() <= 1e-6 * np.abs(y).max()
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+def test_block_causal_padded(pad):
+    cfg = WorkloadConfig("case", f"causal pad={pad}", batch=1, heads=3, seq_len=197, head_dim=64,
+                         b1=15, b2=14, steps=2, dtype="bf16", data="iid", seed=73, pad=pad)
+    check_case(cfg, causal=1)
+
+
+def test_block_causal_one_token_blocks_is_causal_attention():
+    """b2 = 1 with g = 1 is token-causal softmax attention, on the GPU as in
+    the oracle (compared with the masked exact product here)."""
+    cfg = WorkloadConfig("case", "causal b2=1", batch=1, heads=2, seq_len=300, head_dim=64, b1=300,
+                         b2=1, steps=2, dtype="f32", data="iid", seed=74)
+    Q, K, V = make_inputs(cfg)
+    y, _ = run_hip(cfg, Q, K, V, exports=(), causal=1)
+    for h in range(2):
+        q, k, v = (X[0, h].astype(np.float64) for X in (Q, K, V))
+        s_ = q @ k.T / 8.0
+        s_ = np.where(np.tril(np.ones((300, 300), bool)), s_, -np.inf)
+        p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        ex = (p_ @ v) / p_.sum(axis=1, keepdims=True)
+        assert np.abs(y[0, h] - ex).max() / np.abs(ex).max() < 1e-4
+
+
+def test_block_causal_n16k_full():
+    """The headline shape with the block-causal mask over its 128 blocks:
+    every slice, every column, every export."""
+    check_case(WORKLOADS["n16k"], causal=1)
+
+
+def test_block_causal_video_frame_causal_sampled():
+    """The video latent, frame-causal (g = h = 30 grid blocks per frame):
+    two slices, all 52 columns."""
+    check_case(WORKLOADS["video"], slices=[(0, 0), (0, 7)], causal=30)
+
+
+def test_block_causal_video_codes_exact_without_noise():
+    """Zero-noise per-axis codes: one step reproduces frame-causal softmax
+    attention exactly on the (fh, w) layout with g = h."""
+    cfg = WorkloadConfig("case", "video frame-causal exact", batch=1, heads=1, seq_len=3 * 4 * 10,
+                         head_dim=64, b1=12, b2=10, steps=1, dtype="f32", data="video", seed=15,
+                         layout="fh_w", fhw=(3, 4, 10))
+    Q, K, V = make_inputs(cfg, noise_scale=0.0)
+    y, _ = run_hip(cfg, Q, K, V, exports=(), causal=4)
+    q, k, v = (X[0, 0].astype(np.float64) for X in (Q, K, V))
+    frame = np.arange(120) // 40
+    s_ = np.where(frame[None, :] <= frame[:, None], q @ k.T / 8.0, -np.inf)
+    p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
+    ex = (p_ @ v) / p_.sum(axis=1, keepdims=True)
+    assert np.abs(y[0, 0] - ex).max() / np.abs(ex).max() < 1e-4

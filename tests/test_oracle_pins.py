@@ -951,3 +951,225 @@ def test_backward_single_block_is_exact_attention_grad(pad, N):
         (y * torch.as_tensor(dY)).sum().backward()
         for a, b in ((dQ, q.grad), (dK, k.grad), (dV, v.grad)):
             np.testing.assert_allclose(a, b.numpy(), atol=1e-12, rtol=0)
+
+
+# ------------------------------------------------------- P12 block-causal use
+#
+# Reading: query block l attends to key block k iff floor(k/g) <= floor(l/g)
+# (g grid blocks per causal unit), so M is zero outside those blocks and the
+# objective runs over the allowed entries.  The pins below build the allowed
+# set from token indices (never from oracle.causal_allowed) and check the
+# oracle against torch's masked attention, exact masked softmax on separable
+# scores, the masked dense objective and a generic maximiser.
+
+def token_mask_flat(N, b2, g):
+    """allowed[n, n'] for a flat sequence: token n sits in block n // b2, and
+    the blocks form causal units of g blocks."""
+    unit = (np.arange(N) // b2) // g
+    return unit[None, :] <= unit[:, None]
+
+
+def masked_sdpa(q, k, v, scale, allowed):
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=torch.from_numpy(allowed)[None], scale=scale)
+    return ref[0].numpy()
+
+
+@pytest.mark.parametrize("g", [1, 3])
+@pytest.mark.parametrize("steps", [1, 2, 3])
+def test_causal_one_token_blocks_is_causal_attention(g, steps):
+    """b2 = 1: every block is one token, the Monarch set is all of attention,
+    and the block-causal mask is token-causal (g = 1) or causal over chunks of
+    g tokens: Y equals torch's masked softmax attention."""
+    rng = np.random.default_rng(31 + g + steps)
+    N, d = 12, 4
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    scale = 0.8
+    r = om.forward_untiled(q.reshape(N, 1, d), k.reshape(N, 1, d), v.reshape(N, 1, d), steps,
+                           scale, causal=g)
+    if g == 1:
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+            is_causal=True, scale=scale)[0].numpy()
+    else:
+        ref = masked_sdpa(q, k, v, scale, token_mask_flat(N, 1, g))
+    np.testing.assert_allclose(r["y"].reshape(N, d), ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("g", [1, 2])
+def test_causal_single_block_and_wide_units(g):
+    """One block (b1 = 1) has nothing to mask: dense attention.  A causal unit
+    covering the whole grid (g >= b1) masks nothing: the bidirectional result,
+    bit for bit."""
+    rng = np.random.default_rng(7 + g)
+    qg, kg, vg = rand_qkv(rng, 1, 9, 4)
+    r = om.forward_untiled(qg, kg, vg, 2, 0.9, causal=g)
+    ex = oracle.exact_attention(qg[0], kg[0], vg[0], 0.9)
+    np.testing.assert_allclose(r["y"][0], ex, atol=1e-12, rtol=0)
+    qg, kg, vg = rand_qkv(rng, 4, 6, 5)
+    for fn, extra in ((om.forward_untiled, ()), (om.forward_tiled, (2, 3))):
+        a = fn(qg, kg, vg, 3, 0.7, *extra, causal=4)
+        b = fn(qg, kg, vg, 3, 0.7, *extra)
+        for key in ("y", "L", "R", "lse", "f_trace"):
+            assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("b1,b2,g", [(4, 3, 1), (6, 2, 2), (5, 4, 1)])
+@pytest.mark.parametrize("tiles", [None, (1, 2), (2, 1)])
+def test_causal_separable_scores_exact(b1, b2, g, tiles):
+    """Separable scores S = x(i,l,k) + y(k,i,j): one step reproduces the
+    masked softmax of S exactly (the allowed set built from token indices),
+    also tiled.  A mask of the wrong direction, or no mask, fails this."""
+    if tiles and (b1 % tiles[0] or b2 % tiles[1]):
+        pytest.skip("tiles must divide")
+    rng = np.random.default_rng(b1 * 13 + b2 + g)
+    x = 2.0 * rng.standard_normal((b2, b1, b1))
+    y = 2.0 * rng.standard_normal((b1, b2, b2))
+    qg, kg = separable_qk(x, y)
+    vg = rng.standard_normal((b1, b2, 3))
+    S = dense_scores(qg, kg, 1.0)
+    allowed = token_mask_flat(b1 * b2, b2, g)
+    A = oracle.softmax(np.where(allowed, S, -np.inf), axis=-1)
+    if tiles is None:
+        r = om.forward_untiled(qg, kg, vg, 1, 1.0, causal=g)
+        M = om.dense_from_factors(r["L"], r["R"], b1, b2)
+    else:
+        r = om.forward_tiled(qg, kg, vg, 1, 1.0, *tiles, causal=g)
+        M = om.dense_from_factors(r["L"], r["R"], b1, b2, *tiles)
+    np.testing.assert_allclose(M, A, atol=1e-12, rtol=0)
+    assert np.all(M[~allowed] == 0.0)
+    np.testing.assert_allclose(r["y"].reshape(-1, 3), A @ vg.reshape(-1, 3), atol=1e-12)
+    # logsumexp of the last L-update = logsumexp of the masked scores of the row
+    np.testing.assert_allclose(r["lse"].reshape(-1),
+                               oracle.logsumexp(np.where(allowed, S, -np.inf), axis=-1),
+                               atol=1e-12)
+
+
+def test_causal_video_frame_causal_exact():
+    """The (fh, w) layout of an f x h x w latent with g = h grid blocks per
+    unit is frame-causal: token (f, h, w) attends to every token of frames
+    f' <= f.  Additive per-axis scores are reproduced exactly in one step
+    (the frame mask built from the latent coordinates)."""
+    fhw = (3, 4, 5)
+    f, h, w = fhw
+    rng = np.random.default_rng(17)
+    q, k = axis_score_qkv(rng, fhw)
+    N = q.shape[0]
+    v = rng.standard_normal((N, 3))
+    frame = np.arange(N) // (h * w)
+    allowed = frame[None, :] <= frame[:, None]
+    S = q @ k.T
+    exact = oracle.softmax(np.where(allowed, S, -np.inf), axis=-1) @ v
+    Q, K, V = (x[None, None] for x in (q, k, v))
+    for tiled in (False, True):
+        r = om.forward(Q, K, V, f * h, w, 1, scale=1.0, layout="fh_w", fhw=fhw, causal=h,
+                       tiled=tiled)
+        np.testing.assert_allclose(r["y"][0, 0], exact, atol=1e-11)
+    # the (f, hw) layout with one frame per block and g = 1 is the same mask
+    r = om.forward(Q, K, V, f, h * w, 1, scale=1.0, layout="f_hw", fhw=fhw, causal=1)
+    np.testing.assert_allclose(r["y"][0, 0], exact, atol=1e-11)
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("pad", [None, "pre", "post"])
+def test_causal_objective_monotone_and_masked_dense(tiled, pad):
+    """Over the half-steps the masked objective is non-decreasing, equals the
+    dense objective of M (restricted to real rows and keys) and stays below
+    sum logsumexp of the masked scores; M has no mass on masked entries."""
+    rng = np.random.default_rng(41 + tiled)
+    b1, b2, d, T, g = 6, 4, 5, 4, 2
+    c1, c2 = (2, 2) if tiled else (1, 1)
+    N = b1 * b2 - (1 if pad else 0)
+    q, k, v = (1.5 * rng.standard_normal((N, d)) for _ in range(3))
+    grid = oracle.grid_index(N, b1, b2, "flat", None, pad or "post")
+    real = grid >= 0
+    qg, kg, vg = (oracle.to_grid(x, grid) for x in (q, k, v))
+    scale = 0.7
+    fn = (lambda *a, **kw: om.forward_tiled(*a, c1, c2, **kw)) if tiled else om.forward_untiled
+    r = fn(qg, kg, vg, T, scale, history=True, real=real, causal=g)
+    ft = r["f_trace"]
+    assert np.all(np.diff(ft) >= -1e-10 * np.abs(ft).max())
+    # dense masked scores over real tokens, in grid order
+    idx = np.nonzero(real.reshape(-1))[0]
+    S = dense_scores(qg, kg, scale)
+    allowed = token_mask_flat(b1 * b2, b2, g)
+    Sm = np.where(allowed, S, -np.inf)[np.ix_(idx, idx)]
+    bound = oracle.logsumexp(Sm, axis=-1).sum()
+    assert ft.max() <= bound + 1e-10
+    for (L, R), fv in zip(r["history"], ft):
+        M = om.dense_from_factors(L, R, b1, b2, c1, c2)
+        assert np.all(M[~allowed] == 0.0)
+        Mr = M[np.ix_(idx, idx)]
+        dense = float(np.sum(np.where(Mr > 0, Mr * S[np.ix_(idx, idx)], 0.0))
+                      + np.sum(oracle.row_entropy(Mr, axis=-1)))
+        assert abs(dense - fv) <= 1e-10 * abs(fv) + 1e-12
+
+
+@pytest.mark.parametrize("b1,b2,c1,c2,g", [(3, 2, 1, 1, 1), (4, 2, 1, 1, 2), (4, 2, 2, 1, 1),
+                                            (2, 4, 1, 2, 1)])
+def test_causal_half_steps_are_argmax(b1, b2, c1, c2, g):
+    """Step 2's R-update and L-update equal a generic numerical maximiser of
+    the dense objective over that factor, L restricted to the allowed blocks
+    (its logits at masked blocks fixed at -inf), no closed form used."""
+    rng = np.random.default_rng(b1 * 5 + b2 + g + c1 * c2)
+    qg, kg, vg = rand_qkv(rng, b1, b2, 3)
+    scale = 0.9
+    if c1 * c2 > 1:
+        r = om.forward_tiled(qg, kg, vg, 2, scale, c1, c2, history=True, causal=g)
+    else:
+        r = om.forward_untiled(qg, kg, vg, 2, scale, history=True, causal=g)
+    hist = r["history"]
+    S = torch.from_numpy(dense_scores(qg, kg, scale))
+    blk = np.arange(b1) // g
+    allow = torch.from_numpy(np.repeat((blk[None, :] <= blk[:, None])[:, :, None], c2, axis=2)
+                             .reshape(b1, b1 * c2))        # [l, (k, s)]
+
+    def as4(L, R):
+        L = L if L.ndim == 4 else L[..., None]
+        R = R if R.ndim == 4 else R[:, :, None, :]
+        return torch.from_numpy(L), torch.from_numpy(R)
+
+    L1, _ = as4(*hist[1])
+    _, R2 = as4(*hist[2])
+    sw = b2 // c2
+
+    # token-level allowed set in grid order (the entry formula's M is zero
+    # outside it); the entropy is taken over allowed entries only, with the
+    # masked ones held at a constant so that x log x has a finite gradient
+    allowed_t = torch.from_numpy(token_mask_flat(b1 * b2, b2, g))
+
+    def f_masked(Lt, Rt):
+        tile = torch.as_tensor(om.tile_of_rows(b1, c1))
+        seg = torch.as_tensor(om.segment_of_cols(b2, c2))
+        M = (Lt[:, :, :, seg].permute(1, 0, 2, 3) * Rt[:, :, tile, :].permute(2, 1, 0, 3)) \
+            .reshape(b1 * b2, b1 * b2)
+        Ms = torch.where(allowed_t, M, torch.ones_like(M))
+        return (M * S).sum() - torch.special.xlogy(Ms, Ms).sum()
+
+    def f_of_R(theta):
+        Rt = torch.softmax(theta.reshape(b1, b2, c1, c2, sw), dim=-1).reshape(b1, b2, c1, b2)
+        return f_masked(L1, Rt)
+    th = _maximise(f_of_R, (b1, b2, c1, b2), 0)
+    R_num = torch.softmax(th.reshape(b1, b2, c1, c2, sw), dim=-1).reshape(b1, b2, c1, b2)
+    # a sub-row (k, i, t) that no row of tile t may reach carries no weight
+    # in L, so the objective does not determine it (the oracle takes the
+    # tile-mean fallback there): compare the determined sub-rows
+    tile = om.tile_of_rows(b1, c1)
+    weight = np.zeros((b1, b2, c1))                       # [k, i, t]
+    for t in range(c1):
+        weight[:, :, t] = L1.numpy()[:, tile == t].sum(axis=(1, 3)).T
+    det = np.repeat((weight > 0)[..., None], b2, axis=-1)
+    assert det.any()
+    np.testing.assert_allclose(R_num.numpy()[det], R2.numpy()[det], atol=2e-6)
+
+    L2, _ = as4(*hist[3])
+
+    def f_of_L(theta):
+        logits = theta.reshape(b2, b1, b1 * c2).masked_fill(~allow[None], float("-inf"))
+        Lt = torch.softmax(logits, dim=-1).reshape(b2, b1, b1, c2)
+        return f_masked(Lt, R2)
+    th = _maximise(f_of_L, (b2, b1, b1 * c2), 1)
+    logits = th.reshape(b2, b1, b1 * c2).masked_fill(~allow[None], float("-inf"))
+    L_num = torch.softmax(logits, dim=-1).reshape(b2, b1, b1, c2)
+    np.testing.assert_allclose(L_num.numpy(), L2.numpy(), atol=2e-6)
