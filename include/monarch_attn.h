@@ -193,6 +193,32 @@ ma_status monarch_attn_forward(const ma_problem* p, const void* q, const void* k
                                const void* v, void* y, const ma_exports* exports,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the library-owned device workspace of monarch_attn_forward_noalloc
+ * (one array per GPU the library runs on, held until the process ends). */
+#define MONARCH_ATTN_SCRATCH_BYTES (64u << 20)
+
+/* monarch_attn_forward without a workspace argument and without allocating,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It runs
+ * the same kernels as monarch_attn_forward, with the workspace taken from a
+ * fixed device array of MONARCH_ATTN_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on (looked up on the first call on each device); it
+ * calls no hipMalloc, hipFree or other allocating routine.  The caller still
+ * passes Q, K, V, Y and the optional exports, with the same rules as
+ * monarch_attn_forward.
+ * Returns MA_ERR_WORKSPACE_TOO_SMALL, with nothing launched, for a problem
+ * whose workspace (monarch_attn_workspace_size) exceeds
+ * MONARCH_ATTN_SCRATCH_BYTES (the 12-head, 16384-token, head_dim 64 bf16
+ * problem needs 53 MB and fits), and MA_ERR_UNSUPPORTED with
+ * MA_FLAG_FORCE_FUSED (the cooperative launch's grid barrier keeps state of
+ * the runtime's own).  The array keeps what the last call left; nothing in
+ * it has to start at zero.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one device (other streams, other host threads)
+ * race, and the caller must order them. */
+ma_status monarch_attn_forward_noalloc(const ma_problem* p, const void* q, const void* k,
+                                       const void* v, void* y, const ma_exports* exports,
+                                       void* stream);
+
 /* Number of kernel launches monarch_attn_forward makes for *p (host only),
  * or -1 for an invalid problem. */
 int32_t monarch_attn_num_launches(const ma_problem* p);

@@ -19,7 +19,7 @@ from ._lib import (MonarchAttnError, LAYOUTS, MA_FLAG_FORCE_STAGED, MA_FLAG_FAST
                    MA_FLAG_FORCE_FUSED, MA_FLAG_PRECISE_AGGREGATE, MA_FLAG_PAD_FRONT,
                    MA_FLAG_REUSE_FORWARD_STATE)
 
-__all__ = ["forward", "forward_timed", "backward", "make_problem",
+__all__ = ["forward", "forward_timed", "forward_noalloc", "backward", "make_problem",
            "workspace_size",
            "backward_workspace_size", "num_launches", "launch_names", "Event",
            "MonarchAttnError", "LAYOUTS", "library_path", "version"]
@@ -193,6 +193,39 @@ def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layo
         ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         ctypes.byref(cex), workspace.data_ptr(), workspace.numel(), st, arr, len(events))
     _lib.check(status, "monarch_attn_forward_timed")
+    return out
+
+
+def forward_noalloc(q, k, v, b1, b2, out, steps=1, c1=1, c2=1, scale=None, layout="flat",
+                    fhw=None, exports=None, fast_aggregate=False, precise_aggregate=False,
+                    pad="post", causal=0):
+    """forward() through monarch_attn_forward_noalloc: no workspace argument
+    and no allocation (the library's own per-device scratch array serves as
+    the workspace; problems whose workspace exceeds
+    MONARCH_ATTN_SCRATCH_BYTES raise MonarchAttnError).  The caller passes
+    the output `out` (shaped like q) and, optionally, `exports`, a dict of
+    preallocated export tensors ("L", "R", "lse", "objective", shaped as in
+    forward()).  Calls that overlap on one device share that array."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d HIP device tensor")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be shaped and typed like q")
+    B, H, N, D = q.shape
+    flags = (MA_FLAG_FAST_AGGREGATE if fast_aggregate else 0) | \
+        (MA_FLAG_PRECISE_AGGREGATE if precise_aggregate else 0) | \
+        (MA_FLAG_PAD_FRONT if pad == "pre" else 0)
+    prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags,
+                        kv_heads=k.shape[1], causal=causal)
+    ex = exports or {}
+    cex = _lib.MAExports(*(ex[n].data_ptr() if n in ex else None
+                           for n in ("L", "R", "lse", "objective")))
+    st = torch.cuda.current_stream(q.device).cuda_stream
+    status = _lib.load().monarch_attn_forward_noalloc(
+        ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        ctypes.byref(cex), st)
+    _lib.check(status, "monarch_attn_forward_noalloc")
     return out
 
 

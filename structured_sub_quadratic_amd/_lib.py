@@ -17,6 +17,7 @@ MA_FLAG_FORCE_FUSED = 4
 MA_FLAG_PRECISE_AGGREGATE = 8
 MA_FLAG_PAD_FRONT = 16
 MA_FLAG_REUSE_FORWARD_STATE = 32
+MONARCH_ATTN_SCRATCH_BYTES = 64 << 20   # the library-owned workspace of the no-alloc entry point
 
 
 class MAProblem(ctypes.Structure):
@@ -68,6 +69,8 @@ def load():
     lib.monarch_attn_forward.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(MAExports), vp,
                                          ctypes.c_size_t, vp]
     lib.monarch_attn_forward.restype = ctypes.c_int
+    lib.monarch_attn_forward_noalloc.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(MAExports), vp]
+    lib.monarch_attn_forward_noalloc.restype = ctypes.c_int
     lib.monarch_attn_forward_timed.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(MAExports), vp,
                                                ctypes.c_size_t, vp, ctypes.POINTER(vp),
                                                ctypes.c_int32]

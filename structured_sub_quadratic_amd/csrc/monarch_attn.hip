@@ -6,10 +6,39 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
+
+// Workspace of monarch_attn_forward_noalloc: one fixed device array, which
+// every GPU the library runs on holds (its own copy, at its own address)
+// from the load of this code object until the process ends.  In host code
+// `scratch` is a host-side stand-in, never a device address: the device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is passed on.
+static __device__ __align__(256) char scratch[MONARCH_ATTN_SCRATCH_BYTES];
 
 namespace {
 
 using namespace ma;
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_at[MAX_DEVICES];      // device address of `scratch` per device, or null
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+ma_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MA_ERR_DEVICE;
+  if (dev < 0 || dev >= MAX_DEVICES) return MA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_at[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MA_ERR_DEVICE;
+    scratch_at[dev] = ptr;
+  }
+  *out = scratch_at[dev];
+  return MA_OK;
+}
 
 ma_status validate_problem(const ma_problem* p) {
   if (!p) return MA_ERR_INVALID_ARGUMENT;
@@ -150,12 +179,20 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// use_scratch: the workspace is the current device's scratch array (looked
+// up after every other host check), not the caller's buffer
 ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const void* v, void* y,
                        const ma_exports* ex, void* workspace, size_t workspace_bytes, void* stream,
-                       void* const* events, int32_t n_events) {
+                       void* const* events, int32_t n_events, bool use_scratch = false) {
   ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
   const Plan pl = make_plan(p);
+  if (use_scratch) {
+    // the cooperative launch's grid barrier keeps runtime-owned state
+    if (pl.fused) return MA_ERR_UNSUPPORTED;
+    if (pl.total > MONARCH_ATTN_SCRATCH_BYTES) return MA_ERR_WORKSPACE_TOO_SMALL;
+    workspace_bytes = MONARCH_ATTN_SCRATCH_BYTES;
+  }
   if (!q || !k || !v || !y) return MA_ERR_INVALID_ARGUMENT;
   auto misaligned = [](const void* x, uintptr_t a) { return ((uintptr_t)x % a) != 0; };
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(y, 16))
@@ -170,6 +207,7 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
       return MA_ERR_INVALID_ARGUMENT;
   }
   if (n_events < 0) return MA_ERR_INVALID_ARGUMENT;
+  if (use_scratch && (s = device_scratch(&workspace)) != MA_OK) return s;
   if (workspace_bytes < pl.total) return MA_ERR_WORKSPACE_TOO_SMALL;
   if (pl.total > 0) {
     if (!workspace || misaligned(workspace, ALIGN)) return MA_ERR_INVALID_ARGUMENT;
@@ -287,6 +325,12 @@ ma_status monarch_attn_forward(const ma_problem* p, const void* q, const void* k
                                void* y, const ma_exports* exports, void* workspace,
                                size_t workspace_bytes, void* stream) {
   return forward_impl(p, q, k, v, y, exports, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+ma_status monarch_attn_forward_noalloc(const ma_problem* p, const void* q, const void* k,
+                                       const void* v, void* y, const ma_exports* exports,
+                                       void* stream) {
+  return forward_impl(p, q, k, v, y, exports, nullptr, 0, stream, nullptr, 0, true);
 }
 
 ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const void* k, const void* v,

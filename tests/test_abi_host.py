@@ -205,3 +205,22 @@ def test_backward_reuse_forward_state_layouts(lib, kw, code):
     p = good(flags=flags, **kw)
     assert lib.monarch_attn_backward(ctypes.byref(p), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == code
 
+
+def test_noalloc_scratch_size_and_host_refusals(lib):
+    """The no-alloc entry point's scratch size in the header matches the
+    binding, and problems it cannot take are refused on the host, before any
+    HIP call: a workspace larger than the scratch array, the fused launch,
+    and invalid problems."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+MONARCH_ATTN_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.MONARCH_ATTN_SCRATCH_BYTES
+    q, k, v, y = (256 * 1024 * 1024 * (j + 1) for j in range(4))
+    video = ma.make_problem(1, 12, 32760, 128, 630, 52, dtype="bf16", layout="fh_w", fhw=(21, 30, 52))
+    assert ma.workspace_size(video) > _lib.MONARCH_ATTN_SCRATCH_BYTES
+    assert lib.monarch_attn_forward_noalloc(ctypes.byref(video), q, k, v, y, None, None) == 3
+    fused = good(flags=ma.MA_FLAG_FORCE_FUSED)
+    assert lib.monarch_attn_forward_noalloc(ctypes.byref(fused), q, k, v, y, None, None) == 2
+    assert lib.monarch_attn_forward_noalloc(ctypes.byref(good(steps=0)), q, k, v, y, None, None) == 1
+    assert lib.monarch_attn_forward_noalloc(ctypes.byref(good()), 0, k, v, y, None, None) == 1
+    n16k = ma.make_problem(1, 12, 16384, 64, 128, 128, dtype="bf16")
+    assert ma.workspace_size(n16k) <= _lib.MONARCH_ATTN_SCRATCH_BYTES
