@@ -44,6 +44,8 @@ struct BwdParams {
   const float* h2x;                 // entropy (bits), one per exchange row
   const float* lse2;                // stage-2 row normaliser (base 2), [S, b2, b1]
   float* dq2;                       // [S, N, D] stage-2 part of dQ, token order
+  float* dq2p;                      // columns of several key chunks: one [S, N, D] part per
+                                    // chunk (summed into dq2 in chunk order), else null
   float* dcx; float* dux;           // [rows, D] gradients of c and u
   float* dhx;                       // [rows] gradient of H_R (nats)
   float* dkp; float* dvp;           // [S, N, D] per-query-head dK, dV (grouped K/V), or null
@@ -376,6 +378,11 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   __shared__ __attribute__((aligned(16))) float ps[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dws[RB * LDP];
   __shared__ float h2k[NB], dhk[NB], lsel[RB], dl[RB];
+  // row sums of P dP per score strip (key strips of a row tile) go to the
+  // padding columns NB .. NB + 3 of ps (which nothing else reads) and are
+  // added up in strip order afterwards, so the sums do not depend on wave
+  // timing
+  static_assert(NB / (16 * NG) <= LDP - NB, "one padding column per key strip");
   constexpr bool RS = MODE == S2_ROWSUM;   // D-only workgroup: RG row chunks stay in LDS
   __shared__ __attribute__((aligned(16))) T qsb[RS ? RG * RB * LDI : 1];
   __shared__ __attribute__((aligned(16))) T dysb[RS ? RG * RB * LDI : 1];
@@ -497,9 +504,19 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v = sum16(part[e]);
-          if (lane % 16 == 0) atomicAdd(&dsum[m0 + 4 * g + e], v);
+          if (lane % 16 == 0) ps[(m0 + 4 * g + e) * LDP + NB + st % ng] = v;
         }
       }
+    }
+  };
+  // dsum[r] += the strips' row sums of the last scores() call, in strip
+  // order (between two barriers)
+  auto add_rowsums = [&](float* dsum, int nbpk) {
+    const int ng = (nbpk / 16 + NG - 1) / NG;
+    for (int r = threadIdx.x; r < RB; r += NTH) {
+      float v = 0.f;
+      for (int j = 0; j < ng; ++j) v += ps[r * LDP + NB + j];
+      dsum[r] += v;
     }
   };
 
@@ -524,6 +541,9 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
         const int l0 = g0 + c * RB;
         if (l0 >= rt) break;
         scores(l0, min(RB, rt - l0), false, dlb + c * RB, qsb + c * RB * LDI, dysb + c * RB * LDI, lsb + c * RB);
+        __syncthreads();
+        add_rowsums(dlb + c * RB, nbp);
+        __syncthreads();
       }
     }
     __syncthreads();
@@ -554,6 +574,10 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
     __syncthreads();
     scores(l0, nr, true, MODE == S2_KEYS ? nullptr : dl, qs, dys, lsel);
     __syncthreads();
+    if (MODE != S2_KEYS) {
+      add_rowsums(dl, nbp);
+      __syncthreads();
+    }
     // dW = P (dP - D)
     for (int idx = threadIdx.x; idx < RB * nbp; idx += NTH) {
       const int r = idx / nbp, k = idx % nbp;
@@ -578,10 +602,12 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
           if (row >= nr || (padded && !col.valid(r0 + l0 + row))) continue;
-          float* at = p.dq2 + ((size_t)sl * p.N + col.at(r0 + l0 + row)) * D + d;
-          if (MODE == S2_KEYS) atomicAdd(at, a[t][e] * p.sc);     // zeroed before the kernel
-          else if (AL) *at += a[t][e] * p.sc + a2[t][e];          // later steps' parts are in
-          else *at = a[t][e] * p.sc;
+          const size_t o = ((size_t)sl * p.N + col.at(r0 + l0 + row)) * D + d;
+          // a key chunk's part of dQ goes to its own buffer (summed in
+          // chunk order later); later steps' parts are in dq2 already
+          if (MODE == S2_KEYS) p.dq2p[(size_t)kc * p.S * p.N * D + o] = a[t][e] * p.sc;
+          else if (AL) p.dq2[o] += a[t][e] * p.sc + a2[t][e];
+          else p.dq2[o] = a[t][e] * p.sc;
         }
       }
       }
@@ -631,10 +657,15 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   }
 }
 
-// Zero n floats (the dQ accumulator of a multi-chunk stage-2 backward).
-static __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, size_t n) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx < n) p[idx] = 0.f;
+// dq2 = sum of the nkc per-key-chunk parts, in chunk order (the stage-2 part
+// of dQ of columns of several key chunks; n floats per part), four floats a
+// thread.
+static __global__ __launch_bounds__(256) void dq2_sum_kernel(const float* parts, float* dq2, size_t n, int nkc) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(parts + i);
+  for (int c = 1; c < nkc; ++c) acc += *reinterpret_cast<const f32x4*>(parts + (size_t)c * n + i);
+  *reinterpret_cast<f32x4*>(dq2 + i) = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -690,6 +721,10 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
   __shared__ __attribute__((aligned(16))) float rs[RB * LDP];
   __shared__ __attribute__((aligned(16))) float dzs[RB * LDP];
   __shared__ float lser[RB], dhr[RB], gr[RB], hr[RB];
+  // per-strip row sums of R dR and R log R go to the padding columns NB ..
+  // NB + 3 of rs and dzs (one per key strip of a row tile), which nothing
+  // else reads
+  static_assert(NB / (16 * NG) <= LDP - NB, "one padding column per key strip");
   __shared__ __attribute__((aligned(16))) float dq2s[SH::PREFETCH && DQO ? RB * (D + 4) : 1];   // dQ (stage 2)
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
@@ -832,10 +867,22 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
       for (int e = 0; e < 4; ++e) {
         const float vg = sum16(pg[e]), vh = sum16(ph[e]);
         if (lane % 16 == 0) {
-          atomicAdd(&gr[m0 + 4 * g + e], vg);
-          atomicAdd(&hr[m0 + 4 * g + e], vh);
+          rs[(m0 + 4 * g + e) * LDP + NB + st % ng] = vg;
+          dzs[(m0 + 4 * g + e) * LDP + NB + st % ng] = vh;
         }
       }
+    }
+    __syncthreads();
+    // G and H of each row: the strips' sums added in strip order, so they do
+    // not depend on wave timing
+    for (int r = threadIdx.x; r < RB; r += NTH) {
+      float vg = gr[r], vh = hr[r];
+      for (int j = 0; j < ng; ++j) {
+        vg += rs[r * LDP + NB + j];
+        vh += dzs[r * LDP + NB + j];
+      }
+      gr[r] = vg;
+      hr[r] = vh;
     }
     __syncthreads();
     // sc * dz = sc * (R (dR - G) - dH R (log R + H))
@@ -1083,6 +1130,7 @@ BwdParams bwd_params(const Plan& pl, const BwdBufs& b) {
               reinterpret_cast<const float*>(ws + pl.off_h2),
               reinterpret_cast<const float*>(ws + pl.off_lse2),
               reinterpret_cast<float*>(ws + pl.off_dq2),
+              pl.dq2_parts > 1 ? reinterpret_cast<float*>(ws + pl.off_dq2p) : nullptr,
               reinterpret_cast<float*>(ws + pl.off_dcx), reinterpret_cast<float*>(ws + pl.off_dux),
               reinterpret_cast<float*>(ws + pl.off_dhx),
               kvp ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
@@ -1217,8 +1265,6 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   if (nkeys <= NB) {
     MA_BWD2(S2_COLUMN, false, nkeys <= 64, dim3(grid1(cols)));
   } else {                                 // D first, then one workgroup per key chunk
-    const size_t n = (size_t)pl.S * pl.N * D;
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, p.dq2, n);
     if (b.y) {                             // D = dY . y
       const size_t rows = (size_t)pl.S * pl.G;
       hipLaunchKernelGGL((dy_dot_y_kernel<T, D>), dim3(grid1((rows * 16 + 255) / 256)), dim3(256), 0, st,
@@ -1228,8 +1274,12 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
       hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM>),
                          dim3(grid1(cols * ((pl.rt + RG * RB - 1) / (RG * RB)))), dim3(NTH2), 0, st, p);
     }
-    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS>), dim3(grid1(cols * ((nkeys + NB - 1) / NB))),
-                       dim3(NTH2), 0, st, p);
+    const int nkc = (nkeys + NB - 1) / NB;
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS>), dim3(grid1(cols * nkc)), dim3(NTH2), 0, st, p);
+    // the key chunks' parts of dQ, added in chunk order
+    const size_t n = (size_t)pl.S * pl.N * D;
+    hipLaunchKernelGGL(dq2_sum_kernel, dim3(grid1((n / 4 + 255) / 256)), dim3(256), 0, st, p.dq2p, p.dq2, n,
+                       nkc);
   }
   if (pl.c1 > 1 || pl.c2 > 1) {            // per (block, segment), then the query gradients
     MA_BWD1(S1_TILED, dim3(grid1((size_t)pl.S * pl.b1 * pl.c2)));

@@ -35,6 +35,8 @@ struct Plan {
   bool precise;
   size_t off_cx, off_ux, off_h2, off_lser, off_lse2, off_qtil, off_qbar, off_qbar_lp, total;
   size_t off_dq2, off_dcx, off_dux, off_dhx, off_dkp, off_dvp, off_dlx, off_dqbar;   // backward only
+  size_t off_dq2p;     // backward, columns of several key chunks: dq2_parts parts of the dQ sum
+  int dq2_parts;
   // backward of T > 1: per-step forward state, T regions of step_bytes from
   // off_steps (offsets so_* inside one), the column sums beta of L, and the
   // gradients of the next queries (dq~ / dalpha rows and dbeta)

@@ -155,9 +155,18 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
   pl.off_qbar_lp = off;
   if (pl.need_qbar_lp) off = align_up(off + (size_t)pl.S * pl.c1 * pl.b2 * pl.D * pl.elt);
   pl.off_dq2 = pl.off_dcx = pl.off_dux = pl.off_dhx = pl.off_dkp = pl.off_dvp = pl.off_dlx = off;
+  pl.off_dq2p = off;
+  pl.dq2_parts = 0;
   pl.off_dqbar = off;
   if (backward) {
     pl.off_dq2 = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
+    // stage-2 columns of several key chunks write one dQ part per chunk,
+    // summed in chunk order (no atomics: the result does not depend on timing)
+    const int nkeys = p->b1 * p->c2, nb = bwd_max_block(p);
+    if (p->steps == 1 && nkeys > nb) {
+      pl.dq2_parts = (nkeys + nb - 1) / nb;
+      pl.off_dq2p = off; off = align_up(off + (size_t)pl.dq2_parts * pl.S * pl.N * pl.D * 4);
+    }
     pl.off_dcx = off; off = align_up(off + rows * pl.D * 4);
     pl.off_dux = off; off = align_up(off + rows * pl.D * 4);
     pl.off_dhx = off; off = align_up(off + rows * 4);

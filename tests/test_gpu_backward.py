@@ -370,3 +370,32 @@ def test_video_layout_variants(variant):
         cfg = case("bwd fh_w tiled", "bf16", 128, 15, 8, data="video", layout="fh_w", fhw=(3, 5, 8),
                    c1=3, c2=2)
     check_backward(cfg)
+
+
+@pytest.mark.parametrize("case", ["video", "tiled"])
+def test_backward_is_deterministic(case):
+    """Two backward calls on the same inputs give bitwise equal dQ, dK, dV:
+    columns of several key chunks write one dQ part per chunk, summed in
+    chunk order, and the row sums of the softmax gradients are added in strip
+    order, so nothing depends on the timing of workgroups or waves.  The
+    video latent's 630-key columns run five key chunks."""
+    import torch
+    import structured_sub_quadratic_amd as ma
+    if case == "video":
+        cfg = WORKLOADS["video"]
+    else:
+        cfg = WorkloadConfig("case", "bwd det tiled", batch=1, heads=3, seq_len=300 * 24,
+                                        head_dim=64, b1=300, b2=24, steps=1, dtype="bf16",
+                                        data="normed", seed=63, c1=2, c2=2)
+    Q, K, V = make_inputs(cfg)
+    dY = upstream(cfg)
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdy = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+                       for x in (Q, K, V, dY))
+    args = dict(b1=cfg.b1, b2=cfg.b2, steps=1, c1=cfg.c1, c2=cfg.c2, layout=cfg.layout, fhw=cfg.fhw)
+    first = [g.clone() for g in ma.backward(tq, tk, tv, tdy, **args)]
+    for _ in range(2):
+        again = ma.backward(tq, tk, tv, tdy, **args)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dQ", "dK", "dV"), first, again):
+            assert torch.equal(a, b), (case, name)
