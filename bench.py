@@ -64,7 +64,8 @@ def method_bytes(cfg, name):
     t = N * d * e                 # one [N, d] tensor of one slice
     kv = t / cfg.kv_group         # K or V, read once per K/V head
     per = {"stage1_last": t + 2 * kv, "stage1": t + kv, "stage2_last": 2 * t,
-           "stage2_stats": t, "alpha": t, "qbar": t, "fused_t1": 2 * t + 2 * kv}.get(name)
+           "stage2_stats": t, "alpha": t, "stage2_alpha": t, "qbar": t,
+           "fused_t1": 2 * t + 2 * kv}.get(name)
     return None if per is None else per * S
 
 
@@ -99,6 +100,9 @@ def design_bytes(cfg, name, precise):
     elif name == "stage2_stats":
         b = N * d * e + rows * d * xc + rows * 4 + N * 4
     elif name == "alpha":
+        b = N * d * e + rows * d * xc + rows * 4 + N * 4 + rows * d * 4
+    elif name == "stage2_alpha":
+        # Q, c and the entropies in; the normalisers and the next queries out
         b = N * d * e + rows * d * xc + rows * 4 + N * 4 + rows * d * 4
     elif name == "fused_t1":
         # the whole T = 1 pass in one launch: Q, K, V in and Y out, plus the

@@ -626,6 +626,140 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p)
 }
 
 // ---------------------------------------------------------------------------
+// A step before the last of an untiled, unpadded run whose columns hold at
+// most 64 rows and 64 keys: the L-update and the next step's queries in one
+// launch.  One workgroup of 4 waves per (slice, column i) copies the
+// column's keys c (hi + lo planes on the split path) and its query rows into
+// LDS.  Each wave scores its 16 rows against every key (MFMA), takes the row
+// softmax over the keys (L; the row normaliser is stored as stage 2 stores
+// it) and writes its rows of L, transposed, into LDS.  Then wave w forms, for
+// the keys of its 16-key tile, alpha = sum_l L[l,k] q[l] (MFMA; L enters as
+// bf16 hi + lo on the split path) and beta = sum_l L[l,k], and stores
+// qt = alpha / beta, or the column mean of q where beta is zero (the
+// zero-weight fallback).  This replaces a stage-2 statistics launch plus
+// the alpha launch, which read c and Q again and recomputed the scores.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stage2AlphaSmem {
+  static constexpr int TILE = 64 * SwzTile<D>::RB;            // 64 rows of D bf16
+  static constexpr int CHI = 0, CLO = TILE, QT = 2 * TILE;    // keys (hi, lo), query rows
+  static constexpr int LDL = 64 + 4;                           // fp32 stride of a row of L^T
+  static constexpr int LT = 3 * TILE;                          // L^T: [64 keys][LDL]
+  static constexpr int BIAS = LT + 64 * LDL * 4;
+  static constexpr int BYTES = BIAS + 64 * 4;
+};
+
+template <int D, bool PRECISE>
+__global__ __launch_bounds__(256) void stage2_alpha_kernel(Stage2Params p, float* qt_out) {
+  typedef bf16 T;
+  constexpr bool KLO = split_x<T, PRECISE>();
+  typedef FlashCore<T, D, D, 1, 64, false, false, KLO, 0> Core;
+  typedef typename Core::frag frag;
+  typedef Stage2AlphaSmem<D> SM;
+  __shared__ __attribute__((aligned(1024))) char lds[SM::BYTES];
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
+  const int i = blockIdx.x % p.b2, sl = blockIdx.x / p.b2;
+  const int nk = p.nkeys, rt = p.rt;           // both at most 64 (host-checked)
+  const size_t xs = x_stride(p.b2, 1), base = x_base(p.b1, p.b2, 1, 1, sl, 0, i);
+  const T* C = static_cast<const T*>(p.cx) + base * D;
+  const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
+  const AxisMap am = p.map.template col_axis<false>(i);
+  // rows past nk / rt repeat the last one (their scores are masked, their L is 0)
+  SwzTile<D>::template load<64, 4>(lds + SM::CHI, [&](int r) { return C + (size_t)r * xs * D; }, nk);
+  if constexpr (KLO)
+    SwzTile<D>::template load<64, 4>(lds + SM::CLO, [&](int r) { return C + p.xlo + (size_t)r * xs * D; }, nk);
+  SwzTile<D>::template load<64, 4>(lds + SM::QT, [&](int r) { return Q + am.raw(r) * D; }, rt);
+  float* bias = reinterpret_cast<float*>(lds + SM::BIAS);
+  if (threadIdx.x < 64) bias[threadIdx.x] = p.h2x[base + (size_t)min((int)threadIdx.x, nk - 1) * xs];
+  wait_vmem();
+  __syncthreads();
+
+  // L-update of this wave's 16 rows
+  Core core;
+  core.init();
+  const int row = 16 * wave + lane % 16;
+  const int rowc = min(row, rt - 1);
+#pragma unroll
+  for (int ks = 0; ks < Core::NKS; ++ks)
+    core.qf[0][ks] = *reinterpret_cast<const frag*>(lds + SM::QT + SwzTile<D>::offset(rowc, 4 * ks + g));
+  core.scores_v(SwzKeys<D>(lds + SM::CHI, lds + SM::CLO), 0, Core::MT);
+  if (nk == 64) core.template softmax_step<true, false>(bias, p.sc2, 0, 64);
+  else core.template softmax_step<true, true>(bias, p.sc2, 0, nk);
+  const float lt = wave_sum_x16x32(core.l[0]);
+  float lse2[1], h2[1];
+  core.finish(lse2, h2, p.sc2);
+  if (g == 0 && row < rt) p.lse2[((size_t)sl * p.b2 + i) * p.b1 + row] = lse2[0];
+  float* Lt = reinterpret_cast<float*>(lds + SM::LT);
+  const float inv = row < rt ? 1.f / lt : 0.f;        // rows past the column carry no L
+#pragma unroll
+  for (int mt = 0; mt < Core::MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Lt[(mt * 16 + 4 * g + r) * SM::LDL + row] = core.s[0][mt][r] * inv;
+  __syncthreads();
+
+  // alpha and beta of this wave's keys, over all rows
+  if (16 * wave >= nk) return;
+  const int key = 16 * wave + lane % 16;
+  const SwzValuesT<D> qv(lds + SM::QT, lds + SM::QT);
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float beta = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    // rows {32kk + 4g + r} and {32kk + 16 + 4g + r}: the k order of qv.at
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(Lt + key * SM::LDL + 32 * kk + 4 * g);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(Lt + key * SM::LDL + 32 * kk + 16 + 4 * g);
+    const bf16x4 h0 = __builtin_convertvector(a0, bf16x4), h1 = __builtin_convertvector(a1, bf16x4);
+    const frag b = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+    frag bl = {};
+    if constexpr (PRECISE) {
+      bl = __builtin_shufflevector(__builtin_convertvector(a0 - __builtin_convertvector(h0, f32x4), bf16x4),
+                                   __builtin_convertvector(a1 - __builtin_convertvector(h1, f32x4), bf16x4),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+      beta += (a0[0] + a0[1]) + (a0[2] + a0[3]) + (a1[0] + a1[1]) + (a1[2] + a1[3]);
+    } else {
+      // the values the MFMA consumes
+      const f32x4 r0 = __builtin_convertvector(h0, f32x4), r1 = __builtin_convertvector(h1, f32x4);
+      beta += (r0[0] + r0[1]) + (r0[2] + r0[3]) + (r1[0] + r1[1]) + (r1[2] + r1[3]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const frag a = qv.at(dt, kk);
+      acc[dt] = Mfma<T>::mma(a, b, acc[dt]);
+      if constexpr (PRECISE) acc[dt] = Mfma<T>::mma(a, bl, acc[dt]);
+    }
+  }
+  beta = wave_sum_x16x32(beta);
+  // lane (g, key) holds alpha[key][16 dt + 4 g + r]
+  float* out = qt_out + (((size_t)sl * p.b1 + min(key, nk - 1)) * p.b2 + i) * D;
+  if (__any(beta <= 0.f)) {
+    // zero weight somewhere in this wave: the column mean of q over its rows
+    f32x4 mean[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      mean[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int d0 = 16 * dt + 4 * g;
+      for (int r = 0; r < rt; ++r) {
+        const bf16x4 v = *reinterpret_cast<const bf16x4*>(lds + SM::QT + SwzTile<D>::offset(r, d0 / 8) +
+                                                          2 * (d0 % 8));
+        mean[dt] += __builtin_convertvector(v, f32x4);
+      }
+      mean[dt] *= 1.f / (float)rt;
+    }
+    if (beta <= 0.f) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mean[dt];
+      beta = 1.f;
+    }
+  }
+  if (key >= nk) return;
+  const float ib = 1.f / beta;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) store4(out + dt * 16 + 4 * g, acc[dt] * ib);
+}
+
+// ---------------------------------------------------------------------------
 // Fused single launch for T = 1 (untiled): stage 1 over every block, a
 // grid-wide barrier, stage 2 over every column, in one cooperative launch of
 // resident persistent workgroups.  Removes the launch gap between the stages;

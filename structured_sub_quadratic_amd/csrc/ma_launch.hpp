@@ -338,6 +338,16 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #undef MA_S2
       break;
     }
+    case L_STAGE2_ALPHA: {
+      if constexpr (!is_f32<T>()) {
+        // one workgroup per column (b1 <= 64 rows and keys, untiled)
+        Stage2Params p{b.q, b.y, cx, ux, h2, lse2, nullptr, pl.map,
+                       S, N, pl.b1, pl.b2, 1, 1, pl.rt, pl.b1, 1, pl.sc2, pl.xlo, 0};
+        hipLaunchKernelGGL((stage2_alpha_kernel<D, PRECISE>), dim3(grid1((size_t)S * pl.b2)), dim3(256), 0, st,
+                           p, qtil);
+      }
+      break;
+    }
     case L_ALPHA:
     case L_EXPORT_L: {
       const int nkeys = pl.b1 * pl.c2;

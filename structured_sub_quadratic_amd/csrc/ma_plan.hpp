@@ -47,6 +47,7 @@ struct Plan {
   bool need_qbar, need_qtil;
   bool need_qbar_lp;   // tile means also in the input type (copied-tile first step)
   bool fused;        // single cooperative launch for T = 1
+  bool fuse_alpha;   // steps before the last: L-update and next queries in one launch
   int causal;        // 0, or grid blocks per causal unit when that masks anything (< b1)
 };
 
@@ -67,7 +68,7 @@ inline Plan step_plan(const Plan& pl, int t) {
 // The launch sequence, shared by the real run, the launch count and the
 // launch names.  `Launcher` is called once per kernel launch in order.
 enum LaunchKind { L_FUSED, L_QBAR, L_STAGE1, L_STAGE1_LAST, L_STAGE2_STATS, L_STAGE2_LAST, L_ALPHA,
-                  L_EXPORT_L, L_EXPORT_R, L_OBJECTIVE };
+                  L_STAGE2_ALPHA, L_EXPORT_L, L_EXPORT_R, L_OBJECTIVE };
 
 inline const char* launch_kind_name(LaunchKind k) {
   switch (k) {
@@ -78,6 +79,7 @@ inline const char* launch_kind_name(LaunchKind k) {
     case L_STAGE2_STATS: return "stage2_stats";
     case L_STAGE2_LAST: return "stage2_last";
     case L_ALPHA: return "alpha";
+    case L_STAGE2_ALPHA: return "stage2_alpha";
     case L_EXPORT_L: return "export_L";
     case L_EXPORT_R: return "export_R";
     case L_OBJECTIVE: return "objective";
@@ -91,11 +93,16 @@ void for_each_launch(const Plan& pl, bool exp_L, bool exp_R, bool exp_obj, F&& f
   if (pl.fused) {
     f(j++, L_FUSED, 0);
   } else {
-    if (pl.need_qbar) f(j++, L_QBAR, 0);
+    // the fused L-update takes the zero-weight fallback (a column mean) itself
+    if (pl.need_qbar && !pl.fuse_alpha) f(j++, L_QBAR, 0);
   }
   for (int step = 0; step < (pl.fused ? 0 : pl.T); ++step) {
     const bool last = step == pl.T - 1;
     f(j++, last ? L_STAGE1_LAST : L_STAGE1, step);
+    if (!last && pl.fuse_alpha) {
+      f(j++, L_STAGE2_ALPHA, step);
+      continue;
+    }
     f(j++, last ? L_STAGE2_LAST : L_STAGE2_STATS, step);
     if (!last) f(j++, L_ALPHA, step);
   }

@@ -122,6 +122,11 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
              !(p->flags & MA_FLAG_FORCE_STAGED);
   // a causal unit of at least b1 blocks masks nothing
   pl.causal = p->causal < p->b1 ? p->causal : 0;
+  // columns of at most 64 rows and keys (untiled, unpadded, bf16, no mask):
+  // the steps before the last run the L-update and the next queries in one
+  // launch
+  pl.fuse_alpha = !backward && p->steps > 1 && p->dtype == MA_BF16 && p->c1 == 1 && p->c2 == 1 &&
+                  !pl.padded && p->b1 <= 64 && pl.causal == 0;
   const size_t rows = (size_t)pl.S * pl.G * pl.c1 * pl.c2;   // exchange rows
   size_t off = 0;
   pl.xlo = (pl.precise && p->dtype == MA_BF16) ? rows * pl.D : 0;

@@ -120,9 +120,18 @@ def test_workspace_size_and_launch_plan(lib):
     p = ma.make_problem(1, 12, 16384, 64, 128, 128,
                         flags=ma.MA_FLAG_FORCE_FUSED | ma.MA_FLAG_FORCE_STAGED)
     assert ma.launch_names(p) == ["stage1_last", "stage2_last"]
+    # columns of at most 64 rows and keys: the L-update and the next queries
+    # of the steps before the last in one launch (which also takes the
+    # zero-weight fallback, so no tile-means launch)
     p = ma.make_problem(8, 12, 4096, 64, 64, 64, steps=3)
+    assert ma.launch_names(p) == ["stage1", "stage2_alpha", "stage1", "stage2_alpha",
+                                  "stage1_last", "stage2_last"]
+    p = ma.make_problem(8, 12, 4096, 64, 64, 64, steps=3, dtype="f32")
     assert ma.launch_names(p) == ["qbar", "stage1", "stage2_stats", "alpha", "stage1",
                                   "stage2_stats", "alpha", "stage1_last", "stage2_last"]
+    p = ma.make_problem(2, 12, 96 * 64, 64, 96, 64, steps=2)      # columns of 96 keys
+    assert ma.launch_names(p) == ["qbar", "stage1", "stage2_stats", "alpha", "stage1_last",
+                                  "stage2_last"]
     p = ma.make_problem(1, 12, 32760, 128, 630, 52, c1=2, c2=2, layout="fh_w", fhw=(21, 30, 52))
     assert ma.launch_names(p) == ["qbar", "stage1_last", "stage2_last"]
     p = ma.make_problem(1, 12, 32760, 128, 630, 52, c1=2, c2=2, layout="fh_w", fhw=(21, 30, 52),
