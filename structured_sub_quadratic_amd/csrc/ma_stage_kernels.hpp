@@ -56,7 +56,7 @@ struct FlashCore {
     if constexpr (B == 0) return s;
     else return s2;
   }
-  float m[NQ], l[NQ], e[NQ], sref[NQ];
+  float m[NQ], l[NQ], e[NQ];
   int qlim[NQ];           // QLIM steps: keys at or past qlim[n] (tile-local) are masked for query n
   bool fresh;             // no key seen since init()
 
@@ -64,7 +64,7 @@ struct FlashCore {
     fresh = true;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-      m[n] = -INFINITY; l[n] = 0.f; e[n] = 0.f; sref[n] = 0.f;
+      m[n] = -INFINITY; l[n] = 0.f; e[n] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -195,15 +195,24 @@ struct FlashCore {
   // than 8 (base 2), so most tiles skip the rescale of l, e and O; the
   // probabilities are then at most 2^8 (exact in fp32, same relative
   // precision in bf16) and the final normalisation divides them out.
-  // Entropy: e = sum p (z - sref) in raw score units, sref = first maximum.
+  // Entropy: e = sum p z in raw score units; finish() turns it into
+  // H = lse - sc2 * e / l (fp32 keeps its absolute error near 1e-6 bits for
+  // scores of a few tens of bits).
   // Maxima and sums over the lane's 4*MT keys are pairwise trees, so the
   // dependent chains are short.
+  // three-input maxima (one v_max3_f32 each) where a level has three left
   template <int K> __device__ static inline float tree_max(const float (&v)[K]) {
     if constexpr (K == 1) return v[0];
+    else if constexpr (K == 2) return fmaxf(v[0], v[1]);
     else {
-      float h[K / 2];
+      constexpr int H = (K + 2) / 3;
+      float h[H];
 #pragma unroll
-      for (int j = 0; j < K / 2; ++j) h[j] = fmaxf(v[2 * j], v[2 * j + 1]);
+      for (int j = 0; j < H; ++j) {
+        if (3 * j + 2 < K) h[j] = fmaxf(fmaxf(v[3 * j], v[3 * j + 1]), v[3 * j + 2]);
+        else if (3 * j + 1 < K) h[j] = fmaxf(v[3 * j], v[3 * j + 1]);
+        else h[j] = v[3 * j];
+      }
       return tree_max(h);
     }
   }
@@ -256,9 +265,8 @@ struct FlashCore {
           for (int dt = 0; dt < DT; ++dt) o[n][dt] *= resc;
         }
       }
-      if (ENTROPY && fresh) sref[n] = tmax;
       m[n] = mnew;
-      float ps[4 * MT], es[4 * MT];
+      float ps[4 * MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -267,12 +275,17 @@ struct FlashCore {
           const float p = HAS_BIAS ? __builtin_amdgcn_exp2f(z - mnew)
                                    : __builtin_amdgcn_exp2f(fmaf(z, sc2, -mnew));
           ps[4 * mt + r] = p;
-          if (ENTROPY) es[4 * mt + r] = p * (z - sref[n]);
           s[n][mt][r] = p;
         }
       }
       l[n] += tree_sum(ps);
-      if (ENTROPY) e[n] += tree_sum(es);
+      if (ENTROPY) {
+        // sum p z over the tile: pairs as one multiply and one fma
+        float pz[2 * MT];
+#pragma unroll
+        for (int j = 0; j < 2 * MT; ++j) pz[j] = fmaf(ps[2 * j], zs[2 * j], ps[2 * j + 1] * zs[2 * j + 1]);
+        e[n] += tree_sum(pz);
+      }
     }
     fresh = false;
   }
@@ -359,9 +372,9 @@ struct FlashCore {
       const float lg = __builtin_amdgcn_logf(lt);
       lse2[n] = m[n] + lg;
       if (ENTROPY) {
-        // H = lse2 - sc2 * (sum p z) / lt with sum p z = e + sref * lt
+        // H = lse2 - sc2 * (sum p z) / lt
         const float et = wave_sum_x16x32(e[n]);
-        h2[n] = (m[n] - sc2 * sref[n]) + lg - sc2 * et * inv;
+        h2[n] = lse2[n] - sc2 * et * inv;
       } else {
         h2[n] = 0.f;
       }
