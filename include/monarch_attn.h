@@ -246,9 +246,9 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * K/V they sum over the query heads of each group.  A padded sequence
  * (MA_FLAG_PAD_FRONT or post-padding) routes the query gradient of a padding
  * position through the tile mean it used.  Covers b2 <= 128 (<= 64 for
- * fp32 with head_dim 128) with: steps = 1, with padding or with row tiles
+ * fp32 with head_dim 128) with: steps = 1, with padding and with row tiles
  * and key segments c1, c2 (whose other-tile queries route their gradient
- * through the tile means), not both; steps > 1 (the gradient through every
+ * through the tile means of the real rows), also together; steps > 1 (the gradient through every
  * unrolled step, each step's L feeding the next step's queries) with
  * c1 = c2 = 1 (padding allowed), b1 within the same limit, and for bf16 at
  * head_dim 128 b1, b2 <= 64.  Other problems return MA_ERR_UNSUPPORTED.

@@ -766,9 +766,10 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
     } else if constexpr (QF) {
       pqf.load(n, [&](int r) { return p.qtil + (xb + i0 + r) * D; });
     } else if constexpr (TL) {
+      // a padding position of the own tile took the tile mean, as the other tiles
       pq.load(n, [&](int r) {
         const int q = i0 + r, t = q / p.b2, i = q % p.b2;
-        return t == own ? Q + row.at(i) * D : QB + (size_t)q * D;
+        return t == own && (!padded || row.valid(i)) ? Q + row.at(i) * D : QB + (size_t)q * D;
       });
     } else {
       pq.load(n, [&](int r) {
@@ -853,7 +854,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = m0 + 4 * g + e;
-          const bool ok = r < nr && key < nb && (!padded || (key >= jlo && key < jhi));
+          // (the tile holds the keys j0 .. j0 + nb of the block)
+          const bool ok = r < nr && key < nb && (!padded || (j0 + key >= jlo && j0 + key < jhi));
           const float lg2 = z[t][e] * p.sc2 - lser[r];        // log2 R
           const float rv = ok ? __builtin_amdgcn_exp2f(lg2) : 0.f;
           const float dv = ok ? dr[t][e] : 0.f;
@@ -966,7 +968,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = m0 + 4 * g + e;
-        if (key >= nb || (padded && (key < jlo || key >= jhi))) continue;
+        if (key >= nb || (padded && (j0 + key < jlo || j0 + key >= jhi))) continue;
         const int64_t tok = row.at(j0 + key);
         if constexpr (SM == S1_LAST || SM == S1_MID || FIRST) {   // several steps
           const size_t at = ((size_t)sl * p.N + tok) * D + d;
@@ -1034,9 +1036,11 @@ __global__ __launch_bounds__(256) void dy_dot_y_kernel(const T* dy, const T* y, 
 }
 
 // Row tiles / key segments (T = 1): the query gradient of exchange row
-// (k, s, t, i) belongs to q(k, i) when t is k's own row tile and to the tile
-// mean qbar(t, i) otherwise; qbar(t, i) is the mean of the rt rows of tile t,
-// so each of them gets 1/rt of its gradient.  One workgroup per (slice, t,
+// (k, s, t, i) belongs to q(k, i) when t is k's own row tile and (k, i) a
+// real position, and to the tile mean qbar(t, i) otherwise; qbar(t, i) is the
+// mean of the real rows of tile t in column i (all rt of them unless the
+// sequence is padded), so each of them gets an equal share of its gradient,
+// and padding rows, which are not tokens, get none.  One workgroup per (slice, t,
 // i): 512 / D groups of D threads split the blocks k (the sum for qbar, then
 // the rows of tile t): dQ(l, i) = stage-2 part + own rows + dqbar / rt.
 template <typename T, int D>
@@ -1051,7 +1055,7 @@ __global__ __launch_bounds__(512) void tiled_dq_kernel(const float* dqx, const f
   auto at = [&](int k, int s) { return dqx[(((((size_t)sl * b1 + k) * c2 + s) * c1 + t) * b2 + i) * D + d]; };
   float bar = 0.f;
   for (int k = grp; k < b1; k += NG) {
-    if (k / rt == t) continue;
+    if (k / rt == t && map.valid(k, i)) continue;
     for (int s = 0; s < c2; ++s) bar += at(k, s);
   }
   part[grp][d] = bar;
@@ -1059,9 +1063,10 @@ __global__ __launch_bounds__(512) void tiled_dq_kernel(const float* dqx, const f
   bar = 0.f;
 #pragma unroll
   for (int g2 = 0; g2 < NG; ++g2) bar += part[g2][d];
-  bar /= (float)rt;
+  bar /= (float)max(1, map.real_rows(i, t * rt, t * rt + rt));
   for (int r = grp; r < rt; r += NG) {
     const int l = t * rt + r;
+    if (!map.valid(l, i)) continue;       // a padding row: no token
     float own = 0.f;
     for (int s = 0; s < c2; ++s) own += at(l, s);
     const size_t o = ((size_t)sl * N + map.token(l, i)) * D + d;
@@ -1288,7 +1293,7 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   } else {
     MA_BWD1(S1_ONLY, dim3(grid1((size_t)pl.S * pl.b1)));
   }
-  if (pl.padded)
+  if (pl.padded && pl.c1 == 1 && pl.c2 == 1)     // (tiled: tiled_dq_kernel routes the tile means)
     hipLaunchKernelGGL((qbar_grad_kernel<T>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(128), 0, st, p.dqbar,
                        static_cast<T*>(b.dq), pl.map, (int)pl.N, D);
   if (pl.group > 1) bwd_kv_out<T, D>(pl, p, b, st);

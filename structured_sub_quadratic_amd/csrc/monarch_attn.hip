@@ -244,7 +244,7 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
 }
 
 // The backward covers stage-1 blocks whose keys fit LDS whole: T = 1 with
-// grouped K/V, any b1, and padding or row tiles / key segments (not both);
+// grouped K/V, any b1, padding, and row tiles / key segments (also padded);
 // T > 1 untiled (padding allowed) with stage-2 columns of one key chunk (b1
 // within the same limit); bf16 at head_dim 128 with T > 1 keeps to 64-key
 // blocks and columns (its split c tiles).
@@ -253,7 +253,7 @@ ma_status validate_backward(const ma_problem* p) {
   if (s != MA_OK) return s;
   if (p->causal > 0 && p->causal < p->b1) return MA_ERR_UNSUPPORTED;   // forward only
   const bool tiled = p->c1 != 1 || p->c2 != 1;
-  if (tiled && (p->steps > 1 || (int64_t)p->b1 * p->b2 != p->seq_len)) return MA_ERR_UNSUPPORTED;
+  if (tiled && p->steps > 1) return MA_ERR_UNSUPPORTED;
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
   if (p->steps > 1) {
     if (p->b1 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;

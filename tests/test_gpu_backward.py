@@ -251,6 +251,30 @@ def test_video_tiled_backward_sampled():
 
 
 @pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("f32", 128), ("bf16", 128)])
+def test_tiled_padded(pad, dtype, d):
+    """Row tiles and key segments on a padded sequence: 205 tokens as 15
+    blocks of 14 (c1 = 3 tiles of 5 rows, c2 = 2 segments of 7 keys), so the
+    padded block keeps 2 real keys in one segment.  The tile means average
+    the real rows only, a padding position's query gradient goes to them,
+    and padding keys get none."""
+    cfg = WorkloadConfig("case", f"bwd tiled pad={pad} {dtype} d{d}", batch=2, heads=2,
+                         seq_len=15 * 14 - 5, head_dim=d, b1=15, b2=14, steps=1, dtype=dtype,
+                         data="iid", seed=67, c1=3, c2=2, pad=pad)
+    check_backward(cfg)
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+def test_tiled_padded_long_columns(pad):
+    """Tiled and padded with columns of more than one key chunk (b1 = 200,
+    c1 = 4, c2 = 2), the upstream row sums taken from the forward's output."""
+    cfg = WorkloadConfig("case", f"bwd tiled b1=200 pad={pad}", batch=1, heads=1,
+                         seq_len=200 * 24 - 9, head_dim=64, b1=200, b2=24, steps=1, dtype="bf16",
+                         data="normed", seed=68, c1=4, c2=2, pad=pad)
+    check_backward(cfg, with_y=True)
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_unrolled_steps_padded_vit(pad, dtype):
     """197 tokens as 15 blocks of 14 at T = 2 (the ViT case): padding rows
