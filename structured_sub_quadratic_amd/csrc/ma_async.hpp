@@ -430,11 +430,22 @@ struct Stage2AsyncSmem {
 };
 
 // PAD: a padded flat sequence (no output at padding positions).
+//
+// The per-chunk path is kept short: the workgroup decodes an item (integer
+// divisions, exchange offsets) once, when its first chunk is issued, and
+// every lane's copy offsets within a full key chunk are computed once per
+// launch, so a chunk's copies cost one address add each.
 template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false>
 struct Stage2Async {
   typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV, KC> SM0;
   static constexpr int STG = WITH_PV ? NW * WaveRows<D>::BYTES : 0;
   static constexpr int LDS_BYTES = 2 * SM0::BUF + STG + 2 * KC * 4;
+
+  // An item (slice, column i, row tile t, query group qg) and its key chunks.
+  struct Item {
+    int item, sl, i, t, qg, nch;
+    size_t base;        // exchange row of its first key
+  };
 
   __device__ static void run(const Stage2Params& p, char* lds) {
   typedef bf16 T;
@@ -451,54 +462,76 @@ struct Stage2Async {
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
   const int nitems = p.S * p.b2 * p.c1 * p.nqg;
-  auto decode = [&](int item, int& sl, int& i, int& t, int& qg) {
-    qg = item % p.nqg; item /= p.nqg;
-    t = item % p.c1; item /= p.c1;
-    i = item % p.b2;
-    sl = item / p.b2;
-  };
+  const size_t xs = x_stride(p.b2, p.c1);                 // exchange rows between keys
+  const size_t key_bytes = xs * D * sizeof(T);
   auto row_of = [&](int qg, int n) { return qg * QG + wave * NQ * 16 + n * 16 + lane % 16; };
   // key chunks of an item: all of them, or (block-causal) those below the
   // key bound of the item's last row
-  auto nch_of = [&](int item) {
-    int sl, i, t, qg;
-    decode(item, sl, i, t, qg);
-    return (stage2_keys(p, t, qg * QG + QG) + KC - 1) / KC;
+  auto decode = [&](int item) {
+    Item it;
+    it.item = item;
+    it.qg = item % p.nqg; item /= p.nqg;
+    it.t = item % p.c1; item /= p.c1;
+    it.i = item % p.b2;
+    it.sl = item / p.b2;
+    it.nch = (stage2_keys(p, it.t, it.qg * QG + QG) + KC - 1) / KC;
+    it.base = x_base(p.b1, p.b2, p.c1, p.c2, it.sl, it.t, it.i);
+    return it;
+  };
+
+  // This lane's copies of a KC-key tile (the layout of SwzTile::load): copy
+  // j of the wave moves 16 bytes of key row crow[j] into LDS slot
+  // (j * NW + wave) * WAVE + lane; coff is its source offset in a full chunk.
+  constexpr int CPR = D / 8, NI = KC * CPR / WAVE, NCW = (NI + NW - 1) / NW;
+  static_assert((KC * CPR) % WAVE == 0, "tile must be whole wave copies");
+  int crow[NCW];
+  uint32_t ccol[NCW];
+  size_t coff[NCW];
+#pragma unroll
+  for (int j = 0; j < NCW; ++j) {
+    const int slot = (j * NW + wave) * WAVE + lane;
+    crow[j] = slot / CPR;
+    ccol[j] = (uint32_t)(((slot % CPR) ^ (crow[j] & 7)) << 4);
+    coff[j] = (size_t)crow[j] * key_bytes + ccol[j];
+  }
+  // keys of a partial chunk past nvalid repeat its last key
+  auto copy_tile = [&](char* dst, const char* src, int nvalid) {
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) {
+      const int ii = j * NW + wave;
+      if (NI % NW != 0 && ii >= NI) break;
+      const size_t off = nvalid == KC ? coff[j] : (size_t)min(crow[j], nvalid - 1) * key_bytes + ccol[j];
+      copy16_to_lds(src + off, dst + ii * WAVE * 16);
+    }
   };
 
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
   float hn[KC / WAVE];          // bias of the unit in flight (last wave, KC/64 keys a lane)
-  auto issue = [&](int item, int ch, char* b) {
-    int sl, i, t, qg;
-    decode(item, sl, i, t, qg);
-    const size_t xs = x_stride(p.b2, p.c1);
-    const size_t base = x_base(p.b1, p.b2, p.c1, p.c2, sl, t, i) + (size_t)ch * KC * xs;
+  auto issue = [&](const Item& it, int ch, char* b) {
+    const size_t row0 = it.base + (size_t)ch * KC * xs;   // exchange row of the chunk's first key
     const int nvalid = min(KC, p.nkeys - ch * KC);
-    const T* C = static_cast<const T*>(p.cx) + base * D;
-    SwzTile<D>::template load<KC, NW>(b + SM::HI, [&](int r) { return C + (size_t)r * xs * D; }, nvalid);
-    if constexpr (KLO)
-      SwzTile<D>::template load<KC, NW>(b + SM::LO, [&](int r) { return C + p.xlo + (size_t)r * xs * D; }, nvalid);
-    if constexpr (WITH_PV) {
-      const T* U = static_cast<const T*>(p.ux) + base * D;
-      SwzTile<D>::template load<KC, NW>(b + SM::U, [&](int r) { return U + (size_t)r * xs * D; }, nvalid);
-    }
+    const char* C = static_cast<const char*>(p.cx) + row0 * D * sizeof(T);
+    copy_tile(b + SM::HI, C, nvalid);
+    if constexpr (KLO) copy_tile(b + SM::LO, C + p.xlo * sizeof(T), nvalid);
+    if constexpr (WITH_PV) copy_tile(b + SM::U, static_cast<const char*>(p.ux) + row0 * D * sizeof(T), nvalid);
     if (wave == NW - 1) {
 #pragma unroll
-      for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[base + (size_t)min(lane + WAVE * j, nvalid - 1) * xs];
+      for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[row0 + (size_t)min(lane + WAVE * j, nvalid - 1) * xs];
     }
     if (ch == 0)
-      Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, sl, i, t, row_of(qg, n)); },
+      Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, row_of(it.qg, n)); },
                           Q_INPUT, qn, qnl);
   };
 
   // Workgroup b takes items pos(b), pos(b) + G, ... where pos groups the
   // workgroups of one XCD on consecutive items, so the query groups of one
   // column (consecutive items) read their shared key tiles through one L2.
-  int item = (int)xcd_swizzle(blockIdx.x, gridDim.x);
-  if (item >= nitems) return;
-  int ch = 0, nch = nch_of(item);
-  issue(item, 0, buf_a);
+  const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+  if (item0 >= nitems) return;
+  Item cur = decode(item0), nx = cur;
+  int ch = 0;
+  issue(cur, 0, buf_a);
   Core core;
 
   // Outputs of an item (y rows and normalisers of this lane's queries),
@@ -541,61 +574,61 @@ struct Stage2Async {
     }
     out.any = false;
   };
-  // unit (item, ch) from buffer cur; the next unit is copied into nxt.
+  // unit (cur, ch) from buffer cb; the next unit is copied into nxt.
   // Returns false after the last unit of this workgroup.
-  auto unit = [&](const char* cur, float* bias, char* nxt) -> bool {
+  auto unit = [&](const char* cb, float* bias, char* nxt) -> bool {
     wait_vmem();
     if (wave == NW - 1) {
 #pragma unroll
       for (int j = 0; j < KC / WAVE; ++j) bias[lane + WAVE * j] = hn[j];
     }
-    __syncthreads();              // cur landed everywhere; nobody reads nxt any more
+    __syncthreads();              // cb landed everywhere; nobody reads nxt any more
     if (ch == 0) {
       core.init();
       core.set_queries(qn, qnl);
     }
-    int nitem = item, nchk = ch + 1;
-    if (nchk == nch) { nitem = item + gridDim.x; nchk = 0; }
-    if (nitem < nitems) issue(nitem, nchk, nxt);
+    int nchk = ch + 1;
+    bool more = true;
+    if (nchk == cur.nch) {        // the next unit opens the workgroup's next item
+      nchk = 0;
+      more = cur.item + (int)gridDim.x < nitems;
+      if (more) nx = decode(cur.item + gridDim.x);
+    }
+    if (more) issue(nchk == 0 ? nx : cur, nchk, nxt);
     flush();
 
     const int nvalid = min(KC, p.nkeys - ch * KC);
     // block-causal use: a wave whose rows all end before this chunk skips
     // it; a chunk that crosses the bound of one of its rows is masked per row
     int how = CH_WHOLE;
-    if (p.causal) {
-      int sl, i, t, qg;
-      decode(item, sl, i, t, qg);
-      how = causal_chunk<NQ>(core, p, t, row_of(qg, 0) - lane % 16,
-                             [&](int n) { return row_of(qg, n); }, ch * KC, nvalid);
-    }
+    if (p.causal)
+      how = causal_chunk<NQ>(core, p, cur.t, row_of(cur.qg, 0) - lane % 16,
+                             [&](int n) { return row_of(cur.qg, n); }, ch * KC, nvalid);
     const bool rowmask = how == CH_ROWMASK;
     if (how != CH_SKIP) {
-      core.scores_v(SwzKeys<D>(cur + SM::HI, cur + SM::LO), 0, Core::MT);
+      core.scores_v(SwzKeys<D>(cb + SM::HI, cb + SM::LO), 0, Core::MT);
       if (rowmask) core.template softmax_step<true, true, 0, true>(bias, p.sc2, 0, nvalid);
       else if (nvalid == KC) core.template softmax_step<true, false>(bias, p.sc2, 0, nvalid);
       else core.template softmax_step<true, true>(bias, p.sc2, 0, nvalid);
       if constexpr (WITH_PV) {
-        const SwzValuesT<D> vv(cur + SM::U, cur + SM::U);
+        const SwzValuesT<D> vv(cb + SM::U, cb + SM::U);
         if (nvalid == KC && !rowmask) core.template pv<false>(vv, 0, nvalid);
         else core.template pv<true>(vv, 0, nvalid);
       }
     }
-    if (ch == nch - 1) {
-      int sl, i, t, qg;
-      decode(item, sl, i, t, qg);
+    if (ch == cur.nch - 1) {
       float lse2[NQ], h2[NQ];
       core.finish(lse2, h2, p.sc2);
-      const AxisMap am = p.map.template col_axis<PAD>(i);
-      out.sl = sl;
-      out.i = i;
-      out.l0 = t * p.rt + row_of(qg, 0) - lane % 16;
-      out.lend = t * p.rt + p.rt;
+      const AxisMap am = p.map.template col_axis<PAD>(cur.i);
+      out.sl = cur.sl;
+      out.i = cur.i;
+      out.l0 = cur.t * p.rt + row_of(cur.qg, 0) - lane % 16;
+      out.lend = cur.t * p.rt + p.rt;
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
-        const int ll = row_of(qg, n);
+        const int ll = row_of(cur.qg, n);
         out.valid[n] = ll < p.rt;
-        out.l[n] = t * p.rt + min(ll, p.rt - 1);
+        out.l[n] = cur.t * p.rt + min(ll, p.rt - 1);
         if constexpr (PAD) out.tok[n] = am.valid(out.l[n]) ? am.at(out.l[n]) : -1;   // -1: padding row
         else out.tok[n] = am.raw(out.l[n]);
         out.lse[n] = lse2[n];
@@ -606,9 +639,8 @@ struct Stage2Async {
       }
       out.any = true;
     }
-    if (nitem >= nitems) return false;
-    if (nitem != item) nch = nch_of(nitem);
-    item = nitem;
+    if (!more) return false;
+    if (nchk == 0) cur = nx;
     ch = nchk;
     return true;
   };

@@ -140,6 +140,10 @@ struct FlashCore {
   // Raw scores S^T for the key sub-tiles [mt0, mt1) of a key tile; kv.a(mt,
   // ks) is this lane's A fragment of key sub-tile mt at head-dim step ks
   // (kv.alo the low part when KLO).
+  // The head-dim steps are the outer loop, so the MFMAs of one step go to
+  // independent accumulators (one per key sub-tile) and the operand reads of
+  // a step are issued together; each accumulator still sums its steps in
+  // order.
   template <int B = 0, class KV>
   __device__ inline void scores_v(const KV& kv, int mt0, int mt1) {
     f32x4 (&s)[NQ][MT] = buf<B>();
@@ -148,8 +152,12 @@ struct FlashCore {
       if (mt < mt0 || mt >= mt1) continue;
 #pragma unroll
       for (int n = 0; n < NQ; ++n) s[n][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int ks_ = 0; ks_ < NKS; ++ks_) {
+    for (int ks_ = 0; ks_ < NKS; ++ks_) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt < mt0 || mt >= mt1) continue;
         const frag a = kv.a(mt, ks_);
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
