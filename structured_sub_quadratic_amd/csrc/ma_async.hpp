@@ -434,12 +434,19 @@ struct Stage2AsyncSmem {
 // The per-chunk path is kept short: the workgroup decodes an item (integer
 // divisions, exchange offsets) once, when its first chunk is issued, and
 // every lane's copy offsets within a full key chunk are computed once per
-// launch, so a chunk's copies cost one address add each.
+// launch, so a chunk's copies cost one address add each.  Each wave copies
+// its own query rows of the next item into LDS with that item's first
+// chunk (where LDS allows; otherwise it prefetches them into registers),
+// and stores an item's outputs as soon as its last chunk is done, which
+// keeps the registers for the arithmetic.
 template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false>
 struct Stage2Async {
   typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV, KC> SM0;
   static constexpr int STG = WITH_PV ? NW * WaveRows<D>::BYTES : 0;
-  static constexpr int LDS_BYTES = 2 * SM0::BUF + STG + 2 * KC * 4;
+  static constexpr int QROWS = NQ * 16 * SwzTile<D>::RB;        // one wave's query rows
+  // queries staged in LDS where they fit (else prefetched into registers)
+  static constexpr bool QLDS = 2 * SM0::BUF + STG + NW * QROWS + 2 * KC * 4 <= 160 * 1024;
+  static constexpr int LDS_BYTES = 2 * SM0::BUF + STG + (QLDS ? NW * QROWS : 0) + 2 * KC * 4;
 
   // An item (slice, column i, row tile t, query group qg) and its key chunks.
   struct Item {
@@ -457,16 +464,16 @@ struct Stage2Async {
   char* const buf_a = lds;
   char* const buf_b = lds + SM::BUF;
   char* const stage_rows = lds + 2 * SM::BUF;
-  float* const bias_a = reinterpret_cast<float*>(lds + 2 * SM::BUF + STG);
+  char* const qrows = lds + 2 * SM::BUF + STG;
+  float* const bias_a = reinterpret_cast<float*>(lds + 2 * SM::BUF + STG + (QLDS ? NW * QROWS : 0));
   float* const bias_b = bias_a + KC;
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
+  char* const qw = qrows + wave * QROWS;          // this wave's query rows (copied by the wave itself)
   const int nitems = p.S * p.b2 * p.c1 * p.nqg;
   const size_t xs = x_stride(p.b2, p.c1);                 // exchange rows between keys
   const size_t key_bytes = xs * D * sizeof(T);
   auto row_of = [&](int qg, int n) { return qg * QG + wave * NQ * 16 + n * 16 + lane % 16; };
-  // key chunks of an item: all of them, or (block-causal) those below the
-  // key bound of the item's last row
   auto decode = [&](int item) {
     Item it;
     it.item = item;
@@ -479,9 +486,6 @@ struct Stage2Async {
     return it;
   };
 
-  // This lane's copies of a KC-key tile (the layout of SwzTile::load): copy
-  // j of the wave moves 16 bytes of key row crow[j] into LDS slot
-  // (j * NW + wave) * WAVE + lane; coff is its source offset in a full chunk.
   constexpr int CPR = D / 8, NI = KC * CPR / WAVE, NCW = (NI + NW - 1) / NW;
   static_assert((KC * CPR) % WAVE == 0, "tile must be whole wave copies");
   int crow[NCW];
@@ -494,7 +498,6 @@ struct Stage2Async {
     ccol[j] = (uint32_t)(((slot % CPR) ^ (crow[j] & 7)) << 4);
     coff[j] = (size_t)crow[j] * key_bytes + ccol[j];
   }
-  // keys of a partial chunk past nvalid repeat its last key
   auto copy_tile = [&](char* dst, const char* src, int nvalid) {
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
@@ -504,12 +507,24 @@ struct Stage2Async {
       copy16_to_lds(src + off, dst + ii * WAVE * 16);
     }
   };
+  // The wave's query rows into qw: copy j moves chunk (slot % CPR) of row
+  // slot / CPR, slot = j * WAVE + lane, to the swizzled place of that chunk.
+  constexpr int QCW = NQ * 16 * CPR / WAVE;
+  auto copy_queries = [&](const Item& it) {
+#pragma unroll
+    for (int j = 0; j < QCW; ++j) {
+      const int slot = j * WAVE + lane, r = slot / CPR, cs = slot % CPR;
+      const int c = cs ^ (r & 7);
+      const T* src = stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, it.qg * QG + wave * NQ * 16 + r).t;
+      copy16_to_lds(src + c * 8, qw + j * WAVE * 16);
+    }
+  };
 
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
   float hn[KC / WAVE];          // bias of the unit in flight (last wave, KC/64 keys a lane)
   auto issue = [&](const Item& it, int ch, char* b) {
-    const size_t row0 = it.base + (size_t)ch * KC * xs;   // exchange row of the chunk's first key
+    const size_t row0 = it.base + (size_t)ch * KC * xs;
     const int nvalid = min(KC, p.nkeys - ch * KC);
     const char* C = static_cast<const char*>(p.cx) + row0 * D * sizeof(T);
     copy_tile(b + SM::HI, C, nvalid);
@@ -519,63 +534,57 @@ struct Stage2Async {
 #pragma unroll
       for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[row0 + (size_t)min(lane + WAVE * j, nvalid - 1) * xs];
     }
-    if (ch == 0)
-      Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, row_of(it.qg, n)); },
-                          Q_INPUT, qn, qnl);
+    if (ch == 0) {
+      if constexpr (QLDS) copy_queries(it);
+      else Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, row_of(it.qg, n)); },
+                               Q_INPUT, qn, qnl);
+    }
   };
 
-  // Workgroup b takes items pos(b), pos(b) + G, ... where pos groups the
-  // workgroups of one XCD on consecutive items, so the query groups of one
-  // column (consecutive items) read their shared key tiles through one L2.
   const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
   if (item0 >= nitems) return;
   Item cur = decode(item0), nx = cur;
   int ch = 0;
   issue(cur, 0, buf_a);
   Core core;
-
-  // Outputs of an item (y rows and normalisers of this lane's queries),
-  // stored after the next unit's copies are issued.
-  struct Out {
-    bf16x4 y[NQ][WITH_PV ? D / 16 : 1];
-    float lse[NQ];
-    int64_t tok[NQ];
-    int l[NQ];
-    bool valid[NQ];
-    int sl, i;
-    int l0, lend;       // grid rows of this wave's first query and of the row tile's end
-    bool any;
-  };
-  Out out;
-  out.any = false;
   char* stg = stage_rows + (WITH_PV ? wave * WaveRows<D>::BYTES : 0);
-  auto flush = [&]() {
-    if (!out.any) return;
-    T* Y = static_cast<T*>(p.y) + (size_t)out.sl * p.N * D;
+
+  // y rows and normalisers of the item just finished
+  auto store = [&]() {
+    float lse2[NQ], h2[NQ];
+    core.finish(lse2, h2, p.sc2);
+    const AxisMap am = p.map.template col_axis<PAD>(cur.i);
+    const int l0 = cur.t * p.rt + row_of(cur.qg, 0) - lane % 16, lend = cur.t * p.rt + p.rt;
     if constexpr (WITH_PV) {
-      const AxisMap am = p.map.template col_axis<PAD>(out.i);
+      T* Y = static_cast<T*>(p.y) + (size_t)cur.sl * p.N * D;
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
-        WaveRows<D>::put(stg, out.y[n]);
+        bf16x4 y[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) y[dt] = __builtin_convertvector(core.o[n][dt], bf16x4);
+        WaveRows<D>::put(stg, y);
         WaveRows<D>::drain(stg, [&](int r) -> T* {
-          const int l = out.l0 + n * 16 + r;
-          if constexpr (PAD) return l < out.lend && am.valid(l) ? Y + am.at(l) * D : nullptr;
-          else return l < out.lend ? Y + am.raw(l) * D : nullptr;
+          const int l = l0 + n * 16 + r;
+          if constexpr (PAD) return l < lend && am.valid(l) ? Y + am.at(l) * D : nullptr;
+          else return l < lend ? Y + am.raw(l) * D : nullptr;
         });
       }
     }
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-      if (!out.valid[n]) continue;
-      if (g == 0) {
-        p.lse2[((size_t)out.sl * p.b2 + out.i) * p.b1 + out.l[n]] = out.lse[n];
-        if (p.lse_out && (!PAD || out.tok[n] >= 0)) p.lse_out[(size_t)out.sl * p.N + out.tok[n]] = out.lse[n] * LN2;
+      const int ll = row_of(cur.qg, n);
+      if (ll >= p.rt || g != 0) continue;
+      const int l = cur.t * p.rt + ll;
+      p.lse2[((size_t)cur.sl * p.b2 + cur.i) * p.b1 + l] = lse2[n];
+      if (p.lse_out) {
+        if constexpr (PAD) {
+          if (am.valid(l)) p.lse_out[(size_t)cur.sl * p.N + am.at(l)] = lse2[n] * LN2;
+        } else {
+          p.lse_out[(size_t)cur.sl * p.N + am.raw(l)] = lse2[n] * LN2;
+        }
       }
     }
-    out.any = false;
   };
-  // unit (cur, ch) from buffer cb; the next unit is copied into nxt.
-  // Returns false after the last unit of this workgroup.
   auto unit = [&](const char* cb, float* bias, char* nxt) -> bool {
     wait_vmem();
     if (wave == NW - 1) {
@@ -585,21 +594,28 @@ struct Stage2Async {
     __syncthreads();              // cb landed everywhere; nobody reads nxt any more
     if (ch == 0) {
       core.init();
-      core.set_queries(qn, qnl);
+      if constexpr (QLDS) {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n)
+#pragma unroll
+          for (int ks_ = 0; ks_ < Core::NKS; ++ks_)
+            core.qf[n][ks_] = *reinterpret_cast<const frag*>(qw + SwzTile<D>::offset(n * 16 + lane % 16, 4 * ks_ + g));
+        // the rows are in registers before the next item's copy may refill qw
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+      } else {
+        core.set_queries(qn, qnl);
+      }
     }
     int nchk = ch + 1;
     bool more = true;
-    if (nchk == cur.nch) {        // the next unit opens the workgroup's next item
+    if (nchk == cur.nch) {
       nchk = 0;
       more = cur.item + (int)gridDim.x < nitems;
       if (more) nx = decode(cur.item + gridDim.x);
     }
     if (more) issue(nchk == 0 ? nx : cur, nchk, nxt);
-    flush();
 
     const int nvalid = min(KC, p.nkeys - ch * KC);
-    // block-causal use: a wave whose rows all end before this chunk skips
-    // it; a chunk that crosses the bound of one of its rows is masked per row
     int how = CH_WHOLE;
     if (p.causal)
       how = causal_chunk<NQ>(core, p, cur.t, row_of(cur.qg, 0) - lane % 16,
@@ -616,29 +632,7 @@ struct Stage2Async {
         else core.template pv<true>(vv, 0, nvalid);
       }
     }
-    if (ch == cur.nch - 1) {
-      float lse2[NQ], h2[NQ];
-      core.finish(lse2, h2, p.sc2);
-      const AxisMap am = p.map.template col_axis<PAD>(cur.i);
-      out.sl = cur.sl;
-      out.i = cur.i;
-      out.l0 = cur.t * p.rt + row_of(cur.qg, 0) - lane % 16;
-      out.lend = cur.t * p.rt + p.rt;
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        const int ll = row_of(cur.qg, n);
-        out.valid[n] = ll < p.rt;
-        out.l[n] = cur.t * p.rt + min(ll, p.rt - 1);
-        if constexpr (PAD) out.tok[n] = am.valid(out.l[n]) ? am.at(out.l[n]) : -1;   // -1: padding row
-        else out.tok[n] = am.raw(out.l[n]);
-        out.lse[n] = lse2[n];
-        if constexpr (WITH_PV) {
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) out.y[n][dt] = __builtin_convertvector(core.o[n][dt], bf16x4);
-        }
-      }
-      out.any = true;
-    }
+    if (ch == cur.nch - 1) store();
     if (!more) return false;
     if (nchk == 0) cur = nx;
     ch = nchk;
@@ -646,7 +640,6 @@ struct Stage2Async {
   };
   while (unit(buf_a, bias_a, buf_b) && unit(buf_b, bias_b, buf_a)) {
   }
-  flush();
   }
 };
 
