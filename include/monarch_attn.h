@@ -248,10 +248,12 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * position through the tile mean it used.  Covers b2 <= 128 (<= 64 for
  * fp32 with head_dim 128) with: steps = 1, with padding and with row tiles
  * and key segments c1, c2 (whose other-tile queries route their gradient
- * through the tile means of the real rows), also together; steps > 1 (the gradient through every
- * unrolled step, each step's L feeding the next step's queries) with
- * c1 = c2 = 1 (padding allowed), b1 within the same limit, and for bf16 at
- * head_dim 128 b1, b2 <= 64.  Other problems return MA_ERR_UNSUPPORTED.
+ * through the tile means of the real rows), also together; steps > 1 (the
+ * gradient through every unrolled step, each step's L feeding the next
+ * step's queries) with c1 = c2 = 1 (padding allowed), and for bf16 at
+ * head_dim 128 b2 <= 64.
+ * Any b1: stage-2 columns longer than one key chunk are walked chunk by
+ * chunk.  Other problems return MA_ERR_UNSUPPORTED.
  * With MA_FLAG_REUSE_FORWARD_STATE the forward state is read from the
  * workspace instead of rebuilt.  For bf16 the recomputed forward takes
  * the c path the forward defaults to (plain for steps = 1, split for
@@ -260,10 +262,11 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * query) passes no gradient back through that query.
  * y: null, or the forward's output Y for these inputs (shaped like Q).  The
  * softmax gradient of every stage-2 row needs D = sum over keys of P dP,
- * which equals dY . y; a column of more than one key chunk (more than 128
- * keys; 64 for fp32 with head_dim 128; steps = 1 only) then takes D from y
- * instead of a separate pass over all its keys (as FlashAttention-2 does);
- * elsewhere y is not read.
+ * which equals dY . y (at the last step when steps > 1); a column of more
+ * than one key chunk (more than 128 keys; 64 for fp32 with head_dim 128 and
+ * for bf16 with head_dim 128 and steps > 1) then takes D from y instead of
+ * a separate pass over all its keys (as FlashAttention-2 does); elsewhere y
+ * is not read.
  * With y the result is that of the given output; for bf16 it may differ from
  * the call without y by the rounding of y.
  * workspace: at least monarch_attn_backward_workspace_size bytes, 256-byte

@@ -345,10 +345,12 @@ __device__ inline void bwd_load_rows(T* dst, T* dt, int NR, int n, Src src) {
 // S2_ALPHA, a step before the last one of T > 1 (columns of one key chunk):
 // that step's L fed the next queries q~ = alpha / beta (alpha = L^T q, beta =
 // column sums of L), so dP = q dalpha^T + dbeta, dQ gains the direct term
-// P dalpha on top of the softmax part, and there is no u.  SPLITC: c is
-// read as its two bf16 planes (the split path of bf16 with T > 1).
+// P dalpha on top of the softmax part, and there is no u.  S2_ROWSUM_A and
+// S2_KEYS_A are the two launches of such a step for columns of several key
+// chunks.  SPLITC: c is read as its two bf16 planes (the split path of bf16
+// with T > 1).
 // ---------------------------------------------------------------------------
-enum { S2_COLUMN = 0, S2_ROWSUM = 1, S2_KEYS = 2, S2_ALPHA = 3 };
+enum { S2_COLUMN = 0, S2_ROWSUM = 1, S2_KEYS = 2, S2_ALPHA = 3, S2_ROWSUM_A = 4, S2_KEYS_A = 5 };
 
 template <typename T, int D, int MODE, bool SPLITC = false, int NBK = 0>
 __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel(BwdParams p) {
@@ -359,7 +361,9 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   constexpr int DS = DT < 4 ? DT : 4;                        // d tiles per dc, du strip
   constexpr int DQ = SH::DQ2;                                // d tiles per dQ strip
   constexpr int SK = SH::SK2;                                // key-tile strips of dc, du per wave
-  constexpr bool AL = MODE == S2_ALPHA;
+  constexpr bool AL = MODE == S2_ALPHA || MODE == S2_ROWSUM_A || MODE == S2_KEYS_A;
+  constexpr bool RS = MODE == S2_ROWSUM || MODE == S2_ROWSUM_A;   // D-only workgroup: RG row chunks stay in LDS
+  constexpr bool KEYS = MODE == S2_KEYS || MODE == S2_KEYS_A;      // one key chunk of a long column
   constexpr int CK = SPLITC ? PL : IN;                       // operand kind of c
   constexpr int CKT = SPLITC ? PLS : INS;                    // and of its transposed copy
   constexpr size_t CPL = (size_t)NB * LDI, CTPL = (size_t)D * LDN;   // lo planes of c, c^T
@@ -383,9 +387,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   // added up in strip order afterwards, so the sums do not depend on wave
   // timing
   static_assert(NB / (16 * NG) <= LDP - NB, "one padding column per key strip");
-  constexpr bool RS = MODE == S2_ROWSUM;   // D-only workgroup: RG row chunks stay in LDS
   __shared__ __attribute__((aligned(16))) T qsb[RS ? RG * RB * LDI : 1];
-  __shared__ __attribute__((aligned(16))) T dysb[RS ? RG * RB * LDI : 1];
+  __shared__ __attribute__((aligned(16))) T dysb[RS && !AL ? RG * RB * LDI : 1];
   __shared__ float lsb[RS ? RG * RB : 1], dlb[RS ? RG * RB : 1];
 
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
@@ -393,7 +396,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   // b1 * c2 exchange rows (k, s) of (t, i)
   const int rt = p.b1 / p.c1, nkeys = p.b1 * p.c2;
   const int nkc = (nkeys + NB - 1) / NB;                     // key chunks of NB keys
-  const int nsub = MODE == S2_COLUMN ? 1 : (MODE == S2_ROWSUM ? (rt + RG * RB - 1) / (RG * RB) : nkc);
+  const int nsub = !RS && !KEYS ? 1 : (RS ? (rt + RG * RB - 1) / (RG * RB) : nkc);
   const int sub = blockIdx.x % nsub;                         // row chunk (ROWSUM) or key chunk (KEYS)
   const int cid = blockIdx.x / nsub;
   const int i = cid % p.b2, t = (cid / p.b2) % p.c1, sl = cid / p.b2 / p.c1, r0 = t * rt;
@@ -452,7 +455,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
       });
     if (threadIdx.x < RB) {
       pls = (int)threadIdx.x < n ? p.lse2[((size_t)sl * p.b2 + i) * p.b1 + r0 + l0 + threadIdx.x] : 0.f;
-      if (MODE == S2_KEYS) pdl = (int)threadIdx.x < n ? dlx[l0 + threadIdx.x] : 0.f;
+      if (KEYS) pdl = (int)threadIdx.x < n ? dlx[l0 + threadIdx.x] : 0.f;
     }
   };
   // P = exp2(sc2 q.c + h2 - lse2) and dP = dY u^T (S2_ALPHA: q dalpha^T +
@@ -520,14 +523,14 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
     }
   };
 
-  if constexpr (MODE == S2_ROWSUM) {
+  if constexpr (RS) {
     // D = rowsum(P dP) of RG row chunks over all key chunks
     const int g0 = sub * RG * RB;
     for (int c = 0; c < RG; ++c) {
       const int l0 = g0 + c * RB;
       fetch(l0);
       pq.template store<LDI, false, LDR>(qsb + c * RB * LDI, nullptr);
-      pdy.template store<LDI, false, LDR>(dysb + c * RB * LDI, nullptr);
+      if constexpr (!AL) pdy.template store<LDI, false, LDR>(dysb + c * RB * LDI, nullptr);
       if (threadIdx.x < RB) {
         lsb[c * RB + threadIdx.x] = pls;
         dlb[c * RB + threadIdx.x] = 0.f;
@@ -540,7 +543,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
       for (int c = 0; c < RG; ++c) {
         const int l0 = g0 + c * RB;
         if (l0 >= rt) break;
-        scores(l0, min(RB, rt - l0), false, dlb + c * RB, qsb + c * RB * LDI, dysb + c * RB * LDI, lsb + c * RB);
+        scores(l0, min(RB, rt - l0), false, dlb + c * RB, qsb + c * RB * LDI, AL ? nullptr : dysb + c * RB * LDI,
+               lsb + c * RB);
         __syncthreads();
         add_rowsums(dlb + c * RB, nbp);
         __syncthreads();
@@ -553,7 +557,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
   }
 
   {
-  const int kc = MODE == S2_KEYS ? sub : 0;
+  const int kc = KEYS ? sub : 0;
   load_keys(kc);
   f32x4 adc[SK][DT], adu[SK][DT];
 #pragma unroll
@@ -568,13 +572,13 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
     if constexpr (!AL) pdy.template store<LDI, true, LDR>(dys, dyt);
     if (threadIdx.x < RB) {
       lsel[threadIdx.x] = pls;
-      dl[threadIdx.x] = MODE == S2_KEYS ? pdl : 0.f;
+      dl[threadIdx.x] = KEYS ? pdl : 0.f;
     }
     if (l0 + RB < rt) fetch(l0 + RB);       // in flight while this chunk computes
     __syncthreads();
-    scores(l0, nr, true, MODE == S2_KEYS ? nullptr : dl, qs, dys, lsel);
+    scores(l0, nr, true, KEYS ? nullptr : dl, qs, dys, lsel);
     __syncthreads();
-    if (MODE != S2_KEYS) {
+    if (!KEYS) {
       add_rowsums(dl, nbp);
       __syncthreads();
     }
@@ -605,7 +609,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
           const size_t o = ((size_t)sl * p.N + col.at(r0 + l0 + row)) * D + d;
           // a key chunk's part of dQ goes to its own buffer (summed in
           // chunk order later); later steps' parts are in dq2 already
-          if (MODE == S2_KEYS) p.dq2p[(size_t)kc * p.S * p.N * D + o] = a[t][e] * p.sc;
+          if (KEYS) p.dq2p[(size_t)kc * p.S * p.N * D + o] = a[t][e] * p.sc + (AL ? a2[t][e] : 0.f);
           else if (AL) p.dq2[o] += a[t][e] * p.sc + a2[t][e];
           else p.dq2[o] = a[t][e] * p.sc;
         }
@@ -659,12 +663,14 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
 
 // dq2 = sum of the nkc per-key-chunk parts, in chunk order (the stage-2 part
 // of dQ of columns of several key chunks; n floats per part), four floats a
-// thread.
-static __global__ __launch_bounds__(256) void dq2_sum_kernel(const float* parts, float* dq2, size_t n, int nkc) {
+// thread; with acc, added to what dq2 holds (the parts of later steps).
+static __global__ __launch_bounds__(256) void dq2_sum_kernel(const float* parts, float* dq2, size_t n, int nkc,
+                                                             int add) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
   f32x4 acc = *reinterpret_cast<const f32x4*>(parts + i);
   for (int c = 1; c < nkc; ++c) acc += *reinterpret_cast<const f32x4*>(parts + (size_t)c * n + i);
+  if (add) acc += *reinterpret_cast<const f32x4*>(dq2 + i);
   *reinterpret_cast<f32x4*>(dq2 + i) = acc;
 }
 
@@ -1184,7 +1190,7 @@ void bwd_kv_out(const Plan& pl, const BwdParams& p, const BwdBufs& b, hipStream_
     else hipLaunchKernelGGL((stage1_bwd_kernel<T, D, SM>), grid, dim3(NTH), 0, st, p);             \
   } while (0)
 
-// T > 1 (untiled, stage-2 columns of one key chunk).  The forward
+// T > 1 (untiled).  The forward
 // is recomputed step by step into per-step state (c, entropy, both
 // normalisers, the step's queries q~ and the column sums beta of L); then
 // the steps are differentiated in reverse.  The last step as for T = 1 but
@@ -1192,7 +1198,9 @@ void bwd_kv_out(const Plan& pl, const BwdParams& p, const BwdBufs& b, hipStream_
 // dq~ of step t + 1 through q~ = alpha / beta into its stage 2 (dQ direct
 // and softmax parts, dc, dH) and its stage 1 (dq~ of step t, or at t = 0
 // the rest of dQ; dK).  dQ and dK accumulate in fp32 over the steps; the
-// step-0 stage 1, which runs last, writes them out.
+// step-0 stage 1, which runs last, writes them out.  A column of more keys
+// than one chunk takes, at every step, a D pass and one workgroup per key
+// chunk, whose parts of dQ are added in chunk order.
 template <typename T, int D, bool PRECISE>
 ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   Bufs fb{b.q, b.k, b.v, nullptr, b.ws, nullptr, nullptr, nullptr, nullptr};
@@ -1217,7 +1225,25 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   const size_t rows = (size_t)pl.S * pl.G;
   BwdParams p = bwd_params<T, D>(pl, b);
   const bool k2 = pl.b1 <= 64;                            // 64-key stage-2 build
-  MA_BWD2(S2_COLUMN, SPLITC, k2, g2);
+  // columns of several key chunks
+  constexpr int NBK = ONLY64 ? 64 : 0;                    // the chunked build
+  constexpr int NBC = BwdShape<T, D, NBK>::NB, RGC = BwdShape<T, D, NBK>::RG, RBC = BwdShape<T, D, NBK>::RB;
+  const bool chunked = pl.b1 > NBC;
+  const int nkc = (pl.b1 + NBC - 1) / NBC;
+  const size_t cols = (size_t)pl.S * pl.b2, nq = (size_t)pl.S * pl.N * D;
+  const dim3 grs(grid1(cols * ((pl.rt + RGC * RBC - 1) / (RGC * RBC)))), gks(grid1(cols * nkc));
+  const dim3 gsum(grid1((nq / 4 + 255) / 256));
+  if (chunked) {                         // D = dY . y, or a D pass; then the key chunks
+    if (b.y)
+      hipLaunchKernelGGL((dy_dot_y_kernel<T, D>), dim3(grid1((rows * 16 + 255) / 256)), dim3(256), 0, st,
+                         static_cast<const T*>(b.dy), static_cast<const T*>(b.y), p.dlx, pl.map, (int)pl.N, rows);
+    else
+      hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM, SPLITC, NBK>), grs, dim3(NTH2), 0, st, p);
+    hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS, SPLITC, NBK>), gks, dim3(NTH2), 0, st, p);
+    hipLaunchKernelGGL(dq2_sum_kernel, gsum, dim3(256), 0, st, p.dq2p, p.dq2, nq, nkc, 0);
+  } else {
+    MA_BWD2(S2_COLUMN, SPLITC, k2, g2);
+  }
   MA_BWD1(S1_LAST, g1);
   for (int t = pl.T - 2; t >= 0; --t) {
     const Plan sp = step_plan(pl, t);
@@ -1231,7 +1257,13 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
                        reinterpret_cast<const float*>(ws + sp.off_beta),
                        reinterpret_cast<const float*>(ws + step_plan(pl, t + 1).off_qtil),
                        reinterpret_cast<float*>(ws + pl.off_dbt), rows);
-    MA_BWD2(S2_ALPHA, SPLITC, k2, g2);
+    if (chunked) {                       // the parts of dQ add to those of later steps
+      hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM_A, SPLITC, NBK>), grs, dim3(NTH2), 0, st, p);
+      hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS_A, SPLITC, NBK>), gks, dim3(NTH2), 0, st, p);
+      hipLaunchKernelGGL(dq2_sum_kernel, gsum, dim3(256), 0, st, p.dq2p, p.dq2, nq, nkc, 1);
+    } else {
+      MA_BWD2(S2_ALPHA, SPLITC, k2, g2);
+    }
     if (t > 0) MA_BWD1(S1_MID, g1);
     else if (pl.padded) MA_BWD1(S1_FIRSTP, g1);
     else MA_BWD1(S1_FIRST, g1);
@@ -1284,7 +1316,7 @@ ma_status run_bwd_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
     // the key chunks' parts of dQ, added in chunk order
     const size_t n = (size_t)pl.S * pl.N * D;
     hipLaunchKernelGGL(dq2_sum_kernel, dim3(grid1((n / 4 + 255) / 256)), dim3(256), 0, st, p.dq2p, p.dq2, n,
-                       nkc);
+                       nkc, 0);
   }
   if (pl.c1 > 1 || pl.c2 > 1) {            // per (block, segment), then the query gradients
     MA_BWD1(S1_TILED, dim3(grid1((size_t)pl.S * pl.b1 * pl.c2)));

@@ -132,6 +132,11 @@ struct BwdBufs {
 inline int bwd_max_block(const ma_problem* p) {
   return (p->dtype == MA_F32 && p->head_dim == 128) ? 64 : 128;
 }
+// Keys of a stage-2 chunk of the backward: bf16 at head_dim 128 with T > 1
+// reads c as two planes and keeps to 64.
+inline int bwd_key_chunk(const ma_problem* p) {
+  return (p->dtype == MA_BF16 && p->head_dim == 128 && p->steps > 1) ? 64 : bwd_max_block(p);
+}
 
 // Kernel-launch entry of one element type and head dimension (one
 // translation unit each): runs the whole launch sequence of *pl on st.

@@ -167,8 +167,8 @@ Plan make_plan(const ma_problem* p, bool backward = false) {
     pl.off_dq2 = off; off = align_up(off + (size_t)pl.S * pl.N * pl.D * 4);
     // stage-2 columns of several key chunks write one dQ part per chunk,
     // summed in chunk order (no atomics: the result does not depend on timing)
-    const int nkeys = p->b1 * p->c2, nb = bwd_max_block(p);
-    if (p->steps == 1 && nkeys > nb) {
+    const int nkeys = p->b1 * p->c2, nb = bwd_key_chunk(p);
+    if (nkeys > nb) {
       pl.dq2_parts = (nkeys + nb - 1) / nb;
       pl.off_dq2p = off; off = align_up(off + (size_t)pl.dq2_parts * pl.S * pl.N * pl.D * 4);
     }
@@ -243,11 +243,10 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
   return run_f32_128(pl, b, st, events, n_events);
 }
 
-// The backward covers stage-1 blocks whose keys fit LDS whole: T = 1 with
-// grouped K/V, any b1, padding, and row tiles / key segments (also padded);
-// T > 1 untiled (padding allowed) with stage-2 columns of one key chunk (b1
-// within the same limit); bf16 at head_dim 128 with T > 1 keeps to 64-key
-// blocks and columns (its split c tiles).
+// The backward covers stage-1 blocks whose keys fit LDS whole, any b1 (long
+// stage-2 columns are walked in key chunks), grouped K/V and padding: T = 1
+// also with row tiles / key segments; T > 1 untiled, where bf16 at head_dim
+// 128 keeps to 64-key blocks (its split c tiles).
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
@@ -255,10 +254,8 @@ ma_status validate_backward(const ma_problem* p) {
   const bool tiled = p->c1 != 1 || p->c2 != 1;
   if (tiled && p->steps > 1) return MA_ERR_UNSUPPORTED;
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
-  if (p->steps > 1) {
-    if (p->b1 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
-    if (p->dtype == MA_BF16 && p->head_dim == 128 && (p->b1 > 64 || p->b2 > 64)) return MA_ERR_UNSUPPORTED;
-  }
+  // bf16 at head_dim 128 with T > 1: its stage-1 blocks hold both c planes
+  if (p->steps > 1 && p->dtype == MA_BF16 && p->head_dim == 128 && p->b2 > 64) return MA_ERR_UNSUPPORTED;
   return MA_OK;
 }
 

@@ -158,9 +158,10 @@ def test_status_strings(lib):
     (dict(steps=2), 0),                       # T > 1: unrolled steps
     (dict(steps=3, dtype="f32", head_dim=128, seq_len=64 * 64, b1=64, b2=64), 0),
     (dict(steps=2, seq_len=250), 0),          # T > 1 padded
-    (dict(steps=2, seq_len=200 * 8, b1=200, b2=8), 2),   # T > 1: columns over one key chunk
+    (dict(steps=2, seq_len=200 * 8, b1=200, b2=8), 0),   # T > 1: columns over one key chunk
     (dict(steps=2, head_dim=128), 0),         # T > 1 bf16 at head_dim 128: 64-key blocks
-    (dict(steps=2, head_dim=128, seq_len=96 * 16, b1=96, b2=16), 2),   # ... columns over 64 keys
+    (dict(steps=2, head_dim=128, seq_len=96 * 16, b1=96, b2=16), 0),   # ... columns over 64 keys
+    (dict(steps=2, head_dim=128, seq_len=16 * 96, b1=16, b2=96), 2),   # ... blocks over 64 keys
     (dict(steps=2, kv_heads=1), 0),           # T > 1 grouped K/V
     (dict(c1=2), 0),                          # row tiles
     (dict(c1=2, c2=4), 0),                    # row tiles and key segments

@@ -295,6 +295,25 @@ def test_unrolled_steps_padded(dtype, d):
     check_backward(cfg)
 
 
+@pytest.mark.parametrize("dtype,d,b1,b2", [("f32", 64, 200, 8), ("bf16", 64, 300, 6), ("f32", 128, 100, 12),
+                                           ("bf16", 128, 96, 16), ("bf16", 128, 150, 8)])
+def test_unrolled_steps_long_columns(dtype, d, b1, b2):
+    """T = 2 with stage-2 columns of several key chunks (128 keys a chunk,
+    64 for fp32 and for bf16 at head_dim 128): each step takes a D pass and
+    one workgroup per key chunk, the earlier step through alpha and beta."""
+    check_backward(case(f"bwd T=2 long columns {dtype} d{d} b1={b1}", dtype, d, b1, b2, heads=2, steps=2))
+
+
+@pytest.mark.parametrize("with_y", [False, True])
+def test_unrolled_steps_long_columns_padded(with_y):
+    """T = 3, 200 blocks of 10 less 7 padding positions in front, grouped K/V;
+    with_y: the last step's row sums come from the forward's output."""
+    cfg = WorkloadConfig("case", f"bwd T=3 long padded y={with_y}", batch=1, heads=4, seq_len=200 * 10 - 7,
+                         head_dim=64, b1=200, b2=10, steps=3, dtype="bf16", data="normed", seed=71,
+                         pad="pre")
+    check_backward(cfg, kv_heads=2, with_y=with_y)
+
+
 def test_n16k_pad_t2_backward_sampled():
     """The padded headline shape (16284 tokens, 100 padding positions in
     front) at T = 2: two slices compared whole."""
