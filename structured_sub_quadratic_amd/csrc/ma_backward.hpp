@@ -687,9 +687,13 @@ static __global__ __launch_bounds__(256) void dq2_sum_kernel(const float* parts,
 // otherwise; each query's gradient goes to its exchange row (dq~).
 // S1_FIRSTP: S1_FIRST of a padded sequence, whose padding positions took the
 // fp32 tile means as queries (held as fp32 planes like q~; their gradient
-// goes to dqbar).
+// goes to dqbar).  S1_LAST_T, S1_MID_T and S1_FIRST_T: the three step modes
+// of several steps with row tiles and key segments, in the S1_TILED
+// geometry; every query gradient goes to its exchange row (step 0's queries
+// are q(k, i) and the fp32 tile means; tiled_dq_kernel finishes dQ).
 // ---------------------------------------------------------------------------
-enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3, S1_TILED = 4, S1_FIRSTP = 5 };
+enum { S1_ONLY = 0, S1_LAST = 1, S1_MID = 2, S1_FIRST = 3, S1_TILED = 4, S1_FIRSTP = 5, S1_LAST_T = 6,
+       S1_MID_T = 7, S1_FIRST_T = 8 };
 
 template <typename T, int D, int SM = S1_ONLY, int NBK = 0>
 __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(BwdParams p) {
@@ -702,13 +706,16 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
   constexpr int SK = SH::SK;                                 // key-tile strips of dK, dV per wave
   constexpr bool SPLIT = !std::is_same<T, float>::value;
   constexpr bool FP = SM == S1_FIRSTP;
-  constexpr bool FIRST = SM == S1_FIRST || FP;               // step 0 of several
-  constexpr bool QF = SM == S1_LAST || SM == S1_MID || FP;   // queries as fp32 planes
-  constexpr bool TL = SM == S1_TILED;
-  constexpr bool XQ = SM == S1_LAST || SM == S1_MID || TL;   // query gradients to exchange rows
-  constexpr bool WV = SM == S1_ONLY || SM == S1_LAST || TL;  // u = R V path
+  constexpr bool FT = SM == S1_FIRST_T;                      // tiled step 0 of several
+  constexpr bool LASTS = SM == S1_LAST || SM == S1_LAST_T;   // the last of several steps
+  constexpr bool MIDS = SM == S1_MID || SM == S1_MID_T;
+  constexpr bool FIRST = SM == S1_FIRST || FP || FT;         // step 0 of several
+  constexpr bool QF = LASTS || MIDS || FP || FT;             // queries as fp32 planes
+  constexpr bool TL = SM == S1_TILED || SM == S1_LAST_T || SM == S1_MID_T || FT;
+  constexpr bool XQ = LASTS || MIDS || TL;                   // query gradients to exchange rows
+  constexpr bool WV = SM == S1_ONLY || LASTS || SM == S1_TILED;   // u = R V path
   constexpr bool QP = QF && SPLIT;                           // queries carry a lo plane
-  constexpr bool DQO = SM == S1_ONLY || FIRST;               // dQ finished here
+  constexpr bool DQO = SM == S1_ONLY || SM == S1_FIRST || FP;     // dQ finished here
   constexpr size_t TPL = (size_t)D * LDR;                    // plane offset of the transposed grads
   constexpr size_t QPL = (size_t)RB * LDI;                   // plane offset of the query rows
   __shared__ __attribute__((aligned(16))) T ks[NB * LDI];
@@ -769,8 +776,20 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
     if constexpr (FP) {
       pqf.load_mixed(n, [&](int r) -> const T* { return row.valid(i0 + r) ? Q + row.at(i0 + r) * D : nullptr; },
                      [&](int r) { return static_cast<const float*>(p.qbt) + ((size_t)sl * p.b2 + i0 + r) * D; });
-    } else if constexpr (QF) {
-      pqf.load(n, [&](int r) { return p.qtil + (xb + i0 + r) * D; });
+    } else if constexpr (FT) {      // own row tile: q(k, i); the others: the fp32 tile means
+      pqf.load_mixed(n, [&](int r) -> const T* {
+        const int q = i0 + r, t = q / p.b2;
+        return t == own ? Q + row.at(q - t * p.b2) * D : nullptr;
+      }, [&](int r) { return static_cast<const float*>(p.qbt) + ((size_t)sl * p.c1 * p.b2 + i0 + r) * D; });
+    } else if constexpr (QF) {      // q~ rows are ordered (k, t, s, i)
+      pqf.load(n, [&](int r) {
+        if constexpr (TL) {
+          const int q = i0 + r, t = q / p.b2;
+          return p.qtil + (((((size_t)sl * p.b1 + k) * p.c1 + t) * p.c2 + sg) * p.b2 + q - t * p.b2) * D;
+        } else {
+          return p.qtil + (xb + i0 + r) * D;
+        }
+      });
     } else if constexpr (TL) {
       // a padding position of the own tile took the tile mean, as the other tiles
       pq.load(n, [&](int r) {
@@ -952,7 +971,7 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
   T* dV = static_cast<T*>(p.dv) + (size_t)sl * p.N * D;
   // several steps: the fp32 sum of dK over the later steps, all loads issued
   // before the first store
-  constexpr bool ADD = SM == S1_MID || FIRST;
+  constexpr bool ADD = MIDS || FIRST;
   float old[ADD ? SK : 1][ADD ? DT : 1][4];
   if constexpr (ADD) {
 #pragma unroll
@@ -976,9 +995,9 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
         const int key = m0 + 4 * g + e;
         if (key >= nb || (padded && (j0 + key < jlo || j0 + key >= jhi))) continue;
         const int64_t tok = row.at(j0 + key);
-        if constexpr (SM == S1_LAST || SM == S1_MID || FIRST) {   // several steps
+        if constexpr (LASTS || MIDS || FIRST) {   // several steps
           const size_t at = ((size_t)sl * p.N + tok) * D + d;
-          if constexpr (SM == S1_LAST) {
+          if constexpr (LASTS) {
             p.dkp[at] = adk[s][t][e];
             if (p.group > 1) p.dvp[at] = adv[s][t][e];
             else dV[tok * D + d] = from_f32<T>(adv[s][t][e]);
@@ -1105,15 +1124,22 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(const float* dkp, const 
 // exchange row (16 lanes a row): dalpha = dq~ / beta, written over dq~, and
 // dbeta = -dq~ . q~ / beta.  A row whose L weights all underflowed (beta =
 // 0) took the tile mean in the forward; no gradient is passed back there.
+// dq~ and beta are in exchange-row order (k, s, t, i), q~ in (k, t, s, i).
 template <int D>
 __global__ __launch_bounds__(256) void alpha_grad_kernel(float* dqt, const float* beta, const float* qnext,
-                                                          float* dbt, size_t rows) {
+                                                          float* dbt, size_t rows, int b2, int c1, int c2) {
   constexpr int PER = D / 16;                   // floats a lane
   const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / 16;
   const int l = threadIdx.x % 16;
   if (row >= rows) return;                      // whole groups of 16 lanes leave together
+  size_t qrow = row;
+  if (c1 * c2 > 1) {
+    const int i = (int)(row % b2), t = (int)(row / b2 % c1), s = (int)(row / b2 / c1 % c2);
+    const size_t ks = row / b2 / c1 / c2;       // (slice, block)
+    qrow = ((ks * c1 + t) * c2 + s) * b2 + i;
+  }
   float* gq = dqt + row * D + l * PER;
-  const float* qn = qnext + row * D + l * PER;
+  const float* qn = qnext + qrow * D + l * PER;
   f32x4 v[PER / 4];
   float dot = 0.f;
 #pragma unroll
@@ -1147,7 +1173,7 @@ BwdParams bwd_params(const Plan& pl, const BwdBufs& b) {
               kvp ? reinterpret_cast<float*>(ws + pl.off_dkp) : nullptr,
               kvp ? reinterpret_cast<float*>(ws + pl.off_dvp) : nullptr,
               reinterpret_cast<float*>(ws + pl.off_dlx),
-              pl.padded || pl.c1 > 1
+              pl.need_qbar
                   ? (pl.precise ? (const void*)(ws + pl.off_qbar) : (const void*)(ws + pl.off_qbar_lp))
                   : nullptr,
               pl.padded ? reinterpret_cast<float*>(ws + pl.off_dqbar) : nullptr,
@@ -1190,7 +1216,7 @@ void bwd_kv_out(const Plan& pl, const BwdParams& p, const BwdBufs& b, hipStream_
     else hipLaunchKernelGGL((stage1_bwd_kernel<T, D, SM>), grid, dim3(NTH), 0, st, p);             \
   } while (0)
 
-// T > 1 (untiled).  The forward
+// T > 1.  The forward
 // is recomputed step by step into per-step state (c, entropy, both
 // normalisers, the step's queries q~ and the column sums beta of L); then
 // the steps are differentiated in reverse.  The last step as for T = 1 but
@@ -1221,16 +1247,21 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   constexpr int NTH = BwdShape<T, D>::NTH, NTH2 = BwdShape<T, D>::NTH2;
   constexpr bool SPLITC = !std::is_same<T, float>::value && PRECISE;
   constexpr bool ONLY64 = SPLITC && D == 128;              // blocks and columns of <= 64 keys
-  const dim3 g2(grid1((size_t)pl.S * pl.b2)), g1(grid1((size_t)pl.S * pl.b1));
-  const size_t rows = (size_t)pl.S * pl.G;
+  // row tiles and key segments: stage 2 per (row tile, column), stage 1 per
+  // (block, segment)
+  const bool tiled = pl.c1 > 1 || pl.c2 > 1;
+  const size_t cols = (size_t)pl.S * pl.c1 * pl.b2, nq = (size_t)pl.S * pl.N * D;
+  const dim3 g2(grid1(cols)), g1(grid1((size_t)pl.S * pl.b1 * pl.c2));
+  const size_t rows = (size_t)pl.S * pl.G;                 // stage-2 rows
+  const size_t xrows = rows * pl.c1 * pl.c2;               // exchange rows
   BwdParams p = bwd_params<T, D>(pl, b);
-  const bool k2 = pl.b1 <= 64;                            // 64-key stage-2 build
+  const int nkeys = pl.b1 * pl.c2;                         // keys of a stage-2 column
+  const bool k2 = nkeys <= 64;                             // 64-key stage-2 build
   // columns of several key chunks
   constexpr int NBK = ONLY64 ? 64 : 0;                    // the chunked build
   constexpr int NBC = BwdShape<T, D, NBK>::NB, RGC = BwdShape<T, D, NBK>::RG, RBC = BwdShape<T, D, NBK>::RB;
-  const bool chunked = pl.b1 > NBC;
-  const int nkc = (pl.b1 + NBC - 1) / NBC;
-  const size_t cols = (size_t)pl.S * pl.b2, nq = (size_t)pl.S * pl.N * D;
+  const bool chunked = nkeys > NBC;
+  const int nkc = (nkeys + NBC - 1) / NBC;
   const dim3 grs(grid1(cols * ((pl.rt + RGC * RBC - 1) / (RGC * RBC)))), gks(grid1(cols * nkc));
   const dim3 gsum(grid1((nq / 4 + 255) / 256));
   if (chunked) {                         // D = dY . y, or a D pass; then the key chunks
@@ -1244,7 +1275,8 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
   } else {
     MA_BWD2(S2_COLUMN, SPLITC, k2, g2);
   }
-  MA_BWD1(S1_LAST, g1);
+  if (tiled) MA_BWD1(S1_LAST_T, g1);
+  else MA_BWD1(S1_LAST, g1);
   for (int t = pl.T - 2; t >= 0; --t) {
     const Plan sp = step_plan(pl, t);
     char* ws = b.ws;
@@ -1253,10 +1285,10 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
     p.h2x = reinterpret_cast<const float*>(ws + sp.off_h2);
     p.lse2 = reinterpret_cast<const float*>(ws + sp.off_lse2);
     p.qtil = reinterpret_cast<const float*>(ws + sp.off_qtil);
-    hipLaunchKernelGGL((alpha_grad_kernel<D>), dim3(grid1((rows * 16 + 255) / 256)), dim3(256), 0, st, p.dqt,
+    hipLaunchKernelGGL((alpha_grad_kernel<D>), dim3(grid1((xrows * 16 + 255) / 256)), dim3(256), 0, st, p.dqt,
                        reinterpret_cast<const float*>(ws + sp.off_beta),
                        reinterpret_cast<const float*>(ws + step_plan(pl, t + 1).off_qtil),
-                       reinterpret_cast<float*>(ws + pl.off_dbt), rows);
+                       reinterpret_cast<float*>(ws + pl.off_dbt), xrows, pl.b2, pl.c1, pl.c2);
     if (chunked) {                       // the parts of dQ add to those of later steps
       hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_ROWSUM_A, SPLITC, NBK>), grs, dim3(NTH2), 0, st, p);
       hipLaunchKernelGGL((stage2_bwd_kernel<T, D, S2_KEYS_A, SPLITC, NBK>), gks, dim3(NTH2), 0, st, p);
@@ -1264,11 +1296,19 @@ ma_status run_bwd_steps_t(const Plan& pl, const BwdBufs& b, hipStream_t st) {
     } else {
       MA_BWD2(S2_ALPHA, SPLITC, k2, g2);
     }
-    if (t > 0) MA_BWD1(S1_MID, g1);
-    else if (pl.padded) MA_BWD1(S1_FIRSTP, g1);
-    else MA_BWD1(S1_FIRST, g1);
+    if (tiled) {
+      if (t > 0) MA_BWD1(S1_MID_T, g1);
+      else MA_BWD1(S1_FIRST_T, g1);
+    } else {
+      if (t > 0) MA_BWD1(S1_MID, g1);
+      else if (pl.padded) MA_BWD1(S1_FIRSTP, g1);
+      else MA_BWD1(S1_FIRST, g1);
+    }
   }
-  if (pl.padded)
+  if (tiled)                            // dQ from the step-0 query gradients and the stage-2 parts
+    hipLaunchKernelGGL((tiled_dq_kernel<T, D>), g2, dim3(512), 0, st, p.dqt, p.dq2, static_cast<T*>(b.dq),
+                       pl.map, (int)pl.N, pl.b1, pl.b2, pl.c1, pl.c2);
+  else if (pl.padded)
     hipLaunchKernelGGL((qbar_grad_kernel<T>), dim3(grid1((size_t)pl.S * pl.b2)), dim3(128), 0, st, p.dqbar,
                        static_cast<T*>(b.dq), pl.map, (int)pl.N, D);
   if (pl.group > 1) bwd_kv_out<T, D>(pl, p, b, st);

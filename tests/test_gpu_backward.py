@@ -250,6 +250,35 @@ def test_video_tiled_backward_sampled():
     check_backward(WORKLOADS["video_tiled"], slices=[(0, 0), (0, 5)])
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("f32", 128), ("bf16", 128)])
+@pytest.mark.parametrize("c1,c2", [(2, 2), (2, 1), (1, 2), (4, 2)])
+def test_tiled_unrolled_steps(dtype, d, c1, c2):
+    """Row tiles and key segments at T = 2: each step's tiled L gives the
+    next queries q~[k, i, t, s] = alpha / beta over the rows of tile t."""
+    check_backward(case(f"bwd tiled {c1}x{c2} T=2 {dtype} d{d}", dtype, d, 16, 16, data="iid", c1=c1, c2=c2,
+                        steps=2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiled_unrolled_steps_ragged(dtype):
+    """T = 3 with ragged tiles: 48 blocks of 52 as 3 x 2 tiles."""
+    check_backward(case(f"bwd tiled 3x2 T=3 ragged {dtype}", dtype, 64, 48, 52, data="normed", c1=3, c2=2,
+                        steps=3))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128), ("bf16", 128)])
+def test_tiled_unrolled_steps_long_columns(dtype, d):
+    """T = 2, 2 x 2 tiles with columns of 200 stage-2 keys (several chunks)."""
+    b2 = 24 if d == 64 else 16
+    check_backward(case(f"bwd tiled 2x2 T=2 b1=100 {dtype} d{d}", dtype, d, 100, b2, heads=1, c1=2, c2=2,
+                        steps=2))
+
+
+def test_tiled_unrolled_steps_grouped_kv():
+    cfg = case("bwd tiled T=2 gqa", "bf16", 64, 32, 24, batch=2, heads=4, c1=2, c2=3, steps=2)
+    check_backward(cfg, kv_heads=1)
+
+
 @pytest.mark.parametrize("pad", ["pre", "post"])
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("f32", 128), ("bf16", 128)])
 def test_tiled_padded(pad, dtype, d):
