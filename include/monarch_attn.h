@@ -250,8 +250,8 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * and key segments c1, c2 (whose other-tile queries route their gradient
  * through the tile means of the real rows), also together; steps > 1 (the
  * gradient through every unrolled step, each step's L feeding the next
- * step's queries) with padding or with row tiles and key segments (not
- * both), and for bf16 at head_dim 128 b2 <= 64.
+ * step's queries) with padding and with row tiles and key segments (also
+ * together), and for bf16 at head_dim 128 b2 <= 64.
  * Any b1: stage-2 columns longer than one key chunk are walked chunk by
  * chunk.  Other problems return MA_ERR_UNSUPPORTED.
  * With MA_FLAG_REUSE_FORWARD_STATE the forward state is read from the

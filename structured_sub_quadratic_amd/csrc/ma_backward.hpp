@@ -776,10 +776,10 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH)) void stage1_bwd_kernel(
     if constexpr (FP) {
       pqf.load_mixed(n, [&](int r) -> const T* { return row.valid(i0 + r) ? Q + row.at(i0 + r) * D : nullptr; },
                      [&](int r) { return static_cast<const float*>(p.qbt) + ((size_t)sl * p.b2 + i0 + r) * D; });
-    } else if constexpr (FT) {      // own row tile: q(k, i); the others: the fp32 tile means
+    } else if constexpr (FT) {      // own row tile: q(k, i); the others and padding: the fp32 tile means
       pqf.load_mixed(n, [&](int r) -> const T* {
-        const int q = i0 + r, t = q / p.b2;
-        return t == own ? Q + row.at(q - t * p.b2) * D : nullptr;
+        const int q = i0 + r, t = q / p.b2, i = q - t * p.b2;
+        return t == own && (!padded || row.valid(i)) ? Q + row.at(i) * D : nullptr;
       }, [&](int r) { return static_cast<const float*>(p.qbt) + ((size_t)sl * p.c1 * p.b2 + i0 + r) * D; });
     } else if constexpr (QF) {      // q~ rows are ordered (k, t, s, i)
       pqf.load(n, [&](int r) {

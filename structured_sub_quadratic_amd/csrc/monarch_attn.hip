@@ -245,14 +245,13 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
 
 // The backward covers stage-1 blocks whose keys fit LDS whole, any b1 (long
 // stage-2 columns are walked in key chunks), grouped K/V, padding, and row
-// tiles / key segments (not together with padding when T > 1); bf16 at
-// head_dim 128 with T > 1 keeps to 64-key blocks (its split c tiles).
+// tiles / key segments, at any T; bf16 at head_dim 128 with T > 1 keeps to
+// 64-key blocks (its split c tiles).
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
   if (p->causal > 0 && p->causal < p->b1) return MA_ERR_UNSUPPORTED;   // forward only
   const bool tiled = p->c1 != 1 || p->c2 != 1;
-  if (tiled && p->steps > 1 && (int64_t)p->b1 * p->b2 != p->seq_len) return MA_ERR_UNSUPPORTED;   // padded
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
   // bf16 at head_dim 128 with T > 1: its stage-1 blocks hold both c planes
   if (p->steps > 1 && p->dtype == MA_BF16 && p->head_dim == 128 && p->b2 > 64) return MA_ERR_UNSUPPORTED;

@@ -166,7 +166,7 @@ def test_status_strings(lib):
     (dict(c1=2), 0),                          # row tiles
     (dict(c1=2, c2=4), 0),                    # row tiles and key segments
     (dict(c1=2, steps=2), 0),                 # tiled T > 1
-    (dict(c1=2, c2=2, steps=2, seq_len=250), 2),   # tiled T > 1 padded
+    (dict(c1=2, c2=2, steps=2, seq_len=250), 0),   # tiled T > 1 padded
     (dict(c2=2, seq_len=250), 0),             # tiled and padded
     (dict(c1=4, c2=2, seq_len=250, flags=ma.MA_FLAG_PAD_FRONT), 0),   # tiled, padded in front
     (dict(kv_heads=1), 0),                    # grouped K/V

@@ -274,6 +274,17 @@ def test_tiled_unrolled_steps_long_columns(dtype, d):
                         steps=2))
 
 
+@pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_tiled_unrolled_steps_padded(pad, dtype, d):
+    """T = 2 with 3 x 2 tiles on 205 tokens in 15 blocks of 14: padding
+    positions start from the tile means and carry no L row at any step."""
+    cfg = WorkloadConfig("case", f"bwd tiled T=2 pad={pad} {dtype} d{d}", batch=1, heads=2,
+                         seq_len=15 * 14 - 5, head_dim=d, b1=15, b2=14, steps=2, dtype=dtype, data="iid",
+                         seed=73, c1=3, c2=2, pad=pad)
+    check_backward(cfg)
+
+
 def test_tiled_unrolled_steps_grouped_kv():
     cfg = case("bwd tiled T=2 gqa", "bf16", 64, 32, 24, batch=2, heads=4, c1=2, c2=3, steps=2)
     check_backward(cfg, kv_heads=1)
