@@ -21,6 +21,7 @@ import numpy as np
 import torch
 
 from .layouts import grid_index
+from .monarch import causal_allowed
 
 
 def _softmax_masked(z, mask):
@@ -41,11 +42,14 @@ def _real_mean(q, rows):
     return (q * rows[..., None]).sum(0) / n[:, None]
 
 
-def forward_slice(qg, kg, vg, steps, scale, c1=1, c2=1, real=None):
+def forward_slice(qg, kg, vg, steps, scale, c1=1, c2=1, real=None, causal=0):
     """One slice in grid order: qg, kg, vg [b1, b2, d] float64 tensors
     (requires_grad allowed).  Same steps as oracle.monarch.forward_tiled
-    (which with c1 = c2 = 1 is the untiled method).  Returns y [b1, b2, dv]."""
+    (which with c1 = c2 = 1 is the untiled method); causal > 0 masks the
+    L-update as there (query block l takes key block k only when
+    floor(k / causal) <= floor(l / causal)).  Returns y [b1, b2, dv]."""
     b1, b2, d = qg.shape
+    allow = torch.as_tensor(causal_allowed(b1, causal))               # [l, k]
     sw = b2 // c2
     real = torch.ones((b1, b2), dtype=torch.bool) if real is None else torch.as_tensor(real)
     rq = real                                       # real query rows (l, i)
@@ -72,6 +76,7 @@ def forward_slice(qg, kg, vg, steps, scale, c1=1, c2=1, real=None):
         for t in range(c1):
             rows = torch.nonzero(tile == t).flatten()
             w = torch.einsum("lid,kisd->ilks", q[rows], C[:, :, t]) + HR[:, :, t].permute(1, 0, 2)[:, None]
+            w = w.masked_fill(~allow[rows][None, :, :, None], float("-inf"))
             Lt = torch.softmax(w.reshape(b2, rows.numel(), b1 * c2), dim=-1).reshape(w.shape)
             Ls.append(Lt * rq[rows].T[:, :, None, None])
         L = torch.cat(Ls, dim=1)                                         # [i, l, k, s]
@@ -98,7 +103,7 @@ def forward_slice(qg, kg, vg, steps, scale, c1=1, c2=1, real=None):
 
 
 def backward(Q, K, V, dY, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat", fhw=None,
-             pad="post", slices=None):
+             pad="post", slices=None, causal=0):
     """dQ, dK, dV (float64 NumPy) of <dY, Y(Q, K, V)> for [B, H, N, d] inputs
     (K, V may have fewer heads: grouped-query attention, their gradients sum
     over the query heads of a group).  slices: optional list of (b, h) query
@@ -125,7 +130,7 @@ def backward(Q, K, V, dY, b1, b2, steps, c1=1, c2=1, scale=None, layout="flat", 
         v = torch.tensor(V[b, h // group], requires_grad=True)
         zero = torch.zeros((), dtype=torch.float64)
         grid_of = lambda x: torch.where(real[..., None], x[g], zero)     # token order -> grid
-        y = forward_slice(grid_of(q), grid_of(k), grid_of(v), steps, scale, c1, c2, real)
+        y = forward_slice(grid_of(q), grid_of(k), grid_of(v), steps, scale, c1, c2, real, causal)
         dyg = torch.where(real[..., None], torch.as_tensor(dY[b, h])[g], zero)
         (y * dyg).sum().backward()
         dQ[b, h] = q.grad.numpy()

@@ -888,6 +888,10 @@ GRAD_CASES = [
     dict(b1=4, b2=6, c1=2, c2=3, T=2, N=24, pad="post", H=2, Hkv=2),
     dict(b1=4, b2=6, c1=1, c2=1, T=2, N=21, pad="pre", H=2, Hkv=2),
     dict(b1=3, b2=5, c1=1, c2=1, T=1, N=15, pad="post", H=4, Hkv=2),
+    # block-causal (the mask on the L-update), untiled at T = 2, tiled, padded
+    dict(b1=4, b2=6, c1=1, c2=1, T=2, N=24, pad="post", H=2, Hkv=2, causal=1),
+    dict(b1=4, b2=6, c1=2, c2=3, T=2, N=24, pad="post", H=2, Hkv=2, causal=2),
+    dict(b1=4, b2=6, c1=1, c2=1, T=1, N=21, pad="pre", H=2, Hkv=2, causal=1),
 ]
 
 
@@ -897,14 +901,15 @@ def test_backward_transcription_matches_forward(case):
     b1, b2, N = case["b1"], case["b2"], case["N"]
     Q = rng.standard_normal((1, case["H"], N, 5))
     K, V = (rng.standard_normal((1, case["Hkv"], N, 5)) for _ in range(2))
-    r = oracle.forward(Q, K, V, b1, b2, case["T"], case["c1"], case["c2"], pad=case["pad"])
+    causal = case.get("causal", 0)
+    r = oracle.forward(Q, K, V, b1, b2, case["T"], case["c1"], case["c2"], pad=case["pad"], causal=causal)
     g, real = padded_grid(N, b1, b2, case["pad"])
     gi, rm = torch.as_tensor(np.maximum(g, 0)), torch.as_tensor(real)
     grp = case["H"] // case["Hkv"]
     for h in range(case["H"]):
         tg = lambda x: torch.where(rm[..., None], torch.as_tensor(x)[gi], torch.zeros((), dtype=torch.float64))
         y = obw.forward_slice(tg(Q[0, h]), tg(K[0, h // grp]), tg(V[0, h // grp]), case["T"],
-                              1 / np.sqrt(5), case["c1"], case["c2"], rm).detach().numpy()
+                              1 / np.sqrt(5), case["c1"], case["c2"], rm, causal).detach().numpy()
         np.testing.assert_allclose(y[real], r["y"][0, h][g[real]], atol=1e-13, rtol=0)
 
 
@@ -918,7 +923,7 @@ def test_backward_matches_finite_differences(case):
     Q = rng.standard_normal((1, case["H"], N, 5))
     K, V = (rng.standard_normal((1, case["Hkv"], N, 5)) for _ in range(2))
     dY = rng.standard_normal(Q.shape)
-    kw = dict(c1=case["c1"], c2=case["c2"], pad=case["pad"])
+    kw = dict(c1=case["c1"], c2=case["c2"], pad=case["pad"], causal=case.get("causal", 0))
     dQ, dK, dV = obw.backward(Q, K, V, dY, b1, b2, T, **kw)
 
     def f(q, k, v):
