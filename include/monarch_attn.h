@@ -157,8 +157,8 @@ typedef struct {
                           the objective runs over the allowed entries, the
                           L-update is a softmax over the allowed keys and the
                           R-update keeps its form.  g >= b1 masks nothing.
-                          Forward only (the backward returns
-                          MA_ERR_UNSUPPORTED for a mask that masks). */
+                          The backward differentiates the masked method
+                          (masked L entries carry no gradient). */
 } ma_problem;
 
 /* Optional exports (device pointers, each may be NULL), always fp32/fp64.
@@ -251,7 +251,8 @@ ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const v
  * through the tile means of the real rows), also together; steps > 1 (the
  * gradient through every unrolled step, each step's L feeding the next
  * step's queries) with padding and with row tiles and key segments (also
- * together), and for bf16 at head_dim 128 b2 <= 64.
+ * together), and for bf16 at head_dim 128 b2 <= 64.  Block-causal use
+ * (causal) at any of these.
  * Any b1: stage-2 columns longer than one key chunk are walked chunk by
  * chunk.  Other problems return MA_ERR_UNSUPPORTED.
  * With MA_FLAG_REUSE_FORWARD_STATE the forward state is read from the

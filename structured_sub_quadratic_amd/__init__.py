@@ -230,12 +230,12 @@ def forward_noalloc(q, k, v, b1, b2, out, steps=1, c1=1, c2=1, scale=None, layou
 
 
 def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw=None,
-             workspace=None, out=None, pad="post", reuse_forward_state=False, y=None):
+             workspace=None, out=None, pad="post", reuse_forward_state=False, y=None, causal=0):
     """Gradients (dq, dk, dv) of <dy, forward(q, k, v, ...)> on the current
     stream.  Covers what monarch_attn_backward documents (blocks of at most
-    128 keys; k, v may have fewer heads; T = 1 with pad as in forward or with
-    tiles c1, c2; T > 1 untiled (pad allowed) with b1 within the same limit,
-    bf16 at head_dim 128 with b1, b2 <= 64).
+    128 keys, any b1; k, v may have fewer heads; pad, tiles c1, c2 and
+    causal as in forward, at any T; bf16 at head_dim 128 with T > 1 keeps to
+    b2 <= 64).
     out: optional (dq, dk, dv) tensors to write.
     reuse_forward_state (T = 1): `workspace` holds the state a forward call
     of the same inputs left there (that call was given this workspace, of at
@@ -262,7 +262,7 @@ def backward(q, k, v, dy, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat"
     flags = (MA_FLAG_PAD_FRONT if pad == "pre" else 0) | \
         (MA_FLAG_REUSE_FORWARD_STATE if reuse_forward_state else 0)
     prob = make_problem(B, H, N, D, b1, b2, steps, c1, c2, scale, q.dtype, layout, fhw, flags,
-                        kv_heads=Hkv)
+                        kv_heads=Hkv, causal=causal)
     ws_bytes = backward_workspace_size(prob)
     if reuse_forward_state and workspace is None:
         raise ValueError("reuse_forward_state needs the workspace the forward call used")

@@ -62,6 +62,7 @@ struct BwdParams {
   int S, N, b1, b2, c1, c2;         // c1 row tiles, c2 key segments
   float sc, sc2;                    // scale, scale * log2(e)
   int heads, group;                 // K/V slice of query slice sl: kv_slice(sl, heads, group)
+  int causal;                       // 0, or grid blocks per causal unit (keys past causal_key_end get no L)
 };
 
 // NBK: keys held in LDS (0: the largest that fits, 128; 64 for fp32 with
@@ -492,8 +493,10 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
-          // padding rows carry no L row (no upstream gradient, no next-query weight)
-          const bool ok = row < nr && key < nb && (!padded || col.valid(r0 + l0s + row));
+          // padding rows carry no L row (no upstream gradient, no next-query weight);
+          // block-causal use: keys past the row's bound carry no L entry
+          const bool ok = row < nr && key < nb && (!padded || col.valid(r0 + l0s + row)) &&
+                          (!p.causal || k0 + key < causal_key_end(r0 + l0s + row, p.causal, p.b1, p.c2));
           const float pv = ok ? __builtin_amdgcn_exp2f(s[t][e] * p.sc2 + h2k[key] - lsel[row]) : 0.f;
           const float dv = ok ? dp[t][e] + (AL ? dbk[key] : 0.f) : 0.f;
           if (store) {
@@ -1182,7 +1185,7 @@ BwdParams bwd_params(const Plan& pl, const BwdBufs& b) {
               pl.T > 1 ? reinterpret_cast<const float*>(ws + pl.off_dbt) : nullptr,
               pl.xlo,
               pl.map, (int)pl.S, (int)pl.N, pl.b1, pl.b2, pl.c1, pl.c2, pl.scale, pl.sc2, pl.heads,
-              pl.group};
+              pl.group, pl.causal};
 }
 
 // dK, dV from their fp32 shares (grouped K/V: summed over the group).

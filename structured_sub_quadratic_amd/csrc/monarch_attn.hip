@@ -250,7 +250,6 @@ ma_status forward_impl(const ma_problem* p, const void* q, const void* k, const 
 ma_status validate_backward(const ma_problem* p) {
   const ma_status s = validate_problem(p);
   if (s != MA_OK) return s;
-  if (p->causal > 0 && p->causal < p->b1) return MA_ERR_UNSUPPORTED;   // forward only
   const bool tiled = p->c1 != 1 || p->c2 != 1;
   if (p->b2 > bwd_max_block(p)) return MA_ERR_UNSUPPORTED;
   // bf16 at head_dim 128 with T > 1: its stage-1 blocks hold both c planes

@@ -177,7 +177,7 @@ def test_status_strings(lib):
     (dict(seq_len=96 * 96, b1=96, b2=96, head_dim=128, dtype="f32"), 2),   # fp32 d128: 64 max
     (dict(seq_len=64 * 64, b1=64, b2=64, head_dim=128, dtype="f32"), 0),
     (dict(steps=0), 1),
-    (dict(causal=1), 2),                      # block-causal: forward only
+    (dict(causal=1), 0),                      # block-causal
     (dict(causal=16), 0),                     # a unit of all 16 blocks masks nothing
     (dict(causal=-1), 1),
 ])

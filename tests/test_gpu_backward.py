@@ -25,7 +25,7 @@ def _gpu():
     ma._lib.load()          # raise loudly if the library is missing
 
 
-def run_backward(cfg, Q, K, V, dY, with_y=False):
+def run_backward(cfg, Q, K, V, dY, with_y=False, causal=0):
     import torch
     import structured_sub_quadratic_amd as ma
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
@@ -34,9 +34,9 @@ def run_backward(cfg, Q, K, V, dY, with_y=False):
     y = None
     if with_y:        # the forward's output: row sums of the softmax gradient from dY . y
         y = ma.forward(tq, tk, tv, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2, layout=cfg.layout,
-                       fhw=cfg.fhw, pad=cfg.pad)
+                       fhw=cfg.fhw, pad=cfg.pad, causal=causal)
     dq, dk, dv = ma.backward(tq, tk, tv, tdy, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                             layout=cfg.layout, fhw=cfg.fhw, pad=cfg.pad, y=y)
+                             layout=cfg.layout, fhw=cfg.fhw, pad=cfg.pad, y=y, causal=causal)
     torch.cuda.synchronize()
     return tuple(x.float().cpu().numpy() for x in (dq, dk, dv))
 
@@ -47,16 +47,16 @@ def upstream(cfg, seed=77):
     return round_to_bf16(dY) if cfg.dtype == "bf16" else dY
 
 
-def check_backward(cfg, slices=None, tol=None, kv_heads=None, with_y=False):
+def check_backward(cfg, slices=None, tol=None, kv_heads=None, with_y=False, causal=0):
     Q, K, V = make_inputs(cfg)
     if kv_heads is not None:        # grouped-query attention: keep the first kv_heads
         K, V = (np.ascontiguousarray(X[:, :kv_heads]) for X in (K, V))
     dY = upstream(cfg)
-    got = run_backward(cfg, Q, K, V, dY, with_y)
+    got = run_backward(cfg, Q, K, V, dY, with_y, causal)
     all_slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     slices = all_slices if slices is None else slices
     ref = obw.backward(Q, K, V, dY, cfg.b1, cfg.b2, cfg.steps, cfg.c1, cfg.c2,
-                       layout=cfg.layout, fhw=cfg.fhw, slices=slices, pad=cfg.pad)
+                       layout=cfg.layout, fhw=cfg.fhw, slices=slices, pad=cfg.pad, causal=causal)
     tol = TOL[cfg.dtype] if tol is None else tol
     group = cfg.heads // K.shape[1]
     kv_slices = sorted({(b, h // group) for (b, h) in slices})
@@ -482,3 +482,42 @@ def test_backward_is_deterministic(case):
         torch.cuda.synchronize()
         for name, a, b in zip(("dQ", "dK", "dV"), first, again):
             assert torch.equal(a, b), (case, name)
+
+
+# ---------------------------------------------------------------------------
+# Block-causal use: query block l takes key block k only when
+# floor(k / g) <= floor(l / g); the masked L entries carry no gradient.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("g,steps,c1,c2", [(1, 1, 1, 1), (4, 1, 1, 1), (2, 1, 2, 2), (1, 2, 1, 1), (2, 3, 1, 1),
+                                           (2, 2, 2, 2)])
+def test_block_causal(dtype, g, steps, c1, c2):
+    cfg = case(f"bwd causal g={g} T={steps} {c1}x{c2} {dtype}", dtype, 64, 16, 16, data="iid", steps=steps,
+               c1=c1, c2=c2)
+    check_backward(cfg, causal=g)
+
+
+@pytest.mark.parametrize("with_y", [False, True])
+@pytest.mark.parametrize("steps", [1, 2])
+def test_block_causal_long_columns(with_y, steps):
+    """200 blocks of 8 in causal units of 16 blocks, head_dim 128: the key
+    chunks past a row's bound hold only masked entries."""
+    cfg = case(f"bwd causal long T={steps} y={with_y}", "bf16", 128, 200, 8, heads=2, steps=steps)
+    check_backward(cfg, causal=16, with_y=with_y)
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
+def test_block_causal_padded(pad):
+    cfg = WorkloadConfig("case", f"bwd causal vit pad={pad}", batch=1, heads=2, seq_len=197, head_dim=64,
+                         b1=15, b2=14, steps=2, dtype="bf16", data="iid", seed=79, pad=pad)
+    check_backward(cfg, causal=3)
+
+
+def test_block_causal_video_frames():
+    """A 4 x 6 x 8 latent in the (fh, w) layout with units of h = 6 blocks:
+    causal over frames."""
+    cfg = WorkloadConfig("case", "bwd causal frames", batch=1, heads=2, seq_len=4 * 6 * 8, head_dim=64,
+                         b1=24, b2=8, steps=1, dtype="bf16", data="normed", seed=81, layout="fh_w",
+                         fhw=(4, 6, 8))
+    check_backward(cfg, causal=6)
