@@ -791,10 +791,10 @@ __global__ __launch_bounds__(256) void stage2_alpha_kernel(Stage2Params p, float
 // the exchange written by phase 1 is read by phase 2 while it is still warm
 // in the Infinity Cache.  Both phases use NW waves per workgroup.
 // ---------------------------------------------------------------------------
-template <int D, int NW, int KTB, bool PRECISE>
+template <int D, int NW, int KTB, bool PRECISE, int KC2 = KT>
 __global__ __launch_bounds__(NW * WAVE) void fused_async_kernel(Stage1Params p1, Stage2Params p2) {
   typedef Stage1Async<D, NW, KTB, true, PRECISE> S1;
-  typedef Stage2Async<D, NW, 1, true, PRECISE> S2;
+  typedef Stage2Async<D, NW, 1, true, PRECISE, KC2> S2;
   constexpr int BYTES = S1::LDS_BYTES > S2::LDS_BYTES ? S1::LDS_BYTES : S2::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[BYTES];
   S1::run(p1, lds);

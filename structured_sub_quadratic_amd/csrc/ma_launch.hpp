@@ -43,6 +43,15 @@ template <int D> inline int stage2_waves(int rows) {
   return D == 128 ? 8 : async_waves(rows);
 }
 
+// Stage 2 of bf16 at head_dim 64 with 8 waves (b2 > 64, one row tile) takes
+// a column of 65 to 128 keys as one chunk of 128 (fewer chunk switches); the
+// staged and the fused copied-tile launches chunk alike, so they give the
+// same result.
+inline bool one_chunk2(const Plan& pl) {
+  return pl.b2 > 64 && pl.c1 == 1 && pl.b1 * pl.c2 > KT && pl.b1 * pl.c2 <= 2 * KT && !pl.causal &&
+         !pl.padded;
+}
+
 template <class K, class P>
 void launch_persistent(K kernel, int threads, size_t items, const P& p, hipStream_t st) {
   const size_t g = resident_slots(kernel, threads, items);
@@ -115,7 +124,9 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           // one 64-key tile, 8 waves otherwise
 #define MA_FA(NW, KTB) e = launch_cooperative(fused_async_kernel<D, NW, KTB, PRECISE>, items, args, st, NW * WAVE)
           if constexpr (D == 64) {
-            if (ktb == 64) MA_FA(4, 64); else MA_FA(8, 128);
+            if (ktb == 64) MA_FA(4, 64);
+            else if (one_chunk2(pl)) e = launch_cooperative(fused_async_kernel<D, 8, 128, PRECISE, 2 * KT>, items, args, st, 8 * WAVE);
+            else MA_FA(8, 128);
           } else {
             if (ktb == 64) MA_FA(4, 64); else MA_FA(4, 128);
           }
@@ -294,7 +305,17 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           if (pl.padded) {
             if (nw == 8) { if (last) MA_A2P(8, true); else MA_A2P(8, false); }
             else { if (last) MA_A2P(4, true); else MA_A2P(4, false); }
-          } else if (nw == 8) { if (last) MA_A2(8, true); else MA_A2(8, false); }
+          } else if (nw == 8) {
+            bool one = false;            // a column of up to 128 keys in one chunk
+            if constexpr (D == 64) {
+              if (one_chunk2(pl)) {
+                one = true;
+                if (last) launch_persistent(stage2_async_kernel<D, 8, 1, true, PRECISE, 2 * KT>, 8 * WAVE, items, p, st);
+                else launch_persistent(stage2_async_kernel<D, 8, 1, false, PRECISE, 2 * KT>, 8 * WAVE, items, p, st);
+              }
+            }
+            if (!one) { if (last) MA_A2(8, true); else MA_A2(8, false); }
+          }
           else { if (last) MA_A2(4, true); else MA_A2(4, false); }
 #undef MA_A2
 #undef MA_A2P
