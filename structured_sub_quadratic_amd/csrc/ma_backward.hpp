@@ -486,6 +486,16 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
         }
       }
       float part[4] = {0.f, 0.f, 0.f, 0.f};
+      // block-causal use: keys at or past kend[e] (chunk-local) carry no L
+      // entry of this lane's row e (computed once per strip)
+      int kend[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kend[e] = nb;
+      if (p.causal) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kend[e] = min(nb, causal_key_end(r0 + l0s + m0 + 4 * g + e, p.causal, p.b1, p.c2) - k0);
+      }
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
         if (t >= nt) continue;
@@ -493,10 +503,8 @@ __global__ __launch_bounds__((BwdShape<T, D, NBK>::NTH2)) void stage2_bwd_kernel
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
-          // padding rows carry no L row (no upstream gradient, no next-query weight);
-          // block-causal use: keys past the row's bound carry no L entry
-          const bool ok = row < nr && key < nb && (!padded || col.valid(r0 + l0s + row)) &&
-                          (!p.causal || k0 + key < causal_key_end(r0 + l0s + row, p.causal, p.b1, p.c2));
+          // padding rows carry no L row (no upstream gradient, no next-query weight)
+          const bool ok = row < nr && key < kend[e] && (!padded || col.valid(r0 + l0s + row));
           const float pv = ok ? __builtin_amdgcn_exp2f(s[t][e] * p.sc2 + h2k[key] - lsel[row]) : 0.f;
           const float dv = ok ? dp[t][e] + (AL ? dbk[key] : 0.f) : 0.f;
           if (store) {
