@@ -234,8 +234,22 @@ struct Stage1Async {
   const int nitems = p.S * p.b1 * p.nqg;
   const int slot0 = wave * 16;            // this wave's first slot within a query group
 
-  auto issue = [&](int item, char* b) {
-    const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
+  // An item (slice, block k, query group qg), decoded once when its copies
+  // are issued and handed to the step that computes it.
+  struct It {
+    int item, qg, k, sl;
+  };
+  auto decode = [&](int item) {
+    It r;
+    r.item = item;
+    r.qg = item % p.nqg;
+    const int q = item / p.nqg;
+    r.k = q % p.b1;
+    r.sl = q / p.b1;
+    return r;
+  };
+  auto issue = [&](const It& it, char* b) {
+    const int qg = it.qg, k = it.k, sl = it.sl;
     const AxisMap am = p.map.template row_axis<PAD>(k);
     auto tok = [&](int r) -> int64_t { if constexpr (PAD) return am.at(r); else return am.raw(r); };
     const int kvs = kv_slice(sl, p.heads, p.group);
@@ -251,6 +265,12 @@ struct Stage1Async {
     // positions (k, i)
     const T* Q = static_cast<const T*>(p.q) + (size_t)sl * p.N * D;
     const T* QB = p.qbar_lp ? static_cast<const T*>(p.qbar_lp) + (size_t)sl * p.c1 * p.b2 * D : Q;
+    if (p.c1 == 1 && !PAD) {        // one row tile: slot i is row (k, i) of Q
+      SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) {
+        return Q + am.raw(min(qg * QG + r, p.nqs - 1)) * D;
+      }, QG);
+      return;
+    }
     const int town = k / p.rt;
     SwzTile<D>::template load<QG, NW>(b + SM::QOFF, [&](int r) {
       const int slot = min(qg * QG + r, p.nqs - 1);
@@ -322,8 +342,8 @@ struct Stage1Async {
   };
 
   // item from buffer cur; the next item of this workgroup is copied into nxt
-  auto step = [&](int item, char* cur, char* nxt) {
-    const int qg = item % p.nqg, k = (item / p.nqg) % p.b1, sl = item / (p.nqg * p.b1);
+  auto step = [&](const It& it, char* cur, char* nxt, It& next) {
+    const int item = it.item, qg = it.qg, k = it.k, sl = it.sl;
     wait_vmem();
     __syncthreads();              // cur landed everywhere; nobody reads nxt any more
     if constexpr (QF) {
@@ -341,7 +361,11 @@ struct Stage1Async {
         core.qf[0][ks_] = *reinterpret_cast<const frag*>(
             cur + SM::QOFF + SwzTile<D>::offset(slot0 + lane % 16, 4 * ks_ + g));
     }
-    if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, nxt);
+    next.item = item + (int)gridDim.x;
+    if (next.item < nitems) {
+      next = decode(next.item);
+      issue(next, nxt);
+    }
     flush(cur);                   // the previous item's last segment
     const char* vt = WITH_U ? cur + SM::TILE : cur;
     if constexpr (KTB == 2 * KT) {
@@ -391,16 +415,17 @@ struct Stage1Async {
 
   // Workgroup b takes items pos(b), pos(b) + G, ... where pos groups the
   // workgroups of one XCD on consecutive items.
-  int item = (int)xcd_swizzle(blockIdx.x, gridDim.x);
-  if (item >= nitems) return;
-  issue(item, buf_a);
+  const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+  if (item0 >= nitems) return;
+  It ia = decode(item0), ib;
+  issue(ia, buf_a);
   char* last = buf_a;
   for (;;) {
-    step(item, buf_a, buf_b);
-    if ((item += gridDim.x) >= nitems) break;
-    step(item, buf_b, buf_a);
+    step(ia, buf_a, buf_b, ib);
+    if (ib.item >= nitems) break;
+    step(ib, buf_b, buf_a, ia);
     last = buf_b;
-    if ((item += gridDim.x) >= nitems) break;
+    if (ia.item >= nitems) break;
     last = buf_a;
   }
   flush(last);
