@@ -455,27 +455,36 @@ def test_video_layout_variants(variant):
     check_backward(cfg)
 
 
-@pytest.mark.parametrize("case", ["video", "tiled"])
+@pytest.mark.parametrize("case", ["video", "tiled", "tiled_t2_causal"])
 def test_backward_is_deterministic(case):
     """Two backward calls on the same inputs give bitwise equal dQ, dK, dV:
     columns of several key chunks write one dQ part per chunk, summed in
-    chunk order, and the row sums of the softmax gradients are added in strip
-    order, so nothing depends on the timing of workgroups or waves.  The
-    video latent's 630-key columns run five key chunks."""
+    chunk order (at earlier steps onto the later steps' sum), and the row
+    sums of the softmax gradients are added in strip order, so nothing
+    depends on the timing of workgroups or waves.  The video latent's
+    630-key columns run five key chunks; the last case runs T = 2 with tiles
+    and a block-causal mask over 600-key columns."""
     import torch
     import structured_sub_quadratic_amd as ma
+    causal = 0
     if case == "video":
         cfg = WORKLOADS["video"]
-    else:
+    elif case == "tiled":
         cfg = WorkloadConfig("case", "bwd det tiled", batch=1, heads=3, seq_len=300 * 24,
                                         head_dim=64, b1=300, b2=24, steps=1, dtype="bf16",
                                         data="normed", seed=63, c1=2, c2=2)
+    else:
+        cfg = WorkloadConfig("case", "bwd det tiled T=2 causal", batch=1, heads=2, seq_len=300 * 24,
+                             head_dim=64, b1=300, b2=24, steps=2, dtype="bf16", data="normed", seed=64,
+                             c1=2, c2=2)
+        causal = 50
     Q, K, V = make_inputs(cfg)
     dY = upstream(cfg)
     dev = torch.device("cuda:0")
     tq, tk, tv, tdy = (torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
                        for x in (Q, K, V, dY))
-    args = dict(b1=cfg.b1, b2=cfg.b2, steps=1, c1=cfg.c1, c2=cfg.c2, layout=cfg.layout, fhw=cfg.fhw)
+    args = dict(b1=cfg.b1, b2=cfg.b2, steps=cfg.steps, c1=cfg.c1, c2=cfg.c2, layout=cfg.layout, fhw=cfg.fhw,
+                causal=causal)
     first = [g.clone() for g in ma.backward(tq, tk, tv, tdy, **args)]
     for _ in range(2):
         again = ma.backward(tq, tk, tv, tdy, **args)
