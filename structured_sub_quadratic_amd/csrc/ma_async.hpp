@@ -440,6 +440,133 @@ __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Stage 1 of a single step (u as well) for blocks of at most 64 keys at
+// head_dim 128 (the video latent's 52-key blocks), first step on the plain c
+// path, unpadded, with or without row tiles and key segments.  Four waves
+// take 64 query slots (t, i) of a block k -- row (k, i) of Q on k's own row
+// tile, the bf16 tile mean of (t, i) elsewhere -- and the K and V tiles of
+// the next item stream into the other of two LDS buffers; each wave reads its
+// query rows of the next item straight into registers.  Per key segment the
+// weighted sums c = R K and u = R V run one after the other on the same
+// probabilities, so only one 128-wide accumulator is live and two workgroups
+// share a CU (two waves a SIMD).
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stage1SmallSmem {
+  static constexpr int TILE = KT * SwzTile<D>::RB;       // one K or V tile (64 rows)
+  static constexpr int BUF = 2 * TILE;
+  static constexpr int LDS_BYTES = 2 * BUF + 4 * WaveRows<D>::BYTES;
+};
+
+template <int D>
+__global__ __launch_bounds__(4 * WAVE, 2) void stage1_small_kernel(Stage1Params p) {
+  typedef bf16 T;
+  constexpr int NW = 4, QG = NW * 16;
+  typedef FlashCore<T, D, D, 1, KT, true, true, false, 0> Core;
+  typedef typename Core::frag frag;
+  typedef Stage1SmallSmem<D> SM;
+  __shared__ __attribute__((aligned(1024))) char lds[SM::LDS_BYTES];
+  char* const buf_a = lds;
+  char* const buf_b = lds + SM::BUF;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
+  char* const stg = lds + 2 * SM::BUF + wave * WaveRows<D>::BYTES;
+  const int nitems = p.S * p.b1 * p.nqg;
+  const int slot0 = wave * 16;                    // this wave's first slot within a query group
+  struct It {
+    int item, qg, k, sl;
+  };
+  auto decode = [&](int item) {
+    It r;
+    r.item = item;
+    r.qg = item % p.nqg;
+    const int q = item / p.nqg;
+    r.k = q % p.b1;
+    r.sl = q / p.b1;
+    return r;
+  };
+  frag qn[Core::NKS];
+  auto issue = [&](const It& it, char* b) {
+    const AxisMap am = p.map.template row_axis<false>(it.k);
+    const int kvs = kv_slice(it.sl, p.heads, p.group);
+    const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
+    const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
+    SwzTile<D>::template load<KT, NW>(b, [&](int r) { return K + am.raw(r) * D; }, p.b2);
+    SwzTile<D>::template load<KT, NW>(b + SM::TILE, [&](int r) { return V + am.raw(r) * D; }, p.b2);
+    // slot (t, i): row (k, i) of Q on the own row tile, the tile mean of (t, i) elsewhere
+    const int q = min(it.qg * QG + slot0 + lane % 16, p.nqs - 1);
+    const int t = p.c1 == 1 ? 0 : q / p.b2, i = q - t * p.b2;
+    const T* src = t == it.k / p.rt
+        ? static_cast<const T*>(p.q) + ((size_t)it.sl * p.N + am.raw(i)) * D
+        : static_cast<const T*>(p.qbar_lp) + ((size_t)it.sl * p.c1 * p.b2 + q) * D;
+#pragma unroll
+    for (int ks_ = 0; ks_ < Core::NKS; ++ks_) qn[ks_] = *reinterpret_cast<const frag*>(src + ks_ * 32 + g * 8);
+  };
+  Core core;
+  // rows of the wave's 16 queries (o normalised) to exchange rows xb + slot
+  auto store_rows = [&](T* x, size_t xb, int qg0) {
+    bf16x4 v[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) v[dt] = __builtin_convertvector(core.o[0][dt], bf16x4);
+    WaveRows<D>::put(stg, v);
+    WaveRows<D>::drain(stg, [&](int r) -> T* {
+      const int q = qg0 + slot0 + r;
+      return q < p.nqs ? x + (xb + q) * D : nullptr;
+    });
+  };
+  auto step = [&](const It& it, const char* cur, char* nxt, It& next) {
+    wait_vmem();
+    __syncthreads();              // cur landed everywhere; nobody reads nxt any more
+#pragma unroll
+    for (int ks_ = 0; ks_ < Core::NKS; ++ks_) core.qf[0][ks_] = qn[ks_];
+    next.item = it.item + (int)gridDim.x;
+    if (next.item < nitems) {
+      next = decode(next.item);
+      issue(next, nxt);
+    }
+    const int qg0 = it.qg * QG, q = qg0 + slot0 + lane % 16;
+    const char* vt = cur + SM::TILE;
+    for (int s = 0; s < p.c2; ++s) {
+      const int klo = s * p.sw, khi = klo + p.sw;
+      const bool whole = klo == 0 && khi == KT;
+      core.init();
+      core.scores_v(SwzKeys<D>(cur, nullptr), klo / 16, (khi + 15) / 16);
+      if (whole) core.template softmax_step<false, false>(nullptr, p.sc2, klo, khi);
+      else core.template softmax_step<false, true>(nullptr, p.sc2, klo, khi);
+      // c = R K
+      if (whole) core.template pv<false>(SwzValuesT<D>(cur, cur), klo, khi);
+      else core.template pv<true>(SwzValuesT<D>(cur, cur), klo, khi);
+      float lse2[1], h2[1];
+      core.finish(lse2, h2, p.sc2);
+      const size_t xb = x_row(p.b1, p.b2, p.c1, p.c2, it.sl, it.k, s, 0, 0);   // slot t*b2 + i -> xb + slot
+      store_rows(static_cast<T*>(p.cx), xb, qg0);
+      if (g == 0 && q < p.nqs) {
+        p.h2x[xb + q] = h2[0];
+        p.lser[xb + q] = lse2[0];
+      }
+      // u = R V on the same probabilities
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) core.o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (whole) core.template pv<false>(SwzValuesT<D>(vt, vt), klo, khi);
+      else core.template pv<true>(SwzValuesT<D>(vt, vt), klo, khi);
+      const float inv = 1.f / wave_sum_x16x32(core.l[0]);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) core.o[0][dt] *= inv;
+      store_rows(static_cast<T*>(p.ux), xb, qg0);
+    }
+  };
+  const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+  if (item0 >= nitems) return;
+  It ia = decode(item0), ib;
+  issue(ia, buf_a);
+  for (;;) {
+    step(ia, buf_a, buf_b, ib);
+    if (ib.item >= nitems) break;
+    step(ib, buf_b, buf_a, ia);
+    if (ia.item >= nitems) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Stage 2.  Item = (slice, column i, row tile t, query group of NW*NQ*16
 // rows); its b1*c2 keys are streamed in chunks of KT.  A workgroup walks the
 // flat sequence of (item, chunk) units of its items, copying unit u+1 into

@@ -219,7 +219,17 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_A1K(NW) do { if (ktb == 64) MA_A1U(NW, 64); else MA_A1U(NW, 128); } while (0)
 #define MA_A1P(NW) do { if (last) MA_A1X(NW, true); else MA_A1X(NW, false); } while (0)
 #define MA_A1X(NW, U) launch_persistent(stage1_async_kernel<D, NW, 128, U, PRECISE, true>, NW * WAVE, items, p, st)
-          if (pl.padded) {     // padded sequences: 128-key tiles only
+          bool small = false;
+          if constexpr (D == 128 && !PRECISE) {
+            // one step over blocks of at most 64 keys: c and u in turn, two
+            // workgroups a CU
+            if (last && step == 0 && !pl.padded && pl.b2 <= KT && (pl.c1 == 1 || qbar_lp)) {
+              small = true;
+              launch_persistent(stage1_small_kernel<D>, 4 * WAVE, items, p, st);
+            }
+          }
+          if (small) {
+          } else if (pl.padded) {     // padded sequences: 128-key tiles only
             if (nw == 8) { if constexpr (D == 64) MA_A1P(8); }
             else MA_A1P(4);
           } else if constexpr (D == 64) { if (nw == 8) MA_A1K(8); else MA_A1K(4); }
