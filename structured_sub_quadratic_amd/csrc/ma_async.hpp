@@ -591,7 +591,7 @@ struct Stage2AsyncSmem {
 // chunk (where LDS allows; otherwise it prefetches them into registers),
 // and stores an item's outputs as soon as its last chunk is done, which
 // keeps the registers for the arithmetic.
-template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false>
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false, bool CAUSAL = true>
 struct Stage2Async {
   typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV, KC> SM0;
   static constexpr int STG = WITH_PV ? NW * WaveRows<D>::BYTES : 0;
@@ -738,10 +738,13 @@ struct Stage2Async {
     }
   };
   auto unit = [&](const char* cb, float* bias, char* nxt) -> bool {
+    const int nvalid = min(KC, p.nkeys - ch * KC);
     wait_vmem();
     if (wave == NW - 1) {
+      // keys past the end of the column get a bias that zeroes their
+      // probabilities, so a partial chunk takes the full-chunk path
 #pragma unroll
-      for (int j = 0; j < KC / WAVE; ++j) bias[lane + WAVE * j] = hn[j];
+      for (int j = 0; j < KC / WAVE; ++j) bias[lane + WAVE * j] = lane + WAVE * j < nvalid ? hn[j] : -1e30f;
     }
     __syncthreads();              // cb landed everywhere; nobody reads nxt any more
     if (ch == 0) {
@@ -767,11 +770,16 @@ struct Stage2Async {
     }
     if (more) issue(nchk == 0 ? nx : cur, nchk, nxt);
 
-    const int nvalid = min(KC, p.nkeys - ch * KC);
     int how = CH_WHOLE;
-    if (p.causal)
+    if constexpr (!CAUSAL) {
+      core.scores_v(SwzKeys<D>(cb + SM::HI, cb + SM::LO), 0, Core::MT);
+      core.template softmax_step<true, false>(bias, p.sc2, 0, KC);
+      if constexpr (WITH_PV) core.template pv<false>(SwzValuesT<D>(cb + SM::U, cb + SM::U), 0, KC);
+      how = CH_SKIP;
+    } else if (p.causal) {
       how = causal_chunk<NQ>(core, p, cur.t, row_of(cur.qg, 0) - lane % 16,
                              [&](int n) { return row_of(cur.qg, n); }, ch * KC, nvalid);
+    }
     const bool rowmask = how == CH_ROWMASK;
     if (how != CH_SKIP) {
       core.scores_v(SwzKeys<D>(cb + SM::HI, cb + SM::LO), 0, Core::MT);
@@ -795,9 +803,9 @@ struct Stage2Async {
   }
 };
 
-template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false>
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false, bool CAUSAL = true>
 __global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p) {
-  typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE, KC, PAD> S;
+  typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE, KC, PAD, CAUSAL> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
 }

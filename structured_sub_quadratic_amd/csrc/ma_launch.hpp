@@ -310,7 +310,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
                          pl.sc2, pl.xlo, pl.causal};
           const size_t items = (size_t)S * pl.b2 * pl.c1 * p.nqg;
           const bool last = kind == L_STAGE2_LAST;
-#define MA_A2(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE>, NW * WAVE, items, p, st)
+#define MA_A2C(NW, PV, C) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE, KT, false, C>, NW * WAVE, items, p, st)
+#define MA_A2(NW, PV) do { if (pl.causal) MA_A2C(NW, PV, true); else MA_A2C(NW, PV, false); } while (0)
 #define MA_A2P(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE, KT, true>, NW * WAVE, items, p, st)
           if (pl.padded) {
             if (nw == 8) { if (last) MA_A2P(8, true); else MA_A2P(8, false); }
@@ -320,14 +321,16 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
             if constexpr (D == 64) {
               if (one_chunk2(pl)) {
                 one = true;
-                if (last) launch_persistent(stage2_async_kernel<D, 8, 1, true, PRECISE, 2 * KT>, 8 * WAVE, items, p, st);
-                else launch_persistent(stage2_async_kernel<D, 8, 1, false, PRECISE, 2 * KT>, 8 * WAVE, items, p, st);
+                // (one_chunk2: no causal mask)
+                if (last) launch_persistent(stage2_async_kernel<D, 8, 1, true, PRECISE, 2 * KT, false, false>, 8 * WAVE, items, p, st);
+                else launch_persistent(stage2_async_kernel<D, 8, 1, false, PRECISE, 2 * KT, false, false>, 8 * WAVE, items, p, st);
               }
             }
             if (!one) { if (last) MA_A2(8, true); else MA_A2(8, false); }
           }
           else { if (last) MA_A2(4, true); else MA_A2(4, false); }
 #undef MA_A2
+#undef MA_A2C
 #undef MA_A2P
           break;
         }
