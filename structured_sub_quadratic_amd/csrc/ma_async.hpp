@@ -214,7 +214,11 @@ struct Stage1AsyncSmem {
 // QF: a step after the first of an untiled, unpadded run; the queries are
 // the fp32 next-step queries q~ (split into hi + lo when `split`), read from
 // global memory into registers, and no query tile is copied.
-template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false, bool QF = false>
+// FULL: every block fills the key tiles in one segment (b2 = KTB, c2 = 1,
+// unpadded); the build holds that path only, whose one update per tile keeps
+// the accumulators in place.
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false, bool QF = false,
+          bool FULL = false>
 struct Stage1Async {
   static constexpr int LDS_BYTES = 2 * Stage1AsyncSmem<D, NW, KTB, WITH_U>::BUF;
 
@@ -370,7 +374,7 @@ struct Stage1Async {
     const char* vt = WITH_U ? cur + SM::TILE : cur;
     if constexpr (KTB == 2 * KT) {
       // (padded: blocks whose keys are all real)
-      if (p.c2 == 1 && p.b2 == KTB && (!PAD || (p.map.key_lo(k) == 0 && p.map.key_hi(k) == KTB))) {
+      if (FULL || (p.c2 == 1 && p.b2 == KTB && (!PAD || (p.map.key_lo(k) == 0 && p.map.key_hi(k) == KTB)))) {
         // two full key tiles: both score products are issued before the
         // first softmax, so the second tile's MFMAs overlap the first
         // tile's exp and sums (the online-softmax updates keep their order)
@@ -385,6 +389,13 @@ struct Stage1Async {
         collect(qg, k, sl, 0);
         return;
       }
+    } else if constexpr (FULL) {
+      core.init();
+      core.scores_v(SwzKeys<D>(cur, nullptr), 0, KT / 16);
+      core.template softmax_step<false, false>(nullptr, p.sc2, 0, KT);
+      core.template pv<false>(SwzValuesT<D>(cur, vt), 0, KT);
+      collect(qg, k, sl, 0);
+      return;
     }
     for (int s = 0; s < p.c2; ++s) {
       int klo = s * p.sw, khi = klo + p.sw;
@@ -432,9 +443,11 @@ struct Stage1Async {
   }
 };
 
-template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false, bool QF = false>
+template <int D, int NW, int KTB, bool WITH_U, bool PRECISE, bool PAD = false, bool QF = false,
+          bool FULL = false>
 __global__ __launch_bounds__(NW * WAVE) void stage1_async_kernel(Stage1Params p) {
-  typedef Stage1Async<D, NW, KTB, WITH_U, PRECISE, PAD, QF> S;
+  static_assert(!FULL || !PAD, "whole tiles: unpadded");
+  typedef Stage1Async<D, NW, KTB, WITH_U, PRECISE, PAD, QF, FULL> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
 }
@@ -527,14 +540,13 @@ __global__ __launch_bounds__(4 * WAVE, 2) void stage1_small_kernel(Stage1Params 
     const char* vt = cur + SM::TILE;
     for (int s = 0; s < p.c2; ++s) {
       const int klo = s * p.sw, khi = klo + p.sw;
-      const bool whole = klo == 0 && khi == KT;
+      // (the masked path for every segment, whole tiles included: one code
+      // path keeps the accumulators in place)
       core.init();
       core.scores_v(SwzKeys<D>(cur, nullptr), klo / 16, (khi + 15) / 16);
-      if (whole) core.template softmax_step<false, false>(nullptr, p.sc2, klo, khi);
-      else core.template softmax_step<false, true>(nullptr, p.sc2, klo, khi);
+      core.template softmax_step<false, true>(nullptr, p.sc2, klo, khi);
       // c = R K
-      if (whole) core.template pv<false>(SwzValuesT<D>(cur, cur), klo, khi);
-      else core.template pv<true>(SwzValuesT<D>(cur, cur), klo, khi);
+      core.template pv<true>(SwzValuesT<D>(cur, cur), klo, khi);
       float lse2[1], h2[1];
       core.finish(lse2, h2, p.sc2);
       const size_t xb = x_row(p.b1, p.b2, p.c1, p.c2, it.sl, it.k, s, 0, 0);   // slot t*b2 + i -> xb + slot
@@ -546,8 +558,7 @@ __global__ __launch_bounds__(4 * WAVE, 2) void stage1_small_kernel(Stage1Params 
       // u = R V on the same probabilities
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) core.o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (whole) core.template pv<false>(SwzValuesT<D>(vt, vt), klo, khi);
-      else core.template pv<true>(SwzValuesT<D>(vt, vt), klo, khi);
+      core.template pv<true>(SwzValuesT<D>(vt, vt), klo, khi);
       const float inv = 1.f / wave_sum_x16x32(core.l[0]);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) core.o[0][dt] *= inv;

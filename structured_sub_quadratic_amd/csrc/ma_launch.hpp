@@ -216,9 +216,15 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_A1Q(NW, KTB, U, Q) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE, false, Q>, NW * WAVE, items, p, st)
 #define MA_A1(NW, KTB, U) do { if (qf) MA_A1Q(NW, KTB, U, true); else MA_A1Q(NW, KTB, U, false); } while (0)
 #define MA_A1U(NW, KTB) do { if (last) MA_A1(NW, KTB, true); else MA_A1(NW, KTB, false); } while (0)
-#define MA_A1K(NW) do { if (ktb == 64) MA_A1U(NW, 64); else MA_A1U(NW, 128); } while (0)
+#define MA_A1F(NW, KTB, U, Q) launch_persistent(stage1_async_kernel<D, NW, KTB, U, PRECISE, false, Q, true>, NW * WAVE, items, p, st)
+#define MA_A1UF(NW, KTB) do { if (last) { if (qf) MA_A1F(NW, KTB, true, true); else MA_A1F(NW, KTB, true, false); } \
+                              else { if (qf) MA_A1F(NW, KTB, false, true); else MA_A1F(NW, KTB, false, false); } } while (0)
+#define MA_A1K(NW) do { if (ktb == 64) { if (full) MA_A1UF(NW, 64); else MA_A1U(NW, 64); } \
+                        else if (full) MA_A1UF(NW, 128); else MA_A1U(NW, 128); } while (0)
 #define MA_A1P(NW) do { if (last) MA_A1X(NW, true); else MA_A1X(NW, false); } while (0)
 #define MA_A1X(NW, U) launch_persistent(stage1_async_kernel<D, NW, 128, U, PRECISE, true>, NW * WAVE, items, p, st)
+          // blocks that fill their key tiles in one segment: a build with that path only
+          const bool full = pl.c2 == 1 && pl.b2 == ktb;
           bool small = false;
           if constexpr (D == 128 && !PRECISE) {
             // one step over blocks of at most 64 keys: c and u in turn, two
@@ -237,6 +243,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #undef MA_A1
 #undef MA_A1Q
 #undef MA_A1U
+#undef MA_A1F
+#undef MA_A1UF
 #undef MA_A1K
 #undef MA_A1P
 #undef MA_A1X
