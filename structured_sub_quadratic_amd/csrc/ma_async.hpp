@@ -605,7 +605,12 @@ struct Stage2AsyncSmem {
 template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false, bool CAUSAL = true>
 struct Stage2Async {
   typedef Stage2AsyncSmem<D, split_x<bf16, PRECISE>(), WITH_PV, KC> SM0;
-  static constexpr int STG = WITH_PV ? NW * WaveRows<D>::BYTES : 0;
+  // y rows leave through a per-wave LDS staging tile (whole 16-byte row
+  // chunks per store), except in the builds of 32 rows a wave, which store
+  // straight from the accumulators (8 bytes a lane) and keep their LDS small
+  // enough for two workgroups a CU
+  static constexpr bool DIRECT_Y = WITH_PV && NQ > 1;
+  static constexpr int STG = WITH_PV && !DIRECT_Y ? NW * WaveRows<D>::BYTES : 0;
   static constexpr int QROWS = NQ * 16 * SwzTile<D>::RB;        // one wave's query rows
   // queries staged in LDS where they fit (else prefetched into registers)
   static constexpr bool QLDS = 2 * SM0::BUF + STG + NW * QROWS + 2 * KC * 4 <= 160 * 1024;
@@ -685,7 +690,7 @@ struct Stage2Async {
 
   frag qn[NQ][Core::NKS];
   typename Core::QLo qnl;
-  float hn[KC / WAVE];          // bias of the unit in flight (last wave, KC/64 keys a lane)
+  float hn[(KC + WAVE - 1) / WAVE];   // bias of the unit in flight (last wave)
   auto issue = [&](const Item& it, int ch, char* b) {
     const size_t row0 = it.base + (size_t)ch * KC * xs;
     const int nvalid = min(KC, p.nkeys - ch * KC);
@@ -695,7 +700,8 @@ struct Stage2Async {
     if constexpr (WITH_PV) copy_tile(b + SM::U, static_cast<const char*>(p.ux) + row0 * D * sizeof(T), nvalid);
     if (wave == NW - 1) {
 #pragma unroll
-      for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[row0 + (size_t)min(lane + WAVE * j, nvalid - 1) * xs];
+      for (int j = 0; j < (KC + WAVE - 1) / WAVE; ++j)
+        hn[j] = p.h2x[row0 + (size_t)min(min(lane + WAVE * j, KC - 1), nvalid - 1) * xs];
     }
     if (ch == 0) {
       if constexpr (QLDS) copy_queries(it);
@@ -710,7 +716,7 @@ struct Stage2Async {
   int ch = 0;
   issue(cur, 0, buf_a);
   Core core;
-  char* stg = stage_rows + (WITH_PV ? wave * WaveRows<D>::BYTES : 0);
+  char* stg = stage_rows + (STG ? wave * WaveRows<D>::BYTES : 0);
 
   // y rows and normalisers of the item just finished
   auto store = [&]() {
@@ -725,12 +731,24 @@ struct Stage2Async {
         bf16x4 y[D / 16];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) y[dt] = __builtin_convertvector(core.o[n][dt], bf16x4);
-        WaveRows<D>::put(stg, y);
-        WaveRows<D>::drain(stg, [&](int r) -> T* {
-          const int l = l0 + n * 16 + r;
-          if constexpr (PAD) return l < lend && am.valid(l) ? Y + am.at(l) * D : nullptr;
-          else return l < lend ? Y + am.raw(l) * D : nullptr;
-        });
+        if constexpr (DIRECT_Y) {
+          // lane (q, g) holds columns 16 dt + 4 g .. + 3 of row q
+          const int l = l0 + n * 16 + lane % 16;
+          T* dst = nullptr;
+          if constexpr (PAD) dst = l < lend && am.valid(l) ? Y + am.at(l) * D : nullptr;
+          else dst = l < lend ? Y + am.raw(l) * D : nullptr;
+          if (dst) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * g) = y[dt];
+          }
+        } else {
+          WaveRows<D>::put(stg, y);
+          WaveRows<D>::drain(stg, [&](int r) -> T* {
+            const int l = l0 + n * 16 + r;
+            if constexpr (PAD) return l < lend && am.valid(l) ? Y + am.at(l) * D : nullptr;
+            else return l < lend ? Y + am.raw(l) * D : nullptr;
+          });
+        }
       }
     }
 #pragma unroll
@@ -755,7 +773,8 @@ struct Stage2Async {
       // keys past the end of the column get a bias that zeroes their
       // probabilities, so a partial chunk takes the full-chunk path
 #pragma unroll
-      for (int j = 0; j < KC / WAVE; ++j) bias[lane + WAVE * j] = lane + WAVE * j < nvalid ? hn[j] : -1e30f;
+      for (int j = 0; j < (KC + WAVE - 1) / WAVE; ++j)
+        if (lane + WAVE * j < KC) bias[lane + WAVE * j] = lane + WAVE * j < nvalid ? hn[j] : -1e30f;
     }
     __syncthreads();              // cb landed everywhere; nobody reads nxt any more
     if (ch == 0) {
@@ -815,7 +834,7 @@ struct Stage2Async {
 };
 
 template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false, bool CAUSAL = true>
-__global__ __launch_bounds__(NW * WAVE) void stage2_async_kernel(Stage2Params p) {
+__global__ __launch_bounds__(NW * WAVE, NQ > 1 ? 2 : 1) void stage2_async_kernel(Stage2Params p) {
   typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE, KC, PAD, CAUSAL> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
@@ -965,7 +984,10 @@ __global__ __launch_bounds__(256) void stage2_alpha_kernel(Stage2Params p, float
 template <int D, int NW, int KTB, bool PRECISE, int KC2 = KT>
 __global__ __launch_bounds__(NW * WAVE) void fused_async_kernel(Stage1Params p1, Stage2Params p2) {
   typedef Stage1Async<D, NW, KTB, true, PRECISE> S1;
-  typedef Stage2Async<D, NW, 1, true, PRECISE, KC2> S2;
+  // head_dim 128 (fast path): the staged launch's stage 2 of 32 rows a wave
+  // and 32-key chunks, so that both give the same result
+  constexpr bool R32 = D == 128 && !PRECISE;
+  typedef Stage2Async<D, NW, R32 ? 2 : 1, true, PRECISE, R32 ? KT / 2 : KC2> S2;
   constexpr int BYTES = S1::LDS_BYTES > S2::LDS_BYTES ? S1::LDS_BYTES : S2::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[BYTES];
   S1::run(p1, lds);

@@ -113,8 +113,10 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
                           pl.sc2, 1, pl.xlo};
           p1.heads = pl.heads;
           p1.group = pl.group;
+          // (stage 2 at head_dim 128 on the fast path: 32 rows a wave)
+          const int qg2 = D == 128 && !PRECISE ? 2 * qg : qg;
           Stage2Params p2{b.q, b.y, cx, ux, h2, lse2, b.lse, pl.map,
-                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
+                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg2 - 1) / qg2,
                           pl.sc2, pl.xlo, pl.causal};
           const size_t items = std::max<size_t>((size_t)S * pl.b1 * p1.nqg, (size_t)S * pl.b2 * p2.nqg);
           void* args[] = {&p1, &p2};
@@ -312,7 +314,10 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     case L_STAGE2_LAST: {
       if constexpr (!is_f32<T>()) {
         {
-          const int nw = stage2_waves<D>(pl.rt), qg = nw * 16;
+          // last step at head_dim 128 (bidirectional, unpadded, fast path): 4
+          // waves of 32 rows, 32-key chunks, two workgroups a CU
+          const bool rows32 = D == 128 && !PRECISE && !pl.causal && !pl.padded && kind == L_STAGE2_LAST;
+          const int nw = rows32 ? 4 : stage2_waves<D>(pl.rt), qg = rows32 ? 128 : nw * 16;
           Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
                          S, N, pl.b1, pl.b2, pl.c1, pl.c2, pl.rt, pl.b1 * pl.c2, (pl.rt + qg - 1) / qg,
                          pl.sc2, pl.xlo, pl.causal};
@@ -321,7 +326,11 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_A2C(NW, PV, C) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE, KT, false, C>, NW * WAVE, items, p, st)
 #define MA_A2(NW, PV) do { if (pl.causal) MA_A2C(NW, PV, true); else MA_A2C(NW, PV, false); } while (0)
 #define MA_A2P(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE, KT, true>, NW * WAVE, items, p, st)
-          if (pl.padded) {
+          if constexpr (D == 128 && !PRECISE) {
+            if (rows32) launch_persistent(stage2_async_kernel<D, 4, 2, true, PRECISE, KT / 2, false, false>, 4 * WAVE, items, p, st);
+          }
+          if (rows32) {
+          } else if (pl.padded) {
             if (nw == 8) { if (last) MA_A2P(8, true); else MA_A2P(8, false); }
             else { if (last) MA_A2P(4, true); else MA_A2P(4, false); }
           } else if (nw == 8) {
