@@ -578,6 +578,165 @@ __global__ __launch_bounds__(4 * WAVE, 2) void stage1_small_kernel(Stage1Params 
 }
 
 // ---------------------------------------------------------------------------
+// Stage 1 of a single step (u as well) for blocks of 65-128 keys at
+// head_dim 64 (the 128 x 128 grid of a 16K sequence), unpadded, one row tile
+// and one segment.  Eight waves take the (up to) 128 query rows of block k;
+// the block's K and V rows (two 64-key tiles each) of the next item stream
+// into the other of two LDS buffers and each wave reads its query rows of
+// the next item straight into registers.  All 128 scores of a row are held
+// at once, so the softmax takes the row maximum over the whole block in one
+// pass; then c = R K and u = R V run one after the other on the same
+// probabilities with one 64-wide accumulator.  80 KB of LDS and at most 128
+// registers a lane: two workgroups share a CU, four waves a SIMD.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stage1Pair {
+  static constexpr int NW = 8, QG = NW * 16;
+  static constexpr int HALF = KT * SwzTile<D>::RB;        // one 64-row tile
+  static constexpr int TILE = 2 * HALF;                   // the K or V rows of a block
+  static constexpr int BUF = 2 * TILE;
+  static constexpr int LDS_BYTES = 2 * BUF + NW * WaveRows<D>::BYTES;
+
+  // the launches this body serves
+  __host__ __device__ static bool serves(int b2, int c1, int c2, bool padded) {
+    return b2 > KT && b2 <= 2 * KT && c1 == 1 && c2 == 1 && !padded;
+  }
+
+  __device__ static void run(const Stage1Params& p, char* lds) {
+    typedef bf16 T;
+    typedef FlashCore<T, D, D, 1, KT, true, true, false, 0> Core;
+    typedef typename Core::frag frag;
+    char* const buf_a = lds;
+    char* const buf_b = lds + BUF;
+    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
+    char* const stg = lds + 2 * BUF + wave * WaveRows<D>::BYTES;
+    const int nitems = p.S * p.b1 * p.nqg;
+    const int slot0 = wave * 16;
+    struct It {
+      int item, qg, k, sl;
+    };
+    auto decode = [&](int item) {
+      It r;
+      r.item = item;
+      r.qg = item % p.nqg;
+      const int q = item / p.nqg;
+      r.k = q % p.b1;
+      r.sl = q / p.b1;
+      return r;
+    };
+    frag qn[Core::NKS];
+    auto issue = [&](const It& it, char* b) {
+      const AxisMap am = p.map.template row_axis<false>(it.k);
+      const int kvs = kv_slice(it.sl, p.heads, p.group);
+      const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
+      const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
+      SwzTile<D>::template load<2 * KT, NW>(b, [&](int r) { return K + am.raw(r) * D; }, p.b2);
+      SwzTile<D>::template load<2 * KT, NW>(b + TILE, [&](int r) { return V + am.raw(r) * D; }, p.b2);
+      const int i = min(it.qg * QG + slot0 + lane % 16, p.nqs - 1);
+      const T* src = static_cast<const T*>(p.q) + ((size_t)it.sl * p.N + am.raw(i)) * D;
+#pragma unroll
+      for (int ks_ = 0; ks_ < Core::NKS; ++ks_) qn[ks_] = *reinterpret_cast<const frag*>(src + ks_ * 32 + g * 8);
+    };
+    Core core;
+    auto store_rows = [&](T* x, size_t xb, int qg0) {
+      bf16x4 v[D / 16];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) v[dt] = __builtin_convertvector(core.o[0][dt], bf16x4);
+      WaveRows<D>::put(stg, v);
+      WaveRows<D>::drain(stg, [&](int r) -> T* {
+        const int q = qg0 + slot0 + r;
+        return q < p.nqs ? x + (xb + q) * D : nullptr;
+      });
+    };
+    auto step = [&](const It& it, const char* cur, char* nxt, It& next) {
+      wait_vmem();
+      __syncthreads();              // cur landed everywhere; nobody reads nxt any more
+#pragma unroll
+      for (int ks_ = 0; ks_ < Core::NKS; ++ks_) core.qf[0][ks_] = qn[ks_];
+      next.item = it.item + (int)gridDim.x;
+      if (next.item < nitems) {
+        next = decode(next.item);
+        issue(next, nxt);
+      }
+      const int qg0 = it.qg * QG, q = qg0 + slot0 + lane % 16;
+      core.template scores_v<0>(SwzKeys<D>(cur, nullptr), 0, Core::MT);
+      core.template scores_v<1>(SwzKeys<D>(cur + HALF, nullptr), 0, Core::MT);
+      // softmax over the block: keys 16 mt + 4 g + r of each tile; keys past
+      // b2 (second tile) masked
+      {
+        constexpr float MASKED = -1e30f;
+        float zs[8 * Core::MT];
+#pragma unroll
+        for (int mt = 0; mt < Core::MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key1 = KT + mt * 16 + 4 * g + r;
+            zs[4 * mt + r] = core.s[0][mt][r];
+            const float z1 = key1 < p.b2 ? core.s2[0][mt][r] : MASKED;
+            core.s2[0][mt][r] = z1;
+            zs[4 * Core::MT + 4 * mt + r] = z1;
+          }
+        const float m = wave_max_x16x32(Core::tree_max(zs)) * p.sc2;   // base-2 units
+        float ps[8 * Core::MT], pz[4 * Core::MT];
+#pragma unroll
+        for (int j = 0; j < 8 * Core::MT; ++j) ps[j] = __builtin_amdgcn_exp2f(fmaf(zs[j], p.sc2, -m));
+#pragma unroll
+        for (int j = 0; j < 4 * Core::MT; ++j) pz[j] = fmaf(ps[2 * j], zs[2 * j], ps[2 * j + 1] * zs[2 * j + 1]);
+#pragma unroll
+        for (int mt = 0; mt < Core::MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            core.s[0][mt][r] = ps[4 * mt + r];
+            core.s2[0][mt][r] = ps[4 * Core::MT + 4 * mt + r];
+          }
+        core.m[0] = m;
+        core.l[0] = Core::tree_sum(ps);
+        core.e[0] = Core::tree_sum(pz);
+      }
+      const size_t xb = x_row(p.b1, p.b2, p.c1, p.c2, it.sl, it.k, 0, 0, 0);   // slot i -> xb + i
+      // c = R K
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) core.o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      core.template pv<false, 0>(SwzValuesT<D>(cur, cur), 0, KT);
+      core.template pv<false, 1>(SwzValuesT<D>(cur + HALF, cur + HALF), 0, KT);
+      float lse2[1], h2[1];
+      core.finish(lse2, h2, p.sc2);
+      store_rows(static_cast<T*>(p.cx), xb, qg0);
+      if (g == 0 && q < p.nqs) {
+        p.h2x[xb + q] = h2[0];
+        p.lser[xb + q] = lse2[0];
+      }
+      // u = R V on the same probabilities
+      const char* vt = cur + TILE;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) core.o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      core.template pv<false, 0>(SwzValuesT<D>(vt, vt), 0, KT);
+      core.template pv<false, 1>(SwzValuesT<D>(vt + HALF, vt + HALF), 0, KT);
+      const float inv = 1.f / wave_sum_x16x32(core.l[0]);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) core.o[0][dt] *= inv;
+      store_rows(static_cast<T*>(p.ux), xb, qg0);
+    };
+    const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+    if (item0 >= nitems) return;
+    It ia = decode(item0), ib;
+    issue(ia, buf_a);
+    for (;;) {
+      step(ia, buf_a, buf_b, ib);
+      if (ib.item >= nitems) break;
+      step(ib, buf_b, buf_a, ia);
+      if (ia.item >= nitems) break;
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(8 * WAVE, 4) void stage1_pair_kernel(Stage1Params p) {
+  __shared__ __attribute__((aligned(1024))) char lds[Stage1Pair<D>::LDS_BYTES];
+  Stage1Pair<D>::run(p, lds);
+}
+
+// ---------------------------------------------------------------------------
 // Stage 2.  Item = (slice, column i, row tile t, query group of NW*NQ*16
 // rows); its b1*c2 keys are streamed in chunks of KT.  A workgroup walks the
 // flat sequence of (item, chunk) units of its items, copying unit u+1 into
@@ -988,9 +1147,18 @@ __global__ __launch_bounds__(NW * WAVE) void fused_async_kernel(Stage1Params p1,
   // and 32-key chunks, so that both give the same result
   constexpr bool R32 = D == 128 && !PRECISE;
   typedef Stage2Async<D, NW, R32 ? 2 : 1, true, PRECISE, R32 ? KT / 2 : KC2> S2;
-  constexpr int BYTES = S1::LDS_BYTES > S2::LDS_BYTES ? S1::LDS_BYTES : S2::LDS_BYTES;
+  // head_dim 64, 8 waves, blocks of 65-128 keys in one segment: the staged
+  // launch's whole-block stage 1, so that both give the same result
+  constexpr bool PAIR = D == 64 && NW == 8 && KTB == 2 * KT && !PRECISE;
+  constexpr int B12 = S1::LDS_BYTES > S2::LDS_BYTES ? S1::LDS_BYTES : S2::LDS_BYTES;
+  constexpr int BYTES = PAIR && Stage1Pair<D>::LDS_BYTES > B12 ? Stage1Pair<D>::LDS_BYTES : B12;
   __shared__ __attribute__((aligned(1024))) char lds[BYTES];
-  S1::run(p1, lds);
+  if constexpr (PAIR) {
+    if (Stage1Pair<D>::serves(p1.b2, p1.c1, p1.c2, false)) Stage1Pair<D>::run(p1, lds);
+    else S1::run(p1, lds);
+  } else {
+    S1::run(p1, lds);
+  }
   __syncthreads();
   cooperative_groups::this_grid().sync();
   S2::run(p2, lds);

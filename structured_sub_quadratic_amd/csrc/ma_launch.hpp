@@ -228,6 +228,14 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           // blocks that fill their key tiles in one segment: a build with that path only
           const bool full = pl.c2 == 1 && pl.b2 == ktb;
           bool small = false;
+          if constexpr (D == 64 && !PRECISE) {
+            // one step over blocks of 65-128 keys: the whole block's softmax
+            // in one pass, c and u in turn, two workgroups a CU
+            if (last && step == 0 && nw == 8 && Stage1Pair<D>::serves(pl.b2, pl.c1, pl.c2, pl.padded)) {
+              small = true;
+              launch_persistent(stage1_pair_kernel<D>, 8 * WAVE, items, p, st);
+            }
+          }
           if constexpr (D == 128 && !PRECISE) {
             // one step over blocks of at most 64 keys: c and u in turn, two
             // workgroups a CU
