@@ -1000,6 +1000,121 @@ __global__ __launch_bounds__(NW * WAVE, NQ > 1 ? 2 : 1) void stage2_async_kernel
 }
 
 // ---------------------------------------------------------------------------
+// Stage 2 of the last step for columns of 65-128 keys at head_dim 64 (the
+// 128 x 128 grid of a 16K sequence), bidirectional, unpadded, one row tile:
+// an item is one column's query group of 128 rows, and its keys are one
+// 128-key chunk.  The same arithmetic as the general stage 2 on such a
+// column (one online-softmax update from a fresh state, then O += P U), with
+// a leaner data path: each wave reads its query rows of the next item into
+// registers, the bias row is staged by one wave, and y leaves straight from
+// the accumulators.  64 KB of LDS and at most 128 registers a lane, so two
+// workgroups share a CU at four waves a SIMD.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stage2Col {
+  static constexpr int NW = 8, QG = NW * 16, KC = 2 * KT;
+  static constexpr int TILE = KC * SwzTile<D>::RB;
+  static constexpr int BUF = 2 * TILE;                     // c tile, u tile
+  static constexpr int LDS_BYTES = 2 * BUF + 2 * KC * 4;
+
+  __host__ __device__ static bool serves(int b2, int c1, int nkeys, int causal, bool padded) {
+    return b2 > KT && c1 == 1 && nkeys > KT && nkeys <= KC && !causal && !padded;
+  }
+
+  __device__ static void run(const Stage2Params& p, char* lds) {
+    typedef bf16 T;
+    typedef FlashCore<T, D, D, 1, KC, false, true, false, 0> Core;
+    typedef typename Core::frag frag;
+    char* const buf_a = lds;
+    char* const buf_b = lds + BUF;
+    float* const bias_a = reinterpret_cast<float*>(lds + 2 * BUF);
+    float* const bias_b = bias_a + KC;
+    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
+    const int nitems = p.S * p.b2 * p.nqg;
+    const size_t xs = x_stride(p.b2, p.c1);
+    struct It {
+      int item, sl, i, qg;
+    };
+    auto decode = [&](int item) {
+      It it;
+      it.item = item;
+      it.qg = item % p.nqg; item /= p.nqg;
+      it.i = item % p.b2;
+      it.sl = item / p.b2;
+      return it;
+    };
+    auto row_of = [&](int qg) { return qg * QG + wave * 16 + lane % 16; };
+    frag qn[1][Core::NKS];
+    typename Core::QLo qnl;
+    float hn[KC / WAVE];            // bias of the item in flight (last wave)
+    auto issue = [&](const It& it, char* b) {
+      const size_t base = x_base(p.b1, p.b2, p.c1, p.c2, it.sl, 0, it.i);
+      const T* C = static_cast<const T*>(p.cx) + base * D;
+      const T* U = static_cast<const T*>(p.ux) + base * D;
+      SwzTile<D>::template load<KC, NW>(b, [&](int r) { return C + (size_t)r * xs * D; }, p.nkeys);
+      SwzTile<D>::template load<KC, NW>(b + TILE, [&](int r) { return U + (size_t)r * xs * D; }, p.nkeys);
+      if (wave == NW - 1) {
+#pragma unroll
+        for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[base + (size_t)min(lane + WAVE * j, p.nkeys - 1) * xs];
+      }
+      Core::fetch_queries([&](int) { return stage2_qsrc<T, D, false>(p, it.sl, it.i, 0, row_of(it.qg)); },
+                          Q_INPUT, qn, qnl);
+    };
+    Core core;
+    auto step = [&](const It& it, const char* cur, float* bias, char* nxt, It& next) {
+      wait_vmem();
+      if (wave == NW - 1) {
+        // keys past the end of the column: a bias that zeroes their probabilities
+#pragma unroll
+        for (int j = 0; j < KC / WAVE; ++j) bias[lane + WAVE * j] = lane + WAVE * j < p.nkeys ? hn[j] : -1e30f;
+      }
+      __syncthreads();              // cur and its bias landed everywhere; nobody reads nxt any more
+      core.init();
+      core.set_queries(qn, qnl);
+      next.item = it.item + (int)gridDim.x;
+      if (next.item < nitems) {
+        next = decode(next.item);
+        issue(next, nxt);
+      }
+      core.scores_v(SwzKeys<D>(cur, nullptr), 0, Core::MT);
+      core.template softmax_step<true, false>(bias, p.sc2, 0, KC);
+      core.template pv<false>(SwzValuesT<D>(cur + TILE, cur + TILE), 0, KC);
+      float lse2[1], h2[1];
+      core.finish(lse2, h2, p.sc2);
+      // y rows: lane (q, g) holds columns 16 dt + 4 g .. + 3 of row q
+      const AxisMap am = p.map.template col_axis<false>(it.i);
+      const int l = row_of(it.qg);
+      if (l < p.rt) {
+        T* dst = static_cast<T*>(p.y) + ((size_t)it.sl * p.N + am.raw(l)) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * g) = __builtin_convertvector(core.o[0][dt], bf16x4);
+        if (g == 0) {
+          p.lse2[((size_t)it.sl * p.b2 + it.i) * p.b1 + l] = lse2[0];
+          if (p.lse_out) p.lse_out[(size_t)it.sl * p.N + am.raw(l)] = lse2[0] * LN2;
+        }
+      }
+    };
+    const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+    if (item0 >= nitems) return;
+    It ia = decode(item0), ib;
+    issue(ia, buf_a);
+    for (;;) {
+      step(ia, buf_a, bias_a, buf_b, ib);
+      if (ib.item >= nitems) break;
+      step(ib, buf_b, bias_b, buf_a, ia);
+      if (ia.item >= nitems) break;
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(8 * WAVE, 4) void stage2_col_kernel(Stage2Params p) {
+  __shared__ __attribute__((aligned(1024))) char lds[Stage2Col<D>::LDS_BYTES];
+  Stage2Col<D>::run(p, lds);
+}
+
+// ---------------------------------------------------------------------------
 // A step before the last of an untiled, unpadded run whose columns hold at
 // most 64 rows and 64 keys: the L-update and the next step's queries in one
 // launch.  One workgroup of 4 waves per (slice, column i) copies the

@@ -347,7 +347,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
               if (one_chunk2(pl)) {
                 one = true;
                 // (one_chunk2: no causal mask)
-                if (last) launch_persistent(stage2_async_kernel<D, 8, 1, true, PRECISE, 2 * KT, false, false>, 8 * WAVE, items, p, st);
+                if (last && !PRECISE) launch_persistent(stage2_col_kernel<D>, 8 * WAVE, items, p, st);
+                else if (last) launch_persistent(stage2_async_kernel<D, 8, 1, true, PRECISE, 2 * KT, false, false>, 8 * WAVE, items, p, st);
                 else launch_persistent(stage2_async_kernel<D, 8, 1, false, PRECISE, 2 * KT, false, false>, 8 * WAVE, items, p, st);
               }
             }
