@@ -280,9 +280,12 @@ ma_status monarch_attn_backward(const ma_problem* p, const void* q, const void* 
                                 void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Diagnostic helpers around hipEvent_t (thin wrappers of the HIP runtime).
- * monarch_attn_event_elapsed_ms synchronises on event b. */
+ * monarch_attn_event_record records the event on a hipStream_t (null: the
+ * default stream) and does not wait; monarch_attn_event_elapsed_ms
+ * synchronises on event b. */
 ma_status monarch_attn_event_create(void** event);
 ma_status monarch_attn_event_destroy(void* event);
+ma_status monarch_attn_event_record(void* event, void* stream);
 ma_status monarch_attn_event_elapsed_ms(void* a, void* b, float* ms);
 
 /* Static description of a status code. */

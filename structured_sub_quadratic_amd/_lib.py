@@ -87,6 +87,8 @@ def load():
     lib.monarch_attn_event_create.restype = ctypes.c_int
     lib.monarch_attn_event_destroy.argtypes = [vp]
     lib.monarch_attn_event_destroy.restype = ctypes.c_int
+    lib.monarch_attn_event_record.argtypes = [vp, vp]
+    lib.monarch_attn_event_record.restype = ctypes.c_int
     lib.monarch_attn_event_elapsed_ms.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_float)]
     lib.monarch_attn_event_elapsed_ms.restype = ctypes.c_int
     lib.monarch_attn_status_string.argtypes = [ctypes.c_int]

@@ -378,6 +378,11 @@ ma_status monarch_attn_event_destroy(void* event) {
   return hipEventDestroy((hipEvent_t)event) == hipSuccess ? MA_OK : MA_ERR_DEVICE;
 }
 
+ma_status monarch_attn_event_record(void* event, void* stream) {
+  if (!event) return MA_ERR_INVALID_ARGUMENT;
+  return hipEventRecord((hipEvent_t)event, (hipStream_t)stream) == hipSuccess ? MA_OK : MA_ERR_DEVICE;
+}
+
 ma_status monarch_attn_event_elapsed_ms(void* a, void* b, float* ms) {
   if (!a || !b || !ms) return MA_ERR_INVALID_ARGUMENT;
   if (hipEventSynchronize((hipEvent_t)b) != hipSuccess) return MA_ERR_DEVICE;
