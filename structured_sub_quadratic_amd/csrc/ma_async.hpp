@@ -742,6 +742,11 @@ __global__ __launch_bounds__(8 * WAVE, 4) void stage1_pair_kernel(Stage1Params p
 // flat sequence of (item, chunk) units of its items, copying unit u+1 into
 // the other buffer while unit u computes.
 // ---------------------------------------------------------------------------
+// Key chunk of the stage-2 builds of 32 query rows a wave (head_dim 128):
+// 64 keys, so a chunk's copies are issued a whole 64-key chunk of arithmetic
+// ahead of their use (32-key chunks left the copy latency exposed).
+constexpr int KC_R32 = KT;
+
 template <int D, bool KLO, bool WITH_PV, int KC>
 struct Stage2AsyncSmem {
   static constexpr int TILE = KC * SwzTile<D>::RB;
@@ -771,8 +776,15 @@ struct Stage2Async {
   static constexpr bool DIRECT_Y = WITH_PV && NQ > 1;
   static constexpr int STG = WITH_PV && !DIRECT_Y ? NW * WaveRows<D>::BYTES : 0;
   static constexpr int QROWS = NQ * 16 * SwzTile<D>::RB;        // one wave's query rows
-  // queries staged in LDS where they fit (else prefetched into registers)
-  static constexpr bool QLDS = 2 * SM0::BUF + STG + NW * QROWS + 2 * KC * 4 <= 160 * 1024;
+  // Builds of 32 rows a wave (NQ > 1) read the next item's query rows into
+  // the score operands as soon as the current item's last score product has
+  // been issued (the operands are free from then on; the loads overlap that
+  // chunk's softmax and weighted sum), so their LDS holds key chunks only;
+  // bidirectional builds (one code path for every chunk).  Other builds
+  // stage the queries in LDS where they fit (else prefetch them into
+  // registers of their own).
+  static constexpr bool QLATE = NQ > 1 && !CAUSAL;
+  static constexpr bool QLDS = !QLATE && 2 * SM0::BUF + STG + NW * QROWS + 2 * KC * 4 <= 160 * 1024;
   static constexpr int LDS_BYTES = 2 * SM0::BUF + STG + (QLDS ? NW * QROWS : 0) + 2 * KC * 4;
 
   // An item (slice, column i, row tile t, query group qg) and its key chunks.
@@ -864,9 +876,15 @@ struct Stage2Async {
     }
     if (ch == 0) {
       if constexpr (QLDS) copy_queries(it);
-      else Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, row_of(it.qg, n)); },
-                               Q_INPUT, qn, qnl);
+      else if constexpr (!QLATE)
+        Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, row_of(it.qg, n)); },
+                            Q_INPUT, qn, qnl);
     }
+  };
+  // QLATE: the item's query rows straight into the score operands
+  auto load_queries = [&](Core& core, const Item& it) {
+    Core::fetch_queries([&](int n) { return stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, row_of(it.qg, n)); },
+                        Q_INPUT, core.qf, qnl);
   };
 
   const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
@@ -875,6 +893,7 @@ struct Stage2Async {
   int ch = 0;
   issue(cur, 0, buf_a);
   Core core;
+  if constexpr (QLATE) load_queries(core, cur);
   char* stg = stage_rows + (STG ? wave * WaveRows<D>::BYTES : 0);
 
   // y rows and normalisers of the item just finished
@@ -946,7 +965,7 @@ struct Stage2Async {
             core.qf[n][ks_] = *reinterpret_cast<const frag*>(qw + SwzTile<D>::offset(n * 16 + lane % 16, 4 * ks_ + g));
         // the rows are in registers before the next item's copy may refill qw
         __builtin_amdgcn_s_waitcnt(0xC07F);
-      } else {
+      } else if constexpr (!QLATE) {
         core.set_queries(qn, qnl);
       }
     }
@@ -962,6 +981,9 @@ struct Stage2Async {
     int how = CH_WHOLE;
     if constexpr (!CAUSAL) {
       core.scores_v(SwzKeys<D>(cb + SM::HI, cb + SM::LO), 0, Core::MT);
+      if constexpr (QLATE) {
+        if (nchk == 0 && more) load_queries(core, nx);
+      }
       core.template softmax_step<true, false>(bias, p.sc2, 0, KC);
       if constexpr (WITH_PV) core.template pv<false>(SwzValuesT<D>(cb + SM::U, cb + SM::U), 0, KC);
       how = CH_SKIP;
@@ -992,8 +1014,9 @@ struct Stage2Async {
   }
 };
 
-template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false, bool CAUSAL = true>
-__global__ __launch_bounds__(NW * WAVE, NQ > 1 ? 2 : 1) void stage2_async_kernel(Stage2Params p) {
+template <int D, int NW, int NQ, bool WITH_PV, bool PRECISE, int KC = KT, bool PAD = false, bool CAUSAL = true,
+          int WPC = (NQ > 1 ? 2 : 1)>
+__global__ __launch_bounds__(NW * WAVE, WPC) void stage2_async_kernel(Stage2Params p) {
   typedef Stage2Async<D, NW, NQ, WITH_PV, PRECISE, KC, PAD, CAUSAL> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS_BYTES];
   S::run(p, lds);
@@ -1259,9 +1282,9 @@ template <int D, int NW, int KTB, bool PRECISE, int KC2 = KT>
 __global__ __launch_bounds__(NW * WAVE) void fused_async_kernel(Stage1Params p1, Stage2Params p2) {
   typedef Stage1Async<D, NW, KTB, true, PRECISE> S1;
   // head_dim 128 (fast path): the staged launch's stage 2 of 32 rows a wave
-  // and 32-key chunks, so that both give the same result
+  // and KC_R32-key chunks, so that both give the same result
   constexpr bool R32 = D == 128 && !PRECISE;
-  typedef Stage2Async<D, NW, R32 ? 2 : 1, true, PRECISE, R32 ? KT / 2 : KC2> S2;
+  typedef Stage2Async<D, NW, R32 ? 2 : 1, true, PRECISE, R32 ? KC_R32 : KC2> S2;
   // head_dim 64, 8 waves, blocks of 65-128 keys in one segment: the staged
   // launch's whole-block stage 1, so that both give the same result
   constexpr bool PAIR = D == 64 && NW == 8 && KTB == 2 * KT && !PRECISE;

@@ -323,7 +323,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       if constexpr (!is_f32<T>()) {
         {
           // last step at head_dim 128 (bidirectional, unpadded, fast path): 4
-          // waves of 32 rows, 32-key chunks, two workgroups a CU
+          // waves of 32 rows, KC_R32-key chunks, two workgroups a CU
           const bool rows32 = D == 128 && !PRECISE && !pl.causal && !pl.padded && kind == L_STAGE2_LAST;
           const int nw = rows32 ? 4 : stage2_waves<D>(pl.rt), qg = rows32 ? 128 : nw * 16;
           Stage2Params p{b.q, b.y, cx, ux, h2, lse2, kind == L_STAGE2_LAST ? b.lse : nullptr, pl.map,
@@ -335,7 +335,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_A2(NW, PV) do { if (pl.causal) MA_A2C(NW, PV, true); else MA_A2C(NW, PV, false); } while (0)
 #define MA_A2P(NW, PV) launch_persistent(stage2_async_kernel<D, NW, 1, PV, PRECISE, KT, true>, NW * WAVE, items, p, st)
           if constexpr (D == 128 && !PRECISE) {
-            if (rows32) launch_persistent(stage2_async_kernel<D, 4, 2, true, PRECISE, KT / 2, false, false>, 4 * WAVE, items, p, st);
+            if (rows32) launch_persistent(stage2_async_kernel<D, 4, 2, true, PRECISE, KC_R32, false, false>, 4 * WAVE, items, p, st);
           }
           if (rows32) {
           } else if (pl.padded) {
