@@ -66,12 +66,24 @@ __device__ inline bf16x4 lds_read_tr4(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// Row-major tile of bf16 rows of D elements with XOR-swizzled 16-byte chunks.
+// Row-major tile of bf16 rows of D elements with XOR-swizzled 16-byte chunks:
+// chunk c of row r sits at chunk c ^ swz(r).  The score operand reads one
+// chunk from each of 16 consecutive rows, and the transposed value read two
+// adjacent chunks (32 bytes) from each of 8 consecutive rows.  64-element
+// rows (128 bytes) take r mod 8.  128-element rows (256 bytes, so every row
+// starts on the same LDS bank) take 2 (r mod 8) + bit 3 of r: with r mod 8,
+// rows 2j and 2j + 1 put their chunk pair on the same banks, which the
+// bank-conflict counters showed in about half of the LDS cycles of the
+// head_dim-128 kernels; the doubled index gives each of 8 rows a pair of
+// its own and keeps 16 rows on 16 distinct chunks.
 template <int D> struct SwzTile {
   static constexpr int RB = 2 * D;        // bytes per row
   static constexpr int CPR = D / 8;       // 16-byte chunks per row
-  static_assert(CPR >= 8, "swizzle needs at least 8 chunks per row");
-  __device__ static constexpr int offset(int row, int chunk) { return row * RB + ((chunk ^ (row & 7)) << 4); }
+  static_assert(CPR == 8 || CPR == 16, "swizzle for rows of 64 or 128 elements");
+  __host__ __device__ static constexpr int swz(int row) {
+    return CPR == 8 ? (row & 7) : (((row & 7) << 1) | ((row >> 3) & 1));
+  }
+  __device__ static constexpr int offset(int row, int chunk) { return row * RB + ((chunk ^ swz(row)) << 4); }
 
   // Fill rows [0, R) of the tile at lds from rowptr(r) (r clamped to
   // nvalid - 1), the NW waves of the workgroup sharing the copies.
@@ -86,7 +98,7 @@ template <int D> struct SwzTile {
       if (NI % NW != 0 && i >= NI) break;
       const int slot = i * WAVE + lane;
       const int row = slot / CPR, cs = slot % CPR;
-      const int c = cs ^ (row & 7);
+      const int c = cs ^ swz(row);
       copy16_to_lds(rowptr(min(row, nvalid - 1)) + c * 8, lds + i * WAVE * 16);
     }
   }
@@ -834,7 +846,7 @@ struct Stage2Async {
   for (int j = 0; j < NCW; ++j) {
     const int slot = (j * NW + wave) * WAVE + lane;
     crow[j] = slot / CPR;
-    ccol[j] = (uint32_t)(((slot % CPR) ^ (crow[j] & 7)) << 4);
+    ccol[j] = (uint32_t)(((slot % CPR) ^ SwzTile<D>::swz(crow[j])) << 4);
     coff[j] = (size_t)crow[j] * key_bytes + ccol[j];
   }
   auto copy_tile = [&](char* dst, const char* src, int nvalid) {
@@ -853,7 +865,7 @@ struct Stage2Async {
 #pragma unroll
     for (int j = 0; j < QCW; ++j) {
       const int slot = j * WAVE + lane, r = slot / CPR, cs = slot % CPR;
-      const int c = cs ^ (r & 7);
+      const int c = cs ^ SwzTile<D>::swz(r);
       const T* src = stage2_qsrc<T, D, PAD>(p, it.sl, it.i, it.t, it.qg * QG + wave * NQ * 16 + r).t;
       copy16_to_lds(src + c * 8, qw + j * WAVE * 16);
     }
