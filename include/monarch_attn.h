@@ -279,10 +279,15 @@ ma_status monarch_attn_backward(const ma_problem* p, const void* q, const void* 
                                 const void* v, const void* y, const void* dy, void* dq, void* dk,
                                 void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Diagnostic helpers around hipEvent_t (thin wrappers of the HIP runtime).
+/* Diagnostic helpers around hipEvent_t (thin wrappers of the HIP runtime),
+ * for timing only: the events are created with hipEventDisableSystemFence,
+ * so recording one adds no system-scope cache writeback and invalidation
+ * between the launches it separates (such a fence would be timed as part of
+ * the next launch), and waiting on one does not make the device's writes
+ * visible to the host (synchronise the stream for that).
  * monarch_attn_event_record records the event on a hipStream_t (null: the
- * default stream) and does not wait; monarch_attn_event_elapsed_ms
- * synchronises on event b. */
+ * default stream) and does not wait; monarch_attn_event_elapsed_ms waits
+ * for event b. */
 ma_status monarch_attn_event_create(void** event);
 ma_status monarch_attn_event_destroy(void* event);
 ma_status monarch_attn_event_record(void* event, void* stream);

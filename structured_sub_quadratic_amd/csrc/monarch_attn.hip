@@ -368,7 +368,7 @@ const char* monarch_attn_launch_name(const ma_problem* p, int32_t j) {
 ma_status monarch_attn_event_create(void** event) {
   if (!event) return MA_ERR_INVALID_ARGUMENT;
   hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return MA_ERR_DEVICE;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return MA_ERR_DEVICE;
   *event = e;
   return MA_OK;
 }
