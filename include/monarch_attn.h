@@ -226,10 +226,13 @@ int32_t monarch_attn_num_launches(const ma_problem* p);
 /* Name of the j-th kernel launch for *p (static string) or NULL. */
 const char* monarch_attn_launch_name(const ma_problem* p, int32_t j);
 
-/* Diagnostic variant of monarch_attn_forward: additionally records
- * events[0] on `stream` before the first launch and events[j+1] right after
- * launch j, for j < n_events - 1 (events are hipEvent_t created by the
- * caller, e.g. with monarch_attn_event_create).  Never synchronises. */
+/* Diagnostic variant of monarch_attn_forward: events[2j] and events[2j+1]
+ * take the start and end time stamps of kernel launch j, for 2j + 1 <
+ * n_events (hipEvent_t created by the caller, e.g. with
+ * monarch_attn_event_create).  They are recorded with the launch itself
+ * (hipExtLaunchKernel), so nothing is queued between two launches; the
+ * single-launch cooperative path records them just before and after its
+ * launch.  Never synchronises. */
 ma_status monarch_attn_forward_timed(const ma_problem* p, const void* q, const void* k,
                                      const void* v, void* y, const ma_exports* exports,
                                      void* workspace, size_t workspace_bytes, void* stream,

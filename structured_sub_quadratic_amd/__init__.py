@@ -181,8 +181,8 @@ def forward(q, k, v, b1, b2, steps=1, c1=1, c2=1, scale=None, layout="flat", fhw
 def forward_timed(q, k, v, b1, b2, events, steps=1, c1=1, c2=1, scale=None, layout="flat",
                   fhw=None, workspace=None, out=None, force_staged=False, fast_aggregate=False,
                   force_fused=False, precise_aggregate=False, pad="post", causal=0):
-    """forward() that also records events[0] before the first kernel launch and
-    events[j+1] after launch j (Event objects) on the current stream."""
+    """forward() that also records the start and end of kernel launch j into
+    events[2j] and events[2j+1] (Event objects) on the current stream."""
     import torch
     prob, workspace, out, ex, cex = _prepare(q, k, v, b1, b2, steps, c1, c2, scale, layout, fhw,
                                              (), workspace, out, force_staged, fast_aggregate,

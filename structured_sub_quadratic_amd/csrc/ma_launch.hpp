@@ -5,6 +5,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "ma_plan.hpp"
 #include "ma_aux_kernels.hpp"
 #include "ma_stage_kernels.hpp"
@@ -14,6 +16,26 @@
 namespace ma {
 
 inline unsigned grid1(size_t n) { return (unsigned)n; }
+
+// Events that take the start and end time stamps of the launch in progress
+// (set by the timed entry point around each launch, null otherwise).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
+// Every kernel launch of the forward goes through here: with launch events
+// set, the kernel's own start and end are recorded with its dispatch
+// (hipExtLaunchKernel), so nothing is queued between the launches.
+template <class F, class... A>
+inline void ma_launch(F kernel, dim3 grid, dim3 block, hipStream_t st, A... args) {
+  const LaunchEvents& ev = launch_events();
+  if (ev.start) hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 // Workgroups of a persistent launch: two per compute unit of the current
 // device (the persistent kernels are built for two resident workgroups).
@@ -55,7 +77,7 @@ inline bool one_chunk2(const Plan& pl) {
 template <class K, class P>
 void launch_persistent(K kernel, int threads, size_t items, const P& p, hipStream_t st) {
   const size_t g = resident_slots(kernel, threads, items);
-  hipLaunchKernelGGL(kernel, dim3(grid1(g)), dim3(threads), 0, st, p);
+  ma_launch(kernel, dim3(grid1(g)), dim3(threads), st, p);
 }
 
 // Query sub-tiles of 16 per wave: the choice (1 or 2) that pads the fewest
@@ -84,8 +106,12 @@ hipError_t launch_cooperative(K kernel, size_t items, void** args, hipStream_t s
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
   const size_t g = std::max<size_t>(1, std::min<size_t>(items, (size_t)per_cu * cus));
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(grid1(g)), dim3(threads),
-                                    args, 0, st);
+  const LaunchEvents& ev = launch_events();
+  if (ev.start && (e = hipEventRecord(ev.start, st)) != hipSuccess) return e;
+  e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(grid1(g)), dim3(threads), args, 0,
+                                 st);
+  if (e == hipSuccess && ev.stop) e = hipEventRecord(ev.stop, st);
+  return e;
 }
 
 template <typename T, int D, bool PRECISE>
@@ -190,7 +216,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
     }
     case L_QBAR: {
       QbarParams p{b.q, qbar, pl.map, S, N, pl.b2, pl.c1, pl.rt, qbar_lp};
-      hipLaunchKernelGGL((qbar_kernel<T, D>), dim3(grid1((size_t)S * pl.c1 * pl.b2)), dim3(256), 0, st, p);
+      ma_launch((qbar_kernel<T, D>), dim3(grid1((size_t)S * pl.c1 * pl.b2)), dim3(256), st, p);
       break;
     }
     case L_STAGE1:
@@ -279,7 +305,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
         const int qgp = WAVES * 16;
         p.nqg = (nqs + qgp - 1) / qgp;
         const dim3 gp(grid1((size_t)S * pl.b1 * p.nqg));
-#define MA_S1P(U, QS) hipLaunchKernelGGL((stage1_kernel<T, D, 1, KP, U, PRECISE, QS, true>), gp, dim3(THREADS), 0, st, p)
+#define MA_S1P(U, QS) ma_launch((stage1_kernel<T, D, 1, KP, U, PRECISE, QS, true>), gp, dim3(THREADS), st, p)
         if (last) { if (qsplit) MA_S1P(true, true); else MA_S1P(true, false); }
         else { if (qsplit) MA_S1P(false, true); else MA_S1P(false, false); }
 #undef MA_S1P
@@ -291,9 +317,9 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_S1_K(NQ, KTB, U, QS)                                                                   \
   do {                                                                                            \
     if (persistent)                                                                               \
-      hipLaunchKernelGGL((stage1_persistent_kernel<T, D, NQ, KTB, U, PRECISE, QS>), pgrid, dim3(THREADS), 0, st, p); \
+      ma_launch((stage1_persistent_kernel<T, D, NQ, KTB, U, PRECISE, QS>), pgrid, dim3(THREADS), st, p); \
     else                                                                                          \
-      hipLaunchKernelGGL((stage1_kernel<T, D, NQ, KTB, U, PRECISE, QS>), grid, dim3(THREADS), 0, st, p); \
+      ma_launch((stage1_kernel<T, D, NQ, KTB, U, PRECISE, QS>), grid, dim3(THREADS), st, p); \
   } while (0)
 #define MA_S1(NQ, KTB, U)                                                                         \
   do {                                                                                            \
@@ -370,8 +396,8 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       if (pl.padded) {     // one build: one query sub-tile a wave
         p.nqg = (pl.rt + WAVES * 16 - 1) / (WAVES * 16);
         const dim3 gp(grid1((size_t)S * pl.b2 * pl.c1 * p.nqg));
-        if (last) hipLaunchKernelGGL((stage2_kernel<T, D, 1, true, PRECISE, true>), gp, dim3(THREADS), 0, st, p);
-        else hipLaunchKernelGGL((stage2_kernel<T, D, 1, false, PRECISE, true>), gp, dim3(THREADS), 0, st, p);
+        if (last) ma_launch((stage2_kernel<T, D, 1, true, PRECISE, true>), gp, dim3(THREADS), st, p);
+        else ma_launch((stage2_kernel<T, D, 1, false, PRECISE, true>), gp, dim3(THREADS), st, p);
         break;
       }
       const size_t items2 = (size_t)S * pl.b2 * pl.c1 * p.nqg;
@@ -383,14 +409,14 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 #define MA_S2_P(NQ, PV)                                                                           \
   do {                                                                                            \
     if (ktb == 64)                                                                                \
-      hipLaunchKernelGGL((stage2_persistent_kernel<T, D, NQ, 64, PV, PRECISE>), pgrid, dim3(THREADS), 0, st, p); \
+      ma_launch((stage2_persistent_kernel<T, D, NQ, 64, PV, PRECISE>), pgrid, dim3(THREADS), st, p); \
     else if constexpr (!(is_f32<T>() && D == 128))                                                \
-      hipLaunchKernelGGL((stage2_persistent_kernel<T, D, NQ, 128, PV, PRECISE>), pgrid, dim3(THREADS), 0, st, p); \
+      ma_launch((stage2_persistent_kernel<T, D, NQ, 128, PV, PRECISE>), pgrid, dim3(THREADS), st, p); \
   } while (0)
 #define MA_S2(NQ, PV)                                                                             \
   do {                                                                                            \
     if (persistent) MA_S2_P(NQ, PV);                                                              \
-    else hipLaunchKernelGGL((stage2_kernel<T, D, NQ, PV, PRECISE>), grid, dim3(THREADS), 0, st, p); \
+    else ma_launch((stage2_kernel<T, D, NQ, PV, PRECISE>), grid, dim3(THREADS), st, p); \
   } while (0)
       if (nq == 1) { if (last) MA_S2(1, true); else MA_S2(1, false); }
       else { if (last) MA_S2(2, true); else MA_S2(2, false); }
@@ -403,7 +429,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
         // one workgroup per column (b1 <= 64 rows and keys, untiled)
         Stage2Params p{b.q, b.y, cx, ux, h2, lse2, nullptr, pl.map,
                        S, N, pl.b1, pl.b2, 1, 1, pl.rt, pl.b1, 1, pl.sc2, pl.xlo, 0};
-        hipLaunchKernelGGL((stage2_alpha_kernel<D, PRECISE>), dim3(grid1((size_t)S * pl.b2)), dim3(256), 0, st,
+        ma_launch((stage2_alpha_kernel<D, PRECISE>), dim3(grid1((size_t)S * pl.b2)), dim3(256), st,
                            p, qtil);
       }
       break;
@@ -418,7 +444,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       p.beta_out = kind == L_ALPHA && pl.beta_out ? reinterpret_cast<float*>(ws + pl.off_beta) : nullptr;
       p.causal = pl.causal;
       const size_t wgs = (size_t)S * pl.b2 * pl.c1 * p.nkt;
-      hipLaunchKernelGGL((alpha_kernel<T, D, PRECISE>), dim3(grid1(wgs)), dim3(THREADS), 0, st, p);
+      ma_launch((alpha_kernel<T, D, PRECISE>), dim3(grid1(wgs)), dim3(THREADS), st, p);
       break;
     }
     case L_EXPORT_R: {
@@ -427,12 +453,12 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
       p.heads = pl.heads;
       p.group = pl.group;
       const size_t total = (size_t)S * pl.b1 * pl.b2 * pl.c1 * pl.b2;
-      hipLaunchKernelGGL(r_export_kernel<T>, dim3(grid1((total + 255) / 256)), dim3(256), 0, st, p);
+      ma_launch(r_export_kernel<T>, dim3(grid1((total + 255) / 256)), dim3(256), st, p);
       break;
     }
     case L_OBJECTIVE: {
       ObjectiveParams p{lse2, b.obj, pl.map};
-      hipLaunchKernelGGL(objective_kernel, dim3(S), dim3(256), 0, st, p);
+      ma_launch(objective_kernel, dim3(S), dim3(256), st, p);
       break;
     }
   }
@@ -442,14 +468,14 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
 template <typename T, int D, bool PRECISE>
 ma_status run_t(const Plan& pl, const Bufs& b, hipStream_t st, void* const* events, int n_events) {
   ma_status status = MA_OK;
-  if (events && n_events > 0 && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess) return MA_ERR_DEVICE;
   for_each_launch(pl, b.L != nullptr, b.R != nullptr, b.obj != nullptr,
                   [&](int j, LaunchKind kind, int step) {
                     if (status != MA_OK) return;
-                    if (launch_one<T, D, PRECISE>(pl, b, kind, step, st) != hipSuccess) { status = MA_ERR_DEVICE; return; }
-                    if (events && j + 1 < n_events &&
-                        hipEventRecord((hipEvent_t)events[j + 1], st) != hipSuccess)
-                      status = MA_ERR_DEVICE;
+                    if (events && 2 * j + 1 < n_events)
+                      launch_events() = LaunchEvents{(hipEvent_t)events[2 * j], (hipEvent_t)events[2 * j + 1]};
+                    const hipError_t e = launch_one<T, D, PRECISE>(pl, b, kind, step, st);
+                    launch_events() = LaunchEvents{};
+                    if (e != hipSuccess) status = MA_ERR_DEVICE;
                   });
   return status;
 }

@@ -182,6 +182,32 @@ def test_single_token_and_tiny_grids():
         check_case(cfg)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_timed_entry_point_times_every_launch(fused):
+    """monarch_attn_forward_timed: the same output as the plain call, and a
+    start and end time stamp for every launch, in launch order."""
+    import torch
+    import structured_sub_quadratic_amd as ma
+    cfg = WorkloadConfig("case", "timed", batch=1, heads=2, seq_len=24 * 100, head_dim=64, b1=24,
+                         b2=100, steps=1 if fused else 3, dtype="bf16", data="normed", seed=29)
+    Q, K, V = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (Q, K, V))
+    prob = ma.make_problem(1, 2, cfg.seq_len, 64, 24, 100, cfg.steps, dtype="bf16",
+                           flags=ma.MA_FLAG_FORCE_FUSED if fused else 0)
+    names = ma.launch_names(prob)
+    assert len(names) == (1 if fused else 2 * cfg.steps)
+    events = [ma.Event() for _ in range(2 * len(names))]
+    y_t = ma.forward_timed(tq, tk, tv, 24, 100, events, cfg.steps, force_fused=fused)
+    y = ma.forward(tq, tk, tv, 24, 100, cfg.steps, force_fused=fused)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_t)
+    for j in range(len(names)):
+        assert events[2 * j].elapsed_ms(events[2 * j + 1]) > 0
+        if j:
+            assert events[2 * j - 1].elapsed_ms(events[2 * j]) >= 0
+
+
 def test_determinism_and_reuse_of_workspace():
     import torch
     import structured_sub_quadratic_amd as ma
