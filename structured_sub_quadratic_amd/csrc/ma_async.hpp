@@ -61,6 +61,42 @@ __device__ inline void copy16_to_lds(const void* g, void* wave_base) {
       : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
 }
 
+// N (2 or 4) such copies of one wave in a row: g[j] -> LDS byte address
+// lds[j] (uniform), M0 saved once.  Same ordering contract as above.
+__device__ inline void copy16x2_to_lds(const void* g0, const void* g1, uint32_t l0, uint32_t l1) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved) : "s"(l0), "s"(l1), "v"(g0), "v"(g1) : "memory");
+}
+__device__ inline void copy16x4_to_lds(const void* g0, const void* g1, const void* g2, const void* g3,
+                                       uint32_t l0, uint32_t l1, uint32_t l2, uint32_t l3) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, off\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, off\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %7, off\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %8, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved) : "s"(l0), "s"(l1), "s"(l2), "s"(l3), "v"(g0), "v"(g1), "v"(g2), "v"(g3) : "memory");
+}
+
 __device__ inline bf16x4 lds_read_tr4(const char* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
   return __builtin_bit_cast(bf16x4, v);
@@ -850,6 +886,18 @@ struct Stage2Async {
     coff[j] = (size_t)crow[j] * key_bytes + ccol[j];
   }
   auto copy_tile = [&](char* dst, const char* src, int nvalid) {
+    if constexpr (NI % NW == 0 && (NCW == 2 || NCW == 4)) {
+      // a whole chunk: one address add a copy, the copies of the tile in
+      // one block (copy j lands NW * WAVE * 16 bytes after copy j - 1)
+      if (nvalid == KC) {
+        constexpr uint32_t ST = NW * WAVE * 16;
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + wave * WAVE * 16));
+        if constexpr (NCW == 2) copy16x2_to_lds(src + coff[0], src + coff[1], l0, l0 + ST);
+        else copy16x4_to_lds(src + coff[0], src + coff[1], src + coff[2], src + coff[3], l0, l0 + ST,
+                             l0 + 2 * ST, l0 + 3 * ST);
+        return;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
       const int ii = j * NW + wave;
