@@ -448,6 +448,12 @@ def test_error_vs_exact_attention_reported(key):
     dict(dtype="bf16", d=64, b1=70, b2=52, g=1, c=(5, 2), steps=3),
     dict(dtype="bf16", d=128, b1=24, b2=100, g=4, c=(1, 1), steps=1),
     dict(dtype="bf16", d=64, b1=96, b2=40, g=7, c=(1, 1), steps=3),
+    # columns of 65-128 keys at head_dim 64 with blocks of more than 64 keys:
+    # one 128-key chunk an item (staged: the one-chunk kernel, fused: the
+    # general stage 2 with 128-key chunks), per-row bounds and whole chunks
+    dict(dtype="bf16", d=64, b1=100, b2=100, g=1, c=(1, 1), steps=1),
+    dict(dtype="bf16", d=64, b1=120, b2=72, g=20, c=(1, 1), steps=1),
+    dict(dtype="bf16", d=64, b1=100, b2=100, g=3, c=(1, 1), steps=2),
 ])
 def test_block_causal(case):
     """Block-causal use: query block l attends to key block k iff
