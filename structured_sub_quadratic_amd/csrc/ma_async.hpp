@@ -637,7 +637,10 @@ __global__ __launch_bounds__(4 * WAVE, 2) void stage1_small_kernel(Stage1Params 
 // probabilities with one 64-wide accumulator.  80 KB of LDS and at most 128
 // registers a lane: two workgroups share a CU, four waves a SIMD.
 // ---------------------------------------------------------------------------
-template <int D>
+// PAD: a padded flat sequence (padding positions clamped on load, the keys
+// outside the block's real range masked, padding query slots read the bf16
+// column means).
+template <int D, bool PAD = false>
 struct Stage1Pair {
   static constexpr int NW = 8, QG = NW * 16;
   static constexpr int HALF = KT * SwzTile<D>::RB;        // one 64-row tile
@@ -647,7 +650,7 @@ struct Stage1Pair {
 
   // the launches this body serves
   __host__ __device__ static bool serves(int b2, int c1, int c2, bool padded) {
-    return b2 > KT && b2 <= 2 * KT && c1 == 1 && c2 == 1 && !padded;
+    return b2 > KT && b2 <= 2 * KT && c1 == 1 && c2 == 1 && padded == PAD;
   }
 
   __device__ static void run(const Stage1Params& p, char* lds) {
@@ -674,14 +677,22 @@ struct Stage1Pair {
     };
     frag qn[Core::NKS];
     auto issue = [&](const It& it, char* b) {
-      const AxisMap am = p.map.template row_axis<false>(it.k);
+      const AxisMap am = p.map.template row_axis<PAD>(it.k);
+      auto tok = [&](int r) -> int64_t { if constexpr (PAD) return am.at(r); else return am.raw(r); };
       const int kvs = kv_slice(it.sl, p.heads, p.group);
       const T* K = static_cast<const T*>(p.k) + (size_t)kvs * p.N * D;
       const T* V = static_cast<const T*>(p.v) + (size_t)kvs * p.N * D;
-      SwzTile<D>::template load<2 * KT, NW>(b, [&](int r) { return K + am.raw(r) * D; }, p.b2);
-      SwzTile<D>::template load<2 * KT, NW>(b + TILE, [&](int r) { return V + am.raw(r) * D; }, p.b2);
+      SwzTile<D>::template load<2 * KT, NW>(b, [&](int r) { return K + tok(r) * D; }, p.b2);
+      SwzTile<D>::template load<2 * KT, NW>(b + TILE, [&](int r) { return V + tok(r) * D; }, p.b2);
       const int i = min(it.qg * QG + slot0 + lane % 16, p.nqs - 1);
-      const T* src = static_cast<const T*>(p.q) + ((size_t)it.sl * p.N + am.raw(i)) * D;
+      const T* src;
+      if constexpr (PAD) {
+        // a padding slot (k, i) takes the mean of the real rows of column i
+        src = am.valid(i) ? static_cast<const T*>(p.q) + ((size_t)it.sl * p.N + am.at(i)) * D
+                          : static_cast<const T*>(p.qbar_lp) + ((size_t)it.sl * p.b2 + i) * D;
+      } else {
+        src = static_cast<const T*>(p.q) + ((size_t)it.sl * p.N + am.raw(i)) * D;
+      }
 #pragma unroll
       for (int ks_ = 0; ks_ < Core::NKS; ++ks_) qn[ks_] = *reinterpret_cast<const frag*>(src + ks_ * 32 + g * 8);
     };
@@ -710,9 +721,25 @@ struct Stage1Pair {
       core.template scores_v<0>(SwzKeys<D>(cur, nullptr), 0, Core::MT);
       core.template scores_v<1>(SwzKeys<D>(cur + HALF, nullptr), 0, Core::MT);
       // softmax over the block: keys 16 mt + 4 g + r of each tile; keys past
-      // b2 (second tile) masked
+      // b2 (second tile) masked, and with padding the keys outside the
+      // block's real range [klo, khi)
       {
         constexpr float MASKED = -1e30f;
+        if constexpr (PAD) {
+          // only the block holding padding positions masks keys here (a
+          // pass of its own, so the other blocks run the unpadded code)
+          const int klo = p.map.key_lo(it.k), khi = min(p.map.key_hi(it.k), p.b2);
+          if (klo > 0 || khi < p.b2) {
+#pragma unroll
+            for (int mt = 0; mt < Core::MT; ++mt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int key0 = mt * 16 + 4 * g + r, key1 = KT + key0;
+                if (key0 < klo || key0 >= khi) core.s[0][mt][r] = MASKED;
+                if (key1 < klo || key1 >= khi) core.s2[0][mt][r] = MASKED;
+              }
+          }
+        }
         float zs[8 * Core::MT];
 #pragma unroll
         for (int mt = 0; mt < Core::MT; ++mt)
@@ -778,10 +805,10 @@ struct Stage1Pair {
   }
 };
 
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(8 * WAVE, 4) void stage1_pair_kernel(Stage1Params p) {
-  __shared__ __attribute__((aligned(1024))) char lds[Stage1Pair<D>::LDS_BYTES];
-  Stage1Pair<D>::run(p, lds);
+  __shared__ __attribute__((aligned(1024))) char lds[Stage1Pair<D, PAD>::LDS_BYTES];
+  Stage1Pair<D, PAD>::run(p, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1093,7 +1120,9 @@ __global__ __launch_bounds__(NW * WAVE, WPC) void stage2_async_kernel(Stage2Para
 // the accumulators.  64 KB of LDS and at most 128 registers a lane, so two
 // workgroups share a CU at four waves a SIMD.
 // ---------------------------------------------------------------------------
-template <int D>
+// PAD: a padded flat sequence (query rows clamped on load, no output at
+// padding positions).
+template <int D, bool PAD = false>
 struct Stage2Col {
   static constexpr int NW = 8, QG = NW * 16, KC = 2 * KT;
   static constexpr int TILE = KC * SwzTile<D>::RB;
@@ -1101,7 +1130,7 @@ struct Stage2Col {
   static constexpr int LDS_BYTES = 2 * BUF + 2 * KC * 4;
 
   __host__ __device__ static bool serves(int b2, int c1, int nkeys, int causal, bool padded) {
-    return b2 > KT && c1 == 1 && nkeys > KT && nkeys <= KC && !causal && !padded;
+    return b2 > KT && c1 == 1 && nkeys > KT && nkeys <= KC && !causal && padded == PAD;
   }
 
   __device__ static void run(const Stage2Params& p, char* lds) {
@@ -1140,7 +1169,7 @@ struct Stage2Col {
 #pragma unroll
         for (int j = 0; j < KC / WAVE; ++j) hn[j] = p.h2x[base + (size_t)min(lane + WAVE * j, p.nkeys - 1) * xs];
       }
-      Core::fetch_queries([&](int) { return stage2_qsrc<T, D, false>(p, it.sl, it.i, 0, row_of(it.qg)); },
+      Core::fetch_queries([&](int) { return stage2_qsrc<T, D, PAD>(p, it.sl, it.i, 0, row_of(it.qg)); },
                           Q_INPUT, qn, qnl);
     };
     Core core;
@@ -1165,16 +1194,26 @@ struct Stage2Col {
       float lse2[1], h2[1];
       core.finish(lse2, h2, p.sc2);
       // y rows: lane (q, g) holds columns 16 dt + 4 g .. + 3 of row q
-      const AxisMap am = p.map.template col_axis<false>(it.i);
+      const AxisMap am = p.map.template col_axis<PAD>(it.i);
       const int l = row_of(it.qg);
       if (l < p.rt) {
-        T* dst = static_cast<T*>(p.y) + ((size_t)it.sl * p.N + am.raw(l)) * D;
+        bool real = true;
+        int64_t tk;
+        if constexpr (PAD) {
+          real = am.valid(l);
+          tk = am.at(l);
+        } else {
+          tk = am.raw(l);
+        }
+        if (real) {
+          T* dst = static_cast<T*>(p.y) + ((size_t)it.sl * p.N + tk) * D;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-          *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * g) = __builtin_convertvector(core.o[0][dt], bf16x4);
+          for (int dt = 0; dt < D / 16; ++dt)
+            *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * g) = __builtin_convertvector(core.o[0][dt], bf16x4);
+        }
         if (g == 0) {
           p.lse2[((size_t)it.sl * p.b2 + it.i) * p.b1 + l] = lse2[0];
-          if (p.lse_out) p.lse_out[(size_t)it.sl * p.N + am.raw(l)] = lse2[0] * LN2;
+          if (p.lse_out && real) p.lse_out[(size_t)it.sl * p.N + tk] = lse2[0] * LN2;
         }
       }
     };
@@ -1191,10 +1230,10 @@ struct Stage2Col {
   }
 };
 
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(8 * WAVE, 4) void stage2_col_kernel(Stage2Params p) {
-  __shared__ __attribute__((aligned(1024))) char lds[Stage2Col<D>::LDS_BYTES];
-  Stage2Col<D>::run(p, lds);
+  __shared__ __attribute__((aligned(1024))) char lds[Stage2Col<D, PAD>::LDS_BYTES];
+  Stage2Col<D, PAD>::run(p, lds);
 }
 
 // ---------------------------------------------------------------------------

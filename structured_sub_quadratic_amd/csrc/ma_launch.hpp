@@ -259,7 +259,11 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
             // in one pass, c and u in turn, two workgroups a CU
             if (last && step == 0 && nw == 8 && Stage1Pair<D>::serves(pl.b2, pl.c1, pl.c2, pl.padded)) {
               small = true;
-              launch_persistent(stage1_pair_kernel<D>, 8 * WAVE, items, p, st);
+              launch_persistent(stage1_pair_kernel<D, false>, 8 * WAVE, items, p, st);
+            } else if (last && step == 0 && nw == 8 && qbar_lp &&
+                       Stage1Pair<D, true>::serves(pl.b2, pl.c1, pl.c2, pl.padded)) {
+              small = true;
+              launch_persistent(stage1_pair_kernel<D, true>, 8 * WAVE, items, p, st);
             }
           }
           if constexpr (D == 128 && !PRECISE) {
@@ -365,7 +369,16 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
           }
           if (rows32) {
           } else if (pl.padded) {
-            if (nw == 8) { if (last) MA_A2P(8, true); else MA_A2P(8, false); }
+            bool col = false;
+            if constexpr (D == 64 && !PRECISE) {
+              // the last step over columns of 65-128 keys: one chunk an item
+              if (last && nw == 8 && Stage2Col<D, true>::serves(pl.b2, pl.c1, pl.b1 * pl.c2, pl.causal, true)) {
+                col = true;
+                launch_persistent(stage2_col_kernel<D, true>, 8 * WAVE, items, p, st);
+              }
+            }
+            if (col) {
+            } else if (nw == 8) { if (last) MA_A2P(8, true); else MA_A2P(8, false); }
             else { if (last) MA_A2P(4, true); else MA_A2P(4, false); }
           } else if (nw == 8) {
             bool one = false;            // a column of up to 128 keys in one chunk
@@ -373,7 +386,7 @@ hipError_t launch_one(const Plan& pl, const Bufs& b, LaunchKind kind, int step, 
               if (one_chunk2(pl)) {
                 one = true;
                 // (one_chunk2: no causal mask)
-                if (last && !PRECISE) launch_persistent(stage2_col_kernel<D>, 8 * WAVE, items, p, st);
+                if (last && !PRECISE) launch_persistent(stage2_col_kernel<D, false>, 8 * WAVE, items, p, st);
                 else if (last) launch_persistent(stage2_async_kernel<D, 8, 1, true, PRECISE, 2 * KT, false, false>, 8 * WAVE, items, p, st);
                 else launch_persistent(stage2_async_kernel<D, 8, 1, false, PRECISE, 2 * KT, false, false>, 8 * WAVE, items, p, st);
               }

@@ -337,6 +337,19 @@ def test_padded_tiles(pad, case):
 
 
 @pytest.mark.parametrize("pad", ["pre", "post"])
+@pytest.mark.parametrize("b1,b2,npad", [(100, 100, 60), (72, 128, 127), (128, 65, 1)])
+def test_padded_blocks_over_64_keys(pad, b1, b2, npad):
+    """T = 1 at head_dim 64 with blocks of 65-128 keys and padding (the
+    whole-block stage 1 and the one-chunk stage 2 with padding): every slice,
+    every column, every export, including a block whose real keys all but
+    one are padding and a grid with a single padding position."""
+    cfg = WorkloadConfig("case", f"pad={pad} {b1}x{b2}-{npad}", batch=2, heads=2,
+                         seq_len=b1 * b2 - npad, head_dim=64, b1=b1, b2=b2, steps=1, dtype="bf16",
+                         data="normed", seed=53, pad=pad)
+    check_case(cfg)
+
+
+@pytest.mark.parametrize("pad", ["pre", "post"])
 def test_padded_long_sequence_sampled(pad):
     """16384 - 100 tokens on the 128 x 128 grid, 12 query heads over 4 K/V
     heads, in the default launch configuration: two slices, every column."""
