@@ -184,17 +184,33 @@ template <int D> struct SwzValuesT {
   }
 };
 
+// Lanes of one wave exchanging data through LDS: the hardware runs a wave's
+// LDS instructions in order, but the compiler reasons per lane and may
+// reuse an earlier read of an address that this lane did not write in
+// between (another lane's write is invisible to it without
+// synchronisation).  A wavefront-scope release, a scheduling barrier and an
+// acquire make the other lanes' writes visible and keep the accesses in
+// program order.
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // A wave's 16-row output tile (accumulator layout: lane (q, g) holds
 // elements 16*dt + 4*g .. +3 of row q) written to global memory as whole
 // 16-byte row chunks through a per-wave LDS staging tile of 16 rows: lanes
 // then cover complete rows, so each store instruction writes full lines
-// instead of sixteen partial ones.  Ordering inside a wave needs no barrier.
+// instead of sixteen partial ones.  The lanes meet at wave_sync() before
+// the tile is written (the previous drain's reads are done) and before it
+// is read.
 template <int D> struct WaveRows {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int RPI = WAVE / CPR;     // rows per store instruction
   static constexpr int BYTES = 16 * SwzTile<D>::RB;
   __device__ static inline void put(char* stg, const bf16x4 (&v)[D / 16]) {
     const int lane = threadIdx.x % WAVE, q = lane % 16, g = lane / 16;
+    wave_sync();
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
       *reinterpret_cast<bf16x4*>(stg + SwzTile<D>::offset(q, 2 * dt + g / 2) + 8 * (g % 2)) = v[dt];
@@ -203,6 +219,7 @@ template <int D> struct WaveRows {
   template <class RowPtr>
   __device__ static inline void drain(const char* stg, RowPtr row) {
     const int lane = threadIdx.x % WAVE, c = lane % CPR;
+    wave_sync();
 #pragma unroll
     for (int r0 = 0; r0 < 16; r0 += RPI) {
       const int r = r0 + lane / CPR;
@@ -1116,9 +1133,9 @@ __global__ __launch_bounds__(NW * WAVE, WPC) void stage2_async_kernel(Stage2Para
 // 128-key chunk.  The same arithmetic as the general stage 2 on such a
 // column (one online-softmax update from a fresh state, then O += P U), with
 // a leaner data path: each wave reads its query rows of the next item into
-// registers, the bias row is staged by one wave, and y leaves straight from
-// the accumulators.  64 KB of LDS and at most 128 registers a lane, so two
-// workgroups share a CU at four waves a SIMD.
+// registers, the bias row is staged by one wave, and y leaves through an
+// 8-row staging tile per wave.  73 KB of LDS and at most 128 registers a
+// lane, so two workgroups share a CU at four waves a SIMD.
 // ---------------------------------------------------------------------------
 // PAD: a padded flat sequence (query rows clamped on load, no output at
 // padding positions).
@@ -1127,7 +1144,8 @@ struct Stage2Col {
   static constexpr int NW = 8, QG = NW * 16, KC = 2 * KT;
   static constexpr int TILE = KC * SwzTile<D>::RB;
   static constexpr int BUF = 2 * TILE;                     // c tile, u tile
-  static constexpr int LDS_BYTES = 2 * BUF + 2 * KC * 4;
+  static constexpr int STG = 8 * SwzTile<D>::RB;           // a wave's y staging: 8 rows
+  static constexpr int LDS_BYTES = 2 * BUF + 2 * KC * 4 + NW * STG;
 
   __host__ __device__ static bool serves(int b2, int c1, int nkeys, int causal, bool padded) {
     return b2 > KT && c1 == 1 && nkeys > KT && nkeys <= KC && !causal && padded == PAD;
@@ -1142,6 +1160,7 @@ struct Stage2Col {
     float* const bias_a = reinterpret_cast<float*>(lds + 2 * BUF);
     float* const bias_b = bias_a + KC;
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, g = lane / 16;
+    char* const stg = lds + 2 * BUF + 2 * KC * 4 + wave * STG;
     const int nitems = p.S * p.b2 * p.nqg;
     const size_t xs = x_stride(p.b2, p.c1);
     struct It {
@@ -1193,28 +1212,51 @@ struct Stage2Col {
       core.template pv<false>(SwzValuesT<D>(cur + TILE, cur + TILE), 0, KC);
       float lse2[1], h2[1];
       core.finish(lse2, h2, p.sc2);
-      // y rows: lane (q, g) holds columns 16 dt + 4 g .. + 3 of row q
+      // y rows: lane (q, g) holds columns 16 dt + 4 g .. + 3 of row q.  They
+      // leave through the wave's 8-row staging tile, half the rows at a
+      // time, so that every store instruction writes whole rows (whole
+      // lines) instead of a quarter of each of 16 rows.
       const AxisMap am = p.map.template col_axis<PAD>(it.i);
-      const int l = row_of(it.qg);
-      if (l < p.rt) {
-        bool real = true;
-        int64_t tk;
+      auto real_row = [&](int l, int64_t& tk) -> bool {
         if constexpr (PAD) {
-          real = am.valid(l);
           tk = am.at(l);
+          return l < p.rt && am.valid(l);
         } else {
           tk = am.raw(l);
+          return l < p.rt;
         }
-        if (real) {
-          T* dst = static_cast<T*>(p.y) + ((size_t)it.sl * p.N + tk) * D;
+      };
+      {
+        bf16x4 v[D / 16];
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt)
-            *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * g) = __builtin_convertvector(core.o[0][dt], bf16x4);
+        for (int dt = 0; dt < D / 16; ++dt) v[dt] = __builtin_convertvector(core.o[0][dt], bf16x4);
+        T* const Y = static_cast<T*>(p.y) + (size_t)it.sl * p.N * D;
+        const int l0 = it.qg * QG + wave * 16, q = lane % 16;
+        constexpr int CPR = D / 8, RPI = WAVE / CPR;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          wave_sync();        // the previous reads of the tile are done
+          if ((q >> 3) == h) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+              *reinterpret_cast<bf16x4*>(stg + SwzTile<D>::offset(q - 8 * h, 2 * dt + g / 2) + 8 * (g % 2)) = v[dt];
+          }
+          wave_sync();        // every lane's half of the rows is in the tile
+#pragma unroll
+          for (int r0 = 0; r0 < 8; r0 += RPI) {
+            const int r = r0 + lane / CPR, c = lane % CPR;
+            const bf16x8 val = *reinterpret_cast<const bf16x8*>(stg + SwzTile<D>::offset(r, c));
+            int64_t tk;
+            if (real_row(l0 + 8 * h + r, tk)) *reinterpret_cast<bf16x8*>(Y + tk * D + c * 8) = val;
+          }
         }
-        if (g == 0) {
-          p.lse2[((size_t)it.sl * p.b2 + it.i) * p.b1 + l] = lse2[0];
-          if (p.lse_out && real) p.lse_out[(size_t)it.sl * p.N + tk] = lse2[0] * LN2;
-        }
+      }
+      const int l = row_of(it.qg);
+      int64_t tk;
+      const bool real = real_row(l, tk);
+      if (l < p.rt && g == 0) {
+        p.lse2[((size_t)it.sl * p.b2 + it.i) * p.b1 + l] = lse2[0];
+        if (p.lse_out && real) p.lse_out[(size_t)it.sl * p.N + tk] = lse2[0] * LN2;
       }
     };
     const int item0 = (int)xcd_swizzle(blockIdx.x, gridDim.x);
